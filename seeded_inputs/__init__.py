@@ -1,0 +1,162 @@
+"""Seeded synthetic inputs for the Lizard hybrid attention layer.
+
+This module is shared by the tests, the benchmark and the oracle's callers.
+It draws random numbers and rounds them to the storage precision; it holds
+none of the layer's arithmetic.  Every (config, tensor, batch, head) slice
+has its own counter-keyed stream
+``PCG64(SeedSequence(ROOT_SEED, spawn_key=(cfg, tensor, b, h)))`` so any
+slice can be regenerated alone, which is how the oracle checks sampled heads
+of the large workloads.
+
+Distributions (the workloads of the Lizard layer on LLaMA-3-8B-shaped
+attention, H=32 and d=128; "Lizard: An Efficient Linearization Framework for
+Large Language Models", gist.science, section 4 "Ergebnisse"):
+
+* q, k, v ~ N(0, 1) / 8
+* gate logits ~ N(mu_g, sd_g) per token per key dim, and the log-gate handed
+  to the layer is log(sigmoid(logit)), computed in float64 and rounded once
+  to float32 (the gate is a sigmoid of a learned projection; same page,
+  section 2, "Kernkomponenten", item 1)
+* meta-memory sink keys ~ N(0, 1) / 8, one set per head
+* upstream gradient dY ~ N(0, 1)
+
+Tensors in bfloat16 are rounded from float64 to the nearest bfloat16 with
+ties to even, once; the float64 widening of those bits is what the oracle
+consumes.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+ROOT_SEED = 250709025
+
+# tensor ids in the spawn key
+T_Q, T_K, T_V, T_GATE, T_META, T_DY = 0, 1, 2, 3, 4, 5
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """Sizes and input distributions of one workload."""
+
+    name: str
+    cfg_id: int
+    dtype: str  # "f32" or "bf16"
+    B: int
+    H: int
+    L: int
+    d: int
+    chunk: int = 64
+    window: int = 64
+    n_meta: int = 4
+    alpha: float = 0.5
+    gate_mu: float = 3.0
+    gate_sd: float = 1.0
+    qkv_sd: float = 0.125
+    meta_sd: float = 0.125
+    steps: int = 0  # decode steps after an L-token prefill
+
+
+# Workload table.  The first is the small case the oracle finishes in
+# seconds; the second is the Llama-3-8B-shaped prefill layer the benchmark
+# times; then long-context prefill, decode and the training backward.
+WORKLOADS: Dict[str, Workload] = {
+    "tiny_fwd_f32": Workload("tiny_fwd_f32", 0, "f32", B=1, H=2, L=256, d=64),
+    "llama3_8b_prefill_bf16": Workload("llama3_8b_prefill_bf16", 1, "bf16", B=4, H=32, L=4096, d=128),
+    "long_ctx_32k_bf16": Workload("long_ctx_32k_bf16", 2, "bf16", B=1, H=32, L=32768, d=128,
+                                  gate_mu=2.0, gate_sd=2.0),
+    "decode_b64_bf16": Workload("decode_b64_bf16", 3, "bf16", B=64, H=32, L=2048, d=128, steps=1024),
+    "train_bwd_bf16": Workload("train_bwd_bf16", 4, "bf16", B=8, H=32, L=2048, d=128),
+}
+
+
+def _rng(cfg: int, tensor: int, b: int, h: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(ROOT_SEED, spawn_key=(cfg, tensor, b, h))))
+
+
+def round_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float64/float32 values to bfloat16 (nearest, ties to even).
+
+    Returns the 16-bit patterns as uint16.  Values are first rounded to
+    float32 (exact for the distributions used here up to one float32 ulp,
+    far below bfloat16 resolution), then the low 16 bits are rounded away.
+    """
+    f = np.ascontiguousarray(x, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    nan = np.isnan(f)
+    if nan.any():
+        r[nan] = 0x7FC0
+    return r
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float64 values to the storage dtype and widen back to float64."""
+    if dtype == "f32":
+        return x.astype(np.float32).astype(np.float64)
+    if dtype == "bf16":
+        return bf16_bits_to_f64(round_bf16_bits(x))
+    raise ValueError(dtype)
+
+
+def _log_sigmoid(x: np.ndarray) -> np.ndarray:
+    # log(1/(1+e^{-x})) without overflow for large |x|
+    return -np.logaddexp(0.0, -x)
+
+
+def slice_inputs(w: Workload, b: int, h: int, L: Optional[int] = None, with_dy: bool = False) -> Dict[str, np.ndarray]:
+    """Float64 values (already rounded to storage precision) of one (b, h) slice.
+
+    Returns q, k, v [L, d], log_g [L, d] (float32 values), and dy [L, d]
+    if requested.  ``L`` defaults to the workload's length (for decode
+    workloads: prefill length + steps).
+    """
+    if L is None:
+        L = w.L + w.steps
+    d = w.d
+    out = {}
+    for name, tid in (("q", T_Q), ("k", T_K), ("v", T_V)):
+        out[name] = round_to(_rng(w.cfg_id, tid, b, h).standard_normal((L, d)) * w.qkv_sd, w.dtype)
+    logits = _rng(w.cfg_id, T_GATE, b, h).normal(w.gate_mu, w.gate_sd, size=(L, d))
+    out["log_g"] = _log_sigmoid(logits).astype(np.float32).astype(np.float64)
+    if with_dy:
+        out["dy"] = round_to(_rng(w.cfg_id, T_DY, b, h).standard_normal((L, d)), w.dtype)
+    return out
+
+
+def meta_keys(w: Workload, h: int) -> np.ndarray:
+    """Meta-memory sink keys of head h: [m, d] float64 (rounded)."""
+    return round_to(_rng(w.cfg_id, T_META, 0, h).standard_normal((w.n_meta, w.d)) * w.meta_sd, w.dtype)
+
+
+def full_inputs(w: Workload, L: Optional[int] = None, with_dy: bool = False,
+                heads: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+    """Whole [B, H, L, d] inputs (float64 values) plus meta keys [H, m, d]."""
+    if L is None:
+        L = w.L + w.steps
+    Hs = list(range(w.H)) if heads is None else list(heads)
+    names = ["q", "k", "v", "log_g"] + (["dy"] if with_dy else [])
+    arrs = {n: np.empty((w.B, len(Hs), L, w.d), dtype=np.float64) for n in names}
+    for b in range(w.B):
+        for j, h in enumerate(Hs):
+            s = slice_inputs(w, b, h, L=L, with_dy=with_dy)
+            for n in names:
+                arrs[n][b, j] = s[n]
+    arrs["meta_k"] = np.stack([meta_keys(w, h) for h in Hs]) if w.n_meta > 0 else np.zeros((len(Hs), 0, w.d))
+    return arrs
+
+
+def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Storage array for upload: float32 array, or uint16 bfloat16 bit patterns."""
+    if dtype == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "bf16":
+        return round_bf16_bits(x)
+    raise ValueError(dtype)
