@@ -1,0 +1,168 @@
+/*
+ * lizard_attn.h -- C ABI of the Lizard hybrid attention layer on MI355X (gfx950).
+ *
+ * The layer ("Lizard: An Efficient Linearization Framework for Large Language
+ * Models", explained on gist.science; German page section 2 "Methodik",
+ * "Kernkomponenten") replaces softmax attention with the sum
+ *
+ *     Y = Y_gate + alpha * Y_anchor                        (item 3 there)
+ *
+ * of a gated linear attention branch (item 1: a sigmoid gate drives a
+ * data-adaptive recurrence with a constant-size state) and an anchor branch
+ * (item 2: a sliding window of width w plus m learnable meta-memory tokens
+ * that act as attention sinks and contribute no value).  Readings taken
+ * where the pages are silent:
+ *
+ *   gate branch   S_t = diag(g_t) S_{t-1} + k_t v_t^T,  o_t = S_t^T q_t,
+ *                 S_{-1} = 0, g_t = exp(log_g_t) per token and key dim;
+ *   anchor        keys s in [max(0, t-w+1), t] plus m sink keys mu_i with
+ *                 logits scale*q_t.k_s and scale*q_t.mu_i in one softmax;
+ *                 sink values are zero; default scale 1/sqrt(dk);
+ *   no positional encoding in either branch; alpha is a constant.
+ *
+ * Three entry points follow from what the pages say the layer must do:
+ * replace attention in a pretrained model (a forward pass), be trained in
+ * two stages (de section 2 "Trainingsprozess": a backward pass), and run
+ * inference with constant memory through incremental state updates (de
+ * section 2 item 1 and section 4 "Effizienz": a decode step).
+ *
+ * Conventions for every call
+ *   - Tensor pointers are DEVICE pointers owned by the caller, 16-byte
+ *     aligned, contiguous, row-major in the shapes given.  Outputs never
+ *     alias inputs (decode's state and rings are the only in-out buffers).
+ *     Every output element the call defines is overwritten, never
+ *     accumulated.
+ *   - The library allocates no device memory.  The backward pass takes a
+ *     caller-owned workspace sized by lizard_attn_bwd_workspace_size().
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream) and never synchronise.  The library keeps no state between
+ *     calls, so calls on different streams may run concurrently.
+ *   - Argument checks run before any HIP call and return a status code
+ *     synchronously; nothing is launched when a check fails.  A failed
+ *     launch returns LIZARD_E_LAUNCH.  Faults inside kernels surface at the
+ *     caller's next synchronisation.  Inputs with NaN or Inf, or log_g > 0,
+ *     are outside the contract (results undefined, no fault).
+ */
+#ifndef LIZARD_ATTN_H
+#define LIZARD_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LIZARD_F32 = 0,  /* float32 storage, float32 MFMA                         */
+  LIZARD_BF16 = 1  /* bfloat16 storage, bf16 MFMA with float32 accumulate   */
+} lizard_dtype_t;
+
+typedef enum {
+  LIZARD_OK = 0,
+  LIZARD_E_NULL = -1,        /* a required pointer is NULL                   */
+  LIZARD_E_SHAPE = -2,       /* a size is negative or out of its range       */
+  LIZARD_E_DTYPE = -3,       /* unknown dtype                                */
+  LIZARD_E_ALIGN = -4,       /* a pointer is not 16-byte aligned             */
+  LIZARD_E_WORKSPACE = -5,   /* backward workspace smaller than required     */
+  LIZARD_E_UNSUPPORTED = -6, /* valid sizes this build has no kernel for     */
+  LIZARD_E_LAUNCH = -7       /* the HIP launch reported an error             */
+} lizard_status_t;
+
+/* Sizes and constants shared by all calls.
+ *   B, H      batch and heads (>= 0; a call with B*H == 0 or L == 0 is a no-op)
+ *   L         sequence length (>= 0, any value; ignored by decode)
+ *   dk, dv    head dims; this build requires dk == dv, and
+ *             dk in {64, 128} for LIZARD_BF16, dk == 64 for LIZARD_F32
+ *   chunk     chunk length of the chunked form; must be 64
+ *   window    w, 1 <= w <= 64 (keys [t-w+1, t])
+ *   n_meta    m, 0 <= m <= 16 sink keys per head
+ *   alpha     weight of the anchor branch
+ *   softmax_scale  logit scale; 0 means 1/sqrt(dk)
+ *   dtype     element type of q, k, v, meta_k, y, y_anchor, dy, dq, dk, dv,
+ *             and the decode rings.  log_g, lse, states, dlog_g and dmeta_k
+ *             are always float32.                                          */
+typedef struct {
+  int32_t B, H, L;
+  int32_t dk, dv;
+  int32_t chunk;
+  int32_t window;
+  int32_t n_meta;
+  float alpha;
+  float softmax_scale;
+  lizard_dtype_t dtype;
+} lizard_params_t;
+
+/* Forward pass (prefill / training), chunked log-space form.
+ *   q, k        [B, H, L, dk]   dtype
+ *   v           [B, H, L, dv]   dtype
+ *   log_g       [B, H, L, dk]   float32, finite, <= 0 (log of the sigmoid gate)
+ *   meta_k      [H, n_meta, dk] dtype (may be NULL when n_meta == 0)
+ *   y           [B, H, L, dv]   dtype, out
+ *   lse         [B, H, L]       float32, out, nullable: natural-log softmax
+ *                               normaliser of the anchor branch (needed by
+ *                               the backward pass)
+ *   y_anchor    [B, H, L, dv]   dtype, out, nullable: the anchor branch alone
+ *   state_out   [B, H, dk, dv]  float32, out, nullable: S_{L-1}, the state a
+ *                               decode continuation starts from             */
+lizard_status_t lizard_attn_fwd(const lizard_params_t* p,
+                                const void* q, const void* k, const void* v,
+                                const float* log_g, const void* meta_k,
+                                void* y, float* lse, void* y_anchor, float* state_out,
+                                void* stream);
+
+/* Bytes of device workspace lizard_attn_bwd needs for these sizes (0 if the
+ * sizes are invalid). */
+size_t lizard_attn_bwd_workspace_size(const lizard_params_t* p);
+
+/* Backward pass of loss = sum(dy * Y) (the layer is trained end to end; de
+ * section 2 "Trainingsprozess").
+ *   q, k, v, log_g, meta_k   as in lizard_attn_fwd
+ *   lse         [B, H, L]       float32, from lizard_attn_fwd with the same inputs
+ *   dy          [B, H, L, dv]   dtype
+ *   dq, dk      [B, H, L, dk]   dtype, out
+ *   dv          [B, H, L, dv]   dtype, out
+ *   dlog_g      [B, H, L, dk]   float32, out (gradient w.r.t. log_g)
+ *   dmeta_k     [H, n_meta, dk] float32, out (summed over the batch; may be
+ *                               NULL when n_meta == 0)
+ *   workspace   device buffer of at least lizard_attn_bwd_workspace_size(p)
+ *               bytes, caller-owned, contents need not be initialised       */
+lizard_status_t lizard_attn_bwd(const lizard_params_t* p,
+                                const void* q, const void* k, const void* v,
+                                const float* log_g, const void* meta_k,
+                                const float* lse, const void* dy,
+                                void* dq, void* dk, void* dv, float* dlog_g, float* dmeta_k,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* One constant-memory decode step for every (b, h) at absolute position pos
+ * (the same for all rows).  The incoming token is written to ring slot
+ * pos mod w, the state is updated, then the window max(0, pos-w+1)..pos and
+ * the sinks are read.
+ *   q_t, k_t    [B, H, dk]      dtype
+ *   v_t         [B, H, dv]      dtype
+ *   log_g_t     [B, H, dk]      float32
+ *   meta_k      [H, n_meta, dk] dtype (NULL allowed when n_meta == 0)
+ *   state       [B, H, dk, dv]  float32, in-out (S_{pos-1} in, S_pos out)
+ *   k_ring      [B, H, w, dk]   dtype, in-out; slot p mod w holds token p
+ *   v_ring      [B, H, w, dv]   dtype, in-out
+ *   y_t         [B, H, dv]      dtype, out
+ * After a prefill of L0 tokens: state = state_out, and slot p mod w holds
+ * k_p, v_p for p in [max(0, L0-w), L0); slots not yet written are never read. */
+lizard_status_t lizard_decode_step(const lizard_params_t* p, int64_t pos,
+                                   const void* q_t, const void* k_t, const void* v_t,
+                                   const float* log_g_t, const void* meta_k,
+                                   float* state, void* k_ring, void* v_ring,
+                                   void* y_t, void* stream);
+
+/* Static description of a status code. */
+const char* lizard_status_string(lizard_status_t s);
+
+/* ABI version of this header: 1. */
+int lizard_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIZARD_ATTN_H */

@@ -160,3 +160,70 @@ def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return round_bf16_bits(x)
     raise ValueError(dtype)
+
+
+def custom_inputs(seed: int, B: int, H: int, L: int, d: int, n_meta: int, dtype: str, *,
+                  qk_sd: float = 0.125, v_sd: float = 0.125, meta_sd: float = 0.125,
+                  gate_mu: float = 3.0, gate_sd: float = 1.0, hard_reset_frac: float = 0.0,
+                  with_dy: bool = False) -> Dict[str, np.ndarray]:
+    """Inputs for parity variants outside the fixed workloads (sharp logits,
+    slow or hard-reset gates, ragged lengths).  Hard resets set log_g = -1000
+    on a random fraction of tokens (all key dims of that token)."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(ROOT_SEED, spawn_key=(1000 + seed,))))
+    out = {
+        "q": round_to(rng.standard_normal((B, H, L, d)) * qk_sd, dtype),
+        "k": round_to(rng.standard_normal((B, H, L, d)) * qk_sd, dtype),
+        "v": round_to(rng.standard_normal((B, H, L, d)) * v_sd, dtype),
+    }
+    lg = _log_sigmoid(rng.normal(gate_mu, gate_sd, size=(B, H, L, d)))
+    if hard_reset_frac > 0:
+        hit = rng.random((B, H, L)) < hard_reset_frac
+        lg[hit] = -1000.0
+    out["log_g"] = lg.astype(np.float32).astype(np.float64)
+    out["meta_k"] = round_to(rng.standard_normal((H, n_meta, d)) * meta_sd, dtype)
+    if with_dy:
+        out["dy"] = round_to(rng.standard_normal((B, H, L, d)), dtype)
+    return out
+
+
+def _storage_row(args):
+    w, b, L, with_dy = args
+    rows = {}
+    for h in range(w.H):
+        s = slice_inputs(w, b, h, L=L, with_dy=with_dy)
+        for n, a in s.items():
+            st = np.ascontiguousarray(a, dtype=np.float32) if n == "log_g" else to_storage(a, w.dtype)
+            rows.setdefault(n, []).append(st)
+    return b, {n: np.stack(v) for n, v in rows.items()}
+
+
+def storage_inputs(w: Workload, L: Optional[int] = None, with_dy: bool = False,
+                   workers: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Whole [B, H, L, d] inputs in storage form (uint16 bfloat16 bits or
+    float32; log_g always float32), identical to the slices that
+    ``slice_inputs`` returns, generated in parallel over batch rows."""
+    import concurrent.futures
+    import multiprocessing as mp
+    import os
+
+    if L is None:
+        L = w.L + w.steps
+    names = ["q", "k", "v", "log_g"] + (["dy"] if with_dy else [])
+    sdt = np.uint16 if w.dtype == "bf16" else np.float32
+    out = {n: np.empty((w.B, w.H, L, w.d), dtype=np.float32 if n == "log_g" else sdt) for n in names}
+    if workers is None:
+        workers = min(16, os.cpu_count() or 1, w.B)
+    jobs = [(w, b, L, with_dy) for b in range(w.B)]
+    if workers <= 1:
+        results = map(_storage_row, jobs)
+        for b, rows in results:
+            for n in names:
+                out[n][b] = rows[n]
+    else:
+        with concurrent.futures.ProcessPoolExecutor(workers, mp_context=mp.get_context("fork")) as ex:
+            for b, rows in ex.map(_storage_row, jobs):
+                for n in names:
+                    out[n][b] = rows[n]
+    meta = np.stack([meta_keys(w, h) for h in range(w.H)]) if w.n_meta > 0 else np.zeros((w.H, 0, w.d))
+    out["meta_k"] = to_storage(meta, w.dtype)
+    return out

@@ -1,0 +1,200 @@
+"""Python binding of liblizard_attn.so, the Lizard hybrid attention library.
+
+Argument marshalling only: torch tensors provide device memory and the
+current HIP stream; every step of the layer runs in the library's HIP
+kernels.  There is no fallback: without the built library every call
+raises.  The names mirror the C ABI in include/lizard_attn.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Dict, Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblizard_attn.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "lizard_attn.h")
+
+LIZARD_F32, LIZARD_BF16 = 0, 1
+STATUS = {
+    0: "LIZARD_OK", -1: "LIZARD_E_NULL", -2: "LIZARD_E_SHAPE", -3: "LIZARD_E_DTYPE",
+    -4: "LIZARD_E_ALIGN", -5: "LIZARD_E_WORKSPACE", -6: "LIZARD_E_UNSUPPORTED", -7: "LIZARD_E_LAUNCH",
+}
+STATUS_CODE = {v: k for k, v in STATUS.items()}
+
+
+class LizardParams(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("L", ctypes.c_int32),
+        ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("chunk", ctypes.c_int32),
+        ("window", ctypes.c_int32), ("n_meta", ctypes.c_int32),
+        ("alpha", ctypes.c_float), ("softmax_scale", ctypes.c_float),
+        ("dtype", ctypes.c_int),
+    ]
+
+
+class LizardError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} returned {STATUS.get(status, status)}")
+
+
+_lib: Optional[ctypes.CDLL] = None
+_vp = ctypes.c_void_p
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m subquadratic_attention_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER(LizardParams)
+    lib.lizard_attn_fwd.argtypes = [P] + [_vp] * 10
+    lib.lizard_attn_fwd.restype = ctypes.c_int
+    lib.lizard_attn_bwd_workspace_size.argtypes = [P]
+    lib.lizard_attn_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.lizard_attn_bwd.argtypes = [P] + [_vp] * 13 + [ctypes.c_size_t, _vp]
+    lib.lizard_attn_bwd.restype = ctypes.c_int
+    lib.lizard_decode_step.argtypes = [P, ctypes.c_int64] + [_vp] * 10
+    lib.lizard_decode_step.restype = ctypes.c_int
+    lib.lizard_status_string.argtypes = [ctypes.c_int]
+    lib.lizard_status_string.restype = ctypes.c_char_p
+    lib.lizard_abi_version.argtypes = []
+    lib.lizard_abi_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def make_params(B, H, L, d, *, window, n_meta, alpha, dtype, chunk=64, softmax_scale=0.0) -> LizardParams:
+    return LizardParams(B, H, L, d, d, chunk, window, n_meta, float(alpha), float(softmax_scale), int(dtype))
+
+
+# ---------------------------------------------------------------------------
+# torch-level wrappers
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return LIZARD_BF16
+    if t.dtype == torch.float32:
+        return LIZARD_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device) -> int:
+    return _torch().cuda.current_stream(device).cuda_stream
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise LizardError(fn, status)
+
+
+def lizard_attn_fwd(q, k, v, log_g, meta_k, *, window: int, alpha: float, softmax_scale: float = 0.0,
+                    chunk: int = 64, need_lse: bool = False, need_y_anchor: bool = False,
+                    need_state: bool = False, out: Optional[Dict] = None) -> Dict:
+    """Forward pass.  q, k, v: [B, H, L, d]; log_g: [B, H, L, d] float32;
+    meta_k: [H, m, d].  Returns {"y", and optionally "lse", "y_anchor",
+    "state"}; pass ``out`` (same keys) to reuse preallocated outputs."""
+    torch = _torch()
+    lib = load_library()
+    B, H, L, d = q.shape
+    m = meta_k.shape[1] if meta_k is not None else 0
+    dt = _dtype_code(q)
+    p = make_params(B, H, L, d, window=window, n_meta=m, alpha=alpha, dtype=dt, chunk=chunk,
+                    softmax_scale=softmax_scale)
+    o = dict(out) if out is not None else {}
+    if "y" not in o:
+        o["y"] = torch.empty_like(q)
+    if need_lse and "lse" not in o:
+        o["lse"] = torch.empty((B, H, L), device=q.device, dtype=torch.float32)
+    if need_y_anchor and "y_anchor" not in o:
+        o["y_anchor"] = torch.empty_like(q)
+    if need_state and "state" not in o:
+        o["state"] = torch.empty((B, H, d, d), device=q.device, dtype=torch.float32)
+    st = lib.lizard_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(meta_k),
+                             _ptr(o["y"]), _ptr(o.get("lse")), _ptr(o.get("y_anchor")), _ptr(o.get("state")),
+                             _stream(q.device))
+    _check("lizard_attn_fwd", st)
+    return o
+
+
+def lizard_attn_bwd_workspace_size(B, H, L, d, *, window: int, n_meta: int, dtype: int, chunk: int = 64) -> int:
+    lib = load_library()
+    p = make_params(B, H, L, d, window=window, n_meta=n_meta, alpha=0.0, dtype=dtype, chunk=chunk)
+    return int(lib.lizard_attn_bwd_workspace_size(ctypes.byref(p)))
+
+
+def lizard_attn_bwd(q, k, v, log_g, meta_k, lse, dy, *, window: int, alpha: float, softmax_scale: float = 0.0,
+                    chunk: int = 64, workspace=None, out: Optional[Dict] = None) -> Dict:
+    """Backward pass of sum(dy * Y).  Returns {"dq", "dk", "dv", "dlog_g",
+    "dmeta"} (dmeta summed over the batch)."""
+    torch = _torch()
+    lib = load_library()
+    B, H, L, d = q.shape
+    m = meta_k.shape[1] if meta_k is not None else 0
+    dt = _dtype_code(q)
+    p = make_params(B, H, L, d, window=window, n_meta=m, alpha=alpha, dtype=dt, chunk=chunk,
+                    softmax_scale=softmax_scale)
+    ws_bytes = int(lib.lizard_attn_bwd_workspace_size(ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), device=q.device, dtype=torch.uint8)
+    o = dict(out) if out is not None else {}
+    for key, like in (("dq", q), ("dk", k), ("dv", v)):
+        if key not in o:
+            o[key] = torch.empty_like(like)
+    if "dlog_g" not in o:
+        o["dlog_g"] = torch.empty_like(log_g)
+    if "dmeta" not in o:
+        o["dmeta"] = torch.empty((H, m, d), device=q.device, dtype=torch.float32) if m > 0 else None
+    st = lib.lizard_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(meta_k), _ptr(lse),
+                             _ptr(dy), _ptr(o["dq"]), _ptr(o["dk"]), _ptr(o["dv"]), _ptr(o["dlog_g"]),
+                             _ptr(o["dmeta"]), _ptr(workspace), workspace.numel(), _stream(q.device))
+    _check("lizard_attn_bwd", st)
+    return o
+
+
+def lizard_decode_step(pos: int, q_t, k_t, v_t, log_g_t, meta_k, state, k_ring, v_ring, *, alpha: float,
+                       softmax_scale: float = 0.0, y_t=None):
+    """One decode step at absolute position ``pos`` (same for every row).
+    q_t, k_t, v_t: [B, H, d]; log_g_t: [B, H, d] float32; state:
+    [B, H, d, d] float32 (in-out); rings: [B, H, w, d] (in-out).  Returns y_t."""
+    torch = _torch()
+    lib = load_library()
+    B, H, d = q_t.shape
+    w = k_ring.shape[2]
+    m = meta_k.shape[1] if meta_k is not None else 0
+    p = make_params(B, H, 0, d, window=w, n_meta=m, alpha=alpha, dtype=_dtype_code(q_t),
+                    softmax_scale=softmax_scale)
+    if y_t is None:
+        y_t = torch.empty_like(q_t)
+    st = lib.lizard_decode_step(ctypes.byref(p), int(pos), _ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(log_g_t),
+                                _ptr(meta_k), _ptr(state), _ptr(k_ring), _ptr(v_ring), _ptr(y_t),
+                                _stream(q_t.device))
+    _check("lizard_decode_step", st)
+    return y_t
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)

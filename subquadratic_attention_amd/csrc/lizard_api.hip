@@ -1,0 +1,176 @@
+// C ABI of the Lizard hybrid attention library: argument checks, sizing and
+// dispatch.  Every check runs before the first HIP call, so invalid calls
+// return their status without touching the device.
+#include <math.h>
+#include <stdint.h>
+
+#include "lizard_attn.h"
+#include "lizard_kernels.hpp"
+
+#define LIZARD_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int64_t kMaxBH = 1 << 24;
+constexpr int64_t kMaxL = 1 << 26;
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+// Sizes common to every call.  need_seq: the call walks a sequence of L tokens.
+lizard_status_t check_params(const lizard_params_t* p, bool need_seq) {
+  if (p == nullptr) return LIZARD_E_NULL;
+  if (p->dtype != LIZARD_F32 && p->dtype != LIZARD_BF16) return LIZARD_E_DTYPE;
+  if (p->B < 0 || p->H < 0 || p->dk <= 0 || p->dv <= 0 || p->window < 1 || p->n_meta < 0 || p->chunk < 1)
+    return LIZARD_E_SHAPE;
+  if (need_seq && (p->L < 0 || p->L > kMaxL)) return LIZARD_E_SHAPE;
+  if ((int64_t)p->B * p->H > kMaxBH) return LIZARD_E_SHAPE;
+  if (!isfinite(p->alpha) || !isfinite(p->softmax_scale) || p->softmax_scale < 0.f) return LIZARD_E_SHAPE;
+  if (p->dk != p->dv) return LIZARD_E_UNSUPPORTED;
+  if (p->dtype == LIZARD_BF16 && p->dk != 64 && p->dk != 128) return LIZARD_E_UNSUPPORTED;
+  if (p->dtype == LIZARD_F32 && p->dk != 64) return LIZARD_E_UNSUPPORTED;
+  if (p->chunk != 64 || p->window > 64 || p->n_meta > 16) return LIZARD_E_UNSUPPORTED;
+  return LIZARD_OK;
+}
+
+float scale_of(const lizard_params_t* p) {
+  return p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / sqrtf((float)p->dk);
+}
+
+lizard_status_t launched(hipError_t e) { return e == hipSuccess ? LIZARD_OK : LIZARD_E_LAUNCH; }
+
+}  // namespace
+
+LIZARD_API lizard_status_t lizard_attn_fwd(const lizard_params_t* p, const void* q, const void* k, const void* v,
+                                           const float* log_g, const void* meta_k, void* y, float* lse,
+                                           void* y_anchor, float* state_out, void* stream) {
+  lizard_status_t s = check_params(p, true);
+  if (s != LIZARD_OK) return s;
+  const int BH = p->B * p->H;
+  if (BH == 0) return LIZARD_OK;  // nothing to read or write; empty tensors may have NULL data
+  const bool seq = p->L > 0;
+  if ((seq && (!q || !k || !v || !log_g || !y)) || (p->n_meta > 0 && !meta_k)) return LIZARD_E_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(log_g) || misaligned(y) ||
+      misaligned(meta_k) || misaligned(lse) || misaligned(y_anchor) || misaligned(state_out))
+    return LIZARD_E_ALIGN;
+  if (!seq && state_out == nullptr) return LIZARD_OK;
+  const int bf = p->dtype == LIZARD_BF16;
+  const int DV = lizard::fwd_value_slice(bf, p->dk);
+  lizard::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.log_g = log_g;
+  a.meta = meta_k;
+  a.y = y;
+  a.lse = lse;
+  a.y_anchor = y_anchor;
+  a.state_out = state_out;
+  a.BH = BH;
+  a.H = p->H;
+  a.L = p->L;
+  a.n_meta = p->n_meta;
+  a.window = p->window;
+  a.nsplit = p->dv / DV;
+  a.alpha = p->alpha;
+  a.scale_log2 = scale_of(p) * 1.4426950408889634f;
+  return launched(lizard::launch_fwd(a, bf, p->dk, static_cast<hipStream_t>(stream)));
+}
+
+LIZARD_API size_t lizard_attn_bwd_workspace_size(const lizard_params_t* p) {
+  if (check_params(p, true) != LIZARD_OK) return 0;
+  return lizard::bwd_workspace_bytes(p->dtype == LIZARD_BF16, p->B * p->H, p->L, p->dk, p->n_meta);
+}
+
+LIZARD_API lizard_status_t lizard_attn_bwd(const lizard_params_t* p, const void* q, const void* k, const void* v,
+                                           const float* log_g, const void* meta_k, const float* lse,
+                                           const void* dy, void* dq, void* dk, void* dv, float* dlog_g,
+                                           float* dmeta_k, void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+  lizard_status_t s = check_params(p, true);
+  if (s != LIZARD_OK) return s;
+  if (!q || !k || !v || !log_g || !lse || !dy || !dq || !dk || !dv || !dlog_g ||
+      (p->n_meta > 0 && (!meta_k || !dmeta_k)))
+    return LIZARD_E_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(log_g) || misaligned(meta_k) ||
+      misaligned(lse) || misaligned(dy) || misaligned(dq) || misaligned(dk) || misaligned(dv) ||
+      misaligned(dlog_g) || misaligned(dmeta_k) || misaligned(workspace))
+    return LIZARD_E_ALIGN;
+  const size_t need = lizard::bwd_workspace_bytes(p->dtype == LIZARD_BF16, p->B * p->H, p->L, p->dk, p->n_meta);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LIZARD_E_WORKSPACE;
+  const int BH = p->B * p->H;
+  if (BH == 0 && p->H * p->n_meta == 0) return LIZARD_OK;
+  lizard::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.log_g = log_g;
+  a.meta = meta_k;
+  a.lse = lse;
+  a.dy = dy;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dlog_g = dlog_g;
+  a.dmeta = dmeta_k;
+  a.B = p->B;
+  a.BH = BH;
+  a.H = p->H;
+  a.L = p->L;
+  a.n_meta = p->n_meta;
+  a.window = p->window;
+  a.alpha = p->alpha;
+  a.scale = scale_of(p);
+  a.states = workspace;
+  a.dmeta_part = nullptr;
+  return launched(lizard::launch_bwd(a, p->dtype == LIZARD_BF16, p->dk, static_cast<hipStream_t>(stream)));
+}
+
+LIZARD_API lizard_status_t lizard_decode_step(const lizard_params_t* p, int64_t pos, const void* q_t,
+                                              const void* k_t, const void* v_t, const float* log_g_t,
+                                              const void* meta_k, float* state, void* k_ring, void* v_ring,
+                                              void* y_t, void* stream) {
+  lizard_status_t s = check_params(p, false);
+  if (s != LIZARD_OK) return s;
+  if (pos < 0) return LIZARD_E_SHAPE;
+  const int BH = p->B * p->H;
+  if (BH == 0) return LIZARD_OK;
+  if (!q_t || !k_t || !v_t || !log_g_t || !state || !k_ring || !v_ring || !y_t || (p->n_meta > 0 && !meta_k))
+    return LIZARD_E_NULL;
+  if (misaligned(q_t) || misaligned(k_t) || misaligned(v_t) || misaligned(log_g_t) || misaligned(meta_k) ||
+      misaligned(state) || misaligned(k_ring) || misaligned(v_ring) || misaligned(y_t))
+    return LIZARD_E_ALIGN;
+  lizard::DecodeArgs a;
+  a.q = q_t;
+  a.k = k_t;
+  a.v = v_t;
+  a.log_g = log_g_t;
+  a.meta = meta_k;
+  a.state = state;
+  a.k_ring = k_ring;
+  a.v_ring = v_ring;
+  a.y = y_t;
+  a.pos = pos;
+  a.BH = BH;
+  a.H = p->H;
+  a.n_meta = p->n_meta;
+  a.window = p->window;
+  a.alpha = p->alpha;
+  a.scale_log2 = scale_of(p) * 1.4426950408889634f;
+  return launched(lizard::launch_decode(a, p->dtype == LIZARD_BF16, p->dk, static_cast<hipStream_t>(stream)));
+}
+
+LIZARD_API const char* lizard_status_string(lizard_status_t s) {
+  switch (s) {
+    case LIZARD_OK: return "ok";
+    case LIZARD_E_NULL: return "a required pointer is NULL";
+    case LIZARD_E_SHAPE: return "a size or constant is out of range";
+    case LIZARD_E_DTYPE: return "unknown dtype";
+    case LIZARD_E_ALIGN: return "a pointer is not 16-byte aligned";
+    case LIZARD_E_WORKSPACE: return "backward workspace too small";
+    case LIZARD_E_UNSUPPORTED: return "no kernel for these sizes in this build";
+    case LIZARD_E_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+LIZARD_API int lizard_abi_version(void) { return 1; }

@@ -1,0 +1,126 @@
+// Device helpers shared by the Lizard attention kernels (gfx950 only).
+//
+// MFMA operand convention used everywhere in this library.  A 16x16 output
+// tile C[m][n] = sum_k A[m][k] * B[n][k] is computed by one wavefront (64
+// lanes).  Lane l works on row m = l % 16 of A and row n = l % 16 of B, and
+// lane group g = l / 16 owns the contiguous quarter [g*K/4, (g+1)*K/4) of the
+// contraction index k.  Because the contraction is a sum, any assignment of
+// k to (lane group, step) works as long as A and B use the same one; this
+// one keeps every lane's operand data contiguous (vector loads).  The output
+// lands as C[4*g + r][l % 16] in accumulator register r (r = 0..3), which is
+// the gfx950 layout of v_mfma_f32_16x16x32_bf16 and v_mfma_f32_16x16x4_f32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lizard {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return static_cast<float>(x); }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+// float -> bf16 conversion rounds to nearest even (gfx950 v_cvt_pk_bf16_f32).
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }
+
+// exp of a natural-log exponent via the hardware base-2 exponential.
+__device__ __forceinline__ float exp_e(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+__device__ __forceinline__ float exp_2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Per element type: elements per lane per MFMA step (KPL), the contraction
+// length one MFMA covers (KSTEP = 4 * KPL), the fragment type and the op.
+template <typename T> struct Mfma;
+
+template <> struct Mfma<bf16> {
+  static constexpr int KPL = 8;
+  static constexpr int KSTEP = 32;
+  typedef bf16x8 frag;
+  static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ frag load(const bf16* p) { return *reinterpret_cast<const frag*>(p); }
+  static __device__ __forceinline__ frag zero() {
+    frag z;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z[i] = static_cast<bf16>(0.0f);
+    return z;
+  }
+  // Build a fragment from 8 float values (one rounding each).
+  static __device__ __forceinline__ frag pack(const float* x) {
+    frag f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = static_cast<bf16>(x[i]);
+    return f;
+  }
+};
+
+template <> struct Mfma<float> {
+  static constexpr int KPL = 1;
+  static constexpr int KSTEP = 4;
+  typedef float frag;
+  static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ frag load(const float* p) { return *p; }
+  static __device__ __forceinline__ frag zero() { return 0.0f; }
+  static __device__ __forceinline__ frag pack(const float* x) { return x[0]; }
+};
+
+// C += A * B^T over a contraction of length K, with A's row m and B's row n
+// each given as a pointer to the start of that lane's k-quarter.
+template <typename T, int K>
+__device__ __forceinline__ f32x4 mma_rows(f32x4 c, const T* a_q, const T* b_q) {
+  typedef Mfma<T> M;
+  constexpr int STEPS = K / M::KSTEP;
+#pragma unroll
+  for (int e = 0; e < STEPS; ++e) c = M::mma(M::load(a_q + e * M::KPL), M::load(b_q + e * M::KPL), c);
+  return c;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Max / sum across the 16 lanes of a lane group (lanes with equal l / 16).
+__device__ __forceinline__ float group16_max(float x) {
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ float group16_sum(float x) {
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+// Order LDS traffic of one wavefront: writes before the fence are visible
+// to reads after it from any lane of the same wavefront.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// 16-byte global load / store of raw bits.
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+}  // namespace lizard

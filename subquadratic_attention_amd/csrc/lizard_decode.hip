@@ -1,0 +1,180 @@
+// Recurrent decode step of the Lizard hybrid attention layer on gfx950.
+//
+// Constant-memory inference by incremental state updates ("Lizard"
+// explainer, gist.science (de), section 2 "Kernkomponenten" item 1, and
+// section 4 "Effizienz": memory stays constant with context length).  One
+// token per (batch, head) at absolute position pos:
+//
+//   S <- diag(e^{log_g}) S + k v^T      (float32, in place)
+//   o  = S^T q
+//   ring slot pos mod w <- (k, v)
+//   y_anchor = softmax over the window max(0, pos-w+1)..pos and the m sink
+//              keys (zero values), applied to the window values
+//   y  = o + alpha * y_anchor
+//
+// The step is bound by HBM bandwidth: the 64 KiB float32 state of a d=128
+// head is read and written once, the window's keys and values are read
+// once.  One workgroup of 256 threads per (b, h); each thread streams whole
+// 16-byte runs of state rows so every wavefront touches contiguous 1 KiB.
+#include "lizard_common.hpp"
+#include "lizard_kernels.hpp"
+
+namespace lizard {
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void lizard_decode_kernel(DecodeArgs a) {
+  constexpr int CG = D / 4;            // float4 column groups per row
+  constexpr int RG = 256 / CG;         // row groups
+  constexpr int RPT = D / RG;          // rows per thread
+  constexpr int CPT = D / 64;          // value columns per thread in the window product
+  __shared__ float sq[D], sk[D], sv[D], sg[D];
+  __shared__ float sO[RG][D];
+  __shared__ float sZ[80];
+  __shared__ float sYa[4][D];
+  __shared__ float sDen;
+
+  const int bh = blockIdx.x;
+  const int h = bh % a.H;
+  const int tid = threadIdx.x;
+  const int w = a.window;
+  const long long pos = a.pos;
+  const int cur = (int)(pos % w);
+
+  const T* qg = reinterpret_cast<const T*>(a.q) + (size_t)bh * D;
+  const T* kg = reinterpret_cast<const T*>(a.k) + (size_t)bh * D;
+  const T* vg = reinterpret_cast<const T*>(a.v) + (size_t)bh * D;
+  T* kr = reinterpret_cast<T*>(a.k_ring) + (size_t)bh * w * D;
+  T* vr = reinterpret_cast<T*>(a.v_ring) + (size_t)bh * w * D;
+  float* S = a.state + (size_t)bh * D * D;
+
+  if (tid < D) {
+    sq[tid] = to_f32(qg[tid]);
+    sk[tid] = to_f32(kg[tid]);
+    sv[tid] = to_f32(vg[tid]);
+    sg[tid] = exp_e(a.log_g[(size_t)bh * D + tid]);
+  }
+  __syncthreads();
+
+  // ---- state update and readout partials ----
+  const int cg = tid % CG;
+  const int rg = tid / CG;
+  {
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 vv = make_float4(sv[4 * cg], sv[4 * cg + 1], sv[4 * cg + 2], sv[4 * cg + 3]);
+    float4 s[RPT];
+#pragma unroll
+    for (int ii = 0; ii < RPT; ++ii) s[ii] = *reinterpret_cast<const float4*>(S + (size_t)(ii * RG + rg) * D + 4 * cg);
+#pragma unroll
+    for (int ii = 0; ii < RPT; ++ii) {
+      const int i = ii * RG + rg;
+      const float gi = sg[i], ki = sk[i], qi = sq[i];
+      float4 n;
+      n.x = gi * s[ii].x + ki * vv.x;
+      n.y = gi * s[ii].y + ki * vv.y;
+      n.z = gi * s[ii].z + ki * vv.z;
+      n.w = gi * s[ii].w + ki * vv.w;
+      *reinterpret_cast<float4*>(S + (size_t)i * D + 4 * cg) = n;
+      o.x += qi * n.x;
+      o.y += qi * n.y;
+      o.z += qi * n.z;
+      o.w += qi * n.w;
+    }
+    *reinterpret_cast<float4*>(&sO[rg][4 * cg]) = o;
+  }
+
+  // ---- window and sink logits: entry e < 64 is ring slot e, 64 + i is sink i ----
+  {
+    const int part = tid & 3;         // quarter of the dims
+    for (int e = tid >> 2; e < 80; e += 64) {
+      float zv = -INFINITY;
+      bool live;
+      const T* kp;
+      if (e < 64) {
+        const int slot = e;
+        const long long p = pos - (long long)(((pos - slot) % w + w) % w);
+        live = slot < w && p >= 0;
+        kp = kr + (size_t)slot * D;
+      } else {
+        live = (e - 64) < a.n_meta;
+        kp = reinterpret_cast<const T*>(a.meta) + ((size_t)h * a.n_meta + (e - 64)) * D;
+      }
+      if (live) {
+        float dot = 0.f;
+        if (e == cur) {
+#pragma unroll 8
+          for (int i = part * (D / 4); i < (part + 1) * (D / 4); ++i) dot += sq[i] * sk[i];
+        } else {
+#pragma unroll 8
+          for (int i = part * (D / 4); i < (part + 1) * (D / 4); ++i) dot += sq[i] * to_f32(kp[i]);
+        }
+        zv = dot;
+      }
+      zv += __shfl_xor(zv, 1, 64);
+      zv += __shfl_xor(zv, 2, 64);
+      if (part == 0) sZ[e] = live ? zv * a.scale_log2 : -INFINITY;
+    }
+  }
+  __syncthreads();
+
+  // the incoming token goes to its ring slot (that slot is never read from the ring above)
+  if (tid < D) {
+    kr[(size_t)cur * D + tid] = kg[tid];
+    vr[(size_t)cur * D + tid] = vg[tid];
+  }
+
+  // ---- softmax over window + sinks (wavefront 0) ----
+  if (tid < 64) {
+    const float z0 = sZ[tid];
+    const float z1 = tid < 16 ? sZ[64 + tid] : -INFINITY;
+    const float mx = wave_max(fmaxf(z0, z1));
+    const float p0 = exp_2(z0 - mx);
+    const float p1 = exp_2(z1 - mx);
+    const float den = wave_sum(p0 + p1);
+    sZ[tid] = p0;
+    if (tid == 0) sDen = den;
+  }
+  __syncthreads();
+
+  // ---- window values: thread (column set, slot quarter) ----
+  {
+    const int cs = tid & 63;
+    const int sq4 = tid >> 6;
+    float ya[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) ya[c] = 0.f;
+    for (int slot = sq4 * 16; slot < sq4 * 16 + 16 && slot < w; ++slot) {
+      const float p = sZ[slot];
+      if (p != 0.f) {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+          const int j = cs * CPT + c;
+          const float vj = slot == cur ? sv[j] : to_f32(vr[(size_t)slot * D + j]);
+          ya[c] += p * vj;
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) sYa[sq4][cs * CPT + c] = ya[c];
+  }
+  __syncthreads();
+
+  if (tid < D) {
+    float o = 0.f;
+#pragma unroll
+    for (int r = 0; r < RG; ++r) o += sO[r][tid];
+    const float ya = (sYa[0][tid] + sYa[1][tid] + sYa[2][tid] + sYa[3][tid]) / sDen;
+    reinterpret_cast<T*>(a.y)[(size_t)bh * D + tid] = from_f32<T>(o + a.alpha * ya);
+  }
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int dtype_bf16, int D, hipStream_t st) {
+  dim3 grid(a.BH);
+  if (dtype_bf16 && D == 128) hipLaunchKernelGGL((lizard_decode_kernel<bf16, 128>), grid, dim3(256), 0, st, a);
+  else if (dtype_bf16 && D == 64) hipLaunchKernelGGL((lizard_decode_kernel<bf16, 64>), grid, dim3(256), 0, st, a);
+  else if (!dtype_bf16 && D == 64) hipLaunchKernelGGL((lizard_decode_kernel<float, 64>), grid, dim3(256), 0, st, a);
+  else if (!dtype_bf16 && D == 128) hipLaunchKernelGGL((lizard_decode_kernel<float, 128>), grid, dim3(256), 0, st, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace lizard

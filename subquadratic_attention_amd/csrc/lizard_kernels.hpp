@@ -1,0 +1,68 @@
+// Internal interface between the C-ABI host code and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lizard {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* log_g;
+  const void* meta;     // [H, n_meta, D]
+  void* y;
+  float* lse;           // nullable
+  void* y_anchor;       // nullable
+  float* state_out;     // nullable
+  int BH, H, L, n_meta, window, nsplit;
+  float alpha;
+  float scale_log2;     // softmax scale * log2(e)
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* log_g;
+  const void* meta;
+  float* state;
+  void* k_ring;
+  void* v_ring;
+  void* y;
+  long long pos;
+  int BH, H, n_meta, window;
+  float alpha;
+  float scale_log2;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* log_g;
+  const void* meta;
+  const float* lse;
+  const void* dy;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dlog_g;
+  float* dmeta;          // [H, n_meta, D]
+  void* states;          // workspace: chunk-start states [BH, nc, D, D] (element type)
+  float* dmeta_part;     // workspace: per-(b,h) sink-key gradients [BH, n_meta, D]
+  int B, BH, H, L, n_meta, window;
+  float alpha;
+  float scale;           // softmax scale (natural units)
+};
+
+// Value-column slice width the forward kernel uses (0 = unsupported).
+int fwd_value_slice(int dtype_bf16, int D);
+hipError_t launch_fwd(const FwdArgs& a, int dtype_bf16, int D, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs& a, int dtype_bf16, int D, hipStream_t st);
+size_t bwd_workspace_bytes(int dtype_bf16, int BH, int L, int D, int n_meta);
+hipError_t launch_bwd(const BwdArgs& a, int dtype_bf16, int D, hipStream_t st);
+
+}  // namespace lizard

@@ -1,0 +1,163 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function the header declares, the parameter struct has the same
+layout in C and in the binding, and every argument error returns its status
+before any HIP call (fake device pointers are never dereferenced)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import subquadratic_attention_amd as sqa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sqa.LIB_PATH):
+        from subquadratic_attention_amd import build
+
+        build.build()
+    return sqa.load_library()
+
+
+def header_functions():
+    src = open(sqa.HEADER_PATH).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lizard_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = header_functions()
+    for want in ("lizard_attn_fwd", "lizard_attn_bwd", "lizard_attn_bwd_workspace_size", "lizard_decode_step",
+                 "lizard_status_string", "lizard_abi_version"):
+        assert want in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", sqa.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = set(re.findall(r"\b[TW] (\w+)$", out.stdout, flags=re.M))
+    for name in header_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+    # nothing else leaks out under the library's prefix
+    assert {n for n in exported if n.startswith("lizard_")} == set(header_functions())
+
+
+def test_param_struct_layout_matches_c(tmp_path):
+    prog = tmp_path / "layout.c"
+    prog.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "lizard_attn.h"\n'
+        "int main(void){printf(\"%zu %zu %zu %zu %zu\\n\", sizeof(lizard_params_t), offsetof(lizard_params_t, n_meta),"
+        " offsetof(lizard_params_t, alpha), offsetof(lizard_params_t, softmax_scale), offsetof(lizard_params_t, dtype));"
+        "return 0;}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(prog), "-o", str(exe)], check=True)
+    c_vals = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    P = sqa.LizardParams
+    py_vals = [ctypes.sizeof(P), P.n_meta.offset, P.alpha.offset, P.softmax_scale.offset, P.dtype.offset]
+    assert c_vals == py_vals
+
+
+def test_version_and_strings(lib):
+    assert lib.lizard_abi_version() == 1
+    for code, name in sqa.STATUS.items():
+        s = lib.lizard_status_string(code)
+        assert isinstance(s, bytes) and len(s) > 0
+    assert lib.lizard_status_string(123) == b"unknown status"
+
+
+FAKE = 0x10000  # aligned, never dereferenced
+MIS = 0x10008   # 8-byte aligned only
+
+
+def params(**kw):
+    base = dict(B=2, H=3, L=128, d=128, window=64, n_meta=4, alpha=0.5, dtype=sqa.LIZARD_BF16)
+    base.update(kw)
+    d = base.pop("d")
+    return sqa.make_params(base.pop("B"), base.pop("H"), base.pop("L"), d, **base)
+
+
+def fwd(lib, p, q=FAKE, meta=FAKE, lse=None):
+    return lib.lizard_attn_fwd(ctypes.byref(p), q, FAKE, FAKE, FAKE, meta, FAKE, lse, None, None, None)
+
+
+def bwd(lib, p, ws=FAKE, ws_bytes=1 << 40, dy=FAKE):
+    return lib.lizard_attn_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dy, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               ws, ws_bytes, None)
+
+
+def dec(lib, p, pos=5, state=FAKE):
+    return lib.lizard_decode_step(ctypes.byref(p), pos, FAKE, FAKE, FAKE, FAKE, FAKE, state, FAKE, FAKE, FAKE, None)
+
+
+S = sqa.STATUS_CODE
+
+
+def test_null_params(lib):
+    assert lib.lizard_attn_fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, None) == S["LIZARD_E_NULL"]
+    assert lib.lizard_attn_bwd_workspace_size(None) == 0
+
+
+@pytest.mark.parametrize("call", ["fwd", "bwd", "dec"])
+def test_argument_errors(lib, call):
+    f = {"fwd": fwd, "bwd": bwd, "dec": dec}[call]
+    assert f(lib, params(dtype=7)) == S["LIZARD_E_DTYPE"]
+    assert f(lib, params(B=-1)) == S["LIZARD_E_SHAPE"]
+    assert f(lib, params(window=0)) == S["LIZARD_E_SHAPE"]
+    assert f(lib, params(n_meta=-2)) == S["LIZARD_E_SHAPE"]
+    assert f(lib, params(alpha=float("nan"))) == S["LIZARD_E_SHAPE"]
+    assert f(lib, params(softmax_scale=-1.0)) == S["LIZARD_E_SHAPE"]
+    assert f(lib, params(d=96)) == S["LIZARD_E_UNSUPPORTED"]
+    assert f(lib, params(d=128, dtype=sqa.LIZARD_F32)) == S["LIZARD_E_UNSUPPORTED"]
+    assert f(lib, params(window=65)) == S["LIZARD_E_UNSUPPORTED"]
+    assert f(lib, params(n_meta=17)) == S["LIZARD_E_UNSUPPORTED"]
+    assert f(lib, params(chunk=32)) == S["LIZARD_E_UNSUPPORTED"]
+    p = params()
+    p.dv = 64
+    assert f(lib, p) == S["LIZARD_E_UNSUPPORTED"]
+
+
+def test_fwd_pointer_errors(lib):
+    assert fwd(lib, params(), q=None) == S["LIZARD_E_NULL"]
+    assert fwd(lib, params(n_meta=4), meta=None) == S["LIZARD_E_NULL"]
+    assert fwd(lib, params(), q=MIS) == S["LIZARD_E_ALIGN"]
+    assert fwd(lib, params(), lse=MIS) == S["LIZARD_E_ALIGN"]
+    assert fwd(lib, params(L=-5)) == S["LIZARD_E_SHAPE"]
+
+
+def test_bwd_workspace_checks(lib):
+    p = params()
+    need = lib.lizard_attn_bwd_workspace_size(ctypes.byref(p))
+    if need > 0:
+        assert bwd(lib, p, ws_bytes=need - 1) == S["LIZARD_E_WORKSPACE"]
+        assert bwd(lib, p, ws=None) == S["LIZARD_E_WORKSPACE"]
+    assert bwd(lib, p, dy=None) == S["LIZARD_E_NULL"]
+    assert bwd(lib, p, ws=MIS) == S["LIZARD_E_ALIGN"]
+
+
+def test_decode_errors(lib):
+    assert dec(lib, params(), pos=-1) == S["LIZARD_E_SHAPE"]
+    assert dec(lib, params(), state=None) == S["LIZARD_E_NULL"]
+    assert dec(lib, params(), state=MIS) == S["LIZARD_E_ALIGN"]
+
+
+def test_empty_calls_do_nothing(lib):
+    # B*H == 0: valid, nothing to launch, the fake pointers are never touched
+    assert fwd(lib, params(B=0)) == 0
+    assert dec(lib, params(H=0)) == 0
+
+
+def test_binding_refuses_without_library(tmp_path):
+    import importlib
+
+    mod = importlib.reload(sqa)
+    saved = mod._lib
+    mod._lib = None
+    try:
+        with pytest.raises(ImportError):
+            mod.load_library(str(tmp_path / "missing.so"))
+    finally:
+        mod._lib = saved
