@@ -1,0 +1,367 @@
+"""Benchmark of the Lizard hybrid attention layer on one MI355X.
+
+One step = one forward pass (the chunked gated branch, window + sink
+softmax and hybrid sum, all in one kernel launch) of the Llama-3-8B-shaped
+prefill layer: B=4, H=32, L=4096, d=128, chunk 64, w=64, m=4, alpha=0.5,
+bf16 operands with fp32 accumulation, inference mode (no lse / y_anchor /
+state outputs).  Inputs are seeded synthetic tensors resident in HBM.
+
+Prints one JSON line: tokens/s (B*L per second), the forward kernel's
+position on the HBM roofline (algorithmic bytes / average launch time) and
+its MFMA fraction, the float64 CPU oracle timed on a bounded sample of the
+same workload, and secondary objects for the decode step (batch 64, H=32,
+1024 steps after a 2048-token prefill: HBM GB/s) and the backward pass
+(B=8, H=32, L=2048).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "hybrid-attn fwd tokens/s + %MFMA peak (L=4k,H=32,d=128); decode GB/s % peak"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["subquadratic_attention_amd/csrc/lizard_fwd.hip", "subquadratic_attention_amd/csrc/lizard_common.hpp",
+                  "subquadratic_attention_amd/csrc/lizard_decode.hip", "subquadratic_attention_amd/csrc/lizard_bwd.hip"]
+
+
+def source_hash(path: str) -> str:
+    with open(os.path.join(ROOT, path), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work (per head-token / per (b, h) decode step)
+# ---------------------------------------------------------------------------
+
+def fwd_bytes_per_head_token(d: int, elem: int = 2) -> int:
+    # q, k, v and y in the element type, log_g in float32
+    return 3 * elem * d + 4 * d + elem * d
+
+
+def fwd_flops_per_head_token(d: int, C: int = 64, w: int = 64, m: int = 4) -> int:
+    # readout + carry 4 d^2, intra causal pairs (C+1)(dk+dv), window+sink logits 2(w+m)d, window values 2wd
+    return 4 * d * d + (C + 1) * 2 * d + 2 * (w + m) * d + 2 * w * d
+
+
+def bwd_bytes_per_head_token(d: int, elem: int = 2) -> int:
+    # reads q, k, v, dy (elem), log_g (f32), lse (f32); writes dq, dk, dv (elem), dlog_g (f32)
+    return 4 * elem * d + 4 * d + 4 + 3 * elem * d + 4 * d
+
+
+def bwd_flops_per_head_token(d: int, C: int = 64, w: int = 64, m: int = 4) -> int:
+    return 10 * d * d + 5 * (C + 1) * d + 6 * (w + m) * d + 4 * w * d
+
+
+def decode_bytes_per_bh(d: int, w: int, elem: int = 2) -> int:
+    # state read + write (f32), window keys and values except the incoming token, q/k/v/log_g in,
+    # ring slot write, y out
+    return 2 * 4 * d * d + 2 * elem * (w - 1) * d + 3 * elem * d + 4 * d + 2 * elem * d + elem * d
+
+
+# ---------------------------------------------------------------------------
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source."""
+    path = os.path.join(PROFILE_DIR, f"{kernel}_{workload}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != source_hash(rec["source"]):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def time_region(fn, steps: int, warmup: int):
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps  # ms
+
+
+def bench_fwd(sqa, si, steps, warmup):
+    import torch
+
+    w = si.WORKLOADS["llama3_8b_prefill_bf16"]
+    st = si.storage_inputs(w)
+    x = {}
+    for k, v in st.items():
+        import numpy as np
+
+        x[k] = torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).cuda() if v.dtype == np.uint16 else \
+            torch.from_numpy(v).cuda()
+    del st
+    out = {"y": torch.empty_like(x["q"])}
+
+    def step():
+        sqa.lizard_attn_fwd(x["q"], x["k"], x["v"], x["log_g"], x["meta_k"], window=w.window, alpha=w.alpha,
+                            out=out)
+
+    ms = time_region(step, steps, warmup)
+    head_tokens = w.B * w.H * w.L
+    alg_bytes = head_tokens * fwd_bytes_per_head_token(w.d)
+    alg_flops = head_tokens * fwd_flops_per_head_token(w.d, w.chunk, w.window, w.n_meta)
+    del x, out
+    torch.cuda.empty_cache()
+    return w, ms, alg_bytes, alg_flops
+
+
+def bench_decode(sqa, si, reps=3):
+    """1024 back-to-back steps after a 2048-token prefill (prefill untimed)."""
+    import numpy as np
+    import torch
+
+    w = si.WORKLOADS["decode_b64_bf16"]
+    st = si.storage_inputs(w)
+
+    def dev(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda() if a.dtype == np.uint16 else \
+            torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    L0, steps = w.L, w.steps
+    pre = {k: dev(np.ascontiguousarray(st[k][:, :, :L0])) for k in ("q", "k", "v", "log_g")}
+    meta = dev(st["meta_k"])
+    # decode inputs laid out [step, B, H, d] so each step reads a contiguous slice
+    dec = {k: dev(np.ascontiguousarray(st[k][:, :, L0:].transpose(2, 0, 1, 3))) for k in ("q", "k", "v", "log_g")}
+    ring0 = {k: dev(np.ascontiguousarray(st[k][:, :, L0 - w.window:L0])) for k in ("k", "v")}
+    del st
+    res = sqa.lizard_attn_fwd(pre["q"], pre["k"], pre["v"], pre["log_g"], meta, window=w.window, alpha=w.alpha,
+                              need_state=True)
+    state0 = res["state"]
+    del pre, res
+    y = torch.empty((steps, w.B, w.H, w.d), device="cuda", dtype=torch.bfloat16)
+    state = torch.empty_like(state0)
+    kr = torch.empty_like(ring0["k"])
+    vr = torch.empty_like(ring0["v"])
+    # (L0 - w) is a multiple of w, so slot p mod w of the ring is row p - (L0 - w)
+
+    def run_all(per_step_events=None, flush=None):
+        state.copy_(state0)
+        kr.copy_(ring0["k"])
+        vr.copy_(ring0["v"])
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(steps):
+            if flush is not None:
+                flush()
+            if per_step_events is not None:
+                per_step_events[i][0].record()
+            sqa.lizard_decode_step(L0 + i, dec["q"][i], dec["k"][i], dec["v"][i], dec["log_g"][i], meta, state, kr,
+                                   vr, alpha=w.alpha, y_t=y[i])
+            if per_step_events is not None:
+                per_step_events[i][1].record()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    run_all()  # warm-up
+    ms_b2b = min(run_all() for _ in range(reps))
+    # cache-flushed: 512 MiB written between steps evicts the 256 MB last-level cache;
+    # only the decode kernel is timed (per-step events)
+    scratch = torch.empty(512 << 20, device="cuda", dtype=torch.uint8)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    run_all(per_step_events=ev, flush=lambda: scratch.fill_(1))
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    ms_flushed = sum(per) / steps
+    bytes_step = w.B * w.H * decode_bytes_per_bh(w.d, w.window)
+    out = {
+        "workload": "decode_b64_bf16", "B": w.B, "H": w.H, "d": w.d, "window": w.window, "n_meta": w.n_meta,
+        "prefill": L0, "steps": steps,
+        "us_per_step": round(ms_b2b * 1e3, 2),
+        "tokens_per_s": round(w.B / (ms_b2b * 1e-3), 1),
+        "alg_bytes_per_step": bytes_step,
+        "gbps": round(bytes_step / (ms_b2b * 1e-3) / 1e9, 1),
+        "frac_hbm_peak": round(bytes_step / (ms_b2b * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "flushed_us_per_step": round(ms_flushed * 1e3, 2),
+        "flushed_p50_us": round(per[steps // 2] * 1e3, 2),
+        "flushed_gbps": round(bytes_step / (ms_flushed * 1e-3) / 1e9, 1),
+        "flushed_frac_hbm_peak": round(bytes_step / (ms_flushed * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "traffic": read_traffic("lizard_decode", "decode_b64_bf16"),
+    }
+    del dec, ring0, y, state, state0, kr, vr, scratch
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_bwd(sqa, si, steps=10, warmup=3):
+    import numpy as np
+    import torch
+
+    w = si.WORKLOADS["train_bwd_bf16"]
+    st = si.storage_inputs(w, with_dy=True)
+    x = {k: (torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).cuda() if v.dtype == np.uint16 else
+             torch.from_numpy(v).cuda()) for k, v in st.items()}
+    del st
+    fw = sqa.lizard_attn_fwd(x["q"], x["k"], x["v"], x["log_g"], x["meta_k"], window=w.window, alpha=w.alpha,
+                             need_lse=True)
+    ws = torch.empty(max(16, sqa.lizard_attn_bwd_workspace_size(w.B, w.H, w.L, w.d, window=w.window,
+                                                                 n_meta=w.n_meta, dtype=sqa.LIZARD_BF16)),
+                     device="cuda", dtype=torch.uint8)
+    out = {}
+
+    def step():
+        sqa.lizard_attn_bwd(x["q"], x["k"], x["v"], x["log_g"], x["meta_k"], fw["lse"], x["dy"], window=w.window,
+                            alpha=w.alpha, workspace=ws, out=out)
+
+    step()
+    ms = time_region(step, steps, warmup)
+    head_tokens = w.B * w.H * w.L
+    alg_bytes = head_tokens * bwd_bytes_per_head_token(w.d)
+    alg_flops = head_tokens * bwd_flops_per_head_token(w.d, w.chunk, w.window, w.n_meta)
+    res = {
+        "workload": "train_bwd_bf16", "B": w.B, "H": w.H, "L": w.L, "d": w.d,
+        "ms": round(ms, 4), "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1),
+        "alg_bytes": alg_bytes, "gbps": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
+        "frac_hbm_peak": round(alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "tflops": round(alg_flops / (ms * 1e-3) / 1e12, 2),
+        "frac_mfma_peak": round(alg_flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "workspace_bytes": int(ws.numel()),
+    }
+    del x, fw, ws, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(si, target_s: float = 15.0):
+    """The float64 oracle (oracle.lizard_fwd) on a bounded sample: whole-length
+    heads of the 4K prefill workload, one BLAS thread."""
+    import numpy as np
+
+    import oracle
+
+    from threadpoolctl import threadpool_limits
+
+    w = si.WORKLOADS["llama3_8b_prefill_bf16"]
+    n = 0
+    elapsed = 0.0
+    with threadpool_limits(limits=1):
+        while elapsed < target_s and n < w.B * w.H:
+            b, h = divmod(n, w.H)
+            s = si.slice_inputs(w, b, h)
+            mk = si.meta_keys(w, h)[None]
+            t0 = time.perf_counter()
+            oracle.lizard_fwd(s["q"][None], s["k"][None], s["v"][None], s["log_g"][None], mk, w.window, w.alpha)
+            elapsed += time.perf_counter() - t0
+            n += 1
+    head_tokens_per_s = n * w.L / elapsed
+    return {
+        "value": round(head_tokens_per_s / w.H, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        "sample": f"{n} whole (b,h) heads x L={w.L} of the 4K prefill workload in {elapsed:.1f} s "
+                  f"(float64 numpy, 1 thread); tokens/s = head-tokens/s / H",
+        "host_cpus": os.cpu_count(), "np_version": np.__version__,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--only", choices=["fwd", "decode", "bwd"], default=None,
+                    help="run one leg only (for profiler runs); prints that leg's record")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the layer's kernels run on a single MI355X; "
+              "use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import seeded_inputs as si
+    import subquadratic_attention_amd as sqa
+
+    sqa.load_library()
+    torch.cuda.init()
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, device="cuda", dtype=torch.uint8).fill_(3)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 1 << 30}), flush=True)
+        del src, dst
+
+    if args.only == "decode":
+        print(json.dumps(bench_decode(sqa, si)), flush=True)
+        return
+    if args.only == "bwd":
+        print(json.dumps(bench_bwd(sqa, si, args.steps, args.warmup)), flush=True)
+        return
+
+    w, ms, alg_bytes, alg_flops = bench_fwd(sqa, si, args.steps, args.warmup)
+    print(f"# fwd done: {ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+    tokens = w.B * w.L
+    gbs = alg_bytes / (ms * 1e-3) / 1e9
+    tflops = alg_flops / (ms * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC,
+        "value": round(tokens / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama3_8b_prefill_bf16", "B": w.B, "H": w.H, "L": w.L, "d": w.d, "chunk": w.chunk,
+                   "window": w.window, "n_meta": w.n_meta, "alpha": w.alpha, "mode": "inference (y only)"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": read_traffic("lizard_fwd", "llama3_8b_prefill_bf16"),
+                     "kernel": "lizard_fwd_kernel<bf16,128,64>", "alg_bytes_per_launch": alg_bytes},
+        "mfma": {"achieved_tflops": round(tflops, 2), "peak_tflops": BF16_PEAK_TFLOPS,
+                 "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "alg_flops_per_launch": alg_flops,
+                 "frac_ceiling_at_hbm_bound": round(fwd_flops_per_head_token(w.d) / fwd_bytes_per_head_token(w.d)
+                                                    * HBM_PEAK_GBS / 1e3 / BF16_PEAK_TFLOPS, 4)},
+    }
+    if args.only == "fwd":
+        print(json.dumps(rec), flush=True)
+        return
+    if not args.no_decode:
+        rec["decode"] = bench_decode(sqa, si)
+        print("# decode done", file=sys.stderr, flush=True)
+    if not args.no_bwd:
+        try:
+            rec["bwd"] = bench_bwd(sqa, si)
+        except sqa.LizardError as e:
+            rec["bwd"] = {"error": str(e)}
+        print("# bwd done", file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(si)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -111,6 +111,50 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
+// Reductions across the four 16-lane groups of a wavefront (lanes l, l^16,
+// l^32, l^48).  (The gfx950 permlane16/32 swap builtins would do this on the
+// VALU, but this compiler folds their two outputs into one, so the portable
+// lane shuffle is used.)
+__device__ __forceinline__ float xgroup_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16, 64));
+  return fmaxf(x, __shfl_xor(x, 32, 64));
+}
+__device__ __forceinline__ float xgroup_sum(float x) {
+  x += __shfl_xor(x, 16, 64);
+  return x + __shfl_xor(x, 32, 64);
+}
+
+// Pack n float values (n = 4, 8, 16) into consecutive elements of type T and
+// store them with 8/16-byte LDS or global writes.
+template <typename T, int N> __device__ __forceinline__ void store_pack(T* dst, const float* v);
+template <> __device__ __forceinline__ void store_pack<bf16, 4>(bf16* dst, const float* v) {
+  bf16x4 p;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = static_cast<bf16>(v[i]);
+  *reinterpret_cast<bf16x4*>(dst) = p;
+}
+template <> __device__ __forceinline__ void store_pack<bf16, 8>(bf16* dst, const float* v) {
+  bf16x8 p;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p[i] = static_cast<bf16>(v[i]);
+  *reinterpret_cast<bf16x8*>(dst) = p;
+}
+template <> __device__ __forceinline__ void store_pack<bf16, 16>(bf16* dst, const float* v) {
+  store_pack<bf16, 8>(dst, v);
+  store_pack<bf16, 8>(dst + 8, v + 8);
+}
+template <> __device__ __forceinline__ void store_pack<float, 4>(float* dst, const float* v) {
+  *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+}
+template <> __device__ __forceinline__ void store_pack<float, 8>(float* dst, const float* v) {
+  store_pack<float, 4>(dst, v);
+  store_pack<float, 4>(dst + 4, v + 4);
+}
+template <> __device__ __forceinline__ void store_pack<float, 16>(float* dst, const float* v) {
+  store_pack<float, 8>(dst, v);
+  store_pack<float, 8>(dst + 8, v + 8);
+}
+
 // Order LDS traffic of one wavefront: writes before the fence are visible
 // to reads after it from any lane of the same wavefront.
 __device__ __forceinline__ void wave_lds_sync() {
