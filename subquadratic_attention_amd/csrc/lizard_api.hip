@@ -65,6 +65,7 @@ LIZARD_API lizard_status_t lizard_attn_fwd(const lizard_params_t* p, const void*
   a.lse = lse;
   a.y_anchor = y_anchor;
   a.state_out = state_out;
+  a.states = nullptr;
   a.BH = BH;
   a.H = p->H;
   a.L = p->L;
@@ -88,18 +89,19 @@ LIZARD_API lizard_status_t lizard_attn_bwd(const lizard_params_t* p, const void*
                                            void* stream) {
   lizard_status_t s = check_params(p, true);
   if (s != LIZARD_OK) return s;
-  if (!q || !k || !v || !log_g || !lse || !dy || !dq || !dk || !dv || !dlog_g ||
-      (p->n_meta > 0 && (!meta_k || !dmeta_k)))
+  const int BH = p->B * p->H;
+  const bool seq = BH > 0 && p->L > 0;   // otherwise only dmeta_k (zero) is written
+  if ((seq && (!q || !k || !v || !log_g || !lse || !dy || !dq || !dk || !dv || !dlog_g)) ||
+      (p->n_meta > 0 && p->H > 0 && !dmeta_k) || (seq && p->n_meta > 0 && !meta_k))
     return LIZARD_E_NULL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(log_g) || misaligned(meta_k) ||
       misaligned(lse) || misaligned(dy) || misaligned(dq) || misaligned(dk) || misaligned(dv) ||
       misaligned(dlog_g) || misaligned(dmeta_k) || misaligned(workspace))
     return LIZARD_E_ALIGN;
-  const size_t need = lizard::bwd_workspace_bytes(p->dtype == LIZARD_BF16, p->B * p->H, p->L, p->dk, p->n_meta);
+  const size_t need = lizard::bwd_workspace_bytes(p->dtype == LIZARD_BF16, BH, p->L, p->dk, p->n_meta);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LIZARD_E_WORKSPACE;
-  const int BH = p->B * p->H;
-  if (BH == 0 && p->H * p->n_meta == 0) return LIZARD_OK;
-  lizard::BwdArgs a;
+  if (!seq && (p->n_meta == 0 || p->H == 0)) return LIZARD_OK;
+  lizard::BwdArgs a{};
   a.q = q;
   a.k = k;
   a.v = v;
@@ -112,6 +114,7 @@ LIZARD_API lizard_status_t lizard_attn_bwd(const lizard_params_t* p, const void*
   a.dv = dv;
   a.dlog_g = dlog_g;
   a.dmeta = dmeta_k;
+  a.workspace = workspace;
   a.B = p->B;
   a.BH = BH;
   a.H = p->H;
@@ -120,8 +123,6 @@ LIZARD_API lizard_status_t lizard_attn_bwd(const lizard_params_t* p, const void*
   a.window = p->window;
   a.alpha = p->alpha;
   a.scale = scale_of(p);
-  a.states = workspace;
-  a.dmeta_part = nullptr;
   return launched(lizard::launch_bwd(a, p->dtype == LIZARD_BF16, p->dk, static_cast<hipStream_t>(stream)));
 }
 

@@ -1,11 +1,989 @@
-// Backward pass of the Lizard hybrid attention layer (not yet built).
+// Backward pass of the Lizard hybrid attention layer on gfx950.
+//
+// The layer is trained end to end ("Lizard" explainer, gist.science (de),
+// section 2 "Trainingsprozess"); this file computes the gradients of
+// loss = sum(dY * Y) for Y = Y_gate + alpha * Y_anchor.  Notation as in the
+// forward kernel: per chunk of 64 tokens, beta_t is the log2-gate prefix
+// from the chunk start, B the chunk total, Qe = q*2^beta, Kp = k*2^-beta,
+// Kh = k*2^{B-beta}, A[t][s] = Qe_t . Kp_s (s <= t), S_c the state entering
+// chunk c and G_c = dL/dS_c.
+//
+//   gated branch, chunk c, dO = dY:
+//     G_c    = diag(2^B) G_{c+1} + Qe^T dO
+//     dA     = dO V^T (s <= t)
+//     dq_t   = 2^{beta_t} * (S_c dO_t + sum_s dA_ts Kp_s)
+//     dk_s   = 2^{-beta_s} * sum_t dA_ts Qe_t + 2^{B-beta_s} * (G_{c+1} v_s)
+//     dv_s   = sum_t A_ts dO_t + G_{c+1}^T Kh_s
+//     dlog_g_t = sum_{u >= t} (q_u * dq_u - k_u * dk_u)      (natural log)
+//   anchor branch (softmax over the window and sinks, P = exp(z - lse)):
+//     dP = alpha dY V^T (window; zero for sinks), D_t = sum P dP,
+//     dZ = P (dP - D_t); dq += scale (dZ K + dZs mu); dk += scale dZ^T Q;
+//     dv += alpha P^T dY; dmu += scale dZs^T Q (summed over batch and time)
+//
+// Kernels, in launch order (all on the caller's stream):
+//   1. the forward kernel in its states-only mode writes S_c for every chunk;
+//   2. bwd_dstate walks the chunks in reverse and writes G_{c+1} (and its
+//      transpose) for every chunk;
+//   3. bwd_anchor_q (per chunk of queries): D_t, the anchor part of dq, and
+//      per-chunk sink-key gradients;
+//   4. bwd_anchor_k (per chunk of keys, queries of this and the next chunk):
+//      the anchor parts of dk and dv;
+//   5. bwd_gate (per chunk): the gated dq, dk, dv, adds the anchor parts and
+//      writes the outputs; writes q*dq - k*dk into dlog_g;
+//   6. bwd_dlogg_scan: reverse cumulative sum of dlog_g along the sequence;
+//   7. bwd_dmeta_reduce: sums the sink-key partials over batch and chunks in
+//      a fixed order (deterministic, no float atomics).
+// Chunks whose decay span exceeds 2^92 form the gated intra terms pairwise
+// in fp32 (as the forward pass does).
+#include <type_traits>
+
 #include "lizard_common.hpp"
 #include "lizard_kernels.hpp"
 
 namespace lizard {
 
-size_t bwd_workspace_bytes(int, int, int, int, int) { return 0; }
+namespace {
 
-hipError_t launch_bwd(const BwdArgs&, int, int, hipStream_t) { return hipErrorNotSupported; }
+constexpr int C = 64;
+constexpr float kMaxSpan = 92.0f;   // log2 units, as in the forward kernel
+
+template <typename T> __device__ __forceinline__ float elem_of(const uint4* raw, int i) {
+  if constexpr (sizeof(T) == 2) {
+    const bf16x8 v = __builtin_bit_cast(bf16x8, raw[i >> 3]);
+    return static_cast<float>(v[i & 7]);
+  } else {
+    const uint4 r = raw[i >> 2];
+    const uint32_t u = (i & 3) == 0 ? r.x : (i & 3) == 1 ? r.y : (i & 3) == 2 ? r.z : r.w;
+    return __builtin_bit_cast(float, u);
+  }
+}
+template <typename T> __device__ __forceinline__ typename Mfma<T>::frag frag_of(const uint4* raw, int e) {
+  if constexpr (sizeof(T) == 2) {
+    return __builtin_bit_cast(bf16x8, raw[e]);
+  } else {
+    return elem_of<float>(raw, e);
+  }
+}
+// The lane's k-quarter [g*D/4, (g+1)*D/4) of global row `row` (zeros if the
+// row is outside [0, L)).
+template <typename T, int D>
+__device__ __forceinline__ void load_quarter(uint4* raw, const T* base, int row, int L, int g) {
+  constexpr int QV = D / 4 / (16 / sizeof(T));
+  const bool ok = row >= 0 && row < L;
+  const T* p = base + (size_t)(ok ? row : 0) * D + g * (D / 4);
+#pragma unroll
+  for (int e = 0; e < QV; ++e) {
+    const uint4 r = ld16(p + e * (16 / sizeof(T)));
+    raw[e] = ok ? r : make_uint4(0, 0, 0, 0);
+  }
+}
+// element i of a packed 32-bit word of T values
+template <typename T> __device__ __forceinline__ float elem32(uint32_t u, int i) {
+  if constexpr (sizeof(T) == 4) return __builtin_bit_cast(float, u);
+  else return __builtin_bit_cast(float, i == 0 ? (u << 16) : (u & 0xffff0000u));
+}
+
+// Stage rows [r0, r0 + NR) x columns [c0, c0 + COLS) of a [L, D] tensor into
+// LDS transposed: dst[col * ld + row] (rows outside [0, L) are zero).  Each
+// thread loads 32-bit words (VC columns) of RPT consecutive rows and writes
+// 8-row runs with 16-byte stores.  scale multiplies every value.
+template <typename T, int D, int COLS, int NR>
+__device__ __forceinline__ void stage_T(T* dst, int ld, const T* src, int r0, int c0, int L, float scale) {
+  constexpr int VC = 4 / sizeof(T);
+  constexpr int VRW = COLS / VC;
+  constexpr int RPT = NR * VRW / 256;
+  static_assert(RPT % 8 == 0 && RPT * 256 == NR * VRW, "stage_T shape");
+  const int tid = threadIdx.x;
+  const int vj = tid % VRW;
+  const int vs = tid / VRW;
+  uint32_t w[RPT];
+#pragma unroll
+  for (int rr = 0; rr < RPT; ++rr) {
+    const int row = r0 + vs * RPT + rr;
+    const bool ok = row >= 0 && row < L;
+    const uint32_t u = *reinterpret_cast<const uint32_t*>(src + (size_t)(ok ? row : 0) * D + c0 + VC * vj);
+    w[rr] = ok ? u : 0u;
+  }
+#pragma unroll
+  for (int cc = 0; cc < VC; ++cc)
+#pragma unroll
+    for (int b = 0; b < RPT / 8; ++b) {
+      float v8[8];
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) v8[rr] = elem32<T>(w[8 * b + rr], cc) * scale;
+      store_pack<T, 8>(dst + (VC * vj + cc) * ld + vs * RPT + 8 * b, v8);
+    }
+}
+
+// Stage rows [r0, r0 + NR) of a [L, D] tensor into LDS row-major (ld elements per row).
+template <typename T, int D, int NR>
+__device__ __forceinline__ void stage_rows(T* dst, int ld, const T* src, int r0, int L) {
+  constexpr int EPV = 16 / sizeof(T);
+  constexpr int VPR = D / EPV;
+  for (int i = threadIdx.x; i < NR * VPR; i += 256) {
+    const int row = i / VPR, cv = i % VPR;
+    const int gr = r0 + row;
+    const bool ok = gr >= 0 && gr < L;
+    const uint4 u = ld16(src + (size_t)(ok ? gr : 0) * D + cv * EPV);
+    *reinterpret_cast<uint4*>(dst + row * ld + cv * EPV) = ok ? u : make_uint4(0, 0, 0, 0);
+  }
+}
+
+// Block -> (bh, chunk) with every chunk of one head on the same XCD.
+__device__ __forceinline__ bool chunk_block(int BH, int nc, int& bh, int& c) {
+  const int x = blockIdx.x;
+  const int xcd = x & 7;
+  const int idx = x >> 3;
+  c = idx % nc;
+  bh = (idx / nc) * 8 + xcd;
+  return bh < BH;
+}
+
+// Chunk-local log2-gate prefix for 256 threads: thread (w, l) owns rows
+// 16w..16w+15 and dims DPL*l..; returns beta (chunk-inclusive prefix) and B
+// (chunk total) for those; sTot is [4][D] scratch.  Contains one barrier.
+template <int D>
+__device__ __forceinline__ void chunk_prefix(const float* lg, int t0, int L, float* sTot,
+                                             float (&beta)[16][D / 64], float (&Bt)[D / 64]) {
+  constexpr int DPL = D / 64;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  float tot[DPL];
+#pragma unroll
+  for (int dd = 0; dd < DPL; ++dd) tot[dd] = 0.f;
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) {
+    const int t = t0 + 16 * w + rr;
+    const bool ok = t < L;
+#pragma unroll
+    for (int dd = 0; dd < DPL; ++dd) {
+      const float v = ok ? lg[(size_t)(ok ? t : 0) * D + DPL * l + dd] : 0.f;
+      tot[dd] += log2_gate(v);
+      beta[rr][dd] = tot[dd];
+    }
+  }
+#pragma unroll
+  for (int dd = 0; dd < DPL; ++dd) sTot[w * D + DPL * l + dd] = tot[dd];
+  __syncthreads();
+#pragma unroll
+  for (int dd = 0; dd < DPL; ++dd) {
+    const int i = DPL * l + dd;
+    const float a0 = sTot[i], a1 = sTot[D + i], a2 = sTot[2 * D + i], a3 = sTot[3 * D + i];
+    const float off = w == 0 ? 0.f : w == 1 ? a0 : w == 2 ? a0 + a1 : a0 + a1 + a2;
+    Bt[dd] = a0 + a1 + a2 + a3;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) beta[rr][dd] += off;
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// 2. reverse state-gradient pass: G_c = diag(2^B) G_{c+1} + Qe^T dO
+// ---------------------------------------------------------------------------
+template <typename T, int D, int DV>
+__global__ __launch_bounds__(256, 1) void bwd_dstate_kernel(BwdArgs a) {
+  typedef Mfma<T> M;
+  constexpr int PAD = 16 / sizeof(T);
+  constexpr int LDQ = 64 + PAD;
+  constexpr int NCT = DV / 16;
+  constexpr int NRT = D / 64;
+  constexpr int DPL = D / 64;
+  __shared__ __align__(16) T sQeT[D * LDQ];
+  __shared__ __align__(16) T sdOT[DV * LDQ];
+  __shared__ float sTot[4 * D];
+  __shared__ float sBexp[D];
+
+  const int nsplit = D / DV;
+  const int x = blockIdx.x, xcd = x & 7, idx = x >> 3;
+  const int split = idx % nsplit;
+  const int bh = (idx / nsplit) * 8 + xcd;
+  if (bh >= a.BH) return;
+  const int j0 = split * DV;
+  const int L = a.L, nc = (L + C - 1) / C;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
+  const T* qg = reinterpret_cast<const T*>(a.q) + (size_t)bh * L * D;
+  const T* dyg = reinterpret_cast<const T*>(a.dy) + (size_t)bh * L * D;
+  const float* lgg = a.log_g + (size_t)bh * L * D;
+  T* Gg = reinterpret_cast<T*>(a.ws_dS) + (size_t)bh * nc * D * D;
+  T* GTg = reinterpret_cast<T*>(a.ws_dST) + (size_t)bh * nc * D * D;
+
+  f32x4 acc[NRT][NCT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[rt][ct] = zero4();
+
+  for (int c = nc - 1; c >= 0; --c) {
+    const int t0 = c * C;
+    // G_{c+1}: rows i, columns j (row-major) and its transpose
+    T* G = Gg + (size_t)c * D * D;
+    T* GT = GTg + (size_t)c * D * D;
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const int i = w * (D / 4) + 16 * rt + 4 * g;
+        const int j = j0 + 16 * ct + m;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) G[(size_t)(i + r) * D + j] = from_f32<T>(acc[rt][ct][r]);
+        const float v4[4] = {acc[rt][ct][0], acc[rt][ct][1], acc[rt][ct][2], acc[rt][ct][3]};
+        store_pack<T, 4>(GT + (size_t)j * D + i, v4);
+      }
+    float beta[16][DPL], Bt[DPL];
+    chunk_prefix<D>(lgg, t0, L, sTot, beta, Bt);
+#pragma unroll
+    for (int dd = 0; dd < DPL; ++dd) {
+      const int i = DPL * l + dd;
+      float qe[16];
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int t = t0 + 16 * w + rr;
+        const float qv = t < L ? to_f32(qg[(size_t)(t < L ? t : 0) * D + i]) : 0.f;
+        qe[rr] = qv * exp_2(beta[rr][dd]);
+      }
+      store_pack<T, 16>(sQeT + i * LDQ + 16 * w, qe);
+      if (w == 0) sBexp[i] = exp_2(Bt[dd]);
+    }
+    stage_T<T, D, DV, 64>(sdOT, LDQ, dyg, t0, j0, L, 1.0f);
+    __syncthreads();
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      const int ib = w * (D / 4) + 16 * rt;
+      float dec[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dec[r] = sBexp[ib + 4 * g + r];
+      const T* ap = sQeT + (ib + m) * LDQ + g * 16;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        f32x4 s = acc[rt][ct];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[r] *= dec[r];
+        const T* bp = sdOT + (16 * ct + m) * LDQ + g * 16;
+#pragma unroll
+        for (int e = 0; e < 16 / M::KPL; ++e) s = M::mma(M::load(ap + e * M::KPL), M::load(bp + e * M::KPL), s);
+        acc[rt][ct] = s;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. anchor branch, query side (per chunk of queries)
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+struct AqLayout {
+  static constexpr int PAD = 16 / sizeof(T);
+  static constexpr int LDKT = 128 + PAD;   // sKT [D][LDKT]: window keys transposed
+  static constexpr int LDMT = 32 + PAD;    // sMuT [D][LDMT]: sink keys transposed (zero padded)
+  static constexpr int LDQ = D + PAD;      // sQ [64][LDQ]
+  static constexpr int LDS = 96 + PAD;     // per-wave staging of dZ [16][LDS]
+  static constexpr int LDZS = 32 + PAD;    // per-wave staging of sink dZ [16][LDZS]
+  static constexpr int a16(int x) { return (x + 15) / 16 * 16; }
+  static constexpr int OFF_KT = 0;
+  static constexpr int OFF_MT = OFF_KT + a16(D * LDKT * (int)sizeof(T));
+  static constexpr int OFF_Q = OFF_MT + a16(D * LDMT * (int)sizeof(T));
+  static constexpr int OFF_ST = OFF_Q + a16(64 * LDQ * (int)sizeof(T));
+  static constexpr int OFF_ZS = OFF_ST + a16(4 * 16 * LDS * (int)sizeof(T));
+  static constexpr int OFF_DZS = OFF_ZS + a16(4 * 16 * LDZS * (int)sizeof(T));   // fp32 [64][16]
+  static constexpr int TOTAL = OFF_DZS + a16(64 * 16 * 4);
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256, 1) void bwd_anchor_q_kernel(BwdArgs a) {
+  typedef AqLayout<T, D> Lay;
+  typedef Mfma<T> M;
+  typedef typename M::frag frag;
+  constexpr int EPV = 16 / sizeof(T);
+  constexpr int QV = D / 4 / EPV;
+  constexpr int NF = D / 4 / M::KPL;
+  constexpr int NDT = D / 16;
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* sKT = reinterpret_cast<T*>(smem + Lay::OFF_KT);
+  T* sMuT = reinterpret_cast<T*>(smem + Lay::OFF_MT);
+  T* sQ = reinterpret_cast<T*>(smem + Lay::OFF_Q);
+  float* sdZs = reinterpret_cast<float*>(smem + Lay::OFF_DZS);
+
+  const int L = a.L, nc = (L + C - 1) / C;
+  int bh, c;
+  if (!chunk_block(a.BH, nc, bh, c)) return;
+  const int h = bh % a.H;
+  const int t0 = c * C;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
+  T* sSt = reinterpret_cast<T*>(smem + Lay::OFF_ST) + w * 16 * Lay::LDS;
+  T* sZs = reinterpret_cast<T*>(smem + Lay::OFF_ZS) + w * 16 * Lay::LDZS;
+  const T* qg = reinterpret_cast<const T*>(a.q) + (size_t)bh * L * D;
+  const T* kg = reinterpret_cast<const T*>(a.k) + (size_t)bh * L * D;
+  const T* vg = reinterpret_cast<const T*>(a.v) + (size_t)bh * L * D;
+  const T* dyg = reinterpret_cast<const T*>(a.dy) + (size_t)bh * L * D;
+  const T* mug = reinterpret_cast<const T*>(a.meta) + (size_t)h * a.n_meta * D;
+  const float sl2 = a.scale * kLog2e;
+
+  // window keys [t0 - 64, t0 + 64) transposed; sink keys transposed; this chunk's queries
+  stage_T<T, D, D, 128>(sKT, Lay::LDKT, kg, t0 - 64, 0, L, 1.0f);
+  for (int i = tid; i < D * 32; i += 256) {
+    const int d = i / 32, s = i % 32;
+    sMuT[d * Lay::LDMT + s] = s < a.n_meta ? mug[(size_t)(s < a.n_meta ? s : 0) * D + d] : from_f32<T>(0.f);
+  }
+  stage_rows<T, D, 64>(sQ, Lay::LDQ, qg, t0, L);
+  __syncthreads();
+
+  const int I = w;
+  const int tme = t0 + 16 * I + m;
+  const int U0 = 16 * I < 32 ? 16 * I : 32;
+  uint4 qraw[QV], dyraw[QV];
+  load_quarter<T, D>(qraw, qg, tme, L, g);
+  load_quarter<T, D>(dyraw, dyg, tme, L, g);
+  const float lse2 = tme < L ? a.lse[(size_t)bh * L + tme] * kLog2e : 0.f;
+
+  // logits Z^T[u][t] and value products dP^T[u][t] for window keys u
+  f32x4 z[6], dp[6];
+#pragma unroll
+  for (int kt = 0; kt < 6; ++kt) {
+    const int s = t0 - 64 + U0 + 16 * kt + m;   // key row of this lane (MFMA row)
+    uint4 kraw[QV], vraw[QV];
+    load_quarter<T, D>(kraw, kg, s, L, g);
+    load_quarter<T, D>(vraw, vg, s, L, g);
+    f32x4 zc = zero4(), pc = zero4();
+#pragma unroll
+    for (int e = 0; e < NF; ++e) {
+      zc = M::mma(frag_of<T>(kraw, e), frag_of<T>(qraw, e), zc);
+      pc = M::mma(frag_of<T>(vraw, e), frag_of<T>(dyraw, e), pc);
+    }
+    z[kt] = zc;
+    dp[kt] = pc;
+  }
+  f32x4 zs = zero4();
+  if (a.n_meta > 0) {
+    uint4 mraw[QV];
+    load_quarter<T, D>(mraw, mug, m < a.n_meta ? m : -1, a.n_meta, g);
+#pragma unroll
+    for (int e = 0; e < NF; ++e) zs = M::mma(frag_of<T>(mraw, e), frag_of<T>(qraw, e), zs);
+  }
+  // probabilities from the forward normaliser, D_t, dZ
+  float dsum = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < 6; ++kt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int s = t0 - 64 + U0 + 16 * kt + 4 * g + r;
+      const bool ok = s >= 0 && s <= tme && s > tme - a.window && tme < L;
+      const float p = ok ? exp_2(z[kt][r] * sl2 - lse2) : 0.f;
+      z[kt][r] = p;
+      dp[kt][r] *= a.alpha;
+      dsum += p * dp[kt][r];
+    }
+  const float Dt = xgroup_sum(dsum);
+  if (g == 0 && tme < L) a.ws_D[(size_t)bh * L + tme] = Dt;
+  float ps[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    ps[r] = (4 * g + r < a.n_meta && tme < L) ? exp_2(zs[r] * sl2 - lse2) : 0.f;
+  // stage dZ[t][u] and the sink part dZs[t][i] = -P D_t (rows: this lane's query)
+#pragma unroll
+  for (int kt = 0; kt < 6; ++kt) {
+    float v4[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v4[r] = z[kt][r] * (dp[kt][r] - Dt);
+    store_pack<T, 4>(sSt + m * Lay::LDS + 16 * kt + 4 * g, v4);
+  }
+  {
+    float v4[4], z4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v4[r] = -ps[r] * Dt;
+    store_pack<T, 4>(sZs + m * Lay::LDZS + 4 * g, v4);
+    store_pack<T, 4>(sZs + m * Lay::LDZS + 16 + 4 * g, z4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sdZs[(16 * I + m) * 16 + 4 * g + r] = v4[r];
+  }
+  wave_lds_sync();
+  // dq^T[d][t] = scale (K^T dZ^T + mu^T dZs^T)
+  float* dqa = a.ws_dqa + (size_t)bh * L * D;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    f32x4 o = zero4();
+    const T* bp = sSt + m * Lay::LDS + g * 24;
+    const T* ap = sKT + (16 * dt + m) * Lay::LDKT + U0 + g * 24;
+#pragma unroll
+    for (int e = 0; e < 24 / M::KPL; ++e) o = M::mma(M::load(ap + e * M::KPL), M::load(bp + e * M::KPL), o);
+    const T* bz = sZs + m * Lay::LDZS + g * 8;
+    const T* az = sMuT + (16 * dt + m) * Lay::LDMT + g * 8;
+#pragma unroll
+    for (int e = 0; e < 8 / M::KPL; ++e) o = M::mma(M::load(az + e * M::KPL), M::load(bz + e * M::KPL), o);
+    if (tme < L)
+      *reinterpret_cast<f32x4*>(dqa + (size_t)tme * D + 16 * dt + 4 * g) =
+          f32x4{o[0] * a.scale, o[1] * a.scale, o[2] * a.scale, o[3] * a.scale};
+  }
+  __syncthreads();
+  // per-chunk sink-key gradient: dmu[i][d] = scale sum_t dZs[t][i] q[t][d]
+  if (a.n_meta > 0) {
+    float* part = a.ws_dmu + ((size_t)bh * nc + c) * a.n_meta * D;
+    for (int o = tid; o < a.n_meta * D; o += 256) {
+      const int i = o / D, d = o % D;
+      float s = 0.f;
+      for (int t = 0; t < 64; ++t) s += sdZs[t * 16 + i] * to_f32(sQ[t * Lay::LDQ + d]);
+      part[o] = s * a.scale;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 4. anchor branch, key side (per chunk of keys; queries of this and the next chunk)
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+struct AkLayout {
+  static constexpr int PAD = 16 / sizeof(T);
+  static constexpr int LDT = 128 + PAD;    // sQT, sdYT [D][LDT]
+  static constexpr int LDS = 96 + PAD;     // per-wave staging [16][LDS], two of them
+  static constexpr int a16(int x) { return (x + 15) / 16 * 16; }
+  static constexpr int OFF_QT = 0;
+  static constexpr int OFF_DYT = OFF_QT + a16(D * LDT * (int)sizeof(T));
+  static constexpr int OFF_ST = OFF_DYT + a16(D * LDT * (int)sizeof(T));
+  static constexpr int OFF_RW = OFF_ST + a16(2 * 4 * 16 * LDS * (int)sizeof(T));   // lse*log2e, D_t: [2][128] fp32
+  static constexpr int TOTAL = OFF_RW + a16(2 * 128 * 4);
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256, 1) void bwd_anchor_k_kernel(BwdArgs a) {
+  typedef AkLayout<T, D> Lay;
+  typedef Mfma<T> M;
+  constexpr int EPV = 16 / sizeof(T);
+  constexpr int QV = D / 4 / EPV;
+  constexpr int NF = D / 4 / M::KPL;
+  constexpr int NDT = D / 16;
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* sQT = reinterpret_cast<T*>(smem + Lay::OFF_QT);
+  T* sdYT = reinterpret_cast<T*>(smem + Lay::OFF_DYT);
+  float* sLse = reinterpret_cast<float*>(smem + Lay::OFF_RW);
+  float* sD = sLse + 128;
+
+  const int L = a.L, nc = (L + C - 1) / C;
+  int bh, c;
+  if (!chunk_block(a.BH, nc, bh, c)) return;
+  const int t0 = c * C;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
+  T* sZ = reinterpret_cast<T*>(smem + Lay::OFF_ST) + w * 16 * Lay::LDS;
+  T* sP = reinterpret_cast<T*>(smem + Lay::OFF_ST) + (4 + w) * 16 * Lay::LDS;
+  const T* qg = reinterpret_cast<const T*>(a.q) + (size_t)bh * L * D;
+  const T* kg = reinterpret_cast<const T*>(a.k) + (size_t)bh * L * D;
+  const T* vg = reinterpret_cast<const T*>(a.v) + (size_t)bh * L * D;
+  const T* dyg = reinterpret_cast<const T*>(a.dy) + (size_t)bh * L * D;
+  const float sl2 = a.scale * kLog2e;
+
+  // queries [t0, t0 + 128): transposed q and dY, lse (log2 units) and D_t
+  stage_T<T, D, D, 128>(sQT, Lay::LDT, qg, t0, 0, L, 1.0f);
+  stage_T<T, D, D, 128>(sdYT, Lay::LDT, dyg, t0, 0, L, 1.0f);
+  if (tid < 128) {
+    const int t = t0 + tid;
+    sLse[tid] = t < L ? a.lse[(size_t)bh * L + t] * kLog2e : 0.f;
+    sD[tid] = t < L ? a.ws_D[(size_t)bh * L + t] : 0.f;
+  }
+  __syncthreads();
+
+  const int J = w;                        // key block
+  const int sme = t0 + 16 * J + m;        // this lane's key
+  const int Q0 = 16 * J < 32 ? 16 * J : 32;   // first staged query (relative to t0)
+  uint4 kraw[QV], vraw[QV];
+  load_quarter<T, D>(kraw, kg, sme, L, g);
+  load_quarter<T, D>(vraw, vg, sme, L, g);
+  // Z[t][s] and dP[t][s] tiles: queries t on the MFMA rows
+  f32x4 z[6], dp[6];
+#pragma unroll
+  for (int kt = 0; kt < 6; ++kt) {
+    const int t = t0 + Q0 + 16 * kt + m;
+    uint4 qraw[QV], dyraw[QV];
+    load_quarter<T, D>(qraw, qg, t, L, g);
+    load_quarter<T, D>(dyraw, dyg, t, L, g);
+    f32x4 zc = zero4(), pc = zero4();
+#pragma unroll
+    for (int e = 0; e < NF; ++e) {
+      zc = M::mma(frag_of<T>(qraw, e), frag_of<T>(kraw, e), zc);
+      pc = M::mma(frag_of<T>(dyraw, e), frag_of<T>(vraw, e), pc);
+    }
+    z[kt] = zc;
+    dp[kt] = pc;
+  }
+#pragma unroll
+  for (int kt = 0; kt < 6; ++kt) {
+    float pz[4], pp[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tr = Q0 + 16 * kt + 4 * g + r;   // query relative to t0
+      const int t = t0 + tr;
+      const bool ok = t < L && sme < L && t >= sme && t < sme + a.window;
+      const float p = ok ? exp_2(z[kt][r] * sl2 - sLse[tr]) : 0.f;
+      pz[r] = p * (dp[kt][r] * a.alpha - sD[tr]);
+      pp[r] = p * a.alpha;
+    }
+    store_pack<T, 4>(sZ + m * Lay::LDS + 16 * kt + 4 * g, pz);
+    store_pack<T, 4>(sP + m * Lay::LDS + 16 * kt + 4 * g, pp);
+  }
+  wave_lds_sync();
+  float* dka = a.ws_dka + (size_t)bh * L * D;
+  float* dva = a.ws_dva + (size_t)bh * L * D;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    f32x4 ok_ = zero4(), ov = zero4();
+    const T* bz = sZ + m * Lay::LDS + g * 24;
+    const T* bpp = sP + m * Lay::LDS + g * 24;
+    const T* aq = sQT + (16 * dt + m) * Lay::LDT + Q0 + g * 24;
+    const T* ay = sdYT + (16 * dt + m) * Lay::LDT + Q0 + g * 24;
+#pragma unroll
+    for (int e = 0; e < 24 / M::KPL; ++e) {
+      ok_ = M::mma(M::load(aq + e * M::KPL), M::load(bz + e * M::KPL), ok_);
+      ov = M::mma(M::load(ay + e * M::KPL), M::load(bpp + e * M::KPL), ov);
+    }
+    if (sme < L) {
+      *reinterpret_cast<f32x4*>(dka + (size_t)sme * D + 16 * dt + 4 * g) =
+          f32x4{ok_[0] * a.scale, ok_[1] * a.scale, ok_[2] * a.scale, ok_[3] * a.scale};
+      *reinterpret_cast<f32x4*>(dva + (size_t)sme * D + 16 * dt + 4 * g) = ov;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 5. gated branch (per chunk), combined with the anchor parts
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+struct GateLayout {
+  static constexpr int PAD = 16 / sizeof(T);
+  static constexpr int LDT = 64 + PAD;     // [D][LDT] transposed tiles; [64][LDT] staged scores
+  static constexpr int LDB = D + 4;        // sBeta [64][LDB] fp32
+  static constexpr int a16(int x) { return (x + 15) / 16 * 16; }
+  static constexpr int OFF_B = 0;
+  static constexpr int OFF_QT = OFF_B + a16(64 * LDB * 4);
+  static constexpr int OFF_KT = OFF_QT + a16(D * LDT * (int)sizeof(T));
+  static constexpr int OFF_OT = OFF_KT + a16(D * LDT * (int)sizeof(T));
+  static constexpr int OFF_DA = OFF_OT + a16(D * LDT * (int)sizeof(T));
+  static constexpr int OFF_DAT = OFF_DA + a16(64 * LDT * (int)sizeof(T));
+  static constexpr int OFF_AT = OFF_DAT + a16(64 * LDT * (int)sizeof(T));
+  static constexpr int OFF_TOT = OFF_AT + a16(64 * LDT * (int)sizeof(T));
+  static constexpr int OFF_BX = OFF_TOT + a16(4 * D * 4);
+  static constexpr int TOTAL = OFF_BX + a16(D * 4);
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256, 1) void bwd_gate_kernel(BwdArgs a) {
+  typedef GateLayout<T, D> Lay;
+  typedef Mfma<T> M;
+  typedef typename M::frag frag;
+  constexpr int EPV = 16 / sizeof(T);
+  constexpr int QV = D / 4 / EPV;
+  constexpr int NF = D / 4 / M::KPL;
+  constexpr int DPL = D / 64;
+  constexpr int NIT = D / 64;             // 16-row dim tiles per wavefront (D/4 dims each)
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* sBeta = reinterpret_cast<float*>(smem + Lay::OFF_B);
+  T* sQT = reinterpret_cast<T*>(smem + Lay::OFF_QT);    // Qe^T (or q^T on the pairwise path)
+  T* sKT = reinterpret_cast<T*>(smem + Lay::OFF_KT);    // Kp^T (or k^T on the pairwise path)
+  T* sOT = reinterpret_cast<T*>(smem + Lay::OFF_OT);    // dO^T
+  T* sDA = reinterpret_cast<T*>(smem + Lay::OFF_DA);    // dA[t][s]
+  T* sDAT = reinterpret_cast<T*>(smem + Lay::OFF_DAT);  // dA^T[s][t]
+  T* sAT = reinterpret_cast<T*>(smem + Lay::OFF_AT);    // A^T[s][t]
+  float* sTot = reinterpret_cast<float*>(smem + Lay::OFF_TOT);
+  float* sBx = reinterpret_cast<float*>(smem + Lay::OFF_BX);   // chunk total B (log2) per dim
+
+  const int L = a.L, nc = (L + C - 1) / C;
+  int bh, c;
+  if (!chunk_block(a.BH, nc, bh, c)) return;
+  const int t0 = c * C;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
+  const T* qg = reinterpret_cast<const T*>(a.q) + (size_t)bh * L * D;
+  const T* kg = reinterpret_cast<const T*>(a.k) + (size_t)bh * L * D;
+  const T* vg = reinterpret_cast<const T*>(a.v) + (size_t)bh * L * D;
+  const T* dyg = reinterpret_cast<const T*>(a.dy) + (size_t)bh * L * D;
+  const float* lgg = a.log_g + (size_t)bh * L * D;
+  const T* Sg = reinterpret_cast<const T*>(a.ws_states) + ((size_t)bh * nc + c) * D * D;
+  const T* Gg = reinterpret_cast<const T*>(a.ws_dS) + ((size_t)bh * nc + c) * D * D;
+  const T* GTg = reinterpret_cast<const T*>(a.ws_dST) + ((size_t)bh * nc + c) * D * D;
+
+  // ---- prefix, operands: Qe^T, Kp^T (or raw q^T, k^T), dO^T, beta ----
+  float beta[16][DPL], Bt[DPL];
+  chunk_prefix<D>(lgg, t0, L, sTot, beta, Bt);
+  bool wide = false;
+#pragma unroll
+  for (int dd = 0; dd < DPL; ++dd) wide |= -Bt[dd] > kMaxSpan;
+  const bool pairwise = __any(wide);
+#pragma unroll
+  for (int dd = 0; dd < DPL; ++dd) {
+    const int i = DPL * l + dd;
+    float qe[16], kp[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int t = t0 + 16 * w + rr;
+      const bool ok = t < L;
+      const float qv = ok ? to_f32(qg[(size_t)(ok ? t : 0) * D + i]) : 0.f;
+      const float kv = ok ? to_f32(kg[(size_t)(ok ? t : 0) * D + i]) : 0.f;
+      qe[rr] = pairwise ? qv : qv * exp_2(beta[rr][dd]);
+      kp[rr] = pairwise ? kv : kv * exp_2(-beta[rr][dd]);
+      sBeta[(16 * w + rr) * Lay::LDB + i] = beta[rr][dd];
+    }
+    store_pack<T, 16>(sQT + i * Lay::LDT + 16 * w, qe);
+    store_pack<T, 16>(sKT + i * Lay::LDT + 16 * w, kp);
+    if (w == 0) sBx[i] = Bt[dd];
+  }
+  stage_T<T, D, D, 64>(sOT, Lay::LDT, dyg, t0, 0, L, 1.0f);
+  __syncthreads();
+
+  // ---- phase B: wavefront I stages the score tiles of token block I ----
+  {
+    const int I = w;
+    const int tme = t0 + 16 * I + m;
+    uint4 dyr[QV], vr[QV], kr[QV];
+    load_quarter<T, D>(dyr, dyg, tme, L, g);
+    load_quarter<T, D>(vr, vg, tme, L, g);
+    load_quarter<T, D>(kr, kg, tme, L, g);
+    // Kp of this lane's key row as fragments
+    frag kpf[NF];
+    {
+      const float* bp = sBeta + (16 * I + m) * Lay::LDB + g * (D / 4);
+#pragma unroll
+      for (int e = 0; e < NF; ++e) {
+        float tk[M::KPL];
+#pragma unroll
+        for (int u = 0; u < M::KPL; ++u) {
+          const int kk = e * M::KPL + u;
+          tk[u] = pairwise ? 0.f : elem_of<T>(kr, kk) * exp_2(-bp[kk]);
+        }
+        kpf[e] = M::pack(tk);
+      }
+    }
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      // (a) dA^T tile: keys s in block J (rows), queries t in block I (cols) -> sDA[t][s]
+      // (b) dA tile: queries t in block J (rows), keys s in block I (cols) -> sDAT[s][t]
+      // (c) A tile: queries t in block J (rows), keys s in block I (cols) -> sAT[s][t]
+      uint4 vJ[QV], dyJ[QV], qJ[QV];
+      const int rJ = t0 + 16 * J + m;
+      load_quarter<T, D>(vJ, vg, rJ, L, g);
+      load_quarter<T, D>(dyJ, dyg, rJ, L, g);
+      f32x4 ta = zero4(), tb = zero4(), tc = zero4();
+      if (J <= I) {
+#pragma unroll
+        for (int e = 0; e < NF; ++e) ta = M::mma(frag_of<T>(vJ, e), frag_of<T>(dyr, e), ta);
+      }
+      if (J >= I) {
+#pragma unroll
+        for (int e = 0; e < NF; ++e) tb = M::mma(frag_of<T>(dyJ, e), frag_of<T>(vr, e), tb);
+        if (!pairwise) {
+          load_quarter<T, D>(qJ, qg, rJ, L, g);
+          const float* bp = sBeta + (16 * J + m) * Lay::LDB + g * (D / 4);
+#pragma unroll
+          for (int e = 0; e < NF; ++e) {
+            float tq[M::KPL];
+#pragma unroll
+            for (int u = 0; u < M::KPL; ++u) tq[u] = elem_of<T>(qJ, e * M::KPL + u) * exp_2(bp[e * M::KPL + u]);
+            tc = M::mma(M::pack(tq), kpf[e], tc);
+          }
+        } else {
+          // A[t][s] = sum_i q_ti k_si 2^{beta_ti - beta_si} pairwise
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int tr = 16 * J + 4 * g + r, sr = 16 * I + m;
+            float sum = 0.f;
+            if (sr <= tr && t0 + tr < L) {
+              const float* bt = sBeta + tr * Lay::LDB;
+              const float* bs = sBeta + sr * Lay::LDB;
+              for (int i = 0; i < D; ++i)
+                sum += to_f32(sQT[i * Lay::LDT + tr]) * to_f32(sKT[i * Lay::LDT + sr]) * exp_2(bt[i] - bs[i]);
+            }
+            tc[r] = sum;
+          }
+        }
+      }
+      // masks: s <= t
+      float va[4], vb[4], vc[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rowk = 16 * J + 4 * g + r, colt = 16 * I + m;   // (a): key row, query col
+        va[r] = rowk <= colt ? ta[r] : 0.f;
+        const int rowt = 16 * J + 4 * g + r, cols = 16 * I + m;   // (b), (c): query row, key col
+        vb[r] = cols <= rowt ? tb[r] : 0.f;
+        vc[r] = cols <= rowt ? tc[r] : 0.f;
+      }
+      store_pack<T, 4>(sDA + (16 * I + m) * Lay::LDT + 16 * J + 4 * g, va);
+      store_pack<T, 4>(sDAT + (16 * I + m) * Lay::LDT + 16 * J + 4 * g, vb);
+      store_pack<T, 4>(sAT + (16 * I + m) * Lay::LDT + 16 * J + 4 * g, vc);
+    }
+  }
+  __syncthreads();
+
+  // ---- phase C: wavefront w owns dims / value columns [w*D/4, (w+1)*D/4) ----
+  T* dqo = reinterpret_cast<T*>(a.dq) + (size_t)bh * L * D;
+  T* dko = reinterpret_cast<T*>(a.dk) + (size_t)bh * L * D;
+  T* dvo = reinterpret_cast<T*>(a.dv) + (size_t)bh * L * D;
+  float* dbo = a.dlog_g + (size_t)bh * L * D;
+  const float* dqa = a.ws_dqa + (size_t)bh * L * D;
+  const float* dka = a.ws_dka + (size_t)bh * L * D;
+  const float* dva = a.ws_dva + (size_t)bh * L * D;
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int ib = w * (D / 4) + 16 * it;     // first dim of this 16-row tile
+    uint4 Sr[QV], Gr[QV], GTr[QV];
+    load_quarter<T, D>(Sr, Sg, ib + m, D, g);     // S_c rows i (k = j)
+    load_quarter<T, D>(Gr, Gg, ib + m, D, g);     // G_{c+1} rows i (k = j)
+    load_quarter<T, D>(GTr, GTg, ib + m, D, g);   // G_{c+1}^T rows j (k = i)
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const int trow = t0 + 16 * tt + m;        // token of this lane's output column
+      uint4 dyr[QV], vr[QV], kr[QV];
+      load_quarter<T, D>(dyr, dyg, trow, L, g);
+      load_quarter<T, D>(vr, vg, trow, L, g);
+      load_quarter<T, D>(kr, kg, trow, L, g);
+      // inter-chunk parts
+      f32x4 qi = zero4(), ki = zero4(), vi = zero4();
+#pragma unroll
+      for (int e = 0; e < NF; ++e) {
+        qi = M::mma(frag_of<T>(Sr, e), frag_of<T>(dyr, e), qi);     // (S dO_t)_i
+        ki = M::mma(frag_of<T>(Gr, e), frag_of<T>(vr, e), ki);      // (G v_s)_i
+      }
+      // Kh_s = k_s * 2^{B - beta_s} as a fragment (rows s, k = i)
+      {
+        const float* bp = sBeta + (16 * tt + m) * Lay::LDB + g * (D / 4);
+#pragma unroll
+        for (int e = 0; e < NF; ++e) {
+          float tk[M::KPL];
+#pragma unroll
+          for (int u = 0; u < M::KPL; ++u) {
+            const int kk = e * M::KPL + u;
+            tk[u] = elem_of<T>(kr, kk) * exp_2(sBx[g * (D / 4) + kk] - bp[kk]);
+          }
+          vi = M::mma(frag_of<T>(GTr, e), M::pack(tk), vi);         // (G^T Kh_s)_j
+        }
+      }
+      // intra-chunk parts
+      f32x4 qa = zero4(), ka = zero4(), va = zero4();
+      {
+        const T* bO = sOT + (ib + m) * Lay::LDT + g * 16;            // dO^T rows j (k = t)
+        const T* bAT = sAT + (16 * tt + m) * Lay::LDT + g * 16;      // A^T rows s (k = t)
+#pragma unroll
+        for (int e = 0; e < 16 / M::KPL; ++e) va = M::mma(M::load(bO + e * M::KPL), M::load(bAT + e * M::KPL), va);
+      }
+      if (!pairwise) {
+        const T* aK = sKT + (ib + m) * Lay::LDT + g * 16;            // Kp^T rows i (k = s)
+        const T* bDA = sDA + (16 * tt + m) * Lay::LDT + g * 16;      // dA rows t (k = s)
+        const T* aQ = sQT + (ib + m) * Lay::LDT + g * 16;            // Qe^T rows i (k = t)
+        const T* bDAT = sDAT + (16 * tt + m) * Lay::LDT + g * 16;    // dA^T rows s (k = t)
+#pragma unroll
+        for (int e = 0; e < 16 / M::KPL; ++e) {
+          qa = M::mma(M::load(aK + e * M::KPL), M::load(bDA + e * M::KPL), qa);
+          ka = M::mma(M::load(aQ + e * M::KPL), M::load(bDAT + e * M::KPL), ka);
+        }
+      }
+      // epilogue for the 4 dims i = ib + 4g + r of token trow
+      if (trow < L) {
+        const int tl = 16 * tt + m;
+        const float* bt = sBeta + tl * Lay::LDB + ib + 4 * g;
+        float dqv[4], dkv[4], dvv[4], dbv[4];
+        const f32x4 aq = *reinterpret_cast<const f32x4*>(dqa + (size_t)trow * D + ib + 4 * g);
+        const f32x4 ak = *reinterpret_cast<const f32x4*>(dka + (size_t)trow * D + ib + 4 * g);
+        const f32x4 av = *reinterpret_cast<const f32x4*>(dva + (size_t)trow * D + ib + 4 * g);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = ib + 4 * g + r;
+          const float b = bt[r];
+          float qin = qa[r], kin = ka[r];
+          if (pairwise) {
+            // dq_ti += sum_s dA_ts k_si 2^{b_ti - b_si};  dk_ti += sum_u dA_ut q_ui 2^{b_ui - b_ti}
+            qin = 0.f;
+            kin = 0.f;
+            for (int s = 0; s <= tl; ++s)
+              qin += to_f32(sDA[tl * Lay::LDT + s]) * to_f32(sKT[i * Lay::LDT + s]) *
+                     exp_2(b - sBeta[s * Lay::LDB + i]);
+            for (int u = tl; u < 64; ++u)
+              kin += to_f32(sDAT[tl * Lay::LDT + u]) * to_f32(sQT[i * Lay::LDT + u]) *
+                     exp_2(sBeta[u * Lay::LDB + i] - b);
+          } else {
+            qin *= exp_2(b);
+            kin *= exp_2(-b);
+          }
+          const float dqg = exp_2(b) * qi[r] + qin;
+          const float dkg = exp_2(sBx[i] - b) * ki[r] + kin;
+          const float qv = to_f32(qg[(size_t)trow * D + i]);
+          const float kv = to_f32(kg[(size_t)trow * D + i]);
+          dbv[r] = qv * dqg - kv * dkg;
+          dqv[r] = dqg + aq[r];
+          dkv[r] = dkg + ak[r];
+          dvv[r] = vi[r] + va[r] + av[r];
+        }
+        store_pack<T, 4>(dqo + (size_t)trow * D + ib + 4 * g, dqv);
+        store_pack<T, 4>(dko + (size_t)trow * D + ib + 4 * g, dkv);
+        store_pack<T, 4>(dvo + (size_t)trow * D + ib + 4 * g, dvv);
+        *reinterpret_cast<f32x4*>(dbo + (size_t)trow * D + ib + 4 * g) = f32x4{dbv[0], dbv[1], dbv[2], dbv[3]};
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 6. dlog_g_t = sum_{u >= t} db_u (per (b, h, dim), in place)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dlogg_scan_kernel(float* dlg, int BH, int L) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= BH * D) return;
+  const int bh = idx / D, d = idx % D;
+  float* p = dlg + (size_t)bh * L * D + d;
+  float acc = 0.f;
+  int t = L - 1;
+  for (; t >= 7; t -= 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[(size_t)(t - u) * D];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      acc += v[u];
+      p[(size_t)(t - u) * D] = acc;
+    }
+  }
+  for (; t >= 0; --t) {
+    acc += p[(size_t)t * D];
+    p[(size_t)t * D] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 7. dmeta[h][i][d] = sum over batch rows and chunks of the partials (fixed order)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_dmeta_reduce_kernel(const float* part, float* out, int B, int H, int nc,
+                                                               int nmD) {
+  const int h = blockIdx.y;
+  const int o = blockIdx.x * 256 + threadIdx.x;
+  if (o >= nmD) return;
+  float s = 0.f;
+  for (int b = 0; b < B; ++b) {
+    const float* p = part + ((size_t)(b * H + h) * nc) * nmD + o;
+    for (int c = 0; c < nc; ++c) s += p[(size_t)c * nmD];
+  }
+  out[(size_t)h * nmD + o] = s;
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+namespace {
+
+struct WsPlan {
+  size_t states, dS, dST, dqa, dka, dva, Dt, dmu, total;
+};
+
+size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+
+WsPlan plan_ws(int elem, int BH, int L, int D, int n_meta) {
+  const size_t nc = (size_t)(L + C - 1) / C;
+  const size_t st = al256((size_t)BH * nc * D * D * elem);
+  const size_t fl = al256((size_t)BH * L * D * 4);
+  WsPlan p;
+  p.states = 0;
+  p.dS = p.states + st;
+  p.dST = p.dS + st;
+  p.dqa = p.dST + st;
+  p.dka = p.dqa + fl;
+  p.dva = p.dka + fl;
+  p.Dt = p.dva + fl;
+  p.dmu = p.Dt + al256((size_t)BH * L * 4);
+  p.total = p.dmu + al256((size_t)BH * nc * n_meta * D * 4);
+  return p;
+}
+
+template <typename K>
+hipError_t set_lds(K kernel, int bytes) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+template <typename T, int D, int DV>
+hipError_t launch_bwd_t(BwdArgs a, hipStream_t st) {
+  const int L = a.L, nc = (L + C - 1) / C;
+  const int groups = (a.BH + 7) / 8;
+  hipError_t e;
+  if (a.BH > 0 && L > 0) {
+    // 1. chunk-start states (forward kernel, states only)
+    FwdArgs f{};
+    f.q = a.q;
+    f.k = a.k;
+    f.v = a.v;
+    f.log_g = a.log_g;
+    f.meta = a.meta;
+    f.y = nullptr;
+    f.lse = nullptr;
+    f.y_anchor = nullptr;
+    f.state_out = nullptr;
+    f.states = a.ws_states;
+    f.BH = a.BH;
+    f.H = a.H;
+    f.L = L;
+    f.n_meta = a.n_meta;
+    f.window = a.window;
+    f.nsplit = D / fwd_value_slice(sizeof(T) == 2, D);
+    f.alpha = a.alpha;
+    f.scale_log2 = a.scale * kLog2e;
+    e = launch_fwd(f, sizeof(T) == 2, D, st);
+    if (e != hipSuccess) return e;
+    // 2. state gradients
+    hipLaunchKernelGGL((bwd_dstate_kernel<T, D, DV>), dim3(8 * groups * (D / DV)), dim3(256), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // 3. anchor, query side
+    typedef AqLayout<T, D> AQ;
+    static_assert(AQ::TOTAL <= 160 * 1024, "LDS");
+    if ((e = set_lds(&bwd_anchor_q_kernel<T, D>, AQ::TOTAL)) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_anchor_q_kernel<T, D>), dim3(8 * groups * nc), dim3(256), AQ::TOTAL, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // 4. anchor, key side
+    typedef AkLayout<T, D> AK;
+    static_assert(AK::TOTAL <= 160 * 1024, "LDS");
+    if ((e = set_lds(&bwd_anchor_k_kernel<T, D>, AK::TOTAL)) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_anchor_k_kernel<T, D>), dim3(8 * groups * nc), dim3(256), AK::TOTAL, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // 5. gated branch and outputs
+    typedef GateLayout<T, D> GL;
+    static_assert(GL::TOTAL <= 160 * 1024, "LDS");
+    if ((e = set_lds(&bwd_gate_kernel<T, D>, GL::TOTAL)) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_gate_kernel<T, D>), dim3(8 * groups * nc), dim3(256), GL::TOTAL, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // 6. reverse cumulative sum of the log-gate gradient
+    hipLaunchKernelGGL((bwd_dlogg_scan_kernel<D>), dim3((a.BH * D + 255) / 256), dim3(256), 0, st, a.dlog_g, a.BH, L);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // 7. sink keys (written even when B*L == 0: then zero)
+  if (a.n_meta > 0 && a.H > 0) {
+    const int nmD = a.n_meta * D;
+    if (a.BH > 0 && L > 0) {
+      hipLaunchKernelGGL(bwd_dmeta_reduce_kernel, dim3((nmD + 255) / 256, a.H), dim3(256), 0, st, a.ws_dmu, a.dmeta,
+                         a.B, a.H, nc, nmD);
+    } else {
+      hipLaunchKernelGGL(bwd_dmeta_reduce_kernel, dim3((nmD + 255) / 256, a.H), dim3(256), 0, st, a.ws_dmu, a.dmeta,
+                         0, a.H, 0, nmD);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int dtype_bf16, int BH, int L, int D, int n_meta) {
+  if (BH == 0 || L == 0) return 0;
+  return plan_ws(dtype_bf16 ? 2 : 4, BH, L, D, n_meta).total;
+}
+
+hipError_t launch_bwd(const BwdArgs& in, int dtype_bf16, int D, hipStream_t st) {
+  BwdArgs a = in;
+  if (a.BH > 0 && a.L > 0) {
+    const WsPlan p = plan_ws(dtype_bf16 ? 2 : 4, a.BH, a.L, D, a.n_meta);
+    char* base = static_cast<char*>(a.workspace);
+    a.ws_states = base + p.states;
+    a.ws_dS = base + p.dS;
+    a.ws_dST = base + p.dST;
+    a.ws_dqa = reinterpret_cast<float*>(base + p.dqa);
+    a.ws_dka = reinterpret_cast<float*>(base + p.dka);
+    a.ws_dva = reinterpret_cast<float*>(base + p.dva);
+    a.ws_D = reinterpret_cast<float*>(base + p.Dt);
+    a.ws_dmu = reinterpret_cast<float*>(base + p.dmu);
+  }
+  if (dtype_bf16 && D == 128) return launch_bwd_t<bf16, 128, 64>(a, st);
+  if (dtype_bf16 && D == 64) return launch_bwd_t<bf16, 64, 64>(a, st);
+  if (!dtype_bf16 && D == 64) return launch_bwd_t<float, 64, 32>(a, st);
+  return hipErrorInvalidValue;
+}
 
 }  // namespace lizard

@@ -33,6 +33,13 @@ template <> __device__ __forceinline__ float from_f32<float>(float x) { return x
 // float -> bf16 conversion rounds to nearest even (gfx950 v_cvt_pk_bf16_f32).
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }
 
+// One token's log-gate in log2 units for the prefix sums.  Gates below
+// 2^-100 are taken as 2^-100: any product through such a gate is below 1e-30
+// and indistinguishable from a full reset, while the prefix stays small
+// enough that differences of prefixes keep float precision.
+constexpr float kMinLog2Gate = -100.0f;
+__device__ __forceinline__ float log2_gate(float log_g) { return fmaxf(log_g * 1.4426950408889634f, kMinLog2Gate); }
+
 // exp of a natural-log exponent via the hardware base-2 exponential.
 __device__ __forceinline__ float exp_e(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 __device__ __forceinline__ float exp_2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -239,7 +239,7 @@ __global__ __launch_bounds__(256, 1) void lizard_fwd_kernel(FwdArgs a) {
       float run = 0.f;
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
-        run = fmaf(lgA[rr][dd], kLog2e, run);
+        run += log2_gate(lgA[rr][dd]);
         loc[rr][dd] = run;
       }
       tot[dd] = run;
@@ -268,6 +268,17 @@ __global__ __launch_bounds__(256, 1) void lizard_fwd_kernel(FwdArgs a) {
         const float sv[4] = {acc[rt][ct][0], acc[rt][ct][1], acc[rt][ct][2], acc[rt][ct][3]};
         store_pack<T, 4>(sSt + (16 * ct + m) * Lay::LDST + w * (D / 4) + 16 * rt + 4 * g, sv);
       }
+    if (a.states) {
+      // chunk-start state for the backward pass: S_c[i][j], row-major
+      T* sg = reinterpret_cast<T*>(a.states) + ((size_t)bh * nc + c) * D * D + j0;
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            sg[(size_t)(w * (D / 4) + 16 * rt + 4 * g + r) * D + 16 * ct + m] = from_f32<T>(acc[rt][ct][r]);
+    }
     __syncthreads();
 
     // chunk prefix beta = offset of this wavefront's rows + loc; B = chunk total
@@ -479,11 +490,13 @@ __global__ __launch_bounds__(256, 1) void lizard_fwd_kernel(FwdArgs a) {
         }
       }
     };
-    switch (w) {
-      case 0: phase_b(std::integral_constant<int, 0>{}); break;
-      case 1: phase_b(std::integral_constant<int, 1>{}); break;
-      case 2: phase_b(std::integral_constant<int, 2>{}); break;
-      default: phase_b(std::integral_constant<int, 3>{}); break;
+    if (a.y) {  // (no outputs: the states-only pass of the backward)
+      switch (w) {
+        case 0: phase_b(std::integral_constant<int, 0>{}); break;
+        case 1: phase_b(std::integral_constant<int, 1>{}); break;
+        case 2: phase_b(std::integral_constant<int, 2>{}); break;
+        default: phase_b(std::integral_constant<int, 3>{}); break;
+      }
     }
 
     // ---- state carry: S = 2^B * S + Kh^T V over this chunk's keys ----

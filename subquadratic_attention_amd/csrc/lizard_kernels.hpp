@@ -17,6 +17,7 @@ struct FwdArgs {
   float* lse;           // nullable
   void* y_anchor;       // nullable
   float* state_out;     // nullable
+  void* states;         // nullable: chunk-start states S_c, [BH, nc, D, D] element type, row-major
   int BH, H, L, n_meta, window, nsplit;
   float alpha;
   float scale_log2;     // softmax scale * log2(e)
@@ -51,8 +52,16 @@ struct BwdArgs {
   void* dv;
   float* dlog_g;
   float* dmeta;          // [H, n_meta, D]
-  void* states;          // workspace: chunk-start states [BH, nc, D, D] (element type)
-  float* dmeta_part;     // workspace: per-(b,h) sink-key gradients [BH, n_meta, D]
+  void* workspace;
+  // carved from the workspace by launch_bwd
+  void* ws_states;       // S_c          [BH, nc, D, D] element type
+  void* ws_dS;           // G_{c+1}      [BH, nc, D, D] element type
+  void* ws_dST;          // G_{c+1}^T    [BH, nc, D, D] element type
+  float* ws_dqa;         // anchor dq    [BH, L, D]
+  float* ws_dka;         // anchor dk    [BH, L, D]
+  float* ws_dva;         // anchor dv    [BH, L, D]
+  float* ws_D;           // D_t          [BH, L]
+  float* ws_dmu;         // sink-key partials [BH, nc, n_meta, D]
   int B, BH, H, L, n_meta, window;
   float alpha;
   float scale;           // softmax scale (natural units)
