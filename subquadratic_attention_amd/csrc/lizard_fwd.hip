@@ -25,18 +25,28 @@
 // with a larger span (gates near zero) compute the intra scores pairwise in
 // fp32 from 2^{beta_t - beta_s}.  Nothing ever divides by a gate product.
 //
-// Work decomposition: one workgroup of 8 wavefronts (2 per SIMD) per
-// (batch, head, slice of DV value columns).  The workgroup walks the chunks
-// in order and keeps its slice of the float32 state in MFMA accumulators,
-// 16 state rows per wavefront.  Query block I (16 rows) of a chunk belongs
-// to the wavefront pair (I, I+4): each computes half of the 96 window-key
-// logits (and the intra scores among them), the pair exchanges softmax
-// maxima and sums through LDS, then each produces half of the value
-// columns.  Keys and values of the previous chunk stay in an LDS ring for
-// the window.  All products are computed transposed (keys or value columns
-// on the MFMA rows, the block's 16 queries on its columns), so each lane
-// ends with 4 consecutive keys / columns of one query: packed LDS and global
-// writes, and softmax reductions across 4 lane groups only.
+// Work decomposition: one workgroup of 8 wavefronts per (batch, head, slice
+// of DV value columns), walking the chunks in order.  Wavefronts I and I+4
+// share a SIMD and split query block I (16 rows) of every chunk by kind of
+// work: wavefront I ("softmax") computes the window logits, the softmax and
+// the unnormalised weights P; wavefront I+4 ("gate") computes the gated
+// intra-chunk scores, the readout of the state, the anchor product V^T P^T
+// and the output, and owns D/4 rows of the float32 state in MFMA
+// accumulators.  So the VALU-heavy and the MFMA-heavy half of each block run
+// side by side on one SIMD.  Two workgroup barriers per chunk c:
+//
+//   interval 1: softmax(c) | gated scores, readout, state carry (c);
+//               then every wavefront: prefix partial sums of chunk c+1
+//   interval 2: gate wavefronts: V^T P^T and the output of chunk c;
+//               every wavefront: decay factors and operands of chunk c+1
+//               into LDS, global loads of chunk c+2
+//
+// Keys of the last two chunks stay in an LDS ring for the window, values of
+// the last three (the output of chunk c reads two while chunk c+1's are
+// written).  All products are computed transposed (keys or value columns on
+// the MFMA rows, the block's 16 queries on its columns), so each lane ends
+// with 4 consecutive keys / columns of one query: packed LDS and global
+// writes and softmax reductions across 4 lane groups only.
 #include <type_traits>
 
 #include "lizard_common.hpp"
@@ -46,28 +56,35 @@ namespace lizard {
 
 template <typename T, int D, int DV>
 struct FwdLayout {
-  static constexpr int C = 64;
   static constexpr int PAD = 16 / sizeof(T);
-  static constexpr int LDK = D + PAD;       // sK ring [128][LDK], sKp [64][LDK]
-  static constexpr int LDVT = 128 + PAD;    // sVt ring [DV][LDVT]
+  static constexpr int LDK = D + PAD;       // sK ring [128][LDK]; sKp, sQe [64][LDK]; sMeta [16][LDK]
+  static constexpr int LDVT = 192 + PAD;    // sVt ring of 3 chunk slots [DV][LDVT]
   static constexpr int LDKH = 64 + PAD;     // sKhT [D][LDKH]
   static constexpr int LDST = D + PAD;      // sSt [DV][LDST]
-  static constexpr int LDE = D + 4;         // pairwise path: beta [64][LDE] float in the sQ/sQe region
-  static constexpr int LDSTG = 96 + PAD;    // staging per query block [16][LDSTG]
+  static constexpr int LDP = 96 + PAD;      // window weights P, per query block [16][LDP]
+  static constexpr int LDA = 64 + PAD;      // bf16: intra scores A, per query block [16][LDA]
+  static constexpr int LDE = D + 4;         // wide-span chunks: beta [64][LDE] float over sKp, sQe
+  static constexpr bool STAGE_A = sizeof(T) == 2;
   static constexpr int a16(int x) { return (x + 15) / 16 * 16; }
   static constexpr int OFF_K = 0;
   static constexpr int OFF_VT = OFF_K + a16(128 * LDK * (int)sizeof(T));
   static constexpr int OFF_KP = OFF_VT + a16(DV * LDVT * (int)sizeof(T));
-  static constexpr int OFF_KHT = OFF_KP + a16(64 * LDK * (int)sizeof(T));
+  static constexpr int OFF_QE = OFF_KP + a16(64 * LDK * (int)sizeof(T));
+  static constexpr int OFF_KHT = OFF_QE + a16(64 * LDK * (int)sizeof(T));
   static constexpr int OFF_ST = OFF_KHT + a16(D * LDKH * (int)sizeof(T));
-  static constexpr int OFF_Q = OFF_ST + a16(DV * LDST * (int)sizeof(T));      // raw q [64][LDK]
-  static constexpr int OFF_QE = OFF_Q + a16(64 * LDK * (int)sizeof(T));       // q * 2^beta [64][LDK]
-  static constexpr int QQ_END = OFF_QE + a16(64 * LDK * (int)sizeof(T));
-  static constexpr int OFF_TOT = (QQ_END > OFF_Q + a16(64 * LDE * 4) ? QQ_END : OFF_Q + a16(64 * LDE * 4));
-  static constexpr int OFF_BEXP = OFF_TOT + a16(8 * D * 4);
-  static constexpr int OFF_STAT = OFF_BEXP + a16(D * 4);
-  static constexpr int OFF_STG = OFF_STAT + a16(8 * 16 * 2 * 4);
-  static constexpr int TOTAL = OFF_STG + a16(4 * 16 * LDSTG * (int)sizeof(T));
+  static constexpr int OFF_P = OFF_ST + a16(DV * LDST * (int)sizeof(T));
+  static constexpr int OFF_A = OFF_P + a16(4 * 16 * LDP * (int)sizeof(T));
+  static constexpr int A_BYTES = STAGE_A ? a16(4 * 16 * LDA * (int)sizeof(T)) : 0;
+  static constexpr int OFF_TOT = OFF_A + A_BYTES;
+  // wide-span totals: over the A staging when there is one (both are free in
+  // the operand step), else a region of their own
+  static constexpr int OFF_TOTC = STAGE_A ? OFF_A : OFF_TOT + a16(8 * D * 4);
+  static constexpr int OFF_BEXP = OFF_TOT + a16(8 * D * 4) + (STAGE_A ? 0 : a16(8 * D * 4));
+  static constexpr int OFF_SC = OFF_BEXP + a16(D * 4);          // [2][64]: alpha/den, 1/den
+  static constexpr int OFF_META = OFF_SC + a16(2 * 64 * 4);
+  static constexpr int TOTAL = OFF_META + a16(16 * LDK * (int)sizeof(T));
+  static_assert(64 * LDE * 4 <= OFF_KHT - OFF_KP, "beta fits over sKp and sQe");
+  static_assert(!STAGE_A || 8 * D * 4 <= A_BYTES, "wide-span totals fit over the A staging");
 };
 
 // Raw 16-byte vectors -> MFMA fragment e of a lane's contiguous k-quarter.
@@ -90,6 +107,27 @@ template <> __device__ __forceinline__ float elem_f32<float>(const uint4* raw, i
   return frag_at<float>(raw, i);
 }
 
+// float: o += V^T A^T over one 16-key tile, with the B operand (A^T[s][t]
+// for keys 4g..4g+3 of the tile, query m) straight from the registers of the
+// MFMA that produced it: in step r, lane group g supplies key 4g + r, so the
+// contraction pairs the same key on both operands.  vt points at
+// V^T[j = 16ct + m][first key of the tile + 4g].  (bfloat16 scores are
+// staged through LDS instead and use the 16x16x32 product.)
+__device__ __forceinline__ f32x4 mma_tile_regs_f32(const float* vt, f32x4 ai, f32x4 o) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(vt);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) o = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], ai[r], o, 0, 0, 0);
+  return o;
+}
+
+// An int passed through an empty asm: values derived from it are computed
+// where they are used instead of being hoisted out of the chunk loop (which
+// would hold them in registers across the whole loop).
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // Largest chunk decay span (log2 units) taken by the factorised path: 2^92
 // leaves a factor 2^36 of headroom below the float / bfloat16 maximum.
 constexpr float kMaxSpanLog2 = 92.0f;
@@ -100,30 +138,31 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
   typedef Mfma<T> M;
   typedef typename M::frag frag;
   constexpr int C = 64;
-  constexpr int DPL = D / 64;                 // phase-A dims per lane
+  constexpr int DPL = D / 64;                 // prep dims per lane; state row tiles per gate wavefront
   constexpr int EPV = 16 / sizeof(T);         // elements per 16-byte vector
   constexpr int QV = D / 4 / EPV;             // 16-byte vectors in a lane's k-quarter of a row
   constexpr int NF = D / 4 / M::KPL;          // MFMA steps over a D contraction
   constexpr int NCT = DV / 16;                // value column tiles
-  constexpr int NCH = NCT / 2;                // value column tiles per wavefront of a pair
   constexpr int VC = 4 / sizeof(T);           // value columns per thread in the value load
   constexpr int VRW = DV / VC;                // threads across a value row
   constexpr int VR = 64 * VRW / 512;          // value rows per thread
-  static_assert(VR == 4 && NCH >= 1, "shape");
+  static_assert(VR == 4, "shape");
 
   extern __shared__ __align__(16) unsigned char smem[];
   T* sK = reinterpret_cast<T*>(smem + Lay::OFF_K);
   T* sVt = reinterpret_cast<T*>(smem + Lay::OFF_VT);
   T* sKp = reinterpret_cast<T*>(smem + Lay::OFF_KP);
+  T* sQe = reinterpret_cast<T*>(smem + Lay::OFF_QE);
+  float* sBeta = reinterpret_cast<float*>(smem + Lay::OFF_KP);   // wide-span chunks only
   T* sKhT = reinterpret_cast<T*>(smem + Lay::OFF_KHT);
   T* sSt = reinterpret_cast<T*>(smem + Lay::OFF_ST);
-  T* sQ = reinterpret_cast<T*>(smem + Lay::OFF_Q);
-  T* sQe = reinterpret_cast<T*>(smem + Lay::OFF_QE);
-  float* sBeta = reinterpret_cast<float*>(smem + Lay::OFF_Q);   // pairwise path only (aliases sQ, sQe)
+  T* sP = reinterpret_cast<T*>(smem + Lay::OFF_P);
   float* sTot = reinterpret_cast<float*>(smem + Lay::OFF_TOT);
+  T* sA = reinterpret_cast<T*>(smem + Lay::OFF_A);                // bfloat16 only
+  float* sTotC = reinterpret_cast<float*>(smem + Lay::OFF_TOTC);  // wide-span chunks only
   float* sBexp = reinterpret_cast<float*>(smem + Lay::OFF_BEXP);
-  float* sStat = reinterpret_cast<float*>(smem + Lay::OFF_STAT);
-  T* sStgAll = reinterpret_cast<T*>(smem + Lay::OFF_STG);
+  float* sSc = reinterpret_cast<float*>(smem + Lay::OFF_SC);
+  T* sMeta = reinterpret_cast<T*>(smem + Lay::OFF_META);
 
   // ---- block -> (b*h, value slice); siblings of one head share an XCD ----
   const int x = blockIdx.x;
@@ -137,12 +176,12 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
   const int L = a.L;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;      // wavefront 0..7: phase-A rows 8w.., state rows 16w..
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wavefront 0..7: prep rows 8w..8w+7
   const int l = tid & 63;
-  const int m = l & 15;        // MFMA row / column within a tile
-  const int g = l >> 4;        // MFMA lane group
+  const int m_lane = l & 15;   // MFMA row / column within a tile
+  const int g_lane = l >> 4;   // MFMA lane group
+  const bool gate = w >= 4;    // wavefronts 4..7: gated branch and state
   const int I = w & 3;         // query block of this wavefront
-  const bool srow = w < D / 16;   // owns state rows 16w..16w+15
   const int vj = tid % VRW;    // value-load role: columns VC*vj.., rows VR*vs..
   const int vs = tid / VRW;
 
@@ -153,37 +192,43 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
   T* __restrict__ yg = reinterpret_cast<T*>(a.y) + (size_t)bh * L * D + j0;
   T* __restrict__ yag = a.y_anchor ? reinterpret_cast<T*>(a.y_anchor) + (size_t)bh * L * D + j0 : nullptr;
   float* __restrict__ lseg = (a.lse && split == 0) ? a.lse + (size_t)bh * L : nullptr;
-  T* sStg = sStgAll + I * 16 * Lay::LDSTG;
 
   // ---- zero the key/value rings (the window of chunk 0 reads "chunk -1") ----
   for (int i = tid; i < 128 * Lay::LDK; i += 512) sK[i] = from_f32<T>(0.f);
   for (int i = tid; i < DV * Lay::LDVT; i += 512) sVt[i] = from_f32<T>(0.f);
-
-  // ---- sink keys as A-operand fragments (rows = sinks), resident throughout ----
-  frag muf[NF];
-  {
-    const bool live = m < a.n_meta;
-    const T* mp = reinterpret_cast<const T*>(a.meta) + ((size_t)h * a.n_meta + (live ? m : 0)) * D + g * (D / 4);
-    uint4 raw[QV];
-#pragma unroll
-    for (int e = 0; e < QV; ++e) raw[e] = live ? ld16(mp + e * EPV) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int e = 0; e < NF; ++e) muf[e] = frag_at<T>(raw, e);
+  // ---- sink keys (rows >= n_meta zero), resident in LDS throughout ----
+  for (int i = tid; i < 16 * D; i += 512) {
+    const int r = i / D, cidx = i % D;
+    sMeta[r * Lay::LDK + cidx] =
+        r < a.n_meta ? reinterpret_cast<const T*>(a.meta)[((size_t)h * a.n_meta + r) * D + cidx] : from_f32<T>(0.f);
   }
 
-  // ---- state slice in accumulators: rows 16w + 4g + r, cols 16ct + m (w < D/16) ----
-  f32x4 acc[NCT];
+  // ---- gate wavefronts: state rows 16*(DPL*I + rt) + 4g + r, cols 16ct + m ----
+  f32x4 acc[DPL][NCT];
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) acc[ct] = zero4();
+  for (int rt = 0; rt < DPL; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[rt][ct] = zero4();
 
-  // ---- per-chunk global data (prefetched one chunk ahead, kept as raw bits) ----
-  float lgA[8][DPL];    // phase A: rows 8w+rr, dims DPL*l + dd
+  // ---- per-chunk global data (prefetched ahead, kept as raw bits) ----
+  float lgA[8][DPL];    // prep rows 8w+rr, dims DPL*l + dd
+  float loc[8][DPL];    // their prefix inside the wavefront's 8 rows
   uint32_t kA[8];       // the same rows' keys: DPL elements packed in 32 bits
   uint32_t qA[8];       // ... and queries
   uint32_t vA[VR];      // values: rows VR*vs + rr, columns VC*vj.. packed in 32 bits
+  // One register array for two roles (a wavefront only ever has one, and the
+  // compiler would otherwise keep both live across the chunk loop):
+  // softmax wavefronts: raw q of row 16I + m, the lane's k-quarter (QV vectors);
+  // gate wavefronts: the gated output of the block, carried over a barrier (NCT tiles).
+  constexpr int RQ = QV > NCT ? QV : NCT;
+  uint4 rq[RQ];
+  uint4* qraw = rq;
 
   auto load_rows = [&](int c, bool full) __attribute__((always_inline)) {
     const int t0 = c * C;
+    const int tid = opaque(threadIdx.x);
+    const int l = tid & 63;
+    const int vj = tid % VRW, vs = tid / VRW;
     {
       const int tb = t0 + 8 * w;
       const float* lp = lgg + (size_t)tb * D + DPL * l;
@@ -231,105 +276,98 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
     if ((c + 1) * C <= L) load_rows(c, true);
     else load_rows(c, false);
   };
+  auto load_q = [&](int c) __attribute__((always_inline)) {
+    const int l = opaque(threadIdx.x) & 63;
+    const int tq = c * C + 16 * I + (l & 15);
+    const bool ok = tq < L;
+    const T* qp = qg + (size_t)(ok ? tq : 0) * D + (l >> 4) * (D / 4);
+#pragma unroll
+    for (int e = 0; e < QV; ++e) qraw[e] = ok ? ld16(qp + e * EPV) : make_uint4(0, 0, 0, 0);
+  };
   // element dd of a packed 32-bit word, as float
   auto elem32 = [&](uint32_t u, int dd) __attribute__((always_inline)) -> float {
     if constexpr (sizeof(T) == 4) return __builtin_bit_cast(float, u);
     else return __builtin_bit_cast(float, dd == 0 ? (u << 16) : (u & 0xffff0000u));
   };
 
-  const int nc = (L + C - 1) / C;
-  if (nc > 0) load_chunk(0);
-  __syncthreads();
-
-  for (int c = 0; c < nc; ++c) {
-    const int t0 = c * C;
-    const int cur = (c & 1) * 64;       // ring half of this chunk
-    const int prv = 64 - cur;           // ring half of the previous chunk
-
-    // ================= phase A: log2-gate prefix and operand staging ========
-    float loc[8][DPL];                  // prefix inside this wavefront's 8 rows
+  // ---- prefix sums inside this wavefront's 8 rows (natural-log units; exact
+  // for the factorised path, where no single gate is small enough for the
+  // 2^-100 floor of the wide-span path) ----
+  auto prefix_part = [&]() __attribute__((always_inline)) {
+    const int l = opaque(threadIdx.x) & 63;
     float tot[DPL];
 #pragma unroll
     for (int dd = 0; dd < DPL; ++dd) {
       float run = 0.f;
 #pragma unroll
       for (int rr = 0; rr < 8; ++rr) {
-        run += log2_gate(lgA[rr][dd]);
+        run += lgA[rr][dd];
         loc[rr][dd] = run;
       }
       tot[dd] = run;
     }
     if constexpr (DPL == 2) *reinterpret_cast<float2*>(sTot + w * D + 2 * l) = make_float2(tot[0], tot[1]);
     else sTot[w * D + l] = tot[0];
-#pragma unroll
-    for (int rr = 0; rr < 8; ++rr) {
-      T* krp = sK + (cur + 8 * w + rr) * Lay::LDK + DPL * l;
-      T* qrp = sQ + (8 * w + rr) * Lay::LDK + DPL * l;
-      if constexpr (DPL * sizeof(T) == 4) {
-        *reinterpret_cast<uint32_t*>(krp) = kA[rr];
-        *reinterpret_cast<uint32_t*>(qrp) = qA[rr];
-      } else {
-        krp[0] = from_f32<T>(elem32(kA[rr], 0));
-        qrp[0] = from_f32<T>(elem32(qA[rr], 0));
-      }
-    }
-    // values, transposed into the ring: sVt[j][cur + s], 4 tokens per write
-#pragma unroll
-    for (int cc = 0; cc < VC; ++cc) {
-      float vv[VR];
-#pragma unroll
-      for (int rr = 0; rr < VR; ++rr) vv[rr] = elem32(vA[rr], cc);
-      store_pack<T, 4>(sVt + (VC * vj + cc) * Lay::LDVT + cur + VR * vs, vv);
-    }
-    // S_c (rounded to the element type) for the readout: sSt[j][i], 4 rows i per write
-    if (srow) {
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const float sv[4] = {acc[ct][0], acc[ct][1], acc[ct][2], acc[ct][3]};
-        store_pack<T, 4>(sSt + (16 * ct + m) * Lay::LDST + 16 * w + 4 * g, sv);
-      }
-    }
-    if (STATES && srow) {
-      // chunk-start state for the backward pass: S_c[i][j], row-major
-      T* sg = reinterpret_cast<T*>(a.states) + ((size_t)bh * nc + c) * D * D + j0;
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sg[(size_t)(16 * w + 4 * g + r) * D + 16 * ct + m] = from_f32<T>(acc[ct][r]);
-    }
-    __syncthreads();
+  };
 
-    // chunk prefix beta = offset of this wavefront's rows + loc; B = chunk total
-    float Bt[DPL], off[DPL];
-    bool wide = false;
+  // offset of this wavefront's rows (sum of the earlier wavefronts' totals)
+  // and the chunk total, from the 8 partial totals in tp
+  auto offsets = [&](const float* tp, float* off, float* Bt) __attribute__((always_inline)) {
+    const int l = opaque(threadIdx.x) & 63;
+    float tv[8][DPL];
+#pragma unroll
+    for (int ww = 0; ww < 8; ++ww) {
+      if constexpr (DPL == 2) {
+        const float2 f = *reinterpret_cast<const float2*>(tp + ww * D + 2 * l);
+        tv[ww][0] = f.x;
+        tv[ww][1] = f.y;
+      } else {
+        tv[ww][0] = tp[ww * D + l];
+      }
+    }
 #pragma unroll
     for (int dd = 0; dd < DPL; ++dd) {
-      const int i = DPL * l + dd;
-      float o = 0.f, b = 0.f;
+      float run = 0.f, o = 0.f;
 #pragma unroll
       for (int ww = 0; ww < 8; ++ww) {
-        const float tv = sTot[ww * D + i];
-        o += ww < w ? tv : 0.f;
-        b += tv;
+        o = ww == w ? run : o;
+        run += tv[ww][dd];
       }
       off[dd] = o;
-      Bt[dd] = b;
-      wide |= -b > kMaxSpanLog2;
+      Bt[dd] = run;
     }
+  };
+
+  // ---- chunk cc's operands into LDS (decay factors, Qe, Kp, Kh, keys,
+  // values, the chunk-start state); returns whether it takes the pairwise path
+  auto operand_part = [&](int cc) __attribute__((always_inline)) -> bool {
+    const int kc = (cc & 1) * 64;       // key ring half
+    const int vc = (cc % 3) * 64;       // value ring slot
+    const int tid = opaque(threadIdx.x);
+    const int l = tid & 63, m_lane = l & 15, g_lane = l >> 4;
+    const int vj = tid % VRW, vs = tid / VRW;
+    float Bt[DPL], off[DPL];
+    offsets(sTot, off, Bt);
+    bool wide = false;
+#pragma unroll
+    for (int dd = 0; dd < DPL; ++dd) wide |= -Bt[dd] * kLog2e > kMaxSpanLog2;
     // every wavefront covers all D dims, so this ballot is the chunk's decision
     const bool pairwise = __any(wide);
     float kh[DPL][8];
+    float eB[DPL];
     if (!pairwise) {
-      float eB[DPL];
 #pragma unroll
-      for (int dd = 0; dd < DPL; ++dd) eB[dd] = exp_2(Bt[dd]);
+      for (int dd = 0; dd < DPL; ++dd) {
+        eB[dd] = exp_2(Bt[dd] * kLog2e);
+        off[dd] *= kLog2e;
+      }
 #pragma unroll
       for (int rr = 0; rr < 8; ++rr) {
         const int s = 8 * w + rr;
         float qe[DPL], kp[DPL];
 #pragma unroll
         for (int dd = 0; dd < DPL; ++dd) {
-          const float beta = off[dd] + loc[rr][dd];
+          const float beta = fmaf(loc[rr][dd], kLog2e, off[dd]);
           kp[dd] = elem32(kA[rr], dd) * exp_2(-beta);
           kh[dd][rr] = kp[dd] * eB[dd];
           qe[dd] = elem32(qA[rr], dd) * exp_2(beta);
@@ -343,12 +381,31 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
         }
       }
     } else {
+      // wide span: log2 prefixes with every gate floored at 2^-100, so that
+      // differences of prefixes keep float precision (a uniform branch)
+      float locc[8][DPL], totc[DPL];
+#pragma unroll
+      for (int dd = 0; dd < DPL; ++dd) {
+        float run = 0.f;
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+          run += log2_gate(lgA[rr][dd]);
+          locc[rr][dd] = run;
+        }
+        totc[dd] = run;
+      }
+#pragma unroll
+      for (int dd = 0; dd < DPL; ++dd) sTotC[w * D + DPL * l + dd] = totc[dd];
+      __syncthreads();
+      offsets(sTotC, off, Bt);
+#pragma unroll
+      for (int dd = 0; dd < DPL; ++dd) eB[dd] = exp_2(Bt[dd]);
 #pragma unroll
       for (int rr = 0; rr < 8; ++rr) {
         const int s = 8 * w + rr;
 #pragma unroll
         for (int dd = 0; dd < DPL; ++dd) {
-          const float beta = off[dd] + loc[rr][dd];
+          const float beta = off[dd] + locc[rr][dd];
           kh[dd][rr] = elem32(kA[rr], dd) * exp_2(Bt[dd] - beta);
           sBeta[s * Lay::LDE + DPL * l + dd] = beta;
         }
@@ -357,30 +414,207 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int dd = 0; dd < DPL; ++dd) {
       store_pack<T, 8>(sKhT + (DPL * l + dd) * Lay::LDKH + 8 * w, kh[dd]);
-      if (w == 0) sBexp[DPL * l + dd] = exp_2(Bt[dd]);
+      if (w == 0) sBexp[DPL * l + dd] = eB[dd];
     }
-    if (c + 1 < nc) load_chunk(c + 1);
-    __syncthreads();
+    // raw keys into the ring
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+      T* krp = sK + (kc + 8 * w + rr) * Lay::LDK + DPL * l;
+      if constexpr (DPL * sizeof(T) == 4) *reinterpret_cast<uint32_t*>(krp) = kA[rr];
+      else krp[0] = from_f32<T>(elem32(kA[rr], 0));
+    }
+    // values, transposed into their ring slot: sVt[j][vc + s], 4 tokens per write
+    if constexpr (sizeof(T) == 2) {
+      // columns 2vj and 2vj+1 of 4 consecutive rows: regroup the 16-bit halves
+      const uint2 lo = make_uint2(__builtin_amdgcn_perm(vA[1], vA[0], 0x05040100u),
+                                  __builtin_amdgcn_perm(vA[3], vA[2], 0x05040100u));
+      const uint2 hi = make_uint2(__builtin_amdgcn_perm(vA[1], vA[0], 0x07060302u),
+                                  __builtin_amdgcn_perm(vA[3], vA[2], 0x07060302u));
+      *reinterpret_cast<uint2*>(sVt + (2 * vj) * Lay::LDVT + vc + VR * vs) = lo;
+      *reinterpret_cast<uint2*>(sVt + (2 * vj + 1) * Lay::LDVT + vc + VR * vs) = hi;
+    } else {
+      *reinterpret_cast<uint4*>(sVt + vj * Lay::LDVT + vc + VR * vs) = make_uint4(vA[0], vA[1], vA[2], vA[3]);
+    }
+    if (gate) {
+      if constexpr (!STATES) {
+        // S_cc (rounded to the element type) for the readout: sSt[j][i], 4 rows i per write
+#pragma unroll
+        for (int rt = 0; rt < DPL; ++rt)
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) {
+            const float sv[4] = {acc[rt][ct][0], acc[rt][ct][1], acc[rt][ct][2], acc[rt][ct][3]};
+            store_pack<T, 4>(sSt + (16 * ct + m_lane) * Lay::LDST + 16 * (DPL * I + rt) + 4 * g_lane, sv);
+          }
+      } else {
+        // chunk-start state for the backward pass: S_cc[i][j], row-major
+        const int ncs = (L + C - 1) / C;
+        T* sg = reinterpret_cast<T*>(a.states) + ((size_t)bh * ncs + cc) * D * D + j0;
+#pragma unroll
+        for (int rt = 0; rt < DPL; ++rt)
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              sg[(size_t)(16 * (DPL * I + rt) + 4 * g_lane + r) * D + 16 * ct + m_lane] = from_f32<T>(acc[rt][ct][r]);
+      }
+    }
+    return pairwise;
+  };
 
-    // ================= phase B: the pair (I, I+4) works on query block I =====
-    auto phase_b = [&](auto Ic, auto Hc) __attribute__((always_inline)) {
-      constexpr int QB = decltype(Ic)::value;         // query block
-      constexpr int HF = decltype(Hc)::value;         // half
+  // ---- state carry over chunk c: S = 2^B * S + Kh^T V (gate wavefronts) ----
+  auto carry = [&](int vc, int m, int g) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rt = 0; rt < DPL; ++rt) {
+      const int ib = 16 * (DPL * I + rt);
+      float dec[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dec[r] = sBexp[ib + 4 * g + r];
+      const T* kp = sKhT + (ib + m) * Lay::LDKH + g * 16;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        f32x4 s = acc[rt][ct];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[r] *= dec[r];
+        const T* vp = sVt + (16 * ct + m) * Lay::LDVT + vc + g * 16;
+#pragma unroll
+        for (int e = 0; e < 16 / M::KPL; ++e) s = M::mma(M::load(kp + e * M::KPL), M::load(vp + e * M::KPL), s);
+        acc[rt][ct] = s;
+      }
+    }
+  };
+
+  const int nc = (L + C - 1) / C;
+  bool pw = false;                      // pairwise path for the chunk about to be processed
+  if (nc > 0) {
+    load_chunk(0);
+    if (!STATES && !gate) load_q(0);
+    prefix_part();
+  }
+  __syncthreads();
+  if (nc > 0) {
+    pw = operand_part(0);
+    if (nc > 1) load_chunk(1);
+  }
+  __syncthreads();
+
+  for (int c = 0; c < nc; ++c) {
+    const int t0 = c * C;
+    const int kcur = (c & 1) * 64;      // key ring half of this chunk
+    const int kprv = 64 - kcur;         // ... and of the previous chunk
+    const int vcur = (c % 3) * 64;      // value ring slot of this chunk
+    const int vprv = ((c + 2) % 3) * 64;   // ... and of the previous chunk
+    const bool pairwise = pw;
+
+    // ================= interval 1, softmax wavefront: weights of block QB ====
+    auto softmax_part = [&](auto Ic) __attribute__((always_inline)) {
+      constexpr int QB = decltype(Ic)::value;
       constexpr int U0 = 16 * QB < 32 ? 16 * QB : 32; // first window key (of [prev; cur]) staged
-      constexpr int JB = QB < 2 ? QB : 2;             // window tile kt holds intra key block kt - 4 + JB
-      constexpr int K0 = 3 * HF;                      // this wavefront's window tiles K0..K0+2
-      const int tme = t0 + 16 * QB + m;               // this lane's query
+      // Lane indices laundered through an empty asm: addresses derived from
+      // them are recomputed per chunk instead of being hoisted out of the
+      // chunk loop by every instance (which would exhaust registers).
+      int m = m_lane, g = g_lane;
+      asm volatile("" : "+v"(m), "+v"(g));
+      const int tme = t0 + 16 * QB + m;
+      frag qf[NF];
+#pragma unroll
+      for (int e = 0; e < NF; ++e) qf[e] = frag_at<T>(qraw, e);
+      // the next chunk's queries (qf holds this chunk's)
+      if (c + 1 < nc) load_q(c + 1);
 
-      // raw q (anchor logits) and Qe = q * 2^beta (readout, intra scores): B operands
-      frag qf[NF], qe[NF];
+      // Window tile kt (keys u in [U0+16kt, U0+16kt+16) of [prev; cur]) is
+      // needed if a query of the block has a key of it inside its window:
+      // valid u lie in [16QB+65-w, 16QB+79], and u >= 64 in the first chunk.
+      bool need[6];
+      {
+        const int vlo = 16 * QB + 65 - a.window;
+        const int vlo0 = (c == 0 && vlo < 64) ? 64 : vlo;
+#pragma unroll
+        for (int kt = 0; kt < 6; ++kt) {
+          const int ulo = U0 + 16 * kt;
+          need[kt] = ulo + 15 >= vlo0 && ulo <= 16 * QB + 79;
+        }
+      }
+      // anchor logits Z^T[u][t]
+      f32x4 z[6];
+#pragma unroll
+      for (int kt = 0; kt < 6; ++kt) {
+        z[kt] = zero4();
+        if (!need[kt]) continue;
+        const T* kp = sK + ((U0 + 16 * kt + kprv + m) & 127) * Lay::LDK + g * (D / 4);
+#pragma unroll
+        for (int e = 0; e < NF; ++e) z[kt] = M::mma(M::load(kp + e * M::KPL), qf[e], z[kt]);
+      }
+      f32x4 zs = zero4();
+#pragma unroll
+      for (int e = 0; e < NF; ++e) zs = M::mma(M::load(sMeta + m * Lay::LDK + g * (D / 4) + e * M::KPL), qf[e], zs);
+
+      // Softmax: maxima on raw logits (the scale is positive), scale folded
+      // into the exponent: P = 2^{z * scale*log2e - max}.
+      float mr = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        zs[r] = 4 * g + r < a.n_meta ? zs[r] : -INFINITY;
+        mr = fmaxf(mr, zs[r]);
+      }
+      // key valid iff 0 <= t - s < lim; in the first chunk also s >= 0 (t - s <= t)
+      const int lim = (c == 0 && 16 * QB + m + 1 < a.window) ? 16 * QB + m + 1 : a.window;
+      const int lim_lo = (c == 0 && 16 * QB + 1 < a.window) ? 16 * QB + 1 : a.window;   // over the block
+      const int dbase = 16 * QB + 64 - U0 + m - 4 * g;   // t - s for tile 0, r = 0
+#pragma unroll
+      for (int kt = 0; kt < 6; ++kt) {
+        if (!need[kt]) continue;
+        // t - s over the tile spans [dlo, dlo + 30]: tiles inside the band skip the mask
+        constexpr int dlo0 = 16 * QB + 64 - U0 - 15;
+        const int dlo = dlo0 - 16 * kt;
+        if (!(dlo >= 0 && dlo + 30 < lim_lo)) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int dts = dbase - 16 * kt - r;
+            z[kt][r] = (unsigned)dts < (unsigned)lim ? z[kt][r] : -INFINITY;
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mr = fmaxf(mr, z[kt][r]);
+      }
+      mr = xgroup_max(mr);                 // finite: the query's own key is always valid
+      const float mref = mr * a.scale_log2;
+      float sr = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sr += exp_2(fmaf(zs[r], a.scale_log2, -mref));
+#pragma unroll
+      for (int kt = 0; kt < 6; ++kt) {
+        float p[4] = {0.f, 0.f, 0.f, 0.f};
+        if (need[kt]) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            p[r] = exp_2(fmaf(z[kt][r], a.scale_log2, -mref));   // 2^-inf = 0 for masked keys
+            sr += p[r];
+          }
+        }
+        store_pack<T, 4>(sP + (16 * QB + m) * Lay::LDP + 16 * kt + 4 * g, p);
+      }
+      const float den = xgroup_sum(sr);
+      if (g == 0) {
+        const float inv = 1.0f / den;
+        sSc[16 * QB + m] = a.alpha * inv;
+        sSc[64 + 16 * QB + m] = inv;
+        if (lseg && tme < L) lseg[tme] = (mref + __log2f(den)) * kLn2;
+      }
+    };
+
+    // ========== interval 1, gate wavefront: gated output, state carry ========
+    auto gate_part = [&](auto Ic) __attribute__((always_inline)) {
+      constexpr int QB = decltype(Ic)::value;
+      int m = m_lane, g = g_lane;
+      asm volatile("" : "+v"(m), "+v"(g));
+      const int tme = t0 + 16 * QB + m;
+
+      // Qe = q * 2^beta of this lane's query (B operand)
+      frag qe[NF];
       if (!pairwise) {
-        const T* qp = sQ + (16 * QB + m) * Lay::LDK + g * (D / 4);
         const T* ep = sQe + (16 * QB + m) * Lay::LDK + g * (D / 4);
 #pragma unroll
-        for (int e = 0; e < NF; ++e) {
-          qf[e] = M::load(qp + e * M::KPL);
-          qe[e] = M::load(ep + e * M::KPL);
-        }
+        for (int e = 0; e < NF; ++e) qe[e] = M::load(ep + e * M::KPL);
       } else {
         uint4 raw[QV];
         const T* qp = qg + (size_t)(tme < L ? tme : 0) * D + g * (D / 4);
@@ -392,56 +626,19 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
           float tmp[M::KPL];
 #pragma unroll
           for (int u = 0; u < M::KPL; ++u) tmp[u] = elem_f32<T>(raw, e * M::KPL + u) * exp_2(bp[e * M::KPL + u]);
-          qf[e] = frag_at<T>(raw, e);
           qe[e] = M::pack(tmp);
         }
       }
 
-      // ---- anchor logits Z^T[u][t] for this half's keys, plus sinks (first half) ----
-      // Window tile kt (keys u in [U0+16kt, U0+16kt+16) of [prev; cur]) is
-      // needed if any query of the block has a key of it inside its window:
-      // valid u lie in [16QB+65-w, 16QB+79], and u >= 64 in the first chunk.
-      bool need[3];
-      {
-        const int vlo = 16 * QB + 65 - a.window;
-        const int vlo0 = (c == 0 && vlo < 64) ? 64 : vlo;
+      // ---- intra-chunk gated scores A^T[s][t], key blocks J <= QB ----
+      f32x4 ai[QB + 1];
 #pragma unroll
-        for (int k3 = 0; k3 < 3; ++k3) {
-          const int ulo = U0 + 16 * (K0 + k3);
-          need[k3] = ulo + 15 >= vlo0 && ulo <= 16 * QB + 79;
-        }
-      }
-      f32x4 z[3];
-#pragma unroll
-      for (int k3 = 0; k3 < 3; ++k3) {
-        z[k3] = zero4();
-        if (!need[k3]) continue;
-        const int u = U0 + 16 * (K0 + k3) + m;
-        const T* kp = sK + ((u + prv) & 127) * Lay::LDK + g * (D / 4);
-        f32x4 cacc = zero4();
-#pragma unroll
-        for (int e = 0; e < NF; ++e) cacc = M::mma(M::load(kp + e * M::KPL), qf[e], cacc);
-        z[k3] = cacc;
-      }
-      f32x4 zs = zero4();
-      if constexpr (HF == 0) {
-#pragma unroll
-        for (int e = 0; e < NF; ++e) zs = M::mma(muf[e], qf[e], zs);
-      }
-
-      // ---- intra-chunk gated scores A^T[s][t] among this half's tiles ----
-      f32x4 ai[3];
-#pragma unroll
-      for (int k3 = 0; k3 < 3; ++k3) {
-        ai[k3] = zero4();
-        const int J = K0 + k3 - 4 + JB;
-        if (J < 0 || J > QB) continue;
+      for (int J = 0; J <= QB; ++J) {
+        ai[J] = zero4();
         if (!pairwise) {
           const T* kp = sKp + (16 * J + m) * Lay::LDK + g * (D / 4);
-          f32x4 sc = zero4();
 #pragma unroll
-          for (int e = 0; e < NF; ++e) sc = M::mma(M::load(kp + e * M::KPL), qe[e], sc);
-          ai[k3] = sc;
+          for (int e = 0; e < NF; ++e) ai[J] = M::mma(M::load(kp + e * M::KPL), qe[e], ai[J]);
         } else {
           // pairwise gate products in fp32 (a decay span too wide to factorise)
           const T* qrow = qg + (size_t)(tme < L ? tme : 0) * D;
@@ -451,168 +648,137 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
             const int ks = 16 * J + 4 * g + r;
             float sum = 0.f;
             if (ks <= 16 * QB + m && tme < L) {
-              const T* krow = sK + (cur + ks) * Lay::LDK;
+              const T* krow = sK + (kcur + ks) * Lay::LDK;
               const float* bs = sBeta + ks * Lay::LDE;
               for (int i = 0; i < D; ++i) sum += to_f32(qrow[i]) * to_f32(krow[i]) * exp_2(bt[i] - bs[i]);
             }
-            ai[k3][r] = sum;
+            ai[J][r] = sum;
           }
         }
         if (J == QB) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) ai[k3][r] = 4 * g + r <= m ? ai[k3][r] : 0.f;
+          for (int r = 0; r < 4; ++r) ai[J][r] = 4 * g + r <= m ? ai[J][r] : 0.f;
         }
       }
 
-      // ---- softmax over this half's keys (+ sinks); the pair combines (max, sum) ----
-      // Maxima are taken on raw logits (the scale is positive) and the scale
-      // is folded into the exponent: P = 2^{z * scale*log2e - max}.
-      float mxo, smo;
-      {
-        float mr = -INFINITY;
-        if constexpr (HF == 0) {
+      if constexpr (Lay::STAGE_A) {
+        // A[t][s] of this block into its own staging rows (keys of blocks
+        // J > QB are zero), read back by this wavefront only
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            zs[r] = 4 * g + r < a.n_meta ? zs[r] : -INFINITY;
-            mr = fmaxf(mr, zs[r]);
+        for (int J = 0; J < 4; ++J) {
+          float v4[4] = {0.f, 0.f, 0.f, 0.f};
+          if (J <= QB) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v4[r] = ai[J < QB + 1 ? J : 0][r];
           }
+          store_pack<T, 4>(sA + (16 * QB + m) * Lay::LDA + 16 * J + 4 * g, v4);
         }
-        // key valid iff 0 <= t - s < lim; in the first chunk also s >= 0 (t - s <= t)
-        const int lim = (c == 0 && 16 * QB + m + 1 < a.window) ? 16 * QB + m + 1 : a.window;
-        const int dbase = 16 * QB + 64 - U0 + m - 4 * g;   // t - s for window tile 0, r = 0
-#pragma unroll
-        for (int k3 = 0; k3 < 3; ++k3)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int dts = dbase - 16 * (K0 + k3) - r;
-            const bool ok = need[k3] && (unsigned)dts < (unsigned)lim;
-            z[k3][r] = ok ? z[k3][r] : -INFINITY;
-            mr = fmaxf(mr, z[k3][r]);
-          }
-        mr = xgroup_max(mr);
-        mxo = mr * a.scale_log2;                            // -inf for a half without a valid key
-        const float mref = mr == -INFINITY ? 0.f : mxo;
-        float sr = 0.f;
-        if constexpr (HF == 0) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sr += exp_2(fmaf(zs[r], a.scale_log2, -mref));
-        }
-#pragma unroll
-        for (int k3 = 0; k3 < 3; ++k3)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            z[k3][r] = exp_2(fmaf(z[k3][r], a.scale_log2, -mref));   // 2^-inf = 0 for masked keys
-            sr += z[k3][r];
-          }
-        smo = xgroup_sum(sr);
-        // (the query's own key is always valid, so the pair's combined maximum is finite)
-        if (g == 0) *reinterpret_cast<float2*>(sStat + (w * 16 + m) * 2) = make_float2(mxo, smo);
+        wave_lds_sync();
       }
-      __syncthreads();
-      const float2 pst = *reinterpret_cast<const float2*>(sStat + ((w ^ 4) * 16 + m) * 2);
-      const float mx = fmaxf(mxo, pst.x);
-      const float den = smo * exp_2(mxo - mx) + pst.y * exp_2(pst.x - mx);
-      const float inv = 1.0f / den;
-      const float fo = exp_2(mxo - mx) * inv;         // this half's P -> softmax weight
-      // ---- staged matrix M[t][u] = alpha * P/den (+ A on this chunk's keys) ----
-#pragma unroll
-      for (int k3 = 0; k3 < 3; ++k3) {
-        float v4[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v4[r] = fmaf(z[k3][r], a.alpha * fo, ai[k3][r]);
-        store_pack<T, 4>(sStg + m * Lay::LDSTG + 16 * (K0 + k3) + 4 * g, v4);
-      }
-      if (HF == 0 && lseg && g == 0 && tme < L) lseg[tme] = (mx + __log2f(den)) * kLn2;
-      __syncthreads();
 
-      // ---- output O^T[j][t] = V^T M^T over the 96 staged keys + S_c^T Qe^T ----
-      const T* bp = sStg + m * Lay::LDSTG + g * 24;
+      // ---- gated output O^T[j][t] = S_c^T Qe^T + V^T A^T ----
 #pragma unroll
-      for (int ch = 0; ch < NCH; ++ch) {
-        const int ct = HF * NCH + ch;
+      for (int ct = 0; ct < NCT; ++ct) {
         f32x4 o = zero4();
-#pragma unroll
-        for (int e = 0; e < 24 / M::KPL; ++e) {
-          const int u = U0 + g * 24 + e * M::KPL;
-          const T* ap = sVt + (16 * ct + m) * Lay::LDVT + ((u + prv) & 127);
-          o = M::mma(M::load(ap), M::load(bp + e * M::KPL), o);
-        }
         const T* sp = sSt + (16 * ct + m) * Lay::LDST + g * (D / 4);
 #pragma unroll
         for (int e = 0; e < NF; ++e) o = M::mma(M::load(sp + e * M::KPL), qe[e], o);
-        if (tme < L) {
-          const float v4[4] = {o[0], o[1], o[2], o[3]};
-          store_pack<T, 4>(yg + (size_t)tme * D + 16 * ct + 4 * g, v4);
+        if constexpr (Lay::STAGE_A) {
+          const T* vp = sVt + (16 * ct + m) * Lay::LDVT + vcur + g * 16;
+          const T* ap = sA + (16 * QB + m) * Lay::LDA + g * 16;
+#pragma unroll
+          for (int e = 0; e < 16 / M::KPL; ++e) o = M::mma(M::load(vp + e * M::KPL), M::load(ap + e * M::KPL), o);
+        } else {
+          const float* vp = reinterpret_cast<const float*>(sVt) + (16 * ct + m) * Lay::LDVT + vcur + 4 * g;
+#pragma unroll
+          for (int J = 0; J <= QB; ++J) o = mma_tile_regs_f32(vp + 16 * J, ai[J], o);
         }
+        rq[ct] = __builtin_bit_cast(uint4, o);
       }
-      if (yag) {
-        // the anchor branch alone (optional output): stage P/den and repeat V^T P^T
-        __syncthreads();
+      carry(vcur, m, g);
+    };
+
+    // ========== interval 2, gate wavefront: anchor product and output =======
+    auto output_part = [&](auto Ic) __attribute__((always_inline)) {
+      constexpr int QB = decltype(Ic)::value;
+      constexpr int U0 = 16 * QB < 32 ? 16 * QB : 32;
+      int m = m_lane, g = g_lane;
+      asm volatile("" : "+v"(m), "+v"(g));
+      const int tme = t0 + 16 * QB + m;
+      const float sc = sSc[16 * QB + m];
+      const float inv = sSc[64 + 16 * QB + m];
+      const T* pp = sP + (16 * QB + m) * Lay::LDP + g * 24;
+      // V^T column of window key u of [prev; cur]: the previous slot is
+      // followed by the current one in the 3-slot ring
+      int col[24 / M::KPL];
 #pragma unroll
-        for (int k3 = 0; k3 < 3; ++k3) {
-          float v4[4];
+      for (int e = 0; e < 24 / M::KPL; ++e) {
+        const unsigned v = vprv + U0 + g * 24 + e * M::KPL;
+        col[e] = (int)min(v, v - 192u);
+      }
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v4[r] = z[k3][r] * fo;
-          store_pack<T, 4>(sStg + m * Lay::LDSTG + 16 * (K0 + k3) + 4 * g, v4);
-        }
-        __syncthreads();
+      for (int ct = 0; ct < NCT; ++ct) {
+        f32x4 o = zero4();
+        const T* vrow = sVt + (16 * ct + m) * Lay::LDVT;
 #pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) {
-          const int ct = HF * NCH + ch;
-          f32x4 o = zero4();
-#pragma unroll
-          for (int e = 0; e < 24 / M::KPL; ++e) {
-            const int u = U0 + g * 24 + e * M::KPL;
-            const T* ap = sVt + (16 * ct + m) * Lay::LDVT + ((u + prv) & 127);
-            o = M::mma(M::load(ap), M::load(bp + e * M::KPL), o);
-          }
-          if (tme < L) {
-            const float v4[4] = {o[0], o[1], o[2], o[3]};
-            store_pack<T, 4>(yag + (size_t)tme * D + 16 * ct + 4 * g, v4);
+        for (int e = 0; e < 24 / M::KPL; ++e) o = M::mma(M::load(vrow + col[e]), M::load(pp + e * M::KPL), o);
+        if (tme < L) {
+          const f32x4 og = __builtin_bit_cast(f32x4, rq[ct]);
+          const float v4[4] = {fmaf(sc, o[0], og[0]), fmaf(sc, o[1], og[1]),
+                               fmaf(sc, o[2], og[2]), fmaf(sc, o[3], og[3])};
+          store_pack<T, 4>(yg + (size_t)tme * D + 16 * ct + 4 * g, v4);
+          if (yag) {
+            const float a4[4] = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+            store_pack<T, 4>(yag + (size_t)tme * D + 16 * ct + 4 * g, a4);
           }
         }
       }
     };
-    if (!STATES) {
+
+    // ---- interval 1 ----
+    if constexpr (STATES) {
+      if (gate) carry(vcur, m_lane, g_lane);
+    } else {
       switch (w) {
-        case 0: phase_b(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}); break;
-        case 1: phase_b(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}); break;
-        case 2: phase_b(std::integral_constant<int, 2>{}, std::integral_constant<int, 0>{}); break;
-        case 3: phase_b(std::integral_constant<int, 3>{}, std::integral_constant<int, 0>{}); break;
-        case 4: phase_b(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}); break;
-        case 5: phase_b(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}); break;
-        case 6: phase_b(std::integral_constant<int, 2>{}, std::integral_constant<int, 1>{}); break;
-        default: phase_b(std::integral_constant<int, 3>{}, std::integral_constant<int, 1>{}); break;
+        case 0: softmax_part(std::integral_constant<int, 0>{}); break;
+        case 1: softmax_part(std::integral_constant<int, 1>{}); break;
+        case 2: softmax_part(std::integral_constant<int, 2>{}); break;
+        case 3: softmax_part(std::integral_constant<int, 3>{}); break;
+        case 4: gate_part(std::integral_constant<int, 0>{}); break;
+        case 5: gate_part(std::integral_constant<int, 1>{}); break;
+        case 6: gate_part(std::integral_constant<int, 2>{}); break;
+        default: gate_part(std::integral_constant<int, 3>{}); break;
       }
     }
+    if (c + 1 < nc) prefix_part();
+    __syncthreads();
 
-    // ---- state carry: S = 2^B * S + Kh^T V over this chunk's keys ----
-    if (srow) {
-      const int ib = 16 * w;
-      float dec[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dec[r] = sBexp[ib + 4 * g + r];
-      const T* ap = sKhT + (ib + m) * Lay::LDKH + g * 16;
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        f32x4 s = acc[ct];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) s[r] *= dec[r];
-        const T* bv = sVt + (16 * ct + m) * Lay::LDVT + cur + g * 16;
-#pragma unroll
-        for (int e = 0; e < 16 / M::KPL; ++e) s = M::mma(M::load(ap + e * M::KPL), M::load(bv + e * M::KPL), s);
-        acc[ct] = s;
+    // ---- interval 2 ----
+    if constexpr (!STATES) {
+      switch (w) {
+        case 4: output_part(std::integral_constant<int, 0>{}); break;
+        case 5: output_part(std::integral_constant<int, 1>{}); break;
+        case 6: output_part(std::integral_constant<int, 2>{}); break;
+        case 7: output_part(std::integral_constant<int, 3>{}); break;
+        default: break;
       }
+    }
+    if (c + 1 < nc) {
+      pw = operand_part(c + 1);
+      if (c + 2 < nc) load_chunk(c + 2);
     }
     __syncthreads();
   }
 
-  if (a.state_out && srow) {
+  if (a.state_out && gate) {
     float* so = a.state_out + (size_t)bh * D * D;
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
+    for (int rt = 0; rt < DPL; ++rt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) so[(size_t)(16 * w + 4 * g + r) * D + j0 + 16 * ct + m] = acc[ct][r];
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          so[(size_t)(16 * (DPL * I + rt) + 4 * g_lane + r) * D + j0 + 16 * ct + m_lane] = acc[rt][ct][r];
   }
 }
 
