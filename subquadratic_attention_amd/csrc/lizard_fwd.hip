@@ -180,8 +180,6 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
   const int l = tid & 63;
   const int m_lane = l & 15;   // MFMA row / column within a tile
   const int g_lane = l >> 4;   // MFMA lane group
-  const bool gate = w >= 4;    // wavefronts 4..7: gated branch and state
-  const int I = w & 3;         // query block of this wavefront
   const int vj = tid % VRW;    // value-load role: columns VC*vj.., rows VR*vs..
   const int vs = tid / VRW;
 
@@ -203,582 +201,567 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
         r < a.n_meta ? reinterpret_cast<const T*>(a.meta)[((size_t)h * a.n_meta + r) * D + cidx] : from_f32<T>(0.f);
   }
 
-  // ---- gate wavefronts: state rows 16*(DPL*I + rt) + 4g + r, cols 16ct + m ----
-  f32x4 acc[DPL][NCT];
-#pragma unroll
-  for (int rt = 0; rt < DPL; ++rt)
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) acc[rt][ct] = zero4();
+  // Each (role, query block) runs its own copy of the chunk loop: role 0 the
+  // softmax wavefronts, role 1 the gate wavefronts (in the states-only mode
+  // role 0 only prepares operands and role 1 carries the state).  Separate
+  // loops keep one role's registers and outstanding loads out of the other's
+  // (a shared loop would make the compiler hold both roles' registers and
+  // wait for every load in flight); the barrier sequence is the same in all.
+  auto run = [&](auto Rc, auto Ic) __attribute__((always_inline)) {
+    constexpr bool GATE = decltype(Rc)::value == 1;
+    constexpr int QB = decltype(Ic)::value;
+    // ---- gate wavefronts: state rows 16*(DPL*I + rt) + 4g + r, cols 16ct + m ----
+    const int I = QB;
+    f32x4 acc[DPL][NCT];
+  #pragma unroll
+    for (int rt = 0; rt < DPL; ++rt)
+  #pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) acc[rt][ct] = zero4();
 
-  // ---- per-chunk global data (prefetched ahead, kept as raw bits) ----
-  float lgA[8][DPL];    // prep rows 8w+rr, dims DPL*l + dd
-  float loc[8][DPL];    // their prefix inside the wavefront's 8 rows
-  uint32_t kA[8];       // the same rows' keys: DPL elements packed in 32 bits
-  uint32_t qA[8];       // ... and queries
-  uint32_t vA[VR];      // values: rows VR*vs + rr, columns VC*vj.. packed in 32 bits
-  // One register array for two roles (a wavefront only ever has one, and the
-  // compiler would otherwise keep both live across the chunk loop):
-  // softmax wavefronts: raw q of row 16I + m, the lane's k-quarter (QV vectors);
-  // gate wavefronts: the gated output of the block, carried over a barrier (NCT tiles).
-  constexpr int RQ = QV > NCT ? QV : NCT;
-  uint4 rq[RQ];
-  uint4* qraw = rq;
+    // ---- per-chunk global data (prefetched ahead, kept as raw bits) ----
+    float lgA[8][DPL];    // prep rows 8w+rr, dims DPL*l + dd
+    float loc[8][DPL];    // their prefix inside the wavefront's 8 rows
+    uint32_t kA[8];       // the same rows' keys: DPL elements packed in 32 bits
+    uint32_t qA[8];       // ... and queries
+    uint32_t vA[VR];      // values: rows VR*vs + rr, columns VC*vj.. packed in 32 bits
+    uint4 qraw[QV];       // softmax wavefronts: raw q of row 16I + m, the lane's k-quarter
+    f32x4 og[NCT];        // gate wavefronts: gated output of the block, carried over a barrier
 
-  auto load_rows = [&](int c, bool full) __attribute__((always_inline)) {
-    const int t0 = c * C;
-    const int tid = opaque(threadIdx.x);
-    const int l = tid & 63;
-    const int vj = tid % VRW, vs = tid / VRW;
-    {
-      const int tb = t0 + 8 * w;
-      const float* lp = lgg + (size_t)tb * D + DPL * l;
-      const T* kp = kg + (size_t)tb * D + DPL * l;
-      const T* qp = qg + (size_t)tb * D + DPL * l;
-#pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        const bool ok = full || tb + rr < L;
-        const int ro = ok ? rr * D : -tb * D;       // row 0 of the slice when out of range
-        float lv[DPL];
-        if constexpr (DPL == 2) {
-          const float2 f = *reinterpret_cast<const float2*>(lp + ro);
-          lv[0] = f.x;
-          lv[1] = f.y;
-        } else {
-          lv[0] = lp[ro];
-        }
-        uint32_t kv, qv;
-        if constexpr (DPL * sizeof(T) == 4) {
-          kv = *reinterpret_cast<const uint32_t*>(kp + ro);
-          qv = *reinterpret_cast<const uint32_t*>(qp + ro);
-        } else {
-          kv = *reinterpret_cast<const uint16_t*>(kp + ro);
-          qv = *reinterpret_cast<const uint16_t*>(qp + ro);
-        }
-#pragma unroll
-        for (int dd = 0; dd < DPL; ++dd) lgA[rr][dd] = ok ? lv[dd] : 0.f;
-        kA[rr] = ok ? kv : 0u;
-        qA[rr] = ok ? qv : 0u;
-      }
-    }
-    {
-      const int tb = t0 + VR * vs;
-      const T* vp = vg + (size_t)tb * D + VC * vj;
-#pragma unroll
-      for (int rr = 0; rr < VR; ++rr) {
-        const bool ok = full || tb + rr < L;
-        const uint32_t u = *reinterpret_cast<const uint32_t*>(vp + (ok ? rr * D : -tb * D));
-        vA[rr] = ok ? u : 0u;
-      }
-    }
-  };
-  // a uniform branch: full chunks load without per-row guards
-  auto load_chunk = [&](int c) __attribute__((always_inline)) {
-    if ((c + 1) * C <= L) load_rows(c, true);
-    else load_rows(c, false);
-  };
-  auto load_q = [&](int c) __attribute__((always_inline)) {
-    const int l = opaque(threadIdx.x) & 63;
-    const int tq = c * C + 16 * I + (l & 15);
-    const bool ok = tq < L;
-    const T* qp = qg + (size_t)(ok ? tq : 0) * D + (l >> 4) * (D / 4);
-#pragma unroll
-    for (int e = 0; e < QV; ++e) qraw[e] = ok ? ld16(qp + e * EPV) : make_uint4(0, 0, 0, 0);
-  };
-  // element dd of a packed 32-bit word, as float
-  auto elem32 = [&](uint32_t u, int dd) __attribute__((always_inline)) -> float {
-    if constexpr (sizeof(T) == 4) return __builtin_bit_cast(float, u);
-    else return __builtin_bit_cast(float, dd == 0 ? (u << 16) : (u & 0xffff0000u));
-  };
-
-  // ---- prefix sums inside this wavefront's 8 rows (natural-log units; exact
-  // for the factorised path, where no single gate is small enough for the
-  // 2^-100 floor of the wide-span path) ----
-  auto prefix_part = [&]() __attribute__((always_inline)) {
-    const int l = opaque(threadIdx.x) & 63;
-    float tot[DPL];
-#pragma unroll
-    for (int dd = 0; dd < DPL; ++dd) {
-      float run = 0.f;
-#pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        run += lgA[rr][dd];
-        loc[rr][dd] = run;
-      }
-      tot[dd] = run;
-    }
-    if constexpr (DPL == 2) *reinterpret_cast<float2*>(sTot + w * D + 2 * l) = make_float2(tot[0], tot[1]);
-    else sTot[w * D + l] = tot[0];
-  };
-
-  // offset of this wavefront's rows (sum of the earlier wavefronts' totals)
-  // and the chunk total, from the 8 partial totals in tp
-  auto offsets = [&](const float* tp, float* off, float* Bt) __attribute__((always_inline)) {
-    const int l = opaque(threadIdx.x) & 63;
-    float tv[8][DPL];
-#pragma unroll
-    for (int ww = 0; ww < 8; ++ww) {
-      if constexpr (DPL == 2) {
-        const float2 f = *reinterpret_cast<const float2*>(tp + ww * D + 2 * l);
-        tv[ww][0] = f.x;
-        tv[ww][1] = f.y;
-      } else {
-        tv[ww][0] = tp[ww * D + l];
-      }
-    }
-#pragma unroll
-    for (int dd = 0; dd < DPL; ++dd) {
-      float run = 0.f, o = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < 8; ++ww) {
-        o = ww == w ? run : o;
-        run += tv[ww][dd];
-      }
-      off[dd] = o;
-      Bt[dd] = run;
-    }
-  };
-
-  // ---- chunk cc's operands into LDS (decay factors, Qe, Kp, Kh, keys,
-  // values, the chunk-start state); returns whether it takes the pairwise path
-  auto operand_part = [&](int cc) __attribute__((always_inline)) -> bool {
-    const int kc = (cc & 1) * 64;       // key ring half
-    const int vc = (cc % 3) * 64;       // value ring slot
-    const int tid = opaque(threadIdx.x);
-    const int l = tid & 63, m_lane = l & 15, g_lane = l >> 4;
-    const int vj = tid % VRW, vs = tid / VRW;
-    float Bt[DPL], off[DPL];
-    offsets(sTot, off, Bt);
-    bool wide = false;
-#pragma unroll
-    for (int dd = 0; dd < DPL; ++dd) wide |= -Bt[dd] * kLog2e > kMaxSpanLog2;
-    // every wavefront covers all D dims, so this ballot is the chunk's decision
-    const bool pairwise = __any(wide);
-    float kh[DPL][8];
-    float eB[DPL];
-    if (!pairwise) {
-#pragma unroll
-      for (int dd = 0; dd < DPL; ++dd) {
-        eB[dd] = exp_2(Bt[dd] * kLog2e);
-        off[dd] *= kLog2e;
-      }
-#pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        const int s = 8 * w + rr;
-        float qe[DPL], kp[DPL];
-#pragma unroll
-        for (int dd = 0; dd < DPL; ++dd) {
-          const float beta = fmaf(loc[rr][dd], kLog2e, off[dd]);
-          kp[dd] = elem32(kA[rr], dd) * exp_2(-beta);
-          kh[dd][rr] = kp[dd] * eB[dd];
-          qe[dd] = elem32(qA[rr], dd) * exp_2(beta);
-        }
-        if constexpr (DPL == 2) {
-          *reinterpret_cast<bf16x2*>(sQe + s * Lay::LDK + 2 * l) = bf16x2{static_cast<bf16>(qe[0]), static_cast<bf16>(qe[1])};
-          *reinterpret_cast<bf16x2*>(sKp + s * Lay::LDK + 2 * l) = bf16x2{static_cast<bf16>(kp[0]), static_cast<bf16>(kp[1])};
-        } else {
-          sQe[s * Lay::LDK + l] = from_f32<T>(qe[0]);
-          sKp[s * Lay::LDK + l] = from_f32<T>(kp[0]);
+    auto load_rows = [&](int c, bool full) __attribute__((always_inline)) {
+      const int t0 = c * C;
+      const int tid = opaque(threadIdx.x);
+      const int l = tid & 63;
+      const int vj = tid % VRW, vs = tid / VRW;
+      {
+        const int tb = t0 + 8 * w;
+        const float* lp = lgg + (size_t)tb * D + DPL * l;
+        const T* kp = kg + (size_t)tb * D + DPL * l;
+        const T* qp = qg + (size_t)tb * D + DPL * l;
+  #pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+          const bool ok = full || tb + rr < L;
+          const int ro = ok ? rr * D : -tb * D;       // row 0 of the slice when out of range
+          float lv[DPL];
+          if constexpr (DPL == 2) {
+            const float2 f = *reinterpret_cast<const float2*>(lp + ro);
+            lv[0] = f.x;
+            lv[1] = f.y;
+          } else {
+            lv[0] = lp[ro];
+          }
+          uint32_t kv, qv;
+          if constexpr (DPL * sizeof(T) == 4) {
+            kv = *reinterpret_cast<const uint32_t*>(kp + ro);
+            qv = *reinterpret_cast<const uint32_t*>(qp + ro);
+          } else {
+            kv = *reinterpret_cast<const uint16_t*>(kp + ro);
+            qv = *reinterpret_cast<const uint16_t*>(qp + ro);
+          }
+  #pragma unroll
+          for (int dd = 0; dd < DPL; ++dd) lgA[rr][dd] = ok ? lv[dd] : 0.f;
+          kA[rr] = ok ? kv : 0u;
+          qA[rr] = ok ? qv : 0u;
         }
       }
-    } else {
-      // wide span: log2 prefixes with every gate floored at 2^-100, so that
-      // differences of prefixes keep float precision (a uniform branch)
-      float locc[8][DPL], totc[DPL];
-#pragma unroll
+      {
+        const int tb = t0 + VR * vs;
+        const T* vp = vg + (size_t)tb * D + VC * vj;
+  #pragma unroll
+        for (int rr = 0; rr < VR; ++rr) {
+          const bool ok = full || tb + rr < L;
+          const uint32_t u = *reinterpret_cast<const uint32_t*>(vp + (ok ? rr * D : -tb * D));
+          vA[rr] = ok ? u : 0u;
+        }
+      }
+    };
+    // a uniform branch: full chunks load without per-row guards
+    auto load_chunk = [&](int c) __attribute__((always_inline)) {
+      if ((c + 1) * C <= L) load_rows(c, true);
+      else load_rows(c, false);
+    };
+    auto load_q = [&](int c) __attribute__((always_inline)) {
+      const int l = opaque(threadIdx.x) & 63;
+      const int tq = c * C + 16 * I + (l & 15);
+      const bool ok = tq < L;
+      const T* qp = qg + (size_t)(ok ? tq : 0) * D + (l >> 4) * (D / 4);
+  #pragma unroll
+      for (int e = 0; e < QV; ++e) qraw[e] = ok ? ld16(qp + e * EPV) : make_uint4(0, 0, 0, 0);
+    };
+    // element dd of a packed 32-bit word, as float
+    auto elem32 = [&](uint32_t u, int dd) __attribute__((always_inline)) -> float {
+      if constexpr (sizeof(T) == 4) return __builtin_bit_cast(float, u);
+      else return __builtin_bit_cast(float, dd == 0 ? (u << 16) : (u & 0xffff0000u));
+    };
+
+    // ---- prefix sums inside this wavefront's 8 rows (natural-log units; exact
+    // for the factorised path, where no single gate is small enough for the
+    // 2^-100 floor of the wide-span path) ----
+    auto prefix_part = [&]() __attribute__((always_inline)) {
+      const int l = opaque(threadIdx.x) & 63;
+      float tot[DPL];
+  #pragma unroll
       for (int dd = 0; dd < DPL; ++dd) {
         float run = 0.f;
-#pragma unroll
+  #pragma unroll
         for (int rr = 0; rr < 8; ++rr) {
-          run += log2_gate(lgA[rr][dd]);
-          locc[rr][dd] = run;
+          run += lgA[rr][dd];
+          loc[rr][dd] = run;
         }
-        totc[dd] = run;
+        tot[dd] = run;
       }
-#pragma unroll
-      for (int dd = 0; dd < DPL; ++dd) sTotC[w * D + DPL * l + dd] = totc[dd];
-      __syncthreads();
-      offsets(sTotC, off, Bt);
-#pragma unroll
-      for (int dd = 0; dd < DPL; ++dd) eB[dd] = exp_2(Bt[dd]);
-#pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        const int s = 8 * w + rr;
-#pragma unroll
+      if constexpr (DPL == 2) *reinterpret_cast<float2*>(sTot + w * D + 2 * l) = make_float2(tot[0], tot[1]);
+      else sTot[w * D + l] = tot[0];
+    };
+
+    // offset of this wavefront's rows (sum of the earlier wavefronts' totals)
+    // and the chunk total, from the 8 partial totals in tp
+    auto offsets = [&](const float* tp, float* off, float* Bt) __attribute__((always_inline)) {
+      const int l = opaque(threadIdx.x) & 63;
+      float tv[8][DPL];
+  #pragma unroll
+      for (int ww = 0; ww < 8; ++ww) {
+        if constexpr (DPL == 2) {
+          const float2 f = *reinterpret_cast<const float2*>(tp + ww * D + 2 * l);
+          tv[ww][0] = f.x;
+          tv[ww][1] = f.y;
+        } else {
+          tv[ww][0] = tp[ww * D + l];
+        }
+      }
+  #pragma unroll
+      for (int dd = 0; dd < DPL; ++dd) {
+        float run = 0.f, o = 0.f;
+  #pragma unroll
+        for (int ww = 0; ww < 8; ++ww) {
+          o = ww == w ? run : o;
+          run += tv[ww][dd];
+        }
+        off[dd] = o;
+        Bt[dd] = run;
+      }
+    };
+
+    // ---- chunk cc's operands into LDS (decay factors, Qe, Kp, Kh, keys,
+    // values, the chunk-start state); returns whether it takes the pairwise path
+    auto operand_part = [&](int cc) __attribute__((always_inline)) -> bool {
+      const int kc = (cc & 1) * 64;       // key ring half
+      const int vc = (cc % 3) * 64;       // value ring slot
+      const int tid = opaque(threadIdx.x);
+      const int l = tid & 63, m_lane = l & 15, g_lane = l >> 4;
+      const int vj = tid % VRW, vs = tid / VRW;
+      float Bt[DPL], off[DPL];
+      offsets(sTot, off, Bt);
+      bool wide = false;
+  #pragma unroll
+      for (int dd = 0; dd < DPL; ++dd) wide |= -Bt[dd] * kLog2e > kMaxSpanLog2;
+      // every wavefront covers all D dims, so this ballot is the chunk's decision
+      const bool pairwise = __any(wide);
+      float kh[DPL][8];
+      float eB[DPL];
+      if (!pairwise) {
+  #pragma unroll
         for (int dd = 0; dd < DPL; ++dd) {
-          const float beta = off[dd] + locc[rr][dd];
-          kh[dd][rr] = elem32(kA[rr], dd) * exp_2(Bt[dd] - beta);
-          sBeta[s * Lay::LDE + DPL * l + dd] = beta;
+          eB[dd] = exp_2(Bt[dd] * kLog2e);
+          off[dd] *= kLog2e;
         }
-      }
-    }
-#pragma unroll
-    for (int dd = 0; dd < DPL; ++dd) {
-      store_pack<T, 8>(sKhT + (DPL * l + dd) * Lay::LDKH + 8 * w, kh[dd]);
-      if (w == 0) sBexp[DPL * l + dd] = eB[dd];
-    }
-    // raw keys into the ring
-#pragma unroll
-    for (int rr = 0; rr < 8; ++rr) {
-      T* krp = sK + (kc + 8 * w + rr) * Lay::LDK + DPL * l;
-      if constexpr (DPL * sizeof(T) == 4) *reinterpret_cast<uint32_t*>(krp) = kA[rr];
-      else krp[0] = from_f32<T>(elem32(kA[rr], 0));
-    }
-    // values, transposed into their ring slot: sVt[j][vc + s], 4 tokens per write
-    if constexpr (sizeof(T) == 2) {
-      // columns 2vj and 2vj+1 of 4 consecutive rows: regroup the 16-bit halves
-      const uint2 lo = make_uint2(__builtin_amdgcn_perm(vA[1], vA[0], 0x05040100u),
-                                  __builtin_amdgcn_perm(vA[3], vA[2], 0x05040100u));
-      const uint2 hi = make_uint2(__builtin_amdgcn_perm(vA[1], vA[0], 0x07060302u),
-                                  __builtin_amdgcn_perm(vA[3], vA[2], 0x07060302u));
-      *reinterpret_cast<uint2*>(sVt + (2 * vj) * Lay::LDVT + vc + VR * vs) = lo;
-      *reinterpret_cast<uint2*>(sVt + (2 * vj + 1) * Lay::LDVT + vc + VR * vs) = hi;
-    } else {
-      *reinterpret_cast<uint4*>(sVt + vj * Lay::LDVT + vc + VR * vs) = make_uint4(vA[0], vA[1], vA[2], vA[3]);
-    }
-    if (gate) {
-      if constexpr (!STATES) {
-        // S_cc (rounded to the element type) for the readout: sSt[j][i], 4 rows i per write
-#pragma unroll
-        for (int rt = 0; rt < DPL; ++rt)
-#pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) {
-            const float sv[4] = {acc[rt][ct][0], acc[rt][ct][1], acc[rt][ct][2], acc[rt][ct][3]};
-            store_pack<T, 4>(sSt + (16 * ct + m_lane) * Lay::LDST + 16 * (DPL * I + rt) + 4 * g_lane, sv);
+  #pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+          const int s = 8 * w + rr;
+          float qe[DPL], kp[DPL];
+  #pragma unroll
+          for (int dd = 0; dd < DPL; ++dd) {
+            const float beta = fmaf(loc[rr][dd], kLog2e, off[dd]);
+            kp[dd] = elem32(kA[rr], dd) * exp_2(-beta);
+            kh[dd][rr] = kp[dd] * eB[dd];
+            qe[dd] = elem32(qA[rr], dd) * exp_2(beta);
           }
+          if constexpr (DPL == 2) {
+            *reinterpret_cast<bf16x2*>(sQe + s * Lay::LDK + 2 * l) = bf16x2{static_cast<bf16>(qe[0]), static_cast<bf16>(qe[1])};
+            *reinterpret_cast<bf16x2*>(sKp + s * Lay::LDK + 2 * l) = bf16x2{static_cast<bf16>(kp[0]), static_cast<bf16>(kp[1])};
+          } else {
+            sQe[s * Lay::LDK + l] = from_f32<T>(qe[0]);
+            sKp[s * Lay::LDK + l] = from_f32<T>(kp[0]);
+          }
+        }
       } else {
-        // chunk-start state for the backward pass: S_cc[i][j], row-major
-        const int ncs = (L + C - 1) / C;
-        T* sg = reinterpret_cast<T*>(a.states) + ((size_t)bh * ncs + cc) * D * D + j0;
-#pragma unroll
-        for (int rt = 0; rt < DPL; ++rt)
-#pragma unroll
-          for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              sg[(size_t)(16 * (DPL * I + rt) + 4 * g_lane + r) * D + 16 * ct + m_lane] = from_f32<T>(acc[rt][ct][r]);
-      }
-    }
-    return pairwise;
-  };
-
-  // ---- state carry over chunk c: S = 2^B * S + Kh^T V (gate wavefronts) ----
-  auto carry = [&](int vc, int m, int g) __attribute__((always_inline)) {
-#pragma unroll
-    for (int rt = 0; rt < DPL; ++rt) {
-      const int ib = 16 * (DPL * I + rt);
-      float dec[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dec[r] = sBexp[ib + 4 * g + r];
-      const T* kp = sKhT + (ib + m) * Lay::LDKH + g * 16;
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        f32x4 s = acc[rt][ct];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) s[r] *= dec[r];
-        const T* vp = sVt + (16 * ct + m) * Lay::LDVT + vc + g * 16;
-#pragma unroll
-        for (int e = 0; e < 16 / M::KPL; ++e) s = M::mma(M::load(kp + e * M::KPL), M::load(vp + e * M::KPL), s);
-        acc[rt][ct] = s;
-      }
-    }
-  };
-
-  const int nc = (L + C - 1) / C;
-  bool pw = false;                      // pairwise path for the chunk about to be processed
-  if (nc > 0) {
-    load_chunk(0);
-    if (!STATES && !gate) load_q(0);
-    prefix_part();
-  }
-  __syncthreads();
-  if (nc > 0) {
-    pw = operand_part(0);
-    if (nc > 1) load_chunk(1);
-  }
-  __syncthreads();
-
-  for (int c = 0; c < nc; ++c) {
-    const int t0 = c * C;
-    const int kcur = (c & 1) * 64;      // key ring half of this chunk
-    const int kprv = 64 - kcur;         // ... and of the previous chunk
-    const int vcur = (c % 3) * 64;      // value ring slot of this chunk
-    const int vprv = ((c + 2) % 3) * 64;   // ... and of the previous chunk
-    const bool pairwise = pw;
-
-    // ================= interval 1, softmax wavefront: weights of block QB ====
-    auto softmax_part = [&](auto Ic) __attribute__((always_inline)) {
-      constexpr int QB = decltype(Ic)::value;
-      constexpr int U0 = 16 * QB < 32 ? 16 * QB : 32; // first window key (of [prev; cur]) staged
-      // Lane indices laundered through an empty asm: addresses derived from
-      // them are recomputed per chunk instead of being hoisted out of the
-      // chunk loop by every instance (which would exhaust registers).
-      int m = m_lane, g = g_lane;
-      asm volatile("" : "+v"(m), "+v"(g));
-      const int tme = t0 + 16 * QB + m;
-      frag qf[NF];
-#pragma unroll
-      for (int e = 0; e < NF; ++e) qf[e] = frag_at<T>(qraw, e);
-      // the next chunk's queries (qf holds this chunk's)
-      if (c + 1 < nc) load_q(c + 1);
-
-      // Window tile kt (keys u in [U0+16kt, U0+16kt+16) of [prev; cur]) is
-      // needed if a query of the block has a key of it inside its window:
-      // valid u lie in [16QB+65-w, 16QB+79], and u >= 64 in the first chunk.
-      bool need[6];
-      {
-        const int vlo = 16 * QB + 65 - a.window;
-        const int vlo0 = (c == 0 && vlo < 64) ? 64 : vlo;
-#pragma unroll
-        for (int kt = 0; kt < 6; ++kt) {
-          const int ulo = U0 + 16 * kt;
-          need[kt] = ulo + 15 >= vlo0 && ulo <= 16 * QB + 79;
+        // wide span: log2 prefixes with every gate floored at 2^-100, so that
+        // differences of prefixes keep float precision (a uniform branch)
+        float locc[8][DPL], totc[DPL];
+  #pragma unroll
+        for (int dd = 0; dd < DPL; ++dd) {
+          float run = 0.f;
+  #pragma unroll
+          for (int rr = 0; rr < 8; ++rr) {
+            run += log2_gate(lgA[rr][dd]);
+            locc[rr][dd] = run;
+          }
+          totc[dd] = run;
         }
-      }
-      // anchor logits Z^T[u][t]
-      f32x4 z[6];
-#pragma unroll
-      for (int kt = 0; kt < 6; ++kt) {
-        z[kt] = zero4();
-        if (!need[kt]) continue;
-        const T* kp = sK + ((U0 + 16 * kt + kprv + m) & 127) * Lay::LDK + g * (D / 4);
-#pragma unroll
-        for (int e = 0; e < NF; ++e) z[kt] = M::mma(M::load(kp + e * M::KPL), qf[e], z[kt]);
-      }
-      f32x4 zs = zero4();
-#pragma unroll
-      for (int e = 0; e < NF; ++e) zs = M::mma(M::load(sMeta + m * Lay::LDK + g * (D / 4) + e * M::KPL), qf[e], zs);
-
-      // Softmax: maxima on raw logits (the scale is positive), scale folded
-      // into the exponent: P = 2^{z * scale*log2e - max}.
-      float mr = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        zs[r] = 4 * g + r < a.n_meta ? zs[r] : -INFINITY;
-        mr = fmaxf(mr, zs[r]);
-      }
-      // key valid iff 0 <= t - s < lim; in the first chunk also s >= 0 (t - s <= t)
-      const int lim = (c == 0 && 16 * QB + m + 1 < a.window) ? 16 * QB + m + 1 : a.window;
-      const int lim_lo = (c == 0 && 16 * QB + 1 < a.window) ? 16 * QB + 1 : a.window;   // over the block
-      const int dbase = 16 * QB + 64 - U0 + m - 4 * g;   // t - s for tile 0, r = 0
-#pragma unroll
-      for (int kt = 0; kt < 6; ++kt) {
-        if (!need[kt]) continue;
-        // t - s over the tile spans [dlo, dlo + 30]: tiles inside the band skip the mask
-        constexpr int dlo0 = 16 * QB + 64 - U0 - 15;
-        const int dlo = dlo0 - 16 * kt;
-        if (!(dlo >= 0 && dlo + 30 < lim_lo)) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int dts = dbase - 16 * kt - r;
-            z[kt][r] = (unsigned)dts < (unsigned)lim ? z[kt][r] : -INFINITY;
+  #pragma unroll
+        for (int dd = 0; dd < DPL; ++dd) sTotC[w * D + DPL * l + dd] = totc[dd];
+        __syncthreads();
+        offsets(sTotC, off, Bt);
+  #pragma unroll
+        for (int dd = 0; dd < DPL; ++dd) eB[dd] = exp_2(Bt[dd]);
+  #pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+          const int s = 8 * w + rr;
+  #pragma unroll
+          for (int dd = 0; dd < DPL; ++dd) {
+            const float beta = off[dd] + locc[rr][dd];
+            kh[dd][rr] = elem32(kA[rr], dd) * exp_2(Bt[dd] - beta);
+            sBeta[s * Lay::LDE + DPL * l + dd] = beta;
           }
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mr = fmaxf(mr, z[kt][r]);
       }
-      mr = xgroup_max(mr);                 // finite: the query's own key is always valid
-      const float mref = mr * a.scale_log2;
-      float sr = 0.f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sr += exp_2(fmaf(zs[r], a.scale_log2, -mref));
-#pragma unroll
-      for (int kt = 0; kt < 6; ++kt) {
-        float p[4] = {0.f, 0.f, 0.f, 0.f};
-        if (need[kt]) {
-#pragma unroll
+  #pragma unroll
+      for (int dd = 0; dd < DPL; ++dd) {
+        store_pack<T, 8>(sKhT + (DPL * l + dd) * Lay::LDKH + 8 * w, kh[dd]);
+        if (w == 0) sBexp[DPL * l + dd] = eB[dd];
+      }
+      // raw keys into the ring
+  #pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        T* krp = sK + (kc + 8 * w + rr) * Lay::LDK + DPL * l;
+        if constexpr (DPL * sizeof(T) == 4) *reinterpret_cast<uint32_t*>(krp) = kA[rr];
+        else krp[0] = from_f32<T>(elem32(kA[rr], 0));
+      }
+      // values, transposed into their ring slot: sVt[j][vc + s], 4 tokens per write
+      if constexpr (sizeof(T) == 2) {
+        // columns 2vj and 2vj+1 of 4 consecutive rows: regroup the 16-bit halves
+        const uint2 lo = make_uint2(__builtin_amdgcn_perm(vA[1], vA[0], 0x05040100u),
+                                    __builtin_amdgcn_perm(vA[3], vA[2], 0x05040100u));
+        const uint2 hi = make_uint2(__builtin_amdgcn_perm(vA[1], vA[0], 0x07060302u),
+                                    __builtin_amdgcn_perm(vA[3], vA[2], 0x07060302u));
+        *reinterpret_cast<uint2*>(sVt + (2 * vj) * Lay::LDVT + vc + VR * vs) = lo;
+        *reinterpret_cast<uint2*>(sVt + (2 * vj + 1) * Lay::LDVT + vc + VR * vs) = hi;
+      } else {
+        *reinterpret_cast<uint4*>(sVt + vj * Lay::LDVT + vc + VR * vs) = make_uint4(vA[0], vA[1], vA[2], vA[3]);
+      }
+      if constexpr (GATE) {
+        if constexpr (!STATES) {
+          // S_cc (rounded to the element type) for the readout: sSt[j][i], 4 rows i per write
+  #pragma unroll
+          for (int rt = 0; rt < DPL; ++rt)
+  #pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+              const float sv[4] = {acc[rt][ct][0], acc[rt][ct][1], acc[rt][ct][2], acc[rt][ct][3]};
+              store_pack<T, 4>(sSt + (16 * ct + m_lane) * Lay::LDST + 16 * (DPL * I + rt) + 4 * g_lane, sv);
+            }
+        } else {
+          // chunk-start state for the backward pass: S_cc[i][j], row-major
+          const int ncs = (L + C - 1) / C;
+          T* sg = reinterpret_cast<T*>(a.states) + ((size_t)bh * ncs + cc) * D * D + j0;
+  #pragma unroll
+          for (int rt = 0; rt < DPL; ++rt)
+  #pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+  #pragma unroll
+              for (int r = 0; r < 4; ++r)
+                sg[(size_t)(16 * (DPL * I + rt) + 4 * g_lane + r) * D + 16 * ct + m_lane] = from_f32<T>(acc[rt][ct][r]);
+        }
+      }
+      return pairwise;
+    };
+
+    // ---- state carry over chunk c: S = 2^B * S + Kh^T V (gate wavefronts) ----
+    auto carry = [&](int vc, int m, int g) __attribute__((always_inline)) {
+  #pragma unroll
+      for (int rt = 0; rt < DPL; ++rt) {
+        const int ib = 16 * (DPL * I + rt);
+        float dec[4];
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) dec[r] = sBexp[ib + 4 * g + r];
+        const T* kp = sKhT + (ib + m) * Lay::LDKH + g * 16;
+  #pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          f32x4 s = acc[rt][ct];
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) s[r] *= dec[r];
+          const T* vp = sVt + (16 * ct + m) * Lay::LDVT + vc + g * 16;
+  #pragma unroll
+          for (int e = 0; e < 16 / M::KPL; ++e) s = M::mma(M::load(kp + e * M::KPL), M::load(vp + e * M::KPL), s);
+          acc[rt][ct] = s;
+        }
+      }
+    };
+
+    const int nc = (L + C - 1) / C;
+    bool pw = false;                      // pairwise path for the chunk about to be processed
+    if (nc > 0) {
+      load_chunk(0);
+      if constexpr (!GATE && !STATES) load_q(0);
+      prefix_part();
+    }
+    __syncthreads();
+    if (nc > 0) {
+      pw = operand_part(0);
+      if (nc > 1) load_chunk(1);
+    }
+    __syncthreads();
+
+    for (int c = 0; c < nc; ++c) {
+      const int t0 = c * C;
+      const int kcur = (c & 1) * 64;      // key ring half of this chunk
+      const int kprv = 64 - kcur;         // ... and of the previous chunk
+      const int vcur = (c % 3) * 64;      // value ring slot of this chunk
+      const int vprv = ((c + 2) % 3) * 64;   // ... and of the previous chunk
+      const bool pairwise = pw;
+
+      // ================= interval 1, softmax wavefront: weights of block QB ====
+      auto softmax_part = [&](auto Ic) __attribute__((always_inline)) {
+        constexpr int QB = decltype(Ic)::value;
+        constexpr int U0 = 16 * QB < 32 ? 16 * QB : 32; // first window key (of [prev; cur]) staged
+        // Lane indices laundered through an empty asm: addresses derived from
+        // them are recomputed per chunk instead of being hoisted out of the
+        // chunk loop by every instance (which would exhaust registers).
+        int m = m_lane, g = g_lane;
+        asm volatile("" : "+v"(m), "+v"(g));
+        const int tme = t0 + 16 * QB + m;
+        frag qf[NF];
+  #pragma unroll
+        for (int e = 0; e < NF; ++e) qf[e] = frag_at<T>(qraw, e);
+        // the next chunk's queries (qf holds this chunk's).  Issued on every
+        // chunk (the last one reloads itself) so that the number of memory
+        // operations between a load and its use is the same on every path:
+        // the wait for it then counts, instead of draining all loads in flight.
+        load_q(c + 1 < nc ? c + 1 : c);
+
+        // anchor logits Z^T[u][t] over the 6 window tiles kt (keys u in
+        // [U0+16kt, U0+16kt+16) of [prev; cur]); every tile is computed, keys
+        // outside the window are masked below (branch-free: a skipped tile
+        // would make the compiler copy the logit arrays between paths)
+        f32x4 z[6];
+  #pragma unroll
+        for (int kt = 0; kt < 6; ++kt) {
+          const T* kp = sK + ((U0 + 16 * kt + kprv + m) & 127) * Lay::LDK + g * (D / 4);
+          z[kt] = zero4();
+  #pragma unroll
+          for (int e = 0; e < NF; ++e) z[kt] = M::mma(M::load(kp + e * M::KPL), qf[e], z[kt]);
+        }
+        f32x4 zs = zero4();
+  #pragma unroll
+        for (int e = 0; e < NF; ++e) zs = M::mma(M::load(sMeta + m * Lay::LDK + g * (D / 4) + e * M::KPL), qf[e], zs);
+
+        // Softmax: maxima on raw logits (the scale is positive), scale folded
+        // into the exponent: P = 2^{z * scale*log2e - max}.
+        float mr = -INFINITY;
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          zs[r] = 4 * g + r < a.n_meta ? zs[r] : -INFINITY;
+          mr = fmaxf(mr, zs[r]);
+        }
+        // key valid iff 0 <= t - s < lim; in the first chunk also s >= 0 (t - s <= t)
+        const int lim = (c == 0 && 16 * QB + m + 1 < a.window) ? 16 * QB + m + 1 : a.window;
+        const int lim_lo = (c == 0 && 16 * QB + 1 < a.window) ? 16 * QB + 1 : a.window;   // over the block
+        const int dl = m - 4 * g;            // t - s = K_kt + dl - r
+  #pragma unroll
+        for (int kt = 0; kt < 6; ++kt) {
+          // t - s over the tile spans [K_kt - 15, K_kt + 15]: tiles inside the band skip the mask
+          constexpr int K0 = 16 * QB + 64 - U0;
+          const int Kt = K0 - 16 * kt;
+          if (!(Kt - 15 >= 0 && Kt + 15 < lim_lo)) {
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) z[kt][r] = (unsigned)(Kt + dl - r) < (unsigned)lim ? z[kt][r] : -INFINITY;
+          }
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) mr = fmaxf(mr, z[kt][r]);
+        }
+        mr = xgroup_max(mr);                 // finite: the query's own key is always valid
+        const float mref = mr * a.scale_log2;
+        float sr = 0.f;
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) sr += exp_2(fmaf(zs[r], a.scale_log2, -mref));
+  #pragma unroll
+        for (int kt = 0; kt < 6; ++kt) {
+          float p[4];
+  #pragma unroll
           for (int r = 0; r < 4; ++r) {
             p[r] = exp_2(fmaf(z[kt][r], a.scale_log2, -mref));   // 2^-inf = 0 for masked keys
             sr += p[r];
           }
+          store_pack<T, 4>(sP + (16 * QB + m) * Lay::LDP + 16 * kt + 4 * g, p);
         }
-        store_pack<T, 4>(sP + (16 * QB + m) * Lay::LDP + 16 * kt + 4 * g, p);
-      }
-      const float den = xgroup_sum(sr);
-      if (g == 0) {
-        const float inv = 1.0f / den;
-        sSc[16 * QB + m] = a.alpha * inv;
-        sSc[64 + 16 * QB + m] = inv;
-        if (lseg && tme < L) lseg[tme] = (mref + __log2f(den)) * kLn2;
-      }
-    };
-
-    // ========== interval 1, gate wavefront: gated output, state carry ========
-    auto gate_part = [&](auto Ic) __attribute__((always_inline)) {
-      constexpr int QB = decltype(Ic)::value;
-      int m = m_lane, g = g_lane;
-      asm volatile("" : "+v"(m), "+v"(g));
-      const int tme = t0 + 16 * QB + m;
-
-      // Qe = q * 2^beta of this lane's query (B operand)
-      frag qe[NF];
-      if (!pairwise) {
-        const T* ep = sQe + (16 * QB + m) * Lay::LDK + g * (D / 4);
-#pragma unroll
-        for (int e = 0; e < NF; ++e) qe[e] = M::load(ep + e * M::KPL);
-      } else {
-        uint4 raw[QV];
-        const T* qp = qg + (size_t)(tme < L ? tme : 0) * D + g * (D / 4);
-#pragma unroll
-        for (int e = 0; e < QV; ++e) raw[e] = tme < L ? ld16(qp + e * EPV) : make_uint4(0, 0, 0, 0);
-        const float* bp = sBeta + (16 * QB + m) * Lay::LDE + g * (D / 4);
-#pragma unroll
-        for (int e = 0; e < NF; ++e) {
-          float tmp[M::KPL];
-#pragma unroll
-          for (int u = 0; u < M::KPL; ++u) tmp[u] = elem_f32<T>(raw, e * M::KPL + u) * exp_2(bp[e * M::KPL + u]);
-          qe[e] = M::pack(tmp);
+        const float den = xgroup_sum(sr);
+        if (g == 0) {
+          const float inv = 1.0f / den;
+          sSc[16 * QB + m] = a.alpha * inv;
+          sSc[64 + 16 * QB + m] = inv;
+          if (lseg && tme < L) lseg[tme] = (mref + __log2f(den)) * kLn2;
         }
-      }
+      };
 
-      // ---- intra-chunk gated scores A^T[s][t], key blocks J <= QB ----
-      f32x4 ai[QB + 1];
-#pragma unroll
-      for (int J = 0; J <= QB; ++J) {
-        ai[J] = zero4();
+      // ========== interval 1, gate wavefront: gated output, state carry ========
+      auto gate_part = [&](auto Ic) __attribute__((always_inline)) {
+        constexpr int QB = decltype(Ic)::value;
+        int m = m_lane, g = g_lane;
+        asm volatile("" : "+v"(m), "+v"(g));
+        const int tme = t0 + 16 * QB + m;
+
+        // Qe = q * 2^beta of this lane's query (B operand)
+        frag qe[NF];
         if (!pairwise) {
-          const T* kp = sKp + (16 * J + m) * Lay::LDK + g * (D / 4);
-#pragma unroll
-          for (int e = 0; e < NF; ++e) ai[J] = M::mma(M::load(kp + e * M::KPL), qe[e], ai[J]);
+          const T* ep = sQe + (16 * QB + m) * Lay::LDK + g * (D / 4);
+  #pragma unroll
+          for (int e = 0; e < NF; ++e) qe[e] = M::load(ep + e * M::KPL);
         } else {
-          // pairwise gate products in fp32 (a decay span too wide to factorise)
-          const T* qrow = qg + (size_t)(tme < L ? tme : 0) * D;
-          const float* bt = sBeta + (16 * QB + m) * Lay::LDE;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int ks = 16 * J + 4 * g + r;
-            float sum = 0.f;
-            if (ks <= 16 * QB + m && tme < L) {
-              const T* krow = sK + (kcur + ks) * Lay::LDK;
-              const float* bs = sBeta + ks * Lay::LDE;
-              for (int i = 0; i < D; ++i) sum += to_f32(qrow[i]) * to_f32(krow[i]) * exp_2(bt[i] - bs[i]);
+          uint4 raw[QV];
+          const T* qp = qg + (size_t)(tme < L ? tme : 0) * D + g * (D / 4);
+  #pragma unroll
+          for (int e = 0; e < QV; ++e) raw[e] = tme < L ? ld16(qp + e * EPV) : make_uint4(0, 0, 0, 0);
+          const float* bp = sBeta + (16 * QB + m) * Lay::LDE + g * (D / 4);
+  #pragma unroll
+          for (int e = 0; e < NF; ++e) {
+            float tmp[M::KPL];
+  #pragma unroll
+            for (int u = 0; u < M::KPL; ++u) tmp[u] = elem_f32<T>(raw, e * M::KPL + u) * exp_2(bp[e * M::KPL + u]);
+            qe[e] = M::pack(tmp);
+          }
+        }
+
+        // ---- intra-chunk gated scores A^T[s][t], key blocks J <= QB ----
+        f32x4 ai[QB + 1];
+  #pragma unroll
+        for (int J = 0; J <= QB; ++J) {
+          ai[J] = zero4();
+          if (!pairwise) {
+            const T* kp = sKp + (16 * J + m) * Lay::LDK + g * (D / 4);
+  #pragma unroll
+            for (int e = 0; e < NF; ++e) ai[J] = M::mma(M::load(kp + e * M::KPL), qe[e], ai[J]);
+          } else {
+            // pairwise gate products in fp32 (a decay span too wide to factorise)
+            const T* qrow = qg + (size_t)(tme < L ? tme : 0) * D;
+            const float* bt = sBeta + (16 * QB + m) * Lay::LDE;
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int ks = 16 * J + 4 * g + r;
+              float sum = 0.f;
+              if (ks <= 16 * QB + m && tme < L) {
+                const T* krow = sK + (kcur + ks) * Lay::LDK;
+                const float* bs = sBeta + ks * Lay::LDE;
+                for (int i = 0; i < D; ++i) sum += to_f32(qrow[i]) * to_f32(krow[i]) * exp_2(bt[i] - bs[i]);
+              }
+              ai[J][r] = sum;
             }
-            ai[J][r] = sum;
+          }
+          if (J == QB) {
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) ai[J][r] = 4 * g + r <= m ? ai[J][r] : 0.f;
           }
         }
-        if (J == QB) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) ai[J][r] = 4 * g + r <= m ? ai[J][r] : 0.f;
-        }
-      }
 
-      if constexpr (Lay::STAGE_A) {
-        // A[t][s] of this block into its own staging rows (keys of blocks
-        // J > QB are zero), read back by this wavefront only
-#pragma unroll
-        for (int J = 0; J < 4; ++J) {
-          float v4[4] = {0.f, 0.f, 0.f, 0.f};
-          if (J <= QB) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) v4[r] = ai[J < QB + 1 ? J : 0][r];
-          }
-          store_pack<T, 4>(sA + (16 * QB + m) * Lay::LDA + 16 * J + 4 * g, v4);
-        }
-        wave_lds_sync();
-      }
-
-      // ---- gated output O^T[j][t] = S_c^T Qe^T + V^T A^T ----
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        f32x4 o = zero4();
-        const T* sp = sSt + (16 * ct + m) * Lay::LDST + g * (D / 4);
-#pragma unroll
-        for (int e = 0; e < NF; ++e) o = M::mma(M::load(sp + e * M::KPL), qe[e], o);
         if constexpr (Lay::STAGE_A) {
-          const T* vp = sVt + (16 * ct + m) * Lay::LDVT + vcur + g * 16;
-          const T* ap = sA + (16 * QB + m) * Lay::LDA + g * 16;
-#pragma unroll
-          for (int e = 0; e < 16 / M::KPL; ++e) o = M::mma(M::load(vp + e * M::KPL), M::load(ap + e * M::KPL), o);
-        } else {
-          const float* vp = reinterpret_cast<const float*>(sVt) + (16 * ct + m) * Lay::LDVT + vcur + 4 * g;
-#pragma unroll
-          for (int J = 0; J <= QB; ++J) o = mma_tile_regs_f32(vp + 16 * J, ai[J], o);
+          // A[t][s] of this block into its own staging rows (keys of blocks
+          // J > QB are zero), read back by this wavefront only
+  #pragma unroll
+          for (int J = 0; J < 4; ++J) {
+            float v4[4] = {0.f, 0.f, 0.f, 0.f};
+            if (J <= QB) {
+  #pragma unroll
+              for (int r = 0; r < 4; ++r) v4[r] = ai[J < QB + 1 ? J : 0][r];
+            }
+            store_pack<T, 4>(sA + (16 * QB + m) * Lay::LDA + 16 * J + 4 * g, v4);
+          }
+          wave_lds_sync();
         }
-        rq[ct] = __builtin_bit_cast(uint4, o);
-      }
-      carry(vcur, m, g);
-    };
 
-    // ========== interval 2, gate wavefront: anchor product and output =======
-    auto output_part = [&](auto Ic) __attribute__((always_inline)) {
-      constexpr int QB = decltype(Ic)::value;
-      constexpr int U0 = 16 * QB < 32 ? 16 * QB : 32;
-      int m = m_lane, g = g_lane;
-      asm volatile("" : "+v"(m), "+v"(g));
-      const int tme = t0 + 16 * QB + m;
-      const float sc = sSc[16 * QB + m];
-      const float inv = sSc[64 + 16 * QB + m];
-      const T* pp = sP + (16 * QB + m) * Lay::LDP + g * 24;
-      // V^T column of window key u of [prev; cur]: the previous slot is
-      // followed by the current one in the 3-slot ring
-      int col[24 / M::KPL];
-#pragma unroll
-      for (int e = 0; e < 24 / M::KPL; ++e) {
-        const unsigned v = vprv + U0 + g * 24 + e * M::KPL;
-        col[e] = (int)min(v, v - 192u);
-      }
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        f32x4 o = zero4();
-        const T* vrow = sVt + (16 * ct + m) * Lay::LDVT;
-#pragma unroll
-        for (int e = 0; e < 24 / M::KPL; ++e) o = M::mma(M::load(vrow + col[e]), M::load(pp + e * M::KPL), o);
-        if (tme < L) {
-          const f32x4 og = __builtin_bit_cast(f32x4, rq[ct]);
-          const float v4[4] = {fmaf(sc, o[0], og[0]), fmaf(sc, o[1], og[1]),
-                               fmaf(sc, o[2], og[2]), fmaf(sc, o[3], og[3])};
-          store_pack<T, 4>(yg + (size_t)tme * D + 16 * ct + 4 * g, v4);
-          if (yag) {
-            const float a4[4] = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
-            store_pack<T, 4>(yag + (size_t)tme * D + 16 * ct + 4 * g, a4);
+        // ---- gated output O^T[j][t] = S_c^T Qe^T + V^T A^T ----
+  #pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          f32x4 o = zero4();
+          const T* sp = sSt + (16 * ct + m) * Lay::LDST + g * (D / 4);
+  #pragma unroll
+          for (int e = 0; e < NF; ++e) o = M::mma(M::load(sp + e * M::KPL), qe[e], o);
+          if constexpr (Lay::STAGE_A) {
+            const T* vp = sVt + (16 * ct + m) * Lay::LDVT + vcur + g * 16;
+            const T* ap = sA + (16 * QB + m) * Lay::LDA + g * 16;
+  #pragma unroll
+            for (int e = 0; e < 16 / M::KPL; ++e) o = M::mma(M::load(vp + e * M::KPL), M::load(ap + e * M::KPL), o);
+          } else {
+            const float* vp = reinterpret_cast<const float*>(sVt) + (16 * ct + m) * Lay::LDVT + vcur + 4 * g;
+  #pragma unroll
+            for (int J = 0; J <= QB; ++J) o = mma_tile_regs_f32(vp + 16 * J, ai[J], o);
+          }
+          og[ct] = o;
+        }
+        carry(vcur, m, g);
+      };
+
+      // ========== interval 2, gate wavefront: anchor product and output =======
+      auto output_part = [&](auto Ic) __attribute__((always_inline)) {
+        constexpr int QB = decltype(Ic)::value;
+        constexpr int U0 = 16 * QB < 32 ? 16 * QB : 32;
+        int m = m_lane, g = g_lane;
+        asm volatile("" : "+v"(m), "+v"(g));
+        const int tme = t0 + 16 * QB + m;
+        const float sc = sSc[16 * QB + m];
+        const float inv = sSc[64 + 16 * QB + m];
+        const T* pp = sP + (16 * QB + m) * Lay::LDP + g * 24;
+        // V^T column of window key u of [prev; cur]: the previous slot is
+        // followed by the current one in the 3-slot ring
+        int col[24 / M::KPL];
+  #pragma unroll
+        for (int e = 0; e < 24 / M::KPL; ++e) {
+          const unsigned v = vprv + U0 + g * 24 + e * M::KPL;
+          col[e] = (int)min(v, v - 192u);
+        }
+  #pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          f32x4 o = zero4();
+          const T* vrow = sVt + (16 * ct + m) * Lay::LDVT;
+  #pragma unroll
+          for (int e = 0; e < 24 / M::KPL; ++e) o = M::mma(M::load(vrow + col[e]), M::load(pp + e * M::KPL), o);
+          if (tme < L) {
+            const float v4[4] = {fmaf(sc, o[0], og[ct][0]), fmaf(sc, o[1], og[ct][1]),
+                                 fmaf(sc, o[2], og[ct][2]), fmaf(sc, o[3], og[ct][3])};
+            store_pack<T, 4>(yg + (size_t)tme * D + 16 * ct + 4 * g, v4);
+            if (yag) {
+              const float a4[4] = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+              store_pack<T, 4>(yag + (size_t)tme * D + 16 * ct + 4 * g, a4);
+            }
           }
         }
-      }
-    };
+      };
 
-    // ---- interval 1 ----
-    if constexpr (STATES) {
-      if (gate) carry(vcur, m_lane, g_lane);
-    } else {
-      switch (w) {
-        case 0: softmax_part(std::integral_constant<int, 0>{}); break;
-        case 1: softmax_part(std::integral_constant<int, 1>{}); break;
-        case 2: softmax_part(std::integral_constant<int, 2>{}); break;
-        case 3: softmax_part(std::integral_constant<int, 3>{}); break;
-        case 4: gate_part(std::integral_constant<int, 0>{}); break;
-        case 5: gate_part(std::integral_constant<int, 1>{}); break;
-        case 6: gate_part(std::integral_constant<int, 2>{}); break;
-        default: gate_part(std::integral_constant<int, 3>{}); break;
+      // ---- interval 1 ----
+      if constexpr (STATES) {
+        if constexpr (GATE) carry(vcur, m_lane, g_lane);
+      } else if constexpr (GATE) {
+        gate_part(Ic);
+      } else {
+        softmax_part(Ic);
       }
-    }
-    if (c + 1 < nc) prefix_part();
-    __syncthreads();
+      if (c + 1 < nc) prefix_part();
+      __syncthreads();
 
-    // ---- interval 2 ----
-    if constexpr (!STATES) {
-      switch (w) {
-        case 4: output_part(std::integral_constant<int, 0>{}); break;
-        case 5: output_part(std::integral_constant<int, 1>{}); break;
-        case 6: output_part(std::integral_constant<int, 2>{}); break;
-        case 7: output_part(std::integral_constant<int, 3>{}); break;
-        default: break;
-      }
+      // ---- interval 2 ----
+      if constexpr (GATE && !STATES) output_part(Ic);
+      if (c + 1 < nc) pw = operand_part(c + 1);
+      // chunk c+2 (clamped: issued on every chunk for the same reason as load_q)
+      load_chunk(c + 2 < nc ? c + 2 : nc - 1);
+      __syncthreads();
     }
-    if (c + 1 < nc) {
-      pw = operand_part(c + 1);
-      if (c + 2 < nc) load_chunk(c + 2);
-    }
-    __syncthreads();
-  }
 
-  if (a.state_out && gate) {
-    float* so = a.state_out + (size_t)bh * D * D;
-#pragma unroll
-    for (int rt = 0; rt < DPL; ++rt)
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          so[(size_t)(16 * (DPL * I + rt) + 4 * g_lane + r) * D + j0 + 16 * ct + m_lane] = acc[rt][ct][r];
+    if (GATE && a.state_out) {
+      float* so = a.state_out + (size_t)bh * D * D;
+  #pragma unroll
+      for (int rt = 0; rt < DPL; ++rt)
+  #pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+  #pragma unroll
+          for (int r = 0; r < 4; ++r)
+            so[(size_t)(16 * (DPL * I + rt) + 4 * g_lane + r) * D + j0 + 16 * ct + m_lane] = acc[rt][ct][r];
+    }
+  };
+  switch (w) {
+    case 0: run(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}); break;
+    case 1: run(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}); break;
+    case 2: run(std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{}); break;
+    case 3: run(std::integral_constant<int, 0>{}, std::integral_constant<int, 3>{}); break;
+    case 4: run(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}); break;
+    case 5: run(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}); break;
+    case 6: run(std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{}); break;
+    default: run(std::integral_constant<int, 1>{}, std::integral_constant<int, 3>{}); break;
   }
 }
 
