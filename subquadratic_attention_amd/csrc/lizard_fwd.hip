@@ -705,17 +705,30 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
           const unsigned v = vprv + U0 + g * 24 + e * M::KPL;
           col[e] = (int)min(v, v - 192u);
         }
+        // all column tiles first (independent MFMA chains in one block), then
+        // the stores under one condition
+        f32x4 oa[NCT];
   #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          f32x4 o = zero4();
-          const T* vrow = sVt + (16 * ct + m) * Lay::LDVT;
+        for (int ct = 0; ct < NCT; ++ct) oa[ct] = zero4();
   #pragma unroll
-          for (int e = 0; e < 24 / M::KPL; ++e) o = M::mma(M::load(vrow + col[e]), M::load(pp + e * M::KPL), o);
-          if (tme < L) {
+        for (int e = 0; e < 24 / M::KPL; ++e) {
+          const typename M::frag pf = M::load(pp + e * M::KPL);
+  #pragma unroll
+          for (int ct = 0; ct < NCT; ++ct)
+            oa[ct] = M::mma(M::load(sVt + (16 * ct + m) * Lay::LDVT + col[e]), pf, oa[ct]);
+        }
+        if (tme < L) {
+  #pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) {
+            const f32x4 o = oa[ct];
             const float v4[4] = {fmaf(sc, o[0], og[ct][0]), fmaf(sc, o[1], og[ct][1]),
                                  fmaf(sc, o[2], og[ct][2]), fmaf(sc, o[3], og[ct][3])};
             store_pack<T, 4>(yg + (size_t)tme * D + 16 * ct + 4 * g, v4);
-            if (yag) {
+          }
+          if (yag) {
+  #pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+              const f32x4 o = oa[ct];
               const float a4[4] = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
               store_pack<T, 4>(yag + (size_t)tme * D + 16 * ct + 4 * g, a4);
             }
