@@ -24,12 +24,12 @@
 //   1. the forward kernel in its states-only mode writes S_c for every chunk;
 //   2. bwd_dstate walks the chunks in reverse and writes G_{c+1} (and its
 //      transpose) for every chunk;
-//   3. bwd_anchor_q (per chunk of queries): D_t, the anchor part of dq, and
-//      per-chunk sink-key gradients;
+//   3. bwd_anchor_q (per chunk of queries): D_t, the anchor part of dq
+//      (written into dq), and per-chunk sink-key gradients;
 //   4. bwd_anchor_k (per chunk of keys, queries of this and the next chunk):
-//      the anchor parts of dk and dv;
-//   5. bwd_gate (per chunk): the gated dq, dk, dv, adds the anchor parts and
-//      writes the outputs; writes q*dq - k*dk into dlog_g;
+//      the anchor parts of dk and dv (written into dk, dv);
+//   5. bwd_gate (per chunk): the gated dq, dk, dv, added to the anchor parts
+//      in the outputs; writes q*dq - k*dk into dlog_g;
 //   6. bwd_dlogg_scan: reverse cumulative sum of dlog_g along the sequence;
 //   7. bwd_dmeta_reduce: sums the sink-key partials over batch and chunks in
 //      a fixed order (deterministic, no float atomics).
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(256, 1) void bwd_anchor_q_kernel(BwdArgs a) {
   }
   wave_lds_sync();
   // dq^T[d][t] = scale (K^T dZ^T + mu^T dZs^T)
-  float* dqa = a.ws_dqa + (size_t)bh * L * D;
+  T* dqa = reinterpret_cast<T*>(a.dq) + (size_t)bh * L * D;   // the anchor part; the gate kernel adds its own
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
     f32x4 o = zero4();
@@ -410,9 +410,10 @@ __global__ __launch_bounds__(256, 1) void bwd_anchor_q_kernel(BwdArgs a) {
     const T* az = sMuT + (16 * dt + m) * Lay::LDMT + g * 8;
 #pragma unroll
     for (int e = 0; e < 8 / M::KPL; ++e) o = M::mma(M::load(az + e * M::KPL), M::load(bz + e * M::KPL), o);
-    if (tme < L)
-      *reinterpret_cast<f32x4*>(dqa + (size_t)tme * D + 16 * dt + 4 * g) =
-          f32x4{o[0] * a.scale, o[1] * a.scale, o[2] * a.scale, o[3] * a.scale};
+    if (tme < L) {
+      const float v4[4] = {o[0] * a.scale, o[1] * a.scale, o[2] * a.scale, o[3] * a.scale};
+      store_pack<T, 4>(dqa + (size_t)tme * D + 16 * dt + 4 * g, v4);
+    }
   }
   __syncthreads();
   // per-chunk sink-key gradient: dmu[i][d] = scale sum_t dZs[t][i] q[t][d]
@@ -519,8 +520,9 @@ __global__ __launch_bounds__(256, 1) void bwd_anchor_k_kernel(BwdArgs a) {
     store_pack<T, 4>(sP + m * Lay::LDS + 16 * kt + 4 * g, pp);
   }
   wave_lds_sync();
-  float* dka = a.ws_dka + (size_t)bh * L * D;
-  float* dva = a.ws_dva + (size_t)bh * L * D;
+  // the anchor parts of dk and dv; the gate kernel adds its own
+  T* dka = reinterpret_cast<T*>(a.dk) + (size_t)bh * L * D;
+  T* dva = reinterpret_cast<T*>(a.dv) + (size_t)bh * L * D;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
     f32x4 ok_ = zero4(), ov = zero4();
@@ -534,9 +536,10 @@ __global__ __launch_bounds__(256, 1) void bwd_anchor_k_kernel(BwdArgs a) {
       ov = M::mma(M::load(ay + e * M::KPL), M::load(bpp + e * M::KPL), ov);
     }
     if (sme < L) {
-      *reinterpret_cast<f32x4*>(dka + (size_t)sme * D + 16 * dt + 4 * g) =
-          f32x4{ok_[0] * a.scale, ok_[1] * a.scale, ok_[2] * a.scale, ok_[3] * a.scale};
-      *reinterpret_cast<f32x4*>(dva + (size_t)sme * D + 16 * dt + 4 * g) = ov;
+      const float k4[4] = {ok_[0] * a.scale, ok_[1] * a.scale, ok_[2] * a.scale, ok_[3] * a.scale};
+      const float v4[4] = {ov[0], ov[1], ov[2], ov[3]};
+      store_pack<T, 4>(dka + (size_t)sme * D + 16 * dt + 4 * g, k4);
+      store_pack<T, 4>(dva + (size_t)sme * D + 16 * dt + 4 * g, v4);
     }
   }
 }
@@ -713,43 +716,47 @@ __global__ __launch_bounds__(256, 1) void bwd_gate_kernel(BwdArgs a) {
   T* dko = reinterpret_cast<T*>(a.dk) + (size_t)bh * L * D;
   T* dvo = reinterpret_cast<T*>(a.dv) + (size_t)bh * L * D;
   float* dbo = a.dlog_g + (size_t)bh * L * D;
-  const float* dqa = a.ws_dqa + (size_t)bh * L * D;
-  const float* dka = a.ws_dka + (size_t)bh * L * D;
-  const float* dva = a.ws_dva + (size_t)bh * L * D;
+  // state rows of this wavefront's dim tiles, loaded once for the 4 token blocks
+  uint4 Sr[NIT][QV], Gr[NIT][QV], GTr[NIT][QV];
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
     const int ib = w * (D / 4) + 16 * it;     // first dim of this 16-row tile
-    uint4 Sr[QV], Gr[QV], GTr[QV];
-    load_quarter<T, D>(Sr, Sg, ib + m, D, g);     // S_c rows i (k = j)
-    load_quarter<T, D>(Gr, Gg, ib + m, D, g);     // G_{c+1} rows i (k = j)
-    load_quarter<T, D>(GTr, GTg, ib + m, D, g);   // G_{c+1}^T rows j (k = i)
+    load_quarter<T, D>(Sr[it], Sg, ib + m, D, g);     // S_c rows i (k = j)
+    load_quarter<T, D>(Gr[it], Gg, ib + m, D, g);     // G_{c+1} rows i (k = j)
+    load_quarter<T, D>(GTr[it], GTg, ib + m, D, g);   // G_{c+1}^T rows j (k = i)
+  }
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const int trow = t0 + 16 * tt + m;        // token of this lane's output column
-      uint4 dyr[QV], vr[QV], kr[QV];
-      load_quarter<T, D>(dyr, dyg, trow, L, g);
-      load_quarter<T, D>(vr, vg, trow, L, g);
-      load_quarter<T, D>(kr, kg, trow, L, g);
+  for (int tt = 0; tt < 4; ++tt) {
+    const int trow = t0 + 16 * tt + m;        // token of this lane's output column
+    uint4 dyr[QV], vr[QV], kr[QV];
+    load_quarter<T, D>(dyr, dyg, trow, L, g);
+    load_quarter<T, D>(vr, vg, trow, L, g);
+    load_quarter<T, D>(kr, kg, trow, L, g);
+    // Kh_s = k_s * 2^{B - beta_s} as fragments (rows s, k = i)
+    frag khf[NF];
+    {
+      const float* bp = sBeta + (16 * tt + m) * Lay::LDB + g * (D / 4);
+#pragma unroll
+      for (int e = 0; e < NF; ++e) {
+        float tk[M::KPL];
+#pragma unroll
+        for (int u = 0; u < M::KPL; ++u) {
+          const int kk = e * M::KPL + u;
+          tk[u] = elem_of<T>(kr, kk) * exp_2(sBx[g * (D / 4) + kk] - bp[kk]);
+        }
+        khf[e] = M::pack(tk);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int ib = w * (D / 4) + 16 * it;   // first dim of this 16-row tile
       // inter-chunk parts
       f32x4 qi = zero4(), ki = zero4(), vi = zero4();
 #pragma unroll
       for (int e = 0; e < NF; ++e) {
-        qi = M::mma(frag_of<T>(Sr, e), frag_of<T>(dyr, e), qi);     // (S dO_t)_i
-        ki = M::mma(frag_of<T>(Gr, e), frag_of<T>(vr, e), ki);      // (G v_s)_i
-      }
-      // Kh_s = k_s * 2^{B - beta_s} as a fragment (rows s, k = i)
-      {
-        const float* bp = sBeta + (16 * tt + m) * Lay::LDB + g * (D / 4);
-#pragma unroll
-        for (int e = 0; e < NF; ++e) {
-          float tk[M::KPL];
-#pragma unroll
-          for (int u = 0; u < M::KPL; ++u) {
-            const int kk = e * M::KPL + u;
-            tk[u] = elem_of<T>(kr, kk) * exp_2(sBx[g * (D / 4) + kk] - bp[kk]);
-          }
-          vi = M::mma(frag_of<T>(GTr, e), M::pack(tk), vi);         // (G^T Kh_s)_j
-        }
+        qi = M::mma(frag_of<T>(Sr[it], e), frag_of<T>(dyr, e), qi);     // (S dO_t)_i
+        ki = M::mma(frag_of<T>(Gr[it], e), frag_of<T>(vr, e), ki);      // (G v_s)_i
+        vi = M::mma(frag_of<T>(GTr[it], e), khf[e], vi);                // (G^T Kh_s)_j
       }
       // intra-chunk parts
       f32x4 qa = zero4(), ka = zero4(), va = zero4();
@@ -775,9 +782,15 @@ __global__ __launch_bounds__(256, 1) void bwd_gate_kernel(BwdArgs a) {
         const int tl = 16 * tt + m;
         const float* bt = sBeta + tl * Lay::LDB + ib + 4 * g;
         float dqv[4], dkv[4], dvv[4], dbv[4];
-        const f32x4 aq = *reinterpret_cast<const f32x4*>(dqa + (size_t)trow * D + ib + 4 * g);
-        const f32x4 ak = *reinterpret_cast<const f32x4*>(dka + (size_t)trow * D + ib + 4 * g);
-        const f32x4 av = *reinterpret_cast<const f32x4*>(dva + (size_t)trow * D + ib + 4 * g);
+        // the anchor parts (written into the outputs by the anchor kernels),
+        // and q, k of these 4 dims for dlog_g
+        const size_t o4 = (size_t)trow * D + ib + 4 * g;
+        float aq[4], ak[4], av[4], q4[4], k4[4];
+        load_pack<T, 4>(dqo + o4, aq);
+        load_pack<T, 4>(dko + o4, ak);
+        load_pack<T, 4>(dvo + o4, av);
+        load_pack<T, 4>(qg + o4, q4);
+        load_pack<T, 4>(kg + o4, k4);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = ib + 4 * g + r;
@@ -799,17 +812,15 @@ __global__ __launch_bounds__(256, 1) void bwd_gate_kernel(BwdArgs a) {
           }
           const float dqg = exp_2(b) * qi[r] + qin;
           const float dkg = exp_2(sBx[i] - b) * ki[r] + kin;
-          const float qv = to_f32(qg[(size_t)trow * D + i]);
-          const float kv = to_f32(kg[(size_t)trow * D + i]);
-          dbv[r] = qv * dqg - kv * dkg;
+          dbv[r] = q4[r] * dqg - k4[r] * dkg;
           dqv[r] = dqg + aq[r];
           dkv[r] = dkg + ak[r];
           dvv[r] = vi[r] + va[r] + av[r];
         }
-        store_pack<T, 4>(dqo + (size_t)trow * D + ib + 4 * g, dqv);
-        store_pack<T, 4>(dko + (size_t)trow * D + ib + 4 * g, dkv);
-        store_pack<T, 4>(dvo + (size_t)trow * D + ib + 4 * g, dvv);
-        *reinterpret_cast<f32x4*>(dbo + (size_t)trow * D + ib + 4 * g) = f32x4{dbv[0], dbv[1], dbv[2], dbv[3]};
+        store_pack<T, 4>(dqo + o4, dqv);
+        store_pack<T, 4>(dko + o4, dkv);
+        store_pack<T, 4>(dvo + o4, dvv);
+        *reinterpret_cast<f32x4*>(dbo + o4) = f32x4{dbv[0], dbv[1], dbv[2], dbv[3]};
       }
     }
   }
@@ -864,7 +875,7 @@ __global__ __launch_bounds__(256) void bwd_dmeta_reduce_kernel(const float* part
 namespace {
 
 struct WsPlan {
-  size_t states, dS, dST, dqa, dka, dva, Dt, dmu, total;
+  size_t states, dS, dST, Dt, dmu, total;
 };
 
 size_t al256(size_t x) { return (x + 255) / 256 * 256; }
@@ -872,15 +883,11 @@ size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 WsPlan plan_ws(int elem, int BH, int L, int D, int n_meta) {
   const size_t nc = (size_t)(L + C - 1) / C;
   const size_t st = al256((size_t)BH * nc * D * D * elem);
-  const size_t fl = al256((size_t)BH * L * D * 4);
   WsPlan p;
   p.states = 0;
   p.dS = p.states + st;
   p.dST = p.dS + st;
-  p.dqa = p.dST + st;
-  p.dka = p.dqa + fl;
-  p.dva = p.dka + fl;
-  p.Dt = p.dva + fl;
+  p.Dt = p.dST + st;
   p.dmu = p.Dt + al256((size_t)BH * L * 4);
   p.total = p.dmu + al256((size_t)BH * nc * n_meta * D * 4);
   return p;
@@ -974,9 +981,6 @@ hipError_t launch_bwd(const BwdArgs& in, int dtype_bf16, int D, hipStream_t st) 
     a.ws_states = base + p.states;
     a.ws_dS = base + p.dS;
     a.ws_dST = base + p.dST;
-    a.ws_dqa = reinterpret_cast<float*>(base + p.dqa);
-    a.ws_dka = reinterpret_cast<float*>(base + p.dka);
-    a.ws_dva = reinterpret_cast<float*>(base + p.dva);
     a.ws_D = reinterpret_cast<float*>(base + p.Dt);
     a.ws_dmu = reinterpret_cast<float*>(base + p.dmu);
   }

@@ -162,6 +162,19 @@ template <> __device__ __forceinline__ void store_pack<float, 16>(float* dst, co
   store_pack<float, 8>(dst + 8, v + 8);
 }
 
+// Load n = 4 consecutive elements of type T as float (one 8/16-byte load).
+template <typename T, int N> __device__ __forceinline__ void load_pack(const T* src, float* v);
+template <> __device__ __forceinline__ void load_pack<bf16, 4>(const bf16* src, float* v) {
+  const bf16x4 p = *reinterpret_cast<const bf16x4*>(src);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = static_cast<float>(p[i]);
+}
+template <> __device__ __forceinline__ void load_pack<float, 4>(const float* src, float* v) {
+  const f32x4 p = *reinterpret_cast<const f32x4*>(src);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = p[i];
+}
+
 // Order LDS traffic of one wavefront: writes before the fence are visible
 // to reads after it from any lane of the same wavefront.
 __device__ __forceinline__ void wave_lds_sync() {

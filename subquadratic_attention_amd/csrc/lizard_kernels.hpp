@@ -57,9 +57,6 @@ struct BwdArgs {
   void* ws_states;       // S_c          [BH, nc, D, D] element type
   void* ws_dS;           // G_{c+1}      [BH, nc, D, D] element type
   void* ws_dST;          // G_{c+1}^T    [BH, nc, D, D] element type
-  float* ws_dqa;         // anchor dq    [BH, L, D]
-  float* ws_dka;         // anchor dk    [BH, L, D]
-  float* ws_dva;         // anchor dv    [BH, L, D]
   float* ws_D;           // D_t          [BH, L]
   float* ws_dmu;         // sink-key partials [BH, nc, n_meta, D]
   int B, BH, H, L, n_meta, window;
