@@ -177,11 +177,13 @@ def bench_decode(sqa, si, reps=3):
 
     run_all()  # warm-up
     ms_b2b = min(run_all() for _ in range(reps))
-    # cache-flushed: 512 MiB written between steps evicts the 256 MB last-level cache;
-    # only the decode kernel is timed (per-step events)
-    scratch = torch.empty(512 << 20, device="cuda", dtype=torch.uint8)
+    # cache-flushed: 512 MiB read between steps evicts the 256 MB last-level cache
+    # (a read, so that no dirty lines of the flush are written back while the
+    # decode kernel runs); only the decode kernel is timed (per-step events)
+    scratch = torch.ones((512 << 20) // 4, device="cuda", dtype=torch.int32)
+    sink = torch.empty((), device="cuda", dtype=torch.int64)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    run_all(per_step_events=ev, flush=lambda: scratch.fill_(1))
+    run_all(per_step_events=ev, flush=lambda: torch.sum(scratch, dim=0, out=sink))
     per = sorted(a.elapsed_time(b) for a, b in ev)
     ms_flushed = sum(per) / steps
     bytes_step = w.B * w.H * decode_bytes_per_bh(w.d, w.window)
@@ -199,7 +201,7 @@ def bench_decode(sqa, si, reps=3):
         "flushed_frac_hbm_peak": round(bytes_step / (ms_flushed * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "traffic": read_traffic("lizard_decode", "decode_b64_bf16"),
     }
-    del dec, ring0, y, state, state0, kr, vr, scratch
+    del dec, ring0, y, state, state0, kr, vr, scratch, sink
     torch.cuda.empty_cache()
     return out
 

@@ -175,6 +175,20 @@ template <> __device__ __forceinline__ void load_pack<float, 4>(const float* src
   for (int i = 0; i < 4; ++i) v[i] = p[i];
 }
 
+// The elements of a raw 16-byte vector of T, as float.
+template <typename T> __device__ __forceinline__ void unpack16(uint4 raw, float* v);
+template <> __device__ __forceinline__ void unpack16<bf16>(uint4 raw, float* v) {
+  const bf16x8 p = __builtin_bit_cast(bf16x8, raw);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = static_cast<float>(p[i]);
+}
+template <> __device__ __forceinline__ void unpack16<float>(uint4 raw, float* v) {
+  v[0] = __builtin_bit_cast(float, raw.x);
+  v[1] = __builtin_bit_cast(float, raw.y);
+  v[2] = __builtin_bit_cast(float, raw.z);
+  v[3] = __builtin_bit_cast(float, raw.w);
+}
+
 // Order LDS traffic of one wavefront: writes before the fence are visible
 // to reads after it from any lane of the same wavefront.
 __device__ __forceinline__ void wave_lds_sync() {

@@ -26,11 +26,16 @@ __global__ __launch_bounds__(256) void lizard_decode_kernel(DecodeArgs a) {
   constexpr int CG = D / 4;            // float4 column groups per row
   constexpr int RG = 256 / CG;         // row groups
   constexpr int RPT = D / RG;          // rows per thread
-  constexpr int CPT = D / 64;          // value columns per thread in the window product
+  constexpr int EPV = 16 / sizeof(T);  // elements per 16-byte vector
+  constexpr int QVD = D / 4 / EPV;     // 16-byte vectors in a quarter row
+  constexpr int NCG = D / EPV;         // window product: column groups of EPV columns
+  constexpr int NSG = 256 / NCG;       // ... and slot groups
+  constexpr int SPG = 64 / NSG;        // slots per slot group
+  static_assert(NCG * NSG == 256 && SPG * NSG == 64, "decode shape");
   __shared__ float sq[D], sk[D], sv[D], sg[D];
   __shared__ float sO[RG][D];
   __shared__ float sZ[80];
-  __shared__ float sYa[4][D];
+  __shared__ float sYa[NSG][D];
   __shared__ float sDen;
 
   const int bh = blockIdx.x;
@@ -47,6 +52,14 @@ __global__ __launch_bounds__(256) void lizard_decode_kernel(DecodeArgs a) {
   T* vr = reinterpret_cast<T*>(a.v_ring) + (size_t)bh * w * D;
   float* S = a.state + (size_t)bh * D * D;
 
+  // the state rows first: they do not depend on the token, and their loads
+  // then overlap the token's loads and the barrier below
+  const int cg = tid % CG;
+  const int rg = tid / CG;
+  float4 s[RPT];
+#pragma unroll
+  for (int ii = 0; ii < RPT; ++ii) s[ii] = *reinterpret_cast<const float4*>(S + (size_t)(ii * RG + rg) * D + 4 * cg);
+
   if (tid < D) {
     sq[tid] = to_f32(qg[tid]);
     sk[tid] = to_f32(kg[tid]);
@@ -56,14 +69,9 @@ __global__ __launch_bounds__(256) void lizard_decode_kernel(DecodeArgs a) {
   __syncthreads();
 
   // ---- state update and readout partials ----
-  const int cg = tid % CG;
-  const int rg = tid / CG;
   {
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
     const float4 vv = make_float4(sv[4 * cg], sv[4 * cg + 1], sv[4 * cg + 2], sv[4 * cg + 3]);
-    float4 s[RPT];
-#pragma unroll
-    for (int ii = 0; ii < RPT; ++ii) s[ii] = *reinterpret_cast<const float4*>(S + (size_t)(ii * RG + rg) * D + 4 * cg);
 #pragma unroll
     for (int ii = 0; ii < RPT; ++ii) {
       const int i = ii * RG + rg;
@@ -100,12 +108,22 @@ __global__ __launch_bounds__(256) void lizard_decode_kernel(DecodeArgs a) {
       }
       if (live) {
         float dot = 0.f;
+        const int i0 = part * (D / 4);
         if (e == cur) {
 #pragma unroll 8
-          for (int i = part * (D / 4); i < (part + 1) * (D / 4); ++i) dot += sq[i] * sk[i];
+          for (int i = i0; i < i0 + D / 4; ++i) dot += sq[i] * sk[i];
         } else {
-#pragma unroll 8
-          for (int i = part * (D / 4); i < (part + 1) * (D / 4); ++i) dot += sq[i] * to_f32(kp[i]);
+          // the key's quarter row as 16-byte loads
+          uint4 raw[QVD];
+#pragma unroll
+          for (int v = 0; v < QVD; ++v) raw[v] = ld16(kp + i0 + v * EPV);
+#pragma unroll
+          for (int v = 0; v < QVD; ++v) {
+            float kv[EPV];
+            unpack16<T>(raw[v], kv);
+#pragma unroll
+            for (int u = 0; u < EPV; ++u) dot += sq[i0 + v * EPV + u] * kv[u];
+          }
         }
         zv = dot;
       }
@@ -135,26 +153,32 @@ __global__ __launch_bounds__(256) void lizard_decode_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  // ---- window values: thread (column set, slot quarter) ----
+  // ---- window values: thread (column group of EPV columns, slot group),
+  // 16-byte loads; partial sums per slot group, reduced below ----
   {
-    const int cs = tid & 63;
-    const int sq4 = tid >> 6;
-    float ya[CPT];
+    const int cgi = tid % NCG;
+    const int sgi = tid / NCG;
+    float ya[EPV];
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) ya[c] = 0.f;
-    for (int slot = sq4 * 16; slot < sq4 * 16 + 16 && slot < w; ++slot) {
-      const float p = sZ[slot];
-      if (p != 0.f) {
+    for (int u = 0; u < EPV; ++u) ya[u] = 0.f;
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-          const int j = cs * CPT + c;
-          const float vj = slot == cur ? sv[j] : to_f32(vr[(size_t)slot * D + j]);
-          ya[c] += p * vj;
+    for (int ss = 0; ss < SPG; ++ss) {
+      const int slot = sgi * SPG + ss;
+      const float p = slot < w ? sZ[slot] : 0.f;
+      if (p != 0.f) {            // dead slots (p = 0) are not read: they may hold anything
+        float vv[EPV];
+        if (slot == cur) {
+#pragma unroll
+          for (int u = 0; u < EPV; ++u) vv[u] = sv[cgi * EPV + u];
+        } else {
+          unpack16<T>(ld16(vr + (size_t)slot * D + cgi * EPV), vv);
         }
+#pragma unroll
+        for (int u = 0; u < EPV; ++u) ya[u] += p * vv[u];
       }
     }
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) sYa[sq4][cs * CPT + c] = ya[c];
+    for (int u = 0; u < EPV; ++u) sYa[sgi][cgi * EPV + u] = ya[u];
   }
   __syncthreads();
 
@@ -162,7 +186,10 @@ __global__ __launch_bounds__(256) void lizard_decode_kernel(DecodeArgs a) {
     float o = 0.f;
 #pragma unroll
     for (int r = 0; r < RG; ++r) o += sO[r][tid];
-    const float ya = (sYa[0][tid] + sYa[1][tid] + sYa[2][tid] + sYa[3][tid]) / sDen;
+    float ya = 0.f;
+#pragma unroll
+    for (int r = 0; r < NSG; ++r) ya += sYa[r][tid];
+    ya /= sDen;
     reinterpret_cast<T*>(a.y)[(size_t)bh * D + tid] = from_f32<T>(o + a.alpha * ya);
   }
 }
