@@ -15,6 +15,7 @@
 //     dk_s   = 2^{-beta_s} * sum_t dA_ts Qe_t + 2^{B-beta_s} * (G_{c+1} v_s)
 //     dv_s   = sum_t A_ts dO_t + G_{c+1}^T Kh_s
 //     dlog_g_t = sum_{u >= t} (q_u * dq_u - k_u * dk_u)      (natural log)
+//              = sum_{u >= t, u in c} (...) + rowsum(S_{c+1} * G_{c+1})
 //   anchor branch (softmax over the window and sinks, P = exp(z - lse)):
 //     dP = alpha dY V^T (window; zero for sinks), D_t = sum P dP,
 //     dZ = P (dP - D_t); dq += scale (dZ K + dZs mu); dk += scale dZ^T Q;
@@ -29,9 +30,9 @@
 //   4. bwd_anchor_k (per chunk of keys, queries of this and the next chunk):
 //      the anchor parts of dk and dv (written into dk, dv);
 //   5. bwd_gate (per chunk): the gated dq, dk, dv, added to the anchor parts
-//      in the outputs; writes q*dq - k*dk into dlog_g;
-//   6. bwd_dlogg_scan: reverse cumulative sum of dlog_g along the sequence;
-//   7. bwd_dmeta_reduce: sums the sink-key partials over batch and chunks in
+//      in the outputs, and dlog_g: the suffix sums of q*dq - k*dk inside the
+//      chunk plus, for everything after it, rowsum(S_{c+1} * G_{c+1});
+//   6. bwd_dmeta_reduce: sums the sink-key partials over batch and chunks in
 //      a fixed order (deterministic, no float atomics).
 // Chunks whose decay span exceeds 2^92 form the gated intra terms pairwise
 // in fp32 (as the forward pass does).
@@ -87,23 +88,36 @@ template <typename T> __device__ __forceinline__ float elem32(uint32_t u, int i)
 // LDS transposed: dst[col * ld + row] (rows outside [0, L) are zero).  Each
 // thread loads 32-bit words (VC columns) of RPT consecutive rows and writes
 // 8-row runs with 16-byte stores.  scale multiplies every value.
-template <typename T, int D, int COLS, int NR>
-__device__ __forceinline__ void stage_T(T* dst, int ld, const T* src, int r0, int c0, int L, float scale) {
-  constexpr int VC = 4 / sizeof(T);
-  constexpr int VRW = COLS / VC;
-  constexpr int RPT = NR * VRW / 256;
+template <typename T, int COLS, int NR>
+struct StageT {
+  static constexpr int VC = 4 / sizeof(T);
+  static constexpr int VRW = COLS / VC;
+  static constexpr int RPT = NR * VRW / 256;   // 32-bit words per thread
   static_assert(RPT % 8 == 0 && RPT * 256 == NR * VRW, "stage_T shape");
+};
+template <typename T, int D, int COLS, int NR>
+__device__ __forceinline__ void stage_T_load(uint32_t* w, const T* src, int r0, int c0,
+                                             int L) {
+  typedef StageT<T, COLS, NR> S;
   const int tid = threadIdx.x;
-  const int vj = tid % VRW;
-  const int vs = tid / VRW;
-  uint32_t w[RPT];
+  const int vj = tid % S::VRW;
+  const int vs = tid / S::VRW;
 #pragma unroll
-  for (int rr = 0; rr < RPT; ++rr) {
-    const int row = r0 + vs * RPT + rr;
+  for (int rr = 0; rr < S::RPT; ++rr) {
+    const int row = r0 + vs * S::RPT + rr;
     const bool ok = row >= 0 && row < L;
-    const uint32_t u = *reinterpret_cast<const uint32_t*>(src + (size_t)(ok ? row : 0) * D + c0 + VC * vj);
+    const uint32_t u = *reinterpret_cast<const uint32_t*>(src + (size_t)(ok ? row : 0) * D + c0 + S::VC * vj);
     w[rr] = ok ? u : 0u;
   }
+}
+template <typename T, int COLS, int NR>
+__device__ __forceinline__ void stage_T_store(T* dst, int ld, const uint32_t* w,
+                                              float scale) {
+  typedef StageT<T, COLS, NR> S;
+  constexpr int VC = S::VC, RPT = S::RPT;
+  const int tid = threadIdx.x;
+  const int vj = tid % S::VRW;
+  const int vs = tid / S::VRW;
 #pragma unroll
   for (int cc = 0; cc < VC; ++cc)
 #pragma unroll
@@ -113,6 +127,12 @@ __device__ __forceinline__ void stage_T(T* dst, int ld, const T* src, int r0, in
       for (int rr = 0; rr < 8; ++rr) v8[rr] = elem32<T>(w[8 * b + rr], cc) * scale;
       store_pack<T, 8>(dst + (VC * vj + cc) * ld + vs * RPT + 8 * b, v8);
     }
+}
+template <typename T, int D, int COLS, int NR>
+__device__ __forceinline__ void stage_T(T* dst, int ld, const T* src, int r0, int c0, int L, float scale) {
+  uint32_t w[StageT<T, COLS, NR>::RPT];
+  stage_T_load<T, D, COLS, NR>(w, src, r0, c0, L);
+  stage_T_store<T, COLS, NR>(dst, ld, w, scale);
 }
 
 // Stage rows [r0, r0 + NR) of a [L, D] tensor into LDS row-major (ld elements per row).
@@ -142,9 +162,26 @@ __device__ __forceinline__ bool chunk_block(int BH, int nc, int& bh, int& c) {
 // Chunk-local log2-gate prefix for 256 threads: thread (w, l) owns rows
 // 16w..16w+15 and dims DPL*l..; returns beta (chunk-inclusive prefix) and B
 // (chunk total) for those; sTot is [4][D] scratch.  Contains one barrier.
+// The log-gates of those rows and dims (zero past L).
 template <int D>
-__device__ __forceinline__ void chunk_prefix(const float* lg, int t0, int L, float* sTot,
-                                             float (&beta)[16][D / 64], float (&Bt)[D / 64]) {
+__device__ __forceinline__ void chunk_gates(const float* lg, int t0, int L, float (&lv)[16][D / 64]) {
+  constexpr int DPL = D / 64;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) {
+    const int t = t0 + 16 * w + rr;
+    const bool ok = t < L;
+#pragma unroll
+    for (int dd = 0; dd < DPL; ++dd) {
+      const float v = lg[(size_t)(ok ? t : 0) * D + DPL * l + dd];
+      lv[rr][dd] = ok ? v : 0.f;
+    }
+  }
+}
+// The prefix from gates loaded by chunk_gates.
+template <int D>
+__device__ __forceinline__ void chunk_prefix_of(const float (&lv)[16][D / 64], float* sTot,
+                                                float (&beta)[16][D / 64], float (&Bt)[D / 64]) {
   constexpr int DPL = D / 64;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   float tot[DPL];
@@ -152,12 +189,9 @@ __device__ __forceinline__ void chunk_prefix(const float* lg, int t0, int L, flo
   for (int dd = 0; dd < DPL; ++dd) tot[dd] = 0.f;
 #pragma unroll
   for (int rr = 0; rr < 16; ++rr) {
-    const int t = t0 + 16 * w + rr;
-    const bool ok = t < L;
 #pragma unroll
     for (int dd = 0; dd < DPL; ++dd) {
-      const float v = ok ? lg[(size_t)(ok ? t : 0) * D + DPL * l + dd] : 0.f;
-      tot[dd] += log2_gate(v);
+      tot[dd] += log2_gate(lv[rr][dd]);
       beta[rr][dd] = tot[dd];
     }
   }
@@ -173,6 +207,14 @@ __device__ __forceinline__ void chunk_prefix(const float* lg, int t0, int L, flo
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) beta[rr][dd] += off;
   }
+}
+
+template <int D>
+__device__ __forceinline__ void chunk_prefix(const float* lg, int t0, int L, float* sTot,
+                                             float (&beta)[16][D / 64], float (&Bt)[D / 64]) {
+  float lv[16][D / 64];
+  chunk_gates<D>(lg, t0, L, lv);
+  chunk_prefix_of<D>(lv, sTot, beta, Bt);
 }
 
 }  // namespace
@@ -213,8 +255,48 @@ __global__ __launch_bounds__(256, 1) void bwd_dstate_kernel(BwdArgs a) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) acc[rt][ct] = zero4();
 
-  for (int c = nc - 1; c >= 0; --c) {
+  // one chunk's inputs, loaded a chunk ahead: log-gates and queries of rows
+  // 16w + rr, dims DPL*l..; dO words for the transposed staging
+  typedef StageT<T, DV, 64> ST;
+  float lv[16][DPL];
+  uint32_t qv[16];
+  uint32_t dyw[ST::RPT];
+  auto load = [&](int c) __attribute__((always_inline)) {
     const int t0 = c * C;
+    chunk_gates<D>(lgg, t0, L, lv);
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int t = t0 + 16 * w + rr;
+      const bool ok = t < L;
+      const T* qp = qg + (size_t)(ok ? t : 0) * D + DPL * l;
+      uint32_t u;
+      if constexpr (DPL * sizeof(T) == 4) u = *reinterpret_cast<const uint32_t*>(qp);
+      else u = *reinterpret_cast<const uint16_t*>(qp);
+      qv[rr] = ok ? u : 0u;
+    }
+    stage_T_load<T, D, DV, 64>(dyw, dyg, t0, j0, L);
+  };
+  if (nc > 0) load(nc - 1);
+
+  for (int c = nc - 1; c >= 0; --c) {
+    // chunk c's operands from the registers: Qe^T and dO^T into LDS
+    float beta[16][DPL], Bt[DPL];
+    chunk_prefix_of<D>(lv, sTot, beta, Bt);
+#pragma unroll
+    for (int dd = 0; dd < DPL; ++dd) {
+      const int i = DPL * l + dd;
+      float qe[16];
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const float qf = elem32<T>(qv[rr], dd);
+        qe[rr] = qf * exp_2(beta[rr][dd]);
+      }
+      store_pack<T, 16>(sQeT + i * LDQ + 16 * w, qe);
+      if (w == 0) sBexp[i] = exp_2(Bt[dd]);
+    }
+    stage_T_store<T, DV, 64>(sdOT, LDQ, dyw, 1.0f);
+    // the next chunk's loads fly while this one is stored and multiplied
+    if (c > 0) load(c - 1);
     // G_{c+1}: rows i, columns j (row-major) and its transpose
     T* G = Gg + (size_t)c * D * D;
     T* GT = GTg + (size_t)c * D * D;
@@ -229,22 +311,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dstate_kernel(BwdArgs a) {
         const float v4[4] = {acc[rt][ct][0], acc[rt][ct][1], acc[rt][ct][2], acc[rt][ct][3]};
         store_pack<T, 4>(GT + (size_t)j * D + i, v4);
       }
-    float beta[16][DPL], Bt[DPL];
-    chunk_prefix<D>(lgg, t0, L, sTot, beta, Bt);
-#pragma unroll
-    for (int dd = 0; dd < DPL; ++dd) {
-      const int i = DPL * l + dd;
-      float qe[16];
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int t = t0 + 16 * w + rr;
-        const float qv = t < L ? to_f32(qg[(size_t)(t < L ? t : 0) * D + i]) : 0.f;
-        qe[rr] = qv * exp_2(beta[rr][dd]);
-      }
-      store_pack<T, 16>(sQeT + i * LDQ + 16 * w, qe);
-      if (w == 0) sBexp[i] = exp_2(Bt[dd]);
-    }
-    stage_T<T, D, DV, 64>(sdOT, LDQ, dyg, t0, j0, L, 1.0f);
     __syncthreads();
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
@@ -725,8 +791,36 @@ __global__ __launch_bounds__(256, 1) void bwd_gate_kernel(BwdArgs a) {
     load_quarter<T, D>(Gr[it], Gg, ib + m, D, g);     // G_{c+1} rows i (k = j)
     load_quarter<T, D>(GTr[it], GTg, ib + m, D, g);   // G_{c+1}^T rows j (k = i)
   }
+  // dlog_g of the chunk's last token gets, from all later tokens, the
+  // boundary term x_i = sum_j S_{c+1}[i][j] G_{c+1}[i][j]: the terms of
+  // q_u.dq_u - k_u.dk_u over u > t (the chunk's end) cancel in pairs except
+  // those of a query after the boundary and a key before it, which sum to
+  // this product (zero after the last chunk).  xin[it][r] holds x of dim
+  // ib + 4g + r.
+  float xin[NIT][4];
 #pragma unroll
-  for (int tt = 0; tt < 4; ++tt) {
+  for (int it = 0; it < NIT; ++it) {
+    const int ib = w * (D / 4) + 16 * it;
+    float x = 0.f;
+    if (c + 1 < nc) {
+      uint4 sn[QV];
+      load_quarter<T, D>(sn, Sg + (size_t)D * D, ib + m, D, g);   // S_{c+1} rows i (k = j)
+#pragma unroll
+      for (int kk = 0; kk < D / 4; ++kk) x += elem_of<T>(sn, kk) * elem_of<T>(Gr[it], kk);
+    }
+    x = xgroup_sum(x);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) xin[it][r] = __shfl(x, 4 * g + r, 64);
+  }
+  // running sums of q.dq - k.dk over the later token tiles of the chunk
+  float carry[NIT][4];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) carry[it][r] = 0.f;
+  // token tiles last to first, so the suffix sums of dlog_g run with them
+#pragma unroll
+  for (int tt = 3; tt >= 0; --tt) {
     const int trow = t0 + 16 * tt + m;        // token of this lane's output column
     uint4 dyr[QV], vr[QV], kr[QV];
     load_quarter<T, D>(dyr, dyg, trow, L, g);
@@ -778,13 +872,14 @@ __global__ __launch_bounds__(256, 1) void bwd_gate_kernel(BwdArgs a) {
         }
       }
       // epilogue for the 4 dims i = ib + 4g + r of token trow
+      const size_t o4 = (size_t)trow * D + ib + 4 * g;
+      float dbv[4] = {0.f, 0.f, 0.f, 0.f};
       if (trow < L) {
         const int tl = 16 * tt + m;
         const float* bt = sBeta + tl * Lay::LDB + ib + 4 * g;
-        float dqv[4], dkv[4], dvv[4], dbv[4];
+        float dqv[4], dkv[4], dvv[4];
         // the anchor parts (written into the outputs by the anchor kernels),
         // and q, k of these 4 dims for dlog_g
-        const size_t o4 = (size_t)trow * D + ib + 4 * g;
         float aq[4], ak[4], av[4], q4[4], k4[4];
         load_pack<T, 4>(dqo + o4, aq);
         load_pack<T, 4>(dko + o4, ak);
@@ -820,53 +915,62 @@ __global__ __launch_bounds__(256, 1) void bwd_gate_kernel(BwdArgs a) {
         store_pack<T, 4>(dqo + o4, dqv);
         store_pack<T, 4>(dko + o4, dkv);
         store_pack<T, 4>(dvo + o4, dvv);
-        *reinterpret_cast<f32x4*>(dbo + o4) = f32x4{dbv[0], dbv[1], dbv[2], dbv[3]};
       }
+      // dlog_g_t = sum over the tile's tokens u >= t (lanes of this lane
+      // group with m' >= m) + the later tiles + the boundary term
+      float dl[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float sfx = dbv[r];
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+          const float y = __shfl_down(sfx, o, 16);
+          sfx += m + o < 16 ? y : 0.f;
+        }
+        const float tile = __shfl(sfx, l & 48, 64);   // m = 0: the whole tile
+        dl[r] = sfx + carry[it][r] + xin[it][r];
+        carry[it][r] += tile;
+      }
+      if (trow < L) *reinterpret_cast<f32x4*>(dbo + o4) = f32x4{dl[0], dl[1], dl[2], dl[3]};
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// 6. dlog_g_t = sum_{u >= t} db_u (per (b, h, dim), in place)
+// 6. dmeta[h][i][d] = sum over batch rows and chunks of the partials (fixed order)
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void bwd_dlogg_scan_kernel(float* dlg, int BH, int L) {
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= BH * D) return;
-  const int bh = idx / D, d = idx % D;
-  float* p = dlg + (size_t)bh * L * D + d;
-  float acc = 0.f;
-  int t = L - 1;
-  for (; t >= 7; t -= 8) {
-    float v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = p[(size_t)(t - u) * D];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      acc += v[u];
-      p[(size_t)(t - u) * D] = acc;
-    }
-  }
-  for (; t >= 0; --t) {
-    acc += p[(size_t)t * D];
-    p[(size_t)t * D] = acc;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// 7. dmeta[h][i][d] = sum over batch rows and chunks of the partials (fixed order)
-// ---------------------------------------------------------------------------
+// Block (x, h) sums outputs o = 64x .. 64x + 63: thread (o, part) adds the
+// terms k = part, part + 4, ... of the B*nc partials (k = b*nc + c) in order,
+// then the 4 part sums are added in order.
 __global__ __launch_bounds__(256) void bwd_dmeta_reduce_kernel(const float* part, float* out, int B, int H, int nc,
                                                                int nmD) {
+  __shared__ float sPart[4][64];
   const int h = blockIdx.y;
-  const int o = blockIdx.x * 256 + threadIdx.x;
-  if (o >= nmD) return;
+  const int ol = threadIdx.x & 63, pi = threadIdx.x >> 6;
+  const int o = blockIdx.x * 64 + ol;
+  const bool live = o < nmD;
+  const int nk = B * nc;
   float s = 0.f;
-  for (int b = 0; b < B; ++b) {
-    const float* p = part + ((size_t)(b * H + h) * nc) * nmD + o;
-    for (int c = 0; c < nc; ++c) s += p[(size_t)c * nmD];
+  if (live) {
+    int k = pi;
+    for (; k + 28 < nk; k += 32) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int kk = k + 4 * u, b = kk / nc, c = kk % nc;
+        v[u] = part[((size_t)(b * H + h) * nc + c) * nmD + o];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; k < nk; k += 4) {
+      const int b = k / nc, c = k % nc;
+      s += part[((size_t)(b * H + h) * nc + c) * nmD + o];
+    }
   }
-  out[(size_t)h * nmD + o] = s;
+  sPart[pi][ol] = s;
+  __syncthreads();
+  if (pi == 0 && live) out[(size_t)h * nmD + o] = ((sPart[0][ol] + sPart[1][ol]) + sPart[2][ol]) + sPart[3][ol];
 }
 
 // ---------------------------------------------------------------------------
@@ -947,18 +1051,15 @@ hipError_t launch_bwd_t(BwdArgs a, hipStream_t st) {
     if ((e = set_lds(&bwd_gate_kernel<T, D>, GL::TOTAL)) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_gate_kernel<T, D>), dim3(8 * groups * nc), dim3(256), GL::TOTAL, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // 6. reverse cumulative sum of the log-gate gradient
-    hipLaunchKernelGGL((bwd_dlogg_scan_kernel<D>), dim3((a.BH * D + 255) / 256), dim3(256), 0, st, a.dlog_g, a.BH, L);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // 7. sink keys (written even when B*L == 0: then zero)
+  // 6. sink keys (written even when B*L == 0: then zero)
   if (a.n_meta > 0 && a.H > 0) {
     const int nmD = a.n_meta * D;
     if (a.BH > 0 && L > 0) {
-      hipLaunchKernelGGL(bwd_dmeta_reduce_kernel, dim3((nmD + 255) / 256, a.H), dim3(256), 0, st, a.ws_dmu, a.dmeta,
+      hipLaunchKernelGGL(bwd_dmeta_reduce_kernel, dim3((nmD + 63) / 64, a.H), dim3(256), 0, st, a.ws_dmu, a.dmeta,
                          a.B, a.H, nc, nmD);
     } else {
-      hipLaunchKernelGGL(bwd_dmeta_reduce_kernel, dim3((nmD + 255) / 256, a.H), dim3(256), 0, st, a.ws_dmu, a.dmeta,
+      hipLaunchKernelGGL(bwd_dmeta_reduce_kernel, dim3((nmD + 63) / 64, a.H), dim3(256), 0, st, a.ws_dmu, a.dmeta,
                          0, a.H, 0, nmD);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
