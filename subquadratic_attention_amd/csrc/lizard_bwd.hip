@@ -66,11 +66,13 @@ template <typename T> __device__ __forceinline__ typename Mfma<T>::frag frag_of(
   }
 }
 // The lane's k-quarter [g*D/4, (g+1)*D/4) of global row `row` (zeros if the
-// row is outside [0, L)).
-template <typename T, int D>
+// row is outside [0, L)).  GUARD = false: the caller guarantees the row is
+// inside (no selects on the loaded data, which the compiler would otherwise
+// place right after the loads and so wait for them early).
+template <typename T, int D, bool GUARD = true>
 __device__ __forceinline__ void load_quarter(uint4* raw, const T* base, int row, int L, int g) {
   constexpr int QV = D / 4 / (16 / sizeof(T));
-  const bool ok = row >= 0 && row < L;
+  const bool ok = !GUARD || (row >= 0 && row < L);
   const T* p = base + (size_t)(ok ? row : 0) * D + g * (D / 4);
 #pragma unroll
   for (int e = 0; e < QV; ++e) {
@@ -88,32 +90,32 @@ template <typename T> __device__ __forceinline__ float elem32(uint32_t u, int i)
 // LDS transposed: dst[col * ld + row] (rows outside [0, L) are zero).  Each
 // thread loads 32-bit words (VC columns) of RPT consecutive rows and writes
 // 8-row runs with 16-byte stores.  scale multiplies every value.
-template <typename T, int COLS, int NR>
+template <typename T, int COLS, int NR, int NTH = 256>
 struct StageT {
   static constexpr int VC = 4 / sizeof(T);
   static constexpr int VRW = COLS / VC;
-  static constexpr int RPT = NR * VRW / 256;   // 32-bit words per thread
-  static_assert(RPT % 8 == 0 && RPT * 256 == NR * VRW, "stage_T shape");
+  static constexpr int RPT = NR * VRW / NTH;   // 32-bit words per thread
+  static_assert(RPT % 8 == 0 && RPT * NTH == NR * VRW, "stage_T shape");
 };
-template <typename T, int D, int COLS, int NR>
+template <typename T, int D, int COLS, int NR, int NTH = 256, bool GUARD = true>
 __device__ __forceinline__ void stage_T_load(uint32_t* w, const T* src, int r0, int c0,
                                              int L) {
-  typedef StageT<T, COLS, NR> S;
+  typedef StageT<T, COLS, NR, NTH> S;
   const int tid = threadIdx.x;
   const int vj = tid % S::VRW;
   const int vs = tid / S::VRW;
 #pragma unroll
   for (int rr = 0; rr < S::RPT; ++rr) {
     const int row = r0 + vs * S::RPT + rr;
-    const bool ok = row >= 0 && row < L;
+    const bool ok = !GUARD || (row >= 0 && row < L);
     const uint32_t u = *reinterpret_cast<const uint32_t*>(src + (size_t)(ok ? row : 0) * D + c0 + S::VC * vj);
     w[rr] = ok ? u : 0u;
   }
 }
-template <typename T, int COLS, int NR>
+template <typename T, int COLS, int NR, int NTH = 256>
 __device__ __forceinline__ void stage_T_store(T* dst, int ld, const uint32_t* w,
                                               float scale) {
-  typedef StageT<T, COLS, NR> S;
+  typedef StageT<T, COLS, NR, NTH> S;
   constexpr int VC = S::VC, RPT = S::RPT;
   const int tid = threadIdx.x;
   const int vj = tid % S::VRW;
@@ -128,11 +130,11 @@ __device__ __forceinline__ void stage_T_store(T* dst, int ld, const uint32_t* w,
       store_pack<T, 8>(dst + (VC * vj + cc) * ld + vs * RPT + 8 * b, v8);
     }
 }
-template <typename T, int D, int COLS, int NR>
+template <typename T, int D, int COLS, int NR, int NTH = 256>
 __device__ __forceinline__ void stage_T(T* dst, int ld, const T* src, int r0, int c0, int L, float scale) {
-  uint32_t w[StageT<T, COLS, NR>::RPT];
-  stage_T_load<T, D, COLS, NR>(w, src, r0, c0, L);
-  stage_T_store<T, COLS, NR>(dst, ld, w, scale);
+  uint32_t w[StageT<T, COLS, NR, NTH>::RPT];
+  stage_T_load<T, D, COLS, NR, NTH>(w, src, r0, c0, L);
+  stage_T_store<T, COLS, NR, NTH>(dst, ld, w, scale);
 }
 
 // Stage rows [r0, r0 + NR) of a [L, D] tensor into LDS row-major (ld elements per row).
@@ -615,6 +617,7 @@ __global__ __launch_bounds__(256, 1) void bwd_anchor_k_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 struct GateLayout {
+  static constexpr int NW = D / 16;        // wavefronts: one 16-dim tile each in the output phase
   static constexpr int PAD = 16 / sizeof(T);
   static constexpr int LDT = 64 + PAD;     // [D][LDT] transposed tiles; [64][LDT] staged scores
   static constexpr int LDB = D + 4;        // sBeta [64][LDB] fp32
@@ -627,20 +630,31 @@ struct GateLayout {
   static constexpr int OFF_DAT = OFF_DA + a16(64 * LDT * (int)sizeof(T));
   static constexpr int OFF_AT = OFF_DAT + a16(64 * LDT * (int)sizeof(T));
   static constexpr int OFF_TOT = OFF_AT + a16(64 * LDT * (int)sizeof(T));
-  static constexpr int OFF_BX = OFF_TOT + a16(4 * D * 4);
+  static constexpr int OFF_BX = OFF_TOT + a16(NW * D * 4);
   static constexpr int TOTAL = OFF_BX + a16(D * 4);
 };
 
-template <typename T, int D>
-__global__ __launch_bounds__(256, 1) void bwd_gate_kernel(BwdArgs a) {
+// One workgroup of D/16 wavefronts per (b*h, chunk).  Phase A: log-gate
+// prefix and the chunk's operands in LDS; phase B: the intra-chunk score
+// tiles dA, dA^T, A^T; phase C: wavefront w owns dims / value columns
+// [16w, 16w + 16) of every token and writes dq, dk, dv, dlog_g.  The global
+// loads of each phase are issued before the barrier that precedes it.  The
+// grid covers chunks cb .. cb + ncl - 1; RAGGED: they may end past L (only
+// the last chunk of a sequence does), so token rows are range-checked.
+template <typename T, int D, bool RAGGED>
+__global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int cb, int ncl) {
   typedef GateLayout<T, D> Lay;
   typedef Mfma<T> M;
   typedef typename M::frag frag;
+  constexpr int NW = Lay::NW;
+  constexpr int NT = 64 * NW;
+  constexpr int RPW = 64 / NW;            // prefix rows per wavefront
+  constexpr int JPW = 16 / NW;            // phase B: blocks J per wavefront
   constexpr int EPV = 16 / sizeof(T);
   constexpr int QV = D / 4 / EPV;
   constexpr int NF = D / 4 / M::KPL;
   constexpr int DPL = D / 64;
-  constexpr int NIT = D / 64;             // 16-row dim tiles per wavefront (D/4 dims each)
+  static_assert(NW == 4 || NW == 8, "gate kernel shape");
   extern __shared__ __align__(16) unsigned char smem[];
   float* sBeta = reinterpret_cast<float*>(smem + Lay::OFF_B);
   T* sQT = reinterpret_cast<T*>(smem + Lay::OFF_QT);    // Qe^T (or q^T on the pairwise path)
@@ -654,21 +668,104 @@ __global__ __launch_bounds__(256, 1) void bwd_gate_kernel(BwdArgs a) {
 
   const int L = a.L, nc = (L + C - 1) / C;
   int bh, c;
-  if (!chunk_block(a.BH, nc, bh, c)) return;
+  if (!chunk_block(a.BH, ncl, bh, c)) return;
+  c += cb;
   const int t0 = c * C;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
-  const T* qg = reinterpret_cast<const T*>(a.q) + (size_t)bh * L * D;
-  const T* kg = reinterpret_cast<const T*>(a.k) + (size_t)bh * L * D;
-  const T* vg = reinterpret_cast<const T*>(a.v) + (size_t)bh * L * D;
-  const T* dyg = reinterpret_cast<const T*>(a.dy) + (size_t)bh * L * D;
-  const float* lgg = a.log_g + (size_t)bh * L * D;
-  const T* Sg = reinterpret_cast<const T*>(a.ws_states) + ((size_t)bh * nc + c) * D * D;
-  const T* Gg = reinterpret_cast<const T*>(a.ws_dS) + ((size_t)bh * nc + c) * D * D;
-  const T* GTg = reinterpret_cast<const T*>(a.ws_dST) + ((size_t)bh * nc + c) * D * D;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, m = l & 15, g = l >> 4;
+  constexpr bool RG = RAGGED;
+  const T* __restrict__ qg = reinterpret_cast<const T*>(a.q) + (size_t)bh * L * D;
+  const T* __restrict__ kg = reinterpret_cast<const T*>(a.k) + (size_t)bh * L * D;
+  const T* __restrict__ vg = reinterpret_cast<const T*>(a.v) + (size_t)bh * L * D;
+  const T* __restrict__ dyg = reinterpret_cast<const T*>(a.dy) + (size_t)bh * L * D;
+  const float* __restrict__ lgg = a.log_g + (size_t)bh * L * D;
+  const T* __restrict__ Sg = reinterpret_cast<const T*>(a.ws_states) + ((size_t)bh * nc + c) * D * D;
+  const T* __restrict__ Gg = reinterpret_cast<const T*>(a.ws_dS) + ((size_t)bh * nc + c) * D * D;
+  const T* __restrict__ GTg = reinterpret_cast<const T*>(a.ws_dST) + ((size_t)bh * nc + c) * D * D;
+  T* __restrict__ dqo = reinterpret_cast<T*>(a.dq) + (size_t)bh * L * D;
+  T* __restrict__ dko = reinterpret_cast<T*>(a.dk) + (size_t)bh * L * D;
+  T* __restrict__ dvo = reinterpret_cast<T*>(a.dv) + (size_t)bh * L * D;
+  float* __restrict__ dbo = a.dlog_g + (size_t)bh * L * D;
+  const int ib = 16 * w;                  // phase C: first dim of this wavefront's tile
 
-  // ---- prefix, operands: Qe^T, Kp^T (or raw q^T, k^T), dO^T, beta ----
-  float beta[16][DPL], Bt[DPL];
-  chunk_prefix<D>(lgg, t0, L, sTot, beta, Bt);
+
+  // ---- phase A: log-gates, q and k of rows RPW*w + rr, dims DPL*l + dd ----
+  float lv[RPW][DPL];
+  uint32_t qw[RPW], kw[RPW];
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr) {
+    const int t = t0 + RPW * w + rr;
+    const bool ok = !RG || t < L;
+    const size_t ro = (size_t)(ok ? t : 0) * D + DPL * l;
+    if constexpr (DPL == 2) {
+      const float2 f = *reinterpret_cast<const float2*>(lgg + ro);
+      lv[rr][0] = ok ? f.x : 0.f;
+      lv[rr][1] = ok ? f.y : 0.f;
+    } else {
+      const float f = lgg[ro];
+      lv[rr][0] = ok ? f : 0.f;
+    }
+    uint32_t qu, ku;
+    if constexpr (DPL * sizeof(T) == 4) {
+      qu = *reinterpret_cast<const uint32_t*>(qg + ro);
+      ku = *reinterpret_cast<const uint32_t*>(kg + ro);
+    } else {
+      qu = *reinterpret_cast<const uint16_t*>(qg + ro);
+      ku = *reinterpret_cast<const uint16_t*>(kg + ro);
+    }
+    qw[rr] = ok ? qu : 0u;
+    kw[rr] = ok ? ku : 0u;
+  }
+  uint32_t dyw[StageT<T, D, 64, NT>::RPT];
+  stage_T_load<T, D, D, 64, NT, RG>(dyw, dyg, t0, 0, L);
+  // phase B's rows: block I of this wavefront (see phase B)
+  int I;
+  if constexpr (NW == 8) {
+    // (I, J) tiles cost about 1 (J < I), 2.5 (J > I) or 3.5 (J = I) units;
+    // wavefronts w and w + 4 share a SIMD, so each SIMD gets two blocks I of
+    // complementary cost: SIMD loads 8, 9.5, 9, 8.5 units
+    I = w < 4 ? w >> 1 : (w < 6 ? 3 : 2);
+  } else {
+    I = w;
+  }
+  uint4 dyI[QV], vI[QV], kI[QV];
+  load_quarter<T, D, RG>(dyI, dyg, t0 + 16 * I + m, L, g);
+  load_quarter<T, D, RG>(vI, vg, t0 + 16 * I + m, L, g);
+  load_quarter<T, D, RG>(kI, kg, t0 + 16 * I + m, L, g);
+  // phase C's state rows (issued after the earlier phases' loads: the load
+  // counter is waited on in issue order)
+  uint4 Sr[QV], Gr[QV], GTr[QV], Sn[QV];
+  load_quarter<T, D, false>(Sr, Sg, ib + m, D, g);      // S_c rows i (k = j)
+  load_quarter<T, D, false>(Gr, Gg, ib + m, D, g);      // G_{c+1} rows i (k = j)
+  load_quarter<T, D, false>(GTr, GTg, ib + m, D, g);    // G_{c+1}^T rows j (k = i)
+  // S_{c+1} rows i (zero after the last chunk)
+  load_quarter<T, D, false>(Sn, c + 1 < nc ? Sg + (size_t)D * D : Sg, ib + m, D, g);
+  const bool has_next = c + 1 < nc;
+
+  // prefix: inside the wavefront's rows, then across wavefronts
+  float beta[RPW][DPL], off[DPL], Bt[DPL];
+#pragma unroll
+  for (int dd = 0; dd < DPL; ++dd) {
+    float run = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) {
+      run += log2_gate(lv[rr][dd]);
+      beta[rr][dd] = run;
+    }
+    sTot[w * D + DPL * l + dd] = run;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int dd = 0; dd < DPL; ++dd) {
+    const int i = DPL * l + dd;
+    off[dd] = 0.f;
+    Bt[dd] = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) {
+      const float v = sTot[w2 * D + i];
+      off[dd] += w2 < w ? v : 0.f;
+      Bt[dd] += v;
+    }
+  }
   bool wide = false;
 #pragma unroll
   for (int dd = 0; dd < DPL; ++dd) wide |= -Bt[dd] > kMaxSpan;
@@ -676,35 +773,63 @@ __global__ __launch_bounds__(256, 1) void bwd_gate_kernel(BwdArgs a) {
 #pragma unroll
   for (int dd = 0; dd < DPL; ++dd) {
     const int i = DPL * l + dd;
-    float qe[16], kp[16];
+    float qe[RPW], kp[RPW];
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int t = t0 + 16 * w + rr;
-      const bool ok = t < L;
-      const float qv = ok ? to_f32(qg[(size_t)(ok ? t : 0) * D + i]) : 0.f;
-      const float kv = ok ? to_f32(kg[(size_t)(ok ? t : 0) * D + i]) : 0.f;
-      qe[rr] = pairwise ? qv : qv * exp_2(beta[rr][dd]);
-      kp[rr] = pairwise ? kv : kv * exp_2(-beta[rr][dd]);
-      sBeta[(16 * w + rr) * Lay::LDB + i] = beta[rr][dd];
+    for (int rr = 0; rr < RPW; ++rr) {
+      const float b = beta[rr][dd] + off[dd];
+      const float qv = elem32<T>(qw[rr], dd), kv = elem32<T>(kw[rr], dd);
+      qe[rr] = pairwise ? qv : qv * exp_2(b);
+      kp[rr] = pairwise ? kv : kv * exp_2(-b);
+      sBeta[(RPW * w + rr) * Lay::LDB + i] = b;
     }
-    store_pack<T, 16>(sQT + i * Lay::LDT + 16 * w, qe);
-    store_pack<T, 16>(sKT + i * Lay::LDT + 16 * w, kp);
+    store_pack<T, RPW>(sQT + i * Lay::LDT + RPW * w, qe);
+    store_pack<T, RPW>(sKT + i * Lay::LDT + RPW * w, kp);
     if (w == 0) sBx[i] = Bt[dd];
   }
-  stage_T<T, D, D, 64>(sOT, Lay::LDT, dyg, t0, 0, L, 1.0f);
+  stage_T_store<T, D, 64, NT>(sOT, Lay::LDT, dyw, 1.0f);
   __syncthreads();
 
-  // ---- phase B: wavefront I stages the score tiles of token block I ----
+  // phase C's first token tile (the last one: the dlog_g suffix sums run
+  // backwards): its rows and, for the epilogue, the anchor parts already in
+  // dq, dk, dv and q, k of the lane's 4 dims; issued during phase B
+  uint4 rows[2][3][QV];   // [buffer][dO, v, k][k-quarter]
+  float ep[2][5][4];      // [buffer][dq, dk, dv, q, k][dim]
+  auto load_ep = [&](int tt, float (&dst)[5][4]) __attribute__((always_inline)) {
+    const int trow = t0 + 16 * tt + m;
+    const size_t o4 = (size_t)(!RG || trow < L ? trow : 0) * D + ib + 4 * g;
+    load_pack<T, 4>(dqo + o4, dst[0]);
+    load_pack<T, 4>(dko + o4, dst[1]);
+    load_pack<T, 4>(dvo + o4, dst[2]);
+    load_pack<T, 4>(qg + o4, dst[3]);
+    load_pack<T, 4>(kg + o4, dst[4]);
+  };
+
+  // ---- phase B: wavefront w stages the score tiles of token block I
+  // against JPW blocks J ----
   {
-    const int I = w;
-    const int tme = t0 + 16 * I + m;
-    uint4 dyr[QV], vr[QV], kr[QV];
-    load_quarter<T, D>(dyr, dyg, tme, L, g);
-    load_quarter<T, D>(vr, vg, tme, L, g);
-    load_quarter<T, D>(kr, kg, tme, L, g);
-    // Kp of this lane's key row as fragments
+    // rows of the blocks J (two at a time)
+    uint4 rowsJ[2][3][QV];
+    auto load_J = [&](int J, uint4 (&dst)[3][QV]) __attribute__((always_inline)) {
+      const int rJ = t0 + 16 * J + m;
+      load_quarter<T, D, RG>(dst[0], vg, rJ, L, g);
+      load_quarter<T, D, RG>(dst[1], dyg, rJ, L, g);
+      load_quarter<T, D, RG>(dst[2], qg, rJ, L, g);
+    };
+    // the blocks J of this wavefront: all four (four wavefronts), or two
+    auto J_of = [&](int jj) __attribute__((always_inline)) -> int {
+      if constexpr (NW == 8) {
+        const int ja[8] = {0, 2, 0, 2, 1, 0, 1, 0};
+        const int jb[8] = {1, 3, 1, 3, 2, 3, 2, 3};
+        return jj == 0 ? ja[w] : jb[w];
+      } else {
+        return jj;
+      }
+    };
+    load_J(J_of(0), rowsJ[0]);
+    load_J(J_of(1), rowsJ[1]);
+    // Kp of this lane's key row as fragments (unused on the pairwise path)
     frag kpf[NF];
-    {
+    if (!pairwise) {
       const float* bp = sBeta + (16 * I + m) * Lay::LDB + g * (D / 4);
 #pragma unroll
       for (int e = 0; e < NF; ++e) {
@@ -712,30 +837,32 @@ __global__ __launch_bounds__(256, 1) void bwd_gate_kernel(BwdArgs a) {
 #pragma unroll
         for (int u = 0; u < M::KPL; ++u) {
           const int kk = e * M::KPL + u;
-          tk[u] = pairwise ? 0.f : elem_of<T>(kr, kk) * exp_2(-bp[kk]);
+          tk[u] = elem_of<T>(kI, kk) * exp_2(-bp[kk]);
         }
         kpf[e] = M::pack(tk);
       }
+    } else {
+#pragma unroll
+      for (int e = 0; e < NF; ++e) kpf[e] = M::zero();
     }
 #pragma unroll
-    for (int J = 0; J < 4; ++J) {
+    for (int jj = 0; jj < JPW; ++jj) {
+      const int J = J_of(jj);
       // (a) dA^T tile: keys s in block J (rows), queries t in block I (cols) -> sDA[t][s]
       // (b) dA tile: queries t in block J (rows), keys s in block I (cols) -> sDAT[s][t]
       // (c) A tile: queries t in block J (rows), keys s in block I (cols) -> sAT[s][t]
-      uint4 vJ[QV], dyJ[QV], qJ[QV];
-      const int rJ = t0 + 16 * J + m;
-      load_quarter<T, D>(vJ, vg, rJ, L, g);
-      load_quarter<T, D>(dyJ, dyg, rJ, L, g);
+      const uint4* vJ = rowsJ[jj & 1][0];
+      const uint4* dyJ = rowsJ[jj & 1][1];
+      const uint4* qJ = rowsJ[jj & 1][2];
       f32x4 ta = zero4(), tb = zero4(), tc = zero4();
       if (J <= I) {
 #pragma unroll
-        for (int e = 0; e < NF; ++e) ta = M::mma(frag_of<T>(vJ, e), frag_of<T>(dyr, e), ta);
+        for (int e = 0; e < NF; ++e) ta = M::mma(frag_of<T>(vJ, e), frag_of<T>(dyI, e), ta);
       }
       if (J >= I) {
 #pragma unroll
-        for (int e = 0; e < NF; ++e) tb = M::mma(frag_of<T>(dyJ, e), frag_of<T>(vr, e), tb);
+        for (int e = 0; e < NF; ++e) tb = M::mma(frag_of<T>(dyJ, e), frag_of<T>(vI, e), tb);
         if (!pairwise) {
-          load_quarter<T, D>(qJ, qg, rJ, L, g);
           const float* bp = sBeta + (16 * J + m) * Lay::LDB + g * (D / 4);
 #pragma unroll
           for (int e = 0; e < NF; ++e) {
@@ -773,59 +900,55 @@ __global__ __launch_bounds__(256, 1) void bwd_gate_kernel(BwdArgs a) {
       store_pack<T, 4>(sDA + (16 * I + m) * Lay::LDT + 16 * J + 4 * g, va);
       store_pack<T, 4>(sDAT + (16 * I + m) * Lay::LDT + 16 * J + 4 * g, vb);
       store_pack<T, 4>(sAT + (16 * I + m) * Lay::LDT + 16 * J + 4 * g, vc);
+      if (jj + 2 < JPW) load_J(J_of(jj + 2), rowsJ[jj & 1]);
+      if (jj == JPW - 2) {
+        // rowsJ[jj & 1] is free from here on
+        load_quarter<T, D, RG>(rows[1][0], dyg, t0 + 48 + m, L, g);
+        load_quarter<T, D, RG>(rows[1][1], vg, t0 + 48 + m, L, g);
+        load_quarter<T, D, RG>(rows[1][2], kg, t0 + 48 + m, L, g);
+        load_ep(3, ep[1]);
+      }
     }
   }
   __syncthreads();
 
-  // ---- phase C: wavefront w owns dims / value columns [w*D/4, (w+1)*D/4) ----
-  T* dqo = reinterpret_cast<T*>(a.dq) + (size_t)bh * L * D;
-  T* dko = reinterpret_cast<T*>(a.dk) + (size_t)bh * L * D;
-  T* dvo = reinterpret_cast<T*>(a.dv) + (size_t)bh * L * D;
-  float* dbo = a.dlog_g + (size_t)bh * L * D;
-  // state rows of this wavefront's dim tiles, loaded once for the 4 token blocks
-  uint4 Sr[NIT][QV], Gr[NIT][QV], GTr[NIT][QV];
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int ib = w * (D / 4) + 16 * it;     // first dim of this 16-row tile
-    load_quarter<T, D>(Sr[it], Sg, ib + m, D, g);     // S_c rows i (k = j)
-    load_quarter<T, D>(Gr[it], Gg, ib + m, D, g);     // G_{c+1} rows i (k = j)
-    load_quarter<T, D>(GTr[it], GTg, ib + m, D, g);   // G_{c+1}^T rows j (k = i)
-  }
+  // ---- phase C: dims / value columns [ib, ib + 16) of every token ----
   // dlog_g of the chunk's last token gets, from all later tokens, the
   // boundary term x_i = sum_j S_{c+1}[i][j] G_{c+1}[i][j]: the terms of
-  // q_u.dq_u - k_u.dk_u over u > t (the chunk's end) cancel in pairs except
-  // those of a query after the boundary and a key before it, which sum to
-  // this product (zero after the last chunk).  xin[it][r] holds x of dim
-  // ib + 4g + r.
-  float xin[NIT][4];
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int ib = w * (D / 4) + 16 * it;
+  // q_u.dq_u - k_u.dk_u over u past the chunk cancel in pairs except those
+  // of a query after the boundary and a key before it, which sum to this
+  // product (zero after the last chunk).  xin[r] is x of dim ib + 4g + r.
+  float xin[4];
+  {
     float x = 0.f;
-    if (c + 1 < nc) {
-      uint4 sn[QV];
-      load_quarter<T, D>(sn, Sg + (size_t)D * D, ib + m, D, g);   // S_{c+1} rows i (k = j)
 #pragma unroll
-      for (int kk = 0; kk < D / 4; ++kk) x += elem_of<T>(sn, kk) * elem_of<T>(Gr[it], kk);
-    }
-    x = xgroup_sum(x);
+    for (int kk = 0; kk < D / 4; ++kk) x += elem_of<T>(Sn, kk) * elem_of<T>(Gr, kk);
+    x = has_next ? xgroup_sum(x) : 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) xin[it][r] = __shfl(x, 4 * g + r, 64);
+    for (int r = 0; r < 4; ++r) xin[r] = __shfl(x, 4 * g + r, 64);
   }
-  // running sums of q.dq - k.dk over the later token tiles of the chunk
-  float carry[NIT][4];
-#pragma unroll
-  for (int it = 0; it < NIT; ++it)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) carry[it][r] = 0.f;
-  // token tiles last to first, so the suffix sums of dlog_g run with them
+  float carry[4] = {0.f, 0.f, 0.f, 0.f};   // sums of q.dq - k.dk over the later tiles
 #pragma unroll
   for (int tt = 3; tt >= 0; --tt) {
+    const int cur = tt & 1;
     const int trow = t0 + 16 * tt + m;        // token of this lane's output column
-    uint4 dyr[QV], vr[QV], kr[QV];
-    load_quarter<T, D>(dyr, dyg, trow, L, g);
-    load_quarter<T, D>(vr, vg, trow, L, g);
-    load_quarter<T, D>(kr, kg, trow, L, g);
+    const bool live = !RG || trow < L;
+    const size_t o4 = (size_t)(live ? trow : 0) * D + ib + 4 * g;
+    const float* aq = ep[cur][0];
+    const float* ak = ep[cur][1];
+    const float* av = ep[cur][2];
+    const float* q4 = ep[cur][3];
+    const float* k4 = ep[cur][4];
+    // the next tile's rows and epilogue inputs
+    if (tt > 0) {
+      load_quarter<T, D, RG>(rows[cur ^ 1][0], dyg, trow - 16, L, g);
+      load_quarter<T, D, RG>(rows[cur ^ 1][1], vg, trow - 16, L, g);
+      load_quarter<T, D, RG>(rows[cur ^ 1][2], kg, trow - 16, L, g);
+      load_ep(tt - 1, ep[cur ^ 1]);
+    }
+    const uint4* dyr = rows[cur][0];
+    const uint4* vr = rows[cur][1];
+    const uint4* kr = rows[cur][2];
     // Kh_s = k_s * 2^{B - beta_s} as fragments (rows s, k = i)
     frag khf[NF];
     {
@@ -841,98 +964,82 @@ __global__ __launch_bounds__(256, 1) void bwd_gate_kernel(BwdArgs a) {
         khf[e] = M::pack(tk);
       }
     }
+    // inter-chunk parts
+    f32x4 qi = zero4(), ki = zero4(), vi = zero4();
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const int ib = w * (D / 4) + 16 * it;   // first dim of this 16-row tile
-      // inter-chunk parts
-      f32x4 qi = zero4(), ki = zero4(), vi = zero4();
-#pragma unroll
-      for (int e = 0; e < NF; ++e) {
-        qi = M::mma(frag_of<T>(Sr[it], e), frag_of<T>(dyr, e), qi);     // (S dO_t)_i
-        ki = M::mma(frag_of<T>(Gr[it], e), frag_of<T>(vr, e), ki);      // (G v_s)_i
-        vi = M::mma(frag_of<T>(GTr[it], e), khf[e], vi);                // (G^T Kh_s)_j
-      }
-      // intra-chunk parts
-      f32x4 qa = zero4(), ka = zero4(), va = zero4();
-      {
-        const T* bO = sOT + (ib + m) * Lay::LDT + g * 16;            // dO^T rows j (k = t)
-        const T* bAT = sAT + (16 * tt + m) * Lay::LDT + g * 16;      // A^T rows s (k = t)
-#pragma unroll
-        for (int e = 0; e < 16 / M::KPL; ++e) va = M::mma(M::load(bO + e * M::KPL), M::load(bAT + e * M::KPL), va);
-      }
-      if (!pairwise) {
-        const T* aK = sKT + (ib + m) * Lay::LDT + g * 16;            // Kp^T rows i (k = s)
-        const T* bDA = sDA + (16 * tt + m) * Lay::LDT + g * 16;      // dA rows t (k = s)
-        const T* aQ = sQT + (ib + m) * Lay::LDT + g * 16;            // Qe^T rows i (k = t)
-        const T* bDAT = sDAT + (16 * tt + m) * Lay::LDT + g * 16;    // dA^T rows s (k = t)
-#pragma unroll
-        for (int e = 0; e < 16 / M::KPL; ++e) {
-          qa = M::mma(M::load(aK + e * M::KPL), M::load(bDA + e * M::KPL), qa);
-          ka = M::mma(M::load(aQ + e * M::KPL), M::load(bDAT + e * M::KPL), ka);
-        }
-      }
-      // epilogue for the 4 dims i = ib + 4g + r of token trow
-      const size_t o4 = (size_t)trow * D + ib + 4 * g;
-      float dbv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (trow < L) {
-        const int tl = 16 * tt + m;
-        const float* bt = sBeta + tl * Lay::LDB + ib + 4 * g;
-        float dqv[4], dkv[4], dvv[4];
-        // the anchor parts (written into the outputs by the anchor kernels),
-        // and q, k of these 4 dims for dlog_g
-        float aq[4], ak[4], av[4], q4[4], k4[4];
-        load_pack<T, 4>(dqo + o4, aq);
-        load_pack<T, 4>(dko + o4, ak);
-        load_pack<T, 4>(dvo + o4, av);
-        load_pack<T, 4>(qg + o4, q4);
-        load_pack<T, 4>(kg + o4, k4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = ib + 4 * g + r;
-          const float b = bt[r];
-          float qin = qa[r], kin = ka[r];
-          if (pairwise) {
-            // dq_ti += sum_s dA_ts k_si 2^{b_ti - b_si};  dk_ti += sum_u dA_ut q_ui 2^{b_ui - b_ti}
-            qin = 0.f;
-            kin = 0.f;
-            for (int s = 0; s <= tl; ++s)
-              qin += to_f32(sDA[tl * Lay::LDT + s]) * to_f32(sKT[i * Lay::LDT + s]) *
-                     exp_2(b - sBeta[s * Lay::LDB + i]);
-            for (int u = tl; u < 64; ++u)
-              kin += to_f32(sDAT[tl * Lay::LDT + u]) * to_f32(sQT[i * Lay::LDT + u]) *
-                     exp_2(sBeta[u * Lay::LDB + i] - b);
-          } else {
-            qin *= exp_2(b);
-            kin *= exp_2(-b);
-          }
-          const float dqg = exp_2(b) * qi[r] + qin;
-          const float dkg = exp_2(sBx[i] - b) * ki[r] + kin;
-          dbv[r] = q4[r] * dqg - k4[r] * dkg;
-          dqv[r] = dqg + aq[r];
-          dkv[r] = dkg + ak[r];
-          dvv[r] = vi[r] + va[r] + av[r];
-        }
-        store_pack<T, 4>(dqo + o4, dqv);
-        store_pack<T, 4>(dko + o4, dkv);
-        store_pack<T, 4>(dvo + o4, dvv);
-      }
-      // dlog_g_t = sum over the tile's tokens u >= t (lanes of this lane
-      // group with m' >= m) + the later tiles + the boundary term
-      float dl[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float sfx = dbv[r];
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-          const float y = __shfl_down(sfx, o, 16);
-          sfx += m + o < 16 ? y : 0.f;
-        }
-        const float tile = __shfl(sfx, l & 48, 64);   // m = 0: the whole tile
-        dl[r] = sfx + carry[it][r] + xin[it][r];
-        carry[it][r] += tile;
-      }
-      if (trow < L) *reinterpret_cast<f32x4*>(dbo + o4) = f32x4{dl[0], dl[1], dl[2], dl[3]};
+    for (int e = 0; e < NF; ++e) {
+      qi = M::mma(frag_of<T>(Sr, e), frag_of<T>(dyr, e), qi);     // (S dO_t)_i
+      ki = M::mma(frag_of<T>(Gr, e), frag_of<T>(vr, e), ki);      // (G v_s)_i
+      vi = M::mma(frag_of<T>(GTr, e), khf[e], vi);                // (G^T Kh_s)_j
     }
+    // intra-chunk parts
+    f32x4 qa = zero4(), ka = zero4(), va = zero4();
+    {
+      const T* bO = sOT + (ib + m) * Lay::LDT + g * 16;            // dO^T rows j (k = t)
+      const T* bAT = sAT + (16 * tt + m) * Lay::LDT + g * 16;      // A^T rows s (k = t)
+#pragma unroll
+      for (int e = 0; e < 16 / M::KPL; ++e) va = M::mma(M::load(bO + e * M::KPL), M::load(bAT + e * M::KPL), va);
+    }
+    if (!pairwise) {
+      const T* aK = sKT + (ib + m) * Lay::LDT + g * 16;            // Kp^T rows i (k = s)
+      const T* bDA = sDA + (16 * tt + m) * Lay::LDT + g * 16;      // dA rows t (k = s)
+      const T* aQ = sQT + (ib + m) * Lay::LDT + g * 16;            // Qe^T rows i (k = t)
+      const T* bDAT = sDAT + (16 * tt + m) * Lay::LDT + g * 16;    // dA^T rows s (k = t)
+#pragma unroll
+      for (int e = 0; e < 16 / M::KPL; ++e) {
+        qa = M::mma(M::load(aK + e * M::KPL), M::load(bDA + e * M::KPL), qa);
+        ka = M::mma(M::load(aQ + e * M::KPL), M::load(bDAT + e * M::KPL), ka);
+      }
+    }
+    // epilogue for the 4 dims i = ib + 4g + r of token trow
+    const int tl = 16 * tt + m;
+    const float* bt = sBeta + tl * Lay::LDB + ib + 4 * g;
+    float dqv[4], dkv[4], dvv[4], dbv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = ib + 4 * g + r;
+      const float b = bt[r];
+      float qin = qa[r], kin = ka[r];
+      if (pairwise) {
+        // dq_ti += sum_s dA_ts k_si 2^{b_ti - b_si};  dk_ti += sum_u dA_ut q_ui 2^{b_ui - b_ti}
+        qin = 0.f;
+        kin = 0.f;
+        for (int s = 0; s <= tl; ++s)
+          qin += to_f32(sDA[tl * Lay::LDT + s]) * to_f32(sKT[i * Lay::LDT + s]) * exp_2(b - sBeta[s * Lay::LDB + i]);
+        for (int u = tl; u < 64; ++u)
+          kin += to_f32(sDAT[tl * Lay::LDT + u]) * to_f32(sQT[i * Lay::LDT + u]) * exp_2(sBeta[u * Lay::LDB + i] - b);
+      } else {
+        qin *= exp_2(b);
+        kin *= exp_2(-b);
+      }
+      const float dqg = exp_2(b) * qi[r] + qin;
+      const float dkg = exp_2(sBx[i] - b) * ki[r] + kin;
+      dbv[r] = live ? q4[r] * dqg - k4[r] * dkg : 0.f;
+      dqv[r] = dqg + aq[r];
+      dkv[r] = dkg + ak[r];
+      dvv[r] = vi[r] + va[r] + av[r];
+    }
+    if (live) {
+      store_pack<T, 4>(dqo + o4, dqv);
+      store_pack<T, 4>(dko + o4, dkv);
+      store_pack<T, 4>(dvo + o4, dvv);
+    }
+    // dlog_g_t = sum over the tile's tokens u >= t (lanes of this lane
+    // group with m' >= m) + the later tiles + the boundary term
+    float dl[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float sfx = dbv[r];
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const float y = __shfl_down(sfx, o, 16);
+        sfx += m + o < 16 ? y : 0.f;
+      }
+      const float tile = __shfl(sfx, l & 48, 64);   // m = 0: the whole tile
+      dl[r] = sfx + carry[r] + xin[r];
+      carry[r] += tile;
+    }
+    if (live) *reinterpret_cast<f32x4*>(dbo + o4) = f32x4{dl[0], dl[1], dl[2], dl[3]};
   }
 }
 
@@ -1046,11 +1153,22 @@ hipError_t launch_bwd_t(BwdArgs a, hipStream_t st) {
     hipLaunchKernelGGL((bwd_anchor_k_kernel<T, D>), dim3(8 * groups * nc), dim3(256), AK::TOTAL, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // 5. gated branch and outputs
+    // (full chunks, then the last chunk if it ends past L)
     typedef GateLayout<T, D> GL;
     static_assert(GL::TOTAL <= 160 * 1024, "LDS");
-    if ((e = set_lds(&bwd_gate_kernel<T, D>, GL::TOTAL)) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_gate_kernel<T, D>), dim3(8 * groups * nc), dim3(256), GL::TOTAL, st, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int nfull = L / C;
+    if (nfull > 0) {
+      if ((e = set_lds(&bwd_gate_kernel<T, D, false>, GL::TOTAL)) != hipSuccess) return e;
+      hipLaunchKernelGGL((bwd_gate_kernel<T, D, false>), dim3(8 * groups * nfull), dim3(GL::NW * 64), GL::TOTAL, st,
+                         a, 0, nfull);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (nfull < nc) {
+      if ((e = set_lds(&bwd_gate_kernel<T, D, true>, GL::TOTAL)) != hipSuccess) return e;
+      hipLaunchKernelGGL((bwd_gate_kernel<T, D, true>), dim3(8 * groups), dim3(GL::NW * 64), GL::TOTAL, st, a, nfull,
+                         1);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
   // 6. sink keys (written even when B*L == 0: then zero)
   if (a.n_meta > 0 && a.H > 0) {
