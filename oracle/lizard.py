@@ -298,3 +298,39 @@ def lizard_bwd(q, k, v, log_g, meta_k, w: int, alpha: float, dy, scale: Optional
     aq, ak, av, amu = anchor_bwd(q, k, v, meta_k, w, alpha * dy, scale)
     return {"dq": gq + aq, "dk": gk + ak, "dv": gv + av, "dlog_g": glg, "dmeta": amu,
             "dq_gate": gq, "dk_gate": gk}
+
+
+# ---------------------------------------------------------------------------
+# Gate from its logits
+# ---------------------------------------------------------------------------
+
+
+def log_sigmoid(x):
+    """log Gamma for the gate Gamma = sigmoid(x), x = W_gamma x_i the gate
+    projection's output (de §2 "Kernkomponenten" item 1; it §2 "Architettura
+    Ibrida").  Written as min(x, 0) - log(1 + e^{-|x|}): no overflow for
+    either sign, and the small tail -e^{-x} for large x is kept by log1p."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.minimum(x, 0.0) - np.log1p(np.exp(-np.abs(x)))
+
+
+def lizard_fwd_logit(q, k, v, gate_logit, meta_k, w: int, alpha: float, scale: Optional[float] = None):
+    """The layer fed with gate logits: log_g = log_sigmoid(gate_logit)."""
+    return lizard_fwd(q, k, v, log_sigmoid(gate_logit), meta_k, w, alpha, scale)
+
+
+def lizard_bwd_logit(q, k, v, gate_logit, meta_k, w: int, alpha: float, dy, scale: Optional[float] = None):
+    """Gradients of sum(dy * Y) with the gate given by its logits.  Chain
+    rule through the log-sigmoid: d/dx log sigmoid(x) = 1 - sigmoid(x) =
+    sigmoid(-x) = exp(log_sigmoid(-x)).  Adds "dgate_logit" to lizard_bwd's
+    dict."""
+    r = lizard_bwd(q, k, v, log_sigmoid(gate_logit), meta_k, w, alpha, dy, scale)
+    r["dgate_logit"] = r["dlog_g"] * np.exp(log_sigmoid(-np.asarray(gate_logit, dtype=np.float64)))
+    return r
+
+
+def lizard_decode_step_logit(state, k_ring, v_ring, pos: int, q_t, k_t, v_t, gate_logit_t, meta_k, w: int,
+                             alpha: float, scale: Optional[float] = None):
+    """lizard_decode_step with the token's gate given by its logits."""
+    return lizard_decode_step(state, k_ring, v_ring, pos, q_t, k_t, v_t, log_sigmoid(gate_logit_t), meta_k, w, alpha,
+                              scale)

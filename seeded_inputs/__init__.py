@@ -16,7 +16,9 @@ Large Language Models", gist.science, section 4 "Ergebnisse"):
 * gate logits ~ N(mu_g, sd_g) per token per key dim, and the log-gate handed
   to the layer is log(sigmoid(logit)), computed in float64 and rounded once
   to float32 (the gate is a sigmoid of a learned projection; same page,
-  section 2, "Kernkomponenten", item 1)
+  section 2, "Kernkomponenten", item 1).  The entry points that take the
+  logits themselves get the same draws rounded to the storage dtype
+  ("gate_logit").
 * meta-memory sink keys ~ N(0, 1) / 8, one set per head
 * upstream gradient dY ~ N(0, 1)
 
@@ -114,8 +116,9 @@ def _log_sigmoid(x: np.ndarray) -> np.ndarray:
 def slice_inputs(w: Workload, b: int, h: int, L: Optional[int] = None, with_dy: bool = False) -> Dict[str, np.ndarray]:
     """Float64 values (already rounded to storage precision) of one (b, h) slice.
 
-    Returns q, k, v [L, d], log_g [L, d] (float32 values), and dy [L, d]
-    if requested.  ``L`` defaults to the workload's length (for decode
+    Returns q, k, v [L, d], log_g [L, d] (float32 values), gate_logit
+    [L, d] (the same draws in the storage dtype), and dy [L, d] if
+    requested.  ``L`` defaults to the workload's length (for decode
     workloads: prefill length + steps).
     """
     if L is None:
@@ -126,6 +129,7 @@ def slice_inputs(w: Workload, b: int, h: int, L: Optional[int] = None, with_dy: 
         out[name] = round_to(_rng(w.cfg_id, tid, b, h).standard_normal((L, d)) * w.qkv_sd, w.dtype)
     logits = _rng(w.cfg_id, T_GATE, b, h).normal(w.gate_mu, w.gate_sd, size=(L, d))
     out["log_g"] = _log_sigmoid(logits).astype(np.float32).astype(np.float64)
+    out["gate_logit"] = round_to(logits, w.dtype)
     if with_dy:
         out["dy"] = round_to(_rng(w.cfg_id, T_DY, b, h).standard_normal((L, d)), w.dtype)
     return out
@@ -142,7 +146,7 @@ def full_inputs(w: Workload, L: Optional[int] = None, with_dy: bool = False,
     if L is None:
         L = w.L + w.steps
     Hs = list(range(w.H)) if heads is None else list(heads)
-    names = ["q", "k", "v", "log_g"] + (["dy"] if with_dy else [])
+    names = ["q", "k", "v", "log_g", "gate_logit"] + (["dy"] if with_dy else [])
     arrs = {n: np.empty((w.B, len(Hs), L, w.d), dtype=np.float64) for n in names}
     for b in range(w.B):
         for j, h in enumerate(Hs):
@@ -167,19 +171,21 @@ def custom_inputs(seed: int, B: int, H: int, L: int, d: int, n_meta: int, dtype:
                   gate_mu: float = 3.0, gate_sd: float = 1.0, hard_reset_frac: float = 0.0,
                   with_dy: bool = False) -> Dict[str, np.ndarray]:
     """Inputs for parity variants outside the fixed workloads (sharp logits,
-    slow or hard-reset gates, ragged lengths).  Hard resets set log_g = -1000
-    on a random fraction of tokens (all key dims of that token)."""
+    slow or hard-reset gates, ragged lengths).  Hard resets set the gate
+    logit, and so log_g, to -1000 on a random fraction of tokens (all key
+    dims of that token)."""
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(ROOT_SEED, spawn_key=(1000 + seed,))))
     out = {
         "q": round_to(rng.standard_normal((B, H, L, d)) * qk_sd, dtype),
         "k": round_to(rng.standard_normal((B, H, L, d)) * qk_sd, dtype),
         "v": round_to(rng.standard_normal((B, H, L, d)) * v_sd, dtype),
     }
-    lg = _log_sigmoid(rng.normal(gate_mu, gate_sd, size=(B, H, L, d)))
+    logits = rng.normal(gate_mu, gate_sd, size=(B, H, L, d))
     if hard_reset_frac > 0:
         hit = rng.random((B, H, L)) < hard_reset_frac
-        lg[hit] = -1000.0
-    out["log_g"] = lg.astype(np.float32).astype(np.float64)
+        logits[hit] = -1000.0   # log sigmoid(-1000) = -1000 to double precision
+    out["log_g"] = _log_sigmoid(logits).astype(np.float32).astype(np.float64)
+    out["gate_logit"] = round_to(logits, dtype)
     out["meta_k"] = round_to(rng.standard_normal((H, n_meta, d)) * meta_sd, dtype)
     if with_dy:
         out["dy"] = round_to(rng.standard_normal((B, H, L, d)), dtype)
@@ -198,7 +204,7 @@ def _storage_row(args):
 
 
 def storage_inputs(w: Workload, L: Optional[int] = None, with_dy: bool = False,
-                   workers: Optional[int] = None) -> Dict[str, np.ndarray]:
+                   workers: Optional[int] = None, with_logit: bool = False) -> Dict[str, np.ndarray]:
     """Whole [B, H, L, d] inputs in storage form (uint16 bfloat16 bits or
     float32; log_g always float32), identical to the slices that
     ``slice_inputs`` returns, generated in parallel over batch rows."""
@@ -208,7 +214,7 @@ def storage_inputs(w: Workload, L: Optional[int] = None, with_dy: bool = False,
 
     if L is None:
         L = w.L + w.steps
-    names = ["q", "k", "v", "log_g"] + (["dy"] if with_dy else [])
+    names = ["q", "k", "v", "log_g"] + (["dy"] if with_dy else []) + (["gate_logit"] if with_logit else [])
     sdt = np.uint16 if w.dtype == "bf16" else np.float32
     out = {n: np.empty((w.B, w.H, L, w.d), dtype=np.float32 if n == "log_g" else sdt) for n in names}
     if workers is None:

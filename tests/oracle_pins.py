@@ -348,6 +348,62 @@ def p20_sdpa_gradients(O):
     return max(_rel(dq, ts[0].grad.numpy()), _rel(dk, ts[1].grad.numpy()), _rel(dv, ts[2].grad.numpy()))
 
 
+
+# --- gate given by its logits -------------------------------------------------
+
+def p21_log_sigmoid(O):
+    """log sigmoid against torch's float64 logsigmoid (a different
+    implementation) over [-60, 60], the closed form log sigmoid(0) = -log 2,
+    and the identity log sigmoid(x) - log sigmoid(-x) = x."""
+    import torch
+
+    x = np.concatenate([np.linspace(-60.0, 60.0, 4801), [0.0, 1e-12, -1e-12, 35.0, -35.0]])
+    ref = torch.nn.functional.logsigmoid(torch.from_numpy(x)).numpy()
+    got = O.log_sigmoid(x)
+    err_lib = float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), 1e-300)))
+    err_zero = abs(float(O.log_sigmoid(np.array(0.0))) + math.log(2.0))
+    err_sym = float(np.abs(O.log_sigmoid(x) - O.log_sigmoid(-x) - x).max() / 60.0)
+    return max(err_lib, err_zero, err_sym)
+
+
+def p22_logit_gradients(O):
+    """The layer fed with gate logits against torch autograd through
+    torch's logsigmoid (forward output and every gradient, the logits'
+    included)."""
+    import torch
+
+    q, k, v, _, mu = _rand(22, N=2, L=17, d=5, m=2)
+    x = np.random.default_rng(220).normal(1.5, 2.0, size=q.shape)
+    w, alpha = 5, 0.5
+    dy = np.random.default_rng(221).standard_normal(v.shape)
+    g = O.lizard_bwd_logit(q, k, v, x, mu, w, alpha, dy)
+    fwd = O.lizard_fwd_logit(q, k, v, x, mu, w, alpha)["y"]
+    ts = [torch.tensor(a, requires_grad=True) for a in (q, k, v, x, mu)]
+    y = _torch_layer(ts[0], ts[1], ts[2], torch.nn.functional.logsigmoid(ts[3]), ts[4], w, alpha)
+    y.backward(torch.from_numpy(dy))
+    errs = [_rel(fwd, y.detach().numpy())]
+    for t_, key in zip(ts, ("dq", "dk", "dv", "dgate_logit", "dmeta")):
+        errs.append(_rel(g[key], t_.grad.numpy()))
+    return max(errs)
+
+
+def p23_logit_decode_continues_prefill(O):
+    """Decoding token L-1 after a logit-fed prefill of L-1 tokens gives the
+    logit-fed prefill's output at L-1 (and its final state)."""
+    q, k, v, _, mu = _rand(23, N=2, L=21, d=6, m=2)
+    x = np.random.default_rng(230).normal(2.0, 1.5, size=q.shape)
+    w, alpha, L = 6, 0.5, q.shape[1]
+    full = O.lizard_fwd_logit(q, k, v, x, mu, w, alpha)
+    pre = O.lizard_fwd_logit(q[:, :L - 1], k[:, :L - 1], v[:, :L - 1], x[:, :L - 1], mu, w, alpha)
+    kr = np.zeros((q.shape[0], w, q.shape[2]))
+    vr = np.zeros_like(kr)
+    for p in range(max(0, L - 1 - w), L - 1):
+        kr[:, p % w] = k[:, p]
+        vr[:, p % w] = v[:, p]
+    y, S, _, _ = O.lizard_decode_step_logit(pre["state"], kr, vr, L - 1, q[:, L - 1], k[:, L - 1], v[:, L - 1],
+                                            x[:, L - 1], mu, w, alpha)
+    return max(_rel(y, full["y"][:, L - 1]), _rel(S, full["state"]))
+
 ALL_PINS = {
     "P1": p1_recurrent_equals_quadratic,
     "P2": p2_unit_gate_is_causal_linear_attention,
@@ -369,6 +425,9 @@ ALL_PINS = {
     "P18": p18_torch_autograd,
     "P19": p19_log_gate_gradient_identity,
     "P20": p20_sdpa_gradients,
+    "P21": p21_log_sigmoid,
+    "P22": p22_logit_gradients,
+    "P23": p23_logit_decode_continues_prefill,
 }
 
 # finite differences carry O(h^2) truncation and O(eps/h) rounding error

@@ -51,6 +51,12 @@ MUTATIONS = [
     ("ring slot", "kr[:, pos % w] = k_t", "kr[:, (pos + 1) % w] = k_t"),
     ("key gradient misses the decay adjoint", "dS = g[:, t, :, None] * dS", "dS = dS"),
     ("sink gradient sign", "dZs = -Ps * D", "dZs = Ps * D"),
+    ("logit gradient factor sigmoid(x)", "np.exp(log_sigmoid(-np.asarray(gate_logit, dtype=np.float64)))",
+     "np.exp(log_sigmoid(np.asarray(gate_logit, dtype=np.float64)))"),
+    ("log-sigmoid tail sign", "np.minimum(x, 0.0) - np.log1p(np.exp(-np.abs(x)))",
+     "np.minimum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))"),
+    ("decode logits not through the log-sigmoid", "log_sigmoid(gate_logit_t), meta_k, w, alpha,",
+     "gate_logit_t, meta_k, w, alpha,"),
 ]
 
 
