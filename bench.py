@@ -47,6 +47,11 @@ def fwd_bytes_per_head_token(d: int, elem: int = 2) -> int:
     return 3 * elem * d + 4 * d + elem * d
 
 
+def fwd_logit_bytes_per_head_token(d: int, elem: int = 2) -> int:
+    # q, k, v, the gate logits and y, all in the element type
+    return 5 * elem * d
+
+
 def fwd_flops_per_head_token(d: int, C: int = 64, w: int = 64, m: int = 4) -> int:
     # readout + carry 4 d^2, intra causal pairs (C+1)(dk+dv), window+sink logits 2(w+m)d, window values 2wd
     return 4 * d * d + (C + 1) * 2 * d + 2 * (w + m) * d + 2 * w * d
@@ -98,11 +103,11 @@ def time_region(fn, steps: int, warmup: int):
     return start.elapsed_time(stop) / steps  # ms
 
 
-def bench_fwd(sqa, si, steps, warmup):
+def bench_fwd(sqa, si, steps, warmup, logit=False):
     import torch
 
     w = si.WORKLOADS["llama3_8b_prefill_bf16"]
-    st = si.storage_inputs(w)
+    st = si.storage_inputs(w, with_logit=logit)
     x = {}
     for k, v in st.items():
         import numpy as np
@@ -113,16 +118,30 @@ def bench_fwd(sqa, si, steps, warmup):
     out = {"y": torch.empty_like(x["q"])}
 
     def step():
-        sqa.lizard_attn_fwd(x["q"], x["k"], x["v"], x["log_g"], x["meta_k"], window=w.window, alpha=w.alpha,
-                            out=out)
+        if logit:
+            sqa.lizard_attn_fwd_logit(x["q"], x["k"], x["v"], x["gate_logit"], x["meta_k"], window=w.window,
+                                      alpha=w.alpha, out=out)
+        else:
+            sqa.lizard_attn_fwd(x["q"], x["k"], x["v"], x["log_g"], x["meta_k"], window=w.window, alpha=w.alpha,
+                                out=out)
 
     ms = time_region(step, steps, warmup)
     head_tokens = w.B * w.H * w.L
-    alg_bytes = head_tokens * fwd_bytes_per_head_token(w.d)
+    alg_bytes = head_tokens * (fwd_logit_bytes_per_head_token(w.d) if logit else fwd_bytes_per_head_token(w.d))
     alg_flops = head_tokens * fwd_flops_per_head_token(w.d, w.chunk, w.window, w.n_meta)
     del x, out
     torch.cuda.empty_cache()
     return w, ms, alg_bytes, alg_flops
+
+
+def bench_fwd_logit(sqa, si, steps, warmup):
+    """The same prefill with the gates fed as bf16 logits (log-sigmoid in the
+    kernel's prologue): 1,280 instead of 1,536 algorithmic bytes per head-token."""
+    w, ms, alg_bytes, _ = bench_fwd(sqa, si, steps, warmup, logit=True)
+    gbs = alg_bytes / (ms * 1e-3) / 1e9
+    return {"workload": "llama3_8b_prefill_bf16, gate logits in bf16", "ms": round(ms, 5),
+            "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1), "alg_bytes": alg_bytes, "gbps": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def bench_decode(sqa, si, reps=3):
@@ -206,33 +225,42 @@ def bench_decode(sqa, si, reps=3):
     return out
 
 
-def bench_bwd(sqa, si, steps=10, warmup=3):
+def bench_bwd(sqa, si, steps=10, warmup=3, logit=False):
     import numpy as np
     import torch
 
     w = si.WORKLOADS["train_bwd_bf16"]
-    st = si.storage_inputs(w, with_dy=True)
+    st = si.storage_inputs(w, with_dy=True, with_logit=logit)
     x = {k: (torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).cuda() if v.dtype == np.uint16 else
              torch.from_numpy(v).cuda()) for k, v in st.items()}
     del st
-    fw = sqa.lizard_attn_fwd(x["q"], x["k"], x["v"], x["log_g"], x["meta_k"], window=w.window, alpha=w.alpha,
-                             need_lse=True)
+    if logit:
+        fw = sqa.lizard_attn_fwd_logit(x["q"], x["k"], x["v"], x["gate_logit"], x["meta_k"], window=w.window,
+                                       alpha=w.alpha, need_lse=True)
+    else:
+        fw = sqa.lizard_attn_fwd(x["q"], x["k"], x["v"], x["log_g"], x["meta_k"], window=w.window, alpha=w.alpha,
+                                 need_lse=True)
     ws = torch.empty(max(16, sqa.lizard_attn_bwd_workspace_size(w.B, w.H, w.L, w.d, window=w.window,
                                                                  n_meta=w.n_meta, dtype=sqa.LIZARD_BF16)),
                      device="cuda", dtype=torch.uint8)
     out = {}
 
     def step():
-        sqa.lizard_attn_bwd(x["q"], x["k"], x["v"], x["log_g"], x["meta_k"], fw["lse"], x["dy"], window=w.window,
-                            alpha=w.alpha, workspace=ws, out=out)
+        if logit:
+            sqa.lizard_attn_bwd_logit(x["q"], x["k"], x["v"], x["gate_logit"], x["meta_k"], fw["lse"], x["dy"],
+                                      window=w.window, alpha=w.alpha, workspace=ws, out=out)
+        else:
+            sqa.lizard_attn_bwd(x["q"], x["k"], x["v"], x["log_g"], x["meta_k"], fw["lse"], x["dy"],
+                                window=w.window, alpha=w.alpha, workspace=ws, out=out)
 
     step()
     ms = time_region(step, steps, warmup)
     head_tokens = w.B * w.H * w.L
-    alg_bytes = head_tokens * bwd_bytes_per_head_token(w.d)
+    # with logits: the gate in and its gradient out in bf16 instead of float32
+    alg_bytes = head_tokens * (bwd_bytes_per_head_token(w.d) - (4 * w.d if logit else 0))
     alg_flops = head_tokens * bwd_flops_per_head_token(w.d, w.chunk, w.window, w.n_meta)
     res = {
-        "workload": "train_bwd_bf16", "B": w.B, "H": w.H, "L": w.L, "d": w.d,
+        "workload": "train_bwd_bf16" + (", gate logits in bf16" if logit else ""), "B": w.B, "H": w.H, "L": w.L, "d": w.d,
         "ms": round(ms, 4), "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1),
         "alg_bytes": alg_bytes, "gbps": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
         "frac_hbm_peak": round(alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -283,7 +311,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "decode", "bwd"], default=None,
+    ap.add_argument("--no-logit", action="store_true")
+    ap.add_argument("--only", choices=["fwd", "decode", "bwd", "fwd_logit", "bwd_logit"], default=None,
                     help="run one leg only (for profiler runs); prints that leg's record")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -318,6 +347,12 @@ def main():
     if args.only == "bwd":
         print(json.dumps(bench_bwd(sqa, si, args.steps, args.warmup)), flush=True)
         return
+    if args.only == "fwd_logit":
+        print(json.dumps(bench_fwd_logit(sqa, si, args.steps, args.warmup)), flush=True)
+        return
+    if args.only == "bwd_logit":
+        print(json.dumps(bench_bwd(sqa, si, args.steps, args.warmup, logit=True)), flush=True)
+        return
 
     w, ms, alg_bytes, alg_flops = bench_fwd(sqa, si, args.steps, args.warmup)
     print(f"# fwd done: {ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
@@ -351,12 +386,17 @@ def main():
     if args.only == "fwd":
         print(json.dumps(rec), flush=True)
         return
+    if not args.no_logit:
+        rec["fwd_logit"] = bench_fwd_logit(sqa, si, args.steps, args.warmup)
+        print("# fwd_logit done", file=sys.stderr, flush=True)
     if not args.no_decode:
         rec["decode"] = bench_decode(sqa, si)
         print("# decode done", file=sys.stderr, flush=True)
     if not args.no_bwd:
         try:
             rec["bwd"] = bench_bwd(sqa, si)
+            if not args.no_logit:
+                rec["bwd_logit"] = bench_bwd(sqa, si, logit=True)
         except sqa.LizardError as e:
             rec["bwd"] = {"error": str(e)}
         print("# bwd done", file=sys.stderr, flush=True)

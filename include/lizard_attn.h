@@ -155,10 +155,43 @@ lizard_status_t lizard_decode_step(const lizard_params_t* p, int64_t pos,
                                    float* state, void* k_ring, void* v_ring,
                                    void* y_t, void* stream);
 
+/* ---- The same three calls with the gate given by its logits ------------
+ *
+ * The gate is a sigmoid of a learned projection of the token, Gamma =
+ * sigmoid(W_gamma x) (de section 2 "Kernkomponenten" item 1; it section 2
+ * "Architettura Ibrida").  These entry points take that projection's output
+ * x directly and compute log_g = log(sigmoid(x)) inside the kernels (and,
+ * in the backward pass, the gradient w.r.t. x = dlog_g * sigmoid(-x)), so
+ * the float32 log-gate never makes a round trip through memory.
+ *   gate_logit    [B, H, L, dk] dtype (decode: [B, H, dk]); any finite value
+ *   dgate_logit   [B, H, L, dk] dtype, out
+ * Every other argument, the workspace size and the error behaviour are those
+ * of the log-gate calls above; the results equal theirs for log_g =
+ * log(sigmoid(gate_logit)) evaluated in float32. */
+lizard_status_t lizard_attn_fwd_logit(const lizard_params_t* p,
+                                      const void* q, const void* k, const void* v,
+                                      const void* gate_logit, const void* meta_k,
+                                      void* y, float* lse, void* y_anchor, float* state_out,
+                                      void* stream);
+
+lizard_status_t lizard_attn_bwd_logit(const lizard_params_t* p,
+                                      const void* q, const void* k, const void* v,
+                                      const void* gate_logit, const void* meta_k,
+                                      const float* lse, const void* dy,
+                                      void* dq, void* dk, void* dv, void* dgate_logit, float* dmeta_k,
+                                      void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
+lizard_status_t lizard_decode_step_logit(const lizard_params_t* p, int64_t pos,
+                                         const void* q_t, const void* k_t, const void* v_t,
+                                         const void* gate_logit_t, const void* meta_k,
+                                         float* state, void* k_ring, void* v_ring,
+                                         void* y_t, void* stream);
+
 /* Static description of a status code. */
 const char* lizard_status_string(lizard_status_t s);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2 (version 1 had no *_logit entry points). */
 int lizard_abi_version(void);
 
 #ifdef __cplusplus

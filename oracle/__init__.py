@@ -26,4 +26,8 @@ from .lizard import (  # noqa: F401
     lizard_bwd,
     gla_bwd_recurrent,
     anchor_bwd,
+    log_sigmoid,
+    lizard_fwd_logit,
+    lizard_bwd_logit,
+    lizard_decode_step_logit,
 )

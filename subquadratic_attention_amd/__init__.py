@@ -61,6 +61,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lizard_attn_bwd.restype = ctypes.c_int
     lib.lizard_decode_step.argtypes = [P, ctypes.c_int64] + [_vp] * 10
     lib.lizard_decode_step.restype = ctypes.c_int
+    lib.lizard_attn_fwd_logit.argtypes = [P] + [_vp] * 10
+    lib.lizard_attn_fwd_logit.restype = ctypes.c_int
+    lib.lizard_attn_bwd_logit.argtypes = [P] + [_vp] * 13 + [ctypes.c_size_t, _vp]
+    lib.lizard_attn_bwd_logit.restype = ctypes.c_int
+    lib.lizard_decode_step_logit.argtypes = [P, ctypes.c_int64] + [_vp] * 10
+    lib.lizard_decode_step_logit.restype = ctypes.c_int
     lib.lizard_status_string.argtypes = [ctypes.c_int]
     lib.lizard_status_string.restype = ctypes.c_char_p
     lib.lizard_abi_version.argtypes = []
@@ -117,6 +123,20 @@ def lizard_attn_fwd(q, k, v, log_g, meta_k, *, window: int, alpha: float, softma
     """Forward pass.  q, k, v: [B, H, L, d]; log_g: [B, H, L, d] float32;
     meta_k: [H, m, d].  Returns {"y", and optionally "lse", "y_anchor",
     "state"}; pass ``out`` (same keys) to reuse preallocated outputs."""
+    return _fwd("lizard_attn_fwd", q, k, v, log_g, meta_k, window, alpha, softmax_scale, chunk, need_lse,
+                need_y_anchor, need_state, out)
+
+
+def lizard_attn_fwd_logit(q, k, v, gate_logit, meta_k, *, window: int, alpha: float, softmax_scale: float = 0.0,
+                          chunk: int = 64, need_lse: bool = False, need_y_anchor: bool = False,
+                          need_state: bool = False, out: Optional[Dict] = None) -> Dict:
+    """Forward pass with the gates given by their logits: gate_logit
+    [B, H, L, d] in q's dtype (log_g = log sigmoid(gate_logit) in-kernel)."""
+    return _fwd("lizard_attn_fwd_logit", q, k, v, gate_logit, meta_k, window, alpha, softmax_scale, chunk, need_lse,
+                need_y_anchor, need_state, out)
+
+
+def _fwd(fn, q, k, v, gate, meta_k, window, alpha, softmax_scale, chunk, need_lse, need_y_anchor, need_state, out):
     torch = _torch()
     lib = load_library()
     B, H, L, d = q.shape
@@ -133,10 +153,10 @@ def lizard_attn_fwd(q, k, v, log_g, meta_k, *, window: int, alpha: float, softma
         o["y_anchor"] = torch.empty_like(q)
     if need_state and "state" not in o:
         o["state"] = torch.empty((B, H, d, d), device=q.device, dtype=torch.float32)
-    st = lib.lizard_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(meta_k),
-                             _ptr(o["y"]), _ptr(o.get("lse")), _ptr(o.get("y_anchor")), _ptr(o.get("state")),
-                             _stream(q.device))
-    _check("lizard_attn_fwd", st)
+    st = getattr(lib, fn)(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(meta_k),
+                          _ptr(o["y"]), _ptr(o.get("lse")), _ptr(o.get("y_anchor")), _ptr(o.get("state")),
+                          _stream(q.device))
+    _check(fn, st)
     return o
 
 
@@ -150,6 +170,19 @@ def lizard_attn_bwd(q, k, v, log_g, meta_k, lse, dy, *, window: int, alpha: floa
                     chunk: int = 64, workspace=None, out: Optional[Dict] = None) -> Dict:
     """Backward pass of sum(dy * Y).  Returns {"dq", "dk", "dv", "dlog_g",
     "dmeta"} (dmeta summed over the batch)."""
+    return _bwd("lizard_attn_bwd", "dlog_g", q, k, v, log_g, meta_k, lse, dy, window, alpha, softmax_scale, chunk,
+                workspace, out)
+
+
+def lizard_attn_bwd_logit(q, k, v, gate_logit, meta_k, lse, dy, *, window: int, alpha: float,
+                          softmax_scale: float = 0.0, chunk: int = 64, workspace=None, out: Optional[Dict] = None) -> Dict:
+    """Backward pass with the gates given by their logits.  Returns {"dq",
+    "dk", "dv", "dgate_logit" (q's dtype), "dmeta"}."""
+    return _bwd("lizard_attn_bwd_logit", "dgate_logit", q, k, v, gate_logit, meta_k, lse, dy, window, alpha,
+                softmax_scale, chunk, workspace, out)
+
+
+def _bwd(fn, gkey, q, k, v, gate, meta_k, lse, dy, window, alpha, softmax_scale, chunk, workspace, out):
     torch = _torch()
     lib = load_library()
     B, H, L, d = q.shape
@@ -164,14 +197,14 @@ def lizard_attn_bwd(q, k, v, log_g, meta_k, lse, dy, *, window: int, alpha: floa
     for key, like in (("dq", q), ("dk", k), ("dv", v)):
         if key not in o:
             o[key] = torch.empty_like(like)
-    if "dlog_g" not in o:
-        o["dlog_g"] = torch.empty_like(log_g)
+    if gkey not in o:
+        o[gkey] = torch.empty_like(gate)
     if "dmeta" not in o:
         o["dmeta"] = torch.empty((H, m, d), device=q.device, dtype=torch.float32) if m > 0 else None
-    st = lib.lizard_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(meta_k), _ptr(lse),
-                             _ptr(dy), _ptr(o["dq"]), _ptr(o["dk"]), _ptr(o["dv"]), _ptr(o["dlog_g"]),
-                             _ptr(o["dmeta"]), _ptr(workspace), workspace.numel(), _stream(q.device))
-    _check("lizard_attn_bwd", st)
+    st = getattr(lib, fn)(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(meta_k), _ptr(lse),
+                          _ptr(dy), _ptr(o["dq"]), _ptr(o["dk"]), _ptr(o["dv"]), _ptr(o[gkey]),
+                          _ptr(o["dmeta"]), _ptr(workspace), workspace.numel(), _stream(q.device))
+    _check(fn, st)
     return o
 
 
@@ -180,6 +213,19 @@ def lizard_decode_step(pos: int, q_t, k_t, v_t, log_g_t, meta_k, state, k_ring, 
     """One decode step at absolute position ``pos`` (same for every row).
     q_t, k_t, v_t: [B, H, d]; log_g_t: [B, H, d] float32; state:
     [B, H, d, d] float32 (in-out); rings: [B, H, w, d] (in-out).  Returns y_t."""
+    return _decode("lizard_decode_step", pos, q_t, k_t, v_t, log_g_t, meta_k, state, k_ring, v_ring, alpha,
+                   softmax_scale, y_t)
+
+
+def lizard_decode_step_logit(pos: int, q_t, k_t, v_t, gate_logit_t, meta_k, state, k_ring, v_ring, *,
+                             alpha: float, softmax_scale: float = 0.0, y_t=None):
+    """lizard_decode_step with the token's gates given by their logits
+    (gate_logit_t: [B, H, d] in q's dtype)."""
+    return _decode("lizard_decode_step_logit", pos, q_t, k_t, v_t, gate_logit_t, meta_k, state, k_ring, v_ring,
+                   alpha, softmax_scale, y_t)
+
+
+def _decode(fn, pos, q_t, k_t, v_t, gate, meta_k, state, k_ring, v_ring, alpha, softmax_scale, y_t):
     torch = _torch()
     lib = load_library()
     B, H, d = q_t.shape
@@ -189,10 +235,10 @@ def lizard_decode_step(pos: int, q_t, k_t, v_t, log_g_t, meta_k, state, k_ring, 
                     softmax_scale=softmax_scale)
     if y_t is None:
         y_t = torch.empty_like(q_t)
-    st = lib.lizard_decode_step(ctypes.byref(p), int(pos), _ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(log_g_t),
-                                _ptr(meta_k), _ptr(state), _ptr(k_ring), _ptr(v_ring), _ptr(y_t),
-                                _stream(q_t.device))
-    _check("lizard_decode_step", st)
+    st = getattr(lib, fn)(ctypes.byref(p), int(pos), _ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(gate),
+                          _ptr(meta_k), _ptr(state), _ptr(k_ring), _ptr(v_ring), _ptr(y_t),
+                          _stream(q_t.device))
+    _check(fn, st)
     return y_t
 
 

@@ -38,18 +38,19 @@ float scale_of(const lizard_params_t* p) {
 
 lizard_status_t launched(hipError_t e) { return e == hipSuccess ? LIZARD_OK : LIZARD_E_LAUNCH; }
 
-}  // namespace
-
-LIZARD_API lizard_status_t lizard_attn_fwd(const lizard_params_t* p, const void* q, const void* k, const void* v,
-                                           const float* log_g, const void* meta_k, void* y, float* lse,
-                                           void* y_anchor, float* state_out, void* stream) {
+// The forward pass with the gates given as log-gates (log_g) or as logits
+// (gate_logit); exactly one of the two is used.
+lizard_status_t attn_fwd(const lizard_params_t* p, const void* q, const void* k, const void* v, const float* log_g,
+                         const void* gate_logit, bool logit, const void* meta_k, void* y, float* lse, void* y_anchor,
+                         float* state_out, void* stream) {
   lizard_status_t s = check_params(p, true);
   if (s != LIZARD_OK) return s;
   const int BH = p->B * p->H;
   if (BH == 0) return LIZARD_OK;  // nothing to read or write; empty tensors may have NULL data
   const bool seq = p->L > 0;
-  if ((seq && (!q || !k || !v || !log_g || !y)) || (p->n_meta > 0 && !meta_k)) return LIZARD_E_NULL;
-  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(log_g) || misaligned(y) ||
+  const void* gate = logit ? gate_logit : static_cast<const void*>(log_g);
+  if ((seq && (!q || !k || !v || !gate || !y)) || (p->n_meta > 0 && !meta_k)) return LIZARD_E_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(gate) || misaligned(y) ||
       misaligned(meta_k) || misaligned(lse) || misaligned(y_anchor) || misaligned(state_out))
     return LIZARD_E_ALIGN;
   if (!seq && state_out == nullptr) return LIZARD_OK;
@@ -59,7 +60,8 @@ LIZARD_API lizard_status_t lizard_attn_fwd(const lizard_params_t* p, const void*
   a.q = q;
   a.k = k;
   a.v = v;
-  a.log_g = log_g;
+  a.log_g = logit ? nullptr : log_g;
+  a.gate_logit = logit ? gate_logit : nullptr;
   a.meta = meta_k;
   a.y = y;
   a.lse = lse;
@@ -77,26 +79,23 @@ LIZARD_API lizard_status_t lizard_attn_fwd(const lizard_params_t* p, const void*
   return launched(lizard::launch_fwd(a, bf, p->dk, static_cast<hipStream_t>(stream)));
 }
 
-LIZARD_API size_t lizard_attn_bwd_workspace_size(const lizard_params_t* p) {
-  if (check_params(p, true) != LIZARD_OK) return 0;
-  return lizard::bwd_workspace_bytes(p->dtype == LIZARD_BF16, p->B * p->H, p->L, p->dk, p->n_meta);
-}
-
-LIZARD_API lizard_status_t lizard_attn_bwd(const lizard_params_t* p, const void* q, const void* k, const void* v,
-                                           const float* log_g, const void* meta_k, const float* lse,
-                                           const void* dy, void* dq, void* dk, void* dv, float* dlog_g,
-                                           float* dmeta_k, void* workspace, size_t workspace_bytes,
-                                           void* stream) {
+// The backward pass; with logits, dgate (element type) replaces dlog_g.
+lizard_status_t attn_bwd(const lizard_params_t* p, const void* q, const void* k, const void* v, const float* log_g,
+                         const void* gate_logit, bool logit, const void* meta_k, const float* lse, const void* dy,
+                         void* dq, void* dk, void* dv, float* dlog_g, void* dgate, float* dmeta_k, void* workspace,
+                         size_t workspace_bytes, void* stream) {
   lizard_status_t s = check_params(p, true);
   if (s != LIZARD_OK) return s;
   const int BH = p->B * p->H;
   const bool seq = BH > 0 && p->L > 0;   // otherwise only dmeta_k (zero) is written
-  if ((seq && (!q || !k || !v || !log_g || !lse || !dy || !dq || !dk || !dv || !dlog_g)) ||
+  const void* gate = logit ? gate_logit : static_cast<const void*>(log_g);
+  const void* dgo = logit ? dgate : static_cast<void*>(dlog_g);
+  if ((seq && (!q || !k || !v || !gate || !lse || !dy || !dq || !dk || !dv || !dgo)) ||
       (p->n_meta > 0 && p->H > 0 && !dmeta_k) || (seq && p->n_meta > 0 && !meta_k))
     return LIZARD_E_NULL;
-  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(log_g) || misaligned(meta_k) ||
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(gate) || misaligned(meta_k) ||
       misaligned(lse) || misaligned(dy) || misaligned(dq) || misaligned(dk) || misaligned(dv) ||
-      misaligned(dlog_g) || misaligned(dmeta_k) || misaligned(workspace))
+      misaligned(dgo) || misaligned(dmeta_k) || misaligned(workspace))
     return LIZARD_E_ALIGN;
   const size_t need = lizard::bwd_workspace_bytes(p->dtype == LIZARD_BF16, BH, p->L, p->dk, p->n_meta);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LIZARD_E_WORKSPACE;
@@ -105,14 +104,16 @@ LIZARD_API lizard_status_t lizard_attn_bwd(const lizard_params_t* p, const void*
   a.q = q;
   a.k = k;
   a.v = v;
-  a.log_g = log_g;
+  a.log_g = logit ? nullptr : log_g;
+  a.gate_logit = logit ? gate_logit : nullptr;
   a.meta = meta_k;
   a.lse = lse;
   a.dy = dy;
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  a.dlog_g = dlog_g;
+  a.dlog_g = logit ? nullptr : dlog_g;
+  a.dgate = logit ? dgate : nullptr;
   a.dmeta = dmeta_k;
   a.workspace = workspace;
   a.B = p->B;
@@ -126,25 +127,27 @@ LIZARD_API lizard_status_t lizard_attn_bwd(const lizard_params_t* p, const void*
   return launched(lizard::launch_bwd(a, p->dtype == LIZARD_BF16, p->dk, static_cast<hipStream_t>(stream)));
 }
 
-LIZARD_API lizard_status_t lizard_decode_step(const lizard_params_t* p, int64_t pos, const void* q_t,
-                                              const void* k_t, const void* v_t, const float* log_g_t,
-                                              const void* meta_k, float* state, void* k_ring, void* v_ring,
-                                              void* y_t, void* stream) {
+// One decode step; the token's gate as a log-gate or as a logit.
+lizard_status_t decode_step(const lizard_params_t* p, int64_t pos, const void* q_t, const void* k_t,
+                            const void* v_t, const float* log_g_t, const void* gate_logit_t, bool logit,
+                            const void* meta_k, float* state, void* k_ring, void* v_ring, void* y_t, void* stream) {
   lizard_status_t s = check_params(p, false);
   if (s != LIZARD_OK) return s;
   if (pos < 0) return LIZARD_E_SHAPE;
   const int BH = p->B * p->H;
   if (BH == 0) return LIZARD_OK;
-  if (!q_t || !k_t || !v_t || !log_g_t || !state || !k_ring || !v_ring || !y_t || (p->n_meta > 0 && !meta_k))
+  const void* gate = logit ? gate_logit_t : static_cast<const void*>(log_g_t);
+  if (!q_t || !k_t || !v_t || !gate || !state || !k_ring || !v_ring || !y_t || (p->n_meta > 0 && !meta_k))
     return LIZARD_E_NULL;
-  if (misaligned(q_t) || misaligned(k_t) || misaligned(v_t) || misaligned(log_g_t) || misaligned(meta_k) ||
+  if (misaligned(q_t) || misaligned(k_t) || misaligned(v_t) || misaligned(gate) || misaligned(meta_k) ||
       misaligned(state) || misaligned(k_ring) || misaligned(v_ring) || misaligned(y_t))
     return LIZARD_E_ALIGN;
   lizard::DecodeArgs a;
   a.q = q_t;
   a.k = k_t;
   a.v = v_t;
-  a.log_g = log_g_t;
+  a.log_g = logit ? nullptr : log_g_t;
+  a.gate_logit = logit ? gate_logit_t : nullptr;
   a.meta = meta_k;
   a.state = state;
   a.k_ring = k_ring;
@@ -158,6 +161,57 @@ LIZARD_API lizard_status_t lizard_decode_step(const lizard_params_t* p, int64_t 
   a.alpha = p->alpha;
   a.scale_log2 = scale_of(p) * 1.4426950408889634f;
   return launched(lizard::launch_decode(a, p->dtype == LIZARD_BF16, p->dk, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+LIZARD_API lizard_status_t lizard_attn_fwd(const lizard_params_t* p, const void* q, const void* k, const void* v,
+                                           const float* log_g, const void* meta_k, void* y, float* lse,
+                                           void* y_anchor, float* state_out, void* stream) {
+  return attn_fwd(p, q, k, v, log_g, nullptr, false, meta_k, y, lse, y_anchor, state_out, stream);
+}
+
+LIZARD_API lizard_status_t lizard_attn_fwd_logit(const lizard_params_t* p, const void* q, const void* k,
+                                                 const void* v, const void* gate_logit, const void* meta_k, void* y,
+                                                 float* lse, void* y_anchor, float* state_out, void* stream) {
+  return attn_fwd(p, q, k, v, nullptr, gate_logit, true, meta_k, y, lse, y_anchor, state_out, stream);
+}
+
+LIZARD_API size_t lizard_attn_bwd_workspace_size(const lizard_params_t* p) {
+  if (check_params(p, true) != LIZARD_OK) return 0;
+  return lizard::bwd_workspace_bytes(p->dtype == LIZARD_BF16, p->B * p->H, p->L, p->dk, p->n_meta);
+}
+
+LIZARD_API lizard_status_t lizard_attn_bwd(const lizard_params_t* p, const void* q, const void* k, const void* v,
+                                           const float* log_g, const void* meta_k, const float* lse,
+                                           const void* dy, void* dq, void* dk, void* dv, float* dlog_g,
+                                           float* dmeta_k, void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+  return attn_bwd(p, q, k, v, log_g, nullptr, false, meta_k, lse, dy, dq, dk, dv, dlog_g, nullptr, dmeta_k,
+                  workspace, workspace_bytes, stream);
+}
+
+LIZARD_API lizard_status_t lizard_attn_bwd_logit(const lizard_params_t* p, const void* q, const void* k,
+                                                 const void* v, const void* gate_logit, const void* meta_k,
+                                                 const float* lse, const void* dy, void* dq, void* dk, void* dv,
+                                                 void* dgate_logit, float* dmeta_k, void* workspace,
+                                                 size_t workspace_bytes, void* stream) {
+  return attn_bwd(p, q, k, v, nullptr, gate_logit, true, meta_k, lse, dy, dq, dk, dv, nullptr, dgate_logit, dmeta_k,
+                  workspace, workspace_bytes, stream);
+}
+
+LIZARD_API lizard_status_t lizard_decode_step(const lizard_params_t* p, int64_t pos, const void* q_t,
+                                              const void* k_t, const void* v_t, const float* log_g_t,
+                                              const void* meta_k, float* state, void* k_ring, void* v_ring,
+                                              void* y_t, void* stream) {
+  return decode_step(p, pos, q_t, k_t, v_t, log_g_t, nullptr, false, meta_k, state, k_ring, v_ring, y_t, stream);
+}
+
+LIZARD_API lizard_status_t lizard_decode_step_logit(const lizard_params_t* p, int64_t pos, const void* q_t,
+                                                    const void* k_t, const void* v_t, const void* gate_logit_t,
+                                                    const void* meta_k, float* state, void* k_ring, void* v_ring,
+                                                    void* y_t, void* stream) {
+  return decode_step(p, pos, q_t, k_t, v_t, nullptr, gate_logit_t, true, meta_k, state, k_ring, v_ring, y_t, stream);
 }
 
 LIZARD_API const char* lizard_status_string(lizard_status_t s) {
@@ -174,4 +228,4 @@ LIZARD_API const char* lizard_status_string(lizard_status_t s) {
   return "unknown status";
 }
 
-LIZARD_API int lizard_abi_version(void) { return 1; }
+LIZARD_API int lizard_abi_version(void) { return 2; }

@@ -224,7 +224,7 @@ __device__ __forceinline__ void chunk_prefix(const float* lg, int t0, int L, flo
 // ---------------------------------------------------------------------------
 // 2. reverse state-gradient pass: G_c = diag(2^B) G_{c+1} + Qe^T dO
 // ---------------------------------------------------------------------------
-template <typename T, int D, int DV>
+template <typename T, int D, int DV, bool LOGIT>
 __global__ __launch_bounds__(256, 1) void bwd_dstate_kernel(BwdArgs a) {
   typedef Mfma<T> M;
   constexpr int PAD = 16 / sizeof(T);
@@ -247,7 +247,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dstate_kernel(BwdArgs a) {
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
   const T* qg = reinterpret_cast<const T*>(a.q) + (size_t)bh * L * D;
   const T* dyg = reinterpret_cast<const T*>(a.dy) + (size_t)bh * L * D;
-  const float* lgg = a.log_g + (size_t)bh * L * D;
+  const float* lgg = LOGIT ? nullptr : a.log_g + (size_t)bh * L * D;
+  const T* xg = LOGIT ? reinterpret_cast<const T*>(a.gate_logit) + (size_t)bh * L * D : nullptr;
   T* Gg = reinterpret_cast<T*>(a.ws_dS) + (size_t)bh * nc * D * D;
   T* GTg = reinterpret_cast<T*>(a.ws_dST) + (size_t)bh * nc * D * D;
 
@@ -261,11 +262,27 @@ __global__ __launch_bounds__(256, 1) void bwd_dstate_kernel(BwdArgs a) {
   // 16w + rr, dims DPL*l..; dO words for the transposed staging
   typedef StageT<T, DV, 64> ST;
   float lv[16][DPL];
+  uint32_t xv[16];      // gate logits (DPL elements packed), when the gates come as logits
   uint32_t qv[16];
   uint32_t dyw[ST::RPT];
   auto load = [&](int c) __attribute__((always_inline)) {
     const int t0 = c * C;
-    chunk_gates<D>(lgg, t0, L, lv);
+    if constexpr (LOGIT) {
+      // raw bits; past L a logit of +inf (a gate of one, log gate 0)
+      constexpr uint32_t kInf = sizeof(T) == 4 ? 0x7f800000u : 0x7f807f80u;
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int t = t0 + 16 * w + rr;
+        const bool ok = t < L;
+        const T* xp = xg + (size_t)(ok ? t : 0) * D + DPL * l;
+        uint32_t u;
+        if constexpr (DPL * sizeof(T) == 4) u = *reinterpret_cast<const uint32_t*>(xp);
+        else u = *reinterpret_cast<const uint16_t*>(xp);
+        xv[rr] = ok ? u : kInf;
+      }
+    } else {
+      chunk_gates<D>(lgg, t0, L, lv);
+    }
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       const int t = t0 + 16 * w + rr;
@@ -282,6 +299,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dstate_kernel(BwdArgs a) {
 
   for (int c = nc - 1; c >= 0; --c) {
     // chunk c's operands from the registers: Qe^T and dO^T into LDS
+    if constexpr (LOGIT) {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr)
+#pragma unroll
+        for (int dd = 0; dd < DPL; ++dd) lv[rr][dd] = log_sigmoid(elem32<T>(xv[rr], dd));
+    }
     float beta[16][DPL], Bt[DPL];
     chunk_prefix_of<D>(lv, sTot, beta, Bt);
 #pragma unroll
@@ -641,7 +664,7 @@ struct GateLayout {
 // loads of each phase are issued before the barrier that precedes it.  The
 // grid covers chunks cb .. cb + ncl - 1; RAGGED: they may end past L (only
 // the last chunk of a sequence does), so token rows are range-checked.
-template <typename T, int D, bool RAGGED>
+template <typename T, int D, bool RAGGED, bool LOGIT>
 __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int cb, int ncl) {
   typedef GateLayout<T, D> Lay;
   typedef Mfma<T> M;
@@ -677,14 +700,16 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
   const T* __restrict__ kg = reinterpret_cast<const T*>(a.k) + (size_t)bh * L * D;
   const T* __restrict__ vg = reinterpret_cast<const T*>(a.v) + (size_t)bh * L * D;
   const T* __restrict__ dyg = reinterpret_cast<const T*>(a.dy) + (size_t)bh * L * D;
-  const float* __restrict__ lgg = a.log_g + (size_t)bh * L * D;
+  const float* __restrict__ lgg = LOGIT ? nullptr : a.log_g + (size_t)bh * L * D;
+  const T* __restrict__ xg = LOGIT ? reinterpret_cast<const T*>(a.gate_logit) + (size_t)bh * L * D : nullptr;
   const T* __restrict__ Sg = reinterpret_cast<const T*>(a.ws_states) + ((size_t)bh * nc + c) * D * D;
   const T* __restrict__ Gg = reinterpret_cast<const T*>(a.ws_dS) + ((size_t)bh * nc + c) * D * D;
   const T* __restrict__ GTg = reinterpret_cast<const T*>(a.ws_dST) + ((size_t)bh * nc + c) * D * D;
   T* __restrict__ dqo = reinterpret_cast<T*>(a.dq) + (size_t)bh * L * D;
   T* __restrict__ dko = reinterpret_cast<T*>(a.dk) + (size_t)bh * L * D;
   T* __restrict__ dvo = reinterpret_cast<T*>(a.dv) + (size_t)bh * L * D;
-  float* __restrict__ dbo = a.dlog_g + (size_t)bh * L * D;
+  float* __restrict__ dbo = LOGIT ? nullptr : a.dlog_g + (size_t)bh * L * D;
+  T* __restrict__ dxo = LOGIT ? reinterpret_cast<T*>(a.dgate) + (size_t)bh * L * D : nullptr;
   const int ib = 16 * w;                  // phase C: first dim of this wavefront's tile
 
 
@@ -696,7 +721,13 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
     const int t = t0 + RPW * w + rr;
     const bool ok = !RG || t < L;
     const size_t ro = (size_t)(ok ? t : 0) * D + DPL * l;
-    if constexpr (DPL == 2) {
+    if constexpr (LOGIT) {
+      uint32_t u;
+      if constexpr (DPL * sizeof(T) == 4) u = *reinterpret_cast<const uint32_t*>(xg + ro);
+      else u = *reinterpret_cast<const uint16_t*>(xg + ro);
+#pragma unroll
+      for (int dd = 0; dd < DPL; ++dd) lv[rr][dd] = ok ? log_sigmoid(elem32<T>(u, dd)) : 0.f;
+    } else if constexpr (DPL == 2) {
       const float2 f = *reinterpret_cast<const float2*>(lgg + ro);
       lv[rr][0] = ok ? f.x : 0.f;
       lv[rr][1] = ok ? f.y : 0.f;
@@ -792,9 +823,10 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
   // phase C's first token tile (the last one: the dlog_g suffix sums run
   // backwards): its rows and, for the epilogue, the anchor parts already in
   // dq, dk, dv and q, k of the lane's 4 dims; issued during phase B
+  constexpr int NEP = LOGIT ? 6 : 5;
   uint4 rows[2][3][QV];   // [buffer][dO, v, k][k-quarter]
-  float ep[2][5][4];      // [buffer][dq, dk, dv, q, k][dim]
-  auto load_ep = [&](int tt, float (&dst)[5][4]) __attribute__((always_inline)) {
+  float ep[2][NEP][4];    // [buffer][dq, dk, dv, q, k (, gate logit)][dim]
+  auto load_ep = [&](int tt, float (&dst)[NEP][4]) __attribute__((always_inline)) {
     const int trow = t0 + 16 * tt + m;
     const size_t o4 = (size_t)(!RG || trow < L ? trow : 0) * D + ib + 4 * g;
     load_pack<T, 4>(dqo + o4, dst[0]);
@@ -802,6 +834,7 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
     load_pack<T, 4>(dvo + o4, dst[2]);
     load_pack<T, 4>(qg + o4, dst[3]);
     load_pack<T, 4>(kg + o4, dst[4]);
+    if constexpr (LOGIT) load_pack<T, 4>(xg + o4, dst[NEP - 1]);
   };
 
   // ---- phase B: wavefront w stages the score tiles of token block I
@@ -1039,7 +1072,16 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
       dl[r] = sfx + carry[r] + xin[r];
       carry[r] += tile;
     }
-    if (live) *reinterpret_cast<f32x4*>(dbo + o4) = f32x4{dl[0], dl[1], dl[2], dl[3]};
+    if constexpr (LOGIT) {
+      // gradient w.r.t. the logits: d log sigmoid(x) / dx = sigmoid(-x)
+      const float* x4 = ep[cur][NEP - 1];
+      float dx[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dx[r] = dl[r] * sigmoid_neg(x4[r]);
+      if (live) store_pack<T, 4>(dxo + o4, dx);
+    } else {
+      if (live) *reinterpret_cast<f32x4*>(dbo + o4) = f32x4{dl[0], dl[1], dl[2], dl[3]};
+    }
   }
 }
 
@@ -1109,6 +1151,27 @@ hipError_t set_lds(K kernel, int bytes) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
+// the gate kernel over the full chunks, then over the last chunk if it ends past L
+template <typename T, int D, bool LOGIT>
+hipError_t launch_gate(const BwdArgs& a, int nfull, int nc, int groups, hipStream_t st) {
+  typedef GateLayout<T, D> GL;
+  static_assert(GL::TOTAL <= 160 * 1024, "LDS");
+  hipError_t e;
+  if (nfull > 0) {
+    if ((e = set_lds(&bwd_gate_kernel<T, D, false, LOGIT>, GL::TOTAL)) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_gate_kernel<T, D, false, LOGIT>), dim3(8 * groups * nfull), dim3(GL::NW * 64), GL::TOTAL,
+                       st, a, 0, nfull);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (nfull < nc) {
+    if ((e = set_lds(&bwd_gate_kernel<T, D, true, LOGIT>, GL::TOTAL)) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_gate_kernel<T, D, true, LOGIT>), dim3(8 * groups), dim3(GL::NW * 64), GL::TOTAL, st, a,
+                       nfull, 1);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 template <typename T, int D, int DV>
 hipError_t launch_bwd_t(BwdArgs a, hipStream_t st) {
   const int L = a.L, nc = (L + C - 1) / C;
@@ -1121,6 +1184,7 @@ hipError_t launch_bwd_t(BwdArgs a, hipStream_t st) {
     f.k = a.k;
     f.v = a.v;
     f.log_g = a.log_g;
+    f.gate_logit = a.gate_logit;
     f.meta = a.meta;
     f.y = nullptr;
     f.lse = nullptr;
@@ -1138,7 +1202,10 @@ hipError_t launch_bwd_t(BwdArgs a, hipStream_t st) {
     e = launch_fwd(f, sizeof(T) == 2, D, st);
     if (e != hipSuccess) return e;
     // 2. state gradients
-    hipLaunchKernelGGL((bwd_dstate_kernel<T, D, DV>), dim3(8 * groups * (D / DV)), dim3(256), 0, st, a);
+    if (a.gate_logit)
+      hipLaunchKernelGGL((bwd_dstate_kernel<T, D, DV, true>), dim3(8 * groups * (D / DV)), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((bwd_dstate_kernel<T, D, DV, false>), dim3(8 * groups * (D / DV)), dim3(256), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // 3. anchor, query side
     typedef AqLayout<T, D> AQ;
@@ -1153,21 +1220,11 @@ hipError_t launch_bwd_t(BwdArgs a, hipStream_t st) {
     hipLaunchKernelGGL((bwd_anchor_k_kernel<T, D>), dim3(8 * groups * nc), dim3(256), AK::TOTAL, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // 5. gated branch and outputs
-    // (full chunks, then the last chunk if it ends past L)
-    typedef GateLayout<T, D> GL;
-    static_assert(GL::TOTAL <= 160 * 1024, "LDS");
     const int nfull = L / C;
-    if (nfull > 0) {
-      if ((e = set_lds(&bwd_gate_kernel<T, D, false>, GL::TOTAL)) != hipSuccess) return e;
-      hipLaunchKernelGGL((bwd_gate_kernel<T, D, false>), dim3(8 * groups * nfull), dim3(GL::NW * 64), GL::TOTAL, st,
-                         a, 0, nfull);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    if (nfull < nc) {
-      if ((e = set_lds(&bwd_gate_kernel<T, D, true>, GL::TOTAL)) != hipSuccess) return e;
-      hipLaunchKernelGGL((bwd_gate_kernel<T, D, true>), dim3(8 * groups), dim3(GL::NW * 64), GL::TOTAL, st, a, nfull,
-                         1);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a.gate_logit) {
+      if ((e = launch_gate<T, D, true>(a, nfull, nc, groups, st)) != hipSuccess) return e;
+    } else {
+      if ((e = launch_gate<T, D, false>(a, nfull, nc, groups, st)) != hipSuccess) return e;
     }
   }
   // 6. sink keys (written even when B*L == 0: then zero)

@@ -44,6 +44,18 @@ __device__ __forceinline__ float log2_gate(float log_g) { return fmaxf(log_g * 1
 __device__ __forceinline__ float exp_e(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 __device__ __forceinline__ float exp_2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// The gate from its logit x (the gate projection's output): log sigmoid(x)
+// = min(x, 0) - ln(1 + e^{-|x|}) in natural-log units, from the hardware
+// base-2 exponential and logarithm (no overflow for either sign; +inf gives
+// 0, a gate of one).  Its derivative is sigmoid(-x) = 1 / (1 + e^x).
+__device__ __forceinline__ float log_sigmoid(float x) {
+  const float e = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
+  return fminf(x, 0.f) - kLn2 * __builtin_amdgcn_logf(1.f + e);
+}
+__device__ __forceinline__ float sigmoid_neg(float x) {
+  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(x * kLog2e));
+}
+
 // Per element type: elements per lane per MFMA step (KPL), the contraction
 // length one MFMA covers (KSTEP = 4 * KPL), the fragment type and the op.
 template <typename T> struct Mfma;

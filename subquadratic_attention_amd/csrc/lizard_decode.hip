@@ -5,7 +5,8 @@
 // section 4 "Effizienz": memory stays constant with context length).  One
 // token per (batch, head) at absolute position pos:
 //
-//   S <- diag(e^{log_g}) S + k v^T      (float32, in place)
+//   S <- diag(g) S + k v^T              (float32, in place; g = e^{log_g},
+//                                        or sigmoid(x) from the gate logit x)
 //   o  = S^T q
 //   ring slot pos mod w <- (k, v)
 //   y_anchor = softmax over the window max(0, pos-w+1)..pos and the m sink
@@ -21,7 +22,7 @@
 
 namespace lizard {
 
-template <typename T, int D>
+template <typename T, int D, bool LOGIT>
 __global__ __launch_bounds__(256) void lizard_decode_kernel(DecodeArgs a) {
   constexpr int CG = D / 4;            // float4 column groups per row
   constexpr int RG = 256 / CG;         // row groups
@@ -64,7 +65,12 @@ __global__ __launch_bounds__(256) void lizard_decode_kernel(DecodeArgs a) {
     sq[tid] = to_f32(qg[tid]);
     sk[tid] = to_f32(kg[tid]);
     sv[tid] = to_f32(vg[tid]);
-    sg[tid] = exp_e(a.log_g[(size_t)bh * D + tid]);
+    if constexpr (LOGIT) {
+      // the gate from its logit: sigmoid(x) = 1 / (1 + e^{-x})
+      sg[tid] = sigmoid_neg(-to_f32(reinterpret_cast<const T*>(a.gate_logit)[(size_t)bh * D + tid]));
+    } else {
+      sg[tid] = exp_e(a.log_g[(size_t)bh * D + tid]);
+    }
   }
   __syncthreads();
 
@@ -194,12 +200,18 @@ __global__ __launch_bounds__(256) void lizard_decode_kernel(DecodeArgs a) {
   }
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int dtype_bf16, int D, hipStream_t st) {
+template <typename T, int D>
+static void launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   dim3 grid(a.BH);
-  if (dtype_bf16 && D == 128) hipLaunchKernelGGL((lizard_decode_kernel<bf16, 128>), grid, dim3(256), 0, st, a);
-  else if (dtype_bf16 && D == 64) hipLaunchKernelGGL((lizard_decode_kernel<bf16, 64>), grid, dim3(256), 0, st, a);
-  else if (!dtype_bf16 && D == 64) hipLaunchKernelGGL((lizard_decode_kernel<float, 64>), grid, dim3(256), 0, st, a);
-  else if (!dtype_bf16 && D == 128) hipLaunchKernelGGL((lizard_decode_kernel<float, 128>), grid, dim3(256), 0, st, a);
+  if (a.gate_logit) hipLaunchKernelGGL((lizard_decode_kernel<T, D, true>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((lizard_decode_kernel<T, D, false>), grid, dim3(256), 0, st, a);
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int dtype_bf16, int D, hipStream_t st) {
+  if (dtype_bf16 && D == 128) launch_decode_t<bf16, 128>(a, st);
+  else if (dtype_bf16 && D == 64) launch_decode_t<bf16, 64>(a, st);
+  else if (!dtype_bf16 && D == 64) launch_decode_t<float, 64>(a, st);
+  else if (!dtype_bf16 && D == 128) launch_decode_t<float, 128>(a, st);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

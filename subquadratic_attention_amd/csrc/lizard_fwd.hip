@@ -132,7 +132,7 @@ __device__ __forceinline__ int opaque(int x) {
 // leaves a factor 2^36 of headroom below the float / bfloat16 maximum.
 constexpr float kMaxSpanLog2 = 92.0f;
 
-template <typename T, int D, int DV, bool STATES>
+template <typename T, int D, int DV, bool STATES, bool LOGIT>
 __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
   typedef FwdLayout<T, D, DV> Lay;
   typedef Mfma<T> M;
@@ -186,7 +186,8 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
   const T* __restrict__ qg = reinterpret_cast<const T*>(a.q) + (size_t)bh * L * D;
   const T* __restrict__ kg = reinterpret_cast<const T*>(a.k) + (size_t)bh * L * D;
   const T* __restrict__ vg = reinterpret_cast<const T*>(a.v) + (size_t)bh * L * D + j0;
-  const float* __restrict__ lgg = a.log_g + (size_t)bh * L * D;
+  const float* __restrict__ lgg = LOGIT ? nullptr : a.log_g + (size_t)bh * L * D;
+  const T* __restrict__ xg = LOGIT ? reinterpret_cast<const T*>(a.gate_logit) + (size_t)bh * L * D : nullptr;
   T* __restrict__ yg = reinterpret_cast<T*>(a.y) + (size_t)bh * L * D + j0;
   T* __restrict__ yag = a.y_anchor ? reinterpret_cast<T*>(a.y_anchor) + (size_t)bh * L * D + j0 : nullptr;
   float* __restrict__ lseg = (a.lse && split == 0) ? a.lse + (size_t)bh * L : nullptr;
@@ -219,7 +220,8 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
       for (int ct = 0; ct < NCT; ++ct) acc[rt][ct] = zero4();
 
     // ---- per-chunk global data (prefetched ahead, kept as raw bits) ----
-    float lgA[8][DPL];    // prep rows 8w+rr, dims DPL*l + dd
+    float lgA[8][DPL];    // prep rows 8w+rr, dims DPL*l + dd (from xA when the gates come as logits)
+    uint32_t xA[8];       // gate logits of those rows: DPL elements packed in 32 bits
     float loc[8][DPL];    // their prefix inside the wavefront's 8 rows
     uint32_t kA[8];       // the same rows' keys: DPL elements packed in 32 bits
     uint32_t qA[8];       // ... and queries
@@ -235,6 +237,7 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
       {
         const int tb = t0 + 8 * w;
         const float* lp = lgg + (size_t)tb * D + DPL * l;
+        const T* xp = xg + (size_t)tb * D + DPL * l;
         const T* kp = kg + (size_t)tb * D + DPL * l;
         const T* qp = qg + (size_t)tb * D + DPL * l;
   #pragma unroll
@@ -242,7 +245,11 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
           const bool ok = full || tb + rr < L;
           const int ro = ok ? rr * D : -tb * D;       // row 0 of the slice when out of range
           float lv[DPL];
-          if constexpr (DPL == 2) {
+          uint32_t xv = 0;
+          if constexpr (LOGIT) {
+            if constexpr (DPL * sizeof(T) == 4) xv = *reinterpret_cast<const uint32_t*>(xp + ro);
+            else xv = *reinterpret_cast<const uint16_t*>(xp + ro);
+          } else if constexpr (DPL == 2) {
             const float2 f = *reinterpret_cast<const float2*>(lp + ro);
             lv[0] = f.x;
             lv[1] = f.y;
@@ -257,8 +264,14 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
             kv = *reinterpret_cast<const uint16_t*>(kp + ro);
             qv = *reinterpret_cast<const uint16_t*>(qp + ro);
           }
+          if constexpr (LOGIT) {
+            // past L: a logit of +inf, a gate of one (as log_g = 0 below)
+            constexpr uint32_t kInf = sizeof(T) == 4 ? 0x7f800000u : 0x7f807f80u;
+            xA[rr] = ok ? xv : kInf;
+          } else {
   #pragma unroll
-          for (int dd = 0; dd < DPL; ++dd) lgA[rr][dd] = ok ? lv[dd] : 0.f;
+            for (int dd = 0; dd < DPL; ++dd) lgA[rr][dd] = ok ? lv[dd] : 0.f;
+          }
           kA[rr] = ok ? kv : 0u;
           qA[rr] = ok ? qv : 0u;
         }
@@ -298,6 +311,12 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
     // 2^-100 floor of the wide-span path) ----
     auto prefix_part = [&]() __attribute__((always_inline)) {
       const int l = opaque(threadIdx.x) & 63;
+      if constexpr (LOGIT) {
+  #pragma unroll
+        for (int rr = 0; rr < 8; ++rr)
+  #pragma unroll
+          for (int dd = 0; dd < DPL; ++dd) lgA[rr][dd] = log_sigmoid(elem32(xA[rr], dd));
+      }
       float tot[DPL];
   #pragma unroll
       for (int dd = 0; dd < DPL; ++dd) {
@@ -778,24 +797,25 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
   }
 }
 
-template <typename T, int D, int DV, bool STATES>
+template <typename T, int D, int DV, bool STATES, bool LOGIT>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   typedef FwdLayout<T, D, DV> Lay;
   static_assert(Lay::TOTAL <= 160 * 1024, "LDS budget");
   static_assert(D == 128 || (D == 64 && sizeof(T) == 2) || (D == 64 && DV == 32), "shapes");
   const int smem = Lay::TOTAL;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lizard_fwd_kernel<T, D, DV, STATES>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lizard_fwd_kernel<T, D, DV, STATES, LOGIT>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, smem);
   if (e != hipSuccess) return e;
   const int groups = (a.BH + 7) / 8;
   dim3 grid(8 * groups * a.nsplit);
-  hipLaunchKernelGGL((lizard_fwd_kernel<T, D, DV, STATES>), grid, dim3(512), smem, st, a);
+  hipLaunchKernelGGL((lizard_fwd_kernel<T, D, DV, STATES, LOGIT>), grid, dim3(512), smem, st, a);
   return hipGetLastError();
 }
 
 template <typename T, int D, int DV>
 static hipError_t launch_fwd_s(const FwdArgs& a, hipStream_t st) {
-  return a.states ? launch_fwd_t<T, D, DV, true>(a, st) : launch_fwd_t<T, D, DV, false>(a, st);
+  if (a.gate_logit) return a.states ? launch_fwd_t<T, D, DV, true, true>(a, st) : launch_fwd_t<T, D, DV, false, true>(a, st);
+  return a.states ? launch_fwd_t<T, D, DV, true, false>(a, st) : launch_fwd_t<T, D, DV, false, false>(a, st);
 }
 
 int fwd_value_slice(int dtype_bf16, int D) {

@@ -12,6 +12,7 @@ struct FwdArgs {
   const void* k;
   const void* v;
   const float* log_g;
+  const void* gate_logit;   // non-null: the gates come as logits (element type), log_g unused
   const void* meta;     // [H, n_meta, D]
   void* y;
   float* lse;           // nullable
@@ -28,6 +29,7 @@ struct DecodeArgs {
   const void* k;
   const void* v;
   const float* log_g;
+  const void* gate_logit;   // non-null: the gates come as logits (element type), log_g unused
   const void* meta;
   float* state;
   void* k_ring;
@@ -44,6 +46,7 @@ struct BwdArgs {
   const void* k;
   const void* v;
   const float* log_g;
+  const void* gate_logit;   // non-null: the gates come as logits; dgate (element type) replaces dlog_g
   const void* meta;
   const float* lse;
   const void* dy;
@@ -51,6 +54,7 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* dlog_g;
+  void* dgate;           // gradient w.r.t. the gate logits (when gate_logit is set)
   float* dmeta;          // [H, n_meta, D]
   void* workspace;
   // carved from the workspace by launch_bwd

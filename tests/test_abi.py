@@ -32,6 +32,7 @@ def header_functions():
 def test_header_declares_the_entry_points():
     names = header_functions()
     for want in ("lizard_attn_fwd", "lizard_attn_bwd", "lizard_attn_bwd_workspace_size", "lizard_decode_step",
+                 "lizard_attn_fwd_logit", "lizard_attn_bwd_logit", "lizard_decode_step_logit",
                  "lizard_status_string", "lizard_abi_version"):
         assert want in names
 
@@ -62,7 +63,7 @@ def test_param_struct_layout_matches_c(tmp_path):
 
 
 def test_version_and_strings(lib):
-    assert lib.lizard_abi_version() == 1
+    assert lib.lizard_abi_version() == 2
     for code, name in sqa.STATUS.items():
         s = lib.lizard_status_string(code)
         assert isinstance(s, bytes) and len(s) > 0
@@ -151,9 +152,7 @@ def test_empty_calls_do_nothing(lib):
 
 
 def test_binding_refuses_without_library(tmp_path):
-    import importlib
-
-    mod = importlib.reload(sqa)
+    mod = sqa
     saved = mod._lib
     mod._lib = None
     try:
@@ -161,3 +160,23 @@ def test_binding_refuses_without_library(tmp_path):
             mod.load_library(str(tmp_path / "missing.so"))
     finally:
         mod._lib = saved
+
+
+def test_logit_entry_points_check_their_gate_argument(lib):
+    """The *_logit calls run the same checks; their gate pointer is the
+    logits (a NULL or misaligned one is caught before any launch)."""
+    p = params()
+    f = lambda x: lib.lizard_attn_fwd_logit(ctypes.byref(p), FAKE, FAKE, FAKE, x, FAKE, FAKE, None, None, None, None)
+    assert f(None) == S["LIZARD_E_NULL"]
+    assert f(MIS) == S["LIZARD_E_ALIGN"]
+    b = lambda x, dx: lib.lizard_attn_bwd_logit(ctypes.byref(p), FAKE, FAKE, FAKE, x, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                FAKE, dx, FAKE, FAKE, 1 << 40, None)
+    assert b(None, FAKE) == S["LIZARD_E_NULL"]
+    assert b(FAKE, None) == S["LIZARD_E_NULL"]
+    assert b(FAKE, MIS) == S["LIZARD_E_ALIGN"]
+    dec_ = lambda x: lib.lizard_decode_step_logit(ctypes.byref(p), 3, FAKE, FAKE, FAKE, x, FAKE, FAKE, FAKE, FAKE,
+                                                   FAKE, None)
+    assert dec_(None) == S["LIZARD_E_NULL"]
+    assert dec_(MIS) == S["LIZARD_E_ALIGN"]
+    assert lib.lizard_attn_fwd_logit(ctypes.byref(params(dtype=7)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                                      None, None) == S["LIZARD_E_DTYPE"]
