@@ -220,7 +220,38 @@ def bench_decode(sqa, si, reps=3):
         "flushed_frac_hbm_peak": round(bytes_step / (ms_flushed * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "traffic": read_traffic("lizard_decode", "decode_b64_bf16"),
     }
-    del dec, ring0, y, state, state0, kr, vr, scratch, sink
+    # serving form: the same 1024 tokens as 256 calls of T = 4 tokens per row
+    # (lizard_decode_tokens, positions on the device); the state is read and
+    # written once per call
+    T = 4
+    pos_all = (L0 + T * torch.arange(steps // T, device="cuda", dtype=torch.int64))[:, None].repeat(1, w.B).contiguous()
+    dec4 = {kk: vv.view(steps // T, T, w.B, w.H, w.d).permute(0, 2, 3, 1, 4).contiguous() for kk, vv in dec.items()}
+    y4 = torch.empty((steps // T, w.B, w.H, T, w.d), device="cuda", dtype=torch.bfloat16)
+
+    def run_tokens():
+        state.copy_(state0)
+        kr.copy_(ring0["k"])
+        vr.copy_(ring0["v"])
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(steps // T):
+            sqa.lizard_decode_tokens(pos_all[i], dec4["q"][i], dec4["k"][i], dec4["v"][i], dec4["log_g"][i], meta,
+                                     state, kr, vr, alpha=w.alpha, y=y4[i])
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    run_tokens()
+    ms_tok = min(run_tokens() for _ in range(reps))
+    # per call: the state once, then per token the window, inputs and output
+    bytes_call = w.B * w.H * (decode_bytes_per_bh(w.d, w.window) + (T - 1) * (decode_bytes_per_bh(w.d, w.window)
+                                                                               - 2 * 4 * w.d * w.d))
+    out["tokens4"] = {"T": T, "us_per_token": round(ms_tok * 1e3, 2), "tokens_per_s": round(w.B / (ms_tok * 1e-3), 1),
+                      "alg_bytes_per_call": bytes_call,
+                      "gbps": round(bytes_call / (T * ms_tok * 1e-3) / 1e9, 1)}
+    del dec, dec4, y4, pos_all, ring0, y, state, state0, kr, vr, scratch, sink
     torch.cuda.empty_cache()
     return out
 

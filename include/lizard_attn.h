@@ -155,7 +155,30 @@ lizard_status_t lizard_decode_step(const lizard_params_t* p, int64_t pos,
                                    float* state, void* k_ring, void* v_ring,
                                    void* y_t, void* stream);
 
-/* ---- The same three calls with the gate given by its logits ------------
+/* Serving form of the decode step (constant-memory generation for a batch
+ * of sequences, de section 2 item 1 and section 4 "Effizienz"): T >= 1 new
+ * tokens per row, appended in order, each batch row at its own position.
+ *   pos         [B] int64, DEVICE pointer, 8-byte aligned: absolute position
+ *               of row b's first new token (its tokens take positions
+ *               pos[b] .. pos[b] + T - 1).  A negative value leaves row b
+ *               untouched: nothing of it is read or written, its y rows keep
+ *               their contents (padding slots of a continuous batch).
+ *   T           new tokens per row, 1 <= T <= 65536
+ *   q, k        [B, H, T, dk]   dtype
+ *   v           [B, H, T, dv]   dtype
+ *   log_g       [B, H, T, dk]   float32
+ *   y           [B, H, T, dv]   dtype, out
+ *   meta_k, state, k_ring, v_ring   as in lizard_decode_step
+ * Equal to T successive lizard_decode_step calls per row; the state is read
+ * and written once per call instead of once per token.  The positions are
+ * read on the device, so a caller never synchronises to pass them. */
+lizard_status_t lizard_decode_tokens(const lizard_params_t* p, const int64_t* pos, int32_t T,
+                                     const void* q, const void* k, const void* v,
+                                     const float* log_g, const void* meta_k,
+                                     float* state, void* k_ring, void* v_ring,
+                                     void* y, void* stream);
+
+/* ---- The same calls with the gate given by its logits ------------------
  *
  * The gate is a sigmoid of a learned projection of the token, Gamma =
  * sigmoid(W_gamma x) (de section 2 "Kernkomponenten" item 1; it section 2
@@ -163,7 +186,8 @@ lizard_status_t lizard_decode_step(const lizard_params_t* p, int64_t pos,
  * x directly and compute log_g = log(sigmoid(x)) inside the kernels (and,
  * in the backward pass, the gradient w.r.t. x = dlog_g * sigmoid(-x)), so
  * the float32 log-gate never makes a round trip through memory.
- *   gate_logit    [B, H, L, dk] dtype (decode: [B, H, dk]); any finite value
+ *   gate_logit    [B, H, L, dk] dtype (decode: [B, H, dk], [B, H, T, dk]);
+ *                 any finite value
  *   dgate_logit   [B, H, L, dk] dtype, out
  * Every other argument, the workspace size and the error behaviour are those
  * of the log-gate calls above; the results equal theirs for log_g =
@@ -188,10 +212,17 @@ lizard_status_t lizard_decode_step_logit(const lizard_params_t* p, int64_t pos,
                                          float* state, void* k_ring, void* v_ring,
                                          void* y_t, void* stream);
 
+lizard_status_t lizard_decode_tokens_logit(const lizard_params_t* p, const int64_t* pos, int32_t T,
+                                           const void* q, const void* k, const void* v,
+                                           const void* gate_logit, const void* meta_k,
+                                           float* state, void* k_ring, void* v_ring,
+                                           void* y, void* stream);
+
 /* Static description of a status code. */
 const char* lizard_status_string(lizard_status_t s);
 
-/* ABI version of this header: 2 (version 1 had no *_logit entry points). */
+/* ABI version of this header: 2 (version 1 had neither the *_logit nor the
+ * lizard_decode_tokens entry points). */
 int lizard_abi_version(void);
 
 #ifdef __cplusplus

@@ -51,6 +51,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with `python -m subquadratic_attention_amd.build`")
+    # torch first: its HIP runtime is then the one the library binds to (a
+    # library loaded before torch would bind another copy of the runtime,
+    # whose launches fail on torch's device memory)
+    _torch()
     lib = ctypes.CDLL(path)
     P = ctypes.POINTER(LizardParams)
     lib.lizard_attn_fwd.argtypes = [P] + [_vp] * 10
@@ -67,6 +71,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lizard_attn_bwd_logit.restype = ctypes.c_int
     lib.lizard_decode_step_logit.argtypes = [P, ctypes.c_int64] + [_vp] * 10
     lib.lizard_decode_step_logit.restype = ctypes.c_int
+    for fn in ("lizard_decode_tokens", "lizard_decode_tokens_logit"):
+        getattr(lib, fn).argtypes = [P, _vp, ctypes.c_int32] + [_vp] * 10
+        getattr(lib, fn).restype = ctypes.c_int
     lib.lizard_status_string.argtypes = [ctypes.c_int]
     lib.lizard_status_string.restype = ctypes.c_char_p
     lib.lizard_abi_version.argtypes = []
@@ -244,3 +251,37 @@ def _decode(fn, pos, q_t, k_t, v_t, gate, meta_k, state, k_ring, v_ring, alpha, 
 
 def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
+
+
+def lizard_decode_tokens(pos, q, k, v, log_g, meta_k, state, k_ring, v_ring, *, alpha: float,
+                         softmax_scale: float = 0.0, y=None):
+    """Serving decode: T new tokens per row, each row at its own position.
+    pos: [B] int64 on the GPU (negative = row inactive); q, k, v: [B, H, T, d];
+    log_g: [B, H, T, d] float32; state / rings as lizard_decode_step.
+    Returns y [B, H, T, d]."""
+    return _decode_tokens("lizard_decode_tokens", pos, q, k, v, log_g, meta_k, state, k_ring, v_ring, alpha,
+                          softmax_scale, y)
+
+
+def lizard_decode_tokens_logit(pos, q, k, v, gate_logit, meta_k, state, k_ring, v_ring, *, alpha: float,
+                               softmax_scale: float = 0.0, y=None):
+    """lizard_decode_tokens with the gates given by their logits (q's dtype)."""
+    return _decode_tokens("lizard_decode_tokens_logit", pos, q, k, v, gate_logit, meta_k, state, k_ring, v_ring,
+                          alpha, softmax_scale, y)
+
+
+def _decode_tokens(fn, pos, q, k, v, gate, meta_k, state, k_ring, v_ring, alpha, softmax_scale, y):
+    torch = _torch()
+    lib = load_library()
+    B, H, T, d = q.shape
+    w = k_ring.shape[2]
+    m = meta_k.shape[1] if meta_k is not None else 0
+    if pos.dtype != torch.int64 or pos.shape != (B,):
+        raise ValueError("pos must be an int64 tensor of shape [B]")
+    p = make_params(B, H, 0, d, window=w, n_meta=m, alpha=alpha, dtype=_dtype_code(q), softmax_scale=softmax_scale)
+    if y is None:
+        y = torch.empty_like(q)
+    st = getattr(lib, fn)(ctypes.byref(p), _ptr(pos), int(T), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(meta_k),
+                          _ptr(state), _ptr(k_ring), _ptr(v_ring), _ptr(y), _stream(q.device))
+    _check(fn, st)
+    return y

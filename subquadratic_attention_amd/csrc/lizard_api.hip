@@ -127,20 +127,25 @@ lizard_status_t attn_bwd(const lizard_params_t* p, const void* q, const void* k,
   return launched(lizard::launch_bwd(a, p->dtype == LIZARD_BF16, p->dk, static_cast<hipStream_t>(stream)));
 }
 
-// One decode step; the token's gate as a log-gate or as a logit.
-lizard_status_t decode_step(const lizard_params_t* p, int64_t pos, const void* q_t, const void* k_t,
-                            const void* v_t, const float* log_g_t, const void* gate_logit_t, bool logit,
-                            const void* meta_k, float* state, void* k_ring, void* v_ring, void* y_t, void* stream) {
+constexpr int32_t kMaxTokens = 1 << 16;
+
+// T decode tokens per row (T = 1: one step); the gates as log-gates or as
+// logits; one position for every row (pos_rows NULL) or one per batch row.
+lizard_status_t decode_step(const lizard_params_t* p, int64_t pos, const int64_t* pos_rows, int32_t T,
+                            const void* q_t, const void* k_t, const void* v_t, const float* log_g_t,
+                            const void* gate_logit_t, bool logit, const void* meta_k, float* state, void* k_ring,
+                            void* v_ring, void* y_t, void* stream) {
   lizard_status_t s = check_params(p, false);
   if (s != LIZARD_OK) return s;
-  if (pos < 0) return LIZARD_E_SHAPE;
+  if (pos < 0 || T < 1 || T > kMaxTokens) return LIZARD_E_SHAPE;
   const int BH = p->B * p->H;
   if (BH == 0) return LIZARD_OK;
   const void* gate = logit ? gate_logit_t : static_cast<const void*>(log_g_t);
   if (!q_t || !k_t || !v_t || !gate || !state || !k_ring || !v_ring || !y_t || (p->n_meta > 0 && !meta_k))
     return LIZARD_E_NULL;
   if (misaligned(q_t) || misaligned(k_t) || misaligned(v_t) || misaligned(gate) || misaligned(meta_k) ||
-      misaligned(state) || misaligned(k_ring) || misaligned(v_ring) || misaligned(y_t))
+      misaligned(state) || misaligned(k_ring) || misaligned(v_ring) || misaligned(y_t) ||
+      (reinterpret_cast<uintptr_t>(pos_rows) & 7u) != 0)
     return LIZARD_E_ALIGN;
   lizard::DecodeArgs a;
   a.q = q_t;
@@ -154,6 +159,8 @@ lizard_status_t decode_step(const lizard_params_t* p, int64_t pos, const void* q
   a.v_ring = v_ring;
   a.y = y_t;
   a.pos = pos;
+  a.pos_rows = reinterpret_cast<const long long*>(pos_rows);
+  a.T = T;
   a.BH = BH;
   a.H = p->H;
   a.n_meta = p->n_meta;
@@ -204,14 +211,32 @@ LIZARD_API lizard_status_t lizard_decode_step(const lizard_params_t* p, int64_t 
                                               const void* k_t, const void* v_t, const float* log_g_t,
                                               const void* meta_k, float* state, void* k_ring, void* v_ring,
                                               void* y_t, void* stream) {
-  return decode_step(p, pos, q_t, k_t, v_t, log_g_t, nullptr, false, meta_k, state, k_ring, v_ring, y_t, stream);
+  return decode_step(p, pos, nullptr, 1, q_t, k_t, v_t, log_g_t, nullptr, false, meta_k, state, k_ring, v_ring, y_t,
+                     stream);
 }
 
 LIZARD_API lizard_status_t lizard_decode_step_logit(const lizard_params_t* p, int64_t pos, const void* q_t,
                                                     const void* k_t, const void* v_t, const void* gate_logit_t,
                                                     const void* meta_k, float* state, void* k_ring, void* v_ring,
                                                     void* y_t, void* stream) {
-  return decode_step(p, pos, q_t, k_t, v_t, nullptr, gate_logit_t, true, meta_k, state, k_ring, v_ring, y_t, stream);
+  return decode_step(p, pos, nullptr, 1, q_t, k_t, v_t, nullptr, gate_logit_t, true, meta_k, state, k_ring, v_ring,
+                     y_t, stream);
+}
+
+LIZARD_API lizard_status_t lizard_decode_tokens(const lizard_params_t* p, const int64_t* pos, int32_t T,
+                                                const void* q, const void* k, const void* v, const float* log_g,
+                                                const void* meta_k, float* state, void* k_ring, void* v_ring,
+                                                void* y, void* stream) {
+  if (pos == nullptr && p != nullptr && p->B * (int64_t)p->H > 0) return LIZARD_E_NULL;
+  return decode_step(p, 0, pos, T, q, k, v, log_g, nullptr, false, meta_k, state, k_ring, v_ring, y, stream);
+}
+
+LIZARD_API lizard_status_t lizard_decode_tokens_logit(const lizard_params_t* p, const int64_t* pos, int32_t T,
+                                                      const void* q, const void* k, const void* v,
+                                                      const void* gate_logit, const void* meta_k, float* state,
+                                                      void* k_ring, void* v_ring, void* y, void* stream) {
+  if (pos == nullptr && p != nullptr && p->B * (int64_t)p->H > 0) return LIZARD_E_NULL;
+  return decode_step(p, 0, pos, T, q, k, v, nullptr, gate_logit, true, meta_k, state, k_ring, v_ring, y, stream);
 }
 
 LIZARD_API const char* lizard_status_string(lizard_status_t s) {

@@ -35,7 +35,9 @@ struct DecodeArgs {
   void* k_ring;
   void* v_ring;
   void* y;
-  long long pos;
+  long long pos;              // absolute position of each row's first new token ...
+  const long long* pos_rows;  // ... or, when non-null, per batch row [B] (negative: row inactive)
+  int T;                      // new tokens per row, appended in order (q, k, v, gates, y: [BH, T, D])
   int BH, H, n_meta, window;
   float alpha;
   float scale_log2;

@@ -33,6 +33,7 @@ def test_header_declares_the_entry_points():
     names = header_functions()
     for want in ("lizard_attn_fwd", "lizard_attn_bwd", "lizard_attn_bwd_workspace_size", "lizard_decode_step",
                  "lizard_attn_fwd_logit", "lizard_attn_bwd_logit", "lizard_decode_step_logit",
+                 "lizard_decode_tokens", "lizard_decode_tokens_logit",
                  "lizard_status_string", "lizard_abi_version"):
         assert want in names
 
@@ -180,3 +181,19 @@ def test_logit_entry_points_check_their_gate_argument(lib):
     assert dec_(MIS) == S["LIZARD_E_ALIGN"]
     assert lib.lizard_attn_fwd_logit(ctypes.byref(params(dtype=7)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
                                       None, None) == S["LIZARD_E_DTYPE"]
+
+
+def test_decode_tokens_checks(lib):
+    """Token count and position-array checks of the serving decode."""
+    p = params()
+    f = lambda pos, T, st=FAKE: lib.lizard_decode_tokens(ctypes.byref(p), pos, T, FAKE, FAKE, FAKE, FAKE, FAKE, st,
+                                                          FAKE, FAKE, FAKE, None)
+    assert f(None, 1) == S["LIZARD_E_NULL"]
+    assert f(FAKE, 0) == S["LIZARD_E_SHAPE"]
+    assert f(FAKE, -3) == S["LIZARD_E_SHAPE"]
+    assert f(FAKE, (1 << 16) + 1) == S["LIZARD_E_SHAPE"]
+    assert f(FAKE + 4, 2) == S["LIZARD_E_ALIGN"]
+    assert f(FAKE, 2, st=MIS) == S["LIZARD_E_ALIGN"]
+    pe = params(B=0)
+    assert lib.lizard_decode_tokens(ctypes.byref(pe), None, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                    None) == 0
