@@ -155,6 +155,32 @@ lizard_status_t lizard_decode_step(const lizard_params_t* p, int64_t pos,
                                    float* state, void* k_ring, void* v_ring,
                                    void* y_t, void* stream);
 
+/* Forward pass of a segment that continues a sequence (chunked prefill, and
+ * the prefill of a prompt appended to a conversation, for constant-memory
+ * generation: de section 2 item 1, section 4 "Effizienz").  The segment's
+ * L tokens sit at positions P .. P + L - 1 of a sequence whose first P
+ * tokens were processed before (P is not passed: nothing depends on it
+ * beyond the state and the halo).
+ *   log_g, gate_logit   the gates, as in lizard_attn_fwd or
+ *               lizard_attn_fwd_logit: exactly one of the two is non-NULL
+ *               (both non-NULL: LIZARD_E_SHAPE)
+ *   state_in    [B, H, dk, dv]  float32, nullable: S_{P-1}, the state_out of
+ *               the previous segment (NULL: zero, a sequence that starts here)
+ *   k_halo      [B, H, halo_len, dk] dtype: keys of positions P - halo_len ..
+ *               P - 1, the window's reach into the previous segment
+ *   v_halo      [B, H, halo_len, dv] dtype: their values
+ *   halo_len    0 <= halo_len <= window - 1; min(window - 1, P) reproduces the
+ *               single-call result (k_halo / v_halo may be NULL when 0)
+ * Every other argument as lizard_attn_fwd.  y, lse, y_anchor and state_out
+ * equal those rows of one lizard_attn_fwd call over all P + L tokens. */
+lizard_status_t lizard_attn_fwd_continue(const lizard_params_t* p,
+                                         const void* q, const void* k, const void* v,
+                                         const float* log_g, const void* gate_logit,
+                                         const void* meta_k, const float* state_in,
+                                         const void* k_halo, const void* v_halo, int32_t halo_len,
+                                         void* y, float* lse, void* y_anchor, float* state_out,
+                                         void* stream);
+
 /* Serving form of the decode step (constant-memory generation for a batch
  * of sequences, de section 2 item 1 and section 4 "Effizienz"): T >= 1 new
  * tokens per row, appended in order, each batch row at its own position.
@@ -221,8 +247,8 @@ lizard_status_t lizard_decode_tokens_logit(const lizard_params_t* p, const int64
 /* Static description of a status code. */
 const char* lizard_status_string(lizard_status_t s);
 
-/* ABI version of this header: 2 (version 1 had neither the *_logit nor the
- * lizard_decode_tokens entry points). */
+/* ABI version of this header: 2 (version 1 had none of the *_logit,
+ * lizard_attn_fwd_continue and lizard_decode_tokens entry points). */
 int lizard_abi_version(void);
 
 #ifdef __cplusplus

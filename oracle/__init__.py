@@ -30,4 +30,5 @@ from .lizard import (  # noqa: F401
     lizard_fwd_logit,
     lizard_bwd_logit,
     lizard_decode_step_logit,
+    lizard_fwd_continue,
 )

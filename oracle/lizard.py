@@ -300,6 +300,26 @@ def lizard_bwd(q, k, v, log_g, meta_k, w: int, alpha: float, dy, scale: Optional
             "dq_gate": gq, "dk_gate": gk}
 
 
+def lizard_fwd_continue(q, k, v, log_g, meta_k, w: int, alpha: float, state_in=None, k_halo=None, v_halo=None,
+                        scale: Optional[float] = None):
+    """A segment that continues a sequence (chunked prefill; de §2 item 1 and
+    §4 "Effizienz": the recurrent state carries the whole past).  The gated
+    branch starts from state_in (S before the segment's first token); the
+    window of the segment's first tokens reaches back into k_halo / v_halo
+    [N, h, d], the h tokens just before the segment.  Returns y, y_anchor,
+    lse of the segment's tokens and its final state."""
+    o, S = gla_recurrent(q, k, v, log_g, state_in)
+    h = 0 if k_halo is None else k_halo.shape[1]
+    if h:
+        qq = np.concatenate([np.zeros((q.shape[0], h, q.shape[2])), q], axis=1)   # halo queries: unused rows
+        ya, lse = anchor_window(qq, np.concatenate([k_halo, k], axis=1), np.concatenate([v_halo, v], axis=1),
+                                meta_k, w, scale)
+        ya, lse = ya[:, h:], lse[:, h:]
+    else:
+        ya, lse = anchor_window(q, k, v, meta_k, w, scale)
+    return {"y": o + alpha * ya, "y_anchor": ya, "lse": lse, "state": S}
+
+
 # ---------------------------------------------------------------------------
 # Gate from its logits
 # ---------------------------------------------------------------------------

@@ -71,6 +71,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lizard_attn_bwd_logit.restype = ctypes.c_int
     lib.lizard_decode_step_logit.argtypes = [P, ctypes.c_int64] + [_vp] * 10
     lib.lizard_decode_step_logit.restype = ctypes.c_int
+    lib.lizard_attn_fwd_continue.argtypes = [P] + [_vp] * 9 + [ctypes.c_int32] + [_vp] * 5
+    lib.lizard_attn_fwd_continue.restype = ctypes.c_int
     for fn in ("lizard_decode_tokens", "lizard_decode_tokens_logit"):
         getattr(lib, fn).argtypes = [P, _vp, ctypes.c_int32] + [_vp] * 10
         getattr(lib, fn).restype = ctypes.c_int
@@ -285,3 +287,34 @@ def _decode_tokens(fn, pos, q, k, v, gate, meta_k, state, k_ring, v_ring, alpha,
                           _ptr(state), _ptr(k_ring), _ptr(v_ring), _ptr(y), _stream(q.device))
     _check(fn, st)
     return y
+
+
+def lizard_attn_fwd_continue(q, k, v, meta_k, *, log_g=None, gate_logit=None, state_in=None, k_halo=None,
+                             v_halo=None, window: int, alpha: float, softmax_scale: float = 0.0, chunk: int = 64,
+                             need_lse: bool = False, need_y_anchor: bool = False, need_state: bool = False,
+                             out: Optional[Dict] = None) -> Dict:
+    """Forward pass of a segment that continues a sequence: state_in [B, H, d, d]
+    float32 (the previous segment's state), k_halo / v_halo [B, H, h, d] (the
+    previous h <= window - 1 tokens).  Gates as log_g (float32) or gate_logit."""
+    torch = _torch()
+    lib = load_library()
+    B, H, L, d = q.shape
+    m = meta_k.shape[1] if meta_k is not None else 0
+    hl = 0 if k_halo is None else int(k_halo.shape[2])
+    p = make_params(B, H, L, d, window=window, n_meta=m, alpha=alpha, dtype=_dtype_code(q), chunk=chunk,
+                    softmax_scale=softmax_scale)
+    o = dict(out) if out is not None else {}
+    if "y" not in o:
+        o["y"] = torch.empty_like(q)
+    if need_lse and "lse" not in o:
+        o["lse"] = torch.empty((B, H, L), device=q.device, dtype=torch.float32)
+    if need_y_anchor and "y_anchor" not in o:
+        o["y_anchor"] = torch.empty_like(q)
+    if need_state and "state" not in o:
+        o["state"] = torch.empty((B, H, d, d), device=q.device, dtype=torch.float32)
+    st = lib.lizard_attn_fwd_continue(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(gate_logit),
+                                      _ptr(meta_k), _ptr(state_in), _ptr(k_halo), _ptr(v_halo), hl, _ptr(o["y"]),
+                                      _ptr(o.get("lse")), _ptr(o.get("y_anchor")), _ptr(o.get("state")),
+                                      _stream(q.device))
+    _check("lizard_attn_fwd_continue", st)
+    return o

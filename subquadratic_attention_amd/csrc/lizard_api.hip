@@ -39,24 +39,30 @@ float scale_of(const lizard_params_t* p) {
 lizard_status_t launched(hipError_t e) { return e == hipSuccess ? LIZARD_OK : LIZARD_E_LAUNCH; }
 
 // The forward pass with the gates given as log-gates (log_g) or as logits
-// (gate_logit); exactly one of the two is used.
+// (gate_logit); exactly one of the two is used.  state_in / halo: a
+// continued sequence (NULL / 0 for a sequence that starts at position 0).
 lizard_status_t attn_fwd(const lizard_params_t* p, const void* q, const void* k, const void* v, const float* log_g,
-                         const void* gate_logit, bool logit, const void* meta_k, void* y, float* lse, void* y_anchor,
-                         float* state_out, void* stream) {
+                         const void* gate_logit, bool logit, const void* meta_k, const float* state_in,
+                         const void* k_halo, const void* v_halo, int32_t halo_len, void* y, float* lse,
+                         void* y_anchor, float* state_out, void* stream) {
   lizard_status_t s = check_params(p, true);
   if (s != LIZARD_OK) return s;
+  if (halo_len < 0 || halo_len > p->window - 1) return LIZARD_E_SHAPE;
   const int BH = p->B * p->H;
   if (BH == 0) return LIZARD_OK;  // nothing to read or write; empty tensors may have NULL data
   const bool seq = p->L > 0;
   const void* gate = logit ? gate_logit : static_cast<const void*>(log_g);
-  if ((seq && (!q || !k || !v || !gate || !y)) || (p->n_meta > 0 && !meta_k)) return LIZARD_E_NULL;
+  if ((seq && (!q || !k || !v || !gate || !y)) || (p->n_meta > 0 && !meta_k) ||
+      (seq && halo_len > 0 && (!k_halo || !v_halo)))
+    return LIZARD_E_NULL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(gate) || misaligned(y) ||
-      misaligned(meta_k) || misaligned(lse) || misaligned(y_anchor) || misaligned(state_out))
+      misaligned(meta_k) || misaligned(lse) || misaligned(y_anchor) || misaligned(state_out) ||
+      misaligned(state_in) || misaligned(k_halo) || misaligned(v_halo))
     return LIZARD_E_ALIGN;
   if (!seq && state_out == nullptr) return LIZARD_OK;
   const int bf = p->dtype == LIZARD_BF16;
   const int DV = lizard::fwd_value_slice(bf, p->dk);
-  lizard::FwdArgs a;
+  lizard::FwdArgs a{};
   a.q = q;
   a.k = k;
   a.v = v;
@@ -68,6 +74,10 @@ lizard_status_t attn_fwd(const lizard_params_t* p, const void* q, const void* k,
   a.y_anchor = y_anchor;
   a.state_out = state_out;
   a.states = nullptr;
+  a.state_in = state_in;
+  a.k_halo = halo_len > 0 ? k_halo : nullptr;
+  a.v_halo = halo_len > 0 ? v_halo : nullptr;
+  a.halo = halo_len;
   a.BH = BH;
   a.H = p->H;
   a.L = p->L;
@@ -147,7 +157,7 @@ lizard_status_t decode_step(const lizard_params_t* p, int64_t pos, const int64_t
       misaligned(state) || misaligned(k_ring) || misaligned(v_ring) || misaligned(y_t) ||
       (reinterpret_cast<uintptr_t>(pos_rows) & 7u) != 0)
     return LIZARD_E_ALIGN;
-  lizard::DecodeArgs a;
+  lizard::DecodeArgs a{};
   a.q = q_t;
   a.k = k_t;
   a.v = v_t;
@@ -175,13 +185,25 @@ lizard_status_t decode_step(const lizard_params_t* p, int64_t pos, const int64_t
 LIZARD_API lizard_status_t lizard_attn_fwd(const lizard_params_t* p, const void* q, const void* k, const void* v,
                                            const float* log_g, const void* meta_k, void* y, float* lse,
                                            void* y_anchor, float* state_out, void* stream) {
-  return attn_fwd(p, q, k, v, log_g, nullptr, false, meta_k, y, lse, y_anchor, state_out, stream);
+  return attn_fwd(p, q, k, v, log_g, nullptr, false, meta_k, nullptr, nullptr, nullptr, 0, y, lse, y_anchor, state_out,
+                  stream);
 }
 
 LIZARD_API lizard_status_t lizard_attn_fwd_logit(const lizard_params_t* p, const void* q, const void* k,
                                                  const void* v, const void* gate_logit, const void* meta_k, void* y,
                                                  float* lse, void* y_anchor, float* state_out, void* stream) {
-  return attn_fwd(p, q, k, v, nullptr, gate_logit, true, meta_k, y, lse, y_anchor, state_out, stream);
+  return attn_fwd(p, q, k, v, nullptr, gate_logit, true, meta_k, nullptr, nullptr, nullptr, 0, y, lse, y_anchor,
+                  state_out, stream);
+}
+
+LIZARD_API lizard_status_t lizard_attn_fwd_continue(const lizard_params_t* p, const void* q, const void* k,
+                                                    const void* v, const float* log_g, const void* gate_logit,
+                                                    const void* meta_k, const float* state_in, const void* k_halo,
+                                                    const void* v_halo, int32_t halo_len, void* y, float* lse,
+                                                    void* y_anchor, float* state_out, void* stream) {
+  if (log_g != nullptr && gate_logit != nullptr) return LIZARD_E_SHAPE;
+  return attn_fwd(p, q, k, v, log_g, gate_logit, gate_logit != nullptr, meta_k, state_in, k_halo, v_halo, halo_len, y,
+                  lse, y_anchor, state_out, stream);
 }
 
 LIZARD_API size_t lizard_attn_bwd_workspace_size(const lizard_params_t* p) {

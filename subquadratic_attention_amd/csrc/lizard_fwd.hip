@@ -192,9 +192,22 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
   T* __restrict__ yag = a.y_anchor ? reinterpret_cast<T*>(a.y_anchor) + (size_t)bh * L * D + j0 : nullptr;
   float* __restrict__ lseg = (a.lse && split == 0) ? a.lse + (size_t)bh * L : nullptr;
 
-  // ---- zero the key/value rings (the window of chunk 0 reads "chunk -1") ----
-  for (int i = tid; i < 128 * Lay::LDK; i += 512) sK[i] = from_f32<T>(0.f);
-  for (int i = tid; i < DV * Lay::LDVT; i += 512) sVt[i] = from_f32<T>(0.f);
+  // ---- the key/value rings: the window of chunk 0 reads "chunk -1" (key
+  // ring rows 64..127, value ring columns 128..191), which holds the halo
+  // tokens of a continued sequence in its last a.halo entries, else zeros ----
+  {
+    const int hb = 128 - a.halo;   // first halo row of the key ring / 64 + first halo column of the value ring
+    const T* khp = a.halo > 0 ? reinterpret_cast<const T*>(a.k_halo) + (size_t)bh * a.halo * D : nullptr;
+    const T* vhp = a.halo > 0 ? reinterpret_cast<const T*>(a.v_halo) + (size_t)bh * a.halo * D + j0 : nullptr;
+    for (int i = tid; i < 128 * Lay::LDK; i += 512) {
+      const int row = i / Lay::LDK, col = i % Lay::LDK;
+      sK[i] = row >= hb && col < D ? khp[(size_t)(row - hb) * D + col] : from_f32<T>(0.f);
+    }
+    for (int i = tid; i < DV * Lay::LDVT; i += 512) {
+      const int j = i / Lay::LDVT, col = i % Lay::LDVT;
+      sVt[i] = col >= hb + 64 && col < 192 ? vhp[(size_t)(col - hb - 64) * D + j] : from_f32<T>(0.f);
+    }
+  }
   // ---- sink keys (rows >= n_meta zero), resident in LDS throughout ----
   for (int i = tid; i < 16 * D; i += 512) {
     const int r = i / D, cidx = i % D;
@@ -218,6 +231,26 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
     for (int rt = 0; rt < DPL; ++rt)
   #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) acc[rt][ct] = zero4();
+    if constexpr (GATE && !STATES) {
+      if (a.state_in) {
+        // a continued sequence: the state before its first token
+        const float* si = a.state_in + (size_t)bh * D * D + j0;
+  #pragma unroll
+        for (int rt = 0; rt < DPL; ++rt)
+  #pragma unroll
+          for (int ct = 0; ct < NCT; ++ct)
+  #pragma unroll
+            for (int r = 0; r < 4; ++r)
+              acc[rt][ct][r] = si[(size_t)(16 * (DPL * I + rt) + 4 * g_lane + r) * D + 16 * ct + m_lane];
+        // consume the loads here: otherwise the accumulators enter the chunk
+        // loop with loads in flight on one path only, and their first use in
+        // every chunk would wait for all loads in flight
+  #pragma unroll
+        for (int rt = 0; rt < DPL; ++rt)
+  #pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) asm volatile("" : "+v"(acc[rt][ct]));
+      }
+    }
 
     // ---- per-chunk global data (prefetched ahead, kept as raw bits) ----
     float lgA[8][DPL];    // prep rows 8w+rr, dims DPL*l + dd (from xA when the gates come as logits)
@@ -570,9 +603,11 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
           zs[r] = 4 * g + r < a.n_meta ? zs[r] : -INFINITY;
           mr = fmaxf(mr, zs[r]);
         }
-        // key valid iff 0 <= t - s < lim; in the first chunk also s >= 0 (t - s <= t)
-        const int lim = (c == 0 && 16 * QB + m + 1 < a.window) ? 16 * QB + m + 1 : a.window;
-        const int lim_lo = (c == 0 && 16 * QB + 1 < a.window) ? 16 * QB + 1 : a.window;   // over the block
+        // key valid iff 0 <= t - s < lim; in the first chunk also s >= -halo
+        // (t - s <= t + halo: no keys before the sequence or its halo)
+        const int hl1 = a.halo + 1;
+        const int lim = (c == 0 && 16 * QB + m + hl1 < a.window) ? 16 * QB + m + hl1 : a.window;
+        const int lim_lo = (c == 0 && 16 * QB + hl1 < a.window) ? 16 * QB + hl1 : a.window;   // over the block
         const int dl = m - 4 * g;            // t - s = K_kt + dl - r
   #pragma unroll
         for (int kt = 0; kt < 6; ++kt) {

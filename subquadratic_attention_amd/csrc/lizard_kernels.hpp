@@ -19,6 +19,12 @@ struct FwdArgs {
   void* y_anchor;       // nullable
   float* state_out;     // nullable
   void* states;         // nullable: chunk-start states S_c, [BH, nc, D, D] element type, row-major
+  // continuation of a longer sequence (all nullable / 0): the state before
+  // the first token, and the keys / values of the halo tokens just before it
+  const float* state_in;   // [BH, D, D] float32
+  const void* k_halo;      // [BH, halo, D] element type
+  const void* v_halo;      // [BH, halo, D] element type
+  int halo;                // 0 .. window - 1
   int BH, H, L, n_meta, window, nsplit;
   float alpha;
   float scale_log2;     // softmax scale * log2(e)

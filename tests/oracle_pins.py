@@ -404,6 +404,29 @@ def p23_logit_decode_continues_prefill(O):
                                             x[:, L - 1], mu, w, alpha)
     return max(_rel(y, full["y"][:, L - 1]), _rel(S, full["state"]))
 
+
+def p24_segments_equal_one_pass(O):
+    """A sequence processed as segments (each continuing from the previous
+    one's state and its last min(w - 1, P) keys / values) equals one pass
+    over the whole sequence, for split points inside and outside the first
+    window and a window of one."""
+    q, k, v, lg, mu = _rand(24, N=2, L=40, d=5, m=2)
+    worst = 0.0
+    for w, cuts in ((6, (3, 17, 18, 33)), (1, (1, 20)), (40, (7,))):
+        whole = O.lizard_fwd(q, k, v, lg, mu, w, 0.5)
+        bounds = (0,) + cuts + (q.shape[1],)
+        S = None
+        for a, b in zip(bounds[:-1], bounds[1:]):
+            h = min(w - 1, a)
+            kh = k[:, a - h:a] if h else None
+            vh = v[:, a - h:a] if h else None
+            seg = O.lizard_fwd_continue(q[:, a:b], k[:, a:b], v[:, a:b], lg[:, a:b], mu, w, 0.5, S, kh, vh)
+            S = seg["state"]
+            for key in ("y", "lse"):
+                worst = max(worst, _rel(seg[key], whole[key][:, a:b]))
+        worst = max(worst, _rel(S, whole["state"]))
+    return worst
+
 ALL_PINS = {
     "P1": p1_recurrent_equals_quadratic,
     "P2": p2_unit_gate_is_causal_linear_attention,
@@ -428,6 +451,7 @@ ALL_PINS = {
     "P21": p21_log_sigmoid,
     "P22": p22_logit_gradients,
     "P23": p23_logit_decode_continues_prefill,
+    "P24": p24_segments_equal_one_pass,
 }
 
 # finite differences carry O(h^2) truncation and O(eps/h) rounding error

@@ -33,7 +33,7 @@ def test_header_declares_the_entry_points():
     names = header_functions()
     for want in ("lizard_attn_fwd", "lizard_attn_bwd", "lizard_attn_bwd_workspace_size", "lizard_decode_step",
                  "lizard_attn_fwd_logit", "lizard_attn_bwd_logit", "lizard_decode_step_logit",
-                 "lizard_decode_tokens", "lizard_decode_tokens_logit",
+                 "lizard_decode_tokens", "lizard_decode_tokens_logit", "lizard_attn_fwd_continue",
                  "lizard_status_string", "lizard_abi_version"):
         assert want in names
 
@@ -197,3 +197,16 @@ def test_decode_tokens_checks(lib):
     pe = params(B=0)
     assert lib.lizard_decode_tokens(ctypes.byref(pe), None, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                     None) == 0
+
+
+def test_continue_checks(lib):
+    p = params(window=16)
+    f = lambda lg, xg, hl, kh=FAKE, vh=FAKE, si=FAKE: lib.lizard_attn_fwd_continue(
+        ctypes.byref(p), FAKE, FAKE, FAKE, lg, xg, FAKE, si, kh, vh, hl, FAKE, None, None, None, None)
+    assert f(FAKE, FAKE, 0) == S["LIZARD_E_SHAPE"]          # both gate forms
+    assert f(None, None, 0) == S["LIZARD_E_NULL"]           # neither
+    assert f(FAKE, None, 16) == S["LIZARD_E_SHAPE"]         # halo longer than window - 1
+    assert f(FAKE, None, -1) == S["LIZARD_E_SHAPE"]
+    assert f(FAKE, None, 3, kh=None) == S["LIZARD_E_NULL"]
+    assert f(FAKE, None, 3, vh=MIS) == S["LIZARD_E_ALIGN"]
+    assert f(FAKE, None, 0, si=MIS) == S["LIZARD_E_ALIGN"]

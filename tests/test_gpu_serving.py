@@ -131,3 +131,55 @@ def test_tokens_logit(gpu_lib):
     ref = oracle.lizard_fwd_logit(flat(x["q"]), flat(x["k"]), flat(x["v"]), flat(x["gate_logit"]),
                                   meta_per_slice(x["meta_k"], B), w, 0.5)
     assert_close(down(y).reshape(B * H, T, d), ref["y"][:, L0:], dtype, "decode_tokens_logit y")
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("cuts,w", [((100,), 64), ((10, 70), 64), ((64, 128), 16), ((33,), 1), ((5, 6, 200), 64)])
+def test_prefill_in_segments(gpu_lib, dtype, d, cuts, w):
+    """A sequence prefilled as segments (lizard_attn_fwd_continue with the
+    previous segment's state and last min(w-1, P) keys / values) equals the
+    oracle's one pass over the whole sequence, outputs, lse and final state."""
+    import torch
+
+    B, H, L = 2, 2, 260
+    x = si.custom_inputs(53, B, H, L, d, 4, dtype)
+    log(f"continue dtype={dtype} d={d} cuts={cuts} w={w}")
+    q, k, v, lg, meta = up(x["q"], dtype), up(x["k"], dtype), up(x["v"], dtype), up_f32(x["log_g"]), up(x["meta_k"], dtype)
+    ref = oracle.lizard_fwd(flat(x["q"]), flat(x["k"]), flat(x["v"]), flat(x["log_g"]), meta_per_slice(x["meta_k"], B),
+                            w, 0.5)
+    bounds = (0,) + cuts + (L,)
+    state = None
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        h = min(w - 1, a)
+        kh = k[:, :, a - h:a].contiguous() if h else None
+        vh = v[:, :, a - h:a].contiguous() if h else None
+        seg = gpu_lib.lizard_attn_fwd_continue(q[:, :, a:b].contiguous(), k[:, :, a:b].contiguous(),
+                                               v[:, :, a:b].contiguous(), meta, log_g=lg[:, :, a:b].contiguous(),
+                                               state_in=state, k_halo=kh, v_halo=vh, window=w, alpha=0.5,
+                                               need_lse=True, need_state=True)
+        torch.cuda.synchronize()
+        assert_close(down(seg["y"]).reshape(B * H, b - a, d), ref["y"][:, a:b], dtype, f"segment {a}:{b} y")
+        assert_close(down(seg["lse"]).reshape(B * H, b - a), ref["lse"][:, a:b], "f32", f"segment {a}:{b} lse",
+                     tau=2e-2 if dtype == "bf16" else 1e-4)
+        state = seg["state"]
+    assert_close(down(state).reshape(B * H, d, d), ref["state"], dtype, "final state")
+
+
+def test_prefill_in_segments_logit(gpu_lib):
+    """The same with the gates given by their logits."""
+    import torch
+
+    dtype, d, B, H, L, w, cut = "bf16", 128, 1, 3, 200, 64, 90
+    x = si.custom_inputs(54, B, H, L, d, 4, dtype)
+    q, k, v, xg, meta = (up(x[n], dtype) for n in ("q", "k", "v", "gate_logit", "meta_k"))
+    first = gpu_lib.lizard_attn_fwd_logit(q[:, :, :cut].contiguous(), k[:, :, :cut].contiguous(),
+                                          v[:, :, :cut].contiguous(), xg[:, :, :cut].contiguous(), meta, window=w,
+                                          alpha=0.5, need_state=True)
+    seg = gpu_lib.lizard_attn_fwd_continue(q[:, :, cut:].contiguous(), k[:, :, cut:].contiguous(),
+                                           v[:, :, cut:].contiguous(), meta, gate_logit=xg[:, :, cut:].contiguous(),
+                                           state_in=first["state"], k_halo=k[:, :, cut - w + 1:cut].contiguous(),
+                                           v_halo=v[:, :, cut - w + 1:cut].contiguous(), window=w, alpha=0.5)
+    torch.cuda.synchronize()
+    ref = oracle.lizard_fwd_logit(flat(x["q"]), flat(x["k"]), flat(x["v"]), flat(x["gate_logit"]),
+                                  meta_per_slice(x["meta_k"], B), w, 0.5)
+    assert_close(down(seg["y"]).reshape(B * H, L - cut, d), ref["y"][:, cut:], dtype, "continued y (logits)")

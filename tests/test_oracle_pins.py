@@ -57,6 +57,10 @@ MUTATIONS = [
      "np.minimum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))"),
     ("decode logits not through the log-sigmoid", "log_sigmoid(gate_logit_t), meta_k, w, alpha,",
      "gate_logit_t, meta_k, w, alpha,"),
+    ("continuation drops the incoming state", "o, S = gla_recurrent(q, k, v, log_g, state_in)",
+     "o, S = gla_recurrent(q, k, v, log_g)"),
+    ("continuation ignores the halo", "        ya, lse = ya[:, h:], lse[:, h:]\n",
+     "        ya, lse = anchor_window(q, k, v, meta_k, w, scale)\n"),
 ]
 
 
