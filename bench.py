@@ -103,10 +103,10 @@ def time_region(fn, steps: int, warmup: int):
     return start.elapsed_time(stop) / steps  # ms
 
 
-def bench_fwd(sqa, si, steps, warmup, logit=False):
+def bench_fwd(sqa, si, steps, warmup, logit=False, workload="llama3_8b_prefill_bf16"):
     import torch
 
-    w = si.WORKLOADS["llama3_8b_prefill_bf16"]
+    w = si.WORKLOADS[workload]
     st = si.storage_inputs(w, with_logit=logit)
     x = {}
     for k, v in st.items():
@@ -127,7 +127,9 @@ def bench_fwd(sqa, si, steps, warmup, logit=False):
 
     ms = time_region(step, steps, warmup)
     head_tokens = w.B * w.H * w.L
-    alg_bytes = head_tokens * (fwd_logit_bytes_per_head_token(w.d) if logit else fwd_bytes_per_head_token(w.d))
+    elem = 2 if w.dtype == "bf16" else 4
+    alg_bytes = head_tokens * (fwd_logit_bytes_per_head_token(w.d, elem) if logit else
+                               fwd_bytes_per_head_token(w.d, elem))
     alg_flops = head_tokens * fwd_flops_per_head_token(w.d, w.chunk, w.window, w.n_meta)
     del x, out
     torch.cuda.empty_cache()
@@ -142,6 +144,20 @@ def bench_fwd_logit(sqa, si, steps, warmup):
     return {"workload": "llama3_8b_prefill_bf16, gate logits in bf16", "ms": round(ms, 5),
             "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1), "alg_bytes": alg_bytes, "gbps": round(gbs, 1),
             "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def bench_fp32_ablation(sqa, si, steps, warmup):
+    """The forward with bf16 operands (log-space factors folded into bf16 MFMA
+    operands) against the same kernel with fp32 operands and fp32 MFMA, on the
+    prefill at d=64 (B=4, H=32, L=4096), the largest head dim the fp32 build
+    supports."""
+    res = {}
+    for name in ("prefill_d64_bf16", "prefill_d64_f32"):
+        w, ms, alg_bytes, _ = bench_fwd(sqa, si, steps, warmup, workload=name)
+        res[name] = {"ms": round(ms, 5), "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1),
+                     "gbps": round(alg_bytes / (ms * 1e-3) / 1e9, 1)}
+    res["bf16_over_fp32"] = round(res["prefill_d64_bf16"]["tokens_per_s"] / res["prefill_d64_f32"]["tokens_per_s"], 3)
+    return res
 
 
 def bench_decode(sqa, si, reps=3):
@@ -343,7 +359,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-logit", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "decode", "bwd", "fwd_logit", "bwd_logit"], default=None,
+    ap.add_argument("--no-ablation", action="store_true")
+    ap.add_argument("--only", choices=["fwd", "decode", "bwd", "fwd_logit", "bwd_logit", "fp32_ablation"], default=None,
                     help="run one leg only (for profiler runs); prints that leg's record")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -384,6 +401,9 @@ def main():
     if args.only == "bwd_logit":
         print(json.dumps(bench_bwd(sqa, si, args.steps, args.warmup, logit=True)), flush=True)
         return
+    if args.only == "fp32_ablation":
+        print(json.dumps(bench_fp32_ablation(sqa, si, args.steps, args.warmup)), flush=True)
+        return
 
     w, ms, alg_bytes, alg_flops = bench_fwd(sqa, si, args.steps, args.warmup)
     print(f"# fwd done: {ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
@@ -420,6 +440,9 @@ def main():
     if not args.no_logit:
         rec["fwd_logit"] = bench_fwd_logit(sqa, si, args.steps, args.warmup)
         print("# fwd_logit done", file=sys.stderr, flush=True)
+    if not args.no_ablation:
+        rec["fp32_ablation"] = bench_fp32_ablation(sqa, si, args.steps, args.warmup)
+        print("# fp32 ablation done", file=sys.stderr, flush=True)
     if not args.no_decode:
         rec["decode"] = bench_decode(sqa, si)
         print("# decode done", file=sys.stderr, flush=True)

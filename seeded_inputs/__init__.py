@@ -71,6 +71,10 @@ WORKLOADS: Dict[str, Workload] = {
                                   gate_mu=2.0, gate_sd=2.0),
     "decode_b64_bf16": Workload("decode_b64_bf16", 3, "bf16", B=64, H=32, L=2048, d=128, steps=1024),
     "train_bwd_bf16": Workload("train_bwd_bf16", 4, "bf16", B=8, H=32, L=2048, d=128),
+    # the prefill at d=64 in both operand types (the fp32 build of the forward
+    # kernel exists at d=64 only): the bf16-vs-fp32 ablation
+    "prefill_d64_bf16": Workload("prefill_d64_bf16", 5, "bf16", B=4, H=32, L=4096, d=64),
+    "prefill_d64_f32": Workload("prefill_d64_f32", 6, "f32", B=4, H=32, L=4096, d=64),
 }
 
 

@@ -163,7 +163,7 @@ def _sampled_slices(B, H):
     return sorted(picks)
 
 
-@pytest.mark.parametrize("name", ["llama3_8b_prefill_bf16", "long_ctx_32k_bf16"])
+@pytest.mark.parametrize("name", ["llama3_8b_prefill_bf16", "long_ctx_32k_bf16", "prefill_d64_bf16", "prefill_d64_f32"])
 def test_full_size_workload_sampled(gpu_lib, name):
     """The benchmark's launch configuration at full size; sampled (b, h)
     slices over the full length are compared with the oracle."""
@@ -180,6 +180,6 @@ def test_full_size_workload_sampled(gpu_lib, name):
         s = si.slice_inputs(w, b, h)
         o = oracle.lizard_fwd(s["q"][None], s["k"][None], s["v"][None], s["log_g"][None],
                               si.meta_keys(w, h)[None], w.window, w.alpha)
-        errs = [assert_close(down(out[key][b, h]), o[key][0], "bf16", f"{name} {key}[{b},{h}]")
+        errs = [assert_close(down(out[key][b, h]), o[key][0], w.dtype, f"{name} {key}[{b},{h}]")
                 for key in ("y", "y_anchor", "lse", "state")]
         log(f"{name} slice ({b},{h}): " + " ".join(f"{e:.2e}" for e in errs))
