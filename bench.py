@@ -320,6 +320,52 @@ def bench_bwd(sqa, si, steps=10, warmup=3, logit=False):
     return res
 
 
+def bench_stage1(sqa, si, steps=10, warmup=3):
+    """One synthetic stage-1 attention-transfer step on the backward workload's
+    shapes (B=8, H=32, L=2048, d=128, bf16): the causal softmax teacher, the
+    layer's forward (with lse), the output-matching loss and the layer's
+    backward.  The teacher is also timed alone (causal QK^T and PV flops)."""
+    import numpy as np
+    import torch
+
+    w = si.WORKLOADS["train_bwd_bf16"]
+    st = si.storage_inputs(w)
+    x = {k: (torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).cuda() if v.dtype == np.uint16 else
+             torch.from_numpy(v).cuda()) for k, v in st.items()}
+    del st
+    ws = torch.empty(max(16, sqa.lizard_attn_bwd_workspace_size(w.B, w.H, w.L, w.d, window=w.window,
+                                                                n_meta=w.n_meta, dtype=sqa.LIZARD_BF16)),
+                     device="cuda", dtype=torch.uint8)
+    tout = {"y": torch.empty_like(x["q"])}
+    fout = {"y": torch.empty_like(x["q"]),
+            "lse": torch.empty((w.B, w.H, w.L), device="cuda", dtype=torch.float32)}
+    dy = torch.empty_like(x["q"])
+    loss_bh = torch.empty((w.B, w.H), device="cuda", dtype=torch.float32)
+    gout = {}
+
+    def teacher():
+        sqa.lizard_softmax_attn_fwd(x["q"], x["k"], x["v"], out=tout)
+
+    def step():
+        teacher()
+        sqa.lizard_attn_fwd(x["q"], x["k"], x["v"], x["log_g"], x["meta_k"], window=w.window, alpha=w.alpha,
+                            need_lse=True, out=fout)
+        sqa.lizard_transfer_loss(fout["y"], tout["y"], dy=dy, loss_bh=loss_bh)
+        sqa.lizard_attn_bwd(x["q"], x["k"], x["v"], x["log_g"], x["meta_k"], fout["lse"], dy, window=w.window,
+                            alpha=w.alpha, workspace=ws, out=gout)
+
+    ms = time_region(step, steps, warmup)
+    ms_t = time_region(teacher, 3 * steps, warmup)
+    t_flops = w.B * w.H * 2 * w.L * (w.L + 1) * w.d    # causal pairs x (QK^T + PV) x 2 flops
+    res = {"workload": "train_bwd_bf16 shapes, teacher = causal softmax attention", "ms": round(ms, 4),
+           "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1), "loss": round(float(loss_bh.sum()), 6),
+           "teacher_ms": round(ms_t, 4), "teacher_tflops": round(t_flops / (ms_t * 1e-3) / 1e12, 1),
+           "teacher_frac_mfma_peak": round(t_flops / (ms_t * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    del x, ws, tout, fout, dy, loss_bh, gout
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(si, target_s: float = 15.0):
     """The float64 oracle (oracle.lizard_fwd) on a bounded sample: whole-length
     heads of the 4K prefill workload, one BLAS thread."""
@@ -360,7 +406,9 @@ def main():
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-logit", action="store_true")
     ap.add_argument("--no-ablation", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "decode", "bwd", "fwd_logit", "bwd_logit", "fp32_ablation"], default=None,
+    ap.add_argument("--no-stage1", action="store_true")
+    ap.add_argument("--only", choices=["fwd", "decode", "bwd", "fwd_logit", "bwd_logit", "fp32_ablation", "stage1"],
+                    default=None,
                     help="run one leg only (for profiler runs); prints that leg's record")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -400,6 +448,9 @@ def main():
         return
     if args.only == "bwd_logit":
         print(json.dumps(bench_bwd(sqa, si, args.steps, args.warmup, logit=True)), flush=True)
+        return
+    if args.only == "stage1":
+        print(json.dumps(bench_stage1(sqa, si)), flush=True)
         return
     if args.only == "fp32_ablation":
         print(json.dumps(bench_fp32_ablation(sqa, si, args.steps, args.warmup)), flush=True)
@@ -454,6 +505,9 @@ def main():
         except sqa.LizardError as e:
             rec["bwd"] = {"error": str(e)}
         print("# bwd done", file=sys.stderr, flush=True)
+    if not args.no_stage1:
+        rec["stage1"] = bench_stage1(sqa, si)
+        print("# stage1 done", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(si)
     print(json.dumps(rec), flush=True)

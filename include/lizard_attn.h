@@ -244,11 +244,40 @@ lizard_status_t lizard_decode_tokens_logit(const lizard_params_t* p, const int64
                                            float* state, void* k_ring, void* v_ring,
                                            void* y, void* stream);
 
+/* ---- Stage-1 attention transfer --------------------------------------
+ *
+ * The layer is trained in two stages; the first fits it to reproduce the
+ * outputs of the softmax attention it replaces, on the same q, k, v (de
+ * section 2 "Trainingsprozess"; it section 2 "Fase di Addestramento").  One
+ * step: lizard_softmax_attn_fwd (the teacher), lizard_attn_fwd (need lse),
+ * lizard_transfer_loss (dy), lizard_attn_bwd.
+ *
+ * Causal softmax attention over every earlier token, the teacher:
+ *   y_t = sum_{s <= t} softmax_s(scale * q_t . k_s) v_s
+ *   q, k, v     [B, H, L, dk]   dtype (p->window, n_meta, alpha are ignored)
+ *   y           [B, H, L, dv]   dtype, out
+ *   lse         [B, H, L]       float32, out, nullable: natural-log normaliser */
+lizard_status_t lizard_softmax_attn_fwd(const lizard_params_t* p,
+                                        const void* q, const void* k, const void* v,
+                                        void* y, float* lse, void* stream);
+
+/* The output-matching loss mean((y - y_teacher)^2) over all B*H*L*dv
+ * elements and its gradient.
+ *   y, y_teacher [B, H, L, dv]  dtype
+ *   dy          [B, H, L, dv]   dtype, out: 2 (y - y_teacher) / N
+ *   loss_bh     [B, H]          float32, out: each head's sum of squared
+ *                               errors / N, summed in a fixed order (the loss
+ *                               is the sum of loss_bh; deterministic) */
+lizard_status_t lizard_transfer_loss(const lizard_params_t* p,
+                                     const void* y, const void* y_teacher,
+                                     void* dy, float* loss_bh, void* stream);
+
 /* Static description of a status code. */
 const char* lizard_status_string(lizard_status_t s);
 
 /* ABI version of this header: 2 (version 1 had none of the *_logit,
- * lizard_attn_fwd_continue and lizard_decode_tokens entry points). */
+ * lizard_attn_fwd_continue, lizard_decode_tokens, lizard_softmax_attn_fwd
+ * and lizard_transfer_loss entry points). */
 int lizard_abi_version(void);
 
 #ifdef __cplusplus

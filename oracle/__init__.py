@@ -31,4 +31,7 @@ from .lizard import (  # noqa: F401
     lizard_bwd_logit,
     lizard_decode_step_logit,
     lizard_fwd_continue,
+    softmax_attention_causal,
+    transfer_loss,
+    stage1_step,
 )

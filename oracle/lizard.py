@@ -354,3 +354,45 @@ def lizard_decode_step_logit(state, k_ring, v_ring, pos: int, q_t, k_t, v_t, gat
     """lizard_decode_step with the token's gate given by its logits."""
     return lizard_decode_step(state, k_ring, v_ring, pos, q_t, k_t, v_t, log_sigmoid(gate_logit_t), meta_k, w, alpha,
                               scale)
+
+
+# ---------------------------------------------------------------------------
+# Stage-1 attention transfer
+# ---------------------------------------------------------------------------
+
+
+def softmax_attention_causal(q, k, v, scale: Optional[float] = None):
+    """The teacher of stage 1: softmax attention over every earlier token
+    (stage 1 fits the layer to the outputs of the attention it replaces; de §2
+    "Trainingsprozess", it §2 "Fase di Addestramento").  Returns (y, lse)."""
+    N, L, dk = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(dk)
+    Z = scale * np.einsum("nti,nsi->nts", q, k)
+    Z = np.where(np.tril(np.ones((L, L), dtype=bool))[None], Z, -np.inf)
+    M = Z.max(axis=2, keepdims=True)
+    E = np.exp(Z - M)
+    den = E.sum(axis=2, keepdims=True)
+    return np.einsum("nts,nsj->ntj", E, v) / den, (M + np.log(den))[:, :, 0]
+
+
+def transfer_loss(y, y_teacher):
+    """mean((y - y_teacher)^2) over all elements, and its gradient
+    2 (y - y_teacher) / N with respect to y."""
+    e = np.asarray(y, dtype=np.float64) - np.asarray(y_teacher, dtype=np.float64)
+    return float((e * e).sum() / e.size), 2.0 * e / e.size
+
+
+def stage1_step(q, k, v, log_g, meta_k, w: int, alpha: float, scale: Optional[float] = None):
+    """One synthetic stage-1 step on the same q, k, v: the teacher's outputs
+    are the fixed target, the layer's outputs are fitted to them.  Returns the
+    loss and the layer's gradients (dq, dk, dv, dlog_g, dmeta; in stage 1 the
+    gates and the sink keys are what trains)."""
+    yt, _ = softmax_attention_causal(q, k, v, scale)
+    y = lizard_fwd(q, k, v, log_g, meta_k, w, alpha, scale)["y"]
+    loss, dy = transfer_loss(y, yt)
+    g = lizard_bwd(q, k, v, log_g, meta_k, w, alpha, dy, scale)
+    g["loss"] = loss
+    g["y_teacher"] = yt
+    g["y"] = y
+    return g

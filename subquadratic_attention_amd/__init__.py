@@ -73,6 +73,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lizard_decode_step_logit.restype = ctypes.c_int
     lib.lizard_attn_fwd_continue.argtypes = [P] + [_vp] * 9 + [ctypes.c_int32] + [_vp] * 5
     lib.lizard_attn_fwd_continue.restype = ctypes.c_int
+    lib.lizard_softmax_attn_fwd.argtypes = [P] + [_vp] * 6
+    lib.lizard_softmax_attn_fwd.restype = ctypes.c_int
+    lib.lizard_transfer_loss.argtypes = [P] + [_vp] * 5
+    lib.lizard_transfer_loss.restype = ctypes.c_int
     for fn in ("lizard_decode_tokens", "lizard_decode_tokens_logit"):
         getattr(lib, fn).argtypes = [P, _vp, ctypes.c_int32] + [_vp] * 10
         getattr(lib, fn).restype = ctypes.c_int
@@ -318,3 +322,39 @@ def lizard_attn_fwd_continue(q, k, v, meta_k, *, log_g=None, gate_logit=None, st
                                       _stream(q.device))
     _check("lizard_attn_fwd_continue", st)
     return o
+
+
+def lizard_softmax_attn_fwd(q, k, v, *, softmax_scale: float = 0.0, need_lse: bool = False,
+                            out: Optional[Dict] = None) -> Dict:
+    """Causal softmax attention over all earlier tokens (the stage-1 teacher).
+    Returns {"y", and optionally "lse"}."""
+    torch = _torch()
+    lib = load_library()
+    B, H, L, d = q.shape
+    p = make_params(B, H, L, d, window=1, n_meta=0, alpha=0.0, dtype=_dtype_code(q), softmax_scale=softmax_scale)
+    o = dict(out) if out is not None else {}
+    if "y" not in o:
+        o["y"] = torch.empty_like(q)
+    if need_lse and "lse" not in o:
+        o["lse"] = torch.empty((B, H, L), device=q.device, dtype=torch.float32)
+    st = lib.lizard_softmax_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o["y"]), _ptr(o.get("lse")),
+                                     _stream(q.device))
+    _check("lizard_softmax_attn_fwd", st)
+    return o
+
+
+def lizard_transfer_loss(y, y_teacher, *, dy=None, loss_bh=None):
+    """mean((y - y_teacher)^2): returns (dy = 2 (y - y_teacher) / N, loss_bh [B, H]
+    float32 whose sum is the loss)."""
+    torch = _torch()
+    lib = load_library()
+    B, H, L, d = y.shape
+    p = make_params(B, H, L, d, window=1, n_meta=0, alpha=0.0, dtype=_dtype_code(y))
+    if dy is None:
+        dy = torch.empty_like(y)
+    if loss_bh is None:
+        loss_bh = torch.empty((B, H), device=y.device, dtype=torch.float32)
+    st = lib.lizard_transfer_loss(ctypes.byref(p), _ptr(y), _ptr(y_teacher), _ptr(dy), _ptr(loss_bh),
+                                  _stream(y.device))
+    _check("lizard_transfer_loss", st)
+    return dy, loss_bh

@@ -261,6 +261,41 @@ LIZARD_API lizard_status_t lizard_decode_tokens_logit(const lizard_params_t* p, 
   return decode_step(p, 0, pos, T, q, k, v, nullptr, gate_logit, true, meta_k, state, k_ring, v_ring, y, stream);
 }
 
+LIZARD_API lizard_status_t lizard_softmax_attn_fwd(const lizard_params_t* p, const void* q, const void* k,
+                                                   const void* v, void* y, float* lse, void* stream) {
+  lizard_status_t s = check_params(p, true);
+  if (s != LIZARD_OK) return s;
+  const int BH = p->B * p->H;
+  if (BH == 0 || p->L == 0) return LIZARD_OK;
+  if (!q || !k || !v || !y) return LIZARD_E_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(y) || misaligned(lse)) return LIZARD_E_ALIGN;
+  lizard::TeacherArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.y = y;
+  a.lse = lse;
+  a.BH = BH;
+  a.L = p->L;
+  a.scale_log2 = scale_of(p) * 1.4426950408889634f;
+  return launched(lizard::launch_teacher(a, p->dtype == LIZARD_BF16, p->dk, static_cast<hipStream_t>(stream)));
+}
+
+LIZARD_API lizard_status_t lizard_transfer_loss(const lizard_params_t* p, const void* y, const void* y_teacher,
+                                                void* dy, float* loss_bh, void* stream) {
+  lizard_status_t s = check_params(p, true);
+  if (s != LIZARD_OK) return s;
+  const int BH = p->B * p->H;
+  if (BH == 0) return LIZARD_OK;
+  if (!loss_bh || (p->L > 0 && (!y || !y_teacher || !dy))) return LIZARD_E_NULL;
+  if (misaligned(y) || misaligned(y_teacher) || misaligned(dy) || misaligned(loss_bh)) return LIZARD_E_ALIGN;
+  const long long per_head = (long long)p->L * p->dv;
+  const double n = (double)BH * (double)per_head;
+  const float inv_n = n > 0 ? (float)(1.0 / n) : 0.f;
+  return launched(lizard::launch_transfer_loss(y, y_teacher, dy, loss_bh, BH, per_head, inv_n,
+                                               p->dtype == LIZARD_BF16, static_cast<hipStream_t>(stream)));
+}
+
 LIZARD_API const char* lizard_status_string(lizard_status_t s) {
   switch (s) {
     case LIZARD_OK: return "ok";

@@ -76,11 +76,25 @@ struct BwdArgs {
   float scale;           // softmax scale (natural units)
 };
 
+// Causal softmax attention over all earlier tokens (the stage-1 teacher).
+struct TeacherArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* y;
+  float* lse;            // nullable [BH, L]
+  int BH, L;
+  float scale_log2;      // softmax scale * log2(e)
+};
+
 // Value-column slice width the forward kernel uses (0 = unsupported).
 int fwd_value_slice(int dtype_bf16, int D);
 hipError_t launch_fwd(const FwdArgs& a, int dtype_bf16, int D, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int dtype_bf16, int D, hipStream_t st);
 size_t bwd_workspace_bytes(int dtype_bf16, int BH, int L, int D, int n_meta);
 hipError_t launch_bwd(const BwdArgs& a, int dtype_bf16, int D, hipStream_t st);
+hipError_t launch_teacher(const TeacherArgs& a, int dtype_bf16, int D, hipStream_t st);
+hipError_t launch_transfer_loss(const void* y, const void* yt, void* dy, float* loss_bh, int BH, long long per_head,
+                                float inv_n, int dtype_bf16, hipStream_t st);
 
 }  // namespace lizard

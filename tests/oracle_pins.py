@@ -427,6 +427,53 @@ def p24_segments_equal_one_pass(O):
         worst = max(worst, _rel(S, whole["state"]))
     return worst
 
+
+# --- stage-1 attention transfer -------------------------------------------------
+
+def p25_teacher_is_sdpa(O):
+    """The causal softmax teacher against torch's scaled_dot_product_attention
+    (is_causal, float64), default and explicit scale, and its lse against a
+    direct logsumexp."""
+    import torch
+
+    q, k, v, _, _ = _rand(25, L=23, d=7)
+    errs = []
+    for sc in (None, 0.3):
+        y, lse = O.softmax_attention_causal(q, k, v, sc)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            *(torch.from_numpy(a) for a in (q, k, v)), is_causal=True, scale=sc).numpy()
+        errs.append(_rel(y, ref))
+        s = (1.0 / math.sqrt(q.shape[2])) if sc is None else sc
+        Z = s * np.einsum("nti,nsi->nts", q, k)
+        lref = np.array([[np.log(np.exp(Z[n, t, :t + 1]).sum()) for t in range(q.shape[1])] for n in range(q.shape[0])])
+        errs.append(_rel(lse, lref))
+    return max(errs)
+
+
+def p26_stage1_finite_differences(O, n_coords=10):
+    """The stage-1 gradients (teacher output held fixed) against central
+    differences of mean((Y - Y_teacher)^2) on log-gates and sink keys."""
+    q, k, v, lg, mu = _rand(26, N=1, L=12, d=4, m=2)
+    w, alpha = 4, 0.5
+    g = O.stage1_step(q, k, v, lg, mu, w, alpha)
+    yt = g["y_teacher"]
+    rng = np.random.default_rng(260)
+    h = 1e-6
+    worst = 0.0
+    for name, arr, grad in (("lg", lg, g["dlog_g"]), ("mu", mu, g["dmeta"])):
+        for _ in range(n_coords):
+            idx = tuple(int(rng.integers(0, s_)) for s_ in arr.shape)
+            vals = []
+            for sign in (1.0, -1.0):
+                a2 = arr.copy()
+                a2[idx] += sign * h
+                lg2, mu2 = (a2, mu) if name == "lg" else (lg, a2)
+                y = O.lizard_fwd(q, k, v, lg2, mu2, w, alpha)["y"]
+                vals.append(float(((y - yt) ** 2).mean()))
+            fd = (vals[0] - vals[1]) / (2 * h)
+            worst = max(worst, abs(fd - grad[idx]) / (1e-3 + abs(fd)))
+    return worst
+
 ALL_PINS = {
     "P1": p1_recurrent_equals_quadratic,
     "P2": p2_unit_gate_is_causal_linear_attention,
@@ -452,9 +499,12 @@ ALL_PINS = {
     "P22": p22_logit_gradients,
     "P23": p23_logit_decode_continues_prefill,
     "P24": p24_segments_equal_one_pass,
+    "P25": p25_teacher_is_sdpa,
+    "P26": p26_stage1_finite_differences,
 }
 
 # finite differences carry O(h^2) truncation and O(eps/h) rounding error
 PIN_TOL = {k: TOL for k in ALL_PINS}
 PIN_TOL["P17"] = 1e-6
+PIN_TOL["P26"] = 1e-5
 PIN_TOL["P12"] = 0.5  # an exact count of mismatches: must be 0

@@ -34,6 +34,7 @@ def test_header_declares_the_entry_points():
     for want in ("lizard_attn_fwd", "lizard_attn_bwd", "lizard_attn_bwd_workspace_size", "lizard_decode_step",
                  "lizard_attn_fwd_logit", "lizard_attn_bwd_logit", "lizard_decode_step_logit",
                  "lizard_decode_tokens", "lizard_decode_tokens_logit", "lizard_attn_fwd_continue",
+                 "lizard_softmax_attn_fwd", "lizard_transfer_loss",
                  "lizard_status_string", "lizard_abi_version"):
         assert want in names
 

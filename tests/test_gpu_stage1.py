@@ -1,0 +1,85 @@
+"""GPU parity of the stage-1 attention-transfer pieces: the causal softmax
+teacher (lizard_softmax_attn_fwd), the output-matching loss
+(lizard_transfer_loss), and one whole synthetic stage-1 step (teacher,
+layer forward, loss, layer backward) against oracle.stage1_step."""
+import numpy as np
+import pytest
+
+import oracle
+import seeded_inputs as si
+from tests.gpu_util import TAU, assert_close, down, flat, log, meta_per_slice, up, up_f32
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("L", [1, 64, 150, 300])
+def test_teacher(gpu_lib, dtype, d, L):
+    import torch
+
+    x = si.custom_inputs(60, 2, 2, L, d, 0, dtype, qk_sd=0.5)
+    log(f"teacher dtype={dtype} d={d} L={L}")
+    q, k, v = up(x["q"], dtype), up(x["k"], dtype), up(x["v"], dtype)
+    out = gpu_lib.lizard_softmax_attn_fwd(q, k, v, need_lse=True)
+    torch.cuda.synchronize()
+    y, lse = oracle.softmax_attention_causal(flat(x["q"]), flat(x["k"]), flat(x["v"]))
+    assert_close(down(out["y"]).reshape(4, L, d), y, dtype, "teacher y")
+    assert_close(down(out["lse"]).reshape(4, L), lse, "f32", "teacher lse", tau=TAU[dtype])
+
+
+def test_teacher_scale(gpu_lib):
+    import torch
+
+    dtype, d, L = "bf16", 128, 130
+    x = si.custom_inputs(61, 1, 3, L, d, 0, dtype, qk_sd=1.0)
+    q, k, v = up(x["q"], dtype), up(x["k"], dtype), up(x["v"], dtype)
+    out = gpu_lib.lizard_softmax_attn_fwd(q, k, v, softmax_scale=0.05)
+    torch.cuda.synchronize()
+    y, _ = oracle.softmax_attention_causal(flat(x["q"]), flat(x["k"]), flat(x["v"]), 0.05)
+    assert_close(down(out["y"]).reshape(3, L, d), y, dtype, "teacher y (scale 0.05)")
+
+
+@pytest.mark.parametrize("dtype,d,L", [("f32", 64, 77), ("bf16", 128, 200), ("bf16", 64, 3)])
+def test_transfer_loss(gpu_lib, dtype, d, L):
+    import torch
+
+    x = si.custom_inputs(62, 2, 3, L, d, 0, dtype, with_dy=True)
+    y, yt = up(x["q"], dtype), up(x["dy"], dtype)
+    dy, loss_bh = gpu_lib.lizard_transfer_loss(y, yt)
+    torch.cuda.synchronize()
+    loss, g = oracle.transfer_loss(x["q"], x["dy"])
+    assert_close(down(dy), g, dtype, "transfer dy")
+    e = x["q"] - x["dy"]
+    ref_bh = (e * e).sum(axis=(2, 3)) / e.size
+    assert_close(down(loss_bh), ref_bh, "f32", "loss per head", tau=1e-5)
+    assert abs(float(loss_bh.sum()) - loss) <= 1e-5 * loss
+
+
+@pytest.mark.parametrize("dtype,d,L", [("f32", 64, 150), ("bf16", 128, 200)])
+def test_stage1_step(gpu_lib, dtype, d, L):
+    """Teacher, layer forward (with lse), loss gradient and layer backward on
+    the GPU against the oracle's stage-1 step."""
+    import torch
+
+    B, H, w = 2, 2, 64
+    x = si.custom_inputs(63, B, H, L, d, 4, dtype, qk_sd=0.5)
+    log(f"stage1 dtype={dtype} d={d} L={L}")
+    q, k, v, meta = up(x["q"], dtype), up(x["k"], dtype), up(x["v"], dtype), up(x["meta_k"], dtype)
+    lg = up_f32(x["log_g"])
+    yt = gpu_lib.lizard_softmax_attn_fwd(q, k, v)["y"]
+    fw = gpu_lib.lizard_attn_fwd(q, k, v, lg, meta, window=w, alpha=0.5, need_lse=True)
+    dy, loss_bh = gpu_lib.lizard_transfer_loss(fw["y"], yt)
+    g = gpu_lib.lizard_attn_bwd(q, k, v, lg, meta, fw["lse"], dy, window=w, alpha=0.5)
+    torch.cuda.synchronize()
+    r = oracle.stage1_step(flat(x["q"]), flat(x["k"]), flat(x["v"]), flat(x["log_g"]),
+                           meta_per_slice(x["meta_k"], B), w, 0.5)
+    tol = TAU[dtype]
+    assert abs(float(loss_bh.sum()) - r["loss"]) <= 2 * tol * r["loss"], (float(loss_bh.sum()), r["loss"])
+    shp = x["q"].shape
+    for kk in ("dq", "dk", "dv"):
+        assert_close(down(g[kk]), r[kk].reshape(shp), dtype, f"stage1 {kk}")
+    scale = max(float(np.abs(r["dlog_g"]).max()), float(np.abs(flat(x["q"]) * r["dq_gate"]).max()))
+    e = float(np.abs(down(g["dlog_g"]) - r["dlog_g"].reshape(shp)).max()) / scale
+    assert e <= tol, f"stage1 dlog_g {e:.3e}"
+    dmeta = r["dmeta"].reshape(B, H, *r["dmeta"].shape[1:]).sum(0)
+    assert_close(down(g["dmeta"]), dmeta, dtype, "stage1 dmeta")

@@ -59,6 +59,10 @@ MUTATIONS = [
      "gate_logit_t, meta_k, w, alpha,"),
     ("continuation drops the incoming state", "o, S = gla_recurrent(q, k, v, log_g, state_in)",
      "o, S = gla_recurrent(q, k, v, log_g)"),
+    ("teacher sees one future key", "Z = np.where(np.tril(np.ones((L, L), dtype=bool))[None], Z, -np.inf)",
+     "Z = np.where(np.tril(np.ones((L, L), dtype=bool), 1)[None], Z, -np.inf)"),
+    ("loss gradient without the factor 2", "return float((e * e).sum() / e.size), 2.0 * e / e.size",
+     "return float((e * e).sum() / e.size), e / e.size"),
     ("continuation ignores the halo", "        ya, lse = ya[:, h:], lse[:, h:]\n",
      "        ya, lse = anchor_window(q, k, v, meta_k, w, scale)\n"),
 ]
