@@ -372,16 +372,19 @@ struct AqLayout {
   static constexpr int LDZS = 32 + PAD;    // per-wave staging of sink dZ [16][LDZS]
   static constexpr int a16(int x) { return (x + 15) / 16 * 16; }
   static constexpr int OFF_KT = 0;
+  static constexpr int OFF_Q = 0;          // after the dq products, the chunk's queries replace the keys
+  static_assert(64 * LDQ <= D * LDKT, "query rows fit in the key tile");
   static constexpr int OFF_MT = OFF_KT + a16(D * LDKT * (int)sizeof(T));
-  static constexpr int OFF_Q = OFF_MT + a16(D * LDMT * (int)sizeof(T));
-  static constexpr int OFF_ST = OFF_Q + a16(64 * LDQ * (int)sizeof(T));
+  static constexpr int OFF_ST = OFF_MT + a16(D * LDMT * (int)sizeof(T));
   static constexpr int OFF_ZS = OFF_ST + a16(4 * 16 * LDS * (int)sizeof(T));
   static constexpr int OFF_DZS = OFF_ZS + a16(4 * 16 * LDZS * (int)sizeof(T));   // fp32 [64][16]
   static constexpr int TOTAL = OFF_DZS + a16(64 * 16 * 4);
 };
 
-template <typename T, int D>
-__global__ __launch_bounds__(256, 1) void bwd_anchor_q_kernel(BwdArgs a) {
+// The grid covers chunks cb .. cb + ncl - 1; GUARD = false: they are interior
+// (the window keys [t0 - 64, t0 + 64) and the queries lie inside [0, L)).
+template <typename T, int D, bool GUARD>
+__global__ __launch_bounds__(256, 2) void bwd_anchor_q_kernel(BwdArgs a, int cb, int ncl) {
   typedef AqLayout<T, D> Lay;
   typedef Mfma<T> M;
   typedef typename M::frag frag;
@@ -397,7 +400,8 @@ __global__ __launch_bounds__(256, 1) void bwd_anchor_q_kernel(BwdArgs a) {
 
   const int L = a.L, nc = (L + C - 1) / C;
   int bh, c;
-  if (!chunk_block(a.BH, nc, bh, c)) return;
+  if (!chunk_block(a.BH, ncl, bh, c)) return;
+  c += cb;
   const int h = bh % a.H;
   const int t0 = c * C;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
@@ -410,36 +414,40 @@ __global__ __launch_bounds__(256, 1) void bwd_anchor_q_kernel(BwdArgs a) {
   const T* mug = reinterpret_cast<const T*>(a.meta) + (size_t)h * a.n_meta * D;
   const float sl2 = a.scale * kLog2e;
 
-  // window keys [t0 - 64, t0 + 64) transposed; sink keys transposed; this chunk's queries
+  const int I = w;
+  const int tme = t0 + 16 * I + m;
+  const int U0 = 16 * I < 32 ? 16 * I : 32;
+  // this lane's query and dY row, and the window keys / values of its tiles,
+  // issued before the staging (their loads then overlap it)
+  uint4 qraw[QV], dyraw[QV];
+  load_quarter<T, D, GUARD>(qraw, qg, tme, L, g);
+  load_quarter<T, D, GUARD>(dyraw, dyg, tme, L, g);
+  uint4 kraw[6][QV], vraw[6][QV];
+#pragma unroll
+  for (int kt = 0; kt < 6; ++kt) {
+    const int s = t0 - 64 + U0 + 16 * kt + m;   // key row of this lane (MFMA row)
+    load_quarter<T, D, GUARD>(kraw[kt], kg, s, L, g);
+    load_quarter<T, D, GUARD>(vraw[kt], vg, s, L, g);
+  }
+  const float lse2 = !GUARD || tme < L ? a.lse[(size_t)bh * L + (tme < L ? tme : 0)] * kLog2e : 0.f;
+
+  // window keys [t0 - 64, t0 + 64) transposed; sink keys transposed
   stage_T<T, D, D, 128>(sKT, Lay::LDKT, kg, t0 - 64, 0, L, 1.0f);
   for (int i = tid; i < D * 32; i += 256) {
     const int d = i / 32, s = i % 32;
     sMuT[d * Lay::LDMT + s] = s < a.n_meta ? mug[(size_t)(s < a.n_meta ? s : 0) * D + d] : from_f32<T>(0.f);
   }
-  stage_rows<T, D, 64>(sQ, Lay::LDQ, qg, t0, L);
   __syncthreads();
-
-  const int I = w;
-  const int tme = t0 + 16 * I + m;
-  const int U0 = 16 * I < 32 ? 16 * I : 32;
-  uint4 qraw[QV], dyraw[QV];
-  load_quarter<T, D>(qraw, qg, tme, L, g);
-  load_quarter<T, D>(dyraw, dyg, tme, L, g);
-  const float lse2 = tme < L ? a.lse[(size_t)bh * L + tme] * kLog2e : 0.f;
 
   // logits Z^T[u][t] and value products dP^T[u][t] for window keys u
   f32x4 z[6], dp[6];
 #pragma unroll
   for (int kt = 0; kt < 6; ++kt) {
-    const int s = t0 - 64 + U0 + 16 * kt + m;   // key row of this lane (MFMA row)
-    uint4 kraw[QV], vraw[QV];
-    load_quarter<T, D>(kraw, kg, s, L, g);
-    load_quarter<T, D>(vraw, vg, s, L, g);
     f32x4 zc = zero4(), pc = zero4();
 #pragma unroll
     for (int e = 0; e < NF; ++e) {
-      zc = M::mma(frag_of<T>(kraw, e), frag_of<T>(qraw, e), zc);
-      pc = M::mma(frag_of<T>(vraw, e), frag_of<T>(dyraw, e), pc);
+      zc = M::mma(frag_of<T>(kraw[kt], e), frag_of<T>(qraw, e), zc);
+      pc = M::mma(frag_of<T>(vraw[kt], e), frag_of<T>(dyraw, e), pc);
     }
     z[kt] = zc;
     dp[kt] = pc;
@@ -506,9 +514,11 @@ __global__ __launch_bounds__(256, 1) void bwd_anchor_q_kernel(BwdArgs a) {
       store_pack<T, 4>(dqa + (size_t)tme * D + 16 * dt + 4 * g, v4);
     }
   }
-  __syncthreads();
   // per-chunk sink-key gradient: dmu[i][d] = scale sum_t dZs[t][i] q[t][d]
   if (a.n_meta > 0) {
+    __syncthreads();                      // the key tile is free: the chunk's queries go there
+    stage_rows<T, D, 64>(sQ, Lay::LDQ, qg, t0, L);
+    __syncthreads();
     float* part = a.ws_dmu + ((size_t)bh * nc + c) * a.n_meta * D;
     for (int o = tid; o < a.n_meta * D; o += 256) {
       const int i = o / D, d = o % D;
@@ -535,8 +545,10 @@ struct AkLayout {
   static constexpr int TOTAL = OFF_RW + a16(2 * 128 * 4);
 };
 
-template <typename T, int D>
-__global__ __launch_bounds__(256, 1) void bwd_anchor_k_kernel(BwdArgs a) {
+// The grid covers chunks cb .. cb + ncl - 1; GUARD = false: they are interior
+// (the queries [t0, t0 + 128) lie inside [0, L)).
+template <typename T, int D, bool GUARD>
+__global__ __launch_bounds__(256, 1) void bwd_anchor_k_kernel(BwdArgs a, int cb, int ncl) {
   typedef AkLayout<T, D> Lay;
   typedef Mfma<T> M;
   constexpr int EPV = 16 / sizeof(T);
@@ -549,9 +561,10 @@ __global__ __launch_bounds__(256, 1) void bwd_anchor_k_kernel(BwdArgs a) {
   float* sLse = reinterpret_cast<float*>(smem + Lay::OFF_RW);
   float* sD = sLse + 128;
 
-  const int L = a.L, nc = (L + C - 1) / C;
+  const int L = a.L;
   int bh, c;
-  if (!chunk_block(a.BH, nc, bh, c)) return;
+  if (!chunk_block(a.BH, ncl, bh, c)) return;
+  c += cb;
   const int t0 = c * C;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
   T* sZ = reinterpret_cast<T*>(smem + Lay::OFF_ST) + w * 16 * Lay::LDS;
@@ -561,6 +574,14 @@ __global__ __launch_bounds__(256, 1) void bwd_anchor_k_kernel(BwdArgs a) {
   const T* vg = reinterpret_cast<const T*>(a.v) + (size_t)bh * L * D;
   const T* dyg = reinterpret_cast<const T*>(a.dy) + (size_t)bh * L * D;
   const float sl2 = a.scale * kLog2e;
+
+  const int J = w;                        // key block
+  const int sme = t0 + 16 * J + m;        // this lane's key
+  const int Q0 = 16 * J < 32 ? 16 * J : 32;   // first staged query (relative to t0)
+  // this lane's key and value rows, issued before the staging
+  uint4 kraw[QV], vraw[QV];
+  load_quarter<T, D, GUARD>(kraw, kg, sme, L, g);
+  load_quarter<T, D, GUARD>(vraw, vg, sme, L, g);
 
   // queries [t0, t0 + 128): transposed q and dY, lse (log2 units) and D_t
   stage_T<T, D, D, 128>(sQT, Lay::LDT, qg, t0, 0, L, 1.0f);
@@ -572,20 +593,14 @@ __global__ __launch_bounds__(256, 1) void bwd_anchor_k_kernel(BwdArgs a) {
   }
   __syncthreads();
 
-  const int J = w;                        // key block
-  const int sme = t0 + 16 * J + m;        // this lane's key
-  const int Q0 = 16 * J < 32 ? 16 * J : 32;   // first staged query (relative to t0)
-  uint4 kraw[QV], vraw[QV];
-  load_quarter<T, D>(kraw, kg, sme, L, g);
-  load_quarter<T, D>(vraw, vg, sme, L, g);
   // Z[t][s] and dP[t][s] tiles: queries t on the MFMA rows
   f32x4 z[6], dp[6];
 #pragma unroll
   for (int kt = 0; kt < 6; ++kt) {
     const int t = t0 + Q0 + 16 * kt + m;
     uint4 qraw[QV], dyraw[QV];
-    load_quarter<T, D>(qraw, qg, t, L, g);
-    load_quarter<T, D>(dyraw, dyg, t, L, g);
+    load_quarter<T, D, GUARD>(qraw, qg, t, L, g);
+    load_quarter<T, D, GUARD>(dyraw, dyg, t, L, g);
     f32x4 zc = zero4(), pc = zero4();
 #pragma unroll
     for (int e = 0; e < NF; ++e) {
@@ -1207,20 +1222,32 @@ hipError_t launch_bwd_t(BwdArgs a, hipStream_t st) {
     else
       hipLaunchKernelGGL((bwd_dstate_kernel<T, D, DV, false>), dim3(8 * groups * (D / DV)), dim3(256), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // 3. anchor, query side
+    const int nfull = L / C;
+    // 3. anchor, query side: chunk 0 and a ragged last chunk range-checked, the rest not
     typedef AqLayout<T, D> AQ;
-    static_assert(AQ::TOTAL <= 160 * 1024, "LDS");
-    if ((e = set_lds(&bwd_anchor_q_kernel<T, D>, AQ::TOTAL)) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_anchor_q_kernel<T, D>), dim3(8 * groups * nc), dim3(256), AQ::TOTAL, st, a);
+    static_assert(AQ::TOTAL <= 80 * 1024, "LDS: two workgroups per CU");
+    if ((e = set_lds(&bwd_anchor_q_kernel<T, D, true>, AQ::TOTAL)) != hipSuccess) return e;
+    if ((e = set_lds(&bwd_anchor_q_kernel<T, D, false>, AQ::TOTAL)) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_anchor_q_kernel<T, D, true>), dim3(8 * groups), dim3(256), AQ::TOTAL, st, a, 0, 1);
+    if (nfull > 1)
+      hipLaunchKernelGGL((bwd_anchor_q_kernel<T, D, false>), dim3(8 * groups * (nfull - 1)), dim3(256), AQ::TOTAL, st,
+                         a, 1, nfull - 1);
+    if (nfull >= 1 && nfull < nc)
+      hipLaunchKernelGGL((bwd_anchor_q_kernel<T, D, true>), dim3(8 * groups), dim3(256), AQ::TOTAL, st, a, nfull, 1);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // 4. anchor, key side
+    // 4. anchor, key side: chunks whose query range [t0, t0 + 128) ends past L range-checked
     typedef AkLayout<T, D> AK;
     static_assert(AK::TOTAL <= 160 * 1024, "LDS");
-    if ((e = set_lds(&bwd_anchor_k_kernel<T, D>, AK::TOTAL)) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_anchor_k_kernel<T, D>), dim3(8 * groups * nc), dim3(256), AK::TOTAL, st, a);
+    if ((e = set_lds(&bwd_anchor_k_kernel<T, D, true>, AK::TOTAL)) != hipSuccess) return e;
+    if ((e = set_lds(&bwd_anchor_k_kernel<T, D, false>, AK::TOTAL)) != hipSuccess) return e;
+    const int nk_in = nfull > 1 ? nfull - 1 : 0;   // chunks c with t0 + 128 <= L
+    if (nk_in > 0)
+      hipLaunchKernelGGL((bwd_anchor_k_kernel<T, D, false>), dim3(8 * groups * nk_in), dim3(256), AK::TOTAL, st, a, 0,
+                         nk_in);
+    hipLaunchKernelGGL((bwd_anchor_k_kernel<T, D, true>), dim3(8 * groups * (nc - nk_in)), dim3(256), AK::TOTAL, st, a,
+                       nk_in, nc - nk_in);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // 5. gated branch and outputs
-    const int nfull = L / C;
     if (a.gate_logit) {
       if ((e = launch_gate<T, D, true>(a, nfull, nc, groups, st)) != hipSuccess) return e;
     } else {
