@@ -94,40 +94,70 @@ __global__ __launch_bounds__(256) void teacher_attn_kernel(TeacherArgs a) {
   for (int jt = 0; jt < NJT; ++jt) oacc[jt] = zero4();
   float mrun = -INFINITY, lrun = 0.f;     // running max (log2 units, scaled) and sum for query tq
 
+  // one key block's keys (16-byte vectors, row-major) and values (32-bit
+  // words of VC columns, RPT consecutive keys per thread), loaded a block ahead
+  constexpr int KVEC = 64 * (D / EPV) / 256;  // key vectors per thread
+  constexpr int VC = 4 / sizeof(T);
+  constexpr int VRW = D / VC;                 // threads across a value row
+  constexpr int RPT = 64 * VRW / 256;         // keys per thread in the value load
+  static_assert(KVEC * 256 == 64 * (D / EPV) && RPT % 8 == 0, "teacher staging shape");
+  uint4 kreg[KVEC];
+  uint32_t vreg[RPT];
+  auto load_rows = [&](int kb, bool full) __attribute__((always_inline)) {
+    const int k0 = kb * 64;
+#pragma unroll
+    for (int u = 0; u < KVEC; ++u) {
+      const int i = tid + 256 * u;
+      const int row = i / (D / EPV), cv = i % (D / EPV);
+      const bool ok = full || k0 + row < L;
+      const uint4 r = ld16(kg + (size_t)(ok ? k0 + row : 0) * D + cv * EPV);
+      kreg[u] = ok ? r : make_uint4(0, 0, 0, 0);
+    }
+    const int vj = tid % VRW, vs = tid / VRW;
+#pragma unroll
+    for (int rr = 0; rr < RPT; ++rr) {
+      const int row = k0 + RPT * vs + rr;
+      const bool ok = full || row < L;
+      const uint32_t r = *reinterpret_cast<const uint32_t*>(vg + (size_t)(ok ? row : 0) * D + VC * vj);
+      vreg[rr] = ok ? r : 0u;
+    }
+  };
+  // a uniform branch: full blocks load without row guards (selects on the
+  // loaded data would make the compiler wait for the loads right away)
+  auto load_block = [&](int kb) __attribute__((always_inline)) {
+    if ((kb + 1) * 64 <= L) load_rows(kb, true);
+    else load_rows(kb, false);
+  };
+  load_block(0);
+
   for (int kb = 0; kb <= qb; ++kb) {
     const int k0 = kb * 64;
-    // ---- stage the key block row-major and its values transposed ----
-    for (int i = tid; i < 64 * (D / EPV); i += 256) {
+    // ---- the block into LDS: keys row-major, values transposed (8-key runs) ----
+#pragma unroll
+    for (int u = 0; u < KVEC; ++u) {
+      const int i = tid + 256 * u;
       const int row = i / (D / EPV), cv = i % (D / EPV);
-      const bool ok = k0 + row < L;
-      const uint4 u = ld16(kg + (size_t)(ok ? k0 + row : 0) * D + cv * EPV);
-      *reinterpret_cast<uint4*>(sK + row * Lay::LDK + cv * EPV) = ok ? u : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(sK + row * Lay::LDK + cv * EPV) = kreg[u];
     }
     {
-      // thread: value columns j = VC*vj .. (32-bit words), 4 consecutive keys
-      constexpr int VC = 4 / sizeof(T);
-      constexpr int VRW = D / VC;           // threads across a value row
-      constexpr int RPT = 64 * VRW / 256;   // keys per thread
       const int vj = tid % VRW, vs = tid / VRW;
-      uint32_t wv[RPT];
-#pragma unroll
-      for (int rr = 0; rr < RPT; ++rr) {
-        const int row = k0 + RPT * vs + rr;
-        const bool ok = row < L;
-        const uint32_t u = *reinterpret_cast<const uint32_t*>(vg + (size_t)(ok ? row : 0) * D + VC * vj);
-        wv[rr] = ok ? u : 0u;
-      }
 #pragma unroll
       for (int cc = 0; cc < VC; ++cc)
 #pragma unroll
-        for (int rr = 0; rr < RPT; ++rr) {
-          float f;
-          if constexpr (sizeof(T) == 2) f = __builtin_bit_cast(float, cc == 0 ? (wv[rr] << 16) : (wv[rr] & 0xffff0000u));
-          else f = __builtin_bit_cast(float, wv[rr]);
-          sVt[(VC * vj + cc) * Lay::LDV + RPT * vs + rr] = from_f32<T>(f);
+        for (int b8 = 0; b8 < RPT / 8; ++b8) {
+          float v8[8];
+#pragma unroll
+          for (int rr = 0; rr < 8; ++rr) {
+            const uint32_t wv = vreg[8 * b8 + rr];
+            if constexpr (sizeof(T) == 2) v8[rr] = __builtin_bit_cast(float, cc == 0 ? (wv << 16) : (wv & 0xffff0000u));
+            else v8[rr] = __builtin_bit_cast(float, wv);
+          }
+          store_pack<T, 8>(sVt + (VC * vj + cc) * Lay::LDV + RPT * vs + 8 * b8, v8);
         }
     }
     __syncthreads();
+    // the next block's loads fly while this one is multiplied
+    if (kb < qb) load_block(kb + 1);
 
     // ---- S^T tiles: keys 16kt + 4g + r (rows) x query tq (column m) ----
     f32x4 z[4];
@@ -138,27 +168,34 @@ __global__ __launch_bounds__(256) void teacher_attn_kernel(TeacherArgs a) {
 #pragma unroll
       for (int e = 0; e < NF; ++e) z[kt] = M::mma(M::load(kp + e * M::KPL), qf[e], z[kt]);
     }
-    // causal mask on the diagonal block, and keys past L
-    float mx = mrun;
+    // causal mask, only on the diagonal block (keys past L lie only there:
+    // every earlier block is full); maxima on raw logits (the scale is
+    // positive), the scale folded into the exponent
+    if (kb == qb) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int s = k0 + 16 * kt + 4 * g + r;
+          z[kt][r] = s <= tq && s < L ? z[kt][r] : -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int s = k0 + 16 * kt + 4 * g + r;
-        const bool ok = s <= tq && s < L;
-        z[kt][r] = ok ? z[kt][r] * a.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, z[kt][r]);
-      }
-    mx = xgroup_max(mx);                  // finite: key tq (or key 0) is always valid in the first block
-    const float corr = exp_2(mrun - mx);  // 0 on the first block (mrun = -inf)
-    mrun = mx;
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, z[kt][r]);
+    // finite: key tq (or key 0) is always valid in the first block
+    const float mnew = fmaxf(mrun, xgroup_max(mx) * a.scale_log2);
+    const float corr = exp_2(mrun - mnew);  // 0 on the first block (mrun = -inf)
+    mrun = mnew;
     float ls = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       float p[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p[r] = exp_2(z[kt][r] - mx);
+        p[r] = exp_2(fmaf(z[kt][r], a.scale_log2, -mnew));
         ls += p[r];
       }
       store_pack<T, 4>(sPw + m * Lay::LDP + 16 * kt + 4 * g, p);
