@@ -667,9 +667,13 @@ struct GateLayout {
   static constexpr int OFF_DA = OFF_OT + a16(D * LDT * (int)sizeof(T));
   static constexpr int OFF_DAT = OFF_DA + a16(64 * LDT * (int)sizeof(T));
   static constexpr int OFF_AT = OFF_DAT + a16(64 * LDT * (int)sizeof(T));
-  static constexpr int OFF_TOT = OFF_AT + a16(64 * LDT * (int)sizeof(T));
+  static constexpr int LDR = D + PAD;      // [64][LDR] row-major token tiles
+  static constexpr int OFF_KH = OFF_AT + a16(64 * LDT * (int)sizeof(T));
+  static constexpr int OFF_QE = OFF_KH + a16(64 * LDR * (int)sizeof(T));
+  static constexpr int OFF_TOT = OFF_QE + a16(64 * LDR * (int)sizeof(T));
   static constexpr int OFF_BX = OFF_TOT + a16(NW * D * 4);
-  static constexpr int TOTAL = OFF_BX + a16(D * 4);
+  static constexpr int OFF_EB = OFF_BX + a16(D * 4);       // 2^B and 2^-B per dim
+  static constexpr int TOTAL = OFF_EB + a16(2 * D * 4);
 };
 
 // One workgroup of D/16 wavefronts per (b*h, chunk).  Phase A: log-gate
@@ -701,8 +705,11 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
   T* sDA = reinterpret_cast<T*>(smem + Lay::OFF_DA);    // dA[t][s]
   T* sDAT = reinterpret_cast<T*>(smem + Lay::OFF_DAT);  // dA^T[s][t]
   T* sAT = reinterpret_cast<T*>(smem + Lay::OFF_AT);    // A^T[s][t]
+  T* sKh = reinterpret_cast<T*>(smem + Lay::OFF_KH);    // Kh[s][i] = k 2^{B - beta}, row-major
+  T* sQe = reinterpret_cast<T*>(smem + Lay::OFF_QE);    // Qe[t][i] = q 2^{beta}, row-major
   float* sTot = reinterpret_cast<float*>(smem + Lay::OFF_TOT);
   float* sBx = reinterpret_cast<float*>(smem + Lay::OFF_BX);   // chunk total B (log2) per dim
+  float* sEB = reinterpret_cast<float*>(smem + Lay::OFF_EB);   // [0][i] = 2^B_i, [1][i] = 2^-B_i (fast path)
 
   const int L = a.L, nc = (L + C - 1) / C;
   int bh, c;
@@ -773,19 +780,11 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
   } else {
     I = w;
   }
-  uint4 dyI[QV], vI[QV], kI[QV];
+  uint4 dyI[QV], vI[QV];
   load_quarter<T, D, RG>(dyI, dyg, t0 + 16 * I + m, L, g);
   load_quarter<T, D, RG>(vI, vg, t0 + 16 * I + m, L, g);
-  load_quarter<T, D, RG>(kI, kg, t0 + 16 * I + m, L, g);
-  // phase C's state rows (issued after the earlier phases' loads: the load
-  // counter is waited on in issue order)
-  uint4 Sr[QV], Gr[QV], GTr[QV], Sn[QV];
-  load_quarter<T, D, false>(Sr, Sg, ib + m, D, g);      // S_c rows i (k = j)
-  load_quarter<T, D, false>(Gr, Gg, ib + m, D, g);      // G_{c+1} rows i (k = j)
-  load_quarter<T, D, false>(GTr, GTg, ib + m, D, g);    // G_{c+1}^T rows j (k = i)
-  // S_{c+1} rows i (zero after the last chunk)
-  load_quarter<T, D, false>(Sn, c + 1 < nc ? Sg + (size_t)D * D : Sg, ib + m, D, g);
   const bool has_next = c + 1 < nc;
+  uint4 Sr[QV], Gr[QV], GTr[QV], Sn[QV];
 
   // prefix: inside the wavefront's rows, then across wavefronts
   float beta[RPW][DPL], off[DPL], Bt[DPL];
@@ -816,21 +815,59 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
 #pragma unroll
   for (int dd = 0; dd < DPL; ++dd) wide |= -Bt[dd] > kMaxSpan;
   const bool pairwise = __any(wide);
+  float kh[RPW][DPL], qer[RPW][DPL];
 #pragma unroll
   for (int dd = 0; dd < DPL; ++dd) {
     const int i = DPL * l + dd;
     float qe[RPW], kp[RPW];
+    if (!pairwise) {
+      // every factor from one exponential per element and operand (Kh = Kp 2^B)
+      const float eB = exp_2(Bt[dd]);
 #pragma unroll
-    for (int rr = 0; rr < RPW; ++rr) {
-      const float b = beta[rr][dd] + off[dd];
-      const float qv = elem32<T>(qw[rr], dd), kv = elem32<T>(kw[rr], dd);
-      qe[rr] = pairwise ? qv : qv * exp_2(b);
-      kp[rr] = pairwise ? kv : kv * exp_2(-b);
-      sBeta[(RPW * w + rr) * Lay::LDB + i] = b;
+      for (int rr = 0; rr < RPW; ++rr) {
+        const float b = beta[rr][dd] + off[dd];
+        qe[rr] = elem32<T>(qw[rr], dd) * exp_2(b);
+        kp[rr] = elem32<T>(kw[rr], dd) * exp_2(-b);
+        kh[rr][dd] = kp[rr] * eB;
+        qer[rr][dd] = qe[rr];
+        sBeta[(RPW * w + rr) * Lay::LDB + i] = b;
+      }
+      if (w == 0) {
+        sEB[i] = eB;
+        sEB[D + i] = exp_2(-Bt[dd]);
+      }
+    } else {
+      // wide span: raw q, k for the pairwise terms (2^-beta may overflow)
+#pragma unroll
+      for (int rr = 0; rr < RPW; ++rr) {
+        const float b = beta[rr][dd] + off[dd];
+        const float kv = elem32<T>(kw[rr], dd);
+        qe[rr] = elem32<T>(qw[rr], dd);
+        kp[rr] = kv;
+        kh[rr][dd] = kv * exp_2(Bt[dd] - b);
+        qer[rr][dd] = qe[rr];
+        sBeta[(RPW * w + rr) * Lay::LDB + i] = b;
+      }
     }
     store_pack<T, RPW>(sQT + i * Lay::LDT + RPW * w, qe);
     store_pack<T, RPW>(sKT + i * Lay::LDT + RPW * w, kp);
     if (w == 0) sBx[i] = Bt[dd];
+  }
+  // Kh rows (phase C) and Qe rows (phase B), once for all wavefronts
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr) {
+    T* kr = sKh + (RPW * w + rr) * Lay::LDR + DPL * l;
+    T* qr = sQe + (RPW * w + rr) * Lay::LDR + DPL * l;
+    if constexpr (DPL == 2 && sizeof(T) == 2) {
+      *reinterpret_cast<bf16x2*>(kr) = bf16x2{static_cast<bf16>(kh[rr][0]), static_cast<bf16>(kh[rr][1])};
+      *reinterpret_cast<bf16x2*>(qr) = bf16x2{static_cast<bf16>(qer[rr][0]), static_cast<bf16>(qer[rr][1])};
+    } else {
+#pragma unroll
+      for (int dd = 0; dd < DPL; ++dd) {
+        kr[dd] = from_f32<T>(kh[rr][dd]);
+        qr[dd] = from_f32<T>(qer[rr][dd]);
+      }
+    }
   }
   stage_T_store<T, D, 64, NT>(sOT, Lay::LDT, dyw, 1.0f);
   __syncthreads();
@@ -839,7 +876,7 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
   // backwards): its rows and, for the epilogue, the anchor parts already in
   // dq, dk, dv and q, k of the lane's 4 dims; issued during phase B
   constexpr int NEP = LOGIT ? 6 : 5;
-  uint4 rows[2][3][QV];   // [buffer][dO, v, k][k-quarter]
+  uint4 rows[2][2][QV];   // [buffer][dO, v][k-quarter]
   float ep[2][NEP][4];    // [buffer][dq, dk, dv, q, k (, gate logit)][dim]
   auto load_ep = [&](int tt, float (&dst)[NEP][4]) __attribute__((always_inline)) {
     const int trow = t0 + 16 * tt + m;
@@ -856,12 +893,11 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
   // against JPW blocks J ----
   {
     // rows of the blocks J (two at a time)
-    uint4 rowsJ[2][3][QV];
-    auto load_J = [&](int J, uint4 (&dst)[3][QV]) __attribute__((always_inline)) {
+    uint4 rowsJ[2][2][QV];
+    auto load_J = [&](int J, uint4 (&dst)[2][QV]) __attribute__((always_inline)) {
       const int rJ = t0 + 16 * J + m;
       load_quarter<T, D, RG>(dst[0], vg, rJ, L, g);
       load_quarter<T, D, RG>(dst[1], dyg, rJ, L, g);
-      load_quarter<T, D, RG>(dst[2], qg, rJ, L, g);
     };
     // the blocks J of this wavefront: all four (four wavefronts), or two
     auto J_of = [&](int jj) __attribute__((always_inline)) -> int {
@@ -875,18 +911,25 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
     };
     load_J(J_of(0), rowsJ[0]);
     load_J(J_of(1), rowsJ[1]);
-    // Kp of this lane's key row as fragments (unused on the pairwise path)
+    // phase C's state rows, after phase B's rows (the load counter is waited
+    // on in issue order); they arrive while phase B computes
+    load_quarter<T, D, false>(Sr, Sg, ib + m, D, g);      // S_c rows i (k = j)
+    load_quarter<T, D, false>(Gr, Gg, ib + m, D, g);      // G_{c+1} rows i (k = j)
+    load_quarter<T, D, false>(GTr, GTg, ib + m, D, g);    // G_{c+1}^T rows j (k = i)
+    // S_{c+1} rows i (zero after the last chunk)
+    load_quarter<T, D, false>(Sn, c + 1 < nc ? Sg + (size_t)D * D : Sg, ib + m, D, g);
+    // Kp = Kh 2^-B of this lane's key row as fragments (unused on the pairwise path)
     frag kpf[NF];
     if (!pairwise) {
-      const float* bp = sBeta + (16 * I + m) * Lay::LDB + g * (D / 4);
+      const T* hp = sKh + (16 * I + m) * Lay::LDR + g * (D / 4);
+      const float* enb = sEB + D + g * (D / 4);
 #pragma unroll
       for (int e = 0; e < NF; ++e) {
-        float tk[M::KPL];
+        float hv[M::KPL], tk[M::KPL];
+        if constexpr (sizeof(T) == 2) unpack16<T>(*reinterpret_cast<const uint4*>(hp + e * M::KPL), hv);
+        else hv[0] = hp[e];
 #pragma unroll
-        for (int u = 0; u < M::KPL; ++u) {
-          const int kk = e * M::KPL + u;
-          tk[u] = elem_of<T>(kI, kk) * exp_2(-bp[kk]);
-        }
+        for (int u = 0; u < M::KPL; ++u) tk[u] = hv[u] * enb[e * M::KPL + u];
         kpf[e] = M::pack(tk);
       }
     } else {
@@ -901,7 +944,6 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
       // (c) A tile: queries t in block J (rows), keys s in block I (cols) -> sAT[s][t]
       const uint4* vJ = rowsJ[jj & 1][0];
       const uint4* dyJ = rowsJ[jj & 1][1];
-      const uint4* qJ = rowsJ[jj & 1][2];
       f32x4 ta = zero4(), tb = zero4(), tc = zero4();
       if (J <= I) {
 #pragma unroll
@@ -911,14 +953,9 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
 #pragma unroll
         for (int e = 0; e < NF; ++e) tb = M::mma(frag_of<T>(dyJ, e), frag_of<T>(vI, e), tb);
         if (!pairwise) {
-          const float* bp = sBeta + (16 * J + m) * Lay::LDB + g * (D / 4);
+          const T* qp = sQe + (16 * J + m) * Lay::LDR + g * (D / 4);    // Qe rows t (k = i)
 #pragma unroll
-          for (int e = 0; e < NF; ++e) {
-            float tq[M::KPL];
-#pragma unroll
-            for (int u = 0; u < M::KPL; ++u) tq[u] = elem_of<T>(qJ, e * M::KPL + u) * exp_2(bp[e * M::KPL + u]);
-            tc = M::mma(M::pack(tq), kpf[e], tc);
-          }
+          for (int e = 0; e < NF; ++e) tc = M::mma(M::load(qp + e * M::KPL), kpf[e], tc);
         } else {
           // A[t][s] = sum_i q_ti k_si 2^{beta_ti - beta_si} pairwise
 #pragma unroll
@@ -953,7 +990,6 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
         // rowsJ[jj & 1] is free from here on
         load_quarter<T, D, RG>(rows[1][0], dyg, t0 + 48 + m, L, g);
         load_quarter<T, D, RG>(rows[1][1], vg, t0 + 48 + m, L, g);
-        load_quarter<T, D, RG>(rows[1][2], kg, t0 + 48 + m, L, g);
         load_ep(3, ep[1]);
       }
     }
@@ -991,26 +1027,16 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
     if (tt > 0) {
       load_quarter<T, D, RG>(rows[cur ^ 1][0], dyg, trow - 16, L, g);
       load_quarter<T, D, RG>(rows[cur ^ 1][1], vg, trow - 16, L, g);
-      load_quarter<T, D, RG>(rows[cur ^ 1][2], kg, trow - 16, L, g);
       load_ep(tt - 1, ep[cur ^ 1]);
     }
     const uint4* dyr = rows[cur][0];
     const uint4* vr = rows[cur][1];
-    const uint4* kr = rows[cur][2];
     // Kh_s = k_s * 2^{B - beta_s} as fragments (rows s, k = i)
     frag khf[NF];
     {
-      const float* bp = sBeta + (16 * tt + m) * Lay::LDB + g * (D / 4);
+      const T* kp = sKh + (16 * tt + m) * Lay::LDR + g * (D / 4);
 #pragma unroll
-      for (int e = 0; e < NF; ++e) {
-        float tk[M::KPL];
-#pragma unroll
-        for (int u = 0; u < M::KPL; ++u) {
-          const int kk = e * M::KPL + u;
-          tk[u] = elem_of<T>(kr, kk) * exp_2(sBx[g * (D / 4) + kk] - bp[kk]);
-        }
-        khf[e] = M::pack(tk);
-      }
+      for (int e = 0; e < NF; ++e) khf[e] = M::load(kp + e * M::KPL);
     }
     // inter-chunk parts
     f32x4 qi = zero4(), ki = zero4(), vi = zero4();
@@ -1056,12 +1082,15 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
           qin += to_f32(sDA[tl * Lay::LDT + s]) * to_f32(sKT[i * Lay::LDT + s]) * exp_2(b - sBeta[s * Lay::LDB + i]);
         for (int u = tl; u < 64; ++u)
           kin += to_f32(sDAT[tl * Lay::LDT + u]) * to_f32(sQT[i * Lay::LDT + u]) * exp_2(sBeta[u * Lay::LDB + i] - b);
+        qin = exp_2(b) * qi[r] + qin;
+        kin = exp_2(sBx[i] - b) * ki[r] + kin;
       } else {
-        qin *= exp_2(b);
-        kin *= exp_2(-b);
+        const float ep = exp_2(b), en = exp_2(-b);
+        qin = ep * (qi[r] + qin);
+        kin = en * (sEB[i] * ki[r] + kin);
       }
-      const float dqg = exp_2(b) * qi[r] + qin;
-      const float dkg = exp_2(sBx[i] - b) * ki[r] + kin;
+      const float dqg = qin;
+      const float dkg = kin;
       dbv[r] = live ? q4[r] * dqg - k4[r] * dkg : 0.f;
       dqv[r] = dqg + aq[r];
       dkv[r] = dkg + ak[r];
