@@ -593,19 +593,24 @@ __global__ __launch_bounds__(256, 1) void bwd_anchor_k_kernel(BwdArgs a, int cb,
   }
   __syncthreads();
 
-  // Z[t][s] and dP[t][s] tiles: queries t on the MFMA rows
+  // Z[t][s] and dP[t][s] tiles: queries t on the MFMA rows; each tile's
+  // query and dY rows are loaded one tile ahead
   f32x4 z[6], dp[6];
+  uint4 qraw[2][QV], dyraw[2][QV];
+  load_quarter<T, D, GUARD>(qraw[0], qg, t0 + Q0 + m, L, g);
+  load_quarter<T, D, GUARD>(dyraw[0], dyg, t0 + Q0 + m, L, g);
 #pragma unroll
   for (int kt = 0; kt < 6; ++kt) {
-    const int t = t0 + Q0 + 16 * kt + m;
-    uint4 qraw[QV], dyraw[QV];
-    load_quarter<T, D, GUARD>(qraw, qg, t, L, g);
-    load_quarter<T, D, GUARD>(dyraw, dyg, t, L, g);
+    if (kt + 1 < 6) {
+      const int tn = t0 + Q0 + 16 * (kt + 1) + m;
+      load_quarter<T, D, GUARD>(qraw[(kt + 1) & 1], qg, tn, L, g);
+      load_quarter<T, D, GUARD>(dyraw[(kt + 1) & 1], dyg, tn, L, g);
+    }
     f32x4 zc = zero4(), pc = zero4();
 #pragma unroll
     for (int e = 0; e < NF; ++e) {
-      zc = M::mma(frag_of<T>(qraw, e), frag_of<T>(kraw, e), zc);
-      pc = M::mma(frag_of<T>(dyraw, e), frag_of<T>(vraw, e), pc);
+      zc = M::mma(frag_of<T>(qraw[kt & 1], e), frag_of<T>(kraw, e), zc);
+      pc = M::mma(frag_of<T>(dyraw[kt & 1], e), frag_of<T>(vraw, e), pc);
     }
     z[kt] = zc;
     dp[kt] = pc;
