@@ -33,9 +33,10 @@ struct TeacherLayout {
   static constexpr int LDK = D + PAD;      // sK [64][LDK]: keys of the block
   static constexpr int LDV = 64 + PAD;     // sVt [D][LDV]: values transposed
   static constexpr int LDP = 64 + PAD;     // sP [4][16][LDP]: P of each wavefront
-  static constexpr int OFF_K = 0;
-  static constexpr int OFF_V = OFF_K + 64 * LDK * (int)sizeof(T);
-  static constexpr int OFF_P = OFF_V + D * LDV * (int)sizeof(T);
+  static constexpr int BUF = 64 * LDK * (int)sizeof(T) + D * LDV * (int)sizeof(T);   // one key block
+  static constexpr int OFF_K = 0;                       // + b * BUF for buffer b
+  static constexpr int OFF_V = 64 * LDK * (int)sizeof(T);
+  static constexpr int OFF_P = 2 * BUF;
   static constexpr int TOTAL = OFF_P + 4 * 16 * LDP * (int)sizeof(T);
 };
 
@@ -51,8 +52,6 @@ __global__ __launch_bounds__(256) void teacher_attn_kernel(TeacherArgs a) {
   constexpr int NF = D / 4 / M::KPL;       // MFMA steps over a D contraction
   constexpr int NJT = D / 16;              // output column tiles
   __shared__ __align__(16) unsigned char smem[Lay::TOTAL];
-  T* sK = reinterpret_cast<T*>(smem + Lay::OFF_K);
-  T* sVt = reinterpret_cast<T*>(smem + Lay::OFF_V);
   T* sP = reinterpret_cast<T*>(smem + Lay::OFF_P);
 
   const int L = a.L, nqb = (L + 63) / 64;
@@ -128,35 +127,42 @@ __global__ __launch_bounds__(256) void teacher_attn_kernel(TeacherArgs a) {
     if ((kb + 1) * 64 <= L) load_rows(kb, true);
     else load_rows(kb, false);
   };
-  load_block(0);
-
-  for (int kb = 0; kb <= qb; ++kb) {
-    const int k0 = kb * 64;
-    // ---- the block into LDS: keys row-major, values transposed (8-key runs) ----
+  // the registers into LDS buffer b: keys row-major, values transposed (8-key runs)
+  auto store_block = [&](int b) __attribute__((always_inline)) {
+    T* sK = reinterpret_cast<T*>(smem + b * Lay::BUF + Lay::OFF_K);
+    T* sVt = reinterpret_cast<T*>(smem + b * Lay::BUF + Lay::OFF_V);
 #pragma unroll
     for (int u = 0; u < KVEC; ++u) {
       const int i = tid + 256 * u;
       const int row = i / (D / EPV), cv = i % (D / EPV);
       *reinterpret_cast<uint4*>(sK + row * Lay::LDK + cv * EPV) = kreg[u];
     }
-    {
-      const int vj = tid % VRW, vs = tid / VRW;
+    const int vj = tid % VRW, vs = tid / VRW;
 #pragma unroll
-      for (int cc = 0; cc < VC; ++cc)
+    for (int cc = 0; cc < VC; ++cc)
 #pragma unroll
-        for (int b8 = 0; b8 < RPT / 8; ++b8) {
-          float v8[8];
+      for (int b8 = 0; b8 < RPT / 8; ++b8) {
+        float v8[8];
 #pragma unroll
-          for (int rr = 0; rr < 8; ++rr) {
-            const uint32_t wv = vreg[8 * b8 + rr];
-            if constexpr (sizeof(T) == 2) v8[rr] = __builtin_bit_cast(float, cc == 0 ? (wv << 16) : (wv & 0xffff0000u));
-            else v8[rr] = __builtin_bit_cast(float, wv);
-          }
-          store_pack<T, 8>(sVt + (VC * vj + cc) * Lay::LDV + RPT * vs + 8 * b8, v8);
+        for (int rr = 0; rr < 8; ++rr) {
+          const uint32_t wv = vreg[8 * b8 + rr];
+          if constexpr (sizeof(T) == 2) v8[rr] = __builtin_bit_cast(float, cc == 0 ? (wv << 16) : (wv & 0xffff0000u));
+          else v8[rr] = __builtin_bit_cast(float, wv);
         }
-    }
-    __syncthreads();
-    // the next block's loads fly while this one is multiplied
+        store_pack<T, 8>(sVt + (VC * vj + cc) * Lay::LDV + RPT * vs + 8 * b8, v8);
+      }
+  };
+  load_block(0);
+  store_block(0);
+  __syncthreads();
+
+  // Key block kb is in buffer kb & 1.  Block kb + 1's loads fly while kb is
+  // multiplied, then go to the other buffer, whose last readers (block kb - 1)
+  // finished before the previous barrier: one barrier per block.
+  for (int kb = 0; kb <= qb; ++kb) {
+    const int k0 = kb * 64;
+    const T* sK = reinterpret_cast<const T*>(smem + (kb & 1) * Lay::BUF + Lay::OFF_K);
+    const T* sVt = reinterpret_cast<const T*>(smem + (kb & 1) * Lay::BUF + Lay::OFF_V);
     if (kb < qb) load_block(kb + 1);
 
     // ---- S^T tiles: keys 16kt + 4g + r (rows) x query tq (column m) ----
@@ -211,7 +217,9 @@ __global__ __launch_bounds__(256) void teacher_attn_kernel(TeacherArgs a) {
 #pragma unroll
     for (int jt = 0; jt < NJT; ++jt)
       oacc[jt] = mma_rows<T, 64>(oacc[jt], sVt + (16 * jt + m) * Lay::LDV + g * 16, sPw + m * Lay::LDP + g * 16);
-    __syncthreads();                      // before the next block overwrites sK, sVt (and sP)
+    if (kb < qb) store_block((kb + 1) & 1);
+    // the next block is in place; this wavefront's P tile is free again
+    __syncthreads();
   }
 
   // ---- epilogue: O[tq][16jt + 4g + r] = O^T / l ----
