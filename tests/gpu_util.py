@@ -72,7 +72,7 @@ def up_storage(a: np.ndarray):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
 
 
-def upload_workload(w, L=None, with_dy=False):
+def upload_workload(w, L=None, with_dy=False, with_logit=False):
     """All inputs of a workload on the GPU (generated per slice, in parallel)."""
-    st = si.storage_inputs(w, L=L, with_dy=with_dy)
+    st = si.storage_inputs(w, L=L, with_dy=with_dy, with_logit=with_logit)
     return {k: up_storage(v) for k, v in st.items()}
