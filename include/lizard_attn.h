@@ -64,7 +64,7 @@ typedef enum {
   LIZARD_E_SHAPE = -2,       /* a size is negative or out of its range       */
   LIZARD_E_DTYPE = -3,       /* unknown dtype                                */
   LIZARD_E_ALIGN = -4,       /* a pointer is not 16-byte aligned             */
-  LIZARD_E_WORKSPACE = -5,   /* backward workspace smaller than required     */
+  LIZARD_E_WORKSPACE = -5,   /* workspace missing or smaller than required  */
   LIZARD_E_UNSUPPORTED = -6, /* valid sizes this build has no kernel for     */
   LIZARD_E_LAUNCH = -7       /* the HIP launch reported an error             */
 } lizard_status_t;
@@ -181,6 +181,33 @@ lizard_status_t lizard_attn_fwd_continue(const lizard_params_t* p,
                                          void* y, float* lse, void* y_anchor, float* state_out,
                                          void* stream);
 
+/* lizard_attn_fwd_continue for few heads over long sequences (long-context
+ * prefill, de section 4 "Ergebnisse", "Effizienz": the throughput has to
+ * hold over 32K-token contexts).  One head's sequence is a chain of chunks,
+ * so a one-pass forward runs only B*H*(dv/64) workgroups however long L is.
+ * The recurrence of de section 2 "Kernkomponenten" item 1 is linear in the
+ * state, so this call cuts each sequence into segments run side by side from
+ * a zero state, then a scan chains the segments' final states and each
+ * output row of a later segment gets the term its incoming state adds.
+ *   workspace   device memory of workspace_bytes >=
+ *               lizard_attn_fwd_split_workspace_size(p), 16-byte aligned,
+ *               caller-owned; may be NULL when that size is 0 (then the call
+ *               runs as one pass).  Contents on entry are ignored.
+ * Every other argument, and every result, as lizard_attn_fwd_continue; the
+ * results equal its results up to float rounding (the split adds a second
+ * rounding of y to the element type, and terms carried over a decay below
+ * 2^-128 of a later segment's incoming state are dropped, gates being at
+ * most one).  Returns LIZARD_E_WORKSPACE when the workspace is missing or
+ * too small. */
+size_t lizard_attn_fwd_split_workspace_size(const lizard_params_t* p);
+lizard_status_t lizard_attn_fwd_split(const lizard_params_t* p,
+                                      const void* q, const void* k, const void* v,
+                                      const float* log_g, const void* gate_logit,
+                                      const void* meta_k, const float* state_in,
+                                      const void* k_halo, const void* v_halo, int32_t halo_len,
+                                      void* y, float* lse, void* y_anchor, float* state_out,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* Serving form of the decode step (constant-memory generation for a batch
  * of sequences, de section 2 item 1 and section 4 "Effizienz"): T >= 1 new
  * tokens per row, appended in order, each batch row at its own position.
@@ -275,9 +302,10 @@ lizard_status_t lizard_transfer_loss(const lizard_params_t* p,
 /* Static description of a status code. */
 const char* lizard_status_string(lizard_status_t s);
 
-/* ABI version of this header: 2 (version 1 had none of the *_logit,
- * lizard_attn_fwd_continue, lizard_decode_tokens, lizard_softmax_attn_fwd
- * and lizard_transfer_loss entry points). */
+/* ABI version of this header: 3 (version 2 had no lizard_attn_fwd_split;
+ * version 1 had none of the *_logit, lizard_attn_fwd_continue,
+ * lizard_decode_tokens, lizard_softmax_attn_fwd and lizard_transfer_loss
+ * entry points). */
 int lizard_abi_version(void);
 
 #ifdef __cplusplus

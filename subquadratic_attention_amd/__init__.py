@@ -73,6 +73,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lizard_decode_step_logit.restype = ctypes.c_int
     lib.lizard_attn_fwd_continue.argtypes = [P] + [_vp] * 9 + [ctypes.c_int32] + [_vp] * 5
     lib.lizard_attn_fwd_continue.restype = ctypes.c_int
+    lib.lizard_attn_fwd_split_workspace_size.argtypes = [P]
+    lib.lizard_attn_fwd_split_workspace_size.restype = ctypes.c_size_t
+    lib.lizard_attn_fwd_split.argtypes = [P] + [_vp] * 9 + [ctypes.c_int32] + [_vp] * 5 + [ctypes.c_size_t, _vp]
+    lib.lizard_attn_fwd_split.restype = ctypes.c_int
     lib.lizard_softmax_attn_fwd.argtypes = [P] + [_vp] * 6
     lib.lizard_softmax_attn_fwd.restype = ctypes.c_int
     lib.lizard_transfer_loss.argtypes = [P] + [_vp] * 5
@@ -322,6 +326,49 @@ def lizard_attn_fwd_continue(q, k, v, meta_k, *, log_g=None, gate_logit=None, st
                                       _stream(q.device))
     _check("lizard_attn_fwd_continue", st)
     return o
+
+
+def lizard_attn_fwd_split(q, k, v, meta_k, *, log_g=None, gate_logit=None, state_in=None, k_halo=None,
+                          v_halo=None, window: int, alpha: float, softmax_scale: float = 0.0, chunk: int = 64,
+                          need_lse: bool = False, need_y_anchor: bool = False, need_state: bool = False,
+                          workspace=None, out: Optional[Dict] = None) -> Dict:
+    """lizard_attn_fwd_continue with long sequences cut into segments that run
+    side by side (few heads, long L).  workspace: a uint8 device tensor of at
+    least lizard_attn_fwd_split_workspace_size bytes (allocated when None)."""
+    torch = _torch()
+    lib = load_library()
+    B, H, L, d = q.shape
+    m = meta_k.shape[1] if meta_k is not None else 0
+    hl = 0 if k_halo is None else int(k_halo.shape[2])
+    p = make_params(B, H, L, d, window=window, n_meta=m, alpha=alpha, dtype=_dtype_code(q), chunk=chunk,
+                    softmax_scale=softmax_scale)
+    need = lib.lizard_attn_fwd_split_workspace_size(ctypes.byref(p))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    o = dict(out) if out is not None else {}
+    if "y" not in o:
+        o["y"] = torch.empty_like(q)
+    if need_lse and "lse" not in o:
+        o["lse"] = torch.empty((B, H, L), device=q.device, dtype=torch.float32)
+    if need_y_anchor and "y_anchor" not in o:
+        o["y_anchor"] = torch.empty_like(q)
+    if need_state and "state" not in o:
+        o["state"] = torch.empty((B, H, d, d), device=q.device, dtype=torch.float32)
+    st = lib.lizard_attn_fwd_split(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(gate_logit),
+                                   _ptr(meta_k), _ptr(state_in), _ptr(k_halo), _ptr(v_halo), hl, _ptr(o["y"]),
+                                   _ptr(o.get("lse")), _ptr(o.get("y_anchor")), _ptr(o.get("state")), _ptr(workspace),
+                                   ws_bytes, _stream(q.device))
+    _check("lizard_attn_fwd_split", st)
+    return o
+
+
+def lizard_attn_fwd_split_workspace_size(B: int, H: int, L: int, d: int, *, dtype_code: int = 1,
+                                         window: int = 64, n_meta: int = 0) -> int:
+    """Workspace bytes lizard_attn_fwd_split needs (0: it runs as one pass)."""
+    lib = load_library()
+    p = make_params(B, H, L, d, window=window, n_meta=n_meta, alpha=0.0, dtype=dtype_code)
+    return int(lib.lizard_attn_fwd_split_workspace_size(ctypes.byref(p)))
 
 
 def lizard_softmax_attn_fwd(q, k, v, *, softmax_scale: float = 0.0, need_lse: bool = False,

@@ -38,16 +38,29 @@ float scale_of(const lizard_params_t* p) {
 
 lizard_status_t launched(hipError_t e) { return e == hipSuccess ? LIZARD_OK : LIZARD_E_LAUNCH; }
 
+// Segments per head of a split forward pass (1: one pass) and its workspace.
+int split_segments(const lizard_params_t* p) {
+  const int DV = lizard::fwd_value_slice(p->dtype == LIZARD_BF16, p->dk);
+  if (DV <= 0) return 1;
+  return lizard::fwd_segments(p->B * p->H, p->dv / DV, p->L);
+}
+size_t split_workspace(const lizard_params_t* p, int nseg, size_t* offsets = nullptr) {
+  return lizard::fwd_split_workspace_bytes(p->B * p->H, p->L, p->dk, p->dtype == LIZARD_BF16 ? 2 : 4, nseg, offsets);
+}
+
 // The forward pass with the gates given as log-gates (log_g) or as logits
 // (gate_logit); exactly one of the two is used.  state_in / halo: a
 // continued sequence (NULL / 0 for a sequence that starts at position 0).
 lizard_status_t attn_fwd(const lizard_params_t* p, const void* q, const void* k, const void* v, const float* log_g,
                          const void* gate_logit, bool logit, const void* meta_k, const float* state_in,
                          const void* k_halo, const void* v_halo, int32_t halo_len, void* y, float* lse,
-                         void* y_anchor, float* state_out, void* stream) {
+                         void* y_anchor, float* state_out, void* stream, bool split = false,
+                         void* workspace = nullptr, size_t workspace_bytes = 0) {
   lizard_status_t s = check_params(p, true);
   if (s != LIZARD_OK) return s;
   if (halo_len < 0 || halo_len > p->window - 1) return LIZARD_E_SHAPE;
+  const int nseg = split ? split_segments(p) : 1;
+  if (nseg > 1 && (workspace == nullptr || workspace_bytes < split_workspace(p, nseg))) return LIZARD_E_WORKSPACE;
   const int BH = p->B * p->H;
   if (BH == 0) return LIZARD_OK;  // nothing to read or write; empty tensors may have NULL data
   const bool seq = p->L > 0;
@@ -57,7 +70,7 @@ lizard_status_t attn_fwd(const lizard_params_t* p, const void* q, const void* k,
     return LIZARD_E_NULL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(gate) || misaligned(y) ||
       misaligned(meta_k) || misaligned(lse) || misaligned(y_anchor) || misaligned(state_out) ||
-      misaligned(state_in) || misaligned(k_halo) || misaligned(v_halo))
+      misaligned(state_in) || misaligned(k_halo) || misaligned(v_halo) || misaligned(workspace))
     return LIZARD_E_ALIGN;
   if (!seq && state_out == nullptr) return LIZARD_OK;
   const int bf = p->dtype == LIZARD_BF16;
@@ -86,6 +99,16 @@ lizard_status_t attn_fwd(const lizard_params_t* p, const void* q, const void* k,
   a.nsplit = p->dv / DV;
   a.alpha = p->alpha;
   a.scale_log2 = scale_of(p) * 1.4426950408889634f;
+  a.nseg = nseg;
+  if (nseg > 1) {
+    size_t off[3];
+    split_workspace(p, nseg, off);
+    char* w = static_cast<char*>(workspace);
+    a.seg_state = reinterpret_cast<float*>(w);
+    a.seg_total = reinterpret_cast<float*>(w + off[0]);
+    a.chunk_cum = reinterpret_cast<float*>(w + off[1]);
+    a.seg_in_t = w + off[2];
+  }
   return launched(lizard::launch_fwd(a, bf, p->dk, static_cast<hipStream_t>(stream)));
 }
 
@@ -206,6 +229,22 @@ LIZARD_API lizard_status_t lizard_attn_fwd_continue(const lizard_params_t* p, co
                   lse, y_anchor, state_out, stream);
 }
 
+LIZARD_API size_t lizard_attn_fwd_split_workspace_size(const lizard_params_t* p) {
+  if (check_params(p, true) != LIZARD_OK) return 0;
+  return split_workspace(p, split_segments(p));
+}
+
+LIZARD_API lizard_status_t lizard_attn_fwd_split(const lizard_params_t* p, const void* q, const void* k,
+                                                 const void* v, const float* log_g, const void* gate_logit,
+                                                 const void* meta_k, const float* state_in, const void* k_halo,
+                                                 const void* v_halo, int32_t halo_len, void* y, float* lse,
+                                                 void* y_anchor, float* state_out, void* workspace,
+                                                 size_t workspace_bytes, void* stream) {
+  if (log_g != nullptr && gate_logit != nullptr) return LIZARD_E_SHAPE;
+  return attn_fwd(p, q, k, v, log_g, gate_logit, gate_logit != nullptr, meta_k, state_in, k_halo, v_halo, halo_len, y,
+                  lse, y_anchor, state_out, stream, true, workspace, workspace_bytes);
+}
+
 LIZARD_API size_t lizard_attn_bwd_workspace_size(const lizard_params_t* p) {
   if (check_params(p, true) != LIZARD_OK) return 0;
   return lizard::bwd_workspace_bytes(p->dtype == LIZARD_BF16, p->B * p->H, p->L, p->dk, p->n_meta);
@@ -310,4 +349,4 @@ LIZARD_API const char* lizard_status_string(lizard_status_t s) {
   return "unknown status";
 }
 
-LIZARD_API int lizard_abi_version(void) { return 2; }
+LIZARD_API int lizard_abi_version(void) { return 3; }

@@ -132,7 +132,7 @@ __device__ __forceinline__ int opaque(int x) {
 // leaves a factor 2^36 of headroom below the float / bfloat16 maximum.
 constexpr float kMaxSpanLog2 = 92.0f;
 
-template <typename T, int D, int DV, bool STATES, bool LOGIT>
+template <typename T, int D, int DV, bool STATES, bool LOGIT, bool SEG>
 __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
   typedef FwdLayout<T, D, DV> Lay;
   typedef Mfma<T> M;
@@ -164,16 +164,23 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
   float* sSc = reinterpret_cast<float*>(smem + Lay::OFF_SC);
   T* sMeta = reinterpret_cast<T*>(smem + Lay::OFF_META);
 
-  // ---- block -> (b*h, value slice); siblings of one head share an XCD ----
+  // ---- block -> (b*h, value slice, segment); the blocks of one head share an XCD ----
   const int x = blockIdx.x;
   const int xcd = x & 7;
   const int idx = x >> 3;
   const int split = idx % a.nsplit;
-  const int bh = (idx / a.nsplit) * 8 + xcd;
+  const int seg = SEG ? (idx / a.nsplit) % a.nseg : 0;
+  const int bh = (idx / (SEG ? a.nsplit * a.nseg : a.nsplit)) * 8 + xcd;
   if (bh >= a.BH) return;
   const int h = bh % a.H;
   const int j0 = split * DV;
   const int L = a.L;
+  const int nc = (L + C - 1) / C;
+  int c_lo = 0, c_hi = nc;
+  if constexpr (SEG) {
+    segment_chunks(seg, a.nseg, nc, c_lo, c_hi);
+    if (c_lo >= c_hi) return;
+  }
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wavefront 0..7: prep rows 8w..8w+7
@@ -192,20 +199,33 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
   T* __restrict__ yag = a.y_anchor ? reinterpret_cast<T*>(a.y_anchor) + (size_t)bh * L * D + j0 : nullptr;
   float* __restrict__ lseg = (a.lse && split == 0) ? a.lse + (size_t)bh * L : nullptr;
 
-  // ---- the key/value rings: the window of chunk 0 reads "chunk -1" (key
-  // ring rows 64..127, value ring columns 128..191), which holds the halo
-  // tokens of a continued sequence in its last a.halo entries, else zeros ----
+  // ---- the key/value rings: the window of the first chunk c_lo reads the
+  // ring positions of chunk c_lo - 1 (key ring half (c_lo - 1) & 1, value
+  // ring slot (c_lo - 1) mod 3), which hold, in their last nh entries, the
+  // previous chunk of a split sequence or the halo tokens of a continued
+  // sequence; everything else is zero ----
   {
-    const int hb = 128 - a.halo;   // first halo row of the key ring / 64 + first halo column of the value ring
-    const T* khp = a.halo > 0 ? reinterpret_cast<const T*>(a.k_halo) + (size_t)bh * a.halo * D : nullptr;
-    const T* vhp = a.halo > 0 ? reinterpret_cast<const T*>(a.v_halo) + (size_t)bh * a.halo * D + j0 : nullptr;
+    const int cp = c_lo - 1;                       // -1 for the first segment
+    const int ph = (cp & 1) * 64, ps = ((cp % 3 + 3) % 3) * 64;
+    const int nh = c_lo > 0 ? 64 : a.halo;
+    const T* khp = nullptr;
+    const T* vhp = nullptr;
+    if (c_lo > 0) {
+      khp = kg + (size_t)(c_lo * C - 64) * D;
+      vhp = vg + (size_t)(c_lo * C - 64) * D;
+    } else if (a.halo > 0) {
+      khp = reinterpret_cast<const T*>(a.k_halo) + (size_t)bh * a.halo * D;
+      vhp = reinterpret_cast<const T*>(a.v_halo) + (size_t)bh * a.halo * D + j0;
+    }
+    const int hb = ph + 64 - nh;                   // first filled key ring row
     for (int i = tid; i < 128 * Lay::LDK; i += 512) {
       const int row = i / Lay::LDK, col = i % Lay::LDK;
-      sK[i] = row >= hb && col < D ? khp[(size_t)(row - hb) * D + col] : from_f32<T>(0.f);
+      sK[i] = row >= hb && row < ph + 64 && col < D ? khp[(size_t)(row - hb) * D + col] : from_f32<T>(0.f);
     }
+    const int vb = ps + 64 - nh;                   // first filled value ring column
     for (int i = tid; i < DV * Lay::LDVT; i += 512) {
       const int j = i / Lay::LDVT, col = i % Lay::LDVT;
-      sVt[i] = col >= hb + 64 && col < 192 ? vhp[(size_t)(col - hb - 64) * D + j] : from_f32<T>(0.f);
+      sVt[i] = col >= vb && col < ps + 64 ? vhp[(size_t)(col - vb) * D + j] : from_f32<T>(0.f);
     }
   }
   // ---- sink keys (rows >= n_meta zero), resident in LDS throughout ----
@@ -232,7 +252,7 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
   #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) acc[rt][ct] = zero4();
     if constexpr (GATE && !STATES) {
-      if (a.state_in) {
+      if (a.state_in && seg == 0) {
         // a continued sequence: the state before its first token
         const float* si = a.state_in + (size_t)bh * D * D + j0;
   #pragma unroll
@@ -261,6 +281,7 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
     uint32_t vA[VR];      // values: rows VR*vs + rr, columns VC*vj.. packed in 32 bits
     uint4 qraw[QV];       // softmax wavefronts: raw q of row 16I + m, the lane's k-quarter
     f32x4 og[NCT];        // gate wavefronts: gated output of the block, carried over a barrier
+    float rcum[DPL] = {};  // split sequences: log2-gate sum from the segment start (one gate wavefront)
 
     auto load_rows = [&](int c, bool full) __attribute__((always_inline)) {
       const int t0 = c * C;
@@ -471,6 +492,15 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
         store_pack<T, 8>(sKhT + (DPL * l + dd) * Lay::LDKH + 8 * w, kh[dd]);
         if (w == 0) sBexp[DPL * l + dd] = eB[dd];
       }
+      if constexpr (SEG && GATE && QB == 0) {
+        // a split sequence: the decay from the segment start to this chunk's
+        // start, and its running sum (the exponents of eB)
+  #pragma unroll
+        for (int dd = 0; dd < DPL; ++dd) {
+          if (split == 0) a.chunk_cum[((size_t)bh * nc + cc) * D + DPL * l + dd] = rcum[dd];
+          rcum[dd] += pairwise ? Bt[dd] : Bt[dd] * kLog2e;
+        }
+      }
       // raw keys into the ring
   #pragma unroll
       for (int rr = 0; rr < 8; ++rr) {
@@ -538,21 +568,20 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
       }
     };
 
-    const int nc = (L + C - 1) / C;
     bool pw = false;                      // pairwise path for the chunk about to be processed
-    if (nc > 0) {
-      load_chunk(0);
-      if constexpr (!GATE && !STATES) load_q(0);
+    if (c_hi > c_lo) {
+      load_chunk(c_lo);
+      if constexpr (!GATE && !STATES) load_q(c_lo);
       prefix_part();
     }
     __syncthreads();
-    if (nc > 0) {
-      pw = operand_part(0);
-      if (nc > 1) load_chunk(1);
+    if (c_hi > c_lo) {
+      pw = operand_part(c_lo);
+      if (c_hi > c_lo + 1) load_chunk(c_lo + 1);
     }
     __syncthreads();
 
-    for (int c = 0; c < nc; ++c) {
+    for (int c = c_lo; c < c_hi; ++c) {
       const int t0 = c * C;
       const int kcur = (c & 1) * 64;      // key ring half of this chunk
       const int kprv = 64 - kcur;         // ... and of the previous chunk
@@ -577,7 +606,7 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
         // chunk (the last one reloads itself) so that the number of memory
         // operations between a load and its use is the same on every path:
         // the wait for it then counts, instead of draining all loads in flight.
-        load_q(c + 1 < nc ? c + 1 : c);
+        load_q(c + 1 < c_hi ? c + 1 : c);
 
         // anchor logits Z^T[u][t] over the 6 window tiles kt (keys u in
         // [U0+16kt, U0+16kt+16) of [prev; cur]); every tile is computed, keys
@@ -597,7 +626,7 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
 
         // Softmax: maxima on raw logits (the scale is positive), scale folded
         // into the exponent: P = 2^{z * scale*log2e - max}.
-        float mr = -INFINITY;
+        float mr = -__builtin_huge_valf();
   #pragma unroll
         for (int r = 0; r < 4; ++r) {
           zs[r] = 4 * g + r < a.n_meta ? zs[r] : -INFINITY;
@@ -798,18 +827,37 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
       } else {
         softmax_part(Ic);
       }
-      if (c + 1 < nc) prefix_part();
+      if (c + 1 < c_hi) prefix_part();
       __syncthreads();
 
       // ---- interval 2 ----
       if constexpr (GATE && !STATES) output_part(Ic);
-      if (c + 1 < nc) pw = operand_part(c + 1);
+      if (c + 1 < c_hi) pw = operand_part(c + 1);
       // chunk c+2 (clamped: issued on every chunk for the same reason as load_q)
-      load_chunk(c + 2 < nc ? c + 2 : nc - 1);
+      load_chunk(c + 2 < c_hi ? c + 2 : c_hi - 1);
       __syncthreads();
     }
 
-    if (GATE && a.state_out) {
+    if constexpr (SEG) {
+      if constexpr (GATE) {
+        // a split sequence: this segment's final state (from a zero state,
+        // except the first segment) and its log2-gate total, for the scan
+        float* so = a.seg_state + ((size_t)bh * a.nseg + seg) * D * D;
+  #pragma unroll
+        for (int rt = 0; rt < DPL; ++rt)
+  #pragma unroll
+          for (int ct = 0; ct < NCT; ++ct)
+  #pragma unroll
+            for (int r = 0; r < 4; ++r)
+              so[(size_t)(16 * (DPL * I + rt) + 4 * g_lane + r) * D + j0 + 16 * ct + m_lane] = acc[rt][ct][r];
+        if constexpr (QB == 0) {
+          const int l = threadIdx.x & 63;
+  #pragma unroll
+          for (int dd = 0; dd < DPL; ++dd)
+            if (split == 0) a.seg_total[((size_t)bh * a.nseg + seg) * D + DPL * l + dd] = rcum[dd];
+        }
+      }
+    } else if (GATE && a.state_out) {
       float* so = a.state_out + (size_t)bh * D * D;
   #pragma unroll
       for (int rt = 0; rt < DPL; ++rt)
@@ -832,25 +880,291 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
   }
 }
 
-template <typename T, int D, int DV, bool STATES, bool LOGIT>
+// ---- split sequences (few heads, long sequences) ----
+//
+// With S_in(s) the state entering segment s, DS_s segment s's final state
+// from a zero state and A_s its log2-gate total, the recurrence is linear:
+//   S_in(s+1) = diag(2^{A_s}) S_in(s) + DS_s
+// and a token t of chunk c in segment s misses from its output the term
+//   (q_t * 2^{R_c + beta_t})^T S_in(s),
+// R_c being the log2-gate sum from the segment start to chunk c's start.
+
+// The chain over segments: S_in(s) for s >= 1, transposed and in the element
+// type (the operand layout of the output correction), and the final state
+// into state_out.  A workgroup owns RPB rows i of one head's state, a thread
+// 4 consecutive columns of one row; grid (D / RPB, BH).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void fwd_seg_scan_kernel(FwdArgs a) {
+  constexpr int RPB = 1024 / D;                    // state rows per workgroup
+  constexpr int NV = RPB * (int)sizeof(T) / 16;    // 16-byte vectors per transposed row piece
+  __shared__ float tile[RPB][D + 4];
+  const int bh = blockIdx.y;
+  const int i0 = blockIdx.x * RPB;
+  const int tid = threadIdx.x;
+  const int ri = tid / (D / 4), j = 4 * (tid % (D / 4));
+  const int i = i0 + ri;
+  const float* base = a.seg_state + (size_t)bh * a.nseg * D * D + (size_t)i * D + j;
+  float4 S = *reinterpret_cast<const float4*>(base);      // segment 0 ends with its complete state
+  for (int sg = 1; sg < a.nseg; ++sg) {
+    const float4 ds = *reinterpret_cast<const float4*>(base + (size_t)sg * D * D);
+    const float dec = exp_2(a.seg_total[((size_t)bh * a.nseg + sg) * D + i]);
+    // S_in(sg)^T rows j .. j + 3, columns i0 .. i0 + RPB
+    *reinterpret_cast<float4*>(&tile[ri][j]) = S;
+    __syncthreads();
+    if (tid < D * NV) {
+      const int jj = tid / NV, part = tid % NV;
+      constexpr int EV = 16 / sizeof(T);
+      float x[EV];
+  #pragma unroll
+      for (int e = 0; e < EV; ++e) x[e] = tile[part * EV + e][jj];
+      uint4 o;
+      store_pack<T, EV>(reinterpret_cast<T*>(&o), x);
+      T* dst = reinterpret_cast<T*>(a.seg_in_t) + (((size_t)bh * a.nseg + sg) * D + jj) * D + i0 + part * EV;
+      *reinterpret_cast<uint4*>(dst) = o;
+    }
+    __syncthreads();
+    S.x = fmaf(dec, S.x, ds.x);
+    S.y = fmaf(dec, S.y, ds.y);
+    S.z = fmaf(dec, S.z, ds.z);
+    S.w = fmaf(dec, S.w, ds.w);
+  }
+  if (a.state_out) *reinterpret_cast<float4*>(a.state_out + (size_t)bh * D * D + (size_t)i * D + j) = S;
+}
+
+// Below this log2 decay the carried state's share of an output is under
+// 2^-128 of its size (gates are at most one, so later chunks decay further):
+// such chunks are left as they are.
+constexpr float kSegSkipLog2 = -128.0f;
+
+template <typename T, int D>
+struct FixLayout {
+  static constexpr int PAD = 16 / sizeof(T);
+  static constexpr int LDS = D + PAD;        // sSt [D][LDS]: S_in transposed, element type
+  static constexpr int LDQ = D + PAD;        // sQs [64][LDQ]: scaled queries
+  static constexpr int LDC = D + 4;          // sC [64][LDC] float, over sQs: the correction
+  static constexpr int DG = D / 8;           // threads per token row (8 dimensions each)
+  static constexpr int TG = 256 / DG;        // token groups
+  static constexpr int NTT = 64 / TG;        // consecutive tokens per thread
+  static constexpr int QC = 64 * LDQ * (int)sizeof(T) > 64 * LDC * 4 ? 64 * LDQ * (int)sizeof(T) : 64 * LDC * 4;
+  static constexpr int OFF_S = 0;
+  static constexpr int OFF_Q = OFF_S + D * LDS * (int)sizeof(T);
+  static constexpr int OFF_P = OFF_Q + QC;                // token groups' gate totals [TG][D] float
+  static constexpr int OFF_W = OFF_P + TG * D * 4;        // per-wavefront maxima [4] float
+  static constexpr int TOTAL = OFF_W + 16;
+};
+
+// y_t += (q_t * 2^{R_c + beta_t})^T S_in(s) for the chunks of segments
+// s >= 1.  Grid (chunk groups of FG, nseg - 1, BH); 4 wavefronts.  Thread
+// (tg, dg) loads tokens NTT*tg .. of the chunk in dimensions 8dg .. 8dg+7
+// (16-byte vectors, all issued at the chunk start); wavefront w computes the
+// chunk's rows 16w .. 16w+15 on the matrix cores.
+template <typename T, int D, bool LOGIT>
+__global__ __launch_bounds__(256, 2) void fwd_seg_fix_kernel(FwdArgs a) {
+  typedef FixLayout<T, D> Lay;
+  constexpr int FG = 4;                  // chunks per workgroup
+  constexpr int DG = Lay::DG, NTT = Lay::NTT;
+  constexpr int VT = 8 * (int)sizeof(T) / 16;    // 16-byte vectors per 8 elements of T
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* sSt = reinterpret_cast<T*>(smem + Lay::OFF_S);
+  T* sQs = reinterpret_cast<T*>(smem + Lay::OFF_Q);
+  float* sC = reinterpret_cast<float*>(smem + Lay::OFF_Q);
+  float* sP = reinterpret_cast<float*>(smem + Lay::OFF_P);
+  float* sW = reinterpret_cast<float*>(smem + Lay::OFF_W);
+
+  const int bh = blockIdx.z;
+  const int sg = blockIdx.y + 1;
+  const int L = a.L;
+  const int nc = (L + 63) / 64;
+  int c_lo, c_hi;
+  segment_chunks(sg, a.nseg, nc, c_lo, c_hi);
+  const int cb = c_lo + blockIdx.x * FG;
+  if (cb >= c_hi) return;
+  const int ce = cb + FG < c_hi ? cb + FG : c_hi;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
+  const int dg = tid % DG, tg = tid / DG;
+  const int d0 = 8 * dg;
+
+  // the incoming state, S_in^T rows, 16-byte vectors
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.seg_in_t) +
+                                                      ((size_t)bh * a.nseg + sg) * D * D);
+    constexpr int VPR = D * (int)sizeof(T) / 16;     // vectors per row
+    constexpr int N = D * VPR / 256;
+    uint4 buf[N];
+  #pragma unroll
+    for (int e = 0; e < N; ++e) buf[e] = src[tid + 256 * e];
+  #pragma unroll
+    for (int e = 0; e < N; ++e) {
+      const int v = tid + 256 * e;
+      *reinterpret_cast<uint4*>(sSt + (v / VPR) * Lay::LDS + (v % VPR) * (16 / sizeof(T))) = buf[e];
+    }
+  }
+
+  const T* qg = reinterpret_cast<const T*>(a.q) + (size_t)bh * L * D + d0;
+  T* yg = reinterpret_cast<T*>(a.y) + (size_t)bh * L * D + d0;
+  const float* lgg = a.log_g ? a.log_g + (size_t)bh * L * D + d0 : nullptr;
+  const T* xg = LOGIT ? reinterpret_cast<const T*>(a.gate_logit) + (size_t)bh * L * D + d0 : nullptr;
+  for (int c = cb; c < ce; ++c) {
+    const int t0 = c * 64 + NTT * tg;             // this thread's first token
+    // ---- every global load of the chunk first (rows past L: row L - 1, masked below) ----
+    uint4 qv[NTT][VT], yv[NTT][VT], gv[NTT][LOGIT ? VT : 2];
+  #pragma unroll
+    for (int r = 0; r < NTT; ++r) {
+      const size_t row = (size_t)(t0 + r < L ? t0 + r : L - 1) * D;
+  #pragma unroll
+      for (int e = 0; e < VT; ++e) {
+        qv[r][e] = ld16(qg + row + e * (16 / sizeof(T)));
+        yv[r][e] = ld16(yg + row + e * (16 / sizeof(T)));
+      }
+      if constexpr (LOGIT) {
+  #pragma unroll
+        for (int e = 0; e < VT; ++e) gv[r][e] = ld16(xg + row + e * (16 / sizeof(T)));
+      } else {
+        gv[r][0] = ld16(lgg + row);
+        gv[r][1] = ld16(lgg + row + 4);
+      }
+    }
+    float Rv[8];
+    {
+      const float* rp = a.chunk_cum + ((size_t)bh * nc + c) * D + d0;
+      const float4 r0 = *reinterpret_cast<const float4*>(rp), r1 = *reinterpret_cast<const float4*>(rp + 4);
+      Rv[0] = r0.x; Rv[1] = r0.y; Rv[2] = r0.z; Rv[3] = r0.w;
+      Rv[4] = r1.x; Rv[5] = r1.y; Rv[6] = r1.z; Rv[7] = r1.w;
+    }
+    // ---- log2-gate prefix over the thread's tokens, totals per token group ----
+    float lb[NTT][8];
+  #pragma unroll
+    for (int r = 0; r < NTT; ++r) {
+      if constexpr (LOGIT) {
+  #pragma unroll
+        for (int e = 0; e < VT; ++e) unpack16<T>(gv[r][e], lb[r] + e * (16 / sizeof(T)));
+  #pragma unroll
+        for (int x = 0; x < 8; ++x) lb[r][x] = log_sigmoid(lb[r][x]);
+      } else {
+        unpack16<float>(gv[r][0], lb[r]);
+        unpack16<float>(gv[r][1], lb[r] + 4);
+      }
+    }
+  #pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      float run = 0.f;
+  #pragma unroll
+      for (int r = 0; r < NTT; ++r) {
+        run += t0 + r < L ? log2_gate(lb[r][x]) : 0.f;
+        lb[r][x] = run;
+      }
+      sP[tg * D + d0 + x] = run;
+    }
+    float mx = Rv[0];
+  #pragma unroll
+    for (int x = 1; x < 8; ++x) mx = fmaxf(mx, Rv[x]);
+    mx = wave_max(mx);
+    if (l == 0) sW[w] = mx;
+    __syncthreads();
+    const float cmax = fmaxf(fmaxf(sW[0], sW[1]), fmaxf(sW[2], sW[3]));
+    if (cmax < kSegSkipLog2) break;              // uniform: this and every later chunk of the group
+    // ---- scaled queries into sQs ----
+    {
+      float off[8];
+  #pragma unroll
+      for (int x = 0; x < 8; ++x) off[x] = Rv[x];
+      for (int gg = 0; gg < tg; ++gg) {
+        const float4 p0 = *reinterpret_cast<const float4*>(sP + gg * D + d0);
+        const float4 p1 = *reinterpret_cast<const float4*>(sP + gg * D + d0 + 4);
+        off[0] += p0.x; off[1] += p0.y; off[2] += p0.z; off[3] += p0.w;
+        off[4] += p1.x; off[5] += p1.y; off[6] += p1.z; off[7] += p1.w;
+      }
+  #pragma unroll
+      for (int r = 0; r < NTT; ++r) {
+        float qf[8];
+  #pragma unroll
+        for (int e = 0; e < VT; ++e) unpack16<T>(qv[r][e], qf + e * (16 / sizeof(T)));
+        const bool ok = t0 + r < L;
+  #pragma unroll
+        for (int x = 0; x < 8; ++x) qf[x] = ok ? qf[x] * exp_2(off[x] + lb[r][x]) : 0.f;
+        store_pack<T, 8>(sQs + (NTT * tg + r) * Lay::LDQ + d0, qf);
+      }
+    }
+    __syncthreads();
+    // ---- the correction: rows 16w + 4g + r, columns 16ct + m ----
+    f32x4 cv[D / 16];
+  #pragma unroll
+    for (int ct = 0; ct < D / 16; ++ct)
+      cv[ct] = mma_rows<T, D>(zero4(), sQs + (16 * w + m) * Lay::LDQ + g * (D / 4),
+                              sSt + (16 * ct + m) * Lay::LDS + g * (D / 4));
+    __syncthreads();                              // sC overlays sQs
+  #pragma unroll
+    for (int ct = 0; ct < D / 16; ++ct)
+  #pragma unroll
+      for (int r = 0; r < 4; ++r) sC[(16 * w + 4 * g + r) * Lay::LDC + 16 * ct + m] = cv[ct][r];
+    __syncthreads();
+    // ---- y += correction ----
+  #pragma unroll
+    for (int r = 0; r < NTT; ++r) {
+      if (t0 + r >= L) continue;
+      float yf[8];
+  #pragma unroll
+      for (int e = 0; e < VT; ++e) unpack16<T>(yv[r][e], yf + e * (16 / sizeof(T)));
+      const float* cp = sC + (NTT * tg + r) * Lay::LDC + d0;
+      const float4 c0 = *reinterpret_cast<const float4*>(cp), c1 = *reinterpret_cast<const float4*>(cp + 4);
+      yf[0] += c0.x; yf[1] += c0.y; yf[2] += c0.z; yf[3] += c0.w;
+      yf[4] += c1.x; yf[5] += c1.y; yf[6] += c1.z; yf[7] += c1.w;
+      uint4 o[VT];
+      store_pack<T, 8>(reinterpret_cast<T*>(o), yf);
+  #pragma unroll
+      for (int e = 0; e < VT; ++e) st16(yg + (size_t)(t0 + r) * D + e * (16 / sizeof(T)), o[e]);
+    }
+    __syncthreads();                              // sC / sP reused by the next chunk
+  }
+}
+
+template <typename T, int D, int DV, bool STATES, bool LOGIT, bool SEG>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   typedef FwdLayout<T, D, DV> Lay;
   static_assert(Lay::TOTAL <= 160 * 1024, "LDS budget");
   static_assert(D == 128 || (D == 64 && sizeof(T) == 2) || (D == 64 && DV == 32), "shapes");
   const int smem = Lay::TOTAL;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lizard_fwd_kernel<T, D, DV, STATES, LOGIT>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lizard_fwd_kernel<T, D, DV, STATES, LOGIT, SEG>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, smem);
   if (e != hipSuccess) return e;
   const int groups = (a.BH + 7) / 8;
-  dim3 grid(8 * groups * a.nsplit);
-  hipLaunchKernelGGL((lizard_fwd_kernel<T, D, DV, STATES, LOGIT>), grid, dim3(512), smem, st, a);
+  dim3 grid(8 * groups * a.nsplit * (SEG ? a.nseg : 1));
+  hipLaunchKernelGGL((lizard_fwd_kernel<T, D, DV, STATES, LOGIT, SEG>), grid, dim3(512), smem, st, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D, bool LOGIT>
+static hipError_t launch_seg_finish(const FwdArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((fwd_seg_scan_kernel<T, D>), dim3(D / (1024 / D), a.BH), dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  typedef FixLayout<T, D> Lay;
+  static_assert(Lay::TOTAL <= 160 * 1024, "LDS budget");
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_seg_fix_kernel<T, D, LOGIT>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, Lay::TOTAL);
+  if (e != hipSuccess) return e;
+  const int nc = (a.L + 63) / 64;
+  const int longest = (nc + a.nseg - 1) / a.nseg;
+  hipLaunchKernelGGL((fwd_seg_fix_kernel<T, D, LOGIT>), dim3((longest + 3) / 4, a.nseg - 1, a.BH), dim3(256),
+                     Lay::TOTAL, st, a);
   return hipGetLastError();
 }
 
 template <typename T, int D, int DV>
 static hipError_t launch_fwd_s(const FwdArgs& a, hipStream_t st) {
-  if (a.gate_logit) return a.states ? launch_fwd_t<T, D, DV, true, true>(a, st) : launch_fwd_t<T, D, DV, false, true>(a, st);
-  return a.states ? launch_fwd_t<T, D, DV, true, false>(a, st) : launch_fwd_t<T, D, DV, false, false>(a, st);
+  if (a.states) {
+    if (a.nseg != 1) return hipErrorInvalidValue;
+    return a.gate_logit ? launch_fwd_t<T, D, DV, true, true, false>(a, st)
+                        : launch_fwd_t<T, D, DV, true, false, false>(a, st);
+  }
+  if (a.nseg <= 1)
+    return a.gate_logit ? launch_fwd_t<T, D, DV, false, true, false>(a, st)
+                        : launch_fwd_t<T, D, DV, false, false, false>(a, st);
+  hipError_t e = a.gate_logit ? launch_fwd_t<T, D, DV, false, true, true>(a, st)
+                              : launch_fwd_t<T, D, DV, false, false, true>(a, st);
+  if (e != hipSuccess) return e;
+  return a.gate_logit ? launch_seg_finish<T, D, true>(a, st) : launch_seg_finish<T, D, false>(a, st);
 }
 
 int fwd_value_slice(int dtype_bf16, int D) {

@@ -25,6 +25,15 @@ struct FwdArgs {
   const void* k_halo;      // [BH, halo, D] element type
   const void* v_halo;      // [BH, halo, D] element type
   int halo;                // 0 .. window - 1
+  // sequence split (nseg > 1): every head's chunks are cut into nseg
+  // segments run in parallel, each from a zero state (segment 0 from
+  // state_in); each writes its final state and gate sums, which a scan and
+  // an output correction turn into the one-pass result
+  int nseg = 1;            // 1: one pass
+  float* seg_state;        // [BH, nseg, D, D] float32: each segment's final state
+  float* seg_total;        // [BH, nseg, D] float32: each segment's log2-gate total
+  float* chunk_cum;        // [BH, nc, D] float32: log2-gate sum from the segment start to each chunk start
+  void* seg_in_t;          // [BH, nseg, D, D] element type: S_in(s) transposed (s >= 1)
   int BH, H, L, n_meta, window, nsplit;
   float alpha;
   float scale_log2;     // softmax scale * log2(e)
@@ -90,6 +99,43 @@ struct TeacherArgs {
 // Value-column slice width the forward kernel uses (0 = unsupported).
 int fwd_value_slice(int dtype_bf16, int D);
 hipError_t launch_fwd(const FwdArgs& a, int dtype_bf16, int D, hipStream_t st);
+
+// Chunks [lo, hi) of segment seg when nc chunks are cut into nseg segments
+// (sizes differ by at most one; none is empty while nseg <= nc).
+__host__ __device__ inline void segment_chunks(int seg, int nseg, int nc, int& lo, int& hi) {
+  lo = (int)((long long)seg * nc / nseg);
+  hi = (int)((long long)(seg + 1) * nc / nseg);
+}
+
+// Segments per head for a split forward pass: enough workgroups for the
+// 256 compute units, at least 8 chunks per segment; 1 = one pass.
+inline int fwd_segments(int BH, int nsplit, int L) {
+  const long long blocks = (long long)BH * nsplit;
+  const int nc = (L + 63) / 64;
+  if (blocks <= 0 || blocks >= 256 || nc < 16) return 1;
+  long long n = 256 / blocks;
+  if (n > nc / 8) n = nc / 8;
+  if (n > 32) n = 32;
+  return n >= 2 ? (int)n : 1;
+}
+
+// Workspace of a split forward pass, in this order (each part 256-byte
+// aligned): segment states, segment gate totals, per-chunk gate sums, the
+// incoming states transposed in the element type of esize bytes.
+inline size_t fwd_split_workspace_bytes(int BH, int L, int D, int esize, int nseg, size_t* offsets = nullptr) {
+  if (nseg <= 1) return 0;
+  auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  const size_t nc = (size_t)(L + 63) / 64;
+  const size_t o1 = al((size_t)BH * nseg * D * D * 4);
+  const size_t o2 = o1 + al((size_t)BH * nseg * D * 4);
+  const size_t o3 = o2 + al((size_t)BH * nc * D * 4);
+  if (offsets) {
+    offsets[0] = o1;
+    offsets[1] = o2;
+    offsets[2] = o3;
+  }
+  return o3 + al((size_t)BH * nseg * D * D * esize);
+}
 hipError_t launch_decode(const DecodeArgs& a, int dtype_bf16, int D, hipStream_t st);
 size_t bwd_workspace_bytes(int dtype_bf16, int BH, int L, int D, int n_meta);
 hipError_t launch_bwd(const BwdArgs& a, int dtype_bf16, int D, hipStream_t st);

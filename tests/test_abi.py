@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
     for want in ("lizard_attn_fwd", "lizard_attn_bwd", "lizard_attn_bwd_workspace_size", "lizard_decode_step",
                  "lizard_attn_fwd_logit", "lizard_attn_bwd_logit", "lizard_decode_step_logit",
                  "lizard_decode_tokens", "lizard_decode_tokens_logit", "lizard_attn_fwd_continue",
-                 "lizard_softmax_attn_fwd", "lizard_transfer_loss",
+                 "lizard_softmax_attn_fwd", "lizard_transfer_loss", "lizard_attn_fwd_split",
+                 "lizard_attn_fwd_split_workspace_size",
                  "lizard_status_string", "lizard_abi_version"):
         assert want in names
 
@@ -65,7 +66,7 @@ def test_param_struct_layout_matches_c(tmp_path):
 
 
 def test_version_and_strings(lib):
-    assert lib.lizard_abi_version() == 2
+    assert lib.lizard_abi_version() == 3
     for code, name in sqa.STATUS.items():
         s = lib.lizard_status_string(code)
         assert isinstance(s, bytes) and len(s) > 0
@@ -211,3 +212,23 @@ def test_continue_checks(lib):
     assert f(FAKE, None, 3, kh=None) == S["LIZARD_E_NULL"]
     assert f(FAKE, None, 3, vh=MIS) == S["LIZARD_E_ALIGN"]
     assert f(FAKE, None, 0, si=MIS) == S["LIZARD_E_ALIGN"]
+
+
+def test_split_checks(lib):
+    """The split forward: its workspace size (0 where one pass fills the chip
+    or the sequence is short) and the workspace checks, before any launch."""
+    long_ = params(B=1, H=32, L=32768, window=64)
+    need = lib.lizard_attn_fwd_split_workspace_size(ctypes.byref(long_))
+    # 4 segments of 128 chunks: states, totals, per-chunk sums, transposed incoming states
+    assert need == 32 * 4 * 128 * 128 * 4 + 32 * 4 * 128 * 4 + 32 * 512 * 128 * 4 + 32 * 4 * 128 * 128 * 2
+    assert lib.lizard_attn_fwd_split_workspace_size(ctypes.byref(params(B=4, H=32, L=4096))) == 0
+    assert lib.lizard_attn_fwd_split_workspace_size(ctypes.byref(params(B=1, H=1, L=960))) == 0   # 15 chunks
+    assert lib.lizard_attn_fwd_split_workspace_size(ctypes.byref(params(B=1, H=1, L=1024))) > 0
+    assert lib.lizard_attn_fwd_split_workspace_size(ctypes.byref(params(dtype=7))) == 0
+    f = lambda p, ws, nb, lg=FAKE, xg=None: lib.lizard_attn_fwd_split(
+        ctypes.byref(p), FAKE, FAKE, FAKE, lg, xg, FAKE, None, None, None, 0, FAKE, None, None, None, ws, nb, None)
+    assert f(long_, FAKE, need - 1) == S["LIZARD_E_WORKSPACE"]
+    assert f(long_, None, need) == S["LIZARD_E_WORKSPACE"]
+    assert f(long_, MIS, need) == S["LIZARD_E_ALIGN"]
+    assert f(long_, FAKE, need, lg=FAKE, xg=FAKE) == S["LIZARD_E_SHAPE"]
+    assert f(params(B=0), None, 0) == 0
