@@ -683,12 +683,12 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
 
         // Qe = q * 2^beta of this lane's query (B operand)
         frag qe[NF];
+        uint4 raw[QV];        // wide span: the raw query, this lane's k-quarter
         if (!pairwise) {
           const T* ep = sQe + (16 * QB + m) * Lay::LDK + g * (D / 4);
   #pragma unroll
           for (int e = 0; e < NF; ++e) qe[e] = M::load(ep + e * M::KPL);
         } else {
-          uint4 raw[QV];
           const T* qp = qg + (size_t)(tme < L ? tme : 0) * D + g * (D / 4);
   #pragma unroll
           for (int e = 0; e < QV; ++e) raw[e] = tme < L ? ld16(qp + e * EPV) : make_uint4(0, 0, 0, 0);
@@ -704,34 +704,76 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
 
         // ---- intra-chunk gated scores A^T[s][t], key blocks J <= QB ----
         f32x4 ai[QB + 1];
+        if (!pairwise) {
   #pragma unroll
-        for (int J = 0; J <= QB; ++J) {
-          ai[J] = zero4();
-          if (!pairwise) {
+          for (int J = 0; J <= QB; ++J) {
+            ai[J] = zero4();
             const T* kp = sKp + (16 * J + m) * Lay::LDK + g * (D / 4);
   #pragma unroll
             for (int e = 0; e < NF; ++e) ai[J] = M::mma(M::load(kp + e * M::KPL), qe[e], ai[J]);
-          } else {
-            // pairwise gate products in fp32 (a decay span too wide to factorise)
-            const T* qrow = qg + (size_t)(tme < L ? tme : 0) * D;
-            const float* bt = sBeta + (16 * QB + m) * Lay::LDE;
+          }
+        } else {
+          // a decay span too wide to factorise over the chunk: factorised
+          // per 16-key block J at a reference point b instead, A^T[s][t] =
+          // (k_s 2^{beta_b - beta_s}) . (q_t 2^{beta_t - beta_b}).  For J < QB,
+          // b = the last key of J, which lies between every key of J and every
+          // query of QB, so both factors are <= 1.
+          const float* bt = sBeta + (16 * QB + m) * Lay::LDE + g * (D / 4);
+          auto factored = [&](int J, const float* bb) __attribute__((always_inline)) -> f32x4 {
+            f32x4 acc_j = zero4();
+            const float* bs = sBeta + (16 * J + m) * Lay::LDE + g * (D / 4);
+            const T* kr = sK + (kcur + 16 * J + m) * Lay::LDK + g * (D / 4);
   #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int ks = 16 * J + 4 * g + r;
-              float sum = 0.f;
-              if (ks <= 16 * QB + m && tme < L) {
-                const T* krow = sK + (kcur + ks) * Lay::LDK;
-                const float* bs = sBeta + ks * Lay::LDE;
-                for (int i = 0; i < D; ++i) sum += to_f32(qrow[i]) * to_f32(krow[i]) * exp_2(bt[i] - bs[i]);
+            for (int e = 0; e < NF; ++e) {
+              float tq[M::KPL], tk[M::KPL];
+  #pragma unroll
+              for (int u = 0; u < M::KPL; ++u) {
+                const int x = e * M::KPL + u;
+                const float rb = bb ? bb[x] : 0.f;
+                tq[u] = elem_f32<T>(raw, x) * exp_2(bt[x] - rb);
+                tk[u] = to_f32(kr[x]) * exp_2(rb - bs[x]);
               }
-              ai[J][r] = sum;
+              acc_j = M::mma(M::pack(tk), M::pack(tq), acc_j);
+              __builtin_amdgcn_sched_barrier(0);   // one k-step's operands live at a time
+            }
+            return acc_j;
+          };
+  #pragma unroll
+          for (int J = 0; J < QB; ++J) ai[J] = factored(J, sBeta + (16 * J + 15) * Lay::LDE + g * (D / 4));
+          // the diagonal block: factorised at the block start a while the
+          // block's own span stays within the factorisable range (then
+          // 2^{beta_a - beta_s} <= 2^span), else every pair (t, s) in fp32,
+          // each lane over its k-quarter, summed across the quarters
+          // (the block's span per dimension: minus its two 8-row partial totals)
+          bool wide_b = false;
+  #pragma unroll
+          for (int dd = 0; dd < D / 64; ++dd) {
+            const int i = (D / 64) * (threadIdx.x & 63) + dd;
+            wide_b |= -(sTotC[2 * QB * D + i] + sTotC[(2 * QB + 1) * D + i]) > kMaxSpanLog2;
+          }
+          if (!__any(wide_b)) {
+            ai[QB] = factored(QB, QB > 0 ? sBeta + (16 * QB - 1) * Lay::LDE + g * (D / 4) : nullptr);
+          } else {
+            ai[QB] = zero4();
+  #pragma unroll 1
+            for (int s4 = 0; s4 < 4; ++s4) {
+  #pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int s16 = 4 * s4 + r;
+                const T* kr = sK + (kcur + 16 * QB + s16) * Lay::LDK + g * (D / 4);
+                const float* bs = sBeta + (16 * QB + s16) * Lay::LDE + g * (D / 4);
+                float sum = 0.f;
+  #pragma unroll
+                for (int x = 0; x < D / 4; ++x)
+                  sum = fmaf(elem_f32<T>(raw, x) * to_f32(kr[x]), exp_2(fminf(bt[x] - bs[x], 0.f)), sum);
+                sum = xgroup_sum(sum);
+                ai[QB][r] = s4 == g ? sum : ai[QB][r];     // lane group g keeps keys 4g .. 4g + 3
+              }
             }
           }
-          if (J == QB) {
-  #pragma unroll
-            for (int r = 0; r < 4; ++r) ai[J][r] = 4 * g + r <= m ? ai[J][r] : 0.f;
-          }
         }
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) ai[QB][r] = 4 * g + r <= m ? ai[QB][r] : 0.f;
 
         if constexpr (Lay::STAGE_A) {
           // A[t][s] of this block into its own staging rows (keys of blocks

@@ -64,13 +64,19 @@ def test_window_and_sinks(gpu_lib, window, n_meta):
 
 
 @pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
-@pytest.mark.parametrize("variant", ["sharp", "slow_gate", "fast_gate", "hard_reset", "outliers"])
+@pytest.mark.parametrize("variant", ["sharp", "slow_gate", "fast_gate", "hard_reset", "outliers", "wide_chunk",
+                                     "wide_mixed"])
 def test_variants(gpu_lib, dtype, d, variant):
+    # wide_chunk: every chunk's decay span is too wide to factorise over the
+    # chunk (about 2^-121 over 64 tokens) while each 16-token block's is not;
+    # wide_mixed: both kinds of block in one chunk
     kw = {
         "sharp": dict(qk_sd=1.0, meta_sd=1.0),
         "slow_gate": dict(gate_mu=8.0, gate_sd=1.0),
         "fast_gate": dict(gate_mu=-2.0, gate_sd=4.0),
         "hard_reset": dict(hard_reset_frac=0.01, gate_mu=2.0, gate_sd=2.0),
+        "wide_chunk": dict(gate_mu=-1.0, gate_sd=0.5),
+        "wide_mixed": dict(gate_mu=0.0, gate_sd=3.0),
         "outliers": dict(),
     }[variant]
     x = si.custom_inputs(3, 2, 2, 256, d, 4, dtype, **kw)
