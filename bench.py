@@ -160,6 +160,45 @@ def bench_fp32_ablation(sqa, si, steps, warmup):
     return res
 
 
+def bench_long_ctx(sqa, si, steps, warmup):
+    """Long-context prefill (B=1, H=32, L=32768, gates N(2,2)): the one-pass
+    forward runs one workgroup per (head, value slice), 64 for the whole GPU;
+    lizard_attn_fwd_split cuts each sequence into segments run side by side
+    (workspace allocated once, outside the timed region)."""
+    import numpy as np
+    import torch
+
+    w = si.WORKLOADS["long_ctx_32k_bf16"]
+    st = si.storage_inputs(w)
+    x = {k: (torch.from_numpy(v.view(np.int16)).view(torch.bfloat16) if v.dtype == np.uint16 else
+             torch.from_numpy(v)).cuda() for k, v in st.items()}
+    del st
+    out = {"y": torch.empty_like(x["q"])}
+    need = sqa.lizard_attn_fwd_split_workspace_size(w.B, w.H, w.L, w.d, window=w.window, n_meta=w.n_meta)
+    ws = torch.empty(max(need, 1), device="cuda", dtype=torch.uint8)
+
+    def split():
+        sqa.lizard_attn_fwd_split(x["q"], x["k"], x["v"], x["meta_k"], log_g=x["log_g"], window=w.window,
+                                  alpha=w.alpha, workspace=ws, out=out)
+
+    def one_pass():
+        sqa.lizard_attn_fwd(x["q"], x["k"], x["v"], x["log_g"], x["meta_k"], window=w.window, alpha=w.alpha, out=out)
+
+    n = max(5, steps // 5)
+    ms_split = time_region(split, n, max(10, warmup // 5))
+    ms_one = time_region(one_pass, n, max(10, warmup // 5))
+    alg_bytes = w.B * w.H * w.L * fwd_bytes_per_head_token(w.d)
+    del x, out, ws
+    torch.cuda.empty_cache()
+    res = {"workload": "long_ctx_32k_bf16 (B=1, H=32, L=32768, d=128, gates N(2,2))", "steps": n}
+    for name, ms in (("split", ms_split), ("one_pass", ms_one)):
+        gbs = alg_bytes / (ms * 1e-3) / 1e9
+        res[name] = {"ms": round(ms, 5), "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1), "gbps": round(gbs, 1),
+                     "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    res["split_over_one_pass"] = round(ms_one / ms_split, 3)
+    return res
+
+
 def bench_decode(sqa, si, reps=3):
     """1024 back-to-back steps after a 2048-token prefill (prefill untimed)."""
     import numpy as np
@@ -407,7 +446,9 @@ def main():
     ap.add_argument("--no-logit", action="store_true")
     ap.add_argument("--no-ablation", action="store_true")
     ap.add_argument("--no-stage1", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "decode", "bwd", "fwd_logit", "bwd_logit", "fp32_ablation", "stage1"],
+    ap.add_argument("--no-long-ctx", action="store_true")
+    ap.add_argument("--only", choices=["fwd", "decode", "bwd", "fwd_logit", "bwd_logit", "fp32_ablation", "stage1",
+                                       "long_ctx"],
                     default=None,
                     help="run one leg only (for profiler runs); prints that leg's record")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -452,6 +493,9 @@ def main():
     if args.only == "stage1":
         print(json.dumps(bench_stage1(sqa, si)), flush=True)
         return
+    if args.only == "long_ctx":
+        print(json.dumps(bench_long_ctx(sqa, si, args.steps, args.warmup)), flush=True)
+        return
     if args.only == "fp32_ablation":
         print(json.dumps(bench_fp32_ablation(sqa, si, args.steps, args.warmup)), flush=True)
         return
@@ -494,6 +538,9 @@ def main():
     if not args.no_ablation:
         rec["fp32_ablation"] = bench_fp32_ablation(sqa, si, args.steps, args.warmup)
         print("# fp32 ablation done", file=sys.stderr, flush=True)
+    if not args.no_long_ctx:
+        rec["long_ctx"] = bench_long_ctx(sqa, si, args.steps, args.warmup)
+        print("# long_ctx done", file=sys.stderr, flush=True)
     if not args.no_decode:
         rec["decode"] = bench_decode(sqa, si)
         print("# decode done", file=sys.stderr, flush=True)

@@ -977,6 +977,7 @@ __global__ __launch_bounds__(256) void fwd_seg_scan_kernel(FwdArgs a) {
 // 2^-128 of its size (gates are at most one, so later chunks decay further):
 // such chunks are left as they are.
 constexpr float kSegSkipLog2 = -128.0f;
+constexpr int kFixChunks = 2;           // chunks per workgroup of the output correction
 
 template <typename T, int D>
 struct FixLayout {
@@ -996,14 +997,16 @@ struct FixLayout {
 };
 
 // y_t += (q_t * 2^{R_c + beta_t})^T S_in(s) for the chunks of segments
-// s >= 1.  Grid (chunk groups of FG, nseg - 1, BH); 4 wavefronts.  Thread
+// s >= 1.  Grid (nseg - 1, BH, chunk groups of FG): the groups at the start
+// of every segment, where the carried state matters most, are dispatched
+// first.  4 wavefronts.  Thread
 // (tg, dg) loads tokens NTT*tg .. of the chunk in dimensions 8dg .. 8dg+7
 // (16-byte vectors, all issued at the chunk start); wavefront w computes the
 // chunk's rows 16w .. 16w+15 on the matrix cores.
 template <typename T, int D, bool LOGIT>
 __global__ __launch_bounds__(256, 2) void fwd_seg_fix_kernel(FwdArgs a) {
   typedef FixLayout<T, D> Lay;
-  constexpr int FG = 4;                  // chunks per workgroup
+  constexpr int FG = kFixChunks;         // chunks per workgroup
   constexpr int DG = Lay::DG, NTT = Lay::NTT;
   constexpr int VT = 8 * (int)sizeof(T) / 16;    // 16-byte vectors per 8 elements of T
   extern __shared__ __align__(16) unsigned char smem[];
@@ -1013,22 +1016,20 @@ __global__ __launch_bounds__(256, 2) void fwd_seg_fix_kernel(FwdArgs a) {
   float* sP = reinterpret_cast<float*>(smem + Lay::OFF_P);
   float* sW = reinterpret_cast<float*>(smem + Lay::OFF_W);
 
-  const int bh = blockIdx.z;
-  const int sg = blockIdx.y + 1;
+  const int sg = blockIdx.x + 1;
+  const int bh = blockIdx.y;
   const int L = a.L;
   const int nc = (L + 63) / 64;
   int c_lo, c_hi;
   segment_chunks(sg, a.nseg, nc, c_lo, c_hi);
-  const int cb = c_lo + blockIdx.x * FG;
-  if (cb >= c_hi) return;
-  const int ce = cb + FG < c_hi ? cb + FG : c_hi;
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
   const int dg = tid % DG, tg = tid / DG;
   const int d0 = 8 * dg;
 
-  // the incoming state, S_in^T rows, 16-byte vectors
-  {
+  // the incoming state, S_in^T rows, 16-byte vectors (loaded with the first
+  // chunk that needs it)
+  auto load_state = [&]() __attribute__((always_inline)) {
     const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.seg_in_t) +
                                                       ((size_t)bh * a.nseg + sg) * D * D);
     constexpr int VPR = D * (int)sizeof(T) / 16;     // vectors per row
@@ -1041,12 +1042,17 @@ __global__ __launch_bounds__(256, 2) void fwd_seg_fix_kernel(FwdArgs a) {
       const int v = tid + 256 * e;
       *reinterpret_cast<uint4*>(sSt + (v / VPR) * Lay::LDS + (v % VPR) * (16 / sizeof(T))) = buf[e];
     }
-  }
+  };
 
   const T* qg = reinterpret_cast<const T*>(a.q) + (size_t)bh * L * D + d0;
   T* yg = reinterpret_cast<T*>(a.y) + (size_t)bh * L * D + d0;
   const float* lgg = a.log_g ? a.log_g + (size_t)bh * L * D + d0 : nullptr;
   const T* xg = LOGIT ? reinterpret_cast<const T*>(a.gate_logit) + (size_t)bh * L * D + d0 : nullptr;
+  // chunk groups blockIdx.z, blockIdx.z + gridDim.z, ...; the decay only
+  // grows along a segment, so the first chunk below the cut ends the walk
+  bool have_state = false;
+  for (int cb = c_lo + blockIdx.z * FG; cb < c_hi; cb += gridDim.z * FG) {
+  const int ce = cb + FG < c_hi ? cb + FG : c_hi;
   for (int c = cb; c < ce; ++c) {
     const int t0 = c * 64 + NTT * tg;             // this thread's first token
     // ---- every global load of the chunk first (rows past L: row L - 1, masked below) ----
@@ -1105,7 +1111,11 @@ __global__ __launch_bounds__(256, 2) void fwd_seg_fix_kernel(FwdArgs a) {
     if (l == 0) sW[w] = mx;
     __syncthreads();
     const float cmax = fmaxf(fmaxf(sW[0], sW[1]), fmaxf(sW[2], sW[3]));
-    if (cmax < kSegSkipLog2) break;              // uniform: this and every later chunk of the group
+    if (cmax < kSegSkipLog2) return;             // uniform: this and every later chunk of the segment
+    if (!have_state) {
+      load_state();                               // read after the barrier below
+      have_state = true;
+    }
     // ---- scaled queries into sQs ----
     {
       float off[8];
@@ -1159,6 +1169,7 @@ __global__ __launch_bounds__(256, 2) void fwd_seg_fix_kernel(FwdArgs a) {
     }
     __syncthreads();                              // sC / sP reused by the next chunk
   }
+  }
 }
 
 template <typename T, int D, int DV, bool STATES, bool LOGIT, bool SEG>
@@ -1188,8 +1199,9 @@ static hipError_t launch_seg_finish(const FwdArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   const int nc = (a.L + 63) / 64;
   const int longest = (nc + a.nseg - 1) / a.nseg;
-  hipLaunchKernelGGL((fwd_seg_fix_kernel<T, D, LOGIT>), dim3((longest + 3) / 4, a.nseg - 1, a.BH), dim3(256),
-                     Lay::TOTAL, st, a);
+  const int groups = (longest + kFixChunks - 1) / kFixChunks;
+  hipLaunchKernelGGL((fwd_seg_fix_kernel<T, D, LOGIT>), dim3(a.nseg - 1, a.BH, groups < 2048 ? groups : 2048),
+                     dim3(256), Lay::TOTAL, st, a);
   return hipGetLastError();
 }
 
