@@ -101,13 +101,14 @@ lizard_status_t attn_fwd(const lizard_params_t* p, const void* q, const void* k,
   a.scale_log2 = scale_of(p) * 1.4426950408889634f;
   a.nseg = nseg;
   if (nseg > 1) {
-    size_t off[3];
+    size_t off[4];
     split_workspace(p, nseg, off);
     char* w = static_cast<char*>(workspace);
     a.seg_state = reinterpret_cast<float*>(w);
     a.seg_total = reinterpret_cast<float*>(w + off[0]);
     a.chunk_cum = reinterpret_cast<float*>(w + off[1]);
     a.seg_in_t = w + off[2];
+    a.seg_live = reinterpret_cast<int*>(w + off[3]);
   }
   return launched(lizard::launch_fwd(a, bf, p->dk, static_cast<hipStream_t>(stream)));
 }

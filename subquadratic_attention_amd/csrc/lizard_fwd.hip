@@ -132,6 +132,12 @@ __device__ __forceinline__ int opaque(int x) {
 // leaves a factor 2^36 of headroom below the float / bfloat16 maximum.
 constexpr float kMaxSpanLog2 = 92.0f;
 
+// Split sequences: below this log2 decay from a segment's start the state
+// carried into the segment adds under 2^-128 of its size to an output (gates
+// are at most one, so every later chunk decays further); the output
+// correction stops at the first such chunk.
+constexpr float kSegSkipLog2 = -128.0f;
+
 template <typename T, int D, int DV, bool STATES, bool LOGIT, bool SEG>
 __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
   typedef FwdLayout<T, D, DV> Lay;
@@ -282,6 +288,7 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
     uint4 qraw[QV];       // softmax wavefronts: raw q of row 16I + m, the lane's k-quarter
     f32x4 og[NCT];        // gate wavefronts: gated output of the block, carried over a barrier
     float rcum[DPL] = {};  // split sequences: log2-gate sum from the segment start (one gate wavefront)
+    int live_end = c_hi;   // ... and the first chunk whose decay from the segment start is below the cut
 
     auto load_rows = [&](int c, bool full) __attribute__((always_inline)) {
       const int t0 = c * C;
@@ -495,11 +502,15 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
       if constexpr (SEG && GATE && QB == 0) {
         // a split sequence: the decay from the segment start to this chunk's
         // start, and its running sum (the exponents of eB)
+        float mx = rcum[0];
   #pragma unroll
         for (int dd = 0; dd < DPL; ++dd) {
           if (split == 0) a.chunk_cum[((size_t)bh * nc + cc) * D + DPL * l + dd] = rcum[dd];
+          mx = fmaxf(mx, rcum[dd]);
           rcum[dd] += pairwise ? Bt[dd] : Bt[dd] * kLog2e;
         }
+        // this wavefront's lanes cover all D dimensions: a uniform value
+        if (live_end == c_hi && wave_max(mx) < kSegSkipLog2) live_end = cc;
       }
       // raw keys into the ring
   #pragma unroll
@@ -897,6 +908,7 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
   #pragma unroll
           for (int dd = 0; dd < DPL; ++dd)
             if (split == 0) a.seg_total[((size_t)bh * a.nseg + seg) * D + DPL * l + dd] = rcum[dd];
+          if (split == 0 && l == 0) a.seg_live[(size_t)bh * a.nseg + seg] = live_end;
         }
       }
     } else if (GATE && a.state_out) {
@@ -973,10 +985,6 @@ __global__ __launch_bounds__(256) void fwd_seg_scan_kernel(FwdArgs a) {
   if (a.state_out) *reinterpret_cast<float4*>(a.state_out + (size_t)bh * D * D + (size_t)i * D + j) = S;
 }
 
-// Below this log2 decay the carried state's share of an output is under
-// 2^-128 of its size (gates are at most one, so later chunks decay further):
-// such chunks are left as they are.
-constexpr float kSegSkipLog2 = -128.0f;
 constexpr int kFixChunks = 2;           // chunks per workgroup of the output correction
 
 template <typename T, int D>
@@ -992,8 +1000,7 @@ struct FixLayout {
   static constexpr int OFF_S = 0;
   static constexpr int OFF_Q = OFF_S + D * LDS * (int)sizeof(T);
   static constexpr int OFF_P = OFF_Q + QC;                // token groups' gate totals [TG][D] float
-  static constexpr int OFF_W = OFF_P + TG * D * 4;        // per-wavefront maxima [4] float
-  static constexpr int TOTAL = OFF_W + 16;
+  static constexpr int TOTAL = OFF_P + TG * D * 4;
 };
 
 // y_t += (q_t * 2^{R_c + beta_t})^T S_in(s) for the chunks of segments
@@ -1014,7 +1021,6 @@ __global__ __launch_bounds__(256, 2) void fwd_seg_fix_kernel(FwdArgs a) {
   T* sQs = reinterpret_cast<T*>(smem + Lay::OFF_Q);
   float* sC = reinterpret_cast<float*>(smem + Lay::OFF_Q);
   float* sP = reinterpret_cast<float*>(smem + Lay::OFF_P);
-  float* sW = reinterpret_cast<float*>(smem + Lay::OFF_W);
 
   const int sg = blockIdx.x + 1;
   const int bh = blockIdx.y;
@@ -1027,9 +1033,18 @@ __global__ __launch_bounds__(256, 2) void fwd_seg_fix_kernel(FwdArgs a) {
   const int dg = tid % DG, tg = tid / DG;
   const int d0 = 8 * dg;
 
-  // the incoming state, S_in^T rows, 16-byte vectors (loaded with the first
-  // chunk that needs it)
-  auto load_state = [&]() __attribute__((always_inline)) {
+
+  const T* qg = reinterpret_cast<const T*>(a.q) + (size_t)bh * L * D + d0;
+  T* yg = reinterpret_cast<T*>(a.y) + (size_t)bh * L * D + d0;
+  const float* lgg = a.log_g ? a.log_g + (size_t)bh * L * D + d0 : nullptr;
+  const T* xg = LOGIT ? reinterpret_cast<const T*>(a.gate_logit) + (size_t)bh * L * D + d0 : nullptr;
+  // chunk groups blockIdx.z, blockIdx.z + gridDim.z, ... up to the first
+  // chunk below the cut (found by the forward pass)
+  const int c_end = a.seg_live[(size_t)bh * a.nseg + sg];
+  if (c_lo + (int)blockIdx.z * FG >= c_end) return;
+  // the incoming state, S_in^T rows, 16-byte vectors (read after the first
+  // chunk's barriers)
+  {
     const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.seg_in_t) +
                                                       ((size_t)bh * a.nseg + sg) * D * D);
     constexpr int VPR = D * (int)sizeof(T) / 16;     // vectors per row
@@ -1042,133 +1057,114 @@ __global__ __launch_bounds__(256, 2) void fwd_seg_fix_kernel(FwdArgs a) {
       const int v = tid + 256 * e;
       *reinterpret_cast<uint4*>(sSt + (v / VPR) * Lay::LDS + (v % VPR) * (16 / sizeof(T))) = buf[e];
     }
-  };
-
-  const T* qg = reinterpret_cast<const T*>(a.q) + (size_t)bh * L * D + d0;
-  T* yg = reinterpret_cast<T*>(a.y) + (size_t)bh * L * D + d0;
-  const float* lgg = a.log_g ? a.log_g + (size_t)bh * L * D + d0 : nullptr;
-  const T* xg = LOGIT ? reinterpret_cast<const T*>(a.gate_logit) + (size_t)bh * L * D + d0 : nullptr;
-  // chunk groups blockIdx.z, blockIdx.z + gridDim.z, ...; the decay only
-  // grows along a segment, so the first chunk below the cut ends the walk
-  bool have_state = false;
-  for (int cb = c_lo + blockIdx.z * FG; cb < c_hi; cb += gridDim.z * FG) {
-  const int ce = cb + FG < c_hi ? cb + FG : c_hi;
-  for (int c = cb; c < ce; ++c) {
-    const int t0 = c * 64 + NTT * tg;             // this thread's first token
-    // ---- every global load of the chunk first (rows past L: row L - 1, masked below) ----
-    uint4 qv[NTT][VT], yv[NTT][VT], gv[NTT][LOGIT ? VT : 2];
-  #pragma unroll
-    for (int r = 0; r < NTT; ++r) {
-      const size_t row = (size_t)(t0 + r < L ? t0 + r : L - 1) * D;
-  #pragma unroll
-      for (int e = 0; e < VT; ++e) {
-        qv[r][e] = ld16(qg + row + e * (16 / sizeof(T)));
-        yv[r][e] = ld16(yg + row + e * (16 / sizeof(T)));
-      }
-      if constexpr (LOGIT) {
-  #pragma unroll
-        for (int e = 0; e < VT; ++e) gv[r][e] = ld16(xg + row + e * (16 / sizeof(T)));
-      } else {
-        gv[r][0] = ld16(lgg + row);
-        gv[r][1] = ld16(lgg + row + 4);
-      }
-    }
-    float Rv[8];
-    {
-      const float* rp = a.chunk_cum + ((size_t)bh * nc + c) * D + d0;
-      const float4 r0 = *reinterpret_cast<const float4*>(rp), r1 = *reinterpret_cast<const float4*>(rp + 4);
-      Rv[0] = r0.x; Rv[1] = r0.y; Rv[2] = r0.z; Rv[3] = r0.w;
-      Rv[4] = r1.x; Rv[5] = r1.y; Rv[6] = r1.z; Rv[7] = r1.w;
-    }
-    // ---- log2-gate prefix over the thread's tokens, totals per token group ----
-    float lb[NTT][8];
-  #pragma unroll
-    for (int r = 0; r < NTT; ++r) {
-      if constexpr (LOGIT) {
-  #pragma unroll
-        for (int e = 0; e < VT; ++e) unpack16<T>(gv[r][e], lb[r] + e * (16 / sizeof(T)));
-  #pragma unroll
-        for (int x = 0; x < 8; ++x) lb[r][x] = log_sigmoid(lb[r][x]);
-      } else {
-        unpack16<float>(gv[r][0], lb[r]);
-        unpack16<float>(gv[r][1], lb[r] + 4);
-      }
-    }
-  #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      float run = 0.f;
-  #pragma unroll
-      for (int r = 0; r < NTT; ++r) {
-        run += t0 + r < L ? log2_gate(lb[r][x]) : 0.f;
-        lb[r][x] = run;
-      }
-      sP[tg * D + d0 + x] = run;
-    }
-    float mx = Rv[0];
-  #pragma unroll
-    for (int x = 1; x < 8; ++x) mx = fmaxf(mx, Rv[x]);
-    mx = wave_max(mx);
-    if (l == 0) sW[w] = mx;
-    __syncthreads();
-    const float cmax = fmaxf(fmaxf(sW[0], sW[1]), fmaxf(sW[2], sW[3]));
-    if (cmax < kSegSkipLog2) return;             // uniform: this and every later chunk of the segment
-    if (!have_state) {
-      load_state();                               // read after the barrier below
-      have_state = true;
-    }
-    // ---- scaled queries into sQs ----
-    {
-      float off[8];
-  #pragma unroll
-      for (int x = 0; x < 8; ++x) off[x] = Rv[x];
-      for (int gg = 0; gg < tg; ++gg) {
-        const float4 p0 = *reinterpret_cast<const float4*>(sP + gg * D + d0);
-        const float4 p1 = *reinterpret_cast<const float4*>(sP + gg * D + d0 + 4);
-        off[0] += p0.x; off[1] += p0.y; off[2] += p0.z; off[3] += p0.w;
-        off[4] += p1.x; off[5] += p1.y; off[6] += p1.z; off[7] += p1.w;
-      }
-  #pragma unroll
-      for (int r = 0; r < NTT; ++r) {
-        float qf[8];
-  #pragma unroll
-        for (int e = 0; e < VT; ++e) unpack16<T>(qv[r][e], qf + e * (16 / sizeof(T)));
-        const bool ok = t0 + r < L;
-  #pragma unroll
-        for (int x = 0; x < 8; ++x) qf[x] = ok ? qf[x] * exp_2(off[x] + lb[r][x]) : 0.f;
-        store_pack<T, 8>(sQs + (NTT * tg + r) * Lay::LDQ + d0, qf);
-      }
-    }
-    __syncthreads();
-    // ---- the correction: rows 16w + 4g + r, columns 16ct + m ----
-    f32x4 cv[D / 16];
-  #pragma unroll
-    for (int ct = 0; ct < D / 16; ++ct)
-      cv[ct] = mma_rows<T, D>(zero4(), sQs + (16 * w + m) * Lay::LDQ + g * (D / 4),
-                              sSt + (16 * ct + m) * Lay::LDS + g * (D / 4));
-    __syncthreads();                              // sC overlays sQs
-  #pragma unroll
-    for (int ct = 0; ct < D / 16; ++ct)
-  #pragma unroll
-      for (int r = 0; r < 4; ++r) sC[(16 * w + 4 * g + r) * Lay::LDC + 16 * ct + m] = cv[ct][r];
-    __syncthreads();
-    // ---- y += correction ----
-  #pragma unroll
-    for (int r = 0; r < NTT; ++r) {
-      if (t0 + r >= L) continue;
-      float yf[8];
-  #pragma unroll
-      for (int e = 0; e < VT; ++e) unpack16<T>(yv[r][e], yf + e * (16 / sizeof(T)));
-      const float* cp = sC + (NTT * tg + r) * Lay::LDC + d0;
-      const float4 c0 = *reinterpret_cast<const float4*>(cp), c1 = *reinterpret_cast<const float4*>(cp + 4);
-      yf[0] += c0.x; yf[1] += c0.y; yf[2] += c0.z; yf[3] += c0.w;
-      yf[4] += c1.x; yf[5] += c1.y; yf[6] += c1.z; yf[7] += c1.w;
-      uint4 o[VT];
-      store_pack<T, 8>(reinterpret_cast<T*>(o), yf);
-  #pragma unroll
-      for (int e = 0; e < VT; ++e) st16(yg + (size_t)(t0 + r) * D + e * (16 / sizeof(T)), o[e]);
-    }
-    __syncthreads();                              // sC / sP reused by the next chunk
   }
+  for (int cb = c_lo + blockIdx.z * FG; cb < c_end; cb += gridDim.z * FG) {
+    const int ce = cb + FG < c_end ? cb + FG : c_end;
+    for (int c = cb; c < ce; ++c) {
+      const int t0 = c * 64 + NTT * tg;             // this thread's first token
+      // ---- every global load of the chunk first (rows past L: row L - 1, masked below) ----
+      uint4 qv[NTT][VT], yv[NTT][VT], gv[NTT][LOGIT ? VT : 2];
+  #pragma unroll
+      for (int r = 0; r < NTT; ++r) {
+        const size_t row = (size_t)(t0 + r < L ? t0 + r : L - 1) * D;
+  #pragma unroll
+        for (int e = 0; e < VT; ++e) {
+          qv[r][e] = ld16(qg + row + e * (16 / sizeof(T)));
+          yv[r][e] = ld16(yg + row + e * (16 / sizeof(T)));
+        }
+        if constexpr (LOGIT) {
+  #pragma unroll
+          for (int e = 0; e < VT; ++e) gv[r][e] = ld16(xg + row + e * (16 / sizeof(T)));
+        } else {
+          gv[r][0] = ld16(lgg + row);
+          gv[r][1] = ld16(lgg + row + 4);
+        }
+      }
+      float Rv[8];
+      {
+        const float* rp = a.chunk_cum + ((size_t)bh * nc + c) * D + d0;
+        const float4 r0 = *reinterpret_cast<const float4*>(rp), r1 = *reinterpret_cast<const float4*>(rp + 4);
+        Rv[0] = r0.x; Rv[1] = r0.y; Rv[2] = r0.z; Rv[3] = r0.w;
+        Rv[4] = r1.x; Rv[5] = r1.y; Rv[6] = r1.z; Rv[7] = r1.w;
+      }
+      // ---- log2-gate prefix over the thread's tokens, totals per token group ----
+      float lb[NTT][8];
+  #pragma unroll
+      for (int r = 0; r < NTT; ++r) {
+        if constexpr (LOGIT) {
+  #pragma unroll
+          for (int e = 0; e < VT; ++e) unpack16<T>(gv[r][e], lb[r] + e * (16 / sizeof(T)));
+  #pragma unroll
+          for (int x = 0; x < 8; ++x) lb[r][x] = log_sigmoid(lb[r][x]);
+        } else {
+          unpack16<float>(gv[r][0], lb[r]);
+          unpack16<float>(gv[r][1], lb[r] + 4);
+        }
+      }
+  #pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        float run = 0.f;
+  #pragma unroll
+        for (int r = 0; r < NTT; ++r) {
+          run += t0 + r < L ? log2_gate(lb[r][x]) : 0.f;
+          lb[r][x] = run;
+        }
+        sP[tg * D + d0 + x] = run;
+      }
+      __syncthreads();
+      // ---- scaled queries into sQs ----
+      {
+        float off[8];
+  #pragma unroll
+        for (int x = 0; x < 8; ++x) off[x] = Rv[x];
+        for (int gg = 0; gg < tg; ++gg) {
+          const float4 p0 = *reinterpret_cast<const float4*>(sP + gg * D + d0);
+          const float4 p1 = *reinterpret_cast<const float4*>(sP + gg * D + d0 + 4);
+          off[0] += p0.x; off[1] += p0.y; off[2] += p0.z; off[3] += p0.w;
+          off[4] += p1.x; off[5] += p1.y; off[6] += p1.z; off[7] += p1.w;
+        }
+  #pragma unroll
+        for (int r = 0; r < NTT; ++r) {
+          float qf[8];
+  #pragma unroll
+          for (int e = 0; e < VT; ++e) unpack16<T>(qv[r][e], qf + e * (16 / sizeof(T)));
+          const bool ok = t0 + r < L;
+  #pragma unroll
+          for (int x = 0; x < 8; ++x) qf[x] = ok ? qf[x] * exp_2(off[x] + lb[r][x]) : 0.f;
+          store_pack<T, 8>(sQs + (NTT * tg + r) * Lay::LDQ + d0, qf);
+        }
+      }
+      __syncthreads();
+      // ---- the correction: rows 16w + 4g + r, columns 16ct + m ----
+      f32x4 cv[D / 16];
+  #pragma unroll
+      for (int ct = 0; ct < D / 16; ++ct)
+        cv[ct] = mma_rows<T, D>(zero4(), sQs + (16 * w + m) * Lay::LDQ + g * (D / 4),
+                                sSt + (16 * ct + m) * Lay::LDS + g * (D / 4));
+      __syncthreads();                              // sC overlays sQs
+  #pragma unroll
+      for (int ct = 0; ct < D / 16; ++ct)
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) sC[(16 * w + 4 * g + r) * Lay::LDC + 16 * ct + m] = cv[ct][r];
+      __syncthreads();
+      // ---- y += correction ----
+  #pragma unroll
+      for (int r = 0; r < NTT; ++r) {
+        if (t0 + r >= L) continue;
+        float yf[8];
+  #pragma unroll
+        for (int e = 0; e < VT; ++e) unpack16<T>(yv[r][e], yf + e * (16 / sizeof(T)));
+        const float* cp = sC + (NTT * tg + r) * Lay::LDC + d0;
+        const float4 c0 = *reinterpret_cast<const float4*>(cp), c1 = *reinterpret_cast<const float4*>(cp + 4);
+        yf[0] += c0.x; yf[1] += c0.y; yf[2] += c0.z; yf[3] += c0.w;
+        yf[4] += c1.x; yf[5] += c1.y; yf[6] += c1.z; yf[7] += c1.w;
+        uint4 o[VT];
+        store_pack<T, 8>(reinterpret_cast<T*>(o), yf);
+  #pragma unroll
+        for (int e = 0; e < VT; ++e) st16(yg + (size_t)(t0 + r) * D + e * (16 / sizeof(T)), o[e]);
+      }
+      __syncthreads();                              // sC / sP reused by the next chunk
+    }
   }
 }
 

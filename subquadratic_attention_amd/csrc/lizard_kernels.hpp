@@ -34,6 +34,7 @@ struct FwdArgs {
   float* seg_total;        // [BH, nseg, D] float32: each segment's log2-gate total
   float* chunk_cum;        // [BH, nc, D] float32: log2-gate sum from the segment start to each chunk start
   void* seg_in_t;          // [BH, nseg, D, D] element type: S_in(s) transposed (s >= 1)
+  int* seg_live;           // [BH, nseg]: first chunk of each segment whose decay from its start is below the cut
   int BH, H, L, n_meta, window, nsplit;
   float alpha;
   float scale_log2;     // softmax scale * log2(e)
@@ -121,7 +122,8 @@ inline int fwd_segments(int BH, int nsplit, int L) {
 
 // Workspace of a split forward pass, in this order (each part 256-byte
 // aligned): segment states, segment gate totals, per-chunk gate sums, the
-// incoming states transposed in the element type of esize bytes.
+// incoming states transposed in the element type of esize bytes, each
+// segment's live chunk end.
 inline size_t fwd_split_workspace_bytes(int BH, int L, int D, int esize, int nseg, size_t* offsets = nullptr) {
   if (nseg <= 1) return 0;
   auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
@@ -129,12 +131,14 @@ inline size_t fwd_split_workspace_bytes(int BH, int L, int D, int esize, int nse
   const size_t o1 = al((size_t)BH * nseg * D * D * 4);
   const size_t o2 = o1 + al((size_t)BH * nseg * D * 4);
   const size_t o3 = o2 + al((size_t)BH * nc * D * 4);
+  const size_t o4 = o3 + al((size_t)BH * nseg * D * D * esize);
   if (offsets) {
     offsets[0] = o1;
     offsets[1] = o2;
     offsets[2] = o3;
+    offsets[3] = o4;
   }
-  return o3 + al((size_t)BH * nseg * D * D * esize);
+  return o4 + al((size_t)BH * nseg * 4);
 }
 hipError_t launch_decode(const DecodeArgs& a, int dtype_bf16, int D, hipStream_t st);
 size_t bwd_workspace_bytes(int dtype_bf16, int BH, int L, int D, int n_meta);

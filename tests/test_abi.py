@@ -219,8 +219,8 @@ def test_split_checks(lib):
     or the sequence is short) and the workspace checks, before any launch."""
     long_ = params(B=1, H=32, L=32768, window=64)
     need = lib.lizard_attn_fwd_split_workspace_size(ctypes.byref(long_))
-    # 4 segments of 128 chunks: states, totals, per-chunk sums, transposed incoming states
-    assert need == 32 * 4 * 128 * 128 * 4 + 32 * 4 * 128 * 4 + 32 * 512 * 128 * 4 + 32 * 4 * 128 * 128 * 2
+    # 4 segments of 128 chunks: states, totals, per-chunk sums, transposed incoming states, live ends
+    assert need == 32 * 4 * 128 * 128 * 4 + 32 * 4 * 128 * 4 + 32 * 512 * 128 * 4 + 32 * 4 * 128 * 128 * 2 + 512
     assert lib.lizard_attn_fwd_split_workspace_size(ctypes.byref(params(B=4, H=32, L=4096))) == 0
     assert lib.lizard_attn_fwd_split_workspace_size(ctypes.byref(params(B=1, H=1, L=960))) == 0   # 15 chunks
     assert lib.lizard_attn_fwd_split_workspace_size(ctypes.byref(params(B=1, H=1, L=1024))) > 0
