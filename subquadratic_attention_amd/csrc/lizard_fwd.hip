@@ -431,18 +431,42 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
       const int vj = tid % VRW, vs = tid / VRW;
       float Bt[DPL], off[DPL];
       offsets(sTot, off, Bt);
-      bool wide = false;
+      bool wide = false, wider = false;
   #pragma unroll
-      for (int dd = 0; dd < DPL; ++dd) wide |= -Bt[dd] * kLog2e > kMaxSpanLog2;
-      // every wavefront covers all D dims, so this ballot is the chunk's decision
-      const bool pairwise = __any(wide);
+      for (int dd = 0; dd < DPL; ++dd) {
+        wide |= -Bt[dd] * kLog2e > kMaxSpanLog2;
+        wider |= -Bt[dd] * kLog2e > 2.f * kMaxSpanLog2;
+      }
+      // every wavefront covers all D dims, so these ballots are the chunk's
+      // decision.  Spans up to twice the limit take the factorised path with
+      // each dimension's reference point moved from the chunk start to half
+      // its total r = B/2: then Qe = q 2^{beta - r} and Kp = k 2^{r - beta}
+      // are both within 2^{span/2}, and the readout takes 2^r into the state
+      // copy.
+      const bool pairwise = __any(wider);
+      const bool midref = !pairwise && __any(wide);
       float kh[DPL][8];
       float eB[DPL];
+      float rexp[DPL];    // 2^r (one unless midref)
       if (!pairwise) {
+        float ehr[DPL];   // 2^{B - r}: Kh = Kp 2^{B - r}
+        if (!midref) {
   #pragma unroll
-        for (int dd = 0; dd < DPL; ++dd) {
-          eB[dd] = exp_2(Bt[dd] * kLog2e);
-          off[dd] *= kLog2e;
+          for (int dd = 0; dd < DPL; ++dd) {
+            eB[dd] = exp_2(Bt[dd] * kLog2e);
+            ehr[dd] = eB[dd];
+            off[dd] *= kLog2e;
+          }
+        } else {
+  #pragma unroll
+          for (int dd = 0; dd < DPL; ++dd) {
+            const float B2 = Bt[dd] * kLog2e;
+            const float r = 0.5f * B2;
+            eB[dd] = exp_2(B2);
+            ehr[dd] = exp_2(B2 - r);
+            rexp[dd] = exp_2(r);
+            off[dd] = fmaf(off[dd], kLog2e, -r);
+          }
         }
   #pragma unroll
         for (int rr = 0; rr < 8; ++rr) {
@@ -452,7 +476,7 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
           for (int dd = 0; dd < DPL; ++dd) {
             const float beta = fmaf(loc[rr][dd], kLog2e, off[dd]);
             kp[dd] = elem32(kA[rr], dd) * exp_2(-beta);
-            kh[dd][rr] = kp[dd] * eB[dd];
+            kh[dd][rr] = kp[dd] * ehr[dd];
             qe[dd] = elem32(qA[rr], dd) * exp_2(beta);
           }
           if constexpr (DPL == 2) {
@@ -533,14 +557,35 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
       }
       if constexpr (GATE) {
         if constexpr (!STATES) {
-          // S_cc (rounded to the element type) for the readout: sSt[j][i], 4 rows i per write
+          // S_cc (rounded to the element type) for the readout: sSt[j][i], 4 rows i per write;
+          // row i scaled by 2^{r_i} when the reference point moved (2^r of
+          // dimension i sits in lane i / DPL)
+          if (!midref) {
   #pragma unroll
-          for (int rt = 0; rt < DPL; ++rt)
+            for (int rt = 0; rt < DPL; ++rt)
   #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-              const float sv[4] = {acc[rt][ct][0], acc[rt][ct][1], acc[rt][ct][2], acc[rt][ct][3]};
-              store_pack<T, 4>(sSt + (16 * ct + m_lane) * Lay::LDST + 16 * (DPL * I + rt) + 4 * g_lane, sv);
-            }
+              for (int ct = 0; ct < NCT; ++ct) {
+                const float sv[4] = {acc[rt][ct][0], acc[rt][ct][1], acc[rt][ct][2], acc[rt][ct][3]};
+                store_pack<T, 4>(sSt + (16 * ct + m_lane) * Lay::LDST + 16 * (DPL * I + rt) + 4 * g_lane, sv);
+              }
+          } else {
+            float rs[DPL][4];
+  #pragma unroll
+            for (int rt = 0; rt < DPL; ++rt)
+  #pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int i = 16 * (DPL * I + rt) + 4 * g_lane + r;
+                rs[rt][r] = __shfl(rexp[r % DPL], i / DPL, 64);
+              }
+  #pragma unroll
+            for (int rt = 0; rt < DPL; ++rt)
+  #pragma unroll
+              for (int ct = 0; ct < NCT; ++ct) {
+                const float sv[4] = {acc[rt][ct][0] * rs[rt][0], acc[rt][ct][1] * rs[rt][1],
+                                     acc[rt][ct][2] * rs[rt][2], acc[rt][ct][3] * rs[rt][3]};
+                store_pack<T, 4>(sSt + (16 * ct + m_lane) * Lay::LDST + 16 * (DPL * I + rt) + 4 * g_lane, sv);
+              }
+          }
         } else {
           // chunk-start state for the backward pass: S_cc[i][j], row-major
           const int ncs = (L + C - 1) / C;
