@@ -713,8 +713,8 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
   T* sKh = reinterpret_cast<T*>(smem + Lay::OFF_KH);    // Kh[s][i] = k 2^{B - beta}, row-major
   T* sQe = reinterpret_cast<T*>(smem + Lay::OFF_QE);    // Qe[t][i] = q 2^{beta}, row-major
   float* sTot = reinterpret_cast<float*>(smem + Lay::OFF_TOT);
-  float* sBx = reinterpret_cast<float*>(smem + Lay::OFF_BX);   // chunk total B (log2) per dim
-  float* sEB = reinterpret_cast<float*>(smem + Lay::OFF_EB);   // [0][i] = 2^B_i, [1][i] = 2^-B_i (fast path)
+  float* sBx = reinterpret_cast<float*>(smem + Lay::OFF_BX);   // pairwise: chunk total B (log2); else 2^r per dim
+  float* sEB = reinterpret_cast<float*>(smem + Lay::OFF_EB);   // fast path: [0][i] = 2^{B_i - r_i}, [1][i] = 2^{r_i - B_i}
 
   const int L = a.L, nc = (L + C - 1) / C;
   int bh, c;
@@ -816,30 +816,42 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
       Bt[dd] += v;
     }
   }
-  bool wide = false;
+  bool wide = false, wider = false;
 #pragma unroll
-  for (int dd = 0; dd < DPL; ++dd) wide |= -Bt[dd] > kMaxSpan;
-  const bool pairwise = __any(wide);
+  for (int dd = 0; dd < DPL; ++dd) {
+    wide |= -Bt[dd] > kMaxSpan;
+    wider |= -Bt[dd] > 2.f * kMaxSpan;
+  }
+  // spans up to twice the limit stay factorised with each dimension's
+  // reference point at half its chunk total r = B/2 (as in the forward
+  // pass): the stored prefixes are b - r, Qe = q 2^{b-r}, Kp = k 2^{r-b},
+  // and the epilogue restores 2^r on the inter-chunk dq term.  The key tile
+  // then holds Kp, from which Kh = Kp 2^{B-r} is derived: Kp stays within
+  // 2^{+-92}, while Kh may underflow where its true value is that small
+  // (Kp derived from an underflowed Kh would be lost)
+  const bool pairwise = __any(wider);
+  const bool midref = !pairwise && __any(wide);
   float kh[RPW][DPL], qer[RPW][DPL];
 #pragma unroll
   for (int dd = 0; dd < DPL; ++dd) {
     const int i = DPL * l + dd;
     float qe[RPW], kp[RPW];
     if (!pairwise) {
-      // every factor from one exponential per element and operand (Kh = Kp 2^B)
-      const float eB = exp_2(Bt[dd]);
+      // every factor from one exponential per element and operand (Kh = Kp 2^{B-r})
+      const float r = midref ? 0.5f * Bt[dd] : 0.f;
+      const float eB = exp_2(Bt[dd] - r);
 #pragma unroll
       for (int rr = 0; rr < RPW; ++rr) {
-        const float b = beta[rr][dd] + off[dd];
+        const float b = beta[rr][dd] + off[dd] - r;
         qe[rr] = elem32<T>(qw[rr], dd) * exp_2(b);
         kp[rr] = elem32<T>(kw[rr], dd) * exp_2(-b);
-        kh[rr][dd] = kp[rr] * eB;
+        kh[rr][dd] = midref ? kp[rr] : kp[rr] * eB;
         qer[rr][dd] = qe[rr];
         sBeta[(RPW * w + rr) * Lay::LDB + i] = b;
       }
       if (w == 0) {
         sEB[i] = eB;
-        sEB[D + i] = exp_2(-Bt[dd]);
+        sEB[D + i] = exp_2(r - Bt[dd]);
       }
     } else {
       // wide span: raw q, k for the pairwise terms (2^-beta may overflow)
@@ -856,9 +868,11 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
     }
     store_pack<T, RPW>(sQT + i * Lay::LDT + RPW * w, qe);
     store_pack<T, RPW>(sKT + i * Lay::LDT + RPW * w, kp);
-    if (w == 0) sBx[i] = Bt[dd];
+    // the pairwise epilogue's chunk total, or the fast path's 2^r
+    if (w == 0) sBx[i] = pairwise ? Bt[dd] : (midref ? exp_2(0.5f * Bt[dd]) : 1.f);
   }
-  // Kh rows (phase C) and Qe rows (phase B), once for all wavefronts
+  // Kh rows (Kp rows with the shifted reference; phase C) and Qe rows (phase
+  // B), once for all wavefronts
 #pragma unroll
   for (int rr = 0; rr < RPW; ++rr) {
     T* kr = sKh + (RPW * w + rr) * Lay::LDR + DPL * l;
@@ -923,9 +937,14 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
     load_quarter<T, D, false>(GTr, GTg, ib + m, D, g);    // G_{c+1}^T rows j (k = i)
     // S_{c+1} rows i (zero after the last chunk)
     load_quarter<T, D, false>(Sn, c + 1 < nc ? Sg + (size_t)D * D : Sg, ib + m, D, g);
-    // Kp = Kh 2^-B of this lane's key row as fragments (unused on the pairwise path)
+    // Kp of this lane's key row as fragments: Kh 2^-B, or the stored Kp with the shifted
+    // reference (unused on the pairwise path)
     frag kpf[NF];
-    if (!pairwise) {
+    if (midref) {
+      const T* hp = sKh + (16 * I + m) * Lay::LDR + g * (D / 4);    // Kp rows
+#pragma unroll
+      for (int e = 0; e < NF; ++e) kpf[e] = M::load(hp + e * M::KPL);
+    } else if (!pairwise) {
       const T* hp = sKh + (16 * I + m) * Lay::LDR + g * (D / 4);
       const float* enb = sEB + D + g * (D / 4);
 #pragma unroll
@@ -1040,8 +1059,21 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
     frag khf[NF];
     {
       const T* kp = sKh + (16 * tt + m) * Lay::LDR + g * (D / 4);
+      if (!midref) {
 #pragma unroll
-      for (int e = 0; e < NF; ++e) khf[e] = M::load(kp + e * M::KPL);
+        for (int e = 0; e < NF; ++e) khf[e] = M::load(kp + e * M::KPL);
+      } else {
+        const float* ehb = sEB + g * (D / 4);    // 2^{B-r}
+#pragma unroll
+        for (int e = 0; e < NF; ++e) {
+          float hv[M::KPL], tk[M::KPL];
+          if constexpr (sizeof(T) == 2) unpack16<T>(*reinterpret_cast<const uint4*>(kp + e * M::KPL), hv);
+          else hv[0] = kp[e];
+#pragma unroll
+          for (int u = 0; u < M::KPL; ++u) tk[u] = hv[u] * ehb[e * M::KPL + u];
+          khf[e] = M::pack(tk);
+        }
+      }
     }
     // inter-chunk parts
     f32x4 qi = zero4(), ki = zero4(), vi = zero4();
@@ -1091,7 +1123,8 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
         kin = exp_2(sBx[i] - b) * ki[r] + kin;
       } else {
         const float ep = exp_2(b), en = exp_2(-b);
-        qin = ep * (qi[r] + qin);
+        const float rx = midref ? sBx[i] : 1.f;
+        qin = ep * (rx * qi[r] + qin);
         kin = en * (sEB[i] * ki[r] + kin);
       }
       const float dqg = qin;

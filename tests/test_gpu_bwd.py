@@ -79,13 +79,20 @@ def test_window_and_sinks(gpu_lib, window, n_meta):
 
 
 @pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
-@pytest.mark.parametrize("variant", ["sharp", "fast_gate", "hard_reset", "slow_gate"])
+@pytest.mark.parametrize("variant", ["sharp", "fast_gate", "hard_reset", "slow_gate", "wide_chunk", "wide_blocks",
+                                     "wide_mixed"])
 def test_variants(gpu_lib, dtype, d, variant):
+    # wide_chunk: chunk decay spans between one and two times the
+    # factorisable limit (the shifted reference point); wide_blocks: beyond
+    # twice the limit (the pairwise path); wide_mixed: chunks of all kinds
     kw = {
         "sharp": dict(qk_sd=1.0, meta_sd=1.0),
         "fast_gate": dict(gate_mu=-2.0, gate_sd=4.0),
         "hard_reset": dict(hard_reset_frac=0.02, gate_mu=2.0, gate_sd=2.0),
         "slow_gate": dict(gate_mu=8.0, gate_sd=1.0),
+        "wide_chunk": dict(gate_mu=-1.0, gate_sd=0.5),
+        "wide_blocks": dict(gate_mu=-3.0, gate_sd=0.3),
+        "wide_mixed": dict(gate_mu=0.0, gate_sd=3.0),
     }[variant]
     x = si.custom_inputs(32, 2, 2, 192, d, 4, dtype, with_dy=True, **kw)
     log(f"bwd variant={variant} dtype={dtype} d={d}")

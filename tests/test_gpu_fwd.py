@@ -65,17 +65,20 @@ def test_window_and_sinks(gpu_lib, window, n_meta):
 
 @pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
 @pytest.mark.parametrize("variant", ["sharp", "slow_gate", "fast_gate", "hard_reset", "outliers", "wide_chunk",
-                                     "wide_mixed"])
+                                     "wide_blocks", "wide_mixed"])
 def test_variants(gpu_lib, dtype, d, variant):
-    # wide_chunk: every chunk's decay span is too wide to factorise over the
-    # chunk (about 2^-121 over 64 tokens) while each 16-token block's is not;
-    # wide_mixed: both kinds of block in one chunk
+    # wide_chunk: chunk decay spans between one and two times the
+    # factorisable limit (about 2^-121 over 64 tokens: the shifted reference
+    # point); wide_blocks: spans beyond twice the limit (about 2^-280) while
+    # every 16-token block's stays within it (blockwise factorisation);
+    # wide_mixed: all kinds of chunk and block
     kw = {
         "sharp": dict(qk_sd=1.0, meta_sd=1.0),
         "slow_gate": dict(gate_mu=8.0, gate_sd=1.0),
         "fast_gate": dict(gate_mu=-2.0, gate_sd=4.0),
         "hard_reset": dict(hard_reset_frac=0.01, gate_mu=2.0, gate_sd=2.0),
         "wide_chunk": dict(gate_mu=-1.0, gate_sd=0.5),
+        "wide_blocks": dict(gate_mu=-3.0, gate_sd=0.3),
         "wide_mixed": dict(gate_mu=0.0, gate_sd=3.0),
         "outliers": dict(),
     }[variant]
