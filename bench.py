@@ -343,6 +343,18 @@ def bench_bwd(sqa, si, steps=10, warmup=3, logit=False):
 
     step()
     ms = time_region(step, steps, warmup)
+    ms_saved = None
+    if not logit:
+        # the same backward reading the chunk-start states a training forward kept
+        tr = sqa.lizard_attn_fwd_train(x["q"], x["k"], x["v"], x["meta_k"], log_g=x["log_g"], window=w.window,
+                                       alpha=w.alpha)
+
+        def step_saved():
+            sqa.lizard_attn_bwd_train(x["q"], x["k"], x["v"], x["meta_k"], tr["lse"], tr["chunk_states"], x["dy"],
+                                      log_g=x["log_g"], window=w.window, alpha=w.alpha, workspace=ws, out=out)
+
+        ms_saved = time_region(step_saved, steps, warmup)
+        del tr
     head_tokens = w.B * w.H * w.L
     # with logits: the gate in and its gradient out in bf16 instead of float32
     alg_bytes = head_tokens * (bwd_bytes_per_head_token(w.d) - (4 * w.d if logit else 0))
@@ -356,6 +368,8 @@ def bench_bwd(sqa, si, steps=10, warmup=3, logit=False):
         "frac_mfma_peak": round(alg_flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
         "workspace_bytes": int(ws.numel()),
     }
+    if ms_saved is not None:
+        res["ms_with_saved_states"] = round(ms_saved, 4)
     del x, fw, ws, out
     torch.cuda.empty_cache()
     return res
@@ -364,8 +378,10 @@ def bench_bwd(sqa, si, steps=10, warmup=3, logit=False):
 def bench_stage1(sqa, si, steps=10, warmup=3):
     """One synthetic stage-1 attention-transfer step on the backward workload's
     shapes (B=8, H=32, L=2048, d=128, bf16): the causal softmax teacher, the
-    layer's forward (with lse), the output-matching loss and the layer's
-    backward.  The teacher is also timed alone (causal QK^T and PV flops)."""
+    layer's training forward (lse and chunk-start states kept), the
+    output-matching loss and the layer's backward reading those states.  Also
+    timed: the same step with the plain forward and a backward that recomputes
+    the states, and the teacher alone (causal QK^T and PV flops)."""
     import numpy as np
     import torch
 
@@ -379,7 +395,9 @@ def bench_stage1(sqa, si, steps=10, warmup=3):
                      device="cuda", dtype=torch.uint8)
     tout = {"y": torch.empty_like(x["q"])}
     fout = {"y": torch.empty_like(x["q"]),
-            "lse": torch.empty((w.B, w.H, w.L), device="cuda", dtype=torch.float32)}
+            "lse": torch.empty((w.B, w.H, w.L), device="cuda", dtype=torch.float32),
+            "chunk_states": torch.empty((w.B, w.H, (w.L + 63) // 64, w.d, w.d), device="cuda",
+                                        dtype=torch.bfloat16)}
     dy = torch.empty_like(x["q"])
     loss_bh = torch.empty((w.B, w.H), device="cuda", dtype=torch.float32)
     gout = {}
@@ -389,17 +407,27 @@ def bench_stage1(sqa, si, steps=10, warmup=3):
 
     def step():
         teacher()
+        sqa.lizard_attn_fwd_train(x["q"], x["k"], x["v"], x["meta_k"], log_g=x["log_g"], window=w.window,
+                                  alpha=w.alpha, out=fout)
+        sqa.lizard_transfer_loss(fout["y"], tout["y"], dy=dy, loss_bh=loss_bh)
+        sqa.lizard_attn_bwd_train(x["q"], x["k"], x["v"], x["meta_k"], fout["lse"], fout["chunk_states"], dy,
+                                  log_g=x["log_g"], window=w.window, alpha=w.alpha, workspace=ws, out=gout)
+
+    def step_recompute():
+        teacher()
         sqa.lizard_attn_fwd(x["q"], x["k"], x["v"], x["log_g"], x["meta_k"], window=w.window, alpha=w.alpha,
                             need_lse=True, out=fout)
         sqa.lizard_transfer_loss(fout["y"], tout["y"], dy=dy, loss_bh=loss_bh)
         sqa.lizard_attn_bwd(x["q"], x["k"], x["v"], x["log_g"], x["meta_k"], fout["lse"], dy, window=w.window,
                             alpha=w.alpha, workspace=ws, out=gout)
 
+    ms_r = time_region(step_recompute, steps, warmup)
     ms = time_region(step, steps, warmup)
     ms_t = time_region(teacher, 3 * steps, warmup)
     t_flops = w.B * w.H * 2 * w.L * (w.L + 1) * w.d    # causal pairs x (QK^T + PV) x 2 flops
     res = {"workload": "train_bwd_bf16 shapes, teacher = causal softmax attention", "ms": round(ms, 4),
            "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1), "loss": round(float(loss_bh.sum()), 6),
+           "ms_recomputing_states": round(ms_r, 4),
            "teacher_ms": round(ms_t, 4), "teacher_tflops": round(t_flops / (ms_t * 1e-3) / 1e12, 1),
            "teacher_frac_mfma_peak": round(t_flops / (ms_t * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
     del x, ws, tout, fout, dy, loss_bh, gout

@@ -208,6 +208,50 @@ lizard_status_t lizard_attn_fwd_split(const lizard_params_t* p,
                                       void* y, float* lse, void* y_anchor, float* state_out,
                                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Training: the forward pass keeps the states the backward needs ----
+ *
+ * The layer is trained end to end (de section 2 "Trainingsprozess"), so the
+ * backward pass follows a forward pass over the same inputs.  The backward
+ * needs the state at the start of every 64-token chunk; lizard_attn_bwd
+ * recomputes them in a pass of its own, while these calls let the forward
+ * pass write them as it goes and the backward read them.
+ *
+ * Bytes of the chunk-start states for these sizes: B*H*ceil(L/64)*dk*dv
+ * elements of the element type (0 on invalid sizes). */
+size_t lizard_attn_chunk_states_size(const lizard_params_t* p);
+
+/* lizard_attn_fwd (log_g non-NULL) or lizard_attn_fwd_logit (gate_logit
+ * non-NULL; both non-NULL: LIZARD_E_SHAPE), which also writes
+ *   chunk_states  [B, H, ceil(L/64), dk, dv] dtype, out, 16-byte aligned:
+ *                 the state S before the first token of each chunk (zero
+ *                 for chunk 0), rounded to dtype
+ * Every other argument and result as lizard_attn_fwd; y, lse, y_anchor and
+ * state_out are bit for bit those of lizard_attn_fwd.  chunk_states NULL with
+ * B*H*L > 0: LIZARD_E_NULL. */
+lizard_status_t lizard_attn_fwd_train(const lizard_params_t* p,
+                                      const void* q, const void* k, const void* v,
+                                      const float* log_g, const void* gate_logit,
+                                      const void* meta_k, void* y, float* lse,
+                                      void* y_anchor, float* state_out,
+                                      void* chunk_states, void* stream);
+
+/* lizard_attn_bwd (log_g non-NULL; dgate is float* dlog_g [B, H, L, dk]) or
+ * lizard_attn_bwd_logit (gate_logit non-NULL; dgate is the dtype gradient of
+ * the logits), reading the chunk-start states lizard_attn_fwd_train wrote
+ * for the same q, k, v, gates and sizes instead of recomputing them:
+ *   chunk_states  [B, H, ceil(L/64), dk, dv] dtype, in, 16-byte aligned
+ * Every other argument, the workspace (lizard_attn_bwd_workspace_size) and
+ * every result as lizard_attn_bwd; the results are those of lizard_attn_bwd.
+ * chunk_states NULL with B*H*L > 0: LIZARD_E_NULL. */
+lizard_status_t lizard_attn_bwd_train(const lizard_params_t* p,
+                                      const void* q, const void* k, const void* v,
+                                      const float* log_g, const void* gate_logit,
+                                      const void* meta_k, const float* lse,
+                                      const void* chunk_states, const void* dy,
+                                      void* dq, void* dk, void* dv, void* dgate,
+                                      float* dmeta_k, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
 /* Serving form of the decode step (constant-memory generation for a batch
  * of sequences, de section 2 item 1 and section 4 "Effizienz"): T >= 1 new
  * tokens per row, appended in order, each batch row at its own position.
@@ -302,7 +346,9 @@ lizard_status_t lizard_transfer_loss(const lizard_params_t* p,
 /* Static description of a status code. */
 const char* lizard_status_string(lizard_status_t s);
 
-/* ABI version of this header: 3 (version 2 had no lizard_attn_fwd_split;
+/* ABI version of this header: 4 (version 3 had no lizard_attn_fwd_train,
+ * lizard_attn_bwd_train or lizard_attn_chunk_states_size; version 2 had no
+ * lizard_attn_fwd_split;
  * version 1 had none of the *_logit, lizard_attn_fwd_continue,
  * lizard_decode_tokens, lizard_softmax_attn_fwd and lizard_transfer_loss
  * entry points). */

@@ -77,6 +77,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lizard_attn_fwd_split_workspace_size.restype = ctypes.c_size_t
     lib.lizard_attn_fwd_split.argtypes = [P] + [_vp] * 9 + [ctypes.c_int32] + [_vp] * 5 + [ctypes.c_size_t, _vp]
     lib.lizard_attn_fwd_split.restype = ctypes.c_int
+    lib.lizard_attn_chunk_states_size.argtypes = [P]
+    lib.lizard_attn_chunk_states_size.restype = ctypes.c_size_t
+    lib.lizard_attn_fwd_train.argtypes = [P] + [_vp] * 12
+    lib.lizard_attn_fwd_train.restype = ctypes.c_int
+    lib.lizard_attn_bwd_train.argtypes = [P] + [_vp] * 15 + [ctypes.c_size_t, _vp]
+    lib.lizard_attn_bwd_train.restype = ctypes.c_int
     lib.lizard_softmax_attn_fwd.argtypes = [P] + [_vp] * 6
     lib.lizard_softmax_attn_fwd.restype = ctypes.c_int
     lib.lizard_transfer_loss.argtypes = [P] + [_vp] * 5
@@ -222,6 +228,70 @@ def _bwd(fn, gkey, q, k, v, gate, meta_k, lse, dy, window, alpha, softmax_scale,
                           _ptr(dy), _ptr(o["dq"]), _ptr(o["dk"]), _ptr(o["dv"]), _ptr(o[gkey]),
                           _ptr(o["dmeta"]), _ptr(workspace), workspace.numel(), _stream(q.device))
     _check(fn, st)
+    return o
+
+
+def lizard_attn_fwd_train(q, k, v, meta_k, *, log_g=None, gate_logit=None, window: int, alpha: float,
+                          softmax_scale: float = 0.0, chunk: int = 64, need_y_anchor: bool = False,
+                          need_state: bool = False, out: Optional[Dict] = None) -> Dict:
+    """The forward pass of a training step: lizard_attn_fwd (log_g) or
+    lizard_attn_fwd_logit (gate_logit) that also keeps the chunk-start states
+    for lizard_attn_bwd_train.  Returns {"y", "lse", "chunk_states" [B, H,
+    ceil(L/64), d, d] in q's dtype, and optionally "y_anchor", "state"}."""
+    torch = _torch()
+    lib = load_library()
+    B, H, L, d = q.shape
+    m = meta_k.shape[1] if meta_k is not None else 0
+    p = make_params(B, H, L, d, window=window, n_meta=m, alpha=alpha, dtype=_dtype_code(q), chunk=chunk,
+                    softmax_scale=softmax_scale)
+    o = dict(out) if out is not None else {}
+    if "y" not in o:
+        o["y"] = torch.empty_like(q)
+    if "lse" not in o:
+        o["lse"] = torch.empty((B, H, L), device=q.device, dtype=torch.float32)
+    if "chunk_states" not in o:
+        o["chunk_states"] = torch.empty((B, H, (L + 63) // 64, d, d), device=q.device, dtype=q.dtype)
+    if need_y_anchor and "y_anchor" not in o:
+        o["y_anchor"] = torch.empty_like(q)
+    if need_state and "state" not in o:
+        o["state"] = torch.empty((B, H, d, d), device=q.device, dtype=torch.float32)
+    st = lib.lizard_attn_fwd_train(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(gate_logit),
+                                   _ptr(meta_k), _ptr(o["y"]), _ptr(o["lse"]), _ptr(o.get("y_anchor")),
+                                   _ptr(o.get("state")), _ptr(o["chunk_states"]), _stream(q.device))
+    _check("lizard_attn_fwd_train", st)
+    return o
+
+
+def lizard_attn_bwd_train(q, k, v, meta_k, lse, chunk_states, dy, *, log_g=None, gate_logit=None, window: int,
+                          alpha: float, softmax_scale: float = 0.0, chunk: int = 64, workspace=None,
+                          out: Optional[Dict] = None) -> Dict:
+    """lizard_attn_bwd (log_g) or lizard_attn_bwd_logit (gate_logit) reading
+    the chunk-start states lizard_attn_fwd_train kept.  Returns {"dq", "dk",
+    "dv", "dlog_g" or "dgate_logit", "dmeta"}."""
+    torch = _torch()
+    lib = load_library()
+    B, H, L, d = q.shape
+    m = meta_k.shape[1] if meta_k is not None else 0
+    p = make_params(B, H, L, d, window=window, n_meta=m, alpha=alpha, dtype=_dtype_code(q), chunk=chunk,
+                    softmax_scale=softmax_scale)
+    ws_bytes = int(lib.lizard_attn_bwd_workspace_size(ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), device=q.device, dtype=torch.uint8)
+    gate = gate_logit if gate_logit is not None else log_g
+    gkey = "dgate_logit" if gate_logit is not None else "dlog_g"
+    o = dict(out) if out is not None else {}
+    for key, like in (("dq", q), ("dk", k), ("dv", v)):
+        if key not in o:
+            o[key] = torch.empty_like(like)
+    if gkey not in o:
+        o[gkey] = torch.empty_like(gate)
+    if "dmeta" not in o:
+        o["dmeta"] = torch.empty((H, m, d), device=q.device, dtype=torch.float32) if m > 0 else None
+    st = lib.lizard_attn_bwd_train(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(gate_logit),
+                                   _ptr(meta_k), _ptr(lse), _ptr(chunk_states), _ptr(dy), _ptr(o["dq"]),
+                                   _ptr(o["dk"]), _ptr(o["dv"]), _ptr(o[gkey]), _ptr(o["dmeta"]), _ptr(workspace),
+                                   workspace.numel(), _stream(q.device))
+    _check("lizard_attn_bwd_train", st)
     return o
 
 

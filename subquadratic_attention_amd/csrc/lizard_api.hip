@@ -55,7 +55,7 @@ lizard_status_t attn_fwd(const lizard_params_t* p, const void* q, const void* k,
                          const void* gate_logit, bool logit, const void* meta_k, const float* state_in,
                          const void* k_halo, const void* v_halo, int32_t halo_len, void* y, float* lse,
                          void* y_anchor, float* state_out, void* stream, bool split = false,
-                         void* workspace = nullptr, size_t workspace_bytes = 0) {
+                         void* workspace = nullptr, size_t workspace_bytes = 0, void* chunk_states = nullptr) {
   lizard_status_t s = check_params(p, true);
   if (s != LIZARD_OK) return s;
   if (halo_len < 0 || halo_len > p->window - 1) return LIZARD_E_SHAPE;
@@ -70,7 +70,8 @@ lizard_status_t attn_fwd(const lizard_params_t* p, const void* q, const void* k,
     return LIZARD_E_NULL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(gate) || misaligned(y) ||
       misaligned(meta_k) || misaligned(lse) || misaligned(y_anchor) || misaligned(state_out) ||
-      misaligned(state_in) || misaligned(k_halo) || misaligned(v_halo) || misaligned(workspace))
+      misaligned(state_in) || misaligned(k_halo) || misaligned(v_halo) || misaligned(workspace) ||
+      misaligned(chunk_states))
     return LIZARD_E_ALIGN;
   if (!seq && state_out == nullptr) return LIZARD_OK;
   const int bf = p->dtype == LIZARD_BF16;
@@ -86,7 +87,7 @@ lizard_status_t attn_fwd(const lizard_params_t* p, const void* q, const void* k,
   a.lse = lse;
   a.y_anchor = y_anchor;
   a.state_out = state_out;
-  a.states = nullptr;
+  a.states = chunk_states;
   a.state_in = state_in;
   a.k_halo = halo_len > 0 ? k_halo : nullptr;
   a.v_halo = halo_len > 0 ? v_halo : nullptr;
@@ -114,10 +115,12 @@ lizard_status_t attn_fwd(const lizard_params_t* p, const void* q, const void* k,
 }
 
 // The backward pass; with logits, dgate (element type) replaces dlog_g.
+// saved_states: the chunk-start states a training forward kept (NULL: the
+// pass recomputes them).
 lizard_status_t attn_bwd(const lizard_params_t* p, const void* q, const void* k, const void* v, const float* log_g,
                          const void* gate_logit, bool logit, const void* meta_k, const float* lse, const void* dy,
                          void* dq, void* dk, void* dv, float* dlog_g, void* dgate, float* dmeta_k, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+                         size_t workspace_bytes, void* stream, const void* saved_states = nullptr) {
   lizard_status_t s = check_params(p, true);
   if (s != LIZARD_OK) return s;
   const int BH = p->B * p->H;
@@ -129,7 +132,7 @@ lizard_status_t attn_bwd(const lizard_params_t* p, const void* q, const void* k,
     return LIZARD_E_NULL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(gate) || misaligned(meta_k) ||
       misaligned(lse) || misaligned(dy) || misaligned(dq) || misaligned(dk) || misaligned(dv) ||
-      misaligned(dgo) || misaligned(dmeta_k) || misaligned(workspace))
+      misaligned(dgo) || misaligned(dmeta_k) || misaligned(workspace) || misaligned(saved_states))
     return LIZARD_E_ALIGN;
   const size_t need = lizard::bwd_workspace_bytes(p->dtype == LIZARD_BF16, BH, p->L, p->dk, p->n_meta);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LIZARD_E_WORKSPACE;
@@ -150,6 +153,7 @@ lizard_status_t attn_bwd(const lizard_params_t* p, const void* q, const void* k,
   a.dgate = logit ? dgate : nullptr;
   a.dmeta = dmeta_k;
   a.workspace = workspace;
+  a.saved_states = saved_states;
   a.B = p->B;
   a.BH = BH;
   a.H = p->H;
@@ -244,6 +248,36 @@ LIZARD_API lizard_status_t lizard_attn_fwd_split(const lizard_params_t* p, const
   if (log_g != nullptr && gate_logit != nullptr) return LIZARD_E_SHAPE;
   return attn_fwd(p, q, k, v, log_g, gate_logit, gate_logit != nullptr, meta_k, state_in, k_halo, v_halo, halo_len, y,
                   lse, y_anchor, state_out, stream, true, workspace, workspace_bytes);
+}
+
+LIZARD_API size_t lizard_attn_chunk_states_size(const lizard_params_t* p) {
+  if (check_params(p, true) != LIZARD_OK) return 0;
+  const size_t nc = (size_t)(p->L + 63) / 64;
+  return (size_t)p->B * p->H * nc * p->dk * p->dv * (p->dtype == LIZARD_BF16 ? 2 : 4);
+}
+
+LIZARD_API lizard_status_t lizard_attn_fwd_train(const lizard_params_t* p, const void* q, const void* k,
+                                                 const void* v, const float* log_g, const void* gate_logit,
+                                                 const void* meta_k, void* y, float* lse, void* y_anchor,
+                                                 float* state_out, void* chunk_states, void* stream) {
+  if (log_g != nullptr && gate_logit != nullptr) return LIZARD_E_SHAPE;
+  if (p != nullptr && p->B * p->H > 0 && p->L > 0 && chunk_states == nullptr) return LIZARD_E_NULL;
+  return attn_fwd(p, q, k, v, log_g, gate_logit, gate_logit != nullptr, meta_k, nullptr, nullptr, nullptr, 0, y, lse,
+                  y_anchor, state_out, stream, false, nullptr, 0, chunk_states);
+}
+
+LIZARD_API lizard_status_t lizard_attn_bwd_train(const lizard_params_t* p, const void* q, const void* k,
+                                                 const void* v, const float* log_g, const void* gate_logit,
+                                                 const void* meta_k, const float* lse, const void* chunk_states,
+                                                 const void* dy, void* dq, void* dk, void* dv, void* dgate,
+                                                 float* dmeta_k, void* workspace, size_t workspace_bytes,
+                                                 void* stream) {
+  if (log_g != nullptr && gate_logit != nullptr) return LIZARD_E_SHAPE;
+  if (p != nullptr && p->B * p->H > 0 && p->L > 0 && chunk_states == nullptr) return LIZARD_E_NULL;
+  const bool logit = gate_logit != nullptr;
+  return attn_bwd(p, q, k, v, log_g, gate_logit, logit, meta_k, lse, dy, dq, dk, dv,
+                  logit ? nullptr : static_cast<float*>(dgate), logit ? dgate : nullptr, dmeta_k, workspace,
+                  workspace_bytes, stream, chunk_states);
 }
 
 LIZARD_API size_t lizard_attn_bwd_workspace_size(const lizard_params_t* p) {
@@ -350,4 +384,4 @@ LIZARD_API const char* lizard_status_string(lizard_status_t s) {
   return "unknown status";
 }
 
-LIZARD_API int lizard_abi_version(void) { return 3; }
+LIZARD_API int lizard_abi_version(void) { return 4; }

@@ -1260,29 +1260,34 @@ hipError_t launch_bwd_t(BwdArgs a, hipStream_t st) {
   const int groups = (a.BH + 7) / 8;
   hipError_t e;
   if (a.BH > 0 && L > 0) {
-    // 1. chunk-start states (forward kernel, states only)
-    FwdArgs f{};
-    f.q = a.q;
-    f.k = a.k;
-    f.v = a.v;
-    f.log_g = a.log_g;
-    f.gate_logit = a.gate_logit;
-    f.meta = a.meta;
-    f.y = nullptr;
-    f.lse = nullptr;
-    f.y_anchor = nullptr;
-    f.state_out = nullptr;
-    f.states = a.ws_states;
-    f.BH = a.BH;
-    f.H = a.H;
-    f.L = L;
-    f.n_meta = a.n_meta;
-    f.window = a.window;
-    f.nsplit = D / fwd_value_slice(sizeof(T) == 2, D);
-    f.alpha = a.alpha;
-    f.scale_log2 = a.scale * kLog2e;
-    e = launch_fwd(f, sizeof(T) == 2, D, st);
-    if (e != hipSuccess) return e;
+    if (a.saved_states) {
+      // 1. the chunk-start states the forward pass kept (read only)
+      a.ws_states = const_cast<void*>(a.saved_states);
+    } else {
+      // 1. chunk-start states (forward kernel, states only)
+      FwdArgs f{};
+      f.q = a.q;
+      f.k = a.k;
+      f.v = a.v;
+      f.log_g = a.log_g;
+      f.gate_logit = a.gate_logit;
+      f.meta = a.meta;
+      f.y = nullptr;
+      f.lse = nullptr;
+      f.y_anchor = nullptr;
+      f.state_out = nullptr;
+      f.states = a.ws_states;
+      f.BH = a.BH;
+      f.H = a.H;
+      f.L = L;
+      f.n_meta = a.n_meta;
+      f.window = a.window;
+      f.nsplit = D / fwd_value_slice(sizeof(T) == 2, D);
+      f.alpha = a.alpha;
+      f.scale_log2 = a.scale * kLog2e;
+      e = launch_fwd(f, sizeof(T) == 2, D, st);
+      if (e != hipSuccess) return e;
+    }
     // 2. state gradients
     if (a.gate_logit)
       hipLaunchKernelGGL((bwd_dstate_kernel<T, D, DV, true>), dim3(8 * groups * (D / DV)), dim3(256), 0, st, a);

@@ -586,8 +586,10 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
                 store_pack<T, 4>(sSt + (16 * ct + m_lane) * Lay::LDST + 16 * (DPL * I + rt) + 4 * g_lane, sv);
               }
           }
-        } else {
+        }
+        if (STATES || (!SEG && a.states)) {
           // chunk-start state for the backward pass: S_cc[i][j], row-major
+          // (the states-only pass, or a training forward that keeps them)
           const int ncs = (L + C - 1) / C;
           T* sg = reinterpret_cast<T*>(a.states) + ((size_t)bh * ncs + cc) * D * D + j0;
   #pragma unroll
@@ -1248,7 +1250,9 @@ static hipError_t launch_seg_finish(const FwdArgs& a, hipStream_t st) {
 
 template <typename T, int D, int DV>
 static hipError_t launch_fwd_s(const FwdArgs& a, hipStream_t st) {
-  if (a.states) {
+  // states and no outputs: the states-only pass of the backward; states and
+  // outputs: the full forward, keeping the states as well
+  if (a.states && !a.y) {
     if (a.nseg != 1) return hipErrorInvalidValue;
     return a.gate_logit ? launch_fwd_t<T, D, DV, true, true, false>(a, st)
                         : launch_fwd_t<T, D, DV, true, false, false>(a, st);

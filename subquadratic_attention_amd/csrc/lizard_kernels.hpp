@@ -75,6 +75,7 @@ struct BwdArgs {
   void* dgate;           // gradient w.r.t. the gate logits (when gate_logit is set)
   float* dmeta;          // [H, n_meta, D]
   void* workspace;
+  const void* saved_states;   // nullable: chunk-start states kept by the forward pass (no states pass)
   // carved from the workspace by launch_bwd
   void* ws_states;       // S_c          [BH, nc, D, D] element type
   void* ws_dS;           // G_{c+1}      [BH, nc, D, D] element type

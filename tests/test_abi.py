@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
                  "lizard_attn_fwd_logit", "lizard_attn_bwd_logit", "lizard_decode_step_logit",
                  "lizard_decode_tokens", "lizard_decode_tokens_logit", "lizard_attn_fwd_continue",
                  "lizard_softmax_attn_fwd", "lizard_transfer_loss", "lizard_attn_fwd_split",
-                 "lizard_attn_fwd_split_workspace_size",
+                 "lizard_attn_fwd_split_workspace_size", "lizard_attn_fwd_train", "lizard_attn_bwd_train",
+                 "lizard_attn_chunk_states_size",
                  "lizard_status_string", "lizard_abi_version"):
         assert want in names
 
@@ -66,7 +67,7 @@ def test_param_struct_layout_matches_c(tmp_path):
 
 
 def test_version_and_strings(lib):
-    assert lib.lizard_abi_version() == 3
+    assert lib.lizard_abi_version() == 4
     for code, name in sqa.STATUS.items():
         s = lib.lizard_status_string(code)
         assert isinstance(s, bytes) and len(s) > 0
@@ -232,3 +233,27 @@ def test_split_checks(lib):
     assert f(long_, MIS, need) == S["LIZARD_E_ALIGN"]
     assert f(long_, FAKE, need, lg=FAKE, xg=FAKE) == S["LIZARD_E_SHAPE"]
     assert f(params(B=0), None, 0) == 0
+
+
+def test_train_entry_points_check_their_arguments(lib):
+    """The training forward and backward: the chunk-states size and the
+    checks of the saved states and gate arguments, before any launch."""
+    p = params(B=2, H=3, L=130, d=128)
+    assert lib.lizard_attn_chunk_states_size(ctypes.byref(p)) == 2 * 3 * 3 * 128 * 128 * 2
+    assert lib.lizard_attn_chunk_states_size(ctypes.byref(params(dtype=7))) == 0
+    fw = lambda cs, lg=FAKE, xg=None: lib.lizard_attn_fwd_train(ctypes.byref(p), FAKE, FAKE, FAKE, lg, xg, FAKE, FAKE,
+                                                              FAKE, None, None, cs, None)
+    assert fw(None) == S["LIZARD_E_NULL"]
+    assert fw(MIS) == S["LIZARD_E_ALIGN"]
+    assert fw(FAKE, lg=FAKE, xg=FAKE) == S["LIZARD_E_SHAPE"]
+    assert fw(FAKE, lg=None, xg=None) == S["LIZARD_E_NULL"]
+    bw = lambda cs, ws=FAKE, nb=1 << 40: lib.lizard_attn_bwd_train(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                                                   FAKE, cs, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, nb,
+                                                                   None)
+    assert bw(None) == S["LIZARD_E_NULL"]
+    assert bw(MIS) == S["LIZARD_E_ALIGN"]
+    need = lib.lizard_attn_bwd_workspace_size(ctypes.byref(p))
+    assert bw(FAKE, nb=need - 1) == S["LIZARD_E_WORKSPACE"]
+    pe = params(B=0)
+    assert lib.lizard_attn_fwd_train(ctypes.byref(pe), None, None, None, FAKE, None, FAKE, None, None, None, None,
+                                     None, None) == 0
