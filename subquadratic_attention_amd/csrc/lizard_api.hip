@@ -261,7 +261,7 @@ LIZARD_API lizard_status_t lizard_attn_fwd_train(const lizard_params_t* p, const
                                                  const void* meta_k, void* y, float* lse, void* y_anchor,
                                                  float* state_out, void* chunk_states, void* stream) {
   if (log_g != nullptr && gate_logit != nullptr) return LIZARD_E_SHAPE;
-  if (p != nullptr && p->B * p->H > 0 && p->L > 0 && chunk_states == nullptr) return LIZARD_E_NULL;
+  if (p != nullptr && (int64_t)p->B * p->H > 0 && p->L > 0 && chunk_states == nullptr) return LIZARD_E_NULL;
   return attn_fwd(p, q, k, v, log_g, gate_logit, gate_logit != nullptr, meta_k, nullptr, nullptr, nullptr, 0, y, lse,
                   y_anchor, state_out, stream, false, nullptr, 0, chunk_states);
 }
@@ -273,7 +273,7 @@ LIZARD_API lizard_status_t lizard_attn_bwd_train(const lizard_params_t* p, const
                                                  float* dmeta_k, void* workspace, size_t workspace_bytes,
                                                  void* stream) {
   if (log_g != nullptr && gate_logit != nullptr) return LIZARD_E_SHAPE;
-  if (p != nullptr && p->B * p->H > 0 && p->L > 0 && chunk_states == nullptr) return LIZARD_E_NULL;
+  if (p != nullptr && (int64_t)p->B * p->H > 0 && p->L > 0 && chunk_states == nullptr) return LIZARD_E_NULL;
   const bool logit = gate_logit != nullptr;
   return attn_bwd(p, q, k, v, log_g, gate_logit, logit, meta_k, lse, dy, dq, dk, dv,
                   logit ? nullptr : static_cast<float*>(dgate), logit ? dgate : nullptr, dmeta_k, workspace,
