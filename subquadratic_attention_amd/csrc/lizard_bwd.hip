@@ -359,6 +359,39 @@ __global__ __launch_bounds__(256, 1) void bwd_dstate_kernel(BwdArgs a) {
   }
 }
 
+// Fragment e of a window-ordered operand row: the MFMA contraction runs over
+// the 96 window positions (keys for the query side, queries for the key
+// side) in the order the score tiles leave them in a lane's registers (value
+// v = 4 kt + r of lane group g is position 16 kt + 4 g + r), so the scores
+// feed the next product from registers; the other operand (row p of a
+// transposed tile, positions from q0) is gathered in that order.
+template <typename T>
+__device__ __forceinline__ typename Mfma<T>::frag window_frag(const T* p, int q0, int g, int e) {
+  typedef Mfma<T> M;
+  if constexpr (sizeof(T) == 2) {
+    // values 8e .. 8e+7: tiles 2e and 2e+1, four consecutive queries each
+    const uint2 a = *reinterpret_cast<const uint2*>(p + q0 + 32 * e + 4 * g);
+    const uint2 b = *reinterpret_cast<const uint2*>(p + q0 + 32 * e + 16 + 4 * g);
+    return __builtin_bit_cast(typename M::frag, make_uint4(a.x, a.y, b.x, b.y));
+  } else {
+    return p[q0 + 16 * (e >> 2) + 4 * g + (e & 3)];
+  }
+}
+
+// Fragment of the sink operand row p (16 sinks) in the same register order:
+// lane group g holds sinks 4g .. 4g + 3 (bf16: one step, the other four
+// slots zero; fp32: step e is sink 4g + e).
+template <typename T>
+__device__ __forceinline__ typename Mfma<T>::frag sink_frag(const T* p, int g, int e) {
+  typedef Mfma<T> M;
+  if constexpr (sizeof(T) == 2) {
+    const uint2 a = *reinterpret_cast<const uint2*>(p + 4 * g);
+    return __builtin_bit_cast(typename M::frag, make_uint4(a.x, a.y, 0u, 0u));
+  } else {
+    return p[4 * g + e];
+  }
+}
+
 // ---------------------------------------------------------------------------
 // 3. anchor branch, query side (per chunk of queries)
 // ---------------------------------------------------------------------------
@@ -368,23 +401,19 @@ struct AqLayout {
   static constexpr int LDKT = 128 + PAD;   // sKT [D][LDKT]: window keys transposed
   static constexpr int LDMT = 32 + PAD;    // sMuT [D][LDMT]: sink keys transposed (zero padded)
   static constexpr int LDQ = D + PAD;      // sQ [64][LDQ]
-  static constexpr int LDS = 96 + PAD;     // per-wave staging of dZ [16][LDS]
-  static constexpr int LDZS = 32 + PAD;    // per-wave staging of sink dZ [16][LDZS]
   static constexpr int a16(int x) { return (x + 15) / 16 * 16; }
   static constexpr int OFF_KT = 0;
   static constexpr int OFF_Q = 0;          // after the dq products, the chunk's queries replace the keys
   static_assert(64 * LDQ <= D * LDKT, "query rows fit in the key tile");
   static constexpr int OFF_MT = OFF_KT + a16(D * LDKT * (int)sizeof(T));
-  static constexpr int OFF_ST = OFF_MT + a16(D * LDMT * (int)sizeof(T));
-  static constexpr int OFF_ZS = OFF_ST + a16(4 * 16 * LDS * (int)sizeof(T));
-  static constexpr int OFF_DZS = OFF_ZS + a16(4 * 16 * LDZS * (int)sizeof(T));   // fp32 [64][16]
+  static constexpr int OFF_DZS = OFF_MT + a16(D * LDMT * (int)sizeof(T));   // sink dZ, fp32 [64][16]
   static constexpr int TOTAL = OFF_DZS + a16(64 * 16 * 4);
 };
 
 // The grid covers chunks cb .. cb + ncl - 1; GUARD = false: they are interior
 // (the window keys [t0 - 64, t0 + 64) and the queries lie inside [0, L)).
 template <typename T, int D, bool GUARD>
-__global__ __launch_bounds__(256, 2) void bwd_anchor_q_kernel(BwdArgs a, int cb, int ncl) {
+__global__ __launch_bounds__(256, 3) void bwd_anchor_q_kernel(BwdArgs a, int cb, int ncl) {
   typedef AqLayout<T, D> Lay;
   typedef Mfma<T> M;
   typedef typename M::frag frag;
@@ -405,8 +434,6 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_q_kernel(BwdArgs a, int cb,
   const int h = bh % a.H;
   const int t0 = c * C;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
-  T* sSt = reinterpret_cast<T*>(smem + Lay::OFF_ST) + w * 16 * Lay::LDS;
-  T* sZs = reinterpret_cast<T*>(smem + Lay::OFF_ZS) + w * 16 * Lay::LDZS;
   const T* qg = reinterpret_cast<const T*>(a.q) + (size_t)bh * L * D;
   const T* kg = reinterpret_cast<const T*>(a.k) + (size_t)bh * L * D;
   const T* vg = reinterpret_cast<const T*>(a.v) + (size_t)bh * L * D;
@@ -417,18 +444,22 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_q_kernel(BwdArgs a, int cb,
   const int I = w;
   const int tme = t0 + 16 * I + m;
   const int U0 = 16 * I < 32 ? 16 * I : 32;
-  // this lane's query and dY row, and the window keys / values of its tiles,
-  // issued before the staging (their loads then overlap it)
+  // this lane's query and dY row, and the window keys / values of its
+  // first three tiles, issued before the staging (their loads then overlap
+  // it); the other three tiles reuse the registers (three workgroups per CU)
   uint4 qraw[QV], dyraw[QV];
   load_quarter<T, D, GUARD>(qraw, qg, tme, L, g);
   load_quarter<T, D, GUARD>(dyraw, dyg, tme, L, g);
-  uint4 kraw[6][QV], vraw[6][QV];
+  uint4 kraw[3][QV], vraw[3][QV];
+  auto load_tiles = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
-  for (int kt = 0; kt < 6; ++kt) {
-    const int s = t0 - 64 + U0 + 16 * kt + m;   // key row of this lane (MFMA row)
-    load_quarter<T, D, GUARD>(kraw[kt], kg, s, L, g);
-    load_quarter<T, D, GUARD>(vraw[kt], vg, s, L, g);
-  }
+    for (int kk = 0; kk < 3; ++kk) {
+      const int s = t0 - 64 + U0 + 16 * (k0 + kk) + m;   // key row of this lane (MFMA row)
+      load_quarter<T, D, GUARD>(kraw[kk], kg, s, L, g);
+      load_quarter<T, D, GUARD>(vraw[kk], vg, s, L, g);
+    }
+  };
+  load_tiles(0);
   const float lse2 = !GUARD || tme < L ? a.lse[(size_t)bh * L + (tme < L ? tme : 0)] * kLog2e : 0.f;
 
   // window keys [t0 - 64, t0 + 64) transposed; sink keys transposed
@@ -442,15 +473,19 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_q_kernel(BwdArgs a, int cb,
   // logits Z^T[u][t] and value products dP^T[u][t] for window keys u
   f32x4 z[6], dp[6];
 #pragma unroll
-  for (int kt = 0; kt < 6; ++kt) {
-    f32x4 zc = zero4(), pc = zero4();
+  for (int half = 0; half < 2; ++half) {
+    if (half == 1) load_tiles(3);
 #pragma unroll
-    for (int e = 0; e < NF; ++e) {
-      zc = M::mma(frag_of<T>(kraw[kt], e), frag_of<T>(qraw, e), zc);
-      pc = M::mma(frag_of<T>(vraw[kt], e), frag_of<T>(dyraw, e), pc);
+    for (int kk = 0; kk < 3; ++kk) {
+      f32x4 zc = zero4(), pc = zero4();
+#pragma unroll
+      for (int e = 0; e < NF; ++e) {
+        zc = M::mma(frag_of<T>(kraw[kk], e), frag_of<T>(qraw, e), zc);
+        pc = M::mma(frag_of<T>(vraw[kk], e), frag_of<T>(dyraw, e), pc);
+      }
+      z[3 * half + kk] = zc;
+      dp[3 * half + kk] = pc;
     }
-    z[kt] = zc;
-    dp[kt] = pc;
   }
   f32x4 zs = zero4();
   if (a.n_meta > 0) {
@@ -478,53 +513,70 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_q_kernel(BwdArgs a, int cb,
 #pragma unroll
   for (int r = 0; r < 4; ++r)
     ps[r] = (4 * g + r < a.n_meta && tme < L) ? exp_2(zs[r] * sl2 - lse2) : 0.f;
-  // stage dZ[t][u] and the sink part dZs[t][i] = -P D_t (rows: this lane's query)
+  // dZ[t][u] of the lane's query over its 24 window keys, as operand
+  // fragments in the window order, and the sink part dZs[t][i] = -P D_t
+  float dz[24];
 #pragma unroll
-  for (int kt = 0; kt < 6; ++kt) {
-    float v4[4];
+  for (int kt = 0; kt < 6; ++kt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) v4[r] = z[kt][r] * (dp[kt][r] - Dt);
-    store_pack<T, 4>(sSt + m * Lay::LDS + 16 * kt + 4 * g, v4);
+    for (int r = 0; r < 4; ++r) dz[4 * kt + r] = z[kt][r] * (dp[kt][r] - Dt);
+  typename M::frag zf[24 / M::KPL];
+#pragma unroll
+  for (int e = 0; e < 24 / M::KPL; ++e) zf[e] = M::pack(dz + e * M::KPL);
+  float zsv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    zsv[r] = -ps[r] * Dt;
+    sdZs[(16 * I + m) * 16 + 4 * g + r] = zsv[r];
   }
-  {
-    float v4[4], z4[4] = {0.f, 0.f, 0.f, 0.f};
+  constexpr int NS = sizeof(T) == 2 ? 1 : 4;      // sink steps
+  typename M::frag sf[NS];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) v4[r] = -ps[r] * Dt;
-    store_pack<T, 4>(sZs + m * Lay::LDZS + 4 * g, v4);
-    store_pack<T, 4>(sZs + m * Lay::LDZS + 16 + 4 * g, z4);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sdZs[(16 * I + m) * 16 + 4 * g + r] = v4[r];
-  }
-  wave_lds_sync();
+  for (int e = 0; e < NS; ++e) sf[e] = M::pack(zsv + e * M::KPL);
   // dq^T[d][t] = scale (K^T dZ^T + mu^T dZs^T)
   T* dqa = reinterpret_cast<T*>(a.dq) + (size_t)bh * L * D;   // the anchor part; the gate kernel adds its own
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
     f32x4 o = zero4();
-    const T* bp = sSt + m * Lay::LDS + g * 24;
-    const T* ap = sKT + (16 * dt + m) * Lay::LDKT + U0 + g * 24;
+    const T* ap = sKT + (16 * dt + m) * Lay::LDKT;
 #pragma unroll
-    for (int e = 0; e < 24 / M::KPL; ++e) o = M::mma(M::load(ap + e * M::KPL), M::load(bp + e * M::KPL), o);
-    const T* bz = sZs + m * Lay::LDZS + g * 8;
-    const T* az = sMuT + (16 * dt + m) * Lay::LDMT + g * 8;
+    for (int e = 0; e < 24 / M::KPL; ++e) o = M::mma(window_frag<T>(ap, U0, g, e), zf[e], o);
+    const T* az = sMuT + (16 * dt + m) * Lay::LDMT;
 #pragma unroll
-    for (int e = 0; e < 8 / M::KPL; ++e) o = M::mma(M::load(az + e * M::KPL), M::load(bz + e * M::KPL), o);
+    for (int e = 0; e < NS; ++e) o = M::mma(sink_frag<T>(az, g, e), sf[e], o);
     if (tme < L) {
       const float v4[4] = {o[0] * a.scale, o[1] * a.scale, o[2] * a.scale, o[3] * a.scale};
       store_pack<T, 4>(dqa + (size_t)tme * D + 16 * dt + 4 * g, v4);
     }
   }
-  // per-chunk sink-key gradient: dmu[i][d] = scale sum_t dZs[t][i] q[t][d]
+  // per-chunk sink-key gradient dmu^T[d][i] = scale sum_t q[t][d] dZs[t][i],
+  // on the matrix cores: the chunk's query rows (from the registers) replace
+  // the key tile; wavefront w takes dim tiles w, w + 4, ...
   if (a.n_meta > 0) {
-    __syncthreads();                      // the key tile is free: the chunk's queries go there
-    stage_rows<T, D, 64>(sQ, Lay::LDQ, qg, t0, L);
+    __syncthreads();                      // the key tile is free
+#pragma unroll
+    for (int e = 0; e < QV; ++e) st16(sQ + (16 * I + m) * Lay::LDQ + g * (D / 4) + e * EPV, qraw[e]);
     __syncthreads();
     float* part = a.ws_dmu + ((size_t)bh * nc + c) * a.n_meta * D;
-    for (int o = tid; o < a.n_meta * D; o += 256) {
-      const int i = o / D, d = o % D;
-      float s = 0.f;
-      for (int t = 0; t < 64; ++t) s += sdZs[t * 16 + i] * to_f32(sQ[t * Lay::LDQ + d]);
-      part[o] = s * a.scale;
+#pragma unroll
+    for (int dt = w; dt < NDT; dt += 4) {
+      f32x4 o = zero4();
+#pragma unroll
+      for (int e = 0; e < 64 / M::KSTEP; ++e) {
+        float qa[M::KPL], za[M::KPL];
+#pragma unroll
+        for (int u = 0; u < M::KPL; ++u) {
+          const int t = e * M::KSTEP + g * M::KPL + u;
+          qa[u] = to_f32(sQ[t * Lay::LDQ + 16 * dt + m]);
+          za[u] = sdZs[t * 16 + m];
+        }
+        o = M::mma(M::pack(qa), M::pack(za), o);
+      }
+      // lane: dims 16 dt + 4 g + r of sink m
+      if (m < a.n_meta) {
+        const float v4[4] = {o[0] * a.scale, o[1] * a.scale, o[2] * a.scale, o[3] * a.scale};
+        *reinterpret_cast<float4*>(part + (size_t)m * D + 16 * dt + 4 * g) = make_float4(v4[0], v4[1], v4[2], v4[3]);
+      }
     }
   }
 }
@@ -536,19 +588,17 @@ template <typename T, int D>
 struct AkLayout {
   static constexpr int PAD = 16 / sizeof(T);
   static constexpr int LDT = 128 + PAD;    // sQT, sdYT [D][LDT]
-  static constexpr int LDS = 96 + PAD;     // per-wave staging [16][LDS], two of them
   static constexpr int a16(int x) { return (x + 15) / 16 * 16; }
   static constexpr int OFF_QT = 0;
   static constexpr int OFF_DYT = OFF_QT + a16(D * LDT * (int)sizeof(T));
-  static constexpr int OFF_ST = OFF_DYT + a16(D * LDT * (int)sizeof(T));
-  static constexpr int OFF_RW = OFF_ST + a16(2 * 4 * 16 * LDS * (int)sizeof(T));   // lse*log2e, D_t: [2][128] fp32
+  static constexpr int OFF_RW = OFF_DYT + a16(D * LDT * (int)sizeof(T));   // lse*log2e, D_t: [2][128] fp32
   static constexpr int TOTAL = OFF_RW + a16(2 * 128 * 4);
 };
 
 // The grid covers chunks cb .. cb + ncl - 1; GUARD = false: they are interior
-// (the queries [t0, t0 + 128) lie inside [0, L)).
+// (the queries [t0, t0 + 128) lie inside [0, L)).  Two workgroups per CU.
 template <typename T, int D, bool GUARD>
-__global__ __launch_bounds__(256, 1) void bwd_anchor_k_kernel(BwdArgs a, int cb, int ncl) {
+__global__ __launch_bounds__(256, 2) void bwd_anchor_k_kernel(BwdArgs a, int cb, int ncl) {
   typedef AkLayout<T, D> Lay;
   typedef Mfma<T> M;
   constexpr int EPV = 16 / sizeof(T);
@@ -567,8 +617,6 @@ __global__ __launch_bounds__(256, 1) void bwd_anchor_k_kernel(BwdArgs a, int cb,
   c += cb;
   const int t0 = c * C;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
-  T* sZ = reinterpret_cast<T*>(smem + Lay::OFF_ST) + w * 16 * Lay::LDS;
-  T* sP = reinterpret_cast<T*>(smem + Lay::OFF_ST) + (4 + w) * 16 * Lay::LDS;
   const T* qg = reinterpret_cast<const T*>(a.q) + (size_t)bh * L * D;
   const T* kg = reinterpret_cast<const T*>(a.k) + (size_t)bh * L * D;
   const T* vg = reinterpret_cast<const T*>(a.v) + (size_t)bh * L * D;
@@ -615,36 +663,39 @@ __global__ __launch_bounds__(256, 1) void bwd_anchor_k_kernel(BwdArgs a, int cb,
     z[kt] = zc;
     dp[kt] = pc;
   }
+  // dZ and P of key sme for the lane's 24 window queries, kept as operand
+  // fragments in the window order (value 4 kt + r)
+  float pz[24], pp[24];
 #pragma unroll
   for (int kt = 0; kt < 6; ++kt) {
-    float pz[4], pp[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tr = Q0 + 16 * kt + 4 * g + r;   // query relative to t0
       const int t = t0 + tr;
       const bool ok = t < L && sme < L && t >= sme && t < sme + a.window;
       const float p = ok ? exp_2(z[kt][r] * sl2 - sLse[tr]) : 0.f;
-      pz[r] = p * (dp[kt][r] * a.alpha - sD[tr]);
-      pp[r] = p * a.alpha;
+      pz[4 * kt + r] = p * (dp[kt][r] * a.alpha - sD[tr]);
+      pp[4 * kt + r] = p * a.alpha;
     }
-    store_pack<T, 4>(sZ + m * Lay::LDS + 16 * kt + 4 * g, pz);
-    store_pack<T, 4>(sP + m * Lay::LDS + 16 * kt + 4 * g, pp);
   }
-  wave_lds_sync();
+  typename M::frag zf[24 / M::KPL], pf[24 / M::KPL];
+#pragma unroll
+  for (int e = 0; e < 24 / M::KPL; ++e) {
+    zf[e] = M::pack(pz + e * M::KPL);
+    pf[e] = M::pack(pp + e * M::KPL);
+  }
   // the anchor parts of dk and dv; the gate kernel adds its own
   T* dka = reinterpret_cast<T*>(a.dk) + (size_t)bh * L * D;
   T* dva = reinterpret_cast<T*>(a.dv) + (size_t)bh * L * D;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
     f32x4 ok_ = zero4(), ov = zero4();
-    const T* bz = sZ + m * Lay::LDS + g * 24;
-    const T* bpp = sP + m * Lay::LDS + g * 24;
-    const T* aq = sQT + (16 * dt + m) * Lay::LDT + Q0 + g * 24;
-    const T* ay = sdYT + (16 * dt + m) * Lay::LDT + Q0 + g * 24;
+    const T* aq = sQT + (16 * dt + m) * Lay::LDT;
+    const T* ay = sdYT + (16 * dt + m) * Lay::LDT;
 #pragma unroll
     for (int e = 0; e < 24 / M::KPL; ++e) {
-      ok_ = M::mma(M::load(aq + e * M::KPL), M::load(bz + e * M::KPL), ok_);
-      ov = M::mma(M::load(ay + e * M::KPL), M::load(bpp + e * M::KPL), ov);
+      ok_ = M::mma(window_frag<T>(aq, Q0, g, e), zf[e], ok_);
+      ov = M::mma(window_frag<T>(ay, Q0, g, e), pf[e], ov);
     }
     if (sme < L) {
       const float k4[4] = {ok_[0] * a.scale, ok_[1] * a.scale, ok_[2] * a.scale, ok_[3] * a.scale};
@@ -1297,7 +1348,7 @@ hipError_t launch_bwd_t(BwdArgs a, hipStream_t st) {
     const int nfull = L / C;
     // 3. anchor, query side: chunk 0 and a ragged last chunk range-checked, the rest not
     typedef AqLayout<T, D> AQ;
-    static_assert(AQ::TOTAL <= 80 * 1024, "LDS: two workgroups per CU");
+    static_assert(AQ::TOTAL <= 53 * 1024, "LDS: three workgroups per CU");
     if ((e = set_lds(&bwd_anchor_q_kernel<T, D, true>, AQ::TOTAL)) != hipSuccess) return e;
     if ((e = set_lds(&bwd_anchor_q_kernel<T, D, false>, AQ::TOTAL)) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_anchor_q_kernel<T, D, true>), dim3(8 * groups), dim3(256), AQ::TOTAL, st, a, 0, 1);
@@ -1309,7 +1360,7 @@ hipError_t launch_bwd_t(BwdArgs a, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // 4. anchor, key side: chunks whose query range [t0, t0 + 128) ends past L range-checked
     typedef AkLayout<T, D> AK;
-    static_assert(AK::TOTAL <= 160 * 1024, "LDS");
+    static_assert(AK::TOTAL <= 80 * 1024, "LDS: two workgroups per CU");
     if ((e = set_lds(&bwd_anchor_k_kernel<T, D, true>, AK::TOTAL)) != hipSuccess) return e;
     if ((e = set_lds(&bwd_anchor_k_kernel<T, D, false>, AK::TOTAL)) != hipSuccess) return e;
     const int nk_in = nfull > 1 ? nfull - 1 : 0;   // chunks c with t0 + 128 <= L
