@@ -54,7 +54,9 @@
 
 namespace lizard {
 
-template <typename T, int D, int DV>
+// STATES: the states-only pass, which needs only the value ring, the Kh tile
+// and the prefix totals (two workgroups per CU).
+template <typename T, int D, int DV, bool STATES = false>
 struct FwdLayout {
   static constexpr int PAD = 16 / sizeof(T);
   static constexpr int LDK = D + PAD;       // sK ring [128][LDK]; sKp, sQe [64][LDK]; sMeta [16][LDK]
@@ -64,16 +66,17 @@ struct FwdLayout {
   static constexpr int LDP = 96 + PAD;      // window weights P, per query block [16][LDP]
   static constexpr int LDA = 64 + PAD;      // bf16: intra scores A, per query block [16][LDA]
   static constexpr int LDE = D + 4;         // wide-span chunks: beta [64][LDE] float over sKp, sQe
-  static constexpr bool STAGE_A = sizeof(T) == 2;
+  static constexpr bool STAGE_A = sizeof(T) == 2 && !STATES;
   static constexpr int a16(int x) { return (x + 15) / 16 * 16; }
+  static constexpr int N = STATES ? 0 : 1;  // buffers the states-only pass leaves out
   static constexpr int OFF_K = 0;
-  static constexpr int OFF_VT = OFF_K + a16(128 * LDK * (int)sizeof(T));
+  static constexpr int OFF_VT = OFF_K + N * a16(128 * LDK * (int)sizeof(T));
   static constexpr int OFF_KP = OFF_VT + a16(DV * LDVT * (int)sizeof(T));
-  static constexpr int OFF_QE = OFF_KP + a16(64 * LDK * (int)sizeof(T));
-  static constexpr int OFF_KHT = OFF_QE + a16(64 * LDK * (int)sizeof(T));
+  static constexpr int OFF_QE = OFF_KP + N * a16(64 * LDK * (int)sizeof(T));
+  static constexpr int OFF_KHT = OFF_QE + N * a16(64 * LDK * (int)sizeof(T));
   static constexpr int OFF_ST = OFF_KHT + a16(D * LDKH * (int)sizeof(T));
-  static constexpr int OFF_P = OFF_ST + a16(DV * LDST * (int)sizeof(T));
-  static constexpr int OFF_A = OFF_P + a16(4 * 16 * LDP * (int)sizeof(T));
+  static constexpr int OFF_P = OFF_ST + N * a16(DV * LDST * (int)sizeof(T));
+  static constexpr int OFF_A = OFF_P + N * a16(4 * 16 * LDP * (int)sizeof(T));
   static constexpr int A_BYTES = STAGE_A ? a16(4 * 16 * LDA * (int)sizeof(T)) : 0;
   static constexpr int OFF_TOT = OFF_A + A_BYTES;
   // wide-span totals: over the A staging when there is one (both are free in
@@ -81,9 +84,9 @@ struct FwdLayout {
   static constexpr int OFF_TOTC = STAGE_A ? OFF_A : OFF_TOT + a16(8 * D * 4);
   static constexpr int OFF_BEXP = OFF_TOT + a16(8 * D * 4) + (STAGE_A ? 0 : a16(8 * D * 4));
   static constexpr int OFF_SC = OFF_BEXP + a16(D * 4);          // [2][64]: alpha/den, 1/den
-  static constexpr int OFF_META = OFF_SC + a16(2 * 64 * 4);
-  static constexpr int TOTAL = OFF_META + a16(16 * LDK * (int)sizeof(T));
-  static_assert(64 * LDE * 4 <= OFF_KHT - OFF_KP, "beta fits over sKp and sQe");
+  static constexpr int OFF_META = OFF_SC + N * a16(2 * 64 * 4);
+  static constexpr int TOTAL = OFF_META + N * a16(16 * LDK * (int)sizeof(T));
+  static_assert(STATES || 64 * LDE * 4 <= OFF_KHT - OFF_KP, "beta fits over sKp and sQe");
   static_assert(!STAGE_A || 8 * D * 4 <= A_BYTES, "wide-span totals fit over the A staging");
 };
 
@@ -139,8 +142,8 @@ constexpr float kMaxSpanLog2 = 92.0f;
 constexpr float kSegSkipLog2 = -128.0f;
 
 template <typename T, int D, int DV, bool STATES, bool LOGIT, bool SEG>
-__global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
-  typedef FwdLayout<T, D, DV> Lay;
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(STATES ? 4 : 2))) void lizard_fwd_kernel(FwdArgs a) {
+  typedef FwdLayout<T, D, DV, STATES> Lay;
   typedef Mfma<T> M;
   typedef typename M::frag frag;
   constexpr int C = 64;
@@ -224,21 +227,25 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
       vhp = reinterpret_cast<const T*>(a.v_halo) + (size_t)bh * a.halo * D + j0;
     }
     const int hb = ph + 64 - nh;                   // first filled key ring row
-    for (int i = tid; i < 128 * Lay::LDK; i += 512) {
-      const int row = i / Lay::LDK, col = i % Lay::LDK;
-      sK[i] = row >= hb && row < ph + 64 && col < D ? khp[(size_t)(row - hb) * D + col] : from_f32<T>(0.f);
-    }
     const int vb = ps + 64 - nh;                   // first filled value ring column
-    for (int i = tid; i < DV * Lay::LDVT; i += 512) {
-      const int j = i / Lay::LDVT, col = i % Lay::LDVT;
-      sVt[i] = col >= vb && col < ps + 64 ? vhp[(size_t)(col - vb) * D + j] : from_f32<T>(0.f);
+    if constexpr (!STATES) {                       // (the states-only pass reads neither ring across chunks)
+      for (int i = tid; i < 128 * Lay::LDK; i += 512) {
+        const int row = i / Lay::LDK, col = i % Lay::LDK;
+        sK[i] = row >= hb && row < ph + 64 && col < D ? khp[(size_t)(row - hb) * D + col] : from_f32<T>(0.f);
+      }
+      for (int i = tid; i < DV * Lay::LDVT; i += 512) {
+        const int j = i / Lay::LDVT, col = i % Lay::LDVT;
+        sVt[i] = col >= vb && col < ps + 64 ? vhp[(size_t)(col - vb) * D + j] : from_f32<T>(0.f);
+      }
     }
   }
   // ---- sink keys (rows >= n_meta zero), resident in LDS throughout ----
-  for (int i = tid; i < 16 * D; i += 512) {
-    const int r = i / D, cidx = i % D;
-    sMeta[r * Lay::LDK + cidx] =
-        r < a.n_meta ? reinterpret_cast<const T*>(a.meta)[((size_t)h * a.n_meta + r) * D + cidx] : from_f32<T>(0.f);
+  if constexpr (!STATES) {
+    for (int i = tid; i < 16 * D; i += 512) {
+      const int r = i / D, cidx = i % D;
+      sMeta[r * Lay::LDK + cidx] =
+          r < a.n_meta ? reinterpret_cast<const T*>(a.meta)[((size_t)h * a.n_meta + r) * D + cidx] : from_f32<T>(0.f);
+    }
   }
 
   // Each (role, query block) runs its own copy of the chunk loop: role 0 the
@@ -317,13 +324,13 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
           } else {
             lv[0] = lp[ro];
           }
-          uint32_t kv, qv;
+          uint32_t kv, qv = 0u;   // the states-only pass needs no queries
           if constexpr (DPL * sizeof(T) == 4) {
             kv = *reinterpret_cast<const uint32_t*>(kp + ro);
-            qv = *reinterpret_cast<const uint32_t*>(qp + ro);
+            if constexpr (!STATES) qv = *reinterpret_cast<const uint32_t*>(qp + ro);
           } else {
             kv = *reinterpret_cast<const uint16_t*>(kp + ro);
-            qv = *reinterpret_cast<const uint16_t*>(qp + ro);
+            if constexpr (!STATES) qv = *reinterpret_cast<const uint16_t*>(qp + ro);
           }
           if constexpr (LOGIT) {
             // past L: a logit of +inf, a gate of one (as log_g = 0 below)
@@ -477,9 +484,11 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
             const float beta = fmaf(loc[rr][dd], kLog2e, off[dd]);
             kp[dd] = elem32(kA[rr], dd) * exp_2(-beta);
             kh[dd][rr] = kp[dd] * ehr[dd];
-            qe[dd] = elem32(qA[rr], dd) * exp_2(beta);
+            qe[dd] = STATES ? 0.f : elem32(qA[rr], dd) * exp_2(beta);
           }
-          if constexpr (DPL == 2) {
+          // (the states-only pass needs only Kh)
+          if constexpr (STATES) {
+          } else if constexpr (DPL == 2) {
             *reinterpret_cast<bf16x2*>(sQe + s * Lay::LDK + 2 * l) = bf16x2{static_cast<bf16>(qe[0]), static_cast<bf16>(qe[1])};
             *reinterpret_cast<bf16x2*>(sKp + s * Lay::LDK + 2 * l) = bf16x2{static_cast<bf16>(kp[0]), static_cast<bf16>(kp[1])};
           } else {
@@ -514,7 +523,7 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
           for (int dd = 0; dd < DPL; ++dd) {
             const float beta = off[dd] + locc[rr][dd];
             kh[dd][rr] = elem32(kA[rr], dd) * exp_2(Bt[dd] - beta);
-            sBeta[s * Lay::LDE + DPL * l + dd] = beta;
+            if constexpr (!STATES) sBeta[s * Lay::LDE + DPL * l + dd] = beta;
           }
         }
       }
@@ -536,12 +545,14 @@ __global__ __launch_bounds__(512, 1) void lizard_fwd_kernel(FwdArgs a) {
         // this wavefront's lanes cover all D dimensions: a uniform value
         if (live_end == c_hi && wave_max(mx) < kSegSkipLog2) live_end = cc;
       }
-      // raw keys into the ring
+      // raw keys into the ring (for the window; not in the states-only pass)
+      if constexpr (!STATES) {
   #pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        T* krp = sK + (kc + 8 * w + rr) * Lay::LDK + DPL * l;
-        if constexpr (DPL * sizeof(T) == 4) *reinterpret_cast<uint32_t*>(krp) = kA[rr];
-        else krp[0] = from_f32<T>(elem32(kA[rr], 0));
+        for (int rr = 0; rr < 8; ++rr) {
+          T* krp = sK + (kc + 8 * w + rr) * Lay::LDK + DPL * l;
+          if constexpr (DPL * sizeof(T) == 4) *reinterpret_cast<uint32_t*>(krp) = kA[rr];
+          else krp[0] = from_f32<T>(elem32(kA[rr], 0));
+        }
       }
       // values, transposed into their ring slot: sVt[j][vc + s], 4 tokens per write
       if constexpr (sizeof(T) == 2) {
@@ -1217,7 +1228,7 @@ __global__ __launch_bounds__(256, 2) void fwd_seg_fix_kernel(FwdArgs a) {
 
 template <typename T, int D, int DV, bool STATES, bool LOGIT, bool SEG>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
-  typedef FwdLayout<T, D, DV> Lay;
+  typedef FwdLayout<T, D, DV, STATES> Lay;
   static_assert(Lay::TOTAL <= 160 * 1024, "LDS budget");
   static_assert(D == 128 || (D == 64 && sizeof(T) == 2) || (D == 64 && DV == 32), "shapes");
   const int smem = Lay::TOTAL;
