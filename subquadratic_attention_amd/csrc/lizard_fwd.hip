@@ -141,9 +141,14 @@ constexpr float kMaxSpanLog2 = 92.0f;
 // correction stops at the first such chunk.
 constexpr float kSegSkipLog2 = -128.0f;
 
-template <typename T, int D, int DV, bool STATES, bool LOGIT, bool SEG>
+// MODE: kPlain, kSeg (a segment of a split sequence) or kTrain (the full
+// forward that also keeps the chunk-start states); STATES: the states-only pass.
+enum { kPlain = 0, kSeg = 1, kTrain = 2 };
+template <typename T, int D, int DV, bool STATES, bool LOGIT, int MODE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(STATES ? 4 : 2))) void lizard_fwd_kernel(FwdArgs a) {
   typedef FwdLayout<T, D, DV, STATES> Lay;
+  constexpr bool SEG = MODE == kSeg;
+  constexpr bool KEEP_STATES = STATES || MODE == kTrain;
   typedef Mfma<T> M;
   typedef typename M::frag frag;
   constexpr int C = 64;
@@ -598,7 +603,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(STATES ? 4 
               }
           }
         }
-        if (STATES || (!SEG && a.states)) {
+        if constexpr (KEEP_STATES) {
           // chunk-start state for the backward pass: S_cc[i][j], row-major
           // (the states-only pass, or a training forward that keeps them)
           const int ncs = (L + C - 1) / C;
@@ -1226,18 +1231,19 @@ __global__ __launch_bounds__(256, 2) void fwd_seg_fix_kernel(FwdArgs a) {
   }
 }
 
-template <typename T, int D, int DV, bool STATES, bool LOGIT, bool SEG>
+template <typename T, int D, int DV, bool STATES, bool LOGIT, int MODE>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
+  constexpr bool SEG = MODE == kSeg;
   typedef FwdLayout<T, D, DV, STATES> Lay;
   static_assert(Lay::TOTAL <= 160 * 1024, "LDS budget");
   static_assert(D == 128 || (D == 64 && sizeof(T) == 2) || (D == 64 && DV == 32), "shapes");
   const int smem = Lay::TOTAL;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lizard_fwd_kernel<T, D, DV, STATES, LOGIT, SEG>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lizard_fwd_kernel<T, D, DV, STATES, LOGIT, MODE>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, smem);
   if (e != hipSuccess) return e;
   const int groups = (a.BH + 7) / 8;
   dim3 grid(8 * groups * a.nsplit * (SEG ? a.nseg : 1));
-  hipLaunchKernelGGL((lizard_fwd_kernel<T, D, DV, STATES, LOGIT, SEG>), grid, dim3(512), smem, st, a);
+  hipLaunchKernelGGL((lizard_fwd_kernel<T, D, DV, STATES, LOGIT, MODE>), grid, dim3(512), smem, st, a);
   return hipGetLastError();
 }
 
@@ -1265,14 +1271,19 @@ static hipError_t launch_fwd_s(const FwdArgs& a, hipStream_t st) {
   // outputs: the full forward, keeping the states as well
   if (a.states && !a.y) {
     if (a.nseg != 1) return hipErrorInvalidValue;
-    return a.gate_logit ? launch_fwd_t<T, D, DV, true, true, false>(a, st)
-                        : launch_fwd_t<T, D, DV, true, false, false>(a, st);
+    return a.gate_logit ? launch_fwd_t<T, D, DV, true, true, kPlain>(a, st)
+                        : launch_fwd_t<T, D, DV, true, false, kPlain>(a, st);
+  }
+  if (a.states) {
+    if (a.nseg != 1) return hipErrorInvalidValue;
+    return a.gate_logit ? launch_fwd_t<T, D, DV, false, true, kTrain>(a, st)
+                        : launch_fwd_t<T, D, DV, false, false, kTrain>(a, st);
   }
   if (a.nseg <= 1)
-    return a.gate_logit ? launch_fwd_t<T, D, DV, false, true, false>(a, st)
-                        : launch_fwd_t<T, D, DV, false, false, false>(a, st);
-  hipError_t e = a.gate_logit ? launch_fwd_t<T, D, DV, false, true, true>(a, st)
-                              : launch_fwd_t<T, D, DV, false, false, true>(a, st);
+    return a.gate_logit ? launch_fwd_t<T, D, DV, false, true, kPlain>(a, st)
+                        : launch_fwd_t<T, D, DV, false, false, kPlain>(a, st);
+  hipError_t e = a.gate_logit ? launch_fwd_t<T, D, DV, false, true, kSeg>(a, st)
+                              : launch_fwd_t<T, D, DV, false, false, kSeg>(a, st);
   if (e != hipSuccess) return e;
   return a.gate_logit ? launch_seg_finish<T, D, true>(a, st) : launch_seg_finish<T, D, false>(a, st);
 }
