@@ -137,20 +137,6 @@ __device__ __forceinline__ void stage_T(T* dst, int ld, const T* src, int r0, in
   stage_T_store<T, COLS, NR, NTH>(dst, ld, w, scale);
 }
 
-// Stage rows [r0, r0 + NR) of a [L, D] tensor into LDS row-major (ld elements per row).
-template <typename T, int D, int NR>
-__device__ __forceinline__ void stage_rows(T* dst, int ld, const T* src, int r0, int L) {
-  constexpr int EPV = 16 / sizeof(T);
-  constexpr int VPR = D / EPV;
-  for (int i = threadIdx.x; i < NR * VPR; i += 256) {
-    const int row = i / VPR, cv = i % VPR;
-    const int gr = r0 + row;
-    const bool ok = gr >= 0 && gr < L;
-    const uint4 u = ld16(src + (size_t)(ok ? gr : 0) * D + cv * EPV);
-    *reinterpret_cast<uint4*>(dst + row * ld + cv * EPV) = ok ? u : make_uint4(0, 0, 0, 0);
-  }
-}
-
 // Block -> (bh, chunk) with every chunk of one head on the same XCD.
 __device__ __forceinline__ bool chunk_block(int BH, int nc, int& bh, int& c) {
   const int x = blockIdx.x;
