@@ -241,7 +241,8 @@ lizard_status_t lizard_attn_fwd_train(const lizard_params_t* p,
  * for the same q, k, v, gates and sizes instead of recomputing them:
  *   chunk_states  [B, H, ceil(L/64), dk, dv] dtype, in, 16-byte aligned
  * Every other argument, the workspace (lizard_attn_bwd_workspace_size) and
- * every result as lizard_attn_bwd; the results are those of lizard_attn_bwd.
+ * every result as lizard_attn_bwd; the results are those of lizard_attn_bwd
+ * (at float32 up to the last bits of the carried state's rounding).
  * chunk_states NULL with B*H*L > 0: LIZARD_E_NULL. */
 lizard_status_t lizard_attn_bwd_train(const lizard_params_t* p,
                                       const void* q, const void* k, const void* v,

@@ -13,7 +13,8 @@ from tests.gpu_util import assert_close, down, flat, log, meta_per_slice, up, up
 pytestmark = pytest.mark.gpu
 
 GATES = {"fast": dict(gate_mu=2.0, gate_sd=2.0), "slow": dict(gate_mu=6.0, gate_sd=1.0),
-         "reset": dict(gate_mu=4.0, gate_sd=1.0, hard_reset_frac=0.01)}
+         "reset": dict(gate_mu=4.0, gate_sd=1.0, hard_reset_frac=0.01),
+         "wide": dict(gate_mu=0.0, gate_sd=3.0)}   # chunks of every decay-span tier
 
 
 def _segments(sqa, B, H, L, d, dtype):

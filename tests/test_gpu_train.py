@@ -2,7 +2,8 @@
 the forward's outputs are those of lizard_attn_fwd bit for bit, the chunk-start
 states it keeps are the oracle's recurrent states at every chunk start, and the
 backward that reads them gives lizard_attn_bwd's results (which recomputes
-them) and the oracle's gradients."""
+them: bit for bit at bf16, to float rounding at fp32) and the oracle's
+gradients."""
 import numpy as np
 import pytest
 
@@ -22,13 +23,17 @@ def _upload(x, dtype, logit):
     return q, k, v, dy, meta, gate
 
 
+@pytest.mark.parametrize("gates", ["N(2,2)", "N(0,3)"])
 @pytest.mark.parametrize("logit", [False, True])
 @pytest.mark.parametrize("dtype,d,L", [("f32", 64, 150), ("bf16", 128, 200), ("bf16", 64, 64), ("bf16", 128, 1)])
-def test_train_pair_matches_the_plain_calls(gpu_lib, dtype, d, L, logit):
+def test_train_pair_matches_the_plain_calls(gpu_lib, dtype, d, L, logit, gates):
+    """N(0,3) gate logits put chunks in every decay-span tier (the pairwise
+    path included) on both sides."""
     import torch
 
-    x = si.custom_inputs(70, 2, 2, L, d, 4, dtype, with_dy=True, gate_mu=2.0, gate_sd=2.0)
-    log(f"train pair dtype={dtype} d={d} L={L} logit={logit}")
+    mu, sd = {"N(2,2)": (2.0, 2.0), "N(0,3)": (0.0, 3.0)}[gates]
+    x = si.custom_inputs(70, 2, 2, L, d, 4, dtype, with_dy=True, gate_mu=mu, gate_sd=sd)
+    log(f"train pair dtype={dtype} d={d} L={L} logit={logit} gates={gates}")
     q, k, v, dy, meta, gate = _upload(x, dtype, logit)
     kw = dict(window=48, alpha=0.5)
     tr = gpu_lib.lizard_attn_fwd_train(q, k, v, meta, need_y_anchor=True, need_state=True, **gate, **kw)
@@ -48,7 +53,12 @@ def test_train_pair_matches_the_plain_calls(gpu_lib, dtype, d, L, logit):
         gr = gpu_lib.lizard_attn_bwd(q, k, v, gate["log_g"], meta, fw["lse"], dy, **kw)
     torch.cuda.synchronize()
     for key in ("dq", "dk", "dv", GKEY[logit], "dmeta"):
-        assert torch.equal(gb[key], gr[key]), key
+        if dtype == "bf16":
+            assert torch.equal(gb[key], gr[key]), key
+        else:
+            # fp32: the two forward instances that write the chunk states may
+            # round the carried state differently in the last bits
+            assert_close(down(gb[key]), down(gr[key]), "f32", f"saved vs recomputed {key}", tau=1e-5)
 
 
 @pytest.mark.parametrize("dtype,d,L", [("f32", 64, 200), ("bf16", 128, 300)])
