@@ -244,13 +244,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(STATES ? 4 
       }
     }
   }
-  // ---- sink keys (rows >= n_meta zero), resident in LDS throughout ----
+  // ---- sink keys (rows >= n_meta zero), resident in LDS throughout; the
+  // window weights' last 16 slots (the sixth key tile of the V^T P^T
+  // product, which the five logit tiles never reach) stay zero ----
   if constexpr (!STATES) {
     for (int i = tid; i < 16 * D; i += 512) {
       const int r = i / D, cidx = i % D;
       sMeta[r * Lay::LDK + cidx] =
           r < a.n_meta ? reinterpret_cast<const T*>(a.meta)[((size_t)h * a.n_meta + r) * D + cidx] : from_f32<T>(0.f);
     }
+    for (int i = tid; i < 64 * 16; i += 512) sP[(i / 16) * Lay::LDP + 80 + i % 16] = from_f32<T>(0.f);
   }
 
   // Each (role, query block) runs its own copy of the chunk loop: role 0 the
@@ -666,7 +669,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(STATES ? 4 
       // ================= interval 1, softmax wavefront: weights of block QB ====
       auto softmax_part = [&](auto Ic) __attribute__((always_inline)) {
         constexpr int QB = decltype(Ic)::value;
-        constexpr int U0 = 16 * QB < 32 ? 16 * QB : 32; // first window key (of [prev; cur]) staged
+        constexpr int U0 = 16 * QB;          // first window key (of [prev; cur]) staged
         // Lane indices laundered through an empty asm: addresses derived from
         // them are recomputed per chunk instead of being hoisted out of the
         // chunk loop by every instance (which would exhaust registers).
@@ -682,13 +685,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(STATES ? 4 
         // the wait for it then counts, instead of draining all loads in flight.
         load_q(c + 1 < c_hi ? c + 1 : c);
 
-        // anchor logits Z^T[u][t] over the 6 window tiles kt (keys u in
-        // [U0+16kt, U0+16kt+16) of [prev; cur]); every tile is computed, keys
-        // outside the window are masked below (branch-free: a skipped tile
-        // would make the compiler copy the logit arrays between paths)
-        f32x4 z[6];
+        // anchor logits Z^T[u][t] over the 5 window tiles kt (keys u in
+        // [U0+16kt, U0+16kt+16) of [prev; cur]: the block's queries reach
+        // back at most 63 keys from [U0+64, U0+80)); every tile is computed,
+        // keys outside the window are masked below (branch-free: a skipped
+        // tile would make the compiler copy the logit arrays between paths)
+        f32x4 z[5];
   #pragma unroll
-        for (int kt = 0; kt < 6; ++kt) {
+        for (int kt = 0; kt < 5; ++kt) {
           const T* kp = sK + ((U0 + 16 * kt + kprv + m) & 127) * Lay::LDK + g * (D / 4);
           z[kt] = zero4();
   #pragma unroll
@@ -713,7 +717,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(STATES ? 4 
         const int lim_lo = (c == 0 && 16 * QB + hl1 < a.window) ? 16 * QB + hl1 : a.window;   // over the block
         const int dl = m - 4 * g;            // t - s = K_kt + dl - r
   #pragma unroll
-        for (int kt = 0; kt < 6; ++kt) {
+        for (int kt = 0; kt < 5; ++kt) {
           // t - s over the tile spans [K_kt - 15, K_kt + 15]: tiles inside the band skip the mask
           constexpr int K0 = 16 * QB + 64 - U0;
           const int Kt = K0 - 16 * kt;
@@ -730,7 +734,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(STATES ? 4 
   #pragma unroll
         for (int r = 0; r < 4; ++r) sr += exp_2(fmaf(zs[r], a.scale_log2, -mref));
   #pragma unroll
-        for (int kt = 0; kt < 6; ++kt) {
+        for (int kt = 0; kt < 5; ++kt) {
           float p[4];
   #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -889,7 +893,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(STATES ? 4 
       // ========== interval 2, gate wavefront: anchor product and output =======
       auto output_part = [&](auto Ic) __attribute__((always_inline)) {
         constexpr int QB = decltype(Ic)::value;
-        constexpr int U0 = 16 * QB < 32 ? 16 * QB : 32;
+        constexpr int U0 = 16 * QB;
         int m = m_lane, g = g_lane;
         asm volatile("" : "+v"(m), "+v"(g));
         const int tme = t0 + 16 * QB + m;
