@@ -345,8 +345,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dstate_kernel(BwdArgs a) {
   }
 }
 
+// The window's key (or query) tiles of 16 around a block of 16 queries (or
+// keys): a query reaches back at most 63 keys, so 80 positions cover a block.
+constexpr int kWinTiles = 5;
+
 // Fragment e of a window-ordered operand row: the MFMA contraction runs over
-// the 96 window positions (keys for the query side, queries for the key
+// the 80 window positions (keys for the query side, queries for the key
 // side) in the order the score tiles leave them in a lane's registers (value
 // v = 4 kt + r of lane group g is position 16 kt + 4 g + r), so the scores
 // feed the next product from registers; the other operand (row p of a
@@ -355,14 +359,19 @@ template <typename T>
 __device__ __forceinline__ typename Mfma<T>::frag window_frag(const T* p, int q0, int g, int e) {
   typedef Mfma<T> M;
   if constexpr (sizeof(T) == 2) {
-    // values 8e .. 8e+7: tiles 2e and 2e+1, four consecutive queries each
+    // values 8e .. 8e+7: tiles 2e and 2e+1, four consecutive positions each;
+    // the window has five tiles, so the last step's second half is zero
     const uint2 a = *reinterpret_cast<const uint2*>(p + q0 + 32 * e + 4 * g);
-    const uint2 b = *reinterpret_cast<const uint2*>(p + q0 + 32 * e + 16 + 4 * g);
+    const uint2 b = 2 * e + 1 < kWinTiles ? *reinterpret_cast<const uint2*>(p + q0 + 32 * e + 16 + 4 * g)
+                                          : make_uint2(0u, 0u);
     return __builtin_bit_cast(typename M::frag, make_uint4(a.x, a.y, b.x, b.y));
   } else {
     return p[q0 + 16 * (e >> 2) + 4 * g + (e & 3)];
   }
 }
+// MFMA steps over the window values (bf16: 8 per step, the last one half
+// used; fp32: one per step)
+template <typename T> constexpr int window_steps() { return sizeof(T) == 2 ? 3 : 4 * kWinTiles; }
 
 // Fragment of the sink operand row p (16 sinks) in the same register order:
 // lane group g holds sinks 4g .. 4g + 3 (bf16: one step, the other four
@@ -429,7 +438,7 @@ __global__ __launch_bounds__(256, 3) void bwd_anchor_q_kernel(BwdArgs a, int cb,
 
   const int I = w;
   const int tme = t0 + 16 * I + m;
-  const int U0 = 16 * I < 32 ? 16 * I : 32;
+  const int U0 = 16 * I;                  // first window key of the tiles (of [t0 - 64, t0 + 64))
   // this lane's query and dY row, and the window keys / values of its
   // first three tiles, issued before the staging (their loads then overlap
   // it); the other three tiles reuse the registers (three workgroups per CU)
@@ -437,15 +446,15 @@ __global__ __launch_bounds__(256, 3) void bwd_anchor_q_kernel(BwdArgs a, int cb,
   load_quarter<T, D, GUARD>(qraw, qg, tme, L, g);
   load_quarter<T, D, GUARD>(dyraw, dyg, tme, L, g);
   uint4 kraw[3][QV], vraw[3][QV];
-  auto load_tiles = [&](int k0) __attribute__((always_inline)) {
+  auto load_tiles = [&](int k0, int n) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kk = 0; kk < 3; ++kk) {
+    for (int kk = 0; kk < n; ++kk) {
       const int s = t0 - 64 + U0 + 16 * (k0 + kk) + m;   // key row of this lane (MFMA row)
       load_quarter<T, D, GUARD>(kraw[kk], kg, s, L, g);
       load_quarter<T, D, GUARD>(vraw[kk], vg, s, L, g);
     }
   };
-  load_tiles(0);
+  load_tiles(0, 3);
   const float lse2 = !GUARD || tme < L ? a.lse[(size_t)bh * L + (tme < L ? tme : 0)] * kLog2e : 0.f;
 
   // window keys [t0 - 64, t0 + 64) transposed; sink keys transposed
@@ -457,12 +466,12 @@ __global__ __launch_bounds__(256, 3) void bwd_anchor_q_kernel(BwdArgs a, int cb,
   __syncthreads();
 
   // logits Z^T[u][t] and value products dP^T[u][t] for window keys u
-  f32x4 z[6], dp[6];
+  f32x4 z[kWinTiles], dp[kWinTiles];
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    if (half == 1) load_tiles(3);
+    if (half == 1) load_tiles(3, kWinTiles - 3);
 #pragma unroll
-    for (int kk = 0; kk < 3; ++kk) {
+    for (int kk = 0; kk < (half == 0 ? 3 : kWinTiles - 3); ++kk) {
       f32x4 zc = zero4(), pc = zero4();
 #pragma unroll
       for (int e = 0; e < NF; ++e) {
@@ -483,7 +492,7 @@ __global__ __launch_bounds__(256, 3) void bwd_anchor_q_kernel(BwdArgs a, int cb,
   // probabilities from the forward normaliser, D_t, dZ
   float dsum = 0.f;
 #pragma unroll
-  for (int kt = 0; kt < 6; ++kt)
+  for (int kt = 0; kt < kWinTiles; ++kt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int s = t0 - 64 + U0 + 16 * kt + 4 * g + r;
@@ -501,14 +510,17 @@ __global__ __launch_bounds__(256, 3) void bwd_anchor_q_kernel(BwdArgs a, int cb,
     ps[r] = (4 * g + r < a.n_meta && tme < L) ? exp_2(zs[r] * sl2 - lse2) : 0.f;
   // dZ[t][u] of the lane's query over its 24 window keys, as operand
   // fragments in the window order, and the sink part dZs[t][i] = -P D_t
-  float dz[24];
+  constexpr int NWS = window_steps<T>();
+  float dz[NWS * M::KPL];
 #pragma unroll
-  for (int kt = 0; kt < 6; ++kt)
+  for (int kt = 0; kt < kWinTiles; ++kt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) dz[4 * kt + r] = z[kt][r] * (dp[kt][r] - Dt);
-  typename M::frag zf[24 / M::KPL];
 #pragma unroll
-  for (int e = 0; e < 24 / M::KPL; ++e) zf[e] = M::pack(dz + e * M::KPL);
+  for (int v = 4 * kWinTiles; v < NWS * M::KPL; ++v) dz[v] = 0.f;
+  typename M::frag zf[NWS];
+#pragma unroll
+  for (int e = 0; e < NWS; ++e) zf[e] = M::pack(dz + e * M::KPL);
   float zsv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -526,7 +538,7 @@ __global__ __launch_bounds__(256, 3) void bwd_anchor_q_kernel(BwdArgs a, int cb,
     f32x4 o = zero4();
     const T* ap = sKT + (16 * dt + m) * Lay::LDKT;
 #pragma unroll
-    for (int e = 0; e < 24 / M::KPL; ++e) o = M::mma(window_frag<T>(ap, U0, g, e), zf[e], o);
+    for (int e = 0; e < NWS; ++e) o = M::mma(window_frag<T>(ap, U0, g, e), zf[e], o);
     const T* az = sMuT + (16 * dt + m) * Lay::LDMT;
 #pragma unroll
     for (int e = 0; e < NS; ++e) o = M::mma(sink_frag<T>(az, g, e), sf[e], o);
@@ -611,7 +623,7 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_k_kernel(BwdArgs a, int cb,
 
   const int J = w;                        // key block
   const int sme = t0 + 16 * J + m;        // this lane's key
-  const int Q0 = 16 * J < 32 ? 16 * J : 32;   // first staged query (relative to t0)
+  const int Q0 = 16 * J;                  // first window query of the tiles (relative to t0)
   // this lane's key and value rows, issued before the staging
   uint4 kraw[QV], vraw[QV];
   load_quarter<T, D, GUARD>(kraw, kg, sme, L, g);
@@ -629,13 +641,13 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_k_kernel(BwdArgs a, int cb,
 
   // Z[t][s] and dP[t][s] tiles: queries t on the MFMA rows; each tile's
   // query and dY rows are loaded one tile ahead
-  f32x4 z[6], dp[6];
+  f32x4 z[kWinTiles], dp[kWinTiles];
   uint4 qraw[2][QV], dyraw[2][QV];
   load_quarter<T, D, GUARD>(qraw[0], qg, t0 + Q0 + m, L, g);
   load_quarter<T, D, GUARD>(dyraw[0], dyg, t0 + Q0 + m, L, g);
 #pragma unroll
-  for (int kt = 0; kt < 6; ++kt) {
-    if (kt + 1 < 6) {
+  for (int kt = 0; kt < kWinTiles; ++kt) {
+    if (kt + 1 < kWinTiles) {
       const int tn = t0 + Q0 + 16 * (kt + 1) + m;
       load_quarter<T, D, GUARD>(qraw[(kt + 1) & 1], qg, tn, L, g);
       load_quarter<T, D, GUARD>(dyraw[(kt + 1) & 1], dyg, tn, L, g);
@@ -649,11 +661,14 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_k_kernel(BwdArgs a, int cb,
     z[kt] = zc;
     dp[kt] = pc;
   }
-  // dZ and P of key sme for the lane's 24 window queries, kept as operand
-  // fragments in the window order (value 4 kt + r)
-  float pz[24], pp[24];
+  // dZ and P of key sme for the lane's 20 window queries, kept as operand
+  // fragments in the window order (value 4 kt + r; zero past the window)
+  constexpr int NWS = window_steps<T>();
+  float pz[NWS * M::KPL], pp[NWS * M::KPL];
 #pragma unroll
-  for (int kt = 0; kt < 6; ++kt) {
+  for (int v = 4 * kWinTiles; v < NWS * M::KPL; ++v) pz[v] = pp[v] = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < kWinTiles; ++kt) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tr = Q0 + 16 * kt + 4 * g + r;   // query relative to t0
@@ -664,9 +679,9 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_k_kernel(BwdArgs a, int cb,
       pp[4 * kt + r] = p * a.alpha;
     }
   }
-  typename M::frag zf[24 / M::KPL], pf[24 / M::KPL];
+  typename M::frag zf[NWS], pf[NWS];
 #pragma unroll
-  for (int e = 0; e < 24 / M::KPL; ++e) {
+  for (int e = 0; e < NWS; ++e) {
     zf[e] = M::pack(pz + e * M::KPL);
     pf[e] = M::pack(pp + e * M::KPL);
   }
@@ -679,7 +694,7 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_k_kernel(BwdArgs a, int cb,
     const T* aq = sQT + (16 * dt + m) * Lay::LDT;
     const T* ay = sdYT + (16 * dt + m) * Lay::LDT;
 #pragma unroll
-    for (int e = 0; e < 24 / M::KPL; ++e) {
+    for (int e = 0; e < NWS; ++e) {
       ok_ = M::mma(window_frag<T>(aq, Q0, g, e), zf[e], ok_);
       ov = M::mma(window_frag<T>(ay, Q0, g, e), pf[e], ov);
     }
