@@ -222,6 +222,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dstate_kernel(BwdArgs a) {
   __shared__ __align__(16) T sdOT[DV * LDQ];
   __shared__ float sTot[4 * D];
   __shared__ float sBexp[D];
+  // G_{c+1}'s block (rows 0..D, columns j0..j0+DV) and its transpose, staged
+  // so that both leave in whole 16-byte rows
+  constexpr int LDG = DV + PAD, LDT = D + PAD;
+  __shared__ __align__(16) T sG[D * LDG];
+  __shared__ __align__(16) T sGT[DV * LDT];
 
   const int nsplit = D / DV;
   const int x = blockIdx.x, xcd = x & 7, idx = x >> 3;
@@ -306,23 +311,39 @@ __global__ __launch_bounds__(256, 1) void bwd_dstate_kernel(BwdArgs a) {
       if (w == 0) sBexp[i] = exp_2(Bt[dd]);
     }
     stage_T_store<T, DV, 64>(sdOT, LDQ, dyw, 1.0f);
-    // the next chunk's loads fly while this one is stored and multiplied
-    if (c > 0) load(c - 1);
-    // G_{c+1}: rows i, columns j (row-major) and its transpose
-    T* G = Gg + (size_t)c * D * D;
-    T* GT = GTg + (size_t)c * D * D;
+    // G_{c+1} from the accumulators: rows i, columns j (row-major) and its transpose
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         const int i = w * (D / 4) + 16 * rt + 4 * g;
-        const int j = j0 + 16 * ct + m;
+        const int jl = 16 * ct + m;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) G[(size_t)(i + r) * D + j] = from_f32<T>(acc[rt][ct][r]);
+        for (int r = 0; r < 4; ++r) sG[(i + r) * LDG + jl] = from_f32<T>(acc[rt][ct][r]);
         const float v4[4] = {acc[rt][ct][0], acc[rt][ct][1], acc[rt][ct][2], acc[rt][ct][3]};
-        store_pack<T, 4>(GT + (size_t)j * D + i, v4);
+        store_pack<T, 4>(sGT + jl * LDT + i, v4);
       }
+    // the next chunk's loads fly while this one is stored and multiplied
+    if (c > 0) load(c - 1);
     __syncthreads();
+    {
+      typedef uint4 V;
+      constexpr int E = 16 / sizeof(T);            // elements per 16-byte vector
+      constexpr int GR = DV / E, TR = D / E;       // vectors per row of G's block and of G^T's
+      static_assert((D * GR) % 256 == 0 && (DV * TR) % 256 == 0, "whole passes");
+      T* G = Gg + (size_t)c * D * D;
+      T* GT = GTg + (size_t)c * D * D;
+#pragma unroll
+      for (int p = 0; p < D * GR / 256; ++p) {
+        const int u = 256 * p + tid, row = u / GR, col = (u % GR) * E;
+        *reinterpret_cast<V*>(G + (size_t)row * D + j0 + col) = *reinterpret_cast<const V*>(sG + row * LDG + col);
+      }
+#pragma unroll
+      for (int p = 0; p < DV * TR / 256; ++p) {
+        const int u = 256 * p + tid, row = u / TR, col = (u % TR) * E;
+        *reinterpret_cast<V*>(GT + (size_t)(j0 + row) * D + col) = *reinterpret_cast<const V*>(sGT + row * LDT + col);
+      }
+    }
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
       const int ib = w * (D / 4) + 16 * rt;
