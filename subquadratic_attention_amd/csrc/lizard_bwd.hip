@@ -861,8 +861,7 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
   uint4 dyI[QV], vI[QV];
   load_quarter<T, D, RG>(dyI, dyg, t0 + 16 * I + m, L, g);
   load_quarter<T, D, RG>(vI, vg, t0 + 16 * I + m, L, g);
-  const bool has_next = c + 1 < nc;
-  uint4 Sr[QV], Gr[QV], GTr[QV], Sn[QV];
+  uint4 Sr[QV], Gr[QV], GTr[QV];
 
   // prefix: inside the wavefront's rows, then across wavefronts
   float beta[RPW][DPL], off[DPL], Bt[DPL];
@@ -1008,8 +1007,6 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
     load_quarter<T, D, false>(Sr, Sg, ib + m, D, g);      // S_c rows i (k = j)
     load_quarter<T, D, false>(Gr, Gg, ib + m, D, g);      // G_{c+1} rows i (k = j)
     load_quarter<T, D, false>(GTr, GTg, ib + m, D, g);    // G_{c+1}^T rows j (k = i)
-    // S_{c+1} rows i (zero after the last chunk)
-    load_quarter<T, D, false>(Sn, c + 1 < nc ? Sg + (size_t)D * D : Sg, ib + m, D, g);
     // Kp of this lane's key row as fragments: Kh 2^-B, or the stored Kp with the shifted
     // reference (unused on the pairwise path)
     frag kpf[NF];
@@ -1094,21 +1091,32 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
   __syncthreads();
 
   // ---- phase C: dims / value columns [ib, ib + 16) of every token ----
-  // dlog_g of the chunk's last token gets, from all later tokens, the
+  // dlog_g of every token of the chunk gets, from all later tokens, the
   // boundary term x_i = sum_j S_{c+1}[i][j] G_{c+1}[i][j]: the terms of
   // q_u.dq_u - k_u.dk_u over u past the chunk cancel in pairs except those
   // of a query after the boundary and a key before it, which sum to this
-  // product (zero after the last chunk).  xin[r] is x of dim ib + 4g + r.
-  float xin[4];
+  // product (zero after the last chunk, where G_{c+1} = 0).  With
+  // S_{c+1} = diag(2^B) S_c + sum_s Kh_s v_s^T it is
+  //   x_i = 2^{B_i} (S_c G_{c+1}^T)_ii + sum_s k_si (2^{B_i - beta_si} (G_{c+1} v_s)_i),
+  // the second factor of the sum being the inter-chunk part of dk_si: the
+  // first term from the state rows in registers, the second summed over the
+  // tiles below.  xin[r] / xk[r] are the two terms of dim ib + 4g + r (xk
+  // per lane, over its tokens), so the dlog_g values wait for the last tile.
+  float xin[4], xk[4] = {0.f, 0.f, 0.f, 0.f};
   {
     float x = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < D / 4; ++kk) x += elem_of<T>(Sn, kk) * elem_of<T>(Gr, kk);
-    x = has_next ? xgroup_sum(x) : 0.f;
+    for (int kk = 0; kk < D / 4; ++kk) x += elem_of<T>(Sr, kk) * elem_of<T>(Gr, kk);
+    x = xgroup_sum(x);
+    const int i = ib + m;
+    // 2^{B_i}: from the chunk total (pairwise) or from 2^{B-r} and 2^r
+    x *= pairwise ? exp_2(sBx[i]) : sEB[i] * (midref ? sBx[i] : 1.f);
 #pragma unroll
     for (int r = 0; r < 4; ++r) xin[r] = __shfl(x, 4 * g + r, 64);
   }
   float carry[4] = {0.f, 0.f, 0.f, 0.f};   // sums of q.dq - k.dk over the later tiles
+  float dls[4][4];                         // [tile][dim]: dlog_g without the boundary term
+  float sgn[LOGIT ? 4 : 1][4];             // [tile][dim]: sigmoid(-x) of the gate logits
 #pragma unroll
   for (int tt = 3; tt >= 0; --tt) {
     const int cur = tt & 1;
@@ -1184,6 +1192,7 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
       const int i = ib + 4 * g + r;
       const float b = bt[r];
       float qin = qa[r], kin = ka[r];
+      float kint;   // the inter-chunk part of dk
       if (pairwise) {
         // dq_ti += sum_s dA_ts k_si 2^{b_ti - b_si};  dk_ti += sum_u dA_ut q_ui 2^{b_ui - b_ti}
         qin = 0.f;
@@ -1193,13 +1202,16 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
         for (int u = tl; u < 64; ++u)
           kin += to_f32(sDAT[tl * Lay::LDT + u]) * to_f32(sQT[i * Lay::LDT + u]) * exp_2(sBeta[u * Lay::LDB + i] - b);
         qin = exp_2(b) * qi[r] + qin;
-        kin = exp_2(sBx[i] - b) * ki[r] + kin;
+        kint = exp_2(sBx[i] - b) * ki[r];
+        kin = kint + kin;
       } else {
         const float ep = exp_2(b), en = exp_2(-b);
         const float rx = midref ? sBx[i] : 1.f;
         qin = ep * (rx * qi[r] + qin);
-        kin = en * (sEB[i] * ki[r] + kin);
+        kint = en * (sEB[i] * ki[r]);
+        kin = kint + en * kin;
       }
+      xk[r] += live ? k4[r] * kint : 0.f;
       const float dqg = qin;
       const float dkg = kin;
       dbv[r] = live ? q4[r] * dqg - k4[r] * dkg : 0.f;
@@ -1213,8 +1225,7 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
       store_pack<T, 4>(dvo + o4, dvv);
     }
     // dlog_g_t = sum over the tile's tokens u >= t (lanes of this lane
-    // group with m' >= m) + the later tiles + the boundary term
-    float dl[4];
+    // group with m' >= m) + the later tiles (+ the boundary term, below)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float sfx = dbv[r];
@@ -1224,18 +1235,34 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
         sfx += m + o < 16 ? y : 0.f;
       }
       const float tile = __shfl(sfx, l & 48, 64);   // m = 0: the whole tile
-      dl[r] = sfx + carry[r] + xin[r];
+      dls[tt][r] = sfx + carry[r];
       carry[r] += tile;
-    }
-    if constexpr (LOGIT) {
       // gradient w.r.t. the logits: d log sigmoid(x) / dx = sigmoid(-x)
-      const float* x4 = ep[cur][NEP - 1];
-      float dx[4];
+      if constexpr (LOGIT) sgn[tt][r] = sigmoid_neg(ep[cur][NEP - 1][r]);
+    }
+  }
+  // the boundary term: xk summed over the 16 tokens of each tile (lanes m)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dx[r] = dl[r] * sigmoid_neg(x4[r]);
-      if (live) store_pack<T, 4>(dxo + o4, dx);
+  for (int r = 0; r < 4; ++r) {
+    float x = xk[r];
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o, 64);
+    xin[r] += x;
+  }
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    const int trow = t0 + 16 * tt + m;
+    if (RG && trow >= L) continue;
+    const size_t o4 = (size_t)trow * D + ib + 4 * g;
+    float dl[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dl[r] = dls[tt][r] + xin[r];
+    if constexpr (LOGIT) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dl[r] *= sgn[tt][r];
+      store_pack<T, 4>(dxo + o4, dl);
     } else {
-      if (live) *reinterpret_cast<f32x4*>(dbo + o4) = f32x4{dl[0], dl[1], dl[2], dl[3]};
+      *reinterpret_cast<f32x4*>(dbo + o4) = f32x4{dl[0], dl[1], dl[2], dl[3]};
     }
   }
 }
