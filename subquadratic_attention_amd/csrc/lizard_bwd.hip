@@ -80,6 +80,13 @@ __device__ __forceinline__ void load_quarter(uint4* raw, const T* base, int row,
     raw[e] = ok ? r : make_uint4(0, 0, 0, 0);
   }
 }
+// The same quarter of row `row` clamped into [0, L): for rows that the
+// caller masks out after the product (their values never reach a result),
+// without the data selects of the guarded form.
+template <typename T, int D>
+__device__ __forceinline__ void load_quarter_clamped(uint4* raw, const T* base, int row, int L, int g) {
+  load_quarter<T, D, false>(raw, base, min(max(row, 0), L - 1), L, g);
+}
 // element i of a packed 32-bit word of T values
 template <typename T> __device__ __forceinline__ float elem32(uint32_t u, int i) {
   if constexpr (sizeof(T) == 4) return __builtin_bit_cast(float, u);
@@ -426,8 +433,9 @@ struct AqLayout {
   static constexpr int TOTAL = OFF_DZS + a16(64 * 16 * 4);
 };
 
-// The grid covers chunks cb .. cb + ncl - 1; GUARD = false: they are interior
-// (the window keys [t0 - 64, t0 + 64) and the queries lie inside [0, L)).
+// The grid covers chunks cb .. cb + ncl - 1; GUARD = false: they are full
+// (every query inside [0, L)); window keys before position 0 (chunk 0) are
+// read from row 0 and masked out with the rest of the window.
 template <typename T, int D, bool GUARD>
 __global__ __launch_bounds__(256, 3) void bwd_anchor_q_kernel(BwdArgs a, int cb, int ncl) {
   typedef AqLayout<T, D> Lay;
@@ -471,8 +479,13 @@ __global__ __launch_bounds__(256, 3) void bwd_anchor_q_kernel(BwdArgs a, int cb,
 #pragma unroll
     for (int kk = 0; kk < n; ++kk) {
       const int s = t0 - 64 + U0 + 16 * (k0 + kk) + m;   // key row of this lane (MFMA row)
-      load_quarter<T, D, GUARD>(kraw[kk], kg, s, L, g);
-      load_quarter<T, D, GUARD>(vraw[kk], vg, s, L, g);
+      if constexpr (GUARD) {
+        load_quarter<T, D>(kraw[kk], kg, s, L, g);
+        load_quarter<T, D>(vraw[kk], vg, s, L, g);
+      } else {
+        load_quarter_clamped<T, D>(kraw[kk], kg, s, L, g);
+        load_quarter_clamped<T, D>(vraw[kk], vg, s, L, g);
+      }
     }
   };
   load_tiles(0, 3);
@@ -614,8 +627,9 @@ struct AkLayout {
   static constexpr int TOTAL = OFF_RW + a16(2 * 128 * 4);
 };
 
-// The grid covers chunks cb .. cb + ncl - 1; GUARD = false: they are interior
-// (the queries [t0, t0 + 128) lie inside [0, L)).  Two workgroups per CU.
+// The grid covers chunks cb .. cb + ncl - 1; GUARD = false: they are full
+// (every key inside [0, L)); window queries past L (the last full chunk's
+// next chunk) are read from row L - 1 and masked out.  Two workgroups per CU.
 template <typename T, int D, bool GUARD>
 __global__ __launch_bounds__(256, 2) void bwd_anchor_k_kernel(BwdArgs a, int cb, int ncl) {
   typedef AkLayout<T, D> Lay;
@@ -664,15 +678,19 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_k_kernel(BwdArgs a, int cb,
   // query and dY rows are loaded one tile ahead
   f32x4 z[kWinTiles], dp[kWinTiles];
   uint4 qraw[2][QV], dyraw[2][QV];
-  load_quarter<T, D, GUARD>(qraw[0], qg, t0 + Q0 + m, L, g);
-  load_quarter<T, D, GUARD>(dyraw[0], dyg, t0 + Q0 + m, L, g);
+  auto load_query = [&](uint4* qr, uint4* dr, int t) __attribute__((always_inline)) {
+    if constexpr (GUARD) {
+      load_quarter<T, D>(qr, qg, t, L, g);
+      load_quarter<T, D>(dr, dyg, t, L, g);
+    } else {
+      load_quarter_clamped<T, D>(qr, qg, t, L, g);
+      load_quarter_clamped<T, D>(dr, dyg, t, L, g);
+    }
+  };
+  load_query(qraw[0], dyraw[0], t0 + Q0 + m);
 #pragma unroll
   for (int kt = 0; kt < kWinTiles; ++kt) {
-    if (kt + 1 < kWinTiles) {
-      const int tn = t0 + Q0 + 16 * (kt + 1) + m;
-      load_quarter<T, D, GUARD>(qraw[(kt + 1) & 1], qg, tn, L, g);
-      load_quarter<T, D, GUARD>(dyraw[(kt + 1) & 1], dyg, tn, L, g);
-    }
+    if (kt + 1 < kWinTiles) load_query(qraw[(kt + 1) & 1], dyraw[(kt + 1) & 1], t0 + Q0 + 16 * (kt + 1) + m);
     f32x4 zc = zero4(), pc = zero4();
 #pragma unroll
     for (int e = 0; e < NF; ++e) {
@@ -1395,29 +1413,27 @@ hipError_t launch_bwd_t(BwdArgs a, hipStream_t st) {
       hipLaunchKernelGGL((bwd_dstate_kernel<T, D, DV, false>), dim3(8 * groups * (D / DV)), dim3(256), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int nfull = L / C;
-    // 3. anchor, query side: chunk 0 and a ragged last chunk range-checked, the rest not
+    // 3, 4. anchor, query and key side: the full chunks in one launch each,
+    // a ragged last chunk range-checked in its own
     typedef AqLayout<T, D> AQ;
     static_assert(AQ::TOTAL <= 53 * 1024, "LDS: three workgroups per CU");
-    if ((e = set_lds(&bwd_anchor_q_kernel<T, D, true>, AQ::TOTAL)) != hipSuccess) return e;
-    if ((e = set_lds(&bwd_anchor_q_kernel<T, D, false>, AQ::TOTAL)) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_anchor_q_kernel<T, D, true>), dim3(8 * groups), dim3(256), AQ::TOTAL, st, a, 0, 1);
-    if (nfull > 1)
-      hipLaunchKernelGGL((bwd_anchor_q_kernel<T, D, false>), dim3(8 * groups * (nfull - 1)), dim3(256), AQ::TOTAL, st,
-                         a, 1, nfull - 1);
-    if (nfull >= 1 && nfull < nc)
-      hipLaunchKernelGGL((bwd_anchor_q_kernel<T, D, true>), dim3(8 * groups), dim3(256), AQ::TOTAL, st, a, nfull, 1);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    // 4. anchor, key side: chunks whose query range [t0, t0 + 128) ends past L range-checked
     typedef AkLayout<T, D> AK;
     static_assert(AK::TOTAL <= 80 * 1024, "LDS: two workgroups per CU");
+    if ((e = set_lds(&bwd_anchor_q_kernel<T, D, true>, AQ::TOTAL)) != hipSuccess) return e;
+    if ((e = set_lds(&bwd_anchor_q_kernel<T, D, false>, AQ::TOTAL)) != hipSuccess) return e;
     if ((e = set_lds(&bwd_anchor_k_kernel<T, D, true>, AK::TOTAL)) != hipSuccess) return e;
     if ((e = set_lds(&bwd_anchor_k_kernel<T, D, false>, AK::TOTAL)) != hipSuccess) return e;
-    const int nk_in = nfull > 1 ? nfull - 1 : 0;   // chunks c with t0 + 128 <= L
-    if (nk_in > 0)
-      hipLaunchKernelGGL((bwd_anchor_k_kernel<T, D, false>), dim3(8 * groups * nk_in), dim3(256), AK::TOTAL, st, a, 0,
-                         nk_in);
-    hipLaunchKernelGGL((bwd_anchor_k_kernel<T, D, true>), dim3(8 * groups * (nc - nk_in)), dim3(256), AK::TOTAL, st, a,
-                       nk_in, nc - nk_in);
+    if (nfull > 0)
+      hipLaunchKernelGGL((bwd_anchor_q_kernel<T, D, false>), dim3(8 * groups * nfull), dim3(256), AQ::TOTAL, st, a, 0,
+                         nfull);
+    if (nfull < nc)
+      hipLaunchKernelGGL((bwd_anchor_q_kernel<T, D, true>), dim3(8 * groups), dim3(256), AQ::TOTAL, st, a, nfull, 1);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (nfull > 0)
+      hipLaunchKernelGGL((bwd_anchor_k_kernel<T, D, false>), dim3(8 * groups * nfull), dim3(256), AK::TOTAL, st, a, 0,
+                         nfull);
+    if (nfull < nc)
+      hipLaunchKernelGGL((bwd_anchor_k_kernel<T, D, true>), dim3(8 * groups), dim3(256), AK::TOTAL, st, a, nfull, 1);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // 5. gated branch and outputs
     if (a.gate_logit) {
