@@ -15,7 +15,8 @@
 //     dk_s   = 2^{-beta_s} * sum_t dA_ts Qe_t + 2^{B-beta_s} * (G_{c+1} v_s)
 //     dv_s   = sum_t A_ts dO_t + G_{c+1}^T Kh_s
 //     dlog_g_t = sum_{u >= t} (q_u * dq_u - k_u * dk_u)      (natural log)
-//              = sum_{u >= t, u in c} (...) + rowsum(S_{c+1} * G_{c+1})
+//              = sum_{u >= t, u in c} (...) + rowsum(S_{c+1} * G_{c+1}),
+//       the last term formed from S_c and the inter-chunk part of dk
 //   anchor branch (softmax over the window and sinks, P = exp(z - lse)):
 //     dP = alpha dY V^T (window; zero for sinks), D_t = sum P dP,
 //     dZ = P (dP - D_t); dq += scale (dZ K + dZs mu); dk += scale dZ^T Q;
@@ -34,8 +35,11 @@
 //      chunk plus, for everything after it, rowsum(S_{c+1} * G_{c+1});
 //   6. bwd_dmeta_reduce: sums the sink-key partials over batch and chunks in
 //      a fixed order (deterministic, no float atomics).
-// Chunks whose decay span exceeds 2^92 form the gated intra terms pairwise
-// in fp32 (as the forward pass does).
+// Kernels 3-5 run the full chunks in one launch and a ragged last chunk in a
+// range-checked launch of its own.  Chunks whose decay span exceeds 2^184
+// form the gated intra terms pairwise in fp32; spans between 2^92 and 2^184
+// move each dimension's reference point to half its chunk total (as the
+// forward pass does).
 #include <type_traits>
 
 #include "lizard_common.hpp"
