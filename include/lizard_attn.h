@@ -65,14 +65,14 @@ typedef enum {
   LIZARD_E_DTYPE = -3,       /* unknown dtype                                */
   LIZARD_E_ALIGN = -4,       /* a pointer is not 16-byte aligned             */
   LIZARD_E_WORKSPACE = -5,   /* workspace missing or smaller than required  */
-  LIZARD_E_UNSUPPORTED = -6, /* valid sizes this build has no kernel for     */
+  LIZARD_E_UNSUPPORTED = -6, /* valid sizes the library has no kernel for   */
   LIZARD_E_LAUNCH = -7       /* the HIP launch reported an error             */
 } lizard_status_t;
 
 /* Sizes and constants shared by all calls.
  *   B, H      batch and heads (>= 0; a call with B*H == 0 or L == 0 is a no-op)
  *   L         sequence length (>= 0, any value; ignored by decode)
- *   dk, dv    head dims; this build requires dk == dv, and
+ *   dk, dv    head dims; the library requires dk == dv, and
  *             dk in {64, 128} for LIZARD_BF16, dk == 64 for LIZARD_F32
  *   chunk     chunk length of the chunked form; must be 64
  *   window    w, 1 <= w <= 64 (keys [t-w+1, t])

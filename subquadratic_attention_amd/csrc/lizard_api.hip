@@ -378,7 +378,7 @@ LIZARD_API const char* lizard_status_string(lizard_status_t s) {
     case LIZARD_E_DTYPE: return "unknown dtype";
     case LIZARD_E_ALIGN: return "a pointer is not 16-byte aligned";
     case LIZARD_E_WORKSPACE: return "backward workspace too small";
-    case LIZARD_E_UNSUPPORTED: return "no kernel for these sizes in this build";
+    case LIZARD_E_UNSUPPORTED: return "no kernel for these sizes in this library";
     case LIZARD_E_LAUNCH: return "kernel launch failed";
   }
   return "unknown status";
