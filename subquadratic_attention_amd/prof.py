@@ -5,7 +5,9 @@ Reads rocprofv3 CSV output (``--kernel-trace --stats -f csv`` and
 ``--copy-calibration``) and writes:
 
 * ``<kernel>_<workload>.md``: average duration per kernel from the stats,
-  with the command that produced them;
+  with the command that produced them, and the dominant kernel's average
+  over its last ``--steps`` launches (the bench's timed launches follow its
+  warm-up ones, which run while the GPU clock is still rising);
 * ``<kernel>_<workload>_counters.json``: HBM bytes per launch of the
   dominant kernel, each counter scaled by what it reads for the plain
   1 GiB device copy (``__amd_rocclr_copyBuffer``) of the same run, and the
@@ -51,6 +53,21 @@ def pick(values, sub, how="mean"):
     return max(v) if how == "max" else sum(v) / len(v)
 
 
+def timed_average_us(trace_dir: str, sub: str, command: str):
+    """(launches, average in us) of the last --steps launches of the kernel
+    matching sub in the kernel trace, or None without --steps."""
+    words = command.split()
+    if "--steps" not in words:
+        return None
+    k = int(words[words.index("--steps") + 1])
+    rows = [r for r in _rows(trace_dir, "*kernel_trace.csv") if sub in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    last = rows[-k:]
+    if not last:
+        return None
+    return len(last), sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in last) / len(last) / 1e3
+
+
 def source_hash(root: str, rel: str) -> str:
     with open(os.path.join(root, rel), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -66,6 +83,10 @@ def main(argv):
     for r in stats:
         lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+    timed = timed_average_us(trace_dir, ksub, command.split(";")[0])
+    if timed is not None:
+        lines += ["", f"Dominant kernel, its last {timed[0]} launches in this trace (--steps of the traced "
+                  f"command): average {timed[1]:.2f} us."]
     fetch = counter_values(fetch_dir)
     write = counter_values(write_dir)
     # the calibration copy is the largest device copy of the run
