@@ -12,6 +12,17 @@ its MFMA fraction, the float64 CPU oracle timed on a bounded sample of the
 same workload, and secondary objects for the decode step (batch 64, H=32,
 1024 steps after a 2048-token prefill: HBM GB/s) and the backward pass
 (B=8, H=32, L=2048).
+
+Timing of every leg: the leg's inputs are generated on the host first
+(seconds, during which the GPU idles and its clock drops), then the leg's
+own step runs back to back for a fixed --prewarm-ms of wall time (reported
+as "prewarm_ms"; 0 turns it off) so the clock is settled again, then
+exactly --warmup untimed steps, then exactly --steps timed steps between
+HIP events on the launch stream, one event after every step: the mean is
+the total over the steps, the median and minimum are those of the
+per-step intervals.  In a --only run the leg's timed launches are the last
+launches of its kernels in the process (what the profile summaries
+average).
 """
 from __future__ import annotations
 
@@ -33,9 +44,14 @@ KERNEL_SOURCES = ["subquadratic_attention_amd/csrc/lizard_fwd.hip", "subquadrati
                   "subquadratic_attention_amd/csrc/lizard_decode.hip", "subquadratic_attention_amd/csrc/lizard_bwd.hip"]
 
 
-def source_hash(path: str) -> str:
-    with open(os.path.join(ROOT, path), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(paths: str) -> str:
+    """Hash of the kernel sources a counter record was taken on (comma-separated
+    paths, in order; the same hash as the profile summaries record)."""
+    h = hashlib.sha256()
+    for path in paths.split(","):
+        with open(os.path.join(ROOT, path), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 # ---------------------------------------------------------------------------
@@ -87,20 +103,55 @@ def read_traffic(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def time_region(fn, steps: int, warmup: int):
+PREWARM_MS = 300.0
+
+
+def prewarm(fn, ms: float):
+    """Run fn back to back for `ms` milliseconds of wall time (in batches of
+    8 calls, each batch waited for), so the GPU clock has settled before the
+    warm-up and timed steps."""
     import torch
 
+    if ms <= 0:
+        return
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+
+
+def time_steps(fn, steps: int, warmup: int, prewarm_ms: float = None):
+    """Prewarm, `warmup` untimed steps, then `steps` timed steps with an event
+    after each.  Returns {"mean", "median", "min"} in ms per step (the mean
+    over the whole region, the median and minimum over the per-step
+    intervals) and the number of timed steps."""
+    import torch
+
+    prewarm(fn, PREWARM_MS if prewarm_ms is None else prewarm_ms)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
         fn()
-    stop.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    return start.elapsed_time(stop) / steps  # ms
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    mid = steps // 2
+    median = per[mid] if steps % 2 else 0.5 * (per[mid - 1] + per[mid])
+    return {"mean": ev[0].elapsed_time(ev[-1]) / steps, "median": median, "min": per[0], "steps": steps}
+
+
+def time_region(fn, steps: int, warmup: int, prewarm_ms: float = None):
+    """Mean ms per step (see time_steps)."""
+    return time_steps(fn, steps, warmup, prewarm_ms)["mean"]
+
+
+def stats_us(t):
+    return {"mean_us": round(t["mean"] * 1e3, 2), "median_us": round(t["median"] * 1e3, 2),
+            "min_us": round(t["min"] * 1e3, 2), "timed_steps": t["steps"]}
 
 
 def bench_fwd(sqa, si, steps, warmup, logit=False, workload="llama3_8b_prefill_bf16"):
@@ -125,7 +176,7 @@ def bench_fwd(sqa, si, steps, warmup, logit=False, workload="llama3_8b_prefill_b
             sqa.lizard_attn_fwd(x["q"], x["k"], x["v"], x["log_g"], x["meta_k"], window=w.window, alpha=w.alpha,
                                 out=out)
 
-    ms = time_region(step, steps, warmup)
+    t = time_steps(step, steps, warmup)
     head_tokens = w.B * w.H * w.L
     elem = 2 if w.dtype == "bf16" else 4
     alg_bytes = head_tokens * (fwd_logit_bytes_per_head_token(w.d, elem) if logit else
@@ -133,30 +184,78 @@ def bench_fwd(sqa, si, steps, warmup, logit=False, workload="llama3_8b_prefill_b
     alg_flops = head_tokens * fwd_flops_per_head_token(w.d, w.chunk, w.window, w.n_meta)
     del x, out
     torch.cuda.empty_cache()
-    return w, ms, alg_bytes, alg_flops
+    return w, t, alg_bytes, alg_flops
 
 
 def bench_fwd_logit(sqa, si, steps, warmup):
     """The same prefill with the gates fed as bf16 logits (log-sigmoid in the
     kernel's prologue): 1,280 instead of 1,536 algorithmic bytes per head-token."""
-    w, ms, alg_bytes, _ = bench_fwd(sqa, si, steps, warmup, logit=True)
+    w, t, alg_bytes, _ = bench_fwd(sqa, si, steps, warmup, logit=True)
+    ms = t["mean"]
     gbs = alg_bytes / (ms * 1e-3) / 1e9
-    return {"workload": "llama3_8b_prefill_bf16, gate logits in bf16", "ms": round(ms, 5),
+    return {"workload": "llama3_8b_prefill_bf16, gate logits in bf16", "ms": round(ms, 5), **stats_us(t),
             "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1), "alg_bytes": alg_bytes, "gbps": round(gbs, 1),
             "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def bench_train_step(sqa, si, workload, steps, warmup):
+    """One training step of the layer: the training forward (y, lse and the
+    chunk-start states) and the backward reading those states, with a seeded
+    upstream gradient.  Returns (workload, timing)."""
+    import numpy as np
+    import torch
+
+    w = si.WORKLOADS[workload]
+    st = si.storage_inputs(w, with_dy=True)
+    x = {k: (torch.from_numpy(v.view(np.int16)).view(torch.bfloat16) if v.dtype == np.uint16 else
+             torch.from_numpy(v)).cuda() for k, v in st.items()}
+    del st
+    q = x["q"]
+    fout = {"y": torch.empty_like(q), "lse": torch.empty((w.B, w.H, w.L), device="cuda", dtype=torch.float32),
+            "chunk_states": torch.empty((w.B, w.H, (w.L + 63) // 64, w.d, w.d), device="cuda", dtype=q.dtype)}
+    gout = {key: torch.empty_like(x[src]) for key, src in (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dlog_g", "log_g"))}
+    gout["dmeta"] = torch.empty(tuple(x["meta_k"].shape), device="cuda", dtype=torch.float32)
+    ws = torch.empty(max(16, sqa.lizard_attn_bwd_workspace_size(w.B, w.H, w.L, w.d, window=w.window,
+                                                                n_meta=w.n_meta, dtype=sqa._dtype_code(q))),
+                     device="cuda", dtype=torch.uint8)
+
+    def step():
+        sqa.lizard_attn_fwd_train(x["q"], x["k"], x["v"], x["meta_k"], log_g=x["log_g"], window=w.window,
+                                  alpha=w.alpha, out=fout)
+        sqa.lizard_attn_bwd_train(x["q"], x["k"], x["v"], x["meta_k"], fout["lse"], fout["chunk_states"], x["dy"],
+                                  log_g=x["log_g"], window=w.window, alpha=w.alpha, workspace=ws, out=gout)
+
+    step()
+    t = time_steps(step, steps, warmup)
+    del x, fout, gout, ws
+    torch.cuda.empty_cache()
+    return w, t
+
+
 def bench_fp32_ablation(sqa, si, steps, warmup):
-    """The forward with bf16 operands (log-space factors folded into bf16 MFMA
-    operands) against the same kernel with fp32 operands and fp32 MFMA, on the
-    prefill at d=64 (B=4, H=32, L=4096), the largest head dim the fp32 build
-    supports."""
+    """The pages' one speed claim is that the log-space form, whose gate
+    factors fold into bf16 matrix-core operands, raises training throughput
+    over a float32 fallback.  Measured here two ways, each with the same
+    kernels built for bf16 operands (bf16 MFMA, fp32 accumulate) and for
+    fp32 operands (fp32 MFMA), at d=64, the largest head dim the fp32 build
+    has: the inference forward on the prefill shapes (B=4, H=32, L=4096) and
+    the training step (training forward + backward reading its chunk
+    states) on the backward's shapes (B=8, H=32, L=2048)."""
     res = {}
     for name in ("prefill_d64_bf16", "prefill_d64_f32"):
-        w, ms, alg_bytes, _ = bench_fwd(sqa, si, steps, warmup, workload=name)
-        res[name] = {"ms": round(ms, 5), "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1),
+        w, t, alg_bytes, _ = bench_fwd(sqa, si, steps, warmup, workload=name)
+        ms = t["mean"]
+        res[name] = {"ms": round(ms, 5), **stats_us(t), "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1),
                      "gbps": round(alg_bytes / (ms * 1e-3) / 1e9, 1)}
     res["bf16_over_fp32"] = round(res["prefill_d64_bf16"]["tokens_per_s"] / res["prefill_d64_f32"]["tokens_per_s"], 3)
+    train = {}
+    for name in ("train_d64_bf16", "train_d64_f32"):
+        w, t = bench_train_step(sqa, si, name, steps, warmup)
+        train[name] = {"ms": round(t["mean"], 5), **stats_us(t),
+                       "tokens_per_s": round(w.B * w.L / (t["mean"] * 1e-3), 1)}
+    train["bf16_over_fp32"] = round(train["train_d64_bf16"]["tokens_per_s"] / train["train_d64_f32"]["tokens_per_s"], 3)
+    train["pages_claim"] = "training throughput up to +32 % (de page) / +32-36 % (it page) for bf16 over fp32"
+    res["train_step"] = train
     return res
 
 
@@ -184,20 +283,20 @@ def bench_long_ctx(sqa, si, steps, warmup):
     def one_pass():
         sqa.lizard_attn_fwd(x["q"], x["k"], x["v"], x["log_g"], x["meta_k"], window=w.window, alpha=w.alpha, out=out)
 
-    # each call is 0.6-2 ms: fewer steps than the 4K legs, and warm-up enough
-    # for the clocks to settle (tens of milliseconds of work)
-    n = max(10, steps // 5)
-    ms_split = time_region(split, n, max(40, warmup // 2))
-    ms_one = time_region(one_pass, n, max(20, warmup // 5))
+    # the one-pass call first, the split call last (its launches are then the
+    # last ones of the process, which the profile summary averages)
+    t_one = time_steps(one_pass, steps, warmup)
+    t_split = time_steps(split, steps, warmup)
     alg_bytes = w.B * w.H * w.L * fwd_bytes_per_head_token(w.d)
     del x, out, ws
     torch.cuda.empty_cache()
-    res = {"workload": "long_ctx_32k_bf16 (B=1, H=32, L=32768, d=128, gates N(2,2))", "steps": n}
-    for name, ms in (("split", ms_split), ("one_pass", ms_one)):
+    res = {"workload": "long_ctx_32k_bf16 (B=1, H=32, L=32768, d=128, gates N(2,2))", "steps": steps}
+    for name, call, t in (("split", "lizard_attn_fwd_split", t_split), ("one_pass", "lizard_attn_fwd", t_one)):
+        ms = t["mean"]
         gbs = alg_bytes / (ms * 1e-3) / 1e9
-        res[name] = {"ms": round(ms, 5), "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1), "gbps": round(gbs, 1),
-                     "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
-    res["split_over_one_pass"] = round(ms_one / ms_split, 3)
+        res[name] = {"call": call, "ms": round(ms, 5), **stats_us(t), "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1),
+                     "gbps": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    res["split_over_one_pass"] = round(t_one["mean"] / t_split["mean"], 3)
     return res
 
 
@@ -251,8 +350,8 @@ def bench_decode(sqa, si, reps=3):
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / steps
 
+    prewarm(run_all, PREWARM_MS)
     run_all()  # warm-up
-    ms_b2b = min(run_all() for _ in range(reps))
     # cache-flushed: 512 MiB read between steps evicts the 256 MB last-level cache
     # (a read, so that no dirty lines of the flush are written back while the
     # decode kernel runs); only the decode kernel is timed (per-step events)
@@ -266,13 +365,10 @@ def bench_decode(sqa, si, reps=3):
     out = {
         "workload": "decode_b64_bf16", "B": w.B, "H": w.H, "d": w.d, "window": w.window, "n_meta": w.n_meta,
         "prefill": L0, "steps": steps,
-        "us_per_step": round(ms_b2b * 1e3, 2),
-        "tokens_per_s": round(w.B / (ms_b2b * 1e-3), 1),
         "alg_bytes_per_step": bytes_step,
-        "gbps": round(bytes_step / (ms_b2b * 1e-3) / 1e9, 1),
-        "frac_hbm_peak": round(bytes_step / (ms_b2b * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "flushed_us_per_step": round(ms_flushed * 1e3, 2),
         "flushed_p50_us": round(per[steps // 2] * 1e3, 2),
+        "flushed_min_us": round(per[0] * 1e3, 2),
         "flushed_gbps": round(bytes_step / (ms_flushed * 1e-3) / 1e9, 1),
         "flushed_frac_hbm_peak": round(bytes_step / (ms_flushed * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "traffic": read_traffic("lizard_decode", "decode_b64_bf16"),
@@ -301,19 +397,28 @@ def bench_decode(sqa, si, reps=3):
         return t0.elapsed_time(t1) / steps
 
     run_tokens()
-    ms_tok = min(run_tokens() for _ in range(reps))
+    ms_tok = sum(run_tokens() for _ in range(reps)) / reps
     # per call: the state once, then per token the window, inputs and output
     bytes_call = w.B * w.H * (decode_bytes_per_bh(w.d, w.window) + (T - 1) * (decode_bytes_per_bh(w.d, w.window)
                                                                                - 2 * 4 * w.d * w.d))
     out["tokens4"] = {"T": T, "us_per_token": round(ms_tok * 1e3, 2), "tokens_per_s": round(w.B / (ms_tok * 1e-3), 1),
                       "alg_bytes_per_call": bytes_call,
                       "gbps": round(bytes_call / (T * ms_tok * 1e-3) / 1e9, 1)}
+    # back to back last: `reps` runs of the 1024 steps, the mean over all of
+    # them (these are the last launches of the one-token kernel)
+    prewarm(run_all, PREWARM_MS)
+    runs = [run_all() for _ in range(reps)]
+    ms_b2b = sum(runs) / reps
+    out.update({"us_per_step": round(ms_b2b * 1e3, 2), "best_run_us_per_step": round(min(runs) * 1e3, 2),
+                "timed_steps": reps * steps, "tokens_per_s": round(w.B / (ms_b2b * 1e-3), 1),
+                "gbps": round(bytes_step / (ms_b2b * 1e-3) / 1e9, 1),
+                "frac_hbm_peak": round(bytes_step / (ms_b2b * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
     del dec, dec4, y4, pos_all, ring0, y, state, state0, kr, vr, scratch, sink
     torch.cuda.empty_cache()
     return out
 
 
-def bench_bwd(sqa, si, steps=10, warmup=3, logit=False):
+def bench_bwd(sqa, si, steps, warmup, logit=False):
     import numpy as np
     import torch
 
@@ -331,7 +436,10 @@ def bench_bwd(sqa, si, steps=10, warmup=3, logit=False):
     ws = torch.empty(max(16, sqa.lizard_attn_bwd_workspace_size(w.B, w.H, w.L, w.d, window=w.window,
                                                                  n_meta=w.n_meta, dtype=sqa.LIZARD_BF16)),
                      device="cuda", dtype=torch.uint8)
-    out = {}
+    gname = "gate_logit" if logit else "log_g"
+    out = {key: torch.empty_like(x[src]) for key, src in (("dq", "q"), ("dk", "k"), ("dv", "v"),
+                                                          ("dgate_logit" if logit else "dlog_g", gname))}
+    out["dmeta"] = torch.empty(tuple(x["meta_k"].shape), device="cuda", dtype=torch.float32)
 
     def step():
         if logit:
@@ -342,10 +450,11 @@ def bench_bwd(sqa, si, steps=10, warmup=3, logit=False):
                                 window=w.window, alpha=w.alpha, workspace=ws, out=out)
 
     step()
-    ms = time_region(step, steps, warmup)
-    ms_saved = None
+    t_saved = None
     if not logit:
-        # the same backward reading the chunk-start states a training forward kept
+        # the same backward reading the chunk-start states a training forward
+        # kept (timed first: the plain backward's launches are then the last
+        # ones of the process)
         tr = sqa.lizard_attn_fwd_train(x["q"], x["k"], x["v"], x["meta_k"], log_g=x["log_g"], window=w.window,
                                        alpha=w.alpha)
 
@@ -353,29 +462,33 @@ def bench_bwd(sqa, si, steps=10, warmup=3, logit=False):
             sqa.lizard_attn_bwd_train(x["q"], x["k"], x["v"], x["meta_k"], tr["lse"], tr["chunk_states"], x["dy"],
                                       log_g=x["log_g"], window=w.window, alpha=w.alpha, workspace=ws, out=out)
 
-        ms_saved = time_region(step_saved, steps, warmup)
+        t_saved = time_steps(step_saved, steps, warmup)
         del tr
+    t = time_steps(step, steps, warmup)
+    ms = t["mean"]
     head_tokens = w.B * w.H * w.L
     # with logits: the gate in and its gradient out in bf16 instead of float32
     alg_bytes = head_tokens * (bwd_bytes_per_head_token(w.d) - (4 * w.d if logit else 0))
     alg_flops = head_tokens * bwd_flops_per_head_token(w.d, w.chunk, w.window, w.n_meta)
     res = {
         "workload": "train_bwd_bf16" + (", gate logits in bf16" if logit else ""), "B": w.B, "H": w.H, "L": w.L, "d": w.d,
-        "ms": round(ms, 4), "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1),
+        "ms": round(ms, 4), **stats_us(t), "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1),
         "alg_bytes": alg_bytes, "gbps": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
         "frac_hbm_peak": round(alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "tflops": round(alg_flops / (ms * 1e-3) / 1e12, 2),
         "frac_mfma_peak": round(alg_flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
         "workspace_bytes": int(ws.numel()),
+        "traffic": None if logit else read_traffic("lizard_bwd", "train_bwd_bf16"),
     }
-    if ms_saved is not None:
-        res["ms_with_saved_states"] = round(ms_saved, 4)
+    if t_saved is not None:
+        res["ms_with_saved_states"] = round(t_saved["mean"], 4)
+        res["with_saved_states"] = stats_us(t_saved)
     del x, fw, ws, out
     torch.cuda.empty_cache()
     return res
 
 
-def bench_stage1(sqa, si, steps=10, warmup=3):
+def bench_stage1(sqa, si, steps, warmup):
     """One synthetic stage-1 attention-transfer step on the backward workload's
     shapes (B=8, H=32, L=2048, d=128, bf16): the causal softmax teacher, the
     layer's training forward (lse and chunk-start states kept), the
@@ -400,7 +513,8 @@ def bench_stage1(sqa, si, steps=10, warmup=3):
                                         dtype=torch.bfloat16)}
     dy = torch.empty_like(x["q"])
     loss_bh = torch.empty((w.B, w.H), device="cuda", dtype=torch.float32)
-    gout = {}
+    gout = {key: torch.empty_like(x[src]) for key, src in (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dlog_g", "log_g"))}
+    gout["dmeta"] = torch.empty(tuple(x["meta_k"].shape), device="cuda", dtype=torch.float32)
 
     def teacher():
         sqa.lizard_softmax_attn_fwd(x["q"], x["k"], x["v"], out=tout)
@@ -421,9 +535,9 @@ def bench_stage1(sqa, si, steps=10, warmup=3):
         sqa.lizard_attn_bwd(x["q"], x["k"], x["v"], x["log_g"], x["meta_k"], fout["lse"], dy, window=w.window,
                             alpha=w.alpha, workspace=ws, out=gout)
 
+    ms_t = time_region(teacher, 3 * steps, warmup)
     ms_r = time_region(step_recompute, steps, warmup)
     ms = time_region(step, steps, warmup)
-    ms_t = time_region(teacher, 3 * steps, warmup)
     t_flops = w.B * w.H * 2 * w.L * (w.L + 1) * w.d    # causal pairs x (QK^T + PV) x 2 flops
     res = {"workload": "train_bwd_bf16 shapes, teacher = causal softmax attention", "ms": round(ms, 4),
            "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1), "loss": round(float(loss_bh.sum()), 6),
@@ -466,10 +580,13 @@ def cpu_baseline(si, target_s: float = 15.0):
 
 
 def main():
+    global PREWARM_MS
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--prewarm-ms", type=float, default=PREWARM_MS,
+                    help="wall time each leg's step runs back to back before its warm-up (0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
@@ -497,6 +614,7 @@ def main():
 
     sqa.load_library()
     torch.cuda.init()
+    PREWARM_MS = max(0.0, args.prewarm_ms)
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, device="cuda", dtype=torch.uint8).fill_(3)
@@ -509,7 +627,7 @@ def main():
         del src, dst
 
     if args.only == "decode":
-        print(json.dumps(bench_decode(sqa, si)), flush=True)
+        print(json.dumps({"prewarm_ms": PREWARM_MS, **bench_decode(sqa, si)}), flush=True)
         return
     if args.only == "bwd":
         print(json.dumps(bench_bwd(sqa, si, args.steps, args.warmup)), flush=True)
@@ -521,7 +639,7 @@ def main():
         print(json.dumps(bench_bwd(sqa, si, args.steps, args.warmup, logit=True)), flush=True)
         return
     if args.only == "stage1":
-        print(json.dumps(bench_stage1(sqa, si)), flush=True)
+        print(json.dumps(bench_stage1(sqa, si, args.steps, args.warmup)), flush=True)
         return
     if args.only == "long_ctx":
         print(json.dumps(bench_long_ctx(sqa, si, args.steps, args.warmup)), flush=True)
@@ -530,7 +648,8 @@ def main():
         print(json.dumps(bench_fp32_ablation(sqa, si, args.steps, args.warmup)), flush=True)
         return
 
-    w, ms, alg_bytes, alg_flops = bench_fwd(sqa, si, args.steps, args.warmup)
+    w, t, alg_bytes, alg_flops = bench_fwd(sqa, si, args.steps, args.warmup)
+    ms = t["mean"]
     print(f"# fwd done: {ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
     tokens = w.B * w.L
     gbs = alg_bytes / (ms * 1e-3) / 1e9
@@ -542,7 +661,9 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "prewarm_ms": PREWARM_MS,
         "ms_per_step": round(ms, 5),
+        "step_stats": stats_us(t),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -576,14 +697,14 @@ def main():
         print("# decode done", file=sys.stderr, flush=True)
     if not args.no_bwd:
         try:
-            rec["bwd"] = bench_bwd(sqa, si)
+            rec["bwd"] = bench_bwd(sqa, si, args.steps, args.warmup)
             if not args.no_logit:
-                rec["bwd_logit"] = bench_bwd(sqa, si, logit=True)
+                rec["bwd_logit"] = bench_bwd(sqa, si, args.steps, args.warmup, logit=True)
         except sqa.LizardError as e:
             rec["bwd"] = {"error": str(e)}
         print("# bwd done", file=sys.stderr, flush=True)
     if not args.no_stage1:
-        rec["stage1"] = bench_stage1(sqa, si)
+        rec["stage1"] = bench_stage1(sqa, si, args.steps, args.warmup)
         print("# stage1 done", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(si)

@@ -75,6 +75,11 @@ WORKLOADS: Dict[str, Workload] = {
     # kernel exists at d=64 only): the bf16-vs-fp32 ablation
     "prefill_d64_bf16": Workload("prefill_d64_bf16", 5, "bf16", B=4, H=32, L=4096, d=64),
     "prefill_d64_f32": Workload("prefill_d64_f32", 6, "f32", B=4, H=32, L=4096, d=64),
+    # the training step (forward keeping lse and the chunk states, then the
+    # backward) on the backward's shapes at d=64 in both operand types: the
+    # ablation of the pages' training-throughput claim
+    "train_d64_bf16": Workload("train_d64_bf16", 7, "bf16", B=8, H=32, L=2048, d=64),
+    "train_d64_f32": Workload("train_d64_f32", 8, "f32", B=8, H=32, L=2048, d=64),
 }
 
 

@@ -131,6 +131,64 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+def _expect(name: str, t, shape, dtype, device) -> None:
+    """Shape, dtype and device of one tensor argument, checked before any
+    pointer reaches the library (a wrong size or dtype would make a kernel
+    read or write past the allocation).  None passes (optional arguments)."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(int(x) for x in shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+
+
+def _expect_seq_inputs(q, k, v, meta_k, log_g=None, gate_logit=None):
+    """q, k, v [B, H, L, d] in one dtype; log_g float32 and gate_logit q's
+    dtype, both [B, H, L, d]; meta_k [H, m, d] in q's dtype."""
+    torch = _torch()
+    _dtype_code(q)
+    if q.dim() != 4:
+        raise ValueError(f"q: expected [B, H, L, d], got shape {tuple(q.shape)}")
+    B, H, L, d = q.shape
+    for name, t in (("k", k), ("v", v)):
+        if t is None:
+            raise ValueError(f"{name} is required")
+        _expect(name, t, q.shape, q.dtype, q.device)
+    _expect("log_g", log_g, q.shape, torch.float32, q.device)
+    _expect("gate_logit", gate_logit, q.shape, q.dtype, q.device)
+    if meta_k is not None:
+        if meta_k.dim() != 3:
+            raise ValueError(f"meta_k: expected [H, m, d], got shape {tuple(meta_k.shape)}")
+        _expect("meta_k", meta_k, (H, meta_k.shape[1], d), q.dtype, q.device)
+
+
+def _expect_fwd_out(o, q):
+    torch = _torch()
+    B, H, L, d = q.shape
+    _expect("y", o.get("y"), q.shape, q.dtype, q.device)
+    _expect("lse", o.get("lse"), (B, H, L), torch.float32, q.device)
+    _expect("y_anchor", o.get("y_anchor"), q.shape, q.dtype, q.device)
+    _expect("state", o.get("state"), (B, H, d, d), torch.float32, q.device)
+
+
+def _expect_bwd(q, meta_k, lse, dy, o, gkey, gate, workspace, ws_bytes):
+    torch = _torch()
+    B, H, L, d = q.shape
+    _expect("lse", lse, (B, H, L), torch.float32, q.device)
+    _expect("dy", dy, q.shape, q.dtype, q.device)
+    for key in ("dq", "dk", "dv"):
+        _expect(key, o.get(key), q.shape, q.dtype, q.device)
+    _expect(gkey, o.get(gkey), q.shape, gate.dtype, q.device)
+    if meta_k is not None:
+        _expect("dmeta", o.get("dmeta"), meta_k.shape, torch.float32, q.device)
+    if workspace is not None:
+        if workspace.dtype != torch.uint8 or workspace.device != q.device or workspace.numel() < ws_bytes:
+            raise ValueError(f"workspace: a uint8 tensor of at least {ws_bytes} bytes on {q.device} is required")
+
+
 def _stream(device) -> int:
     return _torch().cuda.current_stream(device).cuda_stream
 
@@ -162,6 +220,10 @@ def lizard_attn_fwd_logit(q, k, v, gate_logit, meta_k, *, window: int, alpha: fl
 def _fwd(fn, q, k, v, gate, meta_k, window, alpha, softmax_scale, chunk, need_lse, need_y_anchor, need_state, out):
     torch = _torch()
     lib = load_library()
+    logit = fn.endswith("_logit")
+    _expect_seq_inputs(q, k, v, meta_k, log_g=None if logit else gate, gate_logit=gate if logit else None)
+    if gate is None:
+        raise ValueError("the gates are required")
     B, H, L, d = q.shape
     m = meta_k.shape[1] if meta_k is not None else 0
     dt = _dtype_code(q)
@@ -176,6 +238,7 @@ def _fwd(fn, q, k, v, gate, meta_k, window, alpha, softmax_scale, chunk, need_ls
         o["y_anchor"] = torch.empty_like(q)
     if need_state and "state" not in o:
         o["state"] = torch.empty((B, H, d, d), device=q.device, dtype=torch.float32)
+    _expect_fwd_out(o, q)
     st = getattr(lib, fn)(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(meta_k),
                           _ptr(o["y"]), _ptr(o.get("lse")), _ptr(o.get("y_anchor")), _ptr(o.get("state")),
                           _stream(q.device))
@@ -208,6 +271,10 @@ def lizard_attn_bwd_logit(q, k, v, gate_logit, meta_k, lse, dy, *, window: int, 
 def _bwd(fn, gkey, q, k, v, gate, meta_k, lse, dy, window, alpha, softmax_scale, chunk, workspace, out):
     torch = _torch()
     lib = load_library()
+    logit = gkey == "dgate_logit"
+    _expect_seq_inputs(q, k, v, meta_k, log_g=None if logit else gate, gate_logit=gate if logit else None)
+    if gate is None or lse is None or dy is None:
+        raise ValueError("the gates, lse and dy are required")
     B, H, L, d = q.shape
     m = meta_k.shape[1] if meta_k is not None else 0
     dt = _dtype_code(q)
@@ -224,6 +291,7 @@ def _bwd(fn, gkey, q, k, v, gate, meta_k, lse, dy, window, alpha, softmax_scale,
         o[gkey] = torch.empty_like(gate)
     if "dmeta" not in o:
         o["dmeta"] = torch.empty((H, m, d), device=q.device, dtype=torch.float32) if m > 0 else None
+    _expect_bwd(q, meta_k, lse, dy, o, gkey, gate, workspace, ws_bytes)
     st = getattr(lib, fn)(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(meta_k), _ptr(lse),
                           _ptr(dy), _ptr(o["dq"]), _ptr(o["dk"]), _ptr(o["dv"]), _ptr(o[gkey]),
                           _ptr(o["dmeta"]), _ptr(workspace), workspace.numel(), _stream(q.device))
@@ -240,6 +308,9 @@ def lizard_attn_fwd_train(q, k, v, meta_k, *, log_g=None, gate_logit=None, windo
     ceil(L/64), d, d] in q's dtype, and optionally "y_anchor", "state"}."""
     torch = _torch()
     lib = load_library()
+    if (log_g is None) == (gate_logit is None):
+        raise ValueError("exactly one of log_g and gate_logit is required")
+    _expect_seq_inputs(q, k, v, meta_k, log_g=log_g, gate_logit=gate_logit)
     B, H, L, d = q.shape
     m = meta_k.shape[1] if meta_k is not None else 0
     p = make_params(B, H, L, d, window=window, n_meta=m, alpha=alpha, dtype=_dtype_code(q), chunk=chunk,
@@ -255,6 +326,8 @@ def lizard_attn_fwd_train(q, k, v, meta_k, *, log_g=None, gate_logit=None, windo
         o["y_anchor"] = torch.empty_like(q)
     if need_state and "state" not in o:
         o["state"] = torch.empty((B, H, d, d), device=q.device, dtype=torch.float32)
+    _expect_fwd_out(o, q)
+    _expect("chunk_states", o["chunk_states"], (B, H, (L + 63) // 64, d, d), q.dtype, q.device)
     st = lib.lizard_attn_fwd_train(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(gate_logit),
                                    _ptr(meta_k), _ptr(o["y"]), _ptr(o["lse"]), _ptr(o.get("y_anchor")),
                                    _ptr(o.get("state")), _ptr(o["chunk_states"]), _stream(q.device))
@@ -270,7 +343,13 @@ def lizard_attn_bwd_train(q, k, v, meta_k, lse, chunk_states, dy, *, log_g=None,
     "dv", "dlog_g" or "dgate_logit", "dmeta"}."""
     torch = _torch()
     lib = load_library()
+    if (log_g is None) == (gate_logit is None):
+        raise ValueError("exactly one of log_g and gate_logit is required")
+    _expect_seq_inputs(q, k, v, meta_k, log_g=log_g, gate_logit=gate_logit)
+    if lse is None or dy is None or chunk_states is None:
+        raise ValueError("lse, chunk_states and dy are required")
     B, H, L, d = q.shape
+    _expect("chunk_states", chunk_states, (B, H, (L + 63) // 64, d, d), q.dtype, q.device)
     m = meta_k.shape[1] if meta_k is not None else 0
     p = make_params(B, H, L, d, window=window, n_meta=m, alpha=alpha, dtype=_dtype_code(q), chunk=chunk,
                     softmax_scale=softmax_scale)
@@ -287,6 +366,7 @@ def lizard_attn_bwd_train(q, k, v, meta_k, lse, chunk_states, dy, *, log_g=None,
         o[gkey] = torch.empty_like(gate)
     if "dmeta" not in o:
         o["dmeta"] = torch.empty((H, m, d), device=q.device, dtype=torch.float32) if m > 0 else None
+    _expect_bwd(q, meta_k, lse, dy, o, gkey, gate, workspace, ws_bytes)
     st = lib.lizard_attn_bwd_train(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(gate_logit),
                                    _ptr(meta_k), _ptr(lse), _ptr(chunk_states), _ptr(dy), _ptr(o["dq"]),
                                    _ptr(o["dk"]), _ptr(o["dv"]), _ptr(o[gkey]), _ptr(o["dmeta"]), _ptr(workspace),
@@ -315,7 +395,11 @@ def lizard_decode_step_logit(pos: int, q_t, k_t, v_t, gate_logit_t, meta_k, stat
 def _decode(fn, pos, q_t, k_t, v_t, gate, meta_k, state, k_ring, v_ring, alpha, softmax_scale, y_t):
     torch = _torch()
     lib = load_library()
+    _dtype_code(q_t)
+    if q_t.dim() != 3:
+        raise ValueError(f"q_t: expected [B, H, d], got shape {tuple(q_t.shape)}")
     B, H, d = q_t.shape
+    _expect_decode(fn, q_t, k_t, v_t, gate, meta_k, state, k_ring, v_ring, y_t)
     w = k_ring.shape[2]
     m = meta_k.shape[1] if meta_k is not None else 0
     p = make_params(B, H, 0, d, window=w, n_meta=m, alpha=alpha, dtype=_dtype_code(q_t),
@@ -327,6 +411,30 @@ def _decode(fn, pos, q_t, k_t, v_t, gate, meta_k, state, k_ring, v_ring, alpha, 
                           _stream(q_t.device))
     _check(fn, st)
     return y_t
+
+
+def _expect_decode(fn, q, k, v, gate, meta_k, state, k_ring, v_ring, y):
+    """Decode arguments: k, v, y like q ([B, H, d] or [B, H, T, d]); the
+    gates float32 (log-gates) or q's dtype (logits) in q's shape; state
+    float32 [B, H, d, d]; rings [B, H, w, d] in q's dtype; meta_k [H, m, d]."""
+    torch = _torch()
+    B, H, d = q.shape[0], q.shape[1], q.shape[-1]
+    for name, t in (("k", k), ("v", v), ("gates", gate), ("state", state), ("k_ring", k_ring), ("v_ring", v_ring)):
+        if t is None:
+            raise ValueError(f"{name} is required")
+    _expect("k", k, q.shape, q.dtype, q.device)
+    _expect("v", v, q.shape, q.dtype, q.device)
+    _expect("gates", gate, q.shape, q.dtype if fn.endswith("_logit") else torch.float32, q.device)
+    _expect("state", state, (B, H, d, d), torch.float32, q.device)
+    if k_ring.dim() != 4:
+        raise ValueError(f"k_ring: expected [B, H, w, d], got shape {tuple(k_ring.shape)}")
+    _expect("k_ring", k_ring, (B, H, k_ring.shape[2], d), q.dtype, q.device)
+    _expect("v_ring", v_ring, k_ring.shape, q.dtype, q.device)
+    _expect("y", y, q.shape, q.dtype, q.device)
+    if meta_k is not None:
+        if meta_k.dim() != 3:
+            raise ValueError(f"meta_k: expected [H, m, d], got shape {tuple(meta_k.shape)}")
+        _expect("meta_k", meta_k, (H, meta_k.shape[1], d), q.dtype, q.device)
 
 
 def default_scale(d: int) -> float:
@@ -353,11 +461,15 @@ def lizard_decode_tokens_logit(pos, q, k, v, gate_logit, meta_k, state, k_ring, 
 def _decode_tokens(fn, pos, q, k, v, gate, meta_k, state, k_ring, v_ring, alpha, softmax_scale, y):
     torch = _torch()
     lib = load_library()
+    _dtype_code(q)
+    if q.dim() != 4:
+        raise ValueError(f"q: expected [B, H, T, d], got shape {tuple(q.shape)}")
     B, H, T, d = q.shape
+    _expect_decode(fn, q, k, v, gate, meta_k, state, k_ring, v_ring, y)
     w = k_ring.shape[2]
     m = meta_k.shape[1] if meta_k is not None else 0
-    if pos.dtype != torch.int64 or pos.shape != (B,):
-        raise ValueError("pos must be an int64 tensor of shape [B]")
+    if pos.dtype != torch.int64 or tuple(pos.shape) != (B,) or pos.device != q.device:
+        raise ValueError(f"pos must be an int64 tensor of shape [B] on {q.device}")
     p = make_params(B, H, 0, d, window=w, n_meta=m, alpha=alpha, dtype=_dtype_code(q), softmax_scale=softmax_scale)
     if y is None:
         y = torch.empty_like(q)
@@ -365,6 +477,24 @@ def _decode_tokens(fn, pos, q, k, v, gate, meta_k, state, k_ring, v_ring, alpha,
                           _ptr(state), _ptr(k_ring), _ptr(v_ring), _ptr(y), _stream(q.device))
     _check(fn, st)
     return y
+
+
+def _expect_continue(q, k, v, meta_k, log_g, gate_logit, state_in, k_halo, v_halo):
+    """A continued segment: one of log_g / gate_logit, state_in float32
+    [B, H, d, d], k_halo and v_halo [B, H, h, d] in q's dtype (both or none)."""
+    torch = _torch()
+    if (log_g is None) == (gate_logit is None):
+        raise ValueError("exactly one of log_g and gate_logit is required")
+    _expect_seq_inputs(q, k, v, meta_k, log_g=log_g, gate_logit=gate_logit)
+    B, H, L, d = q.shape
+    _expect("state_in", state_in, (B, H, d, d), torch.float32, q.device)
+    if (k_halo is None) != (v_halo is None):
+        raise ValueError("k_halo and v_halo go together")
+    if k_halo is not None:
+        if k_halo.dim() != 4:
+            raise ValueError(f"k_halo: expected [B, H, h, d], got shape {tuple(k_halo.shape)}")
+        _expect("k_halo", k_halo, (B, H, k_halo.shape[2], d), q.dtype, q.device)
+        _expect("v_halo", v_halo, k_halo.shape, q.dtype, q.device)
 
 
 def lizard_attn_fwd_continue(q, k, v, meta_k, *, log_g=None, gate_logit=None, state_in=None, k_halo=None,
@@ -376,6 +506,7 @@ def lizard_attn_fwd_continue(q, k, v, meta_k, *, log_g=None, gate_logit=None, st
     previous h <= window - 1 tokens).  Gates as log_g (float32) or gate_logit."""
     torch = _torch()
     lib = load_library()
+    _expect_continue(q, k, v, meta_k, log_g, gate_logit, state_in, k_halo, v_halo)
     B, H, L, d = q.shape
     m = meta_k.shape[1] if meta_k is not None else 0
     hl = 0 if k_halo is None else int(k_halo.shape[2])
@@ -390,6 +521,7 @@ def lizard_attn_fwd_continue(q, k, v, meta_k, *, log_g=None, gate_logit=None, st
         o["y_anchor"] = torch.empty_like(q)
     if need_state and "state" not in o:
         o["state"] = torch.empty((B, H, d, d), device=q.device, dtype=torch.float32)
+    _expect_fwd_out(o, q)
     st = lib.lizard_attn_fwd_continue(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(gate_logit),
                                       _ptr(meta_k), _ptr(state_in), _ptr(k_halo), _ptr(v_halo), hl, _ptr(o["y"]),
                                       _ptr(o.get("lse")), _ptr(o.get("y_anchor")), _ptr(o.get("state")),
@@ -407,6 +539,7 @@ def lizard_attn_fwd_split(q, k, v, meta_k, *, log_g=None, gate_logit=None, state
     least lizard_attn_fwd_split_workspace_size bytes (allocated when None)."""
     torch = _torch()
     lib = load_library()
+    _expect_continue(q, k, v, meta_k, log_g, gate_logit, state_in, k_halo, v_halo)
     B, H, L, d = q.shape
     m = meta_k.shape[1] if meta_k is not None else 0
     hl = 0 if k_halo is None else int(k_halo.shape[2])
@@ -425,6 +558,9 @@ def lizard_attn_fwd_split(q, k, v, meta_k, *, log_g=None, gate_logit=None, state
         o["y_anchor"] = torch.empty_like(q)
     if need_state and "state" not in o:
         o["state"] = torch.empty((B, H, d, d), device=q.device, dtype=torch.float32)
+    _expect_fwd_out(o, q)
+    if workspace is not None and (workspace.dtype != torch.uint8 or workspace.device != q.device):
+        raise ValueError(f"workspace: a uint8 tensor on {q.device} is required")
     st = lib.lizard_attn_fwd_split(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(gate_logit),
                                    _ptr(meta_k), _ptr(state_in), _ptr(k_halo), _ptr(v_halo), hl, _ptr(o["y"]),
                                    _ptr(o.get("lse")), _ptr(o.get("y_anchor")), _ptr(o.get("state")), _ptr(workspace),
@@ -447,6 +583,7 @@ def lizard_softmax_attn_fwd(q, k, v, *, softmax_scale: float = 0.0, need_lse: bo
     Returns {"y", and optionally "lse"}."""
     torch = _torch()
     lib = load_library()
+    _expect_seq_inputs(q, k, v, None)
     B, H, L, d = q.shape
     p = make_params(B, H, L, d, window=1, n_meta=0, alpha=0.0, dtype=_dtype_code(q), softmax_scale=softmax_scale)
     o = dict(out) if out is not None else {}
@@ -454,6 +591,7 @@ def lizard_softmax_attn_fwd(q, k, v, *, softmax_scale: float = 0.0, need_lse: bo
         o["y"] = torch.empty_like(q)
     if need_lse and "lse" not in o:
         o["lse"] = torch.empty((B, H, L), device=q.device, dtype=torch.float32)
+    _expect_fwd_out(o, q)
     st = lib.lizard_softmax_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o["y"]), _ptr(o.get("lse")),
                                      _stream(q.device))
     _check("lizard_softmax_attn_fwd", st)
@@ -465,7 +603,13 @@ def lizard_transfer_loss(y, y_teacher, *, dy=None, loss_bh=None):
     float32 whose sum is the loss)."""
     torch = _torch()
     lib = load_library()
+    _dtype_code(y)
+    if y.dim() != 4:
+        raise ValueError(f"y: expected [B, H, L, d], got shape {tuple(y.shape)}")
     B, H, L, d = y.shape
+    _expect("y_teacher", y_teacher, y.shape, y.dtype, y.device)
+    _expect("dy", dy, y.shape, y.dtype, y.device)
+    _expect("loss_bh", loss_bh, (B, H), torch.float32, y.device)
     p = make_params(B, H, L, d, window=1, n_meta=0, alpha=0.0, dtype=_dtype_code(y))
     if dy is None:
         dy = torch.empty_like(y)

@@ -319,7 +319,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(STATES ? 4 
   #pragma unroll
         for (int rr = 0; rr < 8; ++rr) {
           const bool ok = full || tb + rr < L;
-          const int ro = ok ? rr * D : -tb * D;       // row 0 of the slice when out of range
+          const ptrdiff_t ro = (ptrdiff_t)(ok ? rr : -tb) * D;   // row 0 of the slice when out of range
           float lv[DPL];
           uint32_t xv = 0;
           if constexpr (LOGIT) {
@@ -358,7 +358,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(STATES ? 4 
   #pragma unroll
         for (int rr = 0; rr < VR; ++rr) {
           const bool ok = full || tb + rr < L;
-          const uint32_t u = *reinterpret_cast<const uint32_t*>(vp + (ok ? rr * D : -tb * D));
+          const uint32_t u = *reinterpret_cast<const uint32_t*>(vp + (ptrdiff_t)(ok ? rr : -tb) * D);
           vA[rr] = ok ? u : 0u;
         }
       }

@@ -1,21 +1,25 @@
 """Summaries of rocprofv3 output for the committed profile records.
 
 Reads rocprofv3 CSV output (``--kernel-trace --stats -f csv`` and
-``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs of bench.py with
-``--copy-calibration``) and writes:
+``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs of ``bench.py --only <leg>``
+with ``--copy-calibration``) and writes:
 
-* ``<kernel>_<workload>.md``: average duration per kernel from the stats,
-  with the command that produced them, and the dominant kernel's average
-  over its last ``--steps`` launches (the bench's timed launches follow its
-  warm-up ones, which run while the GPU clock is still rising);
-* ``<kernel>_<workload>_counters.json``: HBM bytes per launch of the
-  dominant kernel, each counter scaled by what it reads for the plain
-  1 GiB device copy (``__amd_rocclr_copyBuffer``) of the same run, and the
-  hash of the kernel source it was measured on (bench.py reports the
-  traffic only while that hash matches).
+* ``<name>_<workload>.md``: the per-kernel statistics of the trace, with the
+  command that produced them, and for each kernel of the leg's step its
+  average over the leg's timed launches.  In a ``--only`` run of bench.py a
+  leg times its step last, so those are the last ``timed`` launches of each
+  such kernel in the trace (each kernel of the benchmark workloads runs once
+  per step); ``timed`` is the leg's own count of timed steps, printed in its
+  JSON record (``timed_steps``);
+* ``<name>_<workload>_counters.json``: HBM bytes per launch of each kernel of
+  the step and their sum per step, each counter scaled by what it reads for
+  the plain 1 GiB device copy (``__amd_rocclr_copyBuffer``) of the same run,
+  and the hash of the kernel source they were measured on (bench.py reports
+  the traffic only while that hash matches).
 
-Usage: python -m subquadratic_attention_amd.prof <name> <workload> <kernel-substring>
-       <source> <trace_dir> <fetch_dir> <write_dir> <out_dir> <command...>
+Usage: python -m subquadratic_attention_amd.prof <name> <workload>
+       <kernel-substring[,kernel-substring...]> <source[,source...]> <trace_dir>
+       <fetch_dir> <write_dir> <out_dir> <timed> <command...>
 """
 from __future__ import annotations
 
@@ -45,67 +49,91 @@ def counter_values(d: str):
     return acc
 
 
-def pick(values, sub, how="mean"):
-    hits = [k for k in values if sub in k]
+def _match(names, sub):
+    hits = sorted(k for k in names if sub in k)
     if not hits:
         raise KeyError(sub)
-    v = values[hits[0]]
+    if len(hits) > 1:
+        raise KeyError(f"{sub} matches {len(hits)} kernels: {hits}")
+    return hits[0]
+
+
+def pick(values, sub, how="mean"):
+    v = values[_match(values, sub)]
     return max(v) if how == "max" else sum(v) / len(v)
 
 
-def timed_average_us(trace_dir: str, sub: str, command: str):
-    """(launches, average in us) of the last --steps launches of the kernel
-    matching sub in the kernel trace, or None without --steps."""
-    words = command.split()
-    if "--steps" not in words:
-        return None
-    k = int(words[words.index("--steps") + 1])
+def timed_average_us(trace_dir: str, sub: str, timed: int):
+    """(launches, average in us) of the last `timed` launches of the kernel
+    matching sub in the kernel trace."""
     rows = [r for r in _rows(trace_dir, "*kernel_trace.csv") if sub in r["Kernel_Name"]]
+    names = {r["Kernel_Name"] for r in rows}
+    if len(names) != 1:
+        raise KeyError(f"{sub} matches {sorted(names)}")
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    last = rows[-k:]
-    if not last:
-        return None
+    last = rows[-timed:]
     return len(last), sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in last) / len(last) / 1e3
 
 
-def source_hash(root: str, rel: str) -> str:
-    with open(os.path.join(root, rel), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(root: str, rels: str) -> str:
+    """Hash of the kernel sources (comma-separated paths, in order)."""
+    h = hashlib.sha256()
+    for rel in rels.split(","):
+        with open(os.path.join(root, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def main(argv):
-    name, workload, ksub, source, trace_dir, fetch_dir, write_dir, out_dir = argv[:8]
-    command = " ".join(argv[8:])
+    name, workload, ksubs, source, trace_dir, fetch_dir, write_dir, out_dir, timed = argv[:9]
+    subs = ksubs.split(",")
+    timed = int(timed)
+    command = " ".join(argv[9:])
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     stats = _rows(trace_dir, "*kernel_stats.csv")
     lines = [f"# {name}: {workload}", "", "Produced by:", "", "```", command, "```", "",
+             "All calls of each kernel in the traced process (warm-up included):", "",
              "| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
     for r in stats:
         lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
-    timed = timed_average_us(trace_dir, ksub, command.split(";")[0])
-    if timed is not None:
-        lines += ["", f"Dominant kernel, its last {timed[0]} launches in this trace (--steps of the traced "
-                  f"command): average {timed[1]:.2f} us."]
+    lines += ["", f"The leg's timed launches (its last {timed} launches of each kernel of its step; the leg's record "
+              f"says timed_steps = {timed}):", "", "| kernel | launches | average (us) |", "|---|---|---|"]
+    total_us = 0.0
+    for sub in subs:
+        n, avg = timed_average_us(trace_dir, sub, timed)
+        total_us += avg
+        lines.append(f"| `{sub}` | {n} | {avg:.2f} |")
+    if len(subs) > 1:
+        lines.append(f"| sum per step | | {total_us:.2f} |")
     fetch = counter_values(fetch_dir)
     write = counter_values(write_dir)
     # the calibration copy is the largest device copy of the run
     f_scale = COPY_BYTES / (pick(fetch, COPY_KERNEL, "max") * 1024)
     w_scale = COPY_BYTES / (pick(write, COPY_KERNEL, "max") * 1024)
-    kf = pick(fetch, ksub) * 1024 * f_scale
-    kw = pick(write, ksub) * 1024 * w_scale
-    lines += ["", "HBM traffic of the dominant kernel (rocprofv3 `--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`, "
-              "each in its own run, scaled by the same counter on a plain 1 GiB device copy):", "",
+    per = {}
+    for sub in subs:
+        per[sub] = {"read_bytes_per_launch": pick(fetch, sub) * 1024 * f_scale,
+                    "write_bytes_per_launch": pick(write, sub) * 1024 * w_scale}
+    tr = sum(v["read_bytes_per_launch"] for v in per.values())
+    tw = sum(v["write_bytes_per_launch"] for v in per.values())
+    lines += ["", "HBM traffic per launch (rocprofv3 `--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`, each in its own run, "
+              "scaled by the same counter on a plain 1 GiB device copy):", "",
               f"- FETCH_SIZE scale factor (1 GiB / copy's FETCH_SIZE): {f_scale:.3f}",
-              f"- WRITE_SIZE scale factor (1 GiB / copy's WRITE_SIZE): {w_scale:.3f}",
-              f"- read bytes per launch: {kf:.4g}", f"- written bytes per launch: {kw:.4g}",
-              f"- source hash of `{source}`: {source_hash(root, source)}"]
+              f"- WRITE_SIZE scale factor (1 GiB / copy's WRITE_SIZE): {w_scale:.3f}", "",
+              "| kernel | read bytes | written bytes |", "|---|---|---|"]
+    for sub, v in per.items():
+        lines.append(f"| `{sub}` | {v['read_bytes_per_launch']:.4g} | {v['write_bytes_per_launch']:.4g} |")
+    if len(subs) > 1:
+        lines.append(f"| sum per step | {tr:.4g} | {tw:.4g} |")
+    lines += ["", f"Source hash of `{source}`: {source_hash(root, source)}"]
     os.makedirs(out_dir, exist_ok=True)
     with open(os.path.join(out_dir, f"{name}_{workload}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
-    rec = {"kernel": ksub, "workload": workload, "source": source, "source_hash": source_hash(root, source),
-           "fetch_scale": f_scale, "write_scale": w_scale, "read_bytes_per_launch": kf,
-           "write_bytes_per_launch": kw, "hbm_bytes_per_launch": kf + kw, "command": command}
+    rec = {"kernels": per, "workload": workload, "source": source, "source_hash": source_hash(root, source),
+           "fetch_scale": f_scale, "write_scale": w_scale, "timed_steps": timed,
+           "read_bytes_per_launch": tr, "write_bytes_per_launch": tw, "hbm_bytes_per_launch": tr + tw,
+           "command": command}
     with open(os.path.join(out_dir, f"{name}_{workload}_counters.json"), "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))

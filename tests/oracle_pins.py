@@ -474,6 +474,26 @@ def p26_stage1_finite_differences(O, n_coords=10):
             worst = max(worst, abs(fd - grad[idx]) / (1e-3 + abs(fd)))
     return worst
 
+
+def p27_transfer_loss_by_hand(O):
+    """The output-matching loss worked by hand.  y = (1, 2, -1, 0) against a
+    zero teacher: the mean of the squares is (1 + 4 + 1 + 0) / 4 = 1.5 and the
+    gradient 2 (y - y_T) / N is (0.5, 1, -0.5, 0).  y = (3, 1) against
+    y_T = (1, 1): (4 + 0) / 2 = 2, gradient (2, 0).  A mean over every element
+    of a [1, 2, 2, 1] tensor (4 elements): errors (1, -1, 2, 0) give 6 / 4 =
+    1.5."""
+    worst = 0.0
+    cases = (
+        (np.array([1.0, 2.0, -1.0, 0.0]), np.zeros(4), 1.5, np.array([0.5, 1.0, -0.5, 0.0])),
+        (np.array([3.0, 1.0]), np.array([1.0, 1.0]), 2.0, np.array([2.0, 0.0])),
+        (np.array([1.0, -1.0, 2.0, 0.0]).reshape(1, 2, 2, 1), np.zeros((1, 2, 2, 1)), 1.5,
+         np.array([0.5, -0.5, 1.0, 0.0]).reshape(1, 2, 2, 1)),
+    )
+    for y, yt, loss_ref, g_ref in cases:
+        loss, g = O.transfer_loss(y, yt)
+        worst = max(worst, abs(loss - loss_ref) / loss_ref, float(np.abs(g - g_ref).max()))
+    return worst
+
 ALL_PINS = {
     "P1": p1_recurrent_equals_quadratic,
     "P2": p2_unit_gate_is_causal_linear_attention,
@@ -501,6 +521,7 @@ ALL_PINS = {
     "P24": p24_segments_equal_one_pass,
     "P25": p25_teacher_is_sdpa,
     "P26": p26_stage1_finite_differences,
+    "P27": p27_transfer_loss_by_hand,
 }
 
 # finite differences carry O(h^2) truncation and O(eps/h) rounding error

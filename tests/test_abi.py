@@ -133,6 +133,17 @@ def test_fwd_pointer_errors(lib):
     assert fwd(lib, params(L=-5)) == S["LIZARD_E_SHAPE"]
 
 
+def test_sequence_length_limit(lib):
+    """L above 2^26 is refused before any launch; at the limit, row offsets
+    of up to L * d elements are formed in 64-bit arithmetic in the kernels
+    (here only the check is exercised: a misaligned q makes the call return
+    before anything is launched, so the fake pointers are never read)."""
+    assert fwd(lib, params(L=(1 << 26) + 1)) == S["LIZARD_E_SHAPE"]
+    assert fwd(lib, params(L=1 << 26), q=MIS) == S["LIZARD_E_ALIGN"]
+    assert bwd(lib, params(L=(1 << 26) + 1)) == S["LIZARD_E_SHAPE"]
+    assert lib.lizard_attn_bwd_workspace_size(ctypes.byref(params(L=(1 << 26) + 1))) == 0
+
+
 def test_bwd_workspace_checks(lib):
     p = params()
     need = lib.lizard_attn_bwd_workspace_size(ctypes.byref(p))

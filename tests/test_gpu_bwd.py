@@ -141,7 +141,7 @@ def test_full_size_workload_sampled(gpu_lib):
     torch.cuda.synchronize()
     for kk in ("dq", "dk", "dv", "dlog_g", "dmeta"):
         assert bool(torch.isfinite(g[kk]).all()), kk
-    picks = [(0, 0), (w.B - 1, w.H - 1), (3, 17)]
+    picks = [(0, 0), (w.B - 1, w.H - 1), (3, 17), (6, 4)]
     for b, h in picks:
         s = si.slice_inputs(w, b, h, with_dy=True)
         r = oracle.lizard_bwd(s["q"][None], s["k"][None], s["v"][None], s["log_g"][None], si.meta_keys(w, h)[None],

@@ -34,7 +34,7 @@ def run_decode(sqa, q, k, v, lg, meta, w, alpha, L0, steps, y_sink=None):
     for p in range(max(0, L0 - w), L0):
         kr[:, :, p % w] = k[:, :, p]
         vr[:, :, p % w] = v[:, :, p]
-    ys = torch.empty((steps, B, H, d), device="cuda", dtype=q.dtype) if y_sink is None else y_sink
+    ys = torch.full((steps, B, H, d), float("nan"), device="cuda", dtype=q.dtype) if y_sink is None else y_sink
     for i in range(steps):
         pos = L0 + i
         sqa.lizard_decode_step(pos, q[:, :, pos].contiguous(), k[:, :, pos].contiguous(), v[:, :, pos].contiguous(),

@@ -121,7 +121,7 @@ def test_decode_logit_continues_prefill(gpu_lib, dtype, d):
     for p in range(max(0, L0 - w), L0):
         kr[:, :, p % w] = k[:, :, p]
         vr[:, :, p % w] = v[:, :, p]
-    ys = torch.empty((steps, B, H, d), device="cuda", dtype=q.dtype)
+    ys = torch.full((steps, B, H, d), float("nan"), device="cuda", dtype=q.dtype)
     for i in range(steps):
         pos = L0 + i
         gpu_lib.lizard_decode_step_logit(pos, q[:, :, pos].contiguous(), k[:, :, pos].contiguous(),

@@ -46,7 +46,7 @@ def test_tokens_equal_single_steps_bitwise(gpu_lib, dtype, d, T, w):
     log(f"decode_tokens vs steps dtype={dtype} d={d} T={T} w={w}")
     q, k, v, lg, meta, state, kr, vr = _prefill_rows(gpu_lib, x, dtype, [L0] * B, w, 0.5)
     st1, kr1, vr1 = state.clone(), kr.clone(), vr.clone()
-    ys1 = torch.empty((T, B, H, d), device="cuda", dtype=q.dtype)
+    ys1 = torch.full((T, B, H, d), float("nan"), device="cuda", dtype=q.dtype)
     for i in range(T):
         pos = L0 + i
         gpu_lib.lizard_decode_step(pos, q[:, :, pos].contiguous(), k[:, :, pos].contiguous(), v[:, :, pos].contiguous(),

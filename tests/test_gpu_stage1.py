@@ -74,7 +74,13 @@ def test_stage1_step(gpu_lib, dtype, d, L):
     r = oracle.stage1_step(flat(x["q"]), flat(x["k"]), flat(x["v"]), flat(x["log_g"]),
                            meta_per_slice(x["meta_k"], B), w, 0.5)
     tol = TAU[dtype]
-    assert abs(float(loss_bh.sum()) - r["loss"]) <= 2 * tol * r["loss"], (float(loss_bh.sum()), r["loss"])
+    # the loss kernel against the oracle's loss of the very y and y_T it was
+    # given (their own parity with the oracle is the layer's and the
+    # teacher's, checked at tau elsewhere); float32 sums in a fixed order
+    own, _ = oracle.transfer_loss(down(fw["y"]), down(yt))
+    assert abs(float(loss_bh.sum()) - own) <= 1e-5 * own, (float(loss_bh.sum()), own)
+    assert_close(down(fw["y"]).reshape(B * H, L, d), r["y"], dtype, "stage1 y")
+    assert_close(down(yt).reshape(B * H, L, d), r["y_teacher"], dtype, "stage1 y_teacher")
     shp = x["q"].shape
     for kk in ("dq", "dk", "dv"):
         assert_close(down(g[kk]), r[kk].reshape(shp), dtype, f"stage1 {kk}")

@@ -113,26 +113,44 @@ def test_train_pair_against_the_oracle(gpu_lib, logit):
     assert e <= TAU[dtype], f"train {gk}: {e:.3e}"
 
 
-def test_train_pair_full_size_sampled(gpu_lib):
-    """B=8, H=32, L=2048, d=128 (the training workload) through the training
-    pair, in the launch configuration the benchmark's stage-1 step times;
-    sampled (b, h) slices against the oracle."""
+@pytest.mark.parametrize("name", ["train_bwd_bf16", "train_d64_bf16", "train_d64_f32"])
+def test_train_pair_full_size_sampled(gpu_lib, name):
+    """The training workloads through the training pair, in the launch
+    configuration the benchmark times (the stage-1 step at B=8, H=32,
+    L=2048, d=128; the bf16-vs-fp32 training-step ablation at d=64 in both
+    operand types): y and lse, then dq, dk, dv and dlog_g of four sampled
+    (b, h) slices against the oracle, and the sink-key gradient of two heads
+    summed over every batch row."""
     import torch
 
-    w = si.WORKLOADS["train_bwd_bf16"]
-    log(f"train pair B={w.B} H={w.H} L={w.L}: generating")
+    w = si.WORKLOADS[name]
+    log(f"train pair {name} B={w.B} H={w.H} L={w.L} d={w.d}: generating")
     x = upload_workload(w, with_dy=True)
     tr = gpu_lib.lizard_attn_fwd_train(x["q"], x["k"], x["v"], x["meta_k"], log_g=x["log_g"], window=w.window,
                                        alpha=w.alpha)
     g = gpu_lib.lizard_attn_bwd_train(x["q"], x["k"], x["v"], x["meta_k"], tr["lse"], tr["chunk_states"], x["dy"],
                                       log_g=x["log_g"], window=w.window, alpha=w.alpha)
     torch.cuda.synchronize()
-    for kk in ("dq", "dk", "dv", "dlog_g"):
+    for kk in ("dq", "dk", "dv", "dlog_g", "dmeta"):
         assert bool(torch.isfinite(g[kk]).all()), kk
-    for b, h in [(0, 0), (w.B - 1, w.H - 1), (5, 9)]:
+    for b, h in [(0, 0), (w.B - 1, w.H - 1), (5, 9), (2, 26)]:
         s = si.slice_inputs(w, b, h, with_dy=True)
-        r = oracle.lizard_bwd(s["q"][None], s["k"][None], s["v"][None], s["log_g"][None], si.meta_keys(w, h)[None],
-                              w.window, w.alpha, s["dy"][None])
-        errs = [assert_close(down(g[kk][b, h]), r[kk][0], "bf16", f"train {kk}[{b},{h}]")
-                for kk in ("dq", "dk", "dv", "dlog_g")]
-        log(f"train slice ({b},{h}): " + " ".join(f"{e:.2e}" for e in errs))
+        mk = si.meta_keys(w, h)[None]
+        o = oracle.lizard_fwd(s["q"][None], s["k"][None], s["v"][None], s["log_g"][None], mk, w.window, w.alpha)
+        r = oracle.lizard_bwd(s["q"][None], s["k"][None], s["v"][None], s["log_g"][None], mk, w.window, w.alpha,
+                              s["dy"][None])
+        errs = [assert_close(down(tr["y"][b, h]), o["y"][0], w.dtype, f"train y[{b},{h}]"),
+                assert_close(down(tr["lse"][b, h]), o["lse"][0], w.dtype, f"train lse[{b},{h}]")]
+        errs += [assert_close(down(g[kk][b, h]), r[kk][0], w.dtype, f"train {kk}[{b},{h}]")
+                 for kk in ("dq", "dk", "dv")]
+        scale = max(float(np.abs(r["dlog_g"]).max()), float(np.abs(s["q"] * r["dq_gate"][0]).max()))
+        e = float(np.abs(down(g["dlog_g"][b, h]) - r["dlog_g"][0]).max()) / scale
+        assert e <= TAU[w.dtype], f"train dlog_g[{b},{h}]: {e:.3e}"
+        log(f"train slice ({b},{h}): " + " ".join(f"{e_:.2e}" for e_ in errs) + f" dlog_g {e:.2e}")
+    for h in (0, w.H - 1):
+        xs = [si.slice_inputs(w, b, h, with_dy=True) for b in range(w.B)]
+        st = lambda n: np.stack([x_[n] for x_ in xs])  # noqa: E731
+        mk = np.broadcast_to(si.meta_keys(w, h)[None], (w.B, w.n_meta, w.d))
+        _, _, _, dmu = oracle.anchor_bwd(st("q"), st("k"), st("v"), mk, w.window, w.alpha * st("dy"))
+        e = assert_close(down(g["dmeta"][h]), dmu.sum(0), w.dtype, f"train dmeta[{h}]")
+        log(f"train dmeta head {h}: {e:.2e}")

@@ -63,6 +63,8 @@ MUTATIONS = [
      "Z = np.where(np.tril(np.ones((L, L), dtype=bool), 1)[None], Z, -np.inf)"),
     ("loss gradient without the factor 2", "return float((e * e).sum() / e.size), 2.0 * e / e.size",
      "return float((e * e).sum() / e.size), e / e.size"),
+    ("loss summed instead of averaged", "return float((e * e).sum() / e.size), 2.0 * e / e.size",
+     "return float((e * e).sum()), 2.0 * e / e.size"),
     ("continuation ignores the halo", "        ya, lse = ya[:, h:], lse[:, h:]\n",
      "        ya, lse = anchor_window(q, k, v, meta_k, w, scale)\n"),
 ]
