@@ -208,6 +208,31 @@ lizard_status_t lizard_attn_fwd_split(const lizard_params_t* p,
                                       void* y, float* lse, void* y_anchor, float* state_out,
                                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- The split forward without allocation ------------------------------
+ *
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, serving loops and harnesses that forbid
+ * hipMalloc.  lizard_attn_fwd_split with its workspace taken from a fixed
+ * array of LIZARD_NOALLOC_SCRATCH_BYTES inside the library (one copy per GPU,
+ * held until the process ends); the call itself allocates nothing.
+ *   Arguments and results are those of lizard_attn_fwd_split without
+ *   workspace / workspace_bytes, bit for bit.
+ *   Sizes whose workspace (lizard_attn_fwd_split_workspace_size) exceeds
+ *   LIZARD_NOALLOC_SCRATCH_BYTES return LIZARD_E_WORKSPACE before anything is
+ *   launched (a 32-head, 32K-token bfloat16 prefill needs about 21 MB).
+ *   Every call on a GPU uses that GPU's one array: calls that may run at the
+ *   same time on one GPU (different streams, or host threads) race on it and
+ *   must be ordered by the caller.  The array keeps the last call's contents;
+ *   no call depends on them. */
+#define LIZARD_NOALLOC_SCRATCH_BYTES (64u << 20)
+lizard_status_t lizard_attn_fwd_split_noalloc(const lizard_params_t* p,
+                                              const void* q, const void* k, const void* v,
+                                              const float* log_g, const void* gate_logit,
+                                              const void* meta_k, const float* state_in,
+                                              const void* k_halo, const void* v_halo, int32_t halo_len,
+                                              void* y, float* lse, void* y_anchor, float* state_out,
+                                              void* stream);
+
 /* ---- Training: the forward pass keeps the states the backward needs ----
  *
  * The layer is trained end to end (de section 2 "Trainingsprozess"), so the

@@ -77,6 +77,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lizard_attn_fwd_split_workspace_size.restype = ctypes.c_size_t
     lib.lizard_attn_fwd_split.argtypes = [P] + [_vp] * 9 + [ctypes.c_int32] + [_vp] * 5 + [ctypes.c_size_t, _vp]
     lib.lizard_attn_fwd_split.restype = ctypes.c_int
+    lib.lizard_attn_fwd_split_noalloc.argtypes = [P] + [_vp] * 9 + [ctypes.c_int32] + [_vp] * 5
+    lib.lizard_attn_fwd_split_noalloc.restype = ctypes.c_int
     lib.lizard_attn_chunk_states_size.argtypes = [P]
     lib.lizard_attn_chunk_states_size.restype = ctypes.c_size_t
     lib.lizard_attn_fwd_train.argtypes = [P] + [_vp] * 12
@@ -567,6 +569,45 @@ def lizard_attn_fwd_split(q, k, v, meta_k, *, log_g=None, gate_logit=None, state
                                    ws_bytes, _stream(q.device))
     _check("lizard_attn_fwd_split", st)
     return o
+
+
+def lizard_attn_fwd_split_noalloc(q, k, v, meta_k, *, log_g=None, gate_logit=None, state_in=None, k_halo=None,
+                                  v_halo=None, window: int, alpha: float, softmax_scale: float = 0.0, chunk: int = 64,
+                                  need_lse: bool = False, need_y_anchor: bool = False, need_state: bool = False,
+                                  out: Optional[Dict] = None) -> Dict:
+    """lizard_attn_fwd_split with its workspace in the library's fixed scratch
+    (NOALLOC_SCRATCH_BYTES per GPU): no workspace argument and no allocation by
+    the library.  Pass every output in ``out`` for a call that allocates
+    nothing at all (missing outputs are allocated here, as in the other
+    calls).  Calls that may overlap on one GPU share the scratch and must be
+    ordered by the caller."""
+    torch = _torch()
+    lib = load_library()
+    _expect_continue(q, k, v, meta_k, log_g, gate_logit, state_in, k_halo, v_halo)
+    B, H, L, d = q.shape
+    m = meta_k.shape[1] if meta_k is not None else 0
+    hl = 0 if k_halo is None else int(k_halo.shape[2])
+    p = make_params(B, H, L, d, window=window, n_meta=m, alpha=alpha, dtype=_dtype_code(q), chunk=chunk,
+                    softmax_scale=softmax_scale)
+    o = dict(out) if out is not None else {}
+    if "y" not in o:
+        o["y"] = torch.empty_like(q)
+    if need_lse and "lse" not in o:
+        o["lse"] = torch.empty((B, H, L), device=q.device, dtype=torch.float32)
+    if need_y_anchor and "y_anchor" not in o:
+        o["y_anchor"] = torch.empty_like(q)
+    if need_state and "state" not in o:
+        o["state"] = torch.empty((B, H, d, d), device=q.device, dtype=torch.float32)
+    _expect_fwd_out(o, q)
+    st = lib.lizard_attn_fwd_split_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(gate_logit),
+                                           _ptr(meta_k), _ptr(state_in), _ptr(k_halo), _ptr(v_halo), hl, _ptr(o["y"]),
+                                           _ptr(o.get("lse")), _ptr(o.get("y_anchor")), _ptr(o.get("state")),
+                                           _stream(q.device))
+    _check("lizard_attn_fwd_split_noalloc", st)
+    return o
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # LIZARD_NOALLOC_SCRATCH_BYTES of include/lizard_attn.h
 
 
 def lizard_attn_fwd_split_workspace_size(B: int, H: int, L: int, d: int, *, dtype_code: int = 1,

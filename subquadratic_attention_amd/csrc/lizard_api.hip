@@ -4,6 +4,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "lizard_attn.h"
 #include "lizard_kernels.hpp"
 
@@ -38,6 +41,30 @@ float scale_of(const lizard_params_t* p) {
 
 lizard_status_t launched(hipError_t e) { return e == hipSuccess ? LIZARD_OK : LIZARD_E_LAUNCH; }
 
+// The fixed scratch of lizard_attn_fwd_split_noalloc: one copy per GPU, held
+// until the process ends.  Host code never uses this name as an address (on
+// the host it is only a handle); the device address of each GPU's copy comes
+// from hipGetSymbolAddress with that GPU current, once, and is kept here.
+static __device__ __align__(256) unsigned char scratch[LIZARD_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current GPU's scratch (nullptr on a HIP error).
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (p != nullptr) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+  g_scratch_ptr[dev].store(p, std::memory_order_release);
+  return p;
+}
+
 // Segments per head of a split forward pass (1: one pass) and its workspace.
 int split_segments(const lizard_params_t* p) {
   const int DV = lizard::fwd_value_slice(p->dtype == LIZARD_BF16, p->dk);
@@ -55,12 +82,19 @@ lizard_status_t attn_fwd(const lizard_params_t* p, const void* q, const void* k,
                          const void* gate_logit, bool logit, const void* meta_k, const float* state_in,
                          const void* k_halo, const void* v_halo, int32_t halo_len, void* y, float* lse,
                          void* y_anchor, float* state_out, void* stream, bool split = false,
-                         void* workspace = nullptr, size_t workspace_bytes = 0, void* chunk_states = nullptr) {
+                         void* workspace = nullptr, size_t workspace_bytes = 0, void* chunk_states = nullptr,
+                         bool fixed_scratch = false) {
   lizard_status_t s = check_params(p, true);
   if (s != LIZARD_OK) return s;
   if (halo_len < 0 || halo_len > p->window - 1) return LIZARD_E_SHAPE;
   const int nseg = split ? split_segments(p) : 1;
-  if (nseg > 1 && (workspace == nullptr || workspace_bytes < split_workspace(p, nseg))) return LIZARD_E_WORKSPACE;
+  if (fixed_scratch) {
+    // the workspace comes from the library's fixed scratch (checked here,
+    // taken after every other check)
+    if (split_workspace(p, nseg) > (size_t)LIZARD_NOALLOC_SCRATCH_BYTES) return LIZARD_E_WORKSPACE;
+  } else if (nseg > 1 && (workspace == nullptr || workspace_bytes < split_workspace(p, nseg))) {
+    return LIZARD_E_WORKSPACE;
+  }
   const int BH = p->B * p->H;
   if (BH == 0) return LIZARD_OK;  // nothing to read or write; empty tensors may have NULL data
   const bool seq = p->L > 0;
@@ -74,6 +108,10 @@ lizard_status_t attn_fwd(const lizard_params_t* p, const void* q, const void* k,
       misaligned(chunk_states))
     return LIZARD_E_ALIGN;
   if (!seq && state_out == nullptr) return LIZARD_OK;
+  if (fixed_scratch && nseg > 1) {
+    workspace = scratch_ptr();
+    if (workspace == nullptr) return LIZARD_E_LAUNCH;
+  }
   const int bf = p->dtype == LIZARD_BF16;
   const int DV = lizard::fwd_value_slice(bf, p->dk);
   lizard::FwdArgs a{};
@@ -248,6 +286,17 @@ LIZARD_API lizard_status_t lizard_attn_fwd_split(const lizard_params_t* p, const
   if (log_g != nullptr && gate_logit != nullptr) return LIZARD_E_SHAPE;
   return attn_fwd(p, q, k, v, log_g, gate_logit, gate_logit != nullptr, meta_k, state_in, k_halo, v_halo, halo_len, y,
                   lse, y_anchor, state_out, stream, true, workspace, workspace_bytes);
+}
+
+LIZARD_API lizard_status_t lizard_attn_fwd_split_noalloc(const lizard_params_t* p, const void* q, const void* k,
+                                                         const void* v, const float* log_g, const void* gate_logit,
+                                                         const void* meta_k, const float* state_in,
+                                                         const void* k_halo, const void* v_halo, int32_t halo_len,
+                                                         void* y, float* lse, void* y_anchor, float* state_out,
+                                                         void* stream) {
+  if (log_g != nullptr && gate_logit != nullptr) return LIZARD_E_SHAPE;
+  return attn_fwd(p, q, k, v, log_g, gate_logit, gate_logit != nullptr, meta_k, state_in, k_halo, v_halo, halo_len, y,
+                  lse, y_anchor, state_out, stream, true, nullptr, 0, nullptr, true);
 }
 
 LIZARD_API size_t lizard_attn_chunk_states_size(const lizard_params_t* p) {
