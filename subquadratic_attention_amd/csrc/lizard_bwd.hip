@@ -440,7 +440,9 @@ struct AqLayout {
 // The grid covers chunks cb .. cb + ncl - 1; GUARD = false: they are full
 // (every query inside [0, L)); window keys before position 0 (chunk 0) are
 // read from row 0 and masked out with the rest of the window.
-template <typename T, int D, bool GUARD>
+// ACC: add the anchor part to what dq holds (the gated part, written before by
+// the reverse walk) instead of writing it alone.
+template <typename T, int D, bool GUARD, bool ACC = false>
 __global__ __launch_bounds__(256, 3) void bwd_anchor_q_kernel(BwdArgs a, int cb, int ncl) {
   typedef AqLayout<T, D> Lay;
   typedef Mfma<T> M;
@@ -570,7 +572,12 @@ __global__ __launch_bounds__(256, 3) void bwd_anchor_q_kernel(BwdArgs a, int cb,
 #pragma unroll
   for (int e = 0; e < NS; ++e) sf[e] = M::pack(zsv + e * M::KPL);
   // dq^T[d][t] = scale (K^T dZ^T + mu^T dZs^T)
-  T* dqa = reinterpret_cast<T*>(a.dq) + (size_t)bh * L * D;   // the anchor part; the gate kernel adds its own
+  T* dqa = reinterpret_cast<T*>(a.dq) + (size_t)bh * L * D;   // the anchor part (ACC: added to the gated part)
+  float prev[ACC ? NDT : 1][4];
+  if constexpr (ACC) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) load_pack<T, 4>(dqa + (size_t)(tme < L ? tme : 0) * D + 16 * dt + 4 * g, prev[dt]);
+  }
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
     f32x4 o = zero4();
@@ -581,7 +588,11 @@ __global__ __launch_bounds__(256, 3) void bwd_anchor_q_kernel(BwdArgs a, int cb,
 #pragma unroll
     for (int e = 0; e < NS; ++e) o = M::mma(sink_frag<T>(az, g, e), sf[e], o);
     if (tme < L) {
-      const float v4[4] = {o[0] * a.scale, o[1] * a.scale, o[2] * a.scale, o[3] * a.scale};
+      float v4[4] = {o[0] * a.scale, o[1] * a.scale, o[2] * a.scale, o[3] * a.scale};
+      if constexpr (ACC) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v4[r] += prev[dt][r];
+      }
       store_pack<T, 4>(dqa + (size_t)tme * D + 16 * dt + 4 * g, v4);
     }
   }
@@ -634,7 +645,8 @@ struct AkLayout {
 // The grid covers chunks cb .. cb + ncl - 1; GUARD = false: they are full
 // (every key inside [0, L)); window queries past L (the last full chunk's
 // next chunk) are read from row L - 1 and masked out.  Two workgroups per CU.
-template <typename T, int D, bool GUARD>
+// ACC: as for the query side (dk and dv hold the gated parts).
+template <typename T, int D, bool GUARD, bool ACC = false>
 __global__ __launch_bounds__(256, 2) void bwd_anchor_k_kernel(BwdArgs a, int cb, int ncl) {
   typedef AkLayout<T, D> Lay;
   typedef Mfma<T> M;
@@ -728,9 +740,18 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_k_kernel(BwdArgs a, int cb,
     zf[e] = M::pack(pz + e * M::KPL);
     pf[e] = M::pack(pp + e * M::KPL);
   }
-  // the anchor parts of dk and dv; the gate kernel adds its own
+  // the anchor parts of dk and dv (ACC: added to the gated parts)
   T* dka = reinterpret_cast<T*>(a.dk) + (size_t)bh * L * D;
   T* dva = reinterpret_cast<T*>(a.dv) + (size_t)bh * L * D;
+  float prevk[ACC ? NDT : 1][4], prevv[ACC ? NDT : 1][4];
+  if constexpr (ACC) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const size_t o = (size_t)(sme < L ? sme : 0) * D + 16 * dt + 4 * g;
+      load_pack<T, 4>(dka + o, prevk[dt]);
+      load_pack<T, 4>(dva + o, prevv[dt]);
+    }
+  }
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
     f32x4 ok_ = zero4(), ov = zero4();
@@ -742,8 +763,15 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_k_kernel(BwdArgs a, int cb,
       ov = M::mma(window_frag<T>(ay, Q0, g, e), pf[e], ov);
     }
     if (sme < L) {
-      const float k4[4] = {ok_[0] * a.scale, ok_[1] * a.scale, ok_[2] * a.scale, ok_[3] * a.scale};
-      const float v4[4] = {ov[0], ov[1], ov[2], ov[3]};
+      float k4[4] = {ok_[0] * a.scale, ok_[1] * a.scale, ok_[2] * a.scale, ok_[3] * a.scale};
+      float v4[4] = {ov[0], ov[1], ov[2], ov[3]};
+      if constexpr (ACC) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          k4[r] += prevk[dt][r];
+          v4[r] += prevv[dt][r];
+        }
+      }
       store_pack<T, 4>(dka + (size_t)sme * D + 16 * dt + 4 * g, k4);
       store_pack<T, 4>(dva + (size_t)sme * D + 16 * dt + 4 * g, v4);
     }
@@ -784,7 +812,7 @@ struct GateLayout {
 // grid covers chunks cb .. cb + ncl - 1; RAGGED: they may end past L (only
 // the last chunk of a sequence does), so token rows are range-checked.
 template <typename T, int D, bool RAGGED, bool LOGIT>
-__global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int cb, int ncl) {
+__device__ __forceinline__ void gate_chunk(const BwdArgs& a, const int bh, const int c) {
   typedef GateLayout<T, D> Lay;
   typedef Mfma<T> M;
   typedef typename M::frag frag;
@@ -812,9 +840,6 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
   float* sEB = reinterpret_cast<float*>(smem + Lay::OFF_EB);   // fast path: [0][i] = 2^{B_i - r_i}, [1][i] = 2^{r_i - B_i}
 
   const int L = a.L, nc = (L + C - 1) / C;
-  int bh, c;
-  if (!chunk_block(a.BH, ncl, bh, c)) return;
-  c += cb;
   const int t0 = c * C;
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, m = l & 15, g = l >> 4;
   constexpr bool RG = RAGGED;
@@ -1289,6 +1314,620 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
   }
 }
 
+template <typename T, int D, bool RAGGED, bool LOGIT>
+__global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int cb, int ncl) {
+  int bh, c;
+  if (!chunk_block(a.BH, ncl, bh, c)) return;
+  gate_chunk<T, D, RAGGED, LOGIT>(a, bh, c + cb);
+}
+
+// The chunks the reverse walk flagged (decay span beyond twice the
+// factorisable limit in some dimension), from G_{c+1} and its transpose the
+// walk wrote for them: a persistent grid, each workgroup scanning every
+// gridDim.x-th flag (uniform per workgroup), range-checked rows.
+template <typename T, int D, bool LOGIT>
+__global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_flagged_kernel(BwdArgs a) {
+  const int nc = (a.L + C - 1) / C;
+  const long long n = (long long)a.BH * nc;
+  for (long long idx = blockIdx.x; idx < n; idx += gridDim.x) {
+    if (a.ws_flag[idx]) {
+      gate_chunk<T, D, true, LOGIT>(a, (int)(idx / nc), (int)(idx % nc));
+      __syncthreads();   // the next chunk's operands overwrite this one's in LDS
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 5 (bf16, d = 128). Reverse walk: the gated branch of every chunk of one
+// head, last chunk first, with the state gradient held in MFMA accumulators
+// ---------------------------------------------------------------------------
+//
+// G_c = diag(2^B) G_{c+1} + Qe^T dO is carried from chunk to chunk in
+// registers instead of a pass that writes every G_{c+1} (and its transpose)
+// to memory for a per-chunk kernel to read back.  One workgroup of 8
+// wavefronts per (b, h).  Wavefront w owns the 16-dim group dg = w of the
+// key dims / value columns: lane (m, g) holds token 16tt + m and dims
+// 16dg + 4g + r (r = 0..3) of every 16-token tile tt of the chunk, for the log-gate prefix
+// (a scan over the 16 lanes of a row), the decay factors and the outputs
+// alike, so every global load and store of token data is a whole 8- or
+// 16-byte piece and no value changes lanes between the prefix and the
+// epilogue.  Per group the wavefront also holds two copies of G in fp32
+// accumulators: X[it] = G[16it .. +16][16dg .. +16] and
+// Y[jt] = G[16dg .. +16][16jt .. +16]^T.
+// Rounded to bf16, the registers of X are directly the rows of G^T (for
+// dv = G^T Kh, contraction over i) and those of Y the rows of G (for
+// dk = G V, contraction over j) in the lane order the accumulators leave
+// them: the contraction runs over {32e + 4g + r, 32e + 16 + 4g + r}, and the
+// other operand is gathered in that order (two 8-byte LDS reads).
+//
+// Per chunk, three barriers: (1) prefix, factors, operands into LDS, the
+// state rows and the next chunk's rows issued; (2) the causal score tiles
+// A = Qe Kp^T and dA = dO V^T; (3) per token tile, last to first: the
+// inter-chunk terms (S dO, G V, G^T Kh), the intra-chunk terms (Kp^T dA,
+// Qe^T dA^T, dO^T A^T), the outputs (added to the anchor parts already in
+// dq, dk, dv) and dlog_g; then the update of G.
+//
+// dlog_g of a token t of chunk c is the suffix sum of q.dq - k.dk over the
+// chunk's tokens u >= t plus, for everything after the chunk, the boundary
+// term rowsum(S_{c+1} * G_{c+1}) (the identity the per-chunk kernel uses),
+// formed at the end of the previous step from the state rows this lane
+// loaded for S dO, gathered in Y's column order, and from Y.
+//
+// Chunks whose decay span exceeds twice the factorisable limit in some
+// dimension are not computed here: the walk writes G_{c+1} and its transpose
+// for them and flags them, and the per-chunk kernel (pairwise fp32 terms)
+// completes them afterwards.  Spans between the limit and twice it move
+// that dimension's reference point to half its chunk total (per dimension:
+// Qe = q 2^{beta - r}, Kp = k 2^{r - beta}, G updated as
+// 2^r (2^{B - r} G + Qe^T dO)).
+struct WalkLayout {
+  static constexpr int D = 128;
+  static constexpr int LDR = D + 8;    // row-major token tiles [64][LDR]
+  static constexpr int LDT = 64 + 8;   // transposed tiles [D][LDT]; score tiles [64][LDT]
+  static constexpr int ROWS = 64 * LDR * 2, TRANS = D * LDT * 2, SCORE = 64 * LDT * 2;
+  static constexpr int OFF_QE = 0;                   // Qe[t][i]
+  static constexpr int OFF_KP = OFF_QE + ROWS;       // Kp[s][i]
+  static constexpr int OFF_O = OFF_KP + ROWS;        // dO[t][j]
+  static constexpr int OFF_V = OFF_O + ROWS;         // V[s][j]
+  static constexpr int OFF_QET = OFF_V + ROWS;       // Qe^T[i][t]
+  static constexpr int OFF_KPT = OFF_QET + TRANS;    // Kp^T[i][s]
+  static constexpr int OFF_OT = OFF_KPT + TRANS;     // dO^T[j][t]
+  static constexpr int OFF_AT = OFF_OT + TRANS;      // A^T[s][t]
+  static constexpr int OFF_DA = OFF_AT + SCORE;      // dA[t][s]
+  static constexpr int OFF_DAT = OFF_DA + SCORE;     // dA^T[s][t]
+  static constexpr int OFF_EBR = OFF_DAT + SCORE;    // 2^{B_i - r_i}
+  static constexpr int OFF_RX = OFF_EBR + D * 4;     // 2^{r_i}
+  static constexpr int OFF_FLAG = OFF_RX + D * 4;    // per wavefront: 1 = a dim beyond twice the limit, 2 = a shifted reference
+  static constexpr int TOTAL = OFF_FLAG + 64;
+};
+
+__device__ __forceinline__ uint2 ld8(const void* p) { return *reinterpret_cast<const uint2*>(p); }
+// An int passed through an empty asm (values derived from it are not hoisted
+// out of the loop they are used in).
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+__device__ __forceinline__ void st8(void* p, uint2 v) { *reinterpret_cast<uint2*>(p) = v; }
+__device__ __forceinline__ uint2 pack4(const float* v) {
+  bf16x4 p;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = static_cast<bf16>(v[i]);
+  return __builtin_bit_cast(uint2, p);
+}
+__device__ __forceinline__ uint2 pack4(f32x4 v) {
+  const float f[4] = {v[0], v[1], v[2], v[3]};
+  return pack4(f);
+}
+__device__ __forceinline__ void unpack4(uint2 u, float* v) {
+  const bf16x4 p = __builtin_bit_cast(bf16x4, u);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = static_cast<float>(p[i]);
+}
+__device__ __forceinline__ bf16 half_of(uint2 u, int r) {
+  const uint32_t w = r < 2 ? u.x : u.y;
+  return __builtin_bit_cast(bf16, (unsigned short)((r & 1) ? (w >> 16) : (w & 0xffffu)));
+}
+__device__ __forceinline__ bf16x8 frag2(uint2 a, uint2 b) {
+  return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
+__device__ __forceinline__ bf16x8 frag2(f32x4 a, f32x4 b) {
+  bf16x8 f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[i] = static_cast<bf16>(a[i]);
+    f[4 + i] = static_cast<bf16>(b[i]);
+  }
+  return f;
+}
+
+template <bool LOGIT>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void bwd_walk_kernel(BwdArgs a) {
+  typedef WalkLayout Lay;
+  typedef bf16 T;
+  typedef Mfma<T> M;
+  constexpr int D = Lay::D, LDR = Lay::LDR, LDT = Lay::LDT;
+  constexpr int NW = 8;       // wavefronts
+  constexpr int GPW = 1;      // 16-dim groups per wavefront
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* sQe = reinterpret_cast<T*>(smem + Lay::OFF_QE);
+  T* sKp = reinterpret_cast<T*>(smem + Lay::OFF_KP);
+  T* sO = reinterpret_cast<T*>(smem + Lay::OFF_O);
+  T* sV = reinterpret_cast<T*>(smem + Lay::OFF_V);
+  T* sQeT = reinterpret_cast<T*>(smem + Lay::OFF_QET);
+  T* sKpT = reinterpret_cast<T*>(smem + Lay::OFF_KPT);
+  T* sOT = reinterpret_cast<T*>(smem + Lay::OFF_OT);
+  T* sAT = reinterpret_cast<T*>(smem + Lay::OFF_AT);
+  T* sDA = reinterpret_cast<T*>(smem + Lay::OFF_DA);
+  T* sDAT = reinterpret_cast<T*>(smem + Lay::OFF_DAT);
+  float* sEBr = reinterpret_cast<float*>(smem + Lay::OFF_EBR);
+  float* sRx = reinterpret_cast<float*>(smem + Lay::OFF_RX);
+  int* sFlag = reinterpret_cast<int*>(smem + Lay::OFF_FLAG);
+
+  const int bh = blockIdx.x;
+  if (bh >= a.BH) return;
+  const int L = a.L, nc = (L + C - 1) / C;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // lane indices, passed through an empty asm at the top of every chunk so
+  // that the many addresses derived from them are formed where they are used
+  // instead of being hoisted out of the chunk loop (which would hold them in
+  // registers for the whole walk)
+  int l = tid & 63, m = l & 15, g = l >> 4;
+  // dim group dg = GPW w + h (dims / value columns [16 dg, 16 dg + 16)); this
+  // lane's first dim in it is 16 dg + 4g
+  auto i0_of = [&](int h) __attribute__((always_inline)) { return 16 * (GPW * w + h) + 4 * g; };
+  const size_t hb = (size_t)bh * L * D;
+  const T* __restrict__ qg = reinterpret_cast<const T*>(a.q) + hb;
+  const T* __restrict__ kg = reinterpret_cast<const T*>(a.k) + hb;
+  const T* __restrict__ vg = reinterpret_cast<const T*>(a.v) + hb;
+  const T* __restrict__ dyg = reinterpret_cast<const T*>(a.dy) + hb;
+  const float* __restrict__ lgg = LOGIT ? nullptr : a.log_g + hb;
+  const T* __restrict__ xg = LOGIT ? reinterpret_cast<const T*>(a.gate_logit) + hb : nullptr;
+  const T* __restrict__ Sg = reinterpret_cast<const T*>(a.ws_states) + (size_t)bh * nc * D * D;
+  T* __restrict__ dqo = reinterpret_cast<T*>(a.dq) + hb;
+  T* __restrict__ dko = reinterpret_cast<T*>(a.dk) + hb;
+  T* __restrict__ dvo = reinterpret_cast<T*>(a.dv) + hb;
+  float* __restrict__ dbo = LOGIT ? nullptr : a.dlog_g + hb;
+  T* __restrict__ dxo = LOGIT ? reinterpret_cast<T*>(a.dgate) + hb : nullptr;
+
+  // the score tiles above the diagonal are never written: zero once
+  for (int x = tid; x < 3 * Lay::SCORE / 16; x += 64 * NW)
+    reinterpret_cast<uint4*>(smem + Lay::OFF_AT)[x] = make_uint4(0u, 0u, 0u, 0u);
+
+  f32x4 X[GPW][8], Y[GPW][8];
+#pragma unroll
+  for (int h = 0; h < GPW; ++h)
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      X[h][x] = zero4();
+      Y[h][x] = zero4();
+    }
+  // rowsum(S_{c+1} * G_{c+1}) of dims i0 + r (zero after the last chunk)
+  float bnd[GPW][4];
+#pragma unroll
+  for (int h = 0; h < GPW; ++h)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bnd[h][r] = 0.f;
+
+  // one chunk's rows of this lane: the queries, keys and gates loaded a
+  // chunk ahead (at the start of the previous chunk), the values and dO at
+  // the end of the previous chunk (they go to LDS last in step 1)
+  uint2 pq[GPW][4], pk[GPW][4], pv[GPW][4], po[GPW][4], px[GPW][4];
+  float4 plg[GPW][4];
+  auto load_qkg = [&](int c, bool full) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < GPW; ++h)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int t = c * C + 16 * tt + m;
+        const bool ok = full || t < L;
+        const size_t off = (size_t)(ok ? t : 0) * D + i0_of(h);
+        const uint2 z = make_uint2(0u, 0u);
+        const uint2 q_ = ld8(qg + off), k_ = ld8(kg + off);
+        pq[h][tt] = ok ? q_ : z;
+        pk[h][tt] = ok ? k_ : z;
+        if constexpr (LOGIT) {
+          const uint2 x_ = ld8(xg + off);
+          px[h][tt] = ok ? x_ : make_uint2(0x7f807f80u, 0x7f807f80u);   // past L: a logit of +inf, a gate of one
+        } else {
+          const float4 f = *reinterpret_cast<const float4*>(lgg + off);
+          plg[h][tt] = ok ? f : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+  };
+  auto load_vo = [&](int c, bool full) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < GPW; ++h)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int t = c * C + 16 * tt + m;
+        const bool ok = full || t < L;
+        const size_t off = (size_t)(ok ? t : 0) * D + i0_of(h);
+        const uint2 z = make_uint2(0u, 0u);
+        const uint2 v_ = ld8(vg + off), o_ = ld8(dyg + off);
+        pv[h][tt] = ok ? v_ : z;
+        po[h][tt] = ok ? o_ : z;
+      }
+  };
+  if (nc > 0) {
+    if (nc * C <= L) {
+      load_qkg(nc - 1, true);
+      load_vo(nc - 1, true);
+    } else {
+      load_qkg(nc - 1, false);
+      load_vo(nc - 1, false);
+    }
+  }
+
+  for (int c = nc - 1; c >= 0; --c) {
+    asm volatile("" : "+v"(l), "+v"(m), "+v"(g));
+    const int t0 = c * C;
+    const bool full = t0 + C <= L;
+    // ================= step 1: prefix, factors, operands ==================
+    uint2 cq[GPW][4], ck[GPW][4], cx[GPW][4];
+    float lgv[GPW][4][4];
+#pragma unroll
+    for (int h = 0; h < GPW; ++h)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        cq[h][tt] = pq[h][tt];
+        ck[h][tt] = pk[h][tt];
+        if constexpr (LOGIT) {
+          cx[h][tt] = px[h][tt];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) lgv[h][tt][r] = log_sigmoid(static_cast<float>(half_of(cx[h][tt], r)));
+        } else {
+          lgv[h][tt][0] = plg[h][tt].x;
+          lgv[h][tt][1] = plg[h][tt].y;
+          lgv[h][tt][2] = plg[h][tt].z;
+          lgv[h][tt][3] = plg[h][tt].w;
+        }
+      }
+    // the state rows for S dO (row 16 dg + m, columns 16x + 4g .. +3), then
+    // the next chunk's rows
+    uint2 Sr[GPW][8];
+#pragma unroll
+    for (int h = 0; h < GPW; ++h) {
+      const T* sp = Sg + (size_t)c * D * D + (size_t)(16 * (GPW * w + h) + m) * D + 4 * g;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) Sr[h][x] = ld8(sp + 16 * x);
+    }
+    if (c > 0) load_qkg(c - 1, true);
+
+    // log2-gate prefix: a scan over the 16 lanes of each row (the tile's
+    // tokens), then the earlier tiles' totals
+    float beta[GPW][4][4], Bt[GPW][4], rr[GPW][4];
+    bool wide = false, mid = false;
+#pragma unroll
+    for (int h = 0; h < GPW; ++h) {
+      float run[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x = log2_gate(lgv[h][tt][r]);
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) {
+            const float y = __shfl_up(x, o, 16);
+            x += m >= o ? y : 0.f;
+          }
+          beta[h][tt][r] = x + run[r];
+          run[r] += __shfl(x, (l & 48) | 15, 64);
+        }
+      // reference points: the chunk start, or half the chunk total for spans
+      // between the factorisable limit and twice it (beyond that the chunk
+      // is left to the per-chunk kernel; its dims keep the chunk start, so
+      // that Qe = q 2^beta stays bounded for the update of G)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        Bt[h][r] = run[r];
+        const float span = -run[r];
+        const bool wd = span > 2.f * kMaxSpan;
+        const bool md = !wd && span > kMaxSpan;
+        wide |= wd;
+        mid |= md;
+        rr[h][r] = md ? 0.5f * run[r] : 0.f;
+      }
+      // from here on beta holds b = beta - r
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) beta[h][tt][r] -= rr[h][r];
+    }
+    // Qe = q 2^{beta - r}, Kp = k 2^{r - beta}: row-major and transposed
+    asm volatile("" : "+v"(l), "+v"(m), "+v"(g));
+#pragma unroll
+    for (int h = 0; h < GPW; ++h) {
+      const int i0 = i0_of(h);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int row = 16 * tt + m;
+        float qf[4], kf[4], qe[4], kp[4];
+        unpack4(cq[h][tt], qf);
+        unpack4(ck[h][tt], kf);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float b = beta[h][tt][r];
+          qe[r] = qf[r] * exp_2(b);
+          kp[r] = kf[r] * exp_2(fminf(-b, 126.f));   // (finite where the chunk is left to the per-chunk kernel)
+        }
+        const uint2 qe4 = pack4(qe), kp4 = pack4(kp);
+        st8(sQe + row * LDR + i0, qe4);
+        st8(sKp + row * LDR + i0, kp4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          sQeT[(i0 + r) * LDT + row] = half_of(qe4, r);
+          sKpT[(i0 + r) * LDT + row] = half_of(kp4, r);
+        }
+      }
+      if (m == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          sEBr[i0 + r] = exp_2(Bt[h][r] - rr[h][r]);
+          sRx[i0 + r] = exp_2(rr[h][r]);
+        }
+      }
+      // dO and V rows (loaded at the end of the previous chunk) into LDS:
+      // row-major, and dO transposed
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int row = 16 * tt + m;
+        st8(sO + row * LDR + i0, po[h][tt]);
+        st8(sV + row * LDR + i0, pv[h][tt]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sOT[(i0 + r) * LDT + row] = half_of(po[h][tt], r);
+      }
+    }
+    {
+      const bool ww = __any(wide), wm = __any(mid);
+      if (l == 0) sFlag[w] = (ww ? 1 : 0) | (wm ? 2 : 0);
+    }
+    __syncthreads();
+
+    // ================= step 2: score tiles ==================================
+    asm volatile("" : "+v"(l), "+v"(m), "+v"(g));
+    int fl = 0;
+#pragma unroll
+    for (int x = 0; x < NW; ++x) fl |= sFlag[x];
+    const bool cwide = (fl & 1) != 0, cmid = (fl & 2) != 0;
+    if (!cwide) {
+      // 10 causal (I, J <= I) tiles of A and of dA: jobs w, w + NW, ...
+#pragma unroll
+      for (int jb = 0; jb < (20 + NW - 1) / NW; ++jb) {
+        const int j = w + NW * jb;
+        if (j >= 20) break;
+        const int tl = j % 10;
+        const int I = tl < 1 ? 0 : tl < 3 ? 1 : tl < 6 ? 2 : 3;
+        const int J = tl - I * (I + 1) / 2;
+        if (j < 10) {
+          // A[t][s] = Qe_t . Kp_s: rows t = 16I + 4g + r, column s = 16J + m -> A^T[s][t..t+3]
+          const f32x4 v = mma_rows<T, D>(zero4(), sQe + (16 * I + m) * LDR + 32 * g, sKp + (16 * J + m) * LDR + 32 * g);
+          float a4[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) a4[r] = (16 * J + m <= 16 * I + 4 * g + r) ? v[r] : 0.f;
+          st8(sAT + (16 * J + m) * LDT + 16 * I + 4 * g, pack4(a4));
+        } else {
+          // dA[t][s] = dO_t . v_s: rows s = 16J + 4g + r, column t = 16I + m -> dA[t][s..s+3] and dA^T
+          const f32x4 v = mma_rows<T, D>(zero4(), sV + (16 * J + m) * LDR + 32 * g, sO + (16 * I + m) * LDR + 32 * g);
+          float a4[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) a4[r] = (16 * J + 4 * g + r <= 16 * I + m) ? v[r] : 0.f;
+          const uint2 p4 = pack4(a4);
+          st8(sDA + (16 * I + m) * LDT + 16 * J + 4 * g, p4);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sDAT[(16 * J + 4 * g + r) * LDT + 16 * I + m] = half_of(p4, r);
+        }
+      }
+    } else {
+      // left to the per-chunk kernel: G_{c+1} (rows of Y) and its transpose
+      // (rows of X), in the element type; the chunk's dq, dk, dv rows zero
+      // (that kernel adds its gated parts to them, the anchor kernels theirs)
+#pragma unroll
+      for (int h = 0; h < GPW; ++h) {
+        const size_t ro = ((size_t)bh * nc + c) * D * D + (size_t)(16 * (GPW * w + h) + m) * D + 4 * g;
+        T* Gd = reinterpret_cast<T*>(a.ws_dS) + ro;
+        T* GTd = reinterpret_cast<T*>(a.ws_dST) + ro;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          st8(GTd + 16 * x, pack4(X[h][x]));
+          st8(Gd + 16 * x, pack4(Y[h][x]));
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          const int t = t0 + 16 * tt + m;
+          if (full || t < L) {
+            const size_t off = (size_t)t * D + i0_of(h);
+            st8(dqo + off, make_uint2(0u, 0u));
+            st8(dko + off, make_uint2(0u, 0u));
+            st8(dvo + off, make_uint2(0u, 0u));
+          }
+        }
+      }
+    }
+    if (tid == 0) a.ws_flag[(size_t)bh * nc + c] = cwide ? 1 : 0;
+    __syncthreads();
+
+    // ================= step 3: outputs of the chunk, then G ================
+    if (!cwide) {
+#pragma unroll
+      for (int h = 0; h < GPW; ++h) {
+        const int dg = GPW * w + h;
+        float tcarry[4] = {0.f, 0.f, 0.f, 0.f};   // q.dq - k.dk over the chunk's later tiles
+#pragma unroll
+        for (int tt = 3; tt >= 0; --tt) {
+          asm volatile("" : "+v"(l), "+v"(m), "+v"(g));
+          const int row = 16 * tt + m;
+          const int i0 = i0_of(h);
+          const int t = t0 + row;
+          const bool live = full || t < L;
+          const size_t off = (size_t)(live ? t : 0) * D + i0;
+          // this tile's raw q, k (and gate logits) again, for dlog_g at the
+          // end of the tile (cache hits: step 1 read them; holding them in
+          // registers across the steps would cost 16 more)
+          uint2 tq = ld8(qg + off), tk = ld8(kg + off), tx = make_uint2(0u, 0u);
+          if constexpr (LOGIT) tx = ld8(xg + off);
+          if (!full && !live) {
+            tq = make_uint2(0u, 0u);
+            tk = make_uint2(0u, 0u);
+          }
+          const T* orow = sO + row * LDR + 4 * g;
+          const T* vrow = sV + row * LDR + 4 * g;
+          const T* krow = sKp + row * LDR + 4 * g;
+          float iq[4], ik[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            iq[r] = exp_2(beta[h][tt][r]);    // 2^{beta - r}
+            ik[r] = exp_2(-beta[h][tt][r]);   // 2^{r - beta}
+          }
+          // (the three outputs one after another: fewer operands and
+          // accumulators live at a time)
+          // dq = 2^{beta} S dO + 2^{beta - r} Kp^T dA
+          float dqg[4];
+          {
+            f32x4 qi = zero4();
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              qi = M::mma(frag2(Sr[h][2 * e], Sr[h][2 * e + 1]),
+                          frag2(ld8(orow + 32 * e), ld8(orow + 32 * e + 16)), qi);   // (S dO_t)_i
+            const f32x4 qa = mma_rows<T, 64>(zero4(), sKpT + (16 * dg + m) * LDT + 16 * g, sDA + row * LDT + 16 * g);
+            const float4 rx = *reinterpret_cast<const float4*>(sRx + i0);     // 2^r
+            const float rxv[4] = {rx.x, rx.y, rx.z, rx.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dqg[r] = iq[r] * fmaf(rxv[r], qi[r], qa[r]);
+            if (live) st8(dqo + off, pack4(dqg));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          // dk = 2^{B - beta} G v + 2^{r - beta} Qe^T dA^T
+          float dkg[4];
+          {
+            f32x4 ki = zero4();
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              ki = M::mma(frag2(Y[h][2 * e], Y[h][2 * e + 1]),
+                          frag2(ld8(vrow + 32 * e), ld8(vrow + 32 * e + 16)), ki);   // (G v_s)_i
+            const f32x4 ka = mma_rows<T, 64>(zero4(), sQeT + (16 * dg + m) * LDT + 16 * g, sDAT + row * LDT + 16 * g);
+            const float4 ebr = *reinterpret_cast<const float4*>(sEBr + i0);   // 2^{B - r}
+            const float eBr[4] = {ebr.x, ebr.y, ebr.z, ebr.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dkg[r] = ik[r] * fmaf(eBr[r], ki[r], ka[r]);
+            if (live) st8(dko + off, pack4(dkg));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          // dv = G^T Kh + A^T dO
+          {
+            f32x4 vi = zero4();
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int o1 = 32 * e, o2 = 32 * e + 16;
+              // Kh_s = Kp_s 2^{B - r} in the gathered dim order
+              float kv[8];
+              unpack4(ld8(krow + o1), kv);
+              unpack4(ld8(krow + o2), kv + 4);
+              const float4 f1 = *reinterpret_cast<const float4*>(sEBr + o1 + 4 * g);
+              const float4 f2 = *reinterpret_cast<const float4*>(sEBr + o2 + 4 * g);
+              kv[0] *= f1.x;
+              kv[1] *= f1.y;
+              kv[2] *= f1.z;
+              kv[3] *= f1.w;
+              kv[4] *= f2.x;
+              kv[5] *= f2.y;
+              kv[6] *= f2.z;
+              kv[7] *= f2.w;
+              vi = M::mma(frag2(X[h][2 * e], X[h][2 * e + 1]), M::pack(kv), vi);   // (G^T Kh_s)_j
+            }
+            const f32x4 va = mma_rows<T, 64>(zero4(), sOT + (16 * dg + m) * LDT + 16 * g, sAT + row * LDT + 16 * g);
+            float dv4[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dv4[r] = vi[r] + va[r];
+            if (live) st8(dvo + off, pack4(dv4));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          // dlog_g: the tile's tokens u >= t (lanes m' >= m of the row), the
+          // later tiles, and everything after the chunk
+          {
+            float qf[4], kf[4], dl[4];
+            unpack4(tq, qf);
+            unpack4(tk, kf);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              float sfx = qf[r] * dqg[r] - kf[r] * dkg[r];
+#pragma unroll
+              for (int o = 1; o < 16; o <<= 1) {
+                const float y = __shfl_down(sfx, o, 16);
+                sfx += m + o < 16 ? y : 0.f;
+              }
+              dl[r] = sfx + tcarry[r] + bnd[h][r];
+              tcarry[r] += __shfl(sfx, l & 48, 64);
+              if constexpr (LOGIT) dl[r] *= sigmoid_neg(static_cast<float>(half_of(tx, r)));
+            }
+            if (live) {
+              if constexpr (LOGIT) st8(dxo + off, pack4(dl));
+              else *reinterpret_cast<float4*>(dbo + off) = make_float4(dl[0], dl[1], dl[2], dl[3]);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);   // one tile at a time
+        }
+      }
+    }
+    // the next chunk's values and dO (they fly during the update of G and
+    // the next chunk's prefix)
+    asm volatile("" : "+v"(l), "+v"(m), "+v"(g));
+    if (c > 0) load_vo(c - 1, true);
+    // G_c = 2^r (2^{B - r} G_{c+1} + Qe^T dO): X rows i = 16it + 4g + r, Y columns i = 16 dg + m
+#pragma unroll
+    for (int h = 0; h < GPW; ++h) {
+      const int dg = GPW * w + h;
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const float4 f = *reinterpret_cast<const float4*>(sEBr + 16 * it + 4 * g);
+        X[h][it][0] *= f.x;
+        X[h][it][1] *= f.y;
+        X[h][it][2] *= f.z;
+        X[h][it][3] *= f.w;
+        X[h][it] = mma_rows<T, 64>(X[h][it], sQeT + (16 * it + m) * LDT + 16 * g, sOT + (16 * dg + m) * LDT + 16 * g);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const float f = sEBr[16 * dg + m];
+#pragma unroll
+      for (int jt = 0; jt < 8; ++jt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Y[h][jt][r] *= f;
+        Y[h][jt] = mma_rows<T, 64>(Y[h][jt], sOT + (16 * jt + m) * LDT + 16 * g, sQeT + (16 * dg + m) * LDT + 16 * g);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (cmid) {
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+          const float4 fr = *reinterpret_cast<const float4*>(sRx + 16 * it + 4 * g);
+          X[h][it][0] *= fr.x;
+          X[h][it][1] *= fr.y;
+          X[h][it][2] *= fr.z;
+          X[h][it][3] *= fr.w;
+        }
+        const float fr = sRx[16 * dg + m];
+#pragma unroll
+        for (int jt = 0; jt < 8; ++jt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Y[h][jt][r] *= fr;
+      }
+      // the boundary term of the previous chunk: rowsum(S_c * G_c), row
+      // 16 dg + m over this lane's columns (Y's), summed over the row's lanes
+      float x = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float sv[4];
+        unpack4(Sr[h][e], sv);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x = fmaf(sv[r], Y[h][e][r], x);
+      }
+      x = xgroup_sum(x);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) bnd[h][r] = __shfl(x, 4 * g + r, 64);
+    }
+    __syncthreads();
+  }
+}
+
 // ---------------------------------------------------------------------------
 // 6. dmeta[h][i][d] = sum over batch rows and chunks of the partials (fixed order)
 // ---------------------------------------------------------------------------
@@ -1332,7 +1971,7 @@ __global__ __launch_bounds__(256) void bwd_dmeta_reduce_kernel(const float* part
 namespace {
 
 struct WsPlan {
-  size_t states, dS, dST, Dt, dmu, total;
+  size_t states, dS, dST, Dt, dmu, flag, total;
 };
 
 size_t al256(size_t x) { return (x + 255) / 256 * 256; }
@@ -1346,7 +1985,8 @@ WsPlan plan_ws(int elem, int BH, int L, int D, int n_meta) {
   p.dST = p.dS + st;
   p.Dt = p.dST + st;
   p.dmu = p.Dt + al256((size_t)BH * L * 4);
-  p.total = p.dmu + al256((size_t)BH * nc * n_meta * D * 4);
+  p.flag = p.dmu + al256((size_t)BH * nc * n_meta * D * 4);
+  p.total = p.flag + al256((size_t)BH * nc);
   return p;
 }
 
@@ -1410,40 +2050,76 @@ hipError_t launch_bwd_t(BwdArgs a, hipStream_t st) {
       e = launch_fwd(f, sizeof(T) == 2, D, st);
       if (e != hipSuccess) return e;
     }
-    // 2. state gradients
-    if (a.gate_logit)
-      hipLaunchKernelGGL((bwd_dstate_kernel<T, D, DV, true>), dim3(8 * groups * (D / DV)), dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL((bwd_dstate_kernel<T, D, DV, false>), dim3(8 * groups * (D / DV)), dim3(256), 0, st, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // the reverse walk carries the state gradients itself (bf16, d = 128)
+    constexpr bool WALK = sizeof(T) == 2 && D == 128;
+    if constexpr (!WALK) {
+      // 2. state gradients
+      if (a.gate_logit)
+        hipLaunchKernelGGL((bwd_dstate_kernel<T, D, DV, true>), dim3(8 * groups * (D / DV)), dim3(256), 0, st, a);
+      else
+        hipLaunchKernelGGL((bwd_dstate_kernel<T, D, DV, false>), dim3(8 * groups * (D / DV)), dim3(256), 0, st, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     const int nfull = L / C;
+    if constexpr (WALK) {
+      // 3. the reverse walk (gated parts of dq, dk, dv; dlog_g), then the
+      // chunks it left (none for ordinary gates)
+      const bool logit = a.gate_logit != nullptr;
+      static_assert(WalkLayout::TOTAL <= 160 * 1024, "LDS");
+      const void* wk = logit ? reinterpret_cast<const void*>(&bwd_walk_kernel<true>)
+                             : reinterpret_cast<const void*>(&bwd_walk_kernel<false>);
+      if ((e = hipFuncSetAttribute(wk, hipFuncAttributeMaxDynamicSharedMemorySize, WalkLayout::TOTAL)) != hipSuccess)
+        return e;
+      if (logit)
+        hipLaunchKernelGGL((bwd_walk_kernel<true>), dim3(a.BH), dim3(512), WalkLayout::TOTAL, st, a);
+      else
+        hipLaunchKernelGGL((bwd_walk_kernel<false>), dim3(a.BH), dim3(512), WalkLayout::TOTAL, st, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      typedef GateLayout<T, D> GL;
+      const long long n = (long long)a.BH * nc;
+      const int grid = (int)(n < 256 ? n : 256);
+      if (logit) {
+        if ((e = set_lds(&bwd_gate_flagged_kernel<T, D, true>, GL::TOTAL)) != hipSuccess) return e;
+        hipLaunchKernelGGL((bwd_gate_flagged_kernel<T, D, true>), dim3(grid), dim3(GL::NW * 64), GL::TOTAL, st, a);
+      } else {
+        if ((e = set_lds(&bwd_gate_flagged_kernel<T, D, false>, GL::TOTAL)) != hipSuccess) return e;
+        hipLaunchKernelGGL((bwd_gate_flagged_kernel<T, D, false>), dim3(grid), dim3(GL::NW * 64), GL::TOTAL, st, a);
+      }
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     // 3, 4. anchor, query and key side: the full chunks in one launch each,
-    // a ragged last chunk range-checked in its own
+    // a ragged last chunk range-checked in its own (after the walk: added to
+    // the gated parts; otherwise written alone, the gate kernel adds its own)
+    constexpr bool ACC = WALK;
     typedef AqLayout<T, D> AQ;
     static_assert(AQ::TOTAL <= 53 * 1024, "LDS: three workgroups per CU");
     typedef AkLayout<T, D> AK;
     static_assert(AK::TOTAL <= 80 * 1024, "LDS: two workgroups per CU");
-    if ((e = set_lds(&bwd_anchor_q_kernel<T, D, true>, AQ::TOTAL)) != hipSuccess) return e;
-    if ((e = set_lds(&bwd_anchor_q_kernel<T, D, false>, AQ::TOTAL)) != hipSuccess) return e;
-    if ((e = set_lds(&bwd_anchor_k_kernel<T, D, true>, AK::TOTAL)) != hipSuccess) return e;
-    if ((e = set_lds(&bwd_anchor_k_kernel<T, D, false>, AK::TOTAL)) != hipSuccess) return e;
+    if ((e = set_lds(&bwd_anchor_q_kernel<T, D, true, ACC>, AQ::TOTAL)) != hipSuccess) return e;
+    if ((e = set_lds(&bwd_anchor_q_kernel<T, D, false, ACC>, AQ::TOTAL)) != hipSuccess) return e;
+    if ((e = set_lds(&bwd_anchor_k_kernel<T, D, true, ACC>, AK::TOTAL)) != hipSuccess) return e;
+    if ((e = set_lds(&bwd_anchor_k_kernel<T, D, false, ACC>, AK::TOTAL)) != hipSuccess) return e;
     if (nfull > 0)
-      hipLaunchKernelGGL((bwd_anchor_q_kernel<T, D, false>), dim3(8 * groups * nfull), dim3(256), AQ::TOTAL, st, a, 0,
-                         nfull);
+      hipLaunchKernelGGL((bwd_anchor_q_kernel<T, D, false, ACC>), dim3(8 * groups * nfull), dim3(256), AQ::TOTAL, st, a,
+                         0, nfull);
     if (nfull < nc)
-      hipLaunchKernelGGL((bwd_anchor_q_kernel<T, D, true>), dim3(8 * groups), dim3(256), AQ::TOTAL, st, a, nfull, 1);
+      hipLaunchKernelGGL((bwd_anchor_q_kernel<T, D, true, ACC>), dim3(8 * groups), dim3(256), AQ::TOTAL, st, a, nfull,
+                         1);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (nfull > 0)
-      hipLaunchKernelGGL((bwd_anchor_k_kernel<T, D, false>), dim3(8 * groups * nfull), dim3(256), AK::TOTAL, st, a, 0,
-                         nfull);
+      hipLaunchKernelGGL((bwd_anchor_k_kernel<T, D, false, ACC>), dim3(8 * groups * nfull), dim3(256), AK::TOTAL, st, a,
+                         0, nfull);
     if (nfull < nc)
-      hipLaunchKernelGGL((bwd_anchor_k_kernel<T, D, true>), dim3(8 * groups), dim3(256), AK::TOTAL, st, a, nfull, 1);
+      hipLaunchKernelGGL((bwd_anchor_k_kernel<T, D, true, ACC>), dim3(8 * groups), dim3(256), AK::TOTAL, st, a, nfull,
+                         1);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // 5. gated branch and outputs
-    if (a.gate_logit) {
-      if ((e = launch_gate<T, D, true>(a, nfull, nc, groups, st)) != hipSuccess) return e;
-    } else {
-      if ((e = launch_gate<T, D, false>(a, nfull, nc, groups, st)) != hipSuccess) return e;
+    // 5. gated branch and outputs (the per-chunk kernel)
+    if constexpr (!WALK) {
+      if (a.gate_logit) {
+        if ((e = launch_gate<T, D, true>(a, nfull, nc, groups, st)) != hipSuccess) return e;
+      } else {
+        if ((e = launch_gate<T, D, false>(a, nfull, nc, groups, st)) != hipSuccess) return e;
+      }
     }
   }
   // 6. sink keys (written even when B*L == 0: then zero)
@@ -1478,6 +2154,7 @@ hipError_t launch_bwd(const BwdArgs& in, int dtype_bf16, int D, hipStream_t st) 
     a.ws_dST = base + p.dST;
     a.ws_D = reinterpret_cast<float*>(base + p.Dt);
     a.ws_dmu = reinterpret_cast<float*>(base + p.dmu);
+    a.ws_flag = reinterpret_cast<unsigned char*>(base + p.flag);
   }
   if (dtype_bf16 && D == 128) return launch_bwd_t<bf16, 128, 64>(a, st);
   if (dtype_bf16 && D == 64) return launch_bwd_t<bf16, 64, 64>(a, st);

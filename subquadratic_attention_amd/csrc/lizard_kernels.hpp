@@ -82,6 +82,7 @@ struct BwdArgs {
   void* ws_dST;          // G_{c+1}^T    [BH, nc, D, D] element type
   float* ws_D;           // D_t          [BH, L]
   float* ws_dmu;         // sink-key partials [BH, nc, n_meta, D]
+  unsigned char* ws_flag;   // [BH, nc]: the reverse walk left chunk c to the per-chunk gate kernel
   int B, BH, H, L, n_meta, window;
   float alpha;
   float scale;           // softmax scale (natural units)
