@@ -573,10 +573,13 @@ __global__ __launch_bounds__(256, 3) void bwd_anchor_q_kernel(BwdArgs a, int cb,
   for (int e = 0; e < NS; ++e) sf[e] = M::pack(zsv + e * M::KPL);
   // dq^T[d][t] = scale (K^T dZ^T + mu^T dZs^T)
   T* dqa = reinterpret_cast<T*>(a.dq) + (size_t)bh * L * D;   // the anchor part (ACC: added to the gated part)
-  float prev[ACC ? NDT : 1][4];
+  // (bf16: kept packed, 2 registers per 4 values)
+  typedef typename std::conditional<sizeof(T) == 2, uint2, uint4>::type P4;
+  P4 prev[ACC ? NDT : 1];
   if constexpr (ACC) {
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) load_pack<T, 4>(dqa + (size_t)(tme < L ? tme : 0) * D + 16 * dt + 4 * g, prev[dt]);
+    for (int dt = 0; dt < NDT; ++dt)
+      prev[dt] = *reinterpret_cast<const P4*>(dqa + (size_t)(tme < L ? tme : 0) * D + 16 * dt + 4 * g);
   }
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
@@ -590,8 +593,10 @@ __global__ __launch_bounds__(256, 3) void bwd_anchor_q_kernel(BwdArgs a, int cb,
     if (tme < L) {
       float v4[4] = {o[0] * a.scale, o[1] * a.scale, o[2] * a.scale, o[3] * a.scale};
       if constexpr (ACC) {
+        float pv[4];
+        load_pack<T, 4>(reinterpret_cast<const T*>(&prev[dt]), pv);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v4[r] += prev[dt][r];
+        for (int r = 0; r < 4; ++r) v4[r] += pv[r];
       }
       store_pack<T, 4>(dqa + (size_t)tme * D + 16 * dt + 4 * g, v4);
     }
@@ -743,13 +748,14 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_k_kernel(BwdArgs a, int cb,
   // the anchor parts of dk and dv (ACC: added to the gated parts)
   T* dka = reinterpret_cast<T*>(a.dk) + (size_t)bh * L * D;
   T* dva = reinterpret_cast<T*>(a.dv) + (size_t)bh * L * D;
-  float prevk[ACC ? NDT : 1][4], prevv[ACC ? NDT : 1][4];
+  typedef typename std::conditional<sizeof(T) == 2, uint2, uint4>::type P4;   // 4 values, packed
+  P4 prevk[ACC ? NDT : 1], prevv[ACC ? NDT : 1];
   if constexpr (ACC) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       const size_t o = (size_t)(sme < L ? sme : 0) * D + 16 * dt + 4 * g;
-      load_pack<T, 4>(dka + o, prevk[dt]);
-      load_pack<T, 4>(dva + o, prevv[dt]);
+      prevk[dt] = *reinterpret_cast<const P4*>(dka + o);
+      prevv[dt] = *reinterpret_cast<const P4*>(dva + o);
     }
   }
 #pragma unroll
@@ -766,10 +772,13 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_k_kernel(BwdArgs a, int cb,
       float k4[4] = {ok_[0] * a.scale, ok_[1] * a.scale, ok_[2] * a.scale, ok_[3] * a.scale};
       float v4[4] = {ov[0], ov[1], ov[2], ov[3]};
       if constexpr (ACC) {
+        float pk[4], pv[4];
+        load_pack<T, 4>(reinterpret_cast<const T*>(&prevk[dt]), pk);
+        load_pack<T, 4>(reinterpret_cast<const T*>(&prevv[dt]), pv);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          k4[r] += prevk[dt][r];
-          v4[r] += prevv[dt][r];
+          k4[r] += pk[r];
+          v4[r] += pv[r];
         }
       }
       store_pack<T, 4>(dka + (size_t)sme * D + 16 * dt + 4 * g, k4);
@@ -1327,12 +1336,21 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
 // gridDim.x-th flag (uniform per workgroup), range-checked rows.
 template <typename T, int D, bool LOGIT>
 __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_flagged_kernel(BwdArgs a) {
+  constexpr int NT = D / 16 * 64;
   const int nc = (a.L + C - 1) / C;
   const long long n = (long long)a.BH * nc;
-  for (long long idx = blockIdx.x; idx < n; idx += gridDim.x) {
-    if (a.ws_flag[idx]) {
-      gate_chunk<T, D, true, LOGIT>(a, (int)(idx / nc), (int)(idx % nc));
-      __syncthreads();   // the next chunk's operands overwrite this one's in LDS
+  // the workgroup's flags idx = base + t gridDim.x, one per thread, read
+  // together: the common case (none set) costs one load per thread
+  for (long long base = blockIdx.x; base < n; base += (long long)gridDim.x * NT) {
+    const long long mine = base + (long long)threadIdx.x * gridDim.x;
+    const int f = mine < n ? a.ws_flag[mine] : 0;
+    if (!__syncthreads_or(f)) continue;
+    for (int t = 0; t < NT; ++t) {
+      const long long idx = base + (long long)t * gridDim.x;
+      if (idx < n && a.ws_flag[idx]) {
+        gate_chunk<T, D, true, LOGIT>(a, (int)(idx / nc), (int)(idx % nc));
+        __syncthreads();   // the next chunk's operands overwrite this one's in LDS
+      }
     }
   }
 }
@@ -1428,6 +1446,27 @@ __device__ __forceinline__ bf16 half_of(uint2 u, int r) {
   const uint32_t w = r < 2 ? u.x : u.y;
   return __builtin_bit_cast(bf16, (unsigned short)((r & 1) ? (w >> 16) : (w & 0xffffu)));
 }
+// Inclusive prefix (sum over lanes m' <= m) and suffix (m' >= m) scans over
+// the 16 lanes of a row, on the VALU: DPP row shifts with zero fill.
+template <int N> __device__ __forceinline__ float row_shr(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + N, 0xf, 0xf, true));
+}
+template <int N> __device__ __forceinline__ float row_shl(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x100 + N, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float row_prefix(float x) {
+  x += row_shr<1>(x);
+  x += row_shr<2>(x);
+  x += row_shr<4>(x);
+  return x + row_shr<8>(x);
+}
+__device__ __forceinline__ float row_suffix(float x) {
+  x += row_shl<1>(x);
+  x += row_shl<2>(x);
+  x += row_shl<4>(x);
+  return x + row_shl<8>(x);
+}
+
 __device__ __forceinline__ bf16x8 frag2(uint2 a, uint2 b) {
   return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
 }
@@ -1592,8 +1631,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
       for (int x = 0; x < 8; ++x) Sr[h][x] = ld8(sp + 16 * x);
     }
-    if (c > 0) load_qkg(c - 1, true);
-
     // log2-gate prefix: a scan over the 16 lanes of each row (the tile's
     // tokens), then the earlier tiles' totals
     float beta[GPW][4][4], Bt[GPW][4], rr[GPW][4];
@@ -1605,12 +1642,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
       for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float x = log2_gate(lgv[h][tt][r]);
-#pragma unroll
-          for (int o = 1; o < 16; o <<= 1) {
-            const float y = __shfl_up(x, o, 16);
-            x += m >= o ? y : 0.f;
-          }
+          const float x = row_prefix(log2_gate(lgv[h][tt][r]));
           beta[h][tt][r] = x + run[r];
           run[r] += __shfl(x, (l & 48) | 15, 64);
         }
@@ -1748,6 +1780,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
     __syncthreads();
 
     // ================= step 3: outputs of the chunk, then G ================
+    // G_{c+1} with each row i scaled by 2^{B_i - r_i}: the first half of
+    // the update of G, and the factor the inter-chunk terms need
+    // (2^{B - beta} G v = 2^{-b} (2^{B - r} G) v; G^T Kh = (2^{B - r} G)^T Kp)
+#pragma unroll
+    for (int h = 0; h < GPW; ++h) {
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const float4 f = *reinterpret_cast<const float4*>(sEBr + 16 * it + 4 * g);
+        X[h][it][0] *= f.x;
+        X[h][it][1] *= f.y;
+        X[h][it][2] *= f.z;
+        X[h][it][3] *= f.w;
+      }
+      const float f = sEBr[16 * (GPW * w + h) + m];
+#pragma unroll
+      for (int jt = 0; jt < 8; ++jt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Y[h][jt][r] *= f;
+    }
     if (!cwide) {
 #pragma unroll
       for (int h = 0; h < GPW; ++h) {
@@ -1761,15 +1812,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
           const int t = t0 + row;
           const bool live = full || t < L;
           const size_t off = (size_t)(live ? t : 0) * D + i0;
-          // this tile's raw q, k (and gate logits) again, for dlog_g at the
-          // end of the tile (cache hits: step 1 read them; holding them in
-          // registers across the steps would cost 16 more)
-          uint2 tq = ld8(qg + off), tk = ld8(kg + off), tx = make_uint2(0u, 0u);
-          if constexpr (LOGIT) tx = ld8(xg + off);
-          if (!full && !live) {
-            tq = make_uint2(0u, 0u);
-            tk = make_uint2(0u, 0u);
-          }
+
           const T* orow = sO + row * LDR + 4 * g;
           const T* vrow = sV + row * LDR + 4 * g;
           const T* krow = sKp + row * LDR + 4 * g;
@@ -1804,12 +1847,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               ki = M::mma(frag2(Y[h][2 * e], Y[h][2 * e + 1]),
-                          frag2(ld8(vrow + 32 * e), ld8(vrow + 32 * e + 16)), ki);   // (G v_s)_i
+                          frag2(ld8(vrow + 32 * e), ld8(vrow + 32 * e + 16)), ki);   // (2^{B - r} G v_s)_i
             const f32x4 ka = mma_rows<T, 64>(zero4(), sQeT + (16 * dg + m) * LDT + 16 * g, sDAT + row * LDT + 16 * g);
-            const float4 ebr = *reinterpret_cast<const float4*>(sEBr + i0);   // 2^{B - r}
-            const float eBr[4] = {ebr.x, ebr.y, ebr.z, ebr.w};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dkg[r] = ik[r] * fmaf(eBr[r], ki[r], ka[r]);
+            for (int r = 0; r < 4; ++r) dkg[r] = ik[r] * (ki[r] + ka[r]);
             if (live) st8(dko + off, pack4(dkg));
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -1817,24 +1858,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
           {
             f32x4 vi = zero4();
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int o1 = 32 * e, o2 = 32 * e + 16;
-              // Kh_s = Kp_s 2^{B - r} in the gathered dim order
-              float kv[8];
-              unpack4(ld8(krow + o1), kv);
-              unpack4(ld8(krow + o2), kv + 4);
-              const float4 f1 = *reinterpret_cast<const float4*>(sEBr + o1 + 4 * g);
-              const float4 f2 = *reinterpret_cast<const float4*>(sEBr + o2 + 4 * g);
-              kv[0] *= f1.x;
-              kv[1] *= f1.y;
-              kv[2] *= f1.z;
-              kv[3] *= f1.w;
-              kv[4] *= f2.x;
-              kv[5] *= f2.y;
-              kv[6] *= f2.z;
-              kv[7] *= f2.w;
-              vi = M::mma(frag2(X[h][2 * e], X[h][2 * e + 1]), M::pack(kv), vi);   // (G^T Kh_s)_j
-            }
+            for (int e = 0; e < 4; ++e)
+              vi = M::mma(frag2(X[h][2 * e], X[h][2 * e + 1]),
+                          frag2(ld8(krow + 32 * e), ld8(krow + 32 * e + 16)), vi);   // ((2^{B - r} G)^T Kp_s)_j
             const f32x4 va = mma_rows<T, 64>(zero4(), sOT + (16 * dg + m) * LDT + 16 * g, sAT + row * LDT + 16 * g);
             float dv4[4];
 #pragma unroll
@@ -1846,19 +1872,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
           // later tiles, and everything after the chunk
           {
             float qf[4], kf[4], dl[4];
-            unpack4(tq, qf);
-            unpack4(tk, kf);
+            unpack4(cq[h][tt], qf);
+            unpack4(ck[h][tt], kf);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              float sfx = qf[r] * dqg[r] - kf[r] * dkg[r];
-#pragma unroll
-              for (int o = 1; o < 16; o <<= 1) {
-                const float y = __shfl_down(sfx, o, 16);
-                sfx += m + o < 16 ? y : 0.f;
-              }
+              const float sfx = row_suffix(qf[r] * dqg[r] - kf[r] * dkg[r]);
               dl[r] = sfx + tcarry[r] + bnd[h][r];
               tcarry[r] += __shfl(sfx, l & 48, 64);
-              if constexpr (LOGIT) dl[r] *= sigmoid_neg(static_cast<float>(half_of(tx, r)));
+              if constexpr (LOGIT) dl[r] *= sigmoid_neg(static_cast<float>(half_of(cx[h][tt], r)));
             }
             if (live) {
               if constexpr (LOGIT) st8(dxo + off, pack4(dl));
@@ -1869,29 +1890,26 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
         }
       }
     }
-    // the next chunk's values and dO (they fly during the update of G and
-    // the next chunk's prefix)
+    // the next chunk's rows (they fly during the update of G and the next
+    // chunk's prefix; issued after every load of this chunk, whose waits
+    // would otherwise include them)
     asm volatile("" : "+v"(l), "+v"(m), "+v"(g));
-    if (c > 0) load_vo(c - 1, true);
-    // G_c = 2^r (2^{B - r} G_{c+1} + Qe^T dO): X rows i = 16it + 4g + r, Y columns i = 16 dg + m
+    if (c > 0) {
+      load_qkg(c - 1, true);
+      load_vo(c - 1, true);
+    }
+    // G_c = 2^r (2^{B - r} G_{c+1} + Qe^T dO) (the rows already scaled above):
+    // X rows i = 16it + 4g + r, Y columns i = 16 dg + m
 #pragma unroll
     for (int h = 0; h < GPW; ++h) {
       const int dg = GPW * w + h;
 #pragma unroll
       for (int it = 0; it < 8; ++it) {
-        const float4 f = *reinterpret_cast<const float4*>(sEBr + 16 * it + 4 * g);
-        X[h][it][0] *= f.x;
-        X[h][it][1] *= f.y;
-        X[h][it][2] *= f.z;
-        X[h][it][3] *= f.w;
         X[h][it] = mma_rows<T, 64>(X[h][it], sQeT + (16 * it + m) * LDT + 16 * g, sOT + (16 * dg + m) * LDT + 16 * g);
         __builtin_amdgcn_sched_barrier(0);
       }
-      const float f = sEBr[16 * dg + m];
 #pragma unroll
       for (int jt = 0; jt < 8; ++jt) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Y[h][jt][r] *= f;
         Y[h][jt] = mma_rows<T, 64>(Y[h][jt], sOT + (16 * jt + m) * LDT + 16 * g, sQeT + (16 * dg + m) * LDT + 16 * g);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -2076,8 +2094,11 @@ hipError_t launch_bwd_t(BwdArgs a, hipStream_t st) {
         hipLaunchKernelGGL((bwd_walk_kernel<false>), dim3(a.BH), dim3(512), WalkLayout::TOTAL, st, a);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       typedef GateLayout<T, D> GL;
+      // one flag per thread: enough workgroups to read every flag at once
+      // (the common case, no chunk flagged, then ends after one load)
       const long long n = (long long)a.BH * nc;
-      const int grid = (int)(n < 256 ? n : 256);
+      const long long need = (n + GL::NW * 64 - 1) / (GL::NW * 64);
+      const int grid = (int)(need < 256 ? need : 256);
       if (logit) {
         if ((e = set_lds(&bwd_gate_flagged_kernel<T, D, true>, GL::TOTAL)) != hipSuccess) return e;
         hipLaunchKernelGGL((bwd_gate_flagged_kernel<T, D, true>), dim3(grid), dim3(GL::NW * 64), GL::TOTAL, st, a);
