@@ -443,7 +443,7 @@ struct AqLayout {
 // ACC: add the anchor part to what dq holds (the gated part, written before by
 // the reverse walk) instead of writing it alone.
 template <typename T, int D, bool GUARD, bool ACC = false>
-__global__ __launch_bounds__(256, 3) void bwd_anchor_q_kernel(BwdArgs a, int cb, int ncl) {
+__global__ __launch_bounds__(256, 2) void bwd_anchor_q_kernel(BwdArgs a, int cb, int ncl) {
   typedef AqLayout<T, D> Lay;
   typedef Mfma<T> M;
   typedef typename M::frag frag;
@@ -476,7 +476,7 @@ __global__ __launch_bounds__(256, 3) void bwd_anchor_q_kernel(BwdArgs a, int cb,
   const int U0 = 16 * I;                  // first window key of the tiles (of [t0 - 64, t0 + 64))
   // this lane's query and dY row, and the window keys / values of its
   // first three tiles, issued before the staging (their loads then overlap
-  // it); the other three tiles reuse the registers (three workgroups per CU)
+  // it); the other tiles reuse the registers
   uint4 qraw[QV], dyraw[QV];
   load_quarter<T, D, GUARD>(qraw, qg, tme, L, g);
   load_quarter<T, D, GUARD>(dyraw, dyg, tme, L, g);
@@ -498,11 +498,28 @@ __global__ __launch_bounds__(256, 3) void bwd_anchor_q_kernel(BwdArgs a, int cb,
   const float lse2 = !GUARD || tme < L ? a.lse[(size_t)bh * L + (tme < L ? tme : 0)] * kLog2e : 0.f;
 
   // window keys [t0 - 64, t0 + 64) transposed; sink keys transposed
-  stage_T<T, D, D, 128>(sKT, Lay::LDKT, kg, t0 - 64, 0, L, 1.0f);
-  for (int i = tid; i < D * 32; i += 256) {
-    const int d = i / 32, s = i % 32;
-    sMuT[d * Lay::LDMT + s] = s < a.n_meta ? mug[(size_t)(s < a.n_meta ? s : 0) * D + d] : from_f32<T>(0.f);
+  // (the sink rows, slots 0 .. 15 of the tile, the ones the products read:
+  // one 16-byte run of one sink per item, every load issued before the
+  // first store, so the whole tile waits for one round trip)
+  constexpr int MPI = 16 / sizeof(T);             // values per item
+  constexpr int MIT = 16 * D / MPI;               // items: 16 sink slots x D / MPI runs
+  constexpr int MPT = (MIT + 255) / 256;          // items per thread
+  uint4 mv[MPT];
+#pragma unroll
+  for (int p = 0; p < MPT; ++p) {
+    const int it = tid + 256 * p, s = it / (D / MPI), j = it % (D / MPI);
+    mv[p] = it < MIT && s < a.n_meta ? ld16(mug + (size_t)s * D + MPI * j) : make_uint4(0u, 0u, 0u, 0u);
   }
+#pragma unroll
+  for (int p = 0; p < MPT; ++p) {
+    const int it = tid + 256 * p, s = it / (D / MPI), j = it % (D / MPI);
+    const T* pv = reinterpret_cast<const T*>(&mv[p]);
+    if (it < MIT) {
+#pragma unroll
+      for (int e = 0; e < MPI; ++e) sMuT[(MPI * j + e) * Lay::LDMT + s] = pv[e];
+    }
+  }
+  stage_T<T, D, D, 128>(sKT, Lay::LDKT, kg, t0 - 64, 0, L, 1.0f);
   __syncthreads();
 
   // logits Z^T[u][t] and value products dP^T[u][t] for window keys u
@@ -685,20 +702,10 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_k_kernel(BwdArgs a, int cb,
   load_quarter<T, D, GUARD>(kraw, kg, sme, L, g);
   load_quarter<T, D, GUARD>(vraw, vg, sme, L, g);
 
-  // queries [t0, t0 + 128): transposed q and dY, lse (log2 units) and D_t
-  stage_T<T, D, D, 128>(sQT, Lay::LDT, qg, t0, 0, L, 1.0f);
-  stage_T<T, D, D, 128>(sdYT, Lay::LDT, dyg, t0, 0, L, 1.0f);
-  if (tid < 128) {
-    const int t = t0 + tid;
-    sLse[tid] = t < L ? a.lse[(size_t)bh * L + t] * kLog2e : 0.f;
-    sD[tid] = t < L ? a.ws_D[(size_t)bh * L + t] : 0.f;
-  }
-  __syncthreads();
-
-  // Z[t][s] and dP[t][s] tiles: queries t on the MFMA rows; each tile's
-  // query and dY rows are loaded one tile ahead
-  f32x4 z[kWinTiles], dp[kWinTiles];
-  uint4 qraw[2][QV], dyraw[2][QV];
+  // the first query tiles (queries on the MFMA rows; each tile's q and dY
+  // rows are loaded NB - 1 tiles ahead: two for 16-bit values, one for fp32)
+  constexpr int NB = sizeof(T) == 2 ? 3 : 2;
+  uint4 qraw[NB][QV], dyraw[NB][QV];
   auto load_query = [&](uint4* qr, uint4* dr, int t) __attribute__((always_inline)) {
     if constexpr (GUARD) {
       load_quarter<T, D>(qr, qg, t, L, g);
@@ -708,15 +715,42 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_k_kernel(BwdArgs a, int cb,
       load_quarter_clamped<T, D>(dr, dyg, t, L, g);
     }
   };
-  load_query(qraw[0], dyraw[0], t0 + Q0 + m);
+#pragma unroll
+  for (int kt = 0; kt < NB - 1; ++kt) load_query(qraw[kt], dyraw[kt], t0 + Q0 + 16 * kt + m);
+  // queries [t0, t0 + 128): transposed q and dY, lse (log2 units) and D_t;
+  // every load issued before the first store
+  {
+    uint32_t wq[StageT<T, D, 128>::RPT], wy[StageT<T, D, 128>::RPT];
+    stage_T_load<T, D, D, 128>(wq, qg, t0, 0, L);
+    stage_T_load<T, D, D, 128>(wy, dyg, t0, 0, L);
+    float lse_t = 0.f, d_t = 0.f;
+    if (tid < 128) {
+      const int t = t0 + tid;
+      if (t < L) {
+        lse_t = a.lse[(size_t)bh * L + t] * kLog2e;
+        d_t = a.ws_D[(size_t)bh * L + t];
+      }
+    }
+    stage_T_store<T, D, 128>(sQT, Lay::LDT, wq, 1.0f);
+    stage_T_store<T, D, 128>(sdYT, Lay::LDT, wy, 1.0f);
+    if (tid < 128) {
+      sLse[tid] = lse_t;
+      sD[tid] = d_t;
+    }
+  }
+  __syncthreads();
+
+  // Z[t][s] and dP[t][s] tiles
+  f32x4 z[kWinTiles], dp[kWinTiles];
 #pragma unroll
   for (int kt = 0; kt < kWinTiles; ++kt) {
-    if (kt + 1 < kWinTiles) load_query(qraw[(kt + 1) & 1], dyraw[(kt + 1) & 1], t0 + Q0 + 16 * (kt + 1) + m);
+    if (kt + NB - 1 < kWinTiles)
+      load_query(qraw[(kt + NB - 1) % NB], dyraw[(kt + NB - 1) % NB], t0 + Q0 + 16 * (kt + NB - 1) + m);
     f32x4 zc = zero4(), pc = zero4();
 #pragma unroll
     for (int e = 0; e < NF; ++e) {
-      zc = M::mma(frag_of<T>(qraw[kt & 1], e), frag_of<T>(kraw, e), zc);
-      pc = M::mma(frag_of<T>(dyraw[kt & 1], e), frag_of<T>(vraw, e), pc);
+      zc = M::mma(frag_of<T>(qraw[kt % NB], e), frag_of<T>(kraw, e), zc);
+      pc = M::mma(frag_of<T>(dyraw[kt % NB], e), frag_of<T>(vraw, e), pc);
     }
     z[kt] = zc;
     dp[kt] = pc;
@@ -2113,7 +2147,7 @@ hipError_t launch_bwd_t(BwdArgs a, hipStream_t st) {
     // the gated parts; otherwise written alone, the gate kernel adds its own)
     constexpr bool ACC = WALK;
     typedef AqLayout<T, D> AQ;
-    static_assert(AQ::TOTAL <= 53 * 1024, "LDS: three workgroups per CU");
+    static_assert(AQ::TOTAL <= 80 * 1024, "LDS: two workgroups per CU");
     typedef AkLayout<T, D> AK;
     static_assert(AK::TOTAL <= 80 * 1024, "LDS: two workgroups per CU");
     if ((e = set_lds(&bwd_anchor_q_kernel<T, D, true, ACC>, AQ::TOTAL)) != hipSuccess) return e;
