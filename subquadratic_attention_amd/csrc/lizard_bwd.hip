@@ -1434,9 +1434,12 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_flagged_kernel(BwdArg
 // 2^r (2^{B - r} G + Qe^T dO)).
 struct WalkLayout {
   static constexpr int D = 128;
-  static constexpr int LDR = D + 8;    // row-major token tiles [64][LDR]
-  static constexpr int LDT = 64 + 8;   // transposed tiles [D][LDT]; score tiles [64][LDT]
-  static constexpr int ROWS = 64 * LDR * 2, TRANS = D * LDT * 2, SCORE = 64 * LDT * 2;
+  // row-major token tiles [64][LDR]: rows of 264 bytes, whose 8-byte reads
+  // (16 rows at a time, two runs 32 bytes apart) spread over the banks
+  // (272-byte rows would not); they are then 8-byte aligned only
+  static constexpr int LDR = D + 4;
+  // transposed tiles [D][64] and score tiles [64][64], fragment-major (fm)
+  static constexpr int ROWS = 64 * LDR * 2, TRANS = D * 64 * 2, SCORE = 64 * 64 * 2;
   static constexpr int OFF_QE = 0;                   // Qe[t][i]
   static constexpr int OFF_KP = OFF_QE + ROWS;       // Kp[s][i]
   static constexpr int OFF_O = OFF_KP + ROWS;        // dO[t][j]
@@ -1513,13 +1516,38 @@ __device__ __forceinline__ bf16x8 frag2(f32x4 a, f32x4 b) {
   }
   return f;
 }
+// Element offset of (row, col) in a fragment-major [rows][64] tile: the run
+// of eight values (row, 8c .. 8c + 7) sits at ((row / 16) * 8 + c) * 128 +
+// (row % 16) * 8, so the 16 rows of a row tile read their runs of one column
+// block from 256 contiguous bytes (no two lanes of a 16-lane group on one
+// bank, where a padded row-major tile would put two).
+__device__ __forceinline__ int fm(int row, int col) {
+  return (((row >> 4) << 3) + (col >> 3)) * 128 + (row & 15) * 8 + (col & 7);
+}
+// A K = 64 product of row ra of fragment-major tile A and row rb of B (the
+// lane's rows): lane group g takes values 16g .. 16g + 15 of both.
+__device__ __forceinline__ f32x4 mma_fm(f32x4 c, const bf16* A, int ra, const bf16* B, int rb, int g) {
+  typedef Mfma<bf16> M;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) c = M::mma(M::load(A + fm(ra, 16 * g + 8 * e)), M::load(B + fm(rb, 16 * g + 8 * e)), c);
+  return c;
+}
+// A K = 128 product over two row-major tiles whose rows are 8-byte aligned
+// (not 16): each step's eight values of the lane's quarter come as two 8-byte
+// reads.
+__device__ __forceinline__ f32x4 mma_rows8(f32x4 c, const bf16* a, const bf16* b) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    c = Mfma<bf16>::mma(frag2(ld8(a + 8 * e), ld8(a + 8 * e + 4)), frag2(ld8(b + 8 * e), ld8(b + 8 * e + 4)), c);
+  return c;
+}
 
 template <bool LOGIT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void bwd_walk_kernel(BwdArgs a) {
   typedef WalkLayout Lay;
   typedef bf16 T;
   typedef Mfma<T> M;
-  constexpr int D = Lay::D, LDR = Lay::LDR, LDT = Lay::LDT;
+  constexpr int D = Lay::D, LDR = Lay::LDR;
   constexpr int NW = 8;       // wavefronts
   constexpr int GPW = 1;      // 16-dim groups per wavefront
   extern __shared__ __align__(16) unsigned char smem[];
@@ -1722,8 +1750,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
         st8(sKp + row * LDR + i0, kp4);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          sQeT[(i0 + r) * LDT + row] = half_of(qe4, r);
-          sKpT[(i0 + r) * LDT + row] = half_of(kp4, r);
+          sQeT[fm(i0 + r, row)] = half_of(qe4, r);
+          sKpT[fm(i0 + r, row)] = half_of(kp4, r);
         }
       }
       if (m == 0) {
@@ -1741,7 +1769,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
         st8(sO + row * LDR + i0, po[h][tt]);
         st8(sV + row * LDR + i0, pv[h][tt]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sOT[(i0 + r) * LDT + row] = half_of(po[h][tt], r);
+        for (int r = 0; r < 4; ++r) sOT[fm(i0 + r, row)] = half_of(po[h][tt], r);
       }
     }
     {
@@ -1767,21 +1795,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
         const int J = tl - I * (I + 1) / 2;
         if (j < 10) {
           // A[t][s] = Qe_t . Kp_s: rows t = 16I + 4g + r, column s = 16J + m -> A^T[s][t..t+3]
-          const f32x4 v = mma_rows<T, D>(zero4(), sQe + (16 * I + m) * LDR + 32 * g, sKp + (16 * J + m) * LDR + 32 * g);
+          const f32x4 v = mma_rows8(zero4(), sQe + (16 * I + m) * LDR + 32 * g, sKp + (16 * J + m) * LDR + 32 * g);
           float a4[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) a4[r] = (16 * J + m <= 16 * I + 4 * g + r) ? v[r] : 0.f;
-          st8(sAT + (16 * J + m) * LDT + 16 * I + 4 * g, pack4(a4));
+          st8(sAT + fm(16 * J + m, 16 * I + 4 * g), pack4(a4));
         } else {
           // dA[t][s] = dO_t . v_s: rows s = 16J + 4g + r, column t = 16I + m -> dA[t][s..s+3] and dA^T
-          const f32x4 v = mma_rows<T, D>(zero4(), sV + (16 * J + m) * LDR + 32 * g, sO + (16 * I + m) * LDR + 32 * g);
+          const f32x4 v = mma_rows8(zero4(), sV + (16 * J + m) * LDR + 32 * g, sO + (16 * I + m) * LDR + 32 * g);
           float a4[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) a4[r] = (16 * J + 4 * g + r <= 16 * I + m) ? v[r] : 0.f;
           const uint2 p4 = pack4(a4);
-          st8(sDA + (16 * I + m) * LDT + 16 * J + 4 * g, p4);
+          st8(sDA + fm(16 * I + m, 16 * J + 4 * g), p4);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sDAT[(16 * J + 4 * g + r) * LDT + 16 * I + m] = half_of(p4, r);
+          for (int r = 0; r < 4; ++r) sDAT[fm(16 * J + 4 * g + r, 16 * I + m)] = half_of(p4, r);
         }
       }
     } else {
@@ -1866,7 +1894,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
             for (int e = 0; e < 4; ++e)
               qi = M::mma(frag2(Sr[h][2 * e], Sr[h][2 * e + 1]),
                           frag2(ld8(orow + 32 * e), ld8(orow + 32 * e + 16)), qi);   // (S dO_t)_i
-            const f32x4 qa = mma_rows<T, 64>(zero4(), sKpT + (16 * dg + m) * LDT + 16 * g, sDA + row * LDT + 16 * g);
+            const f32x4 qa = mma_fm(zero4(), sKpT, 16 * dg + m, sDA, row, g);
             const float4 rx = *reinterpret_cast<const float4*>(sRx + i0);     // 2^r
             const float rxv[4] = {rx.x, rx.y, rx.z, rx.w};
 #pragma unroll
@@ -1882,7 +1910,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
             for (int e = 0; e < 4; ++e)
               ki = M::mma(frag2(Y[h][2 * e], Y[h][2 * e + 1]),
                           frag2(ld8(vrow + 32 * e), ld8(vrow + 32 * e + 16)), ki);   // (2^{B - r} G v_s)_i
-            const f32x4 ka = mma_rows<T, 64>(zero4(), sQeT + (16 * dg + m) * LDT + 16 * g, sDAT + row * LDT + 16 * g);
+            const f32x4 ka = mma_fm(zero4(), sQeT, 16 * dg + m, sDAT, row, g);
 #pragma unroll
             for (int r = 0; r < 4; ++r) dkg[r] = ik[r] * (ki[r] + ka[r]);
             if (live) st8(dko + off, pack4(dkg));
@@ -1895,7 +1923,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
             for (int e = 0; e < 4; ++e)
               vi = M::mma(frag2(X[h][2 * e], X[h][2 * e + 1]),
                           frag2(ld8(krow + 32 * e), ld8(krow + 32 * e + 16)), vi);   // ((2^{B - r} G)^T Kp_s)_j
-            const f32x4 va = mma_rows<T, 64>(zero4(), sOT + (16 * dg + m) * LDT + 16 * g, sAT + row * LDT + 16 * g);
+            const f32x4 va = mma_fm(zero4(), sOT, 16 * dg + m, sAT, row, g);
             float dv4[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) dv4[r] = vi[r] + va[r];
@@ -1939,12 +1967,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
       const int dg = GPW * w + h;
 #pragma unroll
       for (int it = 0; it < 8; ++it) {
-        X[h][it] = mma_rows<T, 64>(X[h][it], sQeT + (16 * it + m) * LDT + 16 * g, sOT + (16 * dg + m) * LDT + 16 * g);
+        X[h][it] = mma_fm(X[h][it], sQeT, 16 * it + m, sOT, 16 * dg + m, g);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int jt = 0; jt < 8; ++jt) {
-        Y[h][jt] = mma_rows<T, 64>(Y[h][jt], sOT + (16 * jt + m) * LDT + 16 * g, sQeT + (16 * dg + m) * LDT + 16 * g);
+        Y[h][jt] = mma_fm(Y[h][jt], sOT, 16 * jt + m, sQeT, 16 * dg + m, g);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (cmid) {
