@@ -104,7 +104,18 @@ typedef struct {
  *                               the backward pass)
  *   y_anchor    [B, H, L, dv]   dtype, out, nullable: the anchor branch alone
  *   state_out   [B, H, dk, dv]  float32, out, nullable: S_{L-1}, the state a
- *                               decode continuation starts from             */
+ *                               decode continuation starts from
+ * Schedule: where too few heads are given to fill the GPU with one
+ * workgroup per (head, value slice) and the sequences are long (the cases
+ * in which lizard_attn_fwd_split_workspace_size(p) > 0, e.g. B*H = 32 at
+ * L = 32K), the call runs lizard_attn_fwd_split's segment schedule, with a
+ * workspace of that size taken from HIP's stream-ordered allocator on
+ * `stream` and returned to it after the call's kernels (hipMallocAsync /
+ * hipFreeAsync); its results are then lizard_attn_fwd_split's, equal to
+ * the one-pass results up to float rounding.  If that allocation fails it
+ * runs the one-pass schedule.  lizard_attn_fwd_logit and
+ * lizard_attn_fwd_continue do the same; lizard_attn_fwd_train never
+ * splits. */
 lizard_status_t lizard_attn_fwd(const lizard_params_t* p,
                                 const void* q, const void* k, const void* v,
                                 const float* log_g, const void* meta_k,

@@ -83,12 +83,14 @@ lizard_status_t attn_fwd(const lizard_params_t* p, const void* q, const void* k,
                          const void* k_halo, const void* v_halo, int32_t halo_len, void* y, float* lse,
                          void* y_anchor, float* state_out, void* stream, bool split = false,
                          void* workspace = nullptr, size_t workspace_bytes = 0, void* chunk_states = nullptr,
-                         bool fixed_scratch = false) {
+                         bool fixed_scratch = false, bool auto_split = false) {
   lizard_status_t s = check_params(p, true);
   if (s != LIZARD_OK) return s;
   if (halo_len < 0 || halo_len > p->window - 1) return LIZARD_E_SHAPE;
-  const int nseg = split ? split_segments(p) : 1;
-  if (fixed_scratch) {
+  int nseg = split || auto_split ? split_segments(p) : 1;
+  if (auto_split) {
+    // the workspace is taken from the stream-ordered allocator below
+  } else if (fixed_scratch) {
     // the workspace comes from the library's fixed scratch (checked here,
     // taken after every other check)
     if (split_workspace(p, nseg) > (size_t)LIZARD_NOALLOC_SCRATCH_BYTES) return LIZARD_E_WORKSPACE;
@@ -111,6 +113,17 @@ lizard_status_t attn_fwd(const lizard_params_t* p, const void* q, const void* k,
   if (fixed_scratch && nseg > 1) {
     workspace = scratch_ptr();
     if (workspace == nullptr) return LIZARD_E_LAUNCH;
+  }
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  bool owned = false;   // a workspace of this call, freed after its kernels (stream order)
+  if (auto_split && nseg > 1) {
+    if (hipMallocAsync(&workspace, split_workspace(p, nseg), hs) == hipSuccess && workspace != nullptr) {
+      owned = true;
+    } else {
+      (void)hipGetLastError();   // clear the failed allocation; the one-pass schedule needs no workspace
+      workspace = nullptr;
+      nseg = 1;
+    }
   }
   const int bf = p->dtype == LIZARD_BF16;
   const int DV = lizard::fwd_value_slice(bf, p->dk);
@@ -149,7 +162,9 @@ lizard_status_t attn_fwd(const lizard_params_t* p, const void* q, const void* k,
     a.seg_in_t = w + off[2];
     a.seg_live = reinterpret_cast<int*>(w + off[3]);
   }
-  return launched(lizard::launch_fwd(a, bf, p->dk, static_cast<hipStream_t>(stream)));
+  const hipError_t e = lizard::launch_fwd(a, bf, p->dk, hs);
+  if (owned) (void)hipFreeAsync(workspace, hs);
+  return launched(e);
 }
 
 // The backward pass; with logits, dgate (element type) replaces dlog_g.
@@ -252,14 +267,14 @@ LIZARD_API lizard_status_t lizard_attn_fwd(const lizard_params_t* p, const void*
                                            const float* log_g, const void* meta_k, void* y, float* lse,
                                            void* y_anchor, float* state_out, void* stream) {
   return attn_fwd(p, q, k, v, log_g, nullptr, false, meta_k, nullptr, nullptr, nullptr, 0, y, lse, y_anchor, state_out,
-                  stream);
+                  stream, false, nullptr, 0, nullptr, false, true);
 }
 
 LIZARD_API lizard_status_t lizard_attn_fwd_logit(const lizard_params_t* p, const void* q, const void* k,
                                                  const void* v, const void* gate_logit, const void* meta_k, void* y,
                                                  float* lse, void* y_anchor, float* state_out, void* stream) {
   return attn_fwd(p, q, k, v, nullptr, gate_logit, true, meta_k, nullptr, nullptr, nullptr, 0, y, lse, y_anchor,
-                  state_out, stream);
+                  state_out, stream, false, nullptr, 0, nullptr, false, true);
 }
 
 LIZARD_API lizard_status_t lizard_attn_fwd_continue(const lizard_params_t* p, const void* q, const void* k,
@@ -269,7 +284,7 @@ LIZARD_API lizard_status_t lizard_attn_fwd_continue(const lizard_params_t* p, co
                                                     void* y_anchor, float* state_out, void* stream) {
   if (log_g != nullptr && gate_logit != nullptr) return LIZARD_E_SHAPE;
   return attn_fwd(p, q, k, v, log_g, gate_logit, gate_logit != nullptr, meta_k, state_in, k_halo, v_halo, halo_len, y,
-                  lse, y_anchor, state_out, stream);
+                  lse, y_anchor, state_out, stream, false, nullptr, 0, nullptr, false, true);
 }
 
 LIZARD_API size_t lizard_attn_fwd_split_workspace_size(const lizard_params_t* p) {

@@ -149,3 +149,32 @@ def test_split_full_size_long_context_sampled(gpu_lib):
         errs = [assert_close(down(out[key][0, h]), o[key][0], w.dtype, f"split 32k {key}[0,{h}]")
                 for key in ("y", "y_anchor", "lse", "state")]
         log(f"split 32k head {h}: " + " ".join(f"{e:.2e}" for e in errs))
+
+
+@pytest.mark.parametrize("entry", ["fwd", "fwd_logit", "fwd_continue"])
+def test_named_calls_take_the_split_schedule(gpu_lib, entry):
+    """Where a split pays, lizard_attn_fwd (and its logit and continued forms)
+    runs the split schedule itself, with a workspace of its own: its results
+    are lizard_attn_fwd_split's, bit for bit (the same kernels on the same
+    segments), and so the oracle's to the split's tolerance."""
+    import torch
+
+    dtype, d, B, H, L, w = "bf16", 128, 1, 2, 2011, 64
+    assert _segments(gpu_lib, B, H, L, d, dtype) > 0, "this shape must be split"
+    x = si.custom_inputs(44, B, H, L, d, 4, dtype, **GATES["slow"])
+    logit = entry == "fwd_logit"
+    tag = f"named call {entry} {dtype} d={d} L={L}"
+    log(tag)
+    a = _run_split(gpu_lib, x, dtype, w, 0.5, logit)
+    q, k, v, meta = up(x["q"], dtype), up(x["k"], dtype), up(x["v"], dtype), up(x["meta_k"], dtype)
+    kw = dict(window=w, alpha=0.5, need_lse=True, need_y_anchor=True, need_state=True)
+    if entry == "fwd":
+        b = gpu_lib.lizard_attn_fwd(q, k, v, up_f32(x["log_g"]), meta, **kw)
+    elif entry == "fwd_logit":
+        b = gpu_lib.lizard_attn_fwd_logit(q, k, v, up(x["gate_logit"], dtype), meta, **kw)
+    else:
+        b = gpu_lib.lizard_attn_fwd_continue(q, k, v, meta, log_g=up_f32(x["log_g"]), **kw)
+    torch.cuda.synchronize()
+    for key in ("y", "y_anchor", "lse", "state"):
+        assert np.array_equal(a[key], down(b[key])), key
+    _compare({kk: down(vv) for kk, vv in b.items()}, _ref(x, w, 0.5, logit), dtype, tag)
