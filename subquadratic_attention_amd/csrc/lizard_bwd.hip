@@ -419,6 +419,26 @@ __device__ __forceinline__ typename Mfma<T>::frag sink_frag(const T* p, int g, i
   }
 }
 
+// Transposing LDS read (bf16): within each 16-lane group, lane j reads the
+// 8 bytes at its address and receives, in slot k, value j % 4 of the 8 bytes
+// lane 4k + j / 4 of its group read.  So if lane j reads row r0 + j / 4,
+// columns c0 + 4 (j % 4) .. + 3 of a row-major tile X, lane j receives
+// X[r0 .. r0 + 3][c0 + j]: four consecutive k of column j, as an MFMA
+// operand wants them from a tile stored [k][n].
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 ld_tr(const bf16* p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(const_cast<bf16*>(p)));
+  return __builtin_bit_cast(uint2, r);
+}
+// The operand fragment of rows k0 .. k0 + 7 of column c0 + (lane % 16) of a
+// row-major bf16 tile with ld values per row; p = tile + c0.
+__device__ __forceinline__ bf16x8 frag_tr(const bf16* p, int ld, int k0, int j) {
+  const bf16* a = p + (k0 + (j >> 2)) * ld + 4 * (j & 3);
+  const uint2 lo = ld_tr(a), hi = ld_tr(a + 4 * ld);
+  return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
 // ---------------------------------------------------------------------------
 // 3. anchor branch, query side (per chunk of queries)
 // ---------------------------------------------------------------------------
@@ -702,9 +722,11 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_k_kernel(BwdArgs a, int cb,
   load_quarter<T, D, GUARD>(kraw, kg, sme, L, g);
   load_quarter<T, D, GUARD>(vraw, vg, sme, L, g);
 
-  // the first query tiles (queries on the MFMA rows; each tile's q and dY
-  // rows are loaded NB - 1 tiles ahead: two for 16-bit values, one for fp32)
-  constexpr int NB = sizeof(T) == 2 ? 3 : 2;
+  // the query operands of the logit tiles (queries on the MFMA rows): bf16,
+  // from the staged transposed tiles by transposing LDS reads; fp32, rows
+  // loaded from memory one tile ahead
+  constexpr bool TR = sizeof(T) == 2;
+  constexpr int NB = TR ? 1 : 2;
   uint4 qraw[NB][QV], dyraw[NB][QV];
   auto load_query = [&](uint4* qr, uint4* dr, int t) __attribute__((always_inline)) {
     if constexpr (GUARD) {
@@ -715,8 +737,10 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_k_kernel(BwdArgs a, int cb,
       load_quarter_clamped<T, D>(dr, dyg, t, L, g);
     }
   };
+  if constexpr (!TR) {
 #pragma unroll
-  for (int kt = 0; kt < NB - 1; ++kt) load_query(qraw[kt], dyraw[kt], t0 + Q0 + 16 * kt + m);
+    for (int kt = 0; kt < NB - 1; ++kt) load_query(qraw[kt], dyraw[kt], t0 + Q0 + 16 * kt + m);
+  }
   // queries [t0, t0 + 128): transposed q and dY, lse (log2 units) and D_t;
   // every load issued before the first store
   {
@@ -744,13 +768,25 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_k_kernel(BwdArgs a, int cb,
   f32x4 z[kWinTiles], dp[kWinTiles];
 #pragma unroll
   for (int kt = 0; kt < kWinTiles; ++kt) {
-    if (kt + NB - 1 < kWinTiles)
-      load_query(qraw[(kt + NB - 1) % NB], dyraw[(kt + NB - 1) % NB], t0 + Q0 + 16 * (kt + NB - 1) + m);
     f32x4 zc = zero4(), pc = zero4();
+    if constexpr (TR) {
+      // rows t = Q0 + 16 kt + m of q and dY over the lane group's dims
+      // (D / 4) g + 8 e .. + 7, the dims of its quarter of the key row
+      const T* qp = sQT + Q0 + 16 * kt;
+      const T* yp = sdYT + Q0 + 16 * kt;
 #pragma unroll
-    for (int e = 0; e < NF; ++e) {
-      zc = M::mma(frag_of<T>(qraw[kt % NB], e), frag_of<T>(kraw, e), zc);
-      pc = M::mma(frag_of<T>(dyraw[kt % NB], e), frag_of<T>(vraw, e), pc);
+      for (int e = 0; e < NF; ++e) {
+        zc = M::mma(frag_tr(qp, Lay::LDT, (D / 4) * g + 8 * e, m), frag_of<T>(kraw, e), zc);
+        pc = M::mma(frag_tr(yp, Lay::LDT, (D / 4) * g + 8 * e, m), frag_of<T>(vraw, e), pc);
+      }
+    } else {
+      if (kt + NB - 1 < kWinTiles)
+        load_query(qraw[(kt + NB - 1) % NB], dyraw[(kt + NB - 1) % NB], t0 + Q0 + 16 * (kt + NB - 1) + m);
+#pragma unroll
+      for (int e = 0; e < NF; ++e) {
+        zc = M::mma(frag_of<T>(qraw[kt % NB], e), frag_of<T>(kraw, e), zc);
+        pc = M::mma(frag_of<T>(dyraw[kt % NB], e), frag_of<T>(vraw, e), pc);
+      }
     }
     z[kt] = zc;
     dp[kt] = pc;
