@@ -445,14 +445,18 @@ __device__ __forceinline__ bf16x8 frag_tr(const bf16* p, int ld, int k0, int j) 
 template <typename T, int D>
 struct AqLayout {
   static constexpr int PAD = 16 / sizeof(T);
-  static constexpr int LDKT = 128 + PAD;   // sKT [D][LDKT]: window keys transposed
-  static constexpr int LDMT = 32 + PAD;    // sMuT [D][LDMT]: sink keys transposed (zero padded)
+  // bf16: the logit tiles' key and value operands come from the transposed
+  // window tiles by transposing LDS reads (fp32: from memory, per wavefront)
+  static constexpr bool TR = sizeof(T) == 2;
+  static constexpr int LDKT = 128 + PAD;   // sKT, sVT [D][LDKT]: window keys / values transposed
+  static constexpr int LDMT = 16 + PAD;    // sMuT [D][LDMT]: sink keys transposed (zero padded)
   static constexpr int LDQ = D + PAD;      // sQ [64][LDQ]
   static constexpr int a16(int x) { return (x + 15) / 16 * 16; }
   static constexpr int OFF_KT = 0;
   static constexpr int OFF_Q = 0;          // after the dq products, the chunk's queries replace the keys
   static_assert(64 * LDQ <= D * LDKT, "query rows fit in the key tile");
-  static constexpr int OFF_MT = OFF_KT + a16(D * LDKT * (int)sizeof(T));
+  static constexpr int OFF_VT = OFF_KT + a16(D * LDKT * (int)sizeof(T));
+  static constexpr int OFF_MT = OFF_VT + (TR ? a16(D * LDKT * (int)sizeof(T)) : 0);
   static constexpr int OFF_DZS = OFF_MT + a16(D * LDMT * (int)sizeof(T));   // sink dZ, fp32 [64][16]
   static constexpr int TOTAL = OFF_DZS + a16(64 * 16 * 4);
 };
@@ -473,6 +477,7 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_q_kernel(BwdArgs a, int cb,
   constexpr int NDT = D / 16;
   extern __shared__ __align__(16) unsigned char smem[];
   T* sKT = reinterpret_cast<T*>(smem + Lay::OFF_KT);
+  T* sVT = reinterpret_cast<T*>(smem + Lay::OFF_VT);
   T* sMuT = reinterpret_cast<T*>(smem + Lay::OFF_MT);
   T* sQ = reinterpret_cast<T*>(smem + Lay::OFF_Q);
   float* sdZs = reinterpret_cast<float*>(smem + Lay::OFF_DZS);
@@ -494,13 +499,14 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_q_kernel(BwdArgs a, int cb,
   const int I = w;
   const int tme = t0 + 16 * I + m;
   const int U0 = 16 * I;                  // first window key of the tiles (of [t0 - 64, t0 + 64))
-  // this lane's query and dY row, and the window keys / values of its
+  // this lane's query and dY row; fp32: the window keys / values of its
   // first three tiles, issued before the staging (their loads then overlap
-  // it); the other tiles reuse the registers
+  // it), the other tiles reuse the registers
+  constexpr bool TR = Lay::TR;
   uint4 qraw[QV], dyraw[QV];
   load_quarter<T, D, GUARD>(qraw, qg, tme, L, g);
   load_quarter<T, D, GUARD>(dyraw, dyg, tme, L, g);
-  uint4 kraw[3][QV], vraw[3][QV];
+  uint4 kraw[TR ? 1 : 3][QV], vraw[TR ? 1 : 3][QV];
   auto load_tiles = [&](int k0, int n) __attribute__((always_inline)) {
 #pragma unroll
     for (int kk = 0; kk < n; ++kk) {
@@ -514,7 +520,7 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_q_kernel(BwdArgs a, int cb,
       }
     }
   };
-  load_tiles(0, 3);
+  if constexpr (!TR) load_tiles(0, 3);
   const float lse2 = !GUARD || tme < L ? a.lse[(size_t)bh * L + (tme < L ? tme : 0)] * kLog2e : 0.f;
 
   // window keys [t0 - 64, t0 + 64) transposed; sink keys transposed
@@ -539,32 +545,63 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_q_kernel(BwdArgs a, int cb,
       for (int e = 0; e < MPI; ++e) sMuT[(MPI * j + e) * Lay::LDMT + s] = pv[e];
     }
   }
-  stage_T<T, D, D, 128>(sKT, Lay::LDKT, kg, t0 - 64, 0, L, 1.0f);
+  if constexpr (TR) {
+    // keys and values of the window, every load issued before the first store
+    uint32_t wk[StageT<T, D, 128>::RPT], wv[StageT<T, D, 128>::RPT];
+    stage_T_load<T, D, D, 128>(wk, kg, t0 - 64, 0, L);
+    stage_T_load<T, D, D, 128>(wv, vg, t0 - 64, 0, L);
+    stage_T_store<T, D, 128>(sKT, Lay::LDKT, wk, 1.0f);
+    stage_T_store<T, D, 128>(sVT, Lay::LDKT, wv, 1.0f);
+  } else {
+    stage_T<T, D, D, 128>(sKT, Lay::LDKT, kg, t0 - 64, 0, L, 1.0f);
+  }
   __syncthreads();
 
   // logits Z^T[u][t] and value products dP^T[u][t] for window keys u
   f32x4 z[kWinTiles], dp[kWinTiles];
+  if constexpr (TR) {
+    // key / value rows u = U0 + 16 kk + m of the window over the lane group's
+    // dims (D / 4) g + 8 e .. + 7, the dims of its quarter of the query row
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    if (half == 1) load_tiles(3, kWinTiles - 3);
-#pragma unroll
-    for (int kk = 0; kk < (half == 0 ? 3 : kWinTiles - 3); ++kk) {
+    for (int kk = 0; kk < kWinTiles; ++kk) {
       f32x4 zc = zero4(), pc = zero4();
 #pragma unroll
       for (int e = 0; e < NF; ++e) {
-        zc = M::mma(frag_of<T>(kraw[kk], e), frag_of<T>(qraw, e), zc);
-        pc = M::mma(frag_of<T>(vraw[kk], e), frag_of<T>(dyraw, e), pc);
+        zc = M::mma(frag_tr(sKT + U0 + 16 * kk, Lay::LDKT, (D / 4) * g + 8 * e, m), frag_of<T>(qraw, e), zc);
+        pc = M::mma(frag_tr(sVT + U0 + 16 * kk, Lay::LDKT, (D / 4) * g + 8 * e, m), frag_of<T>(dyraw, e), pc);
       }
-      z[3 * half + kk] = zc;
-      dp[3 * half + kk] = pc;
+      z[kk] = zc;
+      dp[kk] = pc;
+    }
+  } else {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if (half == 1) load_tiles(3, kWinTiles - 3);
+#pragma unroll
+      for (int kk = 0; kk < (half == 0 ? 3 : kWinTiles - 3); ++kk) {
+        f32x4 zc = zero4(), pc = zero4();
+#pragma unroll
+        for (int e = 0; e < NF; ++e) {
+          zc = M::mma(frag_of<T>(kraw[kk], e), frag_of<T>(qraw, e), zc);
+          pc = M::mma(frag_of<T>(vraw[kk], e), frag_of<T>(dyraw, e), pc);
+        }
+        z[3 * half + kk] = zc;
+        dp[3 * half + kk] = pc;
+      }
     }
   }
   f32x4 zs = zero4();
   if (a.n_meta > 0) {
-    uint4 mraw[QV];
-    load_quarter<T, D>(mraw, mug, m < a.n_meta ? m : -1, a.n_meta, g);
+    if constexpr (TR) {
 #pragma unroll
-    for (int e = 0; e < NF; ++e) zs = M::mma(frag_of<T>(mraw, e), frag_of<T>(qraw, e), zs);
+      for (int e = 0; e < NF; ++e)
+        zs = M::mma(frag_tr(sMuT, Lay::LDMT, (D / 4) * g + 8 * e, m), frag_of<T>(qraw, e), zs);
+    } else {
+      uint4 mraw[QV];
+      load_quarter<T, D>(mraw, mug, m < a.n_meta ? m : -1, a.n_meta, g);
+#pragma unroll
+      for (int e = 0; e < NF; ++e) zs = M::mma(frag_of<T>(mraw, e), frag_of<T>(qraw, e), zs);
+    }
   }
   // probabilities from the forward normaliser, D_t, dZ
   float dsum = 0.f;
