@@ -84,6 +84,23 @@ __device__ __forceinline__ void load_quarter(uint4* raw, const T* base, int row,
     raw[e] = ok ? r : make_uint4(0, 0, 0, 0);
   }
 }
+// Lane group g's interleaved share of row `row` (zeros if the row is outside
+// [0, L)): raw[e] holds the 16 bytes at values (4e + g) * V .. + V - 1, V =
+// 16 / sizeof(T) (bf16 d = 128: values 8g + 32e .. + 7).  The transposing
+// reads that pair with it then take LDS rows 8 apart across the lane groups
+// (a quarter's rows would be 32 apart, which puts the groups on one bank set).
+template <typename T, int D, bool GUARD = true>
+__device__ __forceinline__ void load_interleaved(uint4* raw, const T* base, int row, int L, int g) {
+  constexpr int V = 16 / sizeof(T);
+  constexpr int QV = D / 4 / V;
+  const bool ok = !GUARD || (row >= 0 && row < L);
+  const T* p = base + (size_t)(ok ? row : 0) * D + g * V;
+#pragma unroll
+  for (int e = 0; e < QV; ++e) {
+    const uint4 r = ld16(p + 4 * e * V);
+    raw[e] = ok ? r : make_uint4(0, 0, 0, 0);
+  }
+}
 // The same quarter of row `row` clamped into [0, L): for rows that the
 // caller masks out after the product (their values never reach a result),
 // without the data selects of the guarded form.
@@ -123,7 +140,7 @@ __device__ __forceinline__ void stage_T_load(uint32_t* w, const T* src, int r0, 
     w[rr] = ok ? u : 0u;
   }
 }
-template <typename T, int COLS, int NR, int NTH = 256>
+template <typename T, int COLS, int NR, int NTH = 256, bool A8 = false>
 __device__ __forceinline__ void stage_T_store(T* dst, int ld, const uint32_t* w,
                                               float scale) {
   typedef StageT<T, COLS, NR, NTH> S;
@@ -138,7 +155,13 @@ __device__ __forceinline__ void stage_T_store(T* dst, int ld, const uint32_t* w,
       float v8[8];
 #pragma unroll
       for (int rr = 0; rr < 8; ++rr) v8[rr] = elem32<T>(w[8 * b + rr], cc) * scale;
-      store_pack<T, 8>(dst + (VC * vj + cc) * ld + vs * RPT + 8 * b, v8);
+      T* d = dst + (VC * vj + cc) * ld + vs * RPT + 8 * b;
+      if constexpr (A8) {   // rows only 8-byte aligned: two 8-byte stores
+        store_pack<T, 4>(d, v8);
+        store_pack<T, 4>(d + 4, v8 + 4);
+      } else {
+        store_pack<T, 8>(d, v8);
+      }
     }
 }
 template <typename T, int D, int COLS, int NR, int NTH = 256>
@@ -503,9 +526,15 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_q_kernel(BwdArgs a, int cb,
   // first three tiles, issued before the staging (their loads then overlap
   // it), the other tiles reuse the registers
   constexpr bool TR = Lay::TR;
+  // (bf16: the interleaved share; its step e covers values 8g + 32e .. + 7)
   uint4 qraw[QV], dyraw[QV];
-  load_quarter<T, D, GUARD>(qraw, qg, tme, L, g);
-  load_quarter<T, D, GUARD>(dyraw, dyg, tme, L, g);
+  if constexpr (TR) {
+    load_interleaved<T, D, GUARD>(qraw, qg, tme, L, g);
+    load_interleaved<T, D, GUARD>(dyraw, dyg, tme, L, g);
+  } else {
+    load_quarter<T, D, GUARD>(qraw, qg, tme, L, g);
+    load_quarter<T, D, GUARD>(dyraw, dyg, tme, L, g);
+  }
   uint4 kraw[TR ? 1 : 3][QV], vraw[TR ? 1 : 3][QV];
   auto load_tiles = [&](int k0, int n) __attribute__((always_inline)) {
 #pragma unroll
@@ -561,14 +590,14 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_q_kernel(BwdArgs a, int cb,
   f32x4 z[kWinTiles], dp[kWinTiles];
   if constexpr (TR) {
     // key / value rows u = U0 + 16 kk + m of the window over the lane group's
-    // dims (D / 4) g + 8 e .. + 7, the dims of its quarter of the query row
+    // dims 8g + 32e .. + 7, those of its share of the query row
 #pragma unroll
     for (int kk = 0; kk < kWinTiles; ++kk) {
       f32x4 zc = zero4(), pc = zero4();
 #pragma unroll
       for (int e = 0; e < NF; ++e) {
-        zc = M::mma(frag_tr(sKT + U0 + 16 * kk, Lay::LDKT, (D / 4) * g + 8 * e, m), frag_of<T>(qraw, e), zc);
-        pc = M::mma(frag_tr(sVT + U0 + 16 * kk, Lay::LDKT, (D / 4) * g + 8 * e, m), frag_of<T>(dyraw, e), pc);
+        zc = M::mma(frag_tr(sKT + U0 + 16 * kk, Lay::LDKT, 8 * g + 32 * e, m), frag_of<T>(qraw, e), zc);
+        pc = M::mma(frag_tr(sVT + U0 + 16 * kk, Lay::LDKT, 8 * g + 32 * e, m), frag_of<T>(dyraw, e), pc);
       }
       z[kk] = zc;
       dp[kk] = pc;
@@ -595,7 +624,7 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_q_kernel(BwdArgs a, int cb,
     if constexpr (TR) {
 #pragma unroll
       for (int e = 0; e < NF; ++e)
-        zs = M::mma(frag_tr(sMuT, Lay::LDMT, (D / 4) * g + 8 * e, m), frag_of<T>(qraw, e), zs);
+        zs = M::mma(frag_tr(sMuT, Lay::LDMT, 8 * g + 32 * e, m), frag_of<T>(qraw, e), zs);
     } else {
       uint4 mraw[QV];
       load_quarter<T, D>(mraw, mug, m < a.n_meta ? m : -1, a.n_meta, g);
@@ -681,7 +710,8 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_q_kernel(BwdArgs a, int cb,
   if (a.n_meta > 0) {
     __syncthreads();                      // the key tile is free
 #pragma unroll
-    for (int e = 0; e < QV; ++e) st16(sQ + (16 * I + m) * Lay::LDQ + g * (D / 4) + e * EPV, qraw[e]);
+    for (int e = 0; e < QV; ++e)
+      st16(sQ + (16 * I + m) * Lay::LDQ + (TR ? (g + 4 * e) * EPV : g * (D / 4) + e * EPV), qraw[e]);
     __syncthreads();
     float* part = a.ws_dmu + ((size_t)bh * nc + c) * a.n_meta * D;
 #pragma unroll
@@ -713,7 +743,13 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_q_kernel(BwdArgs a, int cb,
 template <typename T, int D>
 struct AkLayout {
   static constexpr int PAD = 16 / sizeof(T);
-  static constexpr int LDT = 128 + PAD;    // sQT, sdYT [D][LDT]
+  // sQT, sdYT [D][LDT].  bf16: rows of 296 bytes, so that both ways they are
+  // read, transposing reads (four rows per 16-lane group, the groups 32 rows
+  // apart) and pairs of 8-byte runs 32 bytes apart on 16 consecutive rows,
+  // spread over the LDS banks (272-byte rows conflict on both); the rows are
+  // then only 8-byte aligned and are staged with 8-byte stores
+  static constexpr bool A8 = sizeof(T) == 2;
+  static constexpr int LDT = 128 + (A8 ? 20 : PAD);
   static constexpr int a16(int x) { return (x + 15) / 16 * 16; }
   static constexpr int OFF_QT = 0;
   static constexpr int OFF_DYT = OFF_QT + a16(D * LDT * (int)sizeof(T));
@@ -792,8 +828,8 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_k_kernel(BwdArgs a, int cb,
         d_t = a.ws_D[(size_t)bh * L + t];
       }
     }
-    stage_T_store<T, D, 128>(sQT, Lay::LDT, wq, 1.0f);
-    stage_T_store<T, D, 128>(sdYT, Lay::LDT, wy, 1.0f);
+    stage_T_store<T, D, 128, 256, Lay::A8>(sQT, Lay::LDT, wq, 1.0f);
+    stage_T_store<T, D, 128, 256, Lay::A8>(sdYT, Lay::LDT, wy, 1.0f);
     if (tid < 128) {
       sLse[tid] = lse_t;
       sD[tid] = d_t;
