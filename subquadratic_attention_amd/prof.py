@@ -20,6 +20,14 @@ with ``--copy-calibration``) and writes:
 Usage: python -m subquadratic_attention_amd.prof <name> <workload>
        <kernel-substring[,kernel-substring...]> <source[,source...]> <trace_dir>
        <fetch_dir> <write_dir> <out_dir> <timed> <command...>
+
+With ``sq`` first, it summarises two SQ counter runs (``--pmc`` of the
+instruction counters, then of the busy / wait cycle counters) into
+``<name>_<workload>_sq.md``: per kernel, instructions per wavefront by kind,
+and MFMA, VALU and LDS activity as fractions of the kernel's cycles:
+
+       python -m subquadratic_attention_amd.prof sq <name> <workload>
+       <kernel-substring[,...]> <insts_dir> <cycles_dir> <out_dir> <command...>
 """
 from __future__ import annotations
 
@@ -139,5 +147,77 @@ def main(argv):
     print(json.dumps(rec))
 
 
+# The kernel's duration in GPU cycles is GRBM_GUI_ACTIVE / 8 (one GRBM per
+# XCD, summed): checked against the traced duration at 2.4 GHz.
+# SQ_VALU_MFMA_BUSY_CYCLES counts SIMD cycles of matrix-core work (16 per
+# 16x16x32 bf16 MFMA: it equals 16 x SQ_INSTS_MFMA for the bf16 kernels);
+# SQ_ACTIVE_INST_VALU / _LDS count, summed over the waves, the quad-cycles
+# (4 cycles) in which a wave issues that kind of instruction;
+# SQ_LDS_BANK_CONFLICT counts CU cycles stalled on LDS bank conflicts;
+# SQ_WAIT_INST_ANY and SQ_WAVE_CYCLES count quad-cycles summed over waves.
+INSTS = ["SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VMEM_RD",
+         "SQ_INSTS_VMEM_WR", "SQ_INSTS_VALU_TRANS_F32"]
+CYCLES = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS",
+          "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_ANY", "GRBM_GUI_ACTIVE"]
+CUS, SIMDS, XCDS = 256, 4, 8
+
+
+def counters_by_kernel(d: str):
+    """{kernel name: {counter: mean over the kernel's dispatches}}."""
+    acc = {}
+    for r in _rows(d, "*counter_collection.csv"):
+        acc.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in acc.items()}
+
+
+def sq_main(argv):
+    name, workload, ksubs, insts_dir, cycles_dir, out_dir = argv[:6]
+    command = " ".join(argv[6:])
+    a = counters_by_kernel(insts_dir)
+    b = counters_by_kernel(cycles_dir)
+    lines = [f"# {name}: {workload}, SQ counters", "", "Produced by:", "", "```", command, "```", "",
+             "Each value is the mean over the kernel's dispatches in that run.  Instructions are per "
+             "wavefront (SQ_INSTS_* / SQ_WAVES).  With T = GRBM_GUI_ACTIVE / 8 the kernel's cycles (one GRBM per "
+             "XCD): MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (T x 1024 SIMDs), the share of SIMD cycles the matrix "
+             "cores work; VALU issue = 4 SQ_ACTIVE_INST_VALU / (T x 1024), the share of SIMD cycles issuing VALU "
+             "instructions (summed over the SIMD's waves); LDS issue likewise from SQ_ACTIVE_INST_LDS; LDS "
+             "conflict = SQ_LDS_BANK_CONFLICT / (T x 256 CUs), the share of CU cycles stalled on bank conflicts; "
+             "waiting = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES, the share of resident-wave time spent waiting for "
+             "outstanding memory or LDS results.", "",
+             "| kernel | waves | VALU | (transc.) | MFMA | LDS | SALU | VMEM rd | VMEM wr | T (us at 2.4 GHz) | "
+             "MFMA busy | VALU issue | LDS issue | LDS conflict | waiting |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    rec = {}
+    for sub in ksubs.split(","):
+        ka = _match(a, sub)
+        kb = _match(b, sub)
+        x, y = a[ka], b[kb]
+        waves = x["SQ_WAVES"]
+        per = {c: x[c] / waves for c in INSTS[1:]}
+        T = y["GRBM_GUI_ACTIVE"] / XCDS
+        mfma = y["SQ_VALU_MFMA_BUSY_CYCLES"] / (T * CUS * SIMDS)
+        valu = 4 * y["SQ_ACTIVE_INST_VALU"] / (T * CUS * SIMDS)
+        lds = 4 * y["SQ_ACTIVE_INST_LDS"] / (T * CUS * SIMDS)
+        conf = y["SQ_LDS_BANK_CONFLICT"] / (T * CUS)
+        wait = y["SQ_WAIT_INST_ANY"] / max(y["SQ_WAVE_CYCLES"], 1.0)
+        lines.append(f"| `{sub}` | {waves:.0f} | {per['SQ_INSTS_VALU']:.0f} | {per['SQ_INSTS_VALU_TRANS_F32']:.0f} | "
+                     f"{per['SQ_INSTS_MFMA']:.0f} | {per['SQ_INSTS_LDS']:.0f} | {per['SQ_INSTS_SALU']:.0f} | "
+                     f"{per['SQ_INSTS_VMEM_RD']:.0f} | {per['SQ_INSTS_VMEM_WR']:.0f} | {T / 2400:.1f} | "
+                     f"{100 * mfma:.1f} % | {100 * valu:.1f} % | {100 * lds:.1f} % | {100 * conf:.1f} % | "
+                     f"{100 * wait:.1f} % |")
+        rec[sub] = {"per_wave": per, "waves": waves, "cycles": T, "mfma_busy": mfma, "valu_issue": valu,
+                    "lds_issue": lds, "lds_conflict": conf, "waiting": wait, "raw_insts": x, "raw_cycles": y}
+    lines += ["", "Raw counter means per dispatch:", ""]
+    for sub, r in rec.items():
+        lines.append(f"- `{sub}`: " + ", ".join(f"{c} = {v:.4g}" for c, v in {**r['raw_insts'], **r['raw_cycles']}.items()))
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, f"{name}_{workload}_sq.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps({k: {kk: vv for kk, vv in v.items() if not kk.startswith("raw")} for k, v in rec.items()}))
+
+
 if __name__ == "__main__":
-    main(sys.argv[1:])
+    if sys.argv[1:2] == ["sq"]:
+        sq_main(sys.argv[2:])
+    else:
+        main(sys.argv[1:])
