@@ -85,7 +85,11 @@ struct FwdLayout {
   static constexpr int OFF_BEXP = OFF_TOT + a16(8 * D * 4) + (STAGE_A ? 0 : a16(8 * D * 4));
   static constexpr int OFF_SC = OFF_BEXP + a16(D * 4);          // [2][64]: alpha/den, 1/den
   static constexpr int OFF_META = OFF_SC + N * a16(2 * 64 * 4);
-  static constexpr int TOTAL = OFF_META + N * a16(16 * LDK * (int)sizeof(T));
+  // wide-span chunks: per query block, whether its own span needs the pairwise
+  // diagonal (set in the operand step, read in the next score step; not in
+  // the A staging the totals share, which the score step writes)
+  static constexpr int OFF_WIDE = OFF_META + N * a16(16 * LDK * (int)sizeof(T));
+  static constexpr int TOTAL = OFF_WIDE + N * 16;
   static_assert(STATES || 64 * LDE * 4 <= OFF_KHT - OFF_KP, "beta fits over sKp and sQe");
   static_assert(!STAGE_A || 8 * D * 4 <= A_BYTES, "wide-span totals fit over the A staging");
 };
@@ -174,6 +178,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(STATES ? 4 
   float* sTot = reinterpret_cast<float*>(smem + Lay::OFF_TOT);
   T* sA = reinterpret_cast<T*>(smem + Lay::OFF_A);                // bfloat16 only
   float* sTotC = reinterpret_cast<float*>(smem + Lay::OFF_TOTC);  // wide-span chunks only
+  int* sWide = reinterpret_cast<int*>(smem + Lay::OFF_WIDE);       // wide-span chunks only
   float* sBexp = reinterpret_cast<float*>(smem + Lay::OFF_BEXP);
   float* sSc = reinterpret_cast<float*>(smem + Lay::OFF_SC);
   T* sMeta = reinterpret_cast<T*>(smem + Lay::OFF_META);
@@ -522,6 +527,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(STATES ? 4 
         for (int dd = 0; dd < DPL; ++dd) sTotC[w * D + DPL * l + dd] = totc[dd];
         __syncthreads();
         offsets(sTotC, off, Bt);
+        if (!STATES && w < 4) {
+          // query block w's own span per dim: minus its two 8-row partial totals
+          bool wb = false;
+  #pragma unroll
+          for (int dd = 0; dd < DPL; ++dd)
+            wb |= -(sTotC[2 * w * D + DPL * l + dd] + sTotC[(2 * w + 1) * D + DPL * l + dd]) > kMaxSpanLog2;
+          const bool any = __any(wb);
+          if (l == 0) sWide[w] = any ? 1 : 0;
+        }
   #pragma unroll
         for (int dd = 0; dd < DPL; ++dd) eB[dd] = exp_2(Bt[dd]);
   #pragma unroll
@@ -822,14 +836,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(STATES ? 4 
           // block's own span stays within the factorisable range (then
           // 2^{beta_a - beta_s} <= 2^span), else every pair (t, s) in fp32,
           // each lane over its k-quarter, summed across the quarters
-          // (the block's span per dimension: minus its two 8-row partial totals)
-          bool wide_b = false;
-  #pragma unroll
-          for (int dd = 0; dd < D / 64; ++dd) {
-            const int i = (D / 64) * (threadIdx.x & 63) + dd;
-            wide_b |= -(sTotC[2 * QB * D + i] + sTotC[(2 * QB + 1) * D + i]) > kMaxSpanLog2;
-          }
-          if (!__any(wide_b)) {
+          // (the block's span, as the operand step found it)
+          if (sWide[QB] == 0) {
             ai[QB] = factored(QB, QB > 0 ? sBeta + (16 * QB - 1) * Lay::LDE + g * (D / 4) : nullptr);
           } else {
             ai[QB] = zero4();
