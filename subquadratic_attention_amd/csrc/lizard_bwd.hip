@@ -36,7 +36,10 @@
 //   6. bwd_dmeta_reduce: sums the sink-key partials over batch and chunks in
 //      a fixed order (deterministic, no float atomics).
 // Kernels 3-5 run the full chunks in one launch and a ragged last chunk in a
-// range-checked launch of its own.  Chunks whose decay span exceeds 2^184
+// range-checked launch of its own.  For bf16 at d = 128, two walks over each
+// head's chunks replace kernels 2-5: the reverse walk (5, bf16) writes the
+// gated dq, dk, dv and dlog_g, carrying G in registers, and the anchor walk
+// (5b) adds the anchor parts to them.  Chunks whose decay span exceeds 2^184
 // form the gated intra terms pairwise in fp32; spans between 2^92 and 2^184
 // move each dimension's reference point to half its chunk total (as the
 // forward pass does).
@@ -487,9 +490,7 @@ struct AqLayout {
 // The grid covers chunks cb .. cb + ncl - 1; GUARD = false: they are full
 // (every query inside [0, L)); window keys before position 0 (chunk 0) are
 // read from row 0 and masked out with the rest of the window.
-// ACC: add the anchor part to what dq holds (the gated part, written before by
-// the reverse walk) instead of writing it alone.
-template <typename T, int D, bool GUARD, bool ACC = false>
+template <typename T, int D, bool GUARD>
 __global__ __launch_bounds__(256, 2) void bwd_anchor_q_kernel(BwdArgs a, int cb, int ncl) {
   typedef AqLayout<T, D> Lay;
   typedef Mfma<T> M;
@@ -675,15 +676,7 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_q_kernel(BwdArgs a, int cb,
 #pragma unroll
   for (int e = 0; e < NS; ++e) sf[e] = M::pack(zsv + e * M::KPL);
   // dq^T[d][t] = scale (K^T dZ^T + mu^T dZs^T)
-  T* dqa = reinterpret_cast<T*>(a.dq) + (size_t)bh * L * D;   // the anchor part (ACC: added to the gated part)
-  // (bf16: kept packed, 2 registers per 4 values)
-  typedef typename std::conditional<sizeof(T) == 2, uint2, uint4>::type P4;
-  P4 prev[ACC ? NDT : 1];
-  if constexpr (ACC) {
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-      prev[dt] = *reinterpret_cast<const P4*>(dqa + (size_t)(tme < L ? tme : 0) * D + 16 * dt + 4 * g);
-  }
+  T* dqa = reinterpret_cast<T*>(a.dq) + (size_t)bh * L * D;   // the anchor part
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
     f32x4 o = zero4();
@@ -695,12 +688,6 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_q_kernel(BwdArgs a, int cb,
     for (int e = 0; e < NS; ++e) o = M::mma(sink_frag<T>(az, g, e), sf[e], o);
     if (tme < L) {
       float v4[4] = {o[0] * a.scale, o[1] * a.scale, o[2] * a.scale, o[3] * a.scale};
-      if constexpr (ACC) {
-        float pv[4];
-        load_pack<T, 4>(reinterpret_cast<const T*>(&prev[dt]), pv);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v4[r] += pv[r];
-      }
       store_pack<T, 4>(dqa + (size_t)tme * D + 16 * dt + 4 * g, v4);
     }
   }
@@ -760,8 +747,7 @@ struct AkLayout {
 // The grid covers chunks cb .. cb + ncl - 1; GUARD = false: they are full
 // (every key inside [0, L)); window queries past L (the last full chunk's
 // next chunk) are read from row L - 1 and masked out.  Two workgroups per CU.
-// ACC: as for the query side (dk and dv hold the gated parts).
-template <typename T, int D, bool GUARD, bool ACC = false>
+template <typename T, int D, bool GUARD>
 __global__ __launch_bounds__(256, 2) void bwd_anchor_k_kernel(BwdArgs a, int cb, int ncl) {
   typedef AkLayout<T, D> Lay;
   typedef Mfma<T> M;
@@ -888,19 +874,9 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_k_kernel(BwdArgs a, int cb,
     zf[e] = M::pack(pz + e * M::KPL);
     pf[e] = M::pack(pp + e * M::KPL);
   }
-  // the anchor parts of dk and dv (ACC: added to the gated parts)
+  // the anchor parts of dk and dv
   T* dka = reinterpret_cast<T*>(a.dk) + (size_t)bh * L * D;
   T* dva = reinterpret_cast<T*>(a.dv) + (size_t)bh * L * D;
-  typedef typename std::conditional<sizeof(T) == 2, uint2, uint4>::type P4;   // 4 values, packed
-  P4 prevk[ACC ? NDT : 1], prevv[ACC ? NDT : 1];
-  if constexpr (ACC) {
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const size_t o = (size_t)(sme < L ? sme : 0) * D + 16 * dt + 4 * g;
-      prevk[dt] = *reinterpret_cast<const P4*>(dka + o);
-      prevv[dt] = *reinterpret_cast<const P4*>(dva + o);
-    }
-  }
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
     f32x4 ok_ = zero4(), ov = zero4();
@@ -914,16 +890,6 @@ __global__ __launch_bounds__(256, 2) void bwd_anchor_k_kernel(BwdArgs a, int cb,
     if (sme < L) {
       float k4[4] = {ok_[0] * a.scale, ok_[1] * a.scale, ok_[2] * a.scale, ok_[3] * a.scale};
       float v4[4] = {ov[0], ov[1], ov[2], ov[3]};
-      if constexpr (ACC) {
-        float pk[4], pv[4];
-        load_pack<T, 4>(reinterpret_cast<const T*>(&prevk[dt]), pk);
-        load_pack<T, 4>(reinterpret_cast<const T*>(&prevv[dt]), pv);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          k4[r] += pk[r];
-          v4[r] += pv[r];
-        }
-      }
       store_pack<T, 4>(dka + (size_t)sme * D + 16 * dt + 4 * g, k4);
       store_pack<T, 4>(dva + (size_t)sme * D + 16 * dt + 4 * g, v4);
     }
@@ -1525,8 +1491,8 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_flagged_kernel(BwdArg
 // state rows and the next chunk's rows issued; (2) the causal score tiles
 // A = Qe Kp^T and dA = dO V^T; (3) per token tile, last to first: the
 // inter-chunk terms (S dO, G V, G^T Kh), the intra-chunk terms (Kp^T dA,
-// Qe^T dA^T, dO^T A^T), the outputs (added to the anchor parts already in
-// dq, dk, dv) and dlog_g; then the update of G.
+// Qe^T dA^T, dO^T A^T), the outputs (dq, dk, dv: the gated parts, which the
+// anchor walk adds to) and dlog_g; then the update of G.
 //
 // dlog_g of a token t of chunk c is the suffix sum of q.dq - k.dk over the
 // chunk's tokens u >= t plus, for everything after the chunk, the boundary
@@ -1924,7 +1890,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
     } else {
       // left to the per-chunk kernel: G_{c+1} (rows of Y) and its transpose
       // (rows of X), in the element type; the chunk's dq, dk, dv rows zero
-      // (that kernel adds its gated parts to them, the anchor kernels theirs)
+      // (that kernel adds its gated parts to them, the anchor walk its own)
 #pragma unroll
       for (int h = 0; h < GPW; ++h) {
         const size_t ro = ((size_t)bh * nc + c) * D * D + (size_t)(16 * (GPW * w + h) + m) * D + 4 * g;
@@ -2118,6 +2084,353 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
 }
 
 // ---------------------------------------------------------------------------
+// 5b. anchor branch, both sides in one forward walk over each head's chunks
+// (bf16, d = 128)
+// ---------------------------------------------------------------------------
+// At chunk c the window block row of the chunk's queries (keys of chunks c-1
+// and c) gives P, dP, D_t and dS once; from it come dq of chunk c
+// (complete), the second and last part of dk, dv of chunk c-1 (the first came
+// from its own queries one chunk earlier and waited in registers) and the
+// first part of dk, dv of chunk c.  Each chunk's q, k, v, dY are read once
+// and each gradient row is read and written once (added to the gated part
+// the reverse walk wrote).
+//
+// Lane orders: the contraction runs over values 8g + 32e .. + 7 of lane group
+// g in step e (both operands alike), so that fragment reads of the 288-byte
+// token rows take lane groups 16 bytes apart and transposing reads take rows
+// 8 apart, both free of LDS bank conflicts at that row stride.
+struct AwLayout {
+  static constexpr int D = 128;
+  static constexpr int LD = D + 16;                   // [64][LD] bf16 token tiles
+  static constexpr int LDZ = 16 + 8;                  // sink dZ [64][LDZ] bf16
+  static constexpr int TILE = 64 * LD * 2;
+  static constexpr int OFF_K = 0;                     // keys, a slot per chunk parity
+  static constexpr int OFF_V = OFF_K + 2 * TILE;      // values, likewise
+  static constexpr int OFF_Q = OFF_V + 2 * TILE;      // queries of chunk c
+  static constexpr int OFF_Y = OFF_Q + TILE;          // dY of chunk c
+  static constexpr int OFF_P = OFF_Y + TILE;          // alpha P[t][s]: s = keys of c-1 (0..63), of c (64..127)
+  static constexpr int OFF_DS = OFF_P + TILE;         // dS[t][s], the same
+  static constexpr int OFF_MU = OFF_DS + TILE;        // sink keys [16][LD]
+  static constexpr int OFF_ZS = OFF_MU + 16 * LD * 2; // sink dZ[t][i]
+  static constexpr int OFF_DH = OFF_ZS + 64 * LDZ * 2;   // D_t over each half of the keys [2][64] fp32
+  static constexpr int OFF_LSE = OFF_DH + 2 * 64 * 4;    // lse (log2 units) of chunk c [64] fp32
+  static constexpr int TOTAL = OFF_LSE + 64 * 4;
+};
+
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void bwd_anchor_walk_kernel(BwdArgs a) {
+  typedef AwLayout Lay;
+  typedef Mfma<bf16> M;
+  typedef bf16 T;
+  constexpr int D = Lay::D, LD = Lay::LD;
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* sK = reinterpret_cast<T*>(smem + Lay::OFF_K);
+  T* sV = reinterpret_cast<T*>(smem + Lay::OFF_V);
+  T* sQ = reinterpret_cast<T*>(smem + Lay::OFF_Q);
+  T* sY = reinterpret_cast<T*>(smem + Lay::OFF_Y);
+  T* sP = reinterpret_cast<T*>(smem + Lay::OFF_P);
+  T* sDS = reinterpret_cast<T*>(smem + Lay::OFF_DS);
+  T* sMu = reinterpret_cast<T*>(smem + Lay::OFF_MU);
+  T* sZs = reinterpret_cast<T*>(smem + Lay::OFF_ZS);
+  float* sDh = reinterpret_cast<float*>(smem + Lay::OFF_DH);
+  float* sLse = reinterpret_cast<float*>(smem + Lay::OFF_LSE);
+
+  const int bh = blockIdx.x;
+  if (bh >= a.BH) return;
+  const int h = bh % a.H, L = a.L, nc = (L + C - 1) / C;
+  const int tid = threadIdx.x, w = tid >> 6;
+  int l = tid & 63, m = l & 15, g = l >> 4;
+  const int qt = w & 3;   // query tile of the scores and of dq; key tile of dk, dv
+  const int hf = w >> 2;  // half: keys of chunk c-1 / c in the scores; dims 0..63 / 64..127 in the outputs
+  const T* qg = reinterpret_cast<const T*>(a.q) + (size_t)bh * L * D;
+  const T* kg = reinterpret_cast<const T*>(a.k) + (size_t)bh * L * D;
+  const T* vg = reinterpret_cast<const T*>(a.v) + (size_t)bh * L * D;
+  const T* yg = reinterpret_cast<const T*>(a.dy) + (size_t)bh * L * D;
+  T* dqg = reinterpret_cast<T*>(a.dq) + (size_t)bh * L * D;
+  T* dkg = reinterpret_cast<T*>(a.dk) + (size_t)bh * L * D;
+  T* dvg = reinterpret_cast<T*>(a.dv) + (size_t)bh * L * D;
+  const float* lseg = a.lse + (size_t)bh * L;
+  const float sl2 = a.scale * kLog2e;
+
+  // rows of chunk c of a [L, D] tensor: thread -> 16-byte runs of rows
+  // tid / 16 and tid / 16 + 32 (zeros outside [0, L))
+  auto load_rows = [&](uint4* buf, const T* base, int c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int t = c * C + 32 * p + (tid >> 4);
+      const bool ok = c >= 0 && t < L;
+      const uint4 u = ld16(base + (size_t)(ok ? t : 0) * D + 8 * (tid & 15));
+      buf[p] = ok ? u : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto store_rows = [&](T* tile, const uint4* buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      *reinterpret_cast<uint4*>(tile + (32 * p + (tid >> 4)) * LD + 8 * (tid & 15)) = buf[p];
+  };
+  auto load_lse = [&](int c) __attribute__((always_inline)) -> float {
+    const int t = c * C + (tid & 63);
+    return t < L ? lseg[t] * kLog2e : 0.f;
+  };
+
+  // chunk 0 (and an empty chunk -1), the sink keys
+  {
+    uint4 bq[2], bk[2], bv[2], by[2], bz[2];
+    load_rows(bq, qg, 0);
+    load_rows(bk, kg, 0);
+    load_rows(bv, vg, 0);
+    load_rows(by, yg, 0);
+    load_rows(bz, kg, -1);   // zeros
+    const float ls = load_lse(0);
+    uint4 mu = make_uint4(0u, 0u, 0u, 0u);
+    const int mrow = tid >> 4;   // threads 0..255: sink rows 0..15
+    if (tid < 256 && mrow < a.n_meta)
+      mu = ld16(reinterpret_cast<const T*>(a.meta) + ((size_t)h * a.n_meta + mrow) * D + 8 * (tid & 15));
+    store_rows(sQ, bq);
+    store_rows(sK, bk);
+    store_rows(sV, bv);
+    store_rows(sY, by);
+    store_rows(sK + 64 * LD, bz);
+    store_rows(sV + 64 * LD, bz);
+    if (tid < 64) sLse[tid] = ls;
+    if (tid < 256) *reinterpret_cast<uint4*>(sMu + mrow * LD + 8 * (tid & 15)) = mu;
+  }
+  __syncthreads();
+
+  // this wavefront's part of dk, dv of the current chunk from its own
+  // queries (key tile qt, dims 64 hf + 16 dt + 4 g + r), unscaled
+  f32x4 ck[4], cv[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) ck[dt] = cv[dt] = zero4();
+
+  for (int c = 0; c < nc; ++c) {
+    asm volatile("" : "+v"(l), "+v"(m), "+v"(g));
+    const int t0 = c * C;
+    const int cs = c & 1, ps = cs ^ 1;
+    T* sKc = sK + cs * 64 * LD;
+    T* sKp = sK + ps * 64 * LD;
+    T* sVc = sV + cs * 64 * LD;
+    T* sVp = sV + ps * 64 * LD;
+    // the next chunk's rows (written after this chunk's last reads) and the
+    // rows of dq (chunk c) and dk, dv (chunk c - 1) this wavefront adds to
+    uint4 nq[2], nk[2], nv[2], ny[2];
+    const bool more = c + 1 < nc;
+    if (more) {
+      load_rows(nq, qg, c + 1);
+      load_rows(nk, kg, c + 1);
+      load_rows(nv, vg, c + 1);
+      load_rows(ny, yg, c + 1);
+    }
+    const float nls = more ? load_lse(c + 1) : 0.f;
+    const int tq = t0 + 16 * qt + m;               // dq row of this lane
+    const int sk = t0 - C + 16 * qt + m;           // dk, dv row (chunk c - 1) of this lane
+    uint2 pq[4], pk[4], pv[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const int col = 64 * hf + 16 * dt + 4 * g;
+      pq[dt] = tq < L ? ld8(dqg + (size_t)tq * D + col) : make_uint2(0u, 0u);
+      pk[dt] = c > 0 ? ld8(dkg + (size_t)(c > 0 ? sk : 0) * D + col) : make_uint2(0u, 0u);
+      pv[dt] = c > 0 ? ld8(dvg + (size_t)(c > 0 ? sk : 0) * D + col) : make_uint2(0u, 0u);
+    }
+
+    // ---- scores: keys of chunk c - 1 (hf = 0) or c (hf = 1) against the
+    // queries of tile qt: Z^T[s][t], dP^T[s][t] (key s = 16 kt + 4g + r of
+    // the half, query t = 16 qt + m) ----
+    const T* sKh = hf ? sKc : sKp;
+    const T* sVh = hf ? sVc : sVp;
+    f32x4 z[4], dp[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      f32x4 zc = zero4(), pc = zero4();
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int col = 8 * g + 32 * e;
+        zc = M::mma(M::load(sKh + (16 * kt + m) * LD + col), M::load(sQ + (16 * qt + m) * LD + col), zc);
+        pc = M::mma(M::load(sVh + (16 * kt + m) * LD + col), M::load(sY + (16 * qt + m) * LD + col), pc);
+      }
+      z[kt] = zc;
+      dp[kt] = pc;
+    }
+    const float lse2 = sLse[16 * qt + m];
+    float dsum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int sgl = t0 - C + 64 * hf + 16 * kt + 4 * g + r;   // key position
+        const bool ok = tq < L && sgl >= 0 && sgl <= tq && sgl > tq - a.window;
+        const float p = ok ? exp_2(z[kt][r] * sl2 - lse2) : 0.f;
+        z[kt][r] = p;
+        dp[kt][r] *= a.alpha;
+        dsum += p * dp[kt][r];
+      }
+    dsum = xgroup_sum(dsum);
+    if (g == 0) sDh[hf * 64 + 16 * qt + m] = dsum;
+    f32x4 zs = zero4();
+    if (hf == 0 && a.n_meta > 0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int col = 8 * g + 32 * e;
+        zs = M::mma(M::load(sMu + m * LD + col), M::load(sQ + (16 * qt + m) * LD + col), zs);
+      }
+    }
+    __syncthreads();
+
+    // ---- dS = P (alpha dP - D), alpha P, sink dZ = -P D into LDS ----
+    {
+      const float Dt = sDh[16 * qt + m] + sDh[64 + 16 * qt + m];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        float ds4[4], pa4[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          ds4[r] = z[kt][r] * (dp[kt][r] - Dt);
+          pa4[r] = z[kt][r] * a.alpha;
+        }
+        const int off = (16 * qt + m) * LD + 64 * hf + 16 * kt + 4 * g;
+        st8(sDS + off, pack4(ds4));
+        st8(sP + off, pack4(pa4));
+      }
+      if (hf == 0) {
+        float zv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          zv[r] = (4 * g + r < a.n_meta && tq < L) ? -exp_2(zs[r] * sl2 - lse2) * Dt : 0.f;
+        st8(sZs + (16 * qt + m) * Lay::LDZ + 4 * g, pack4(zv));
+      }
+    }
+    __syncthreads();
+
+    // ---- dq of chunk c: dq^T[d][t] = scale (K^T dS^T + mu^T dZs^T), the
+    // wavefront's query tile qt and dims 64 hf .. + 63 ----
+    {
+      f32x4 o[4];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) o[dt] = zero4();
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const M::frag b = M::load(sDS + (16 * qt + m) * LD + 8 * g + 32 * e);   // dS[t][s], s = 8g + 32e ..
+        const T* kb = e < 2 ? sKp : sKc;                                        // keys c - 1, then c
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+          o[dt] = M::mma(frag_tr(kb + 64 * hf + 16 * dt, LD, 8 * g + 32 * (e & 1), m), b, o[dt]);
+      }
+      if (a.n_meta > 0) {
+        // sinks 8g .. 8g + 7 for g < 2; the other lane groups add zeros
+        M::frag b = M::load(sZs + (16 * qt + m) * Lay::LDZ + 8 * (g & 1));
+        if (g >= 2) b = M::zero();
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+          o[dt] = M::mma(frag_tr(sMu + 64 * hf + 16 * dt, LD, 8 * (g & 1), m), b, o[dt]);
+      }
+      if (tq < L) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          float pv4[4], v4[4];
+          unpack4(pq[dt], pv4);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v4[r] = fmaf(o[dt][r], a.scale, pv4[r]);
+          st8(dqg + (size_t)tq * D + 64 * hf + 16 * dt + 4 * g, pack4(v4));
+        }
+      }
+    }
+
+    // ---- dk, dv: keys of chunk c - 1 (second part, then complete) and of
+    // chunk c (first part): dk^T[d][s] = Q^T dS, dv^T[d][s] = dY^T (alpha P),
+    // over the chunk's queries (key tile qt, dims 64 hf .. + 63) ----
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      f32x4 ok4[4], ov4[4];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) ok4[dt] = ov4[dt] = zero4();
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int k0 = 8 * g + 32 * e;   // queries
+        const M::frag bs = frag_tr(sDS + 64 * half + 16 * qt, LD, k0, m);
+        const M::frag bp = frag_tr(sP + 64 * half + 16 * qt, LD, k0, m);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          ok4[dt] = M::mma(frag_tr(sQ + 64 * hf + 16 * dt, LD, k0, m), bs, ok4[dt]);
+          ov4[dt] = M::mma(frag_tr(sY + 64 * hf + 16 * dt, LD, k0, m), bp, ov4[dt]);
+        }
+      }
+      if (half == 0) {
+        // chunk c - 1 complete: its first part (ck, cv) plus this one
+        if (c > 0 && sk < L) {
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            float pk4[4], pv4[4], k4[4], v4[4];
+            unpack4(pk[dt], pk4);
+            unpack4(pv[dt], pv4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              k4[r] = fmaf(ck[dt][r] + ok4[dt][r], a.scale, pk4[r]);
+              v4[r] = cv[dt][r] + ov4[dt][r] + pv4[r];
+            }
+            const size_t off = (size_t)sk * D + 64 * hf + 16 * dt + 4 * g;
+            st8(dkg + off, pack4(k4));
+            st8(dvg + off, pack4(v4));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          ck[dt] = ok4[dt];
+          cv[dt] = ov4[dt];
+        }
+      }
+    }
+
+    // ---- sink-key partials of chunk c: dmu^T[d][i] = scale Q^T dZs, dims
+    // 16 w .. + 15 ----
+    if (a.n_meta > 0) {
+      f32x4 o = zero4();
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int k0 = 8 * g + 32 * e;
+        o = M::mma(frag_tr(sQ + 16 * w, LD, k0, m), frag_tr(sZs, Lay::LDZ, k0, m), o);
+      }
+      if (m < a.n_meta) {
+        float* part = a.ws_dmu + ((size_t)bh * nc + c) * a.n_meta * D;
+        *reinterpret_cast<float4*>(part + (size_t)m * D + 16 * w + 4 * g) =
+            make_float4(o[0] * a.scale, o[1] * a.scale, o[2] * a.scale, o[3] * a.scale);
+      }
+    }
+    __syncthreads();
+
+    // ---- the next chunk's rows into the freed tiles ----
+    if (more) {
+      store_rows(sQ, nq);
+      store_rows(sY, ny);
+      store_rows(sKp, nk);
+      store_rows(sVp, nv);
+      if (tid < 64) sLse[tid] = nls;
+    }
+    __syncthreads();
+  }
+  // the last chunk's dk, dv: its own queries' part is all there is
+  {
+    asm volatile("" : "+v"(l), "+v"(m), "+v"(g));
+    const int sk = (nc - 1) * C + 16 * qt + m;
+    if (sk < L) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const size_t off = (size_t)sk * D + 64 * hf + 16 * dt + 4 * g;
+        float pk4[4], pv4[4], k4[4], v4[4];
+        unpack4(ld8(dkg + off), pk4);
+        unpack4(ld8(dvg + off), pv4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          k4[r] = fmaf(ck[dt][r], a.scale, pk4[r]);
+          v4[r] = cv[dt][r] + pv4[r];
+        }
+        st8(dkg + off, pack4(k4));
+        st8(dvg + off, pack4(v4));
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // 6. dmeta[h][i][d] = sum over batch rows and chunks of the partials (fixed order)
 // ---------------------------------------------------------------------------
 // Block (x, h) sums outputs o = 64x .. 64x + 63: thread (o, part) adds the
@@ -2279,32 +2592,37 @@ hipError_t launch_bwd_t(BwdArgs a, hipStream_t st) {
       }
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    // 3, 4. anchor, query and key side: the full chunks in one launch each,
-    // a ragged last chunk range-checked in its own (after the walk: added to
-    // the gated parts; otherwise written alone, the gate kernel adds its own)
-    constexpr bool ACC = WALK;
-    typedef AqLayout<T, D> AQ;
-    static_assert(AQ::TOTAL <= 80 * 1024, "LDS: two workgroups per CU");
-    typedef AkLayout<T, D> AK;
-    static_assert(AK::TOTAL <= 80 * 1024, "LDS: two workgroups per CU");
-    if ((e = set_lds(&bwd_anchor_q_kernel<T, D, true, ACC>, AQ::TOTAL)) != hipSuccess) return e;
-    if ((e = set_lds(&bwd_anchor_q_kernel<T, D, false, ACC>, AQ::TOTAL)) != hipSuccess) return e;
-    if ((e = set_lds(&bwd_anchor_k_kernel<T, D, true, ACC>, AK::TOTAL)) != hipSuccess) return e;
-    if ((e = set_lds(&bwd_anchor_k_kernel<T, D, false, ACC>, AK::TOTAL)) != hipSuccess) return e;
-    if (nfull > 0)
-      hipLaunchKernelGGL((bwd_anchor_q_kernel<T, D, false, ACC>), dim3(8 * groups * nfull), dim3(256), AQ::TOTAL, st, a,
-                         0, nfull);
-    if (nfull < nc)
-      hipLaunchKernelGGL((bwd_anchor_q_kernel<T, D, true, ACC>), dim3(8 * groups), dim3(256), AQ::TOTAL, st, a, nfull,
-                         1);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (nfull > 0)
-      hipLaunchKernelGGL((bwd_anchor_k_kernel<T, D, false, ACC>), dim3(8 * groups * nfull), dim3(256), AK::TOTAL, st, a,
-                         0, nfull);
-    if (nfull < nc)
-      hipLaunchKernelGGL((bwd_anchor_k_kernel<T, D, true, ACC>), dim3(8 * groups), dim3(256), AK::TOTAL, st, a, nfull,
-                         1);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if constexpr (WALK) {
+      // 4. the anchor branch, a forward walk per head (added to the gated parts)
+      static_assert(AwLayout::TOTAL <= 160 * 1024, "LDS");
+      if ((e = set_lds(&bwd_anchor_walk_kernel, AwLayout::TOTAL)) != hipSuccess) return e;
+      hipLaunchKernelGGL(bwd_anchor_walk_kernel, dim3(a.BH), dim3(512), AwLayout::TOTAL, st, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else {
+      // 3, 4. anchor, query and key side: the full chunks in one launch each,
+      // a ragged last chunk range-checked in its own (written alone, the gate
+      // kernel adds its own)
+      typedef AqLayout<T, D> AQ;
+      static_assert(AQ::TOTAL <= 80 * 1024, "LDS: two workgroups per CU");
+      typedef AkLayout<T, D> AK;
+      static_assert(AK::TOTAL <= 80 * 1024, "LDS: two workgroups per CU");
+      if ((e = set_lds(&bwd_anchor_q_kernel<T, D, true>, AQ::TOTAL)) != hipSuccess) return e;
+      if ((e = set_lds(&bwd_anchor_q_kernel<T, D, false>, AQ::TOTAL)) != hipSuccess) return e;
+      if ((e = set_lds(&bwd_anchor_k_kernel<T, D, true>, AK::TOTAL)) != hipSuccess) return e;
+      if ((e = set_lds(&bwd_anchor_k_kernel<T, D, false>, AK::TOTAL)) != hipSuccess) return e;
+      if (nfull > 0)
+        hipLaunchKernelGGL((bwd_anchor_q_kernel<T, D, false>), dim3(8 * groups * nfull), dim3(256), AQ::TOTAL, st, a,
+                           0, nfull);
+      if (nfull < nc)
+        hipLaunchKernelGGL((bwd_anchor_q_kernel<T, D, true>), dim3(8 * groups), dim3(256), AQ::TOTAL, st, a, nfull, 1);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if (nfull > 0)
+        hipLaunchKernelGGL((bwd_anchor_k_kernel<T, D, false>), dim3(8 * groups * nfull), dim3(256), AK::TOTAL, st, a,
+                           0, nfull);
+      if (nfull < nc)
+        hipLaunchKernelGGL((bwd_anchor_k_kernel<T, D, true>), dim3(8 * groups), dim3(256), AK::TOTAL, st, a, nfull, 1);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     // 5. gated branch and outputs (the per-chunk kernel)
     if constexpr (!WALK) {
       if (a.gate_logit) {
