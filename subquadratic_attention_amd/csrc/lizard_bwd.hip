@@ -2099,6 +2099,49 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
 // g in step e (both operands alike), so that fragment reads of the 288-byte
 // token rows take lane groups 16 bytes apart and transposing reads take rows
 // 8 apart, both free of LDS bank conflicts at that row stride.
+// 4 x 4 transpose of 4-register blocks over the four 16-lane groups of a
+// wavefront: on return, block j of lane group g holds what block g of lane
+// group j held.  (gfx950 lane swaps: permlane32 exchanges the upper 32 lanes
+// of its first operand with the lower 32 of its second, permlane16 the odd
+// 16-lane rows of the first with the even rows of the second.)
+__device__ __forceinline__ void xgroup_transpose(f32x4 (&x)[4]) {
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[b][r]), __float_as_uint(x[b + 2][r]), false, false);
+      x[b][r] = __uint_as_float(p[0]);
+      x[b + 2][r] = __uint_as_float(p[1]);
+    }
+#pragma unroll
+  for (int b = 0; b < 4; b += 2)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[b][r]), __float_as_uint(x[b + 1][r]), false, false);
+      x[b][r] = __uint_as_float(p[0]);
+      x[b + 1][r] = __uint_as_float(p[1]);
+    }
+}
+
+// A row's 16 consecutive values 16g .. 16g + 15 of a 64-value half: what
+// the transposed output blocks hold (block j, value r: 16g + 4j + r), plus
+// the 16 values `in` as bf16, scaled by `sc`, rounded and stored.
+__device__ __forceinline__ void add_store16(bf16* dst, const f32x4 (&x)[4], float sc, const uint4 (&in)[2]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float lo[4], hi[4], a4[4], b4[4];
+    unpack4(make_uint2(in[h].x, in[h].y), lo);
+    unpack4(make_uint2(in[h].z, in[h].w), hi);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      a4[r] = fmaf(x[2 * h][r], sc, lo[r]);
+      b4[r] = fmaf(x[2 * h + 1][r], sc, hi[r]);
+    }
+    const uint2 pa = pack4(a4), pb = pack4(b4);
+    *reinterpret_cast<uint4*>(dst + 8 * h) = make_uint4(pa.x, pa.y, pb.x, pb.y);
+  }
+}
+
 struct AwLayout {
   static constexpr int D = 128;
   static constexpr int LD = D + 16;                   // [64][LD] bf16 token tiles
@@ -2223,13 +2266,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
     const float nls = more ? load_lse(c + 1) : 0.f;
     const int tq = t0 + 16 * qt + m;               // dq row of this lane
     const int sk = t0 - C + 16 * qt + m;           // dk, dv row (chunk c - 1) of this lane
-    uint2 pq[4], pk[4], pv[4];
+    // (the lane's row, values 64 hf + 16 g .. + 15: the gradient blocks
+    // are transposed over the lane groups before they are added and stored)
+    const int gcol = 64 * hf + 16 * g;
+    uint4 pq[2], pk[2], pv[2];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const int col = 64 * hf + 16 * dt + 4 * g;
-      pq[dt] = tq < L ? ld8(dqg + (size_t)tq * D + col) : make_uint2(0u, 0u);
-      pk[dt] = c > 0 ? ld8(dkg + (size_t)(c > 0 ? sk : 0) * D + col) : make_uint2(0u, 0u);
-      pv[dt] = c > 0 ? ld8(dvg + (size_t)(c > 0 ? sk : 0) * D + col) : make_uint2(0u, 0u);
+    for (int h = 0; h < 2; ++h) {
+      pq[h] = tq < L ? ld16(dqg + (size_t)tq * D + gcol + 8 * h) : make_uint4(0u, 0u, 0u, 0u);
+      pk[h] = c > 0 ? ld16(dkg + (size_t)(c > 0 ? sk : 0) * D + gcol + 8 * h) : make_uint4(0u, 0u, 0u, 0u);
+      pv[h] = c > 0 ? ld16(dvg + (size_t)(c > 0 ? sk : 0) * D + gcol + 8 * h) : make_uint4(0u, 0u, 0u, 0u);
     }
 
     // ---- scores: keys of chunk c - 1 (hf = 0) or c (hf = 1) against the
@@ -2322,16 +2367,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
         for (int dt = 0; dt < 4; ++dt)
           o[dt] = M::mma(frag_tr(sMu + 64 * hf + 16 * dt, LD, 8 * (g & 1), m), b, o[dt]);
       }
-      if (tq < L) {
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          float pv4[4], v4[4];
-          unpack4(pq[dt], pv4);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) v4[r] = fmaf(o[dt][r], a.scale, pv4[r]);
-          st8(dqg + (size_t)tq * D + 64 * hf + 16 * dt + 4 * g, pack4(v4));
-        }
-      }
+      xgroup_transpose(o);
+      if (tq < L) add_store16(dqg + (size_t)tq * D + gcol, o, a.scale, pq);
     }
 
     // ---- dk, dv: keys of chunk c - 1 (second part, then complete) and of
@@ -2355,21 +2392,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
       }
       if (half == 0) {
         // chunk c - 1 complete: its first part (ck, cv) plus this one
-        if (c > 0 && sk < L) {
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt) {
-            float pk4[4], pv4[4], k4[4], v4[4];
-            unpack4(pk[dt], pk4);
-            unpack4(pv[dt], pv4);
+        for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              k4[r] = fmaf(ck[dt][r] + ok4[dt][r], a.scale, pk4[r]);
-              v4[r] = cv[dt][r] + ov4[dt][r] + pv4[r];
-            }
-            const size_t off = (size_t)sk * D + 64 * hf + 16 * dt + 4 * g;
-            st8(dkg + off, pack4(k4));
-            st8(dvg + off, pack4(v4));
+          for (int r = 0; r < 4; ++r) {
+            ok4[dt][r] += ck[dt][r];
+            ov4[dt][r] += cv[dt][r];
           }
+        xgroup_transpose(ok4);
+        xgroup_transpose(ov4);
+        if (c > 0 && sk < L) {
+          add_store16(dkg + (size_t)sk * D + gcol, ok4, a.scale, pk);
+          add_store16(dvg + (size_t)sk * D + gcol, ov4, 1.f, pv);
         }
       } else {
 #pragma unroll
@@ -2411,21 +2445,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
   {
     asm volatile("" : "+v"(l), "+v"(m), "+v"(g));
     const int sk = (nc - 1) * C + 16 * qt + m;
+    const size_t off = (size_t)(sk < L ? sk : 0) * D + 64 * hf + 16 * g;
+    xgroup_transpose(ck);
+    xgroup_transpose(cv);
     if (sk < L) {
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const size_t off = (size_t)sk * D + 64 * hf + 16 * dt + 4 * g;
-        float pk4[4], pv4[4], k4[4], v4[4];
-        unpack4(ld8(dkg + off), pk4);
-        unpack4(ld8(dvg + off), pv4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          k4[r] = fmaf(ck[dt][r], a.scale, pk4[r]);
-          v4[r] = cv[dt][r] + pv4[r];
-        }
-        st8(dkg + off, pack4(k4));
-        st8(dvg + off, pack4(v4));
-      }
+      const uint4 pk[2] = {ld16(dkg + off), ld16(dkg + off + 8)};
+      const uint4 pv[2] = {ld16(dvg + off), ld16(dvg + off + 8)};
+      add_store16(dkg + off, ck, a.scale, pk);
+      add_store16(dvg + off, cv, 1.f, pv);
     }
   }
 }
