@@ -89,7 +89,11 @@ struct FwdLayout {
   // diagonal (set in the operand step, read in the next score step; not in
   // the A staging the totals share, which the score step writes)
   static constexpr int OFF_WIDE = OFF_META + N * a16(16 * LDK * (int)sizeof(T));
-  static constexpr int TOTAL = OFF_WIDE + N * 16;
+  // the states-only pass: the chunk-start state in row-major order [D][LDSS],
+  // staged for whole-row global stores
+  static constexpr int LDSS = DV + PAD;
+  static constexpr int OFF_SS = a16(OFF_WIDE + N * 16);
+  static constexpr int TOTAL = OFF_SS + (STATES ? a16(D * LDSS * (int)sizeof(T)) : 0);
   static_assert(STATES || 64 * LDE * 4 <= OFF_KHT - OFF_KP, "beta fits over sKp and sQe");
   static_assert(!STAGE_A || 8 * D * 4 <= A_BYTES, "wide-span totals fit over the A staging");
 };
@@ -182,6 +186,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(STATES ? 4 
   float* sBexp = reinterpret_cast<float*>(smem + Lay::OFF_BEXP);
   float* sSc = reinterpret_cast<float*>(smem + Lay::OFF_SC);
   T* sMeta = reinterpret_cast<T*>(smem + Lay::OFF_META);
+  T* sSS = reinterpret_cast<T*>(smem + Lay::OFF_SS);               // states-only pass
 
   // ---- block -> (b*h, value slice, segment); the blocks of one head share an XCD ----
   const int x = blockIdx.x;
@@ -620,9 +625,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(STATES ? 4 
               }
           }
         }
-        if constexpr (KEEP_STATES) {
-          // chunk-start state for the backward pass: S_cc[i][j], row-major
-          // (the states-only pass, or a training forward that keeps them)
+        if constexpr (STATES) {
+          // chunk-start state for the backward pass: S_cc[i][j] into LDS,
+          // row-major; the other wavefronts store whole rows of it during
+          // the next interval
+  #pragma unroll
+          for (int rt = 0; rt < DPL; ++rt)
+  #pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+  #pragma unroll
+              for (int r = 0; r < 4; ++r)
+                sSS[(16 * (DPL * I + rt) + 4 * g_lane + r) * Lay::LDSS + 16 * ct + m_lane] = from_f32<T>(acc[rt][ct][r]);
+        } else if constexpr (KEEP_STATES) {
+          // chunk-start state S_cc[i][j], row-major (a training forward that
+          // keeps them for the backward pass)
           const int ncs = (L + C - 1) / C;
           T* sg = reinterpret_cast<T*>(a.states) + ((size_t)bh * ncs + cc) * D * D + j0;
   #pragma unroll
@@ -949,7 +965,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(STATES ? 4 
 
       // ---- interval 1 ----
       if constexpr (STATES) {
-        if constexpr (GATE) carry(vcur, m_lane, g_lane);
+        if constexpr (GATE) {
+          carry(vcur, m_lane, g_lane);
+        } else {
+          // S_c (staged by the gate wavefronts) to memory: 16-byte pieces of
+          // whole rows, threads 0..255
+          constexpr int VPR = DV / EPV;
+          const int tq = opaque(threadIdx.x);
+          T* sg = reinterpret_cast<T*>(a.states) + ((size_t)bh * nc + c) * D * D + j0;
+  #pragma unroll
+          for (int v = tq; v < D * VPR; v += 256) {
+            const int i = v / VPR, col = (v % VPR) * EPV;
+            *reinterpret_cast<uint4*>(sg + (size_t)i * D + col) = *reinterpret_cast<const uint4*>(sSS + i * Lay::LDSS + col);
+          }
+        }
       } else if constexpr (GATE) {
         gate_part(Ic);
       } else {
@@ -1248,6 +1277,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   constexpr bool SEG = MODE == kSeg;
   typedef FwdLayout<T, D, DV, STATES> Lay;
   static_assert(Lay::TOTAL <= 160 * 1024, "LDS budget");
+  static_assert(!STATES || Lay::TOTAL <= 80 * 1024, "LDS: the states-only pass runs two workgroups per CU");
   static_assert(D == 128 || (D == 64 && sizeof(T) == 2) || (D == 64 && DV == 32), "shapes");
   const int smem = Lay::TOTAL;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lizard_fwd_kernel<T, D, DV, STATES, LOGIT, MODE>),
