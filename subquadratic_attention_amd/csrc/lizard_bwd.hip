@@ -2040,15 +2040,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
     for (int h = 0; h < GPW; ++h) {
       const int dg = GPW * w + h;
+      // (scheduled two products at a time: their operand reads overlap the
+      // previous pair's matrix work without holding more registers)
 #pragma unroll
       for (int it = 0; it < 8; ++it) {
         X[h][it] = mma_fm(X[h][it], sQeT, 16 * it + m, sOT, 16 * dg + m, g);
-        __builtin_amdgcn_sched_barrier(0);
+        if (it & 1) __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int jt = 0; jt < 8; ++jt) {
         Y[h][jt] = mma_fm(Y[h][jt], sOT, 16 * jt + m, sQeT, 16 * dg + m, g);
-        __builtin_amdgcn_sched_barrier(0);
+        if (jt & 1) __builtin_amdgcn_sched_barrier(0);
       }
       if (cmid) {
 #pragma unroll
@@ -2083,22 +2085,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
   }
 }
 
-// ---------------------------------------------------------------------------
-// 5b. anchor branch, both sides in one forward walk over each head's chunks
-// (bf16, d = 128)
-// ---------------------------------------------------------------------------
-// At chunk c the window block row of the chunk's queries (keys of chunks c-1
-// and c) gives P, dP, D_t and dS once; from it come dq of chunk c
-// (complete), the second and last part of dk, dv of chunk c-1 (the first came
-// from its own queries one chunk earlier and waited in registers) and the
-// first part of dk, dv of chunk c.  Each chunk's q, k, v, dY are read once
-// and each gradient row is read and written once (added to the gated part
-// the reverse walk wrote).
-//
-// Lane orders: the contraction runs over values 8g + 32e .. + 7 of lane group
-// g in step e (both operands alike), so that fragment reads of the 288-byte
-// token rows take lane groups 16 bytes apart and transposing reads take rows
-// 8 apart, both free of LDS bank conflicts at that row stride.
 // 4 x 4 transpose of 4-register blocks over the four 16-lane groups of a
 // wavefront: on return, block j of lane group g holds what block g of lane
 // group j held.  (gfx950 lane swaps: permlane32 exchanges the upper 32 lanes
@@ -2142,6 +2128,22 @@ __device__ __forceinline__ void add_store16(bf16* dst, const f32x4 (&x)[4], floa
   }
 }
 
+// ---------------------------------------------------------------------------
+// 5b. anchor branch, both sides in one forward walk over each head's chunks
+// (bf16, d = 128)
+// ---------------------------------------------------------------------------
+// At chunk c the window block row of the chunk's queries (keys of chunks c-1
+// and c) gives P, dP, D_t and dS once; from it come dq of chunk c
+// (complete), the second and last part of dk, dv of chunk c-1 (the first came
+// from its own queries one chunk earlier and waited in registers) and the
+// first part of dk, dv of chunk c.  Each chunk's q, k, v, dY are read once
+// and each gradient row is read and written once (added to the gated part
+// the reverse walk wrote).
+//
+// Lane orders: the contraction runs over values 8g + 32e .. + 7 of lane group
+// g in step e (both operands alike), so that fragment reads of the 288-byte
+// token rows take lane groups 16 bytes apart and transposing reads take rows
+// 8 apart, both free of LDS bank conflicts at that row stride.
 struct AwLayout {
   static constexpr int D = 128;
   static constexpr int LD = D + 16;                   // [64][LD] bf16 token tiles
