@@ -2246,6 +2246,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
   f32x4 ck[4], cv[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) ck[dt] = cv[dt] = zero4();
+  // the head's sink-key gradient over all its chunks (sink m, dims 16 w + 4 g + r)
+  f32x4 dmu = zero4();
 
   for (int c = 0; c < nc; ++c) {
     asm volatile("" : "+v"(l), "+v"(m), "+v"(g));
@@ -2416,19 +2418,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
       }
     }
 
-    // ---- sink-key partials of chunk c: dmu^T[d][i] = scale Q^T dZs, dims
-    // 16 w .. + 15 ----
+    // ---- sink keys: dmu^T[d][i] += Q^T dZs over the chunk, dims 16 w .. + 15 ----
     if (a.n_meta > 0) {
-      f32x4 o = zero4();
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int k0 = 8 * g + 32 * e;
-        o = M::mma(frag_tr(sQ + 16 * w, LD, k0, m), frag_tr(sZs, Lay::LDZ, k0, m), o);
-      }
-      if (m < a.n_meta) {
-        float* part = a.ws_dmu + ((size_t)bh * nc + c) * a.n_meta * D;
-        *reinterpret_cast<float4*>(part + (size_t)m * D + 16 * w + 4 * g) =
-            make_float4(o[0] * a.scale, o[1] * a.scale, o[2] * a.scale, o[3] * a.scale);
+        dmu = M::mma(frag_tr(sQ + 16 * w, LD, k0, m), frag_tr(sZs, Lay::LDZ, k0, m), dmu);
       }
     }
     __syncthreads();
@@ -2442,6 +2437,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
       if (tid < 64) sLse[tid] = nls;
     }
     __syncthreads();
+  }
+  // the head's sink-key partial (one per head: the reduction over the batch
+  // takes one chunk per head)
+  if (a.n_meta > 0 && m < a.n_meta) {
+    float* part = a.ws_dmu + (size_t)bh * a.n_meta * D;
+    *reinterpret_cast<float4*>(part + (size_t)m * D + 16 * w + 4 * g) =
+        make_float4(dmu[0] * a.scale, dmu[1] * a.scale, dmu[2] * a.scale, dmu[3] * a.scale);
   }
   // the last chunk's dk, dv: its own queries' part is all there is
   {
@@ -2665,8 +2667,10 @@ hipError_t launch_bwd_t(BwdArgs a, hipStream_t st) {
   if (a.n_meta > 0 && a.H > 0) {
     const int nmD = a.n_meta * D;
     if (a.BH > 0 && L > 0) {
+      // (bf16 at d = 128: the anchor walk leaves one partial per head)
+      constexpr bool ONE = sizeof(T) == 2 && D == 128;
       hipLaunchKernelGGL(bwd_dmeta_reduce_kernel, dim3((nmD + 63) / 64, a.H), dim3(256), 0, st, a.ws_dmu, a.dmeta,
-                         a.B, a.H, nc, nmD);
+                         a.B, a.H, ONE ? 1 : nc, nmD);
     } else {
       hipLaunchKernelGGL(bwd_dmeta_reduce_kernel, dim3((nmD + 63) / 64, a.H), dim3(256), 0, st, a.ws_dmu, a.dmeta,
                          0, a.H, 0, nmD);
