@@ -391,13 +391,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(STATES ? 4 
       if constexpr (sizeof(T) == 4) return __builtin_bit_cast(float, u);
       else return __builtin_bit_cast(float, dd == 0 ? (u << 16) : (u & 0xffff0000u));
     };
+    // the natural-log gate of prep row rr, dim dd: loaded, or formed from
+    // the logit by the prefix step; the states-only pass forms it where it is
+    // used instead (the logits take half the registers of the gates, which
+    // that pass, at four wavefronts per SIMD, is short of)
+    auto lg_of = [&](int rr, int dd) __attribute__((always_inline)) -> float {
+      if constexpr (LOGIT && STATES) return log_sigmoid(elem32(xA[rr], dd));
+      else return lgA[rr][dd];
+    };
 
     // ---- prefix sums inside this wavefront's 8 rows (natural-log units; exact
     // for the factorised path, where no single gate is small enough for the
     // 2^-100 floor of the wide-span path) ----
     auto prefix_part = [&]() __attribute__((always_inline)) {
       const int l = opaque(threadIdx.x) & 63;
-      if constexpr (LOGIT) {
+      if constexpr (LOGIT && !STATES) {
   #pragma unroll
         for (int rr = 0; rr < 8; ++rr)
   #pragma unroll
@@ -409,7 +417,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(STATES ? 4 
         float run = 0.f;
   #pragma unroll
         for (int rr = 0; rr < 8; ++rr) {
-          run += lgA[rr][dd];
+          run += lg_of(rr, dd);
           loc[rr][dd] = run;
         }
         tot[dd] = run;
@@ -523,7 +531,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(STATES ? 4 
           float run = 0.f;
   #pragma unroll
           for (int rr = 0; rr < 8; ++rr) {
-            run += log2_gate(lgA[rr][dd]);
+            run += log2_gate(lg_of(rr, dd));
             locc[rr][dd] = run;
           }
           totc[dd] = run;
