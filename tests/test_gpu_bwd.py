@@ -71,11 +71,13 @@ def test_ragged_lengths(gpu_lib, dtype, d, L):
     compare(gpu_bwd(gpu_lib, x, dtype, 64, 0.5), ref_bwd(x, 64, 0.5), dtype, f"L={L}")
 
 
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
 @pytest.mark.parametrize("window,n_meta", [(1, 0), (7, 1), (33, 16), (64, 4)])
-def test_window_and_sinks(gpu_lib, window, n_meta):
-    x = si.custom_inputs(31, 1, 3, 200, 64, n_meta, "f32", with_dy=True, qk_sd=1.0, meta_sd=1.0)
-    log(f"bwd window={window} n_meta={n_meta}")
-    compare(gpu_bwd(gpu_lib, x, "f32", window, 0.7), ref_bwd(x, window, 0.7), "f32", f"w={window} m={n_meta}")
+def test_window_and_sinks(gpu_lib, dtype, d, window, n_meta):
+    # (bf16 at d = 128 runs the anchor walk: every window mask and sink count)
+    x = si.custom_inputs(31, 1, 3, 200, d, n_meta, dtype, with_dy=True, qk_sd=1.0, meta_sd=1.0)
+    log(f"bwd {dtype} d={d} window={window} n_meta={n_meta}")
+    compare(gpu_bwd(gpu_lib, x, dtype, window, 0.7), ref_bwd(x, window, 0.7), dtype, f"w={window} m={n_meta}")
 
 
 @pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
