@@ -34,7 +34,8 @@
 //      in the outputs, and dlog_g: the suffix sums of q*dq - k*dk inside the
 //      chunk plus, for everything after it, rowsum(S_{c+1} * G_{c+1});
 //   6. bwd_dmeta_reduce: sums the sink-key partials over batch and chunks in
-//      a fixed order (deterministic, no float atomics).
+//      a fixed order (deterministic, no float atomics); after the two walks
+//      below, the launch that takes the flagged chunks also does this sum.
 // Kernels 3-5 run the full chunks in one launch and a ragged last chunk in a
 // range-checked launch of its own.  For bf16 at d = 128, two walks over each
 // head's chunks replace kernels 2-5: the reverse walk (5, bf16) writes the
@@ -1439,23 +1440,38 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_kernel(BwdArgs a, int
   gate_chunk<T, D, RAGGED, LOGIT>(a, bh, c + cb);
 }
 
-// The chunks the reverse walk flagged (decay span beyond twice the
-// factorisable limit in some dimension), from G_{c+1} and its transpose the
-// walk wrote for them: a persistent grid, each workgroup scanning every
-// gridDim.x-th flag (uniform per workgroup), range-checked rows.
+// The last launch of the two walks, in two roles by block index.
+// Blocks [0, nflag): the chunks the reverse walk flagged (decay span beyond
+// twice the factorisable limit in some dimension), from G_{c+1} and its
+// transpose the walk wrote for them, added to the anchor parts already in
+// dq, dk, dv (the walk left zeros there): a persistent grid, each
+// workgroup scanning every nflag-th flag (uniform per workgroup),
+// range-checked rows.  Blocks nflag + h: the sink-key gradient of head h,
+// the anchor walk's B partials of the head summed in batch order (a fixed
+// order: deterministic).  One launch instead of two.
 template <typename T, int D, bool LOGIT>
-__global__ __launch_bounds__(D / 16 * 64, 1) void bwd_gate_flagged_kernel(BwdArgs a) {
+__global__ __launch_bounds__(D / 16 * 64, 1) void bwd_tail_kernel(BwdArgs a, int nflag) {
   constexpr int NT = D / 16 * 64;
+  if ((int)blockIdx.x >= nflag) {
+    const int h = blockIdx.x - nflag;
+    const int nmD = a.n_meta * D;
+    for (int o = threadIdx.x; o < nmD; o += NT) {
+      float sum = 0.f;
+      for (int b = 0; b < a.B; ++b) sum += a.ws_dmu[(size_t)(b * a.H + h) * nmD + o];
+      a.dmeta[(size_t)h * nmD + o] = sum;
+    }
+    return;
+  }
   const int nc = (a.L + C - 1) / C;
   const long long n = (long long)a.BH * nc;
-  // the workgroup's flags idx = base + t gridDim.x, one per thread, read
+  // the workgroup's flags idx = base + t nflag, one per thread, read
   // together: the common case (none set) costs one load per thread
-  for (long long base = blockIdx.x; base < n; base += (long long)gridDim.x * NT) {
-    const long long mine = base + (long long)threadIdx.x * gridDim.x;
+  for (long long base = blockIdx.x; base < n; base += (long long)nflag * NT) {
+    const long long mine = base + (long long)threadIdx.x * nflag;
     const int f = mine < n ? a.ws_flag[mine] : 0;
     if (!__syncthreads_or(f)) continue;
     for (int t = 0; t < NT; ++t) {
-      const long long idx = base + (long long)t * gridDim.x;
+      const long long idx = base + (long long)t * nflag;
       if (idx < n && a.ws_flag[idx]) {
         gate_chunk<T, D, true, LOGIT>(a, (int)(idx / nc), (int)(idx % nc));
         __syncthreads();   // the next chunk's operands overwrite this one's in LDS
@@ -2551,6 +2567,8 @@ hipError_t launch_gate(const BwdArgs& a, int nfull, int nc, int groups, hipStrea
 
 template <typename T, int D, int DV>
 hipError_t launch_bwd_t(BwdArgs a, hipStream_t st) {
+  // bf16 at d = 128: two walks over each head's chunks
+  constexpr bool WALK = sizeof(T) == 2 && D == 128;
   const int L = a.L, nc = (L + C - 1) / C;
   const int groups = (a.BH + 7) / 8;
   hipError_t e;
@@ -2584,7 +2602,6 @@ hipError_t launch_bwd_t(BwdArgs a, hipStream_t st) {
       if (e != hipSuccess) return e;
     }
     // the reverse walk carries the state gradients itself (bf16, d = 128)
-    constexpr bool WALK = sizeof(T) == 2 && D == 128;
     if constexpr (!WALK) {
       // 2. state gradients
       if (a.gate_logit)
@@ -2595,8 +2612,8 @@ hipError_t launch_bwd_t(BwdArgs a, hipStream_t st) {
     }
     const int nfull = L / C;
     if constexpr (WALK) {
-      // 3. the reverse walk (gated parts of dq, dk, dv; dlog_g), then the
-      // chunks it left (none for ordinary gates)
+      // 3. the reverse walk (gated parts of dq, dk, dv; dlog_g; zeros in
+      // dq, dk, dv for the chunks it leaves to the last launch)
       const bool logit = a.gate_logit != nullptr;
       static_assert(WalkLayout::TOTAL <= 160 * 1024, "LDS");
       const void* wk = logit ? reinterpret_cast<const void*>(&bwd_walk_kernel<true>)
@@ -2608,26 +2625,29 @@ hipError_t launch_bwd_t(BwdArgs a, hipStream_t st) {
       else
         hipLaunchKernelGGL((bwd_walk_kernel<false>), dim3(a.BH), dim3(512), WalkLayout::TOTAL, st, a);
       if ((e = hipGetLastError()) != hipSuccess) return e;
-      typedef GateLayout<T, D> GL;
-      // one flag per thread: enough workgroups to read every flag at once
-      // (the common case, no chunk flagged, then ends after one load)
-      const long long n = (long long)a.BH * nc;
-      const long long need = (n + GL::NW * 64 - 1) / (GL::NW * 64);
-      const int grid = (int)(need < 256 ? need : 256);
-      if (logit) {
-        if ((e = set_lds(&bwd_gate_flagged_kernel<T, D, true>, GL::TOTAL)) != hipSuccess) return e;
-        hipLaunchKernelGGL((bwd_gate_flagged_kernel<T, D, true>), dim3(grid), dim3(GL::NW * 64), GL::TOTAL, st, a);
-      } else {
-        if ((e = set_lds(&bwd_gate_flagged_kernel<T, D, false>, GL::TOTAL)) != hipSuccess) return e;
-        hipLaunchKernelGGL((bwd_gate_flagged_kernel<T, D, false>), dim3(grid), dim3(GL::NW * 64), GL::TOTAL, st, a);
-      }
-      if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if constexpr (WALK) {
       // 4. the anchor branch, a forward walk per head (added to the gated parts)
       static_assert(AwLayout::TOTAL <= 160 * 1024, "LDS");
       if ((e = set_lds(&bwd_anchor_walk_kernel, AwLayout::TOTAL)) != hipSuccess) return e;
       hipLaunchKernelGGL(bwd_anchor_walk_kernel, dim3(a.BH), dim3(512), AwLayout::TOTAL, st, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      // 5. the chunks the reverse walk flagged (none for ordinary gates) and
+      // the sink-key gradient, in one launch: one flag per thread, enough
+      // workgroups to read every flag at once (the common case, no chunk
+      // flagged, then ends after one load), and one workgroup per head
+      typedef GateLayout<T, D> GL;
+      const long long n = (long long)a.BH * nc;
+      const long long need = (n + GL::NW * 64 - 1) / (GL::NW * 64);
+      const int nflag = (int)(need < 256 ? need : 256);
+      const int grid = nflag + (a.n_meta > 0 ? a.H : 0);
+      if (a.gate_logit) {
+        if ((e = set_lds(&bwd_tail_kernel<T, D, true>, GL::TOTAL)) != hipSuccess) return e;
+        hipLaunchKernelGGL((bwd_tail_kernel<T, D, true>), dim3(grid), dim3(GL::NW * 64), GL::TOTAL, st, a, nflag);
+      } else {
+        if ((e = set_lds(&bwd_tail_kernel<T, D, false>, GL::TOTAL)) != hipSuccess) return e;
+        hipLaunchKernelGGL((bwd_tail_kernel<T, D, false>), dim3(grid), dim3(GL::NW * 64), GL::TOTAL, st, a, nflag);
+      }
       if ((e = hipGetLastError()) != hipSuccess) return e;
     } else {
       // 3, 4. anchor, query and key side: the full chunks in one launch each,
@@ -2667,10 +2687,10 @@ hipError_t launch_bwd_t(BwdArgs a, hipStream_t st) {
   if (a.n_meta > 0 && a.H > 0) {
     const int nmD = a.n_meta * D;
     if (a.BH > 0 && L > 0) {
-      // (bf16 at d = 128: the anchor walk leaves one partial per head)
-      constexpr bool ONE = sizeof(T) == 2 && D == 128;
-      hipLaunchKernelGGL(bwd_dmeta_reduce_kernel, dim3((nmD + 63) / 64, a.H), dim3(256), 0, st, a.ws_dmu, a.dmeta,
-                         a.B, a.H, ONE ? 1 : nc, nmD);
+      // (bf16 at d = 128: the last launch of the walks has summed them)
+      if constexpr (!WALK)
+        hipLaunchKernelGGL(bwd_dmeta_reduce_kernel, dim3((nmD + 63) / 64, a.H), dim3(256), 0, st, a.ws_dmu, a.dmeta,
+                           a.B, a.H, nc, nmD);
     } else {
       hipLaunchKernelGGL(bwd_dmeta_reduce_kernel, dim3((nmD + 63) / 64, a.H), dim3(256), 0, st, a.ws_dmu, a.dmeta,
                          0, a.H, 0, nmD);

@@ -307,6 +307,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(STATES ? 4 
     float lgA[8][DPL];    // prep rows 8w+rr, dims DPL*l + dd (from xA when the gates come as logits)
     uint32_t xA[8];       // gate logits of those rows: DPL elements packed in 32 bits
     float loc[8][DPL];    // their prefix inside the wavefront's 8 rows
+    // the states-only pass with log-gates keeps the gates instead and forms
+    // the prefix again where the operands use it (the same sums in the same
+    // order): holding both had spilled registers at four wavefronts per SIMD
+    constexpr bool REPREFIX = STATES && !LOGIT;
     uint32_t kA[8];       // the same rows' keys: DPL elements packed in 32 bits
     uint32_t qA[8];       // ... and queries
     uint32_t vA[VR];      // values: rows VR*vs + rr, columns VC*vj.. packed in 32 bits
@@ -418,7 +422,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(STATES ? 4 
   #pragma unroll
         for (int rr = 0; rr < 8; ++rr) {
           run += lg_of(rr, dd);
-          loc[rr][dd] = run;
+          if constexpr (!REPREFIX) loc[rr][dd] = run;
         }
         tot[dd] = run;
       }
@@ -501,13 +505,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(STATES ? 4 
             off[dd] = fmaf(off[dd], kLog2e, -r);
           }
         }
+        float lrun[DPL] = {};   // the prefix formed again (REPREFIX)
   #pragma unroll
         for (int rr = 0; rr < 8; ++rr) {
           const int s = 8 * w + rr;
           float qe[DPL], kp[DPL];
   #pragma unroll
           for (int dd = 0; dd < DPL; ++dd) {
-            const float beta = fmaf(loc[rr][dd], kLog2e, off[dd]);
+            if constexpr (REPREFIX) lrun[dd] += lgA[rr][dd];
+            const float beta = fmaf(REPREFIX ? lrun[dd] : loc[rr][dd], kLog2e, off[dd]);
             kp[dd] = elem32(kA[rr], dd) * exp_2(-beta);
             kh[dd][rr] = kp[dd] * ehr[dd];
             qe[dd] = STATES ? 0.f : elem32(qA[rr], dd) * exp_2(beta);
@@ -981,8 +987,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(STATES ? 4 
           constexpr int VPR = DV / EPV;
           const int tq = opaque(threadIdx.x);
           T* sg = reinterpret_cast<T*>(a.states) + ((size_t)bh * nc + c) * D * D + j0;
+          static_assert(D * VPR % 256 == 0, "whole passes of threads 0..255");
   #pragma unroll
-          for (int v = tq; v < D * VPR; v += 256) {
+          for (int it = 0; it < D * VPR / 256; ++it) {
+            const int v = tq + 256 * it;
             const int i = v / VPR, col = (v % VPR) * EPV;
             *reinterpret_cast<uint4*>(sg + (size_t)i * D + col) = *reinterpret_cast<const uint4*>(sSS + i * Lay::LDSS + col);
           }
