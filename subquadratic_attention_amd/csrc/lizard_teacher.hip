@@ -17,9 +17,12 @@
 // and walks the key blocks up to the diagonal.  Per key block the keys and
 // the transposed values are staged in LDS; S^T tiles (keys x queries) come
 // from MFMA with the queries as the B operand, the online softmax keeps one
-// running maximum and sum per query in every lane of its column, P goes
-// through LDS (per wavefront) into the O^T = V^T P^T product, whose
-// accumulators hold O[query m][j = 16jt + 4g + r].
+// running maximum and sum per query in every lane of its column, and P goes
+// into the O^T = V^T P^T product, whose accumulators hold O[query m][j =
+// 16jt + 4g + r].  In bf16, P stays in registers: the S^T tiles take their
+// key rows in an order under which the scores a lane holds are exactly the
+// keys its lane group contracts over in the product (see key_of below); in
+// fp32 it goes through LDS (per wavefront).
 #include "lizard_common.hpp"
 #include "lizard_kernels.hpp"
 
@@ -37,7 +40,7 @@ struct TeacherLayout {
   static constexpr int OFF_K = 0;                       // + b * BUF for buffer b
   static constexpr int OFF_V = 64 * LDK * (int)sizeof(T);
   static constexpr int OFF_P = 2 * BUF;
-  static constexpr int TOTAL = OFF_P + 4 * 16 * LDP * (int)sizeof(T);
+  static constexpr int TOTAL = OFF_P + (sizeof(T) == 2 ? 0 : 4 * 16 * LDP * (int)sizeof(T));
 };
 
 }  // namespace
@@ -60,6 +63,14 @@ __global__ __launch_bounds__(256) void teacher_attn_kernel(TeacherArgs a) {
   const int bh = x % a.BH;
   const int qb = nqb - 1 - x / a.BH;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
+  // the key (within the block) of row rho of S^T tile kt.  bf16: tile kt =
+  // 2e + h takes keys 32e + 8(rho / 4) + 4h + rho % 4, so lane group g's
+  // output rows 4g .. 4g + 3 of tiles 2e and 2e + 1 are keys 32e + 8g .. + 7,
+  // its operand run in the product's contraction step e; fp32: row order
+  auto key_of = [](int kt, int rho) __attribute__((always_inline)) -> int {
+    if constexpr (sizeof(T) == 2) return 32 * (kt >> 1) + 8 * (rho >> 2) + 4 * (kt & 1) + (rho & 3);
+    else return 16 * kt + rho;
+  };
   const T* qg = reinterpret_cast<const T*>(a.q) + (size_t)bh * L * D;
   const T* kg = reinterpret_cast<const T*>(a.k) + (size_t)bh * L * D;
   const T* vg = reinterpret_cast<const T*>(a.v) + (size_t)bh * L * D;
@@ -165,11 +176,11 @@ __global__ __launch_bounds__(256) void teacher_attn_kernel(TeacherArgs a) {
     const T* sVt = reinterpret_cast<const T*>(smem + (kb & 1) * Lay::BUF + Lay::OFF_V);
     if (kb < qb) load_block(kb + 1);
 
-    // ---- S^T tiles: keys 16kt + 4g + r (rows) x query tq (column m) ----
+    // ---- S^T tiles: keys key_of(kt, 4g + r) (rows) x query tq (column m) ----
     f32x4 z[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      const T* kp = sK + (16 * kt + m) * Lay::LDK + g * (D / 4);
+      const T* kp = sK + key_of(kt, m) * Lay::LDK + g * (D / 4);
       z[kt] = zero4();
 #pragma unroll
       for (int e = 0; e < NF; ++e) z[kt] = M::mma(M::load(kp + e * M::KPL), qf[e], z[kt]);
@@ -182,7 +193,7 @@ __global__ __launch_bounds__(256) void teacher_attn_kernel(TeacherArgs a) {
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int s = k0 + 16 * kt + 4 * g + r;
+          const int s = k0 + key_of(kt, 4 * g + r);
           z[kt][r] = s <= tq && s < L ? z[kt][r] : -INFINITY;
         }
     }
@@ -196,27 +207,51 @@ __global__ __launch_bounds__(256) void teacher_attn_kernel(TeacherArgs a) {
     const float corr = exp_2(mrun - mnew);  // 0 on the first block (mrun = -inf)
     mrun = mnew;
     float ls = 0.f;
+    float p[4][4];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      float p[4];
+    for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p[r] = exp_2(fmaf(z[kt][r], a.scale_log2, -mnew));
-        ls += p[r];
+        p[kt][r] = exp_2(fmaf(z[kt][r], a.scale_log2, -mnew));
+        ls += p[kt][r];
       }
-      store_pack<T, 4>(sPw + m * Lay::LDP + 16 * kt + 4 * g, p);
+    if constexpr (sizeof(T) != 2) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) store_pack<T, 4>(sPw + m * Lay::LDP + 16 * kt + 4 * g, p[kt]);
     }
     lrun = lrun * corr + xgroup_sum(ls);
 #pragma unroll
     for (int jt = 0; jt < NJT; ++jt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) oacc[jt][r] *= corr;
-    wave_lds_sync();
 
     // ---- O^T[j][tq] += sum over the block's keys of V^T[j][s] P[tq][s] ----
+    if constexpr (sizeof(T) == 2) {
+      // contraction step e over keys 32e .. 32e + 31: lane group g takes
+      // keys 32e + 8g .. + 7, which are the scores of tiles 2e and 2e + 1
+      // this lane holds
+      frag pf[2];
 #pragma unroll
-    for (int jt = 0; jt < NJT; ++jt)
-      oacc[jt] = mma_rows<T, 64>(oacc[jt], sVt + (16 * jt + m) * Lay::LDV + g * 16, sPw + m * Lay::LDP + g * 16);
+      for (int e = 0; e < 2; ++e) {
+        bf16x8 f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          f[r] = static_cast<bf16>(p[2 * e][r]);
+          f[4 + r] = static_cast<bf16>(p[2 * e + 1][r]);
+        }
+        pf[e] = f;
+      }
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          oacc[jt] = M::mma(M::load(sVt + (16 * jt + m) * Lay::LDV + 32 * e + 8 * g), pf[e], oacc[jt]);
+    } else {
+      wave_lds_sync();
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt)
+        oacc[jt] = mma_rows<T, 64>(oacc[jt], sVt + (16 * jt + m) * Lay::LDV + g * 16, sPw + m * Lay::LDP + g * 16);
+    }
     if (kb < qb) store_block((kb + 1) & 1);
     // the next block is in place; this wavefront's P tile is free again
     __syncthreads();
