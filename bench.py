@@ -408,6 +408,40 @@ def bench_decode(sqa, si, reps=3):
     out["tokens4"] = {"T": T, "us_per_token": round(ms_tok * 1e3, 2), "tokens_per_s": round(w.B / (ms_tok * 1e-3), 1),
                       "alg_bytes_per_call": bytes_call,
                       "gbps": round(bytes_call / (T * ms_tok * 1e-3) / 1e9, 1)}
+    # the same 1024 steps recorded once into a HIP graph (torch.cuda.graph)
+    # and replayed: no host launch per token (the positions are kernel
+    # arguments, so a replay repeats the recorded steps from the restored
+    # state); its outputs must equal the eager run's bit for bit
+    y_eager = y.clone()
+    state.copy_(state0)
+    kr.copy_(ring0["k"])
+    vr.copy_(ring0["v"])
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            sqa.lizard_decode_step(L0 + i, dec["q"][i], dec["k"][i], dec["v"][i], dec["log_g"][i], meta, state, kr,
+                                   vr, alpha=w.alpha, y_t=y[i])
+
+    def run_graph():
+        state.copy_(state0)
+        kr.copy_(ring0["k"])
+        vr.copy_(ring0["v"])
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        graph.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    y.fill_(float("nan"))
+    ms_graph = [run_graph() for _ in range(reps + 1)][1:]
+    out["graph"] = {"us_per_step": round(sum(ms_graph) / reps * 1e3, 2), "replays": reps, "steps_per_replay": steps,
+                    "equals_eager_bitwise": bool(torch.equal(y, y_eager))}
+    del graph, y_eager
+    out["graph_b1"] = bench_decode_graph_b1(sqa, reps)
     # back to back last: `reps` runs of the 1024 steps, the mean over all of
     # them (these are the last launches of the one-token kernel)
     prewarm(run_all, PREWARM_MS)
@@ -420,6 +454,70 @@ def bench_decode(sqa, si, reps=3):
     del dec, dec4, y4, pos_all, ring0, y, state, state0, kr, vr, scratch, sink
     torch.cuda.empty_cache()
     return out
+
+
+def bench_decode_graph_b1(sqa, reps, steps=256):
+    """One sequence (B = 1, H = 32, d = 128, window 64, 4 sinks): a decode
+    step moves 5.3 MB, under a microsecond of HBM time, so one host launch
+    per token bounds the eager loop; the same steps as one HIP graph.
+    Seeded synthetic state, rings and tokens (timing only)."""
+    import torch
+
+    g = torch.Generator(device="cuda").manual_seed(20250709)
+    B, H, d, wnd, m = 1, 32, 128, 64, 4
+
+    def rn(*shape, sd=1.0):
+        return torch.randn(*shape, device="cuda", generator=g) * sd
+
+    state0 = rn(B, H, d, d, sd=0.05)
+    kr0 = rn(B, H, wnd, d, sd=0.125).bfloat16()
+    vr0 = rn(B, H, wnd, d, sd=0.125).bfloat16()
+    meta = rn(H, m, d, sd=0.125).bfloat16()
+    q, k, v = (rn(steps, B, H, d, sd=0.125).bfloat16() for _ in range(3))
+    lg = torch.nn.functional.logsigmoid(rn(steps, B, H, d) + 3.0)
+    y = torch.empty((steps, B, H, d), device="cuda", dtype=torch.bfloat16)
+    state, kr, vr = state0.clone(), kr0.clone(), vr0.clone()
+    p0 = 4096
+
+    def launch_all():
+        for i in range(steps):
+            sqa.lizard_decode_step(p0 + i, q[i], k[i], v[i], lg[i], meta, state, kr, vr, alpha=0.5, y_t=y[i])
+
+    def timed(fn):
+        state.copy_(state0)
+        kr.copy_(kr0)
+        vr.copy_(vr0)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    timed(launch_all)
+    eager = [timed(launch_all) for _ in range(reps)]
+    y_eager = y.clone()
+    state.copy_(state0)
+    kr.copy_(kr0)
+    vr.copy_(vr0)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        launch_all()
+    timed(graph.replay)
+    replayed = [timed(graph.replay) for _ in range(reps)]
+    ms_e, ms_g = sum(eager) / reps, sum(replayed) / reps
+    bytes_step = B * H * decode_bytes_per_bh(d, wnd)
+    res = {"workload": "decode B=1 H=32 d=128 window 64, 4 sinks (seeded synthetic)", "steps": steps,
+           "alg_bytes_per_step": bytes_step, "eager_us_per_step": round(ms_e * 1e3, 2),
+           "graph_us_per_step": round(ms_g * 1e3, 2), "graph_speedup": round(ms_e / ms_g, 2),
+           "graph_gbps": round(bytes_step / (ms_g * 1e-3) / 1e9, 1),
+           "equals_eager_bitwise": bool(torch.equal(y, y_eager))}
+    del graph, q, k, v, lg, y, y_eager, state, kr, vr, state0, kr0, vr0
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_bwd(sqa, si, steps, warmup, logit=False):
