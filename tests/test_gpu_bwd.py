@@ -157,3 +157,22 @@ def test_full_size_workload_sampled(gpu_lib):
         _, _, _, dmu = oracle.anchor_bwd(st("q"), st("k"), st("v"), mk, w.window, w.alpha * st("dy"))
         e = assert_close(down(g["dmeta"][h]), dmu.sum(0), "bf16", f"bwd dmeta[{h}]")
         log(f"bwd dmeta head {h}: {e:.2e}")
+
+
+def test_flagged_chunks_over_several_scan_blocks(gpu_lib):
+    """bf16 at d = 128 with every chunk's decay span beyond twice the
+    factorisable limit (each chunk left by the reverse walk to the last
+    launch) and more flags than one scan workgroup reads (1 x 16 heads x 33
+    chunks = 528 > 512): the last launch's flag-scan workgroups and its
+    sink-sum workgroups side by side.  Sampled heads, with their sink-key
+    gradients, against the oracle."""
+    B, H, L, d = 1, 16, 2112, 128
+    x = si.custom_inputs(35, B, H, L, d, 4, "bf16", with_dy=True, gate_mu=-3.0, gate_sd=0.3)
+    log(f"bwd all chunks flagged B={B} H={H} L={L}")
+    g = gpu_bwd(gpu_lib, x, "bf16", 64, 0.5)
+    for h in (0, H - 1):
+        xs = {n: x[n][:, h:h + 1] for n in ("q", "k", "v", "log_g", "dy")}
+        xs["meta_k"] = x["meta_k"][h:h + 1]
+        got = {kk: g[kk][:, h:h + 1] for kk in KEYS}
+        got["dmeta"] = g["dmeta"][h:h + 1]
+        compare(got, ref_bwd(xs, 64, 0.5), "bf16", f"flagged head {h}")
