@@ -441,7 +441,6 @@ def bench_decode(sqa, si, reps=3):
     out["graph"] = {"us_per_step": round(sum(ms_graph) / reps * 1e3, 2), "replays": reps, "steps_per_replay": steps,
                     "equals_eager_bitwise": bool(torch.equal(y, y_eager))}
     del graph, y_eager
-    out["graph_b1"] = bench_decode_graph_b1(sqa, reps)
     # back to back last: `reps` runs of the 1024 steps, the mean over all of
     # them (these are the last launches of the one-token kernel)
     prewarm(run_all, PREWARM_MS)
@@ -496,6 +495,7 @@ def bench_decode_graph_b1(sqa, reps, steps=256):
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / steps
 
+    prewarm(launch_all, PREWARM_MS)   # the host's launch path and the GPU clock settled
     timed(launch_all)
     eager = [timed(launch_all) for _ in range(reps)]
     y_eager = y.clone()
@@ -697,7 +697,7 @@ def main():
     ap.add_argument("--no-stage1", action="store_true")
     ap.add_argument("--no-long-ctx", action="store_true")
     ap.add_argument("--only", choices=["fwd", "decode", "bwd", "fwd_logit", "bwd_logit", "fp32_ablation", "stage1",
-                                       "long_ctx"],
+                                       "long_ctx", "decode_b1"],
                     default=None,
                     help="run one leg only (for profiler runs); prints that leg's record")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -730,6 +730,9 @@ def main():
 
     if args.only == "decode":
         print(json.dumps({"prewarm_ms": PREWARM_MS, **bench_decode(sqa, si)}), flush=True)
+        return
+    if args.only == "decode_b1":
+        print(json.dumps(bench_decode_graph_b1(sqa, 3)), flush=True)
         return
     if args.only == "bwd":
         print(json.dumps(bench_bwd(sqa, si, args.steps, args.warmup)), flush=True)
@@ -796,6 +799,9 @@ def main():
         print("# long_ctx done", file=sys.stderr, flush=True)
     if not args.no_decode:
         rec["decode"] = bench_decode(sqa, si)
+        # one sequence, eager and as a HIP graph (a leg of its own: its launches
+        # of the same kernel stay out of the batch-64 decode's profile)
+        rec["decode_b1"] = bench_decode_graph_b1(sqa, 3)
         print("# decode done", file=sys.stderr, flush=True)
     if not args.no_bwd:
         try:
