@@ -176,3 +176,13 @@ def test_flagged_chunks_over_several_scan_blocks(gpu_lib):
         got = {kk: g[kk][:, h:h + 1] for kk in KEYS}
         got["dmeta"] = g["dmeta"][h:h + 1]
         compare(got, ref_bwd(xs, 64, 0.5), "bf16", f"flagged head {h}")
+
+
+@pytest.mark.parametrize("n_meta", [0, 16])
+def test_flagged_chunks_and_sink_counts(gpu_lib, n_meta):
+    """Every chunk flagged (bf16, d = 128) with no sink keys (the last launch
+    then has flag-scan workgroups only) and with the most sink keys."""
+    x = si.custom_inputs(36, 2, 2, 192, 128, n_meta, "bf16", with_dy=True, gate_mu=-3.0, gate_sd=0.3,
+                         qk_sd=0.5, meta_sd=0.5)
+    log(f"bwd all chunks flagged n_meta={n_meta}")
+    compare(gpu_bwd(gpu_lib, x, "bf16", 64, 0.5), ref_bwd(x, 64, 0.5), "bf16", f"flagged m={n_meta}")
