@@ -195,7 +195,8 @@ def bench_fwd_logit(sqa, si, steps, warmup):
     gbs = alg_bytes / (ms * 1e-3) / 1e9
     return {"workload": "llama3_8b_prefill_bf16, gate logits in bf16", "ms": round(ms, 5), **stats_us(t),
             "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1), "alg_bytes": alg_bytes, "gbps": round(gbs, 1),
-            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": read_traffic("lizard_fwd", "llama3_8b_prefill_logit_bf16")}
 
 
 def bench_train_step(sqa, si, workload, steps, warmup):
@@ -580,7 +581,7 @@ def bench_bwd(sqa, si, steps, warmup, logit=False):
         "tflops": round(alg_flops / (ms * 1e-3) / 1e12, 2),
         "frac_mfma_peak": round(alg_flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
         "workspace_bytes": int(ws.numel()),
-        "traffic": None if logit else read_traffic("lizard_bwd", "train_bwd_bf16"),
+        "traffic": read_traffic("lizard_bwd", "train_bwd_logit_bf16" if logit else "train_bwd_bf16"),
     }
     if t_saved is not None:
         res["ms_with_saved_states"] = round(t_saved["mean"], 4)
