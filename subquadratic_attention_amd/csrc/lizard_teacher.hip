@@ -46,7 +46,10 @@ struct TeacherLayout {
 }  // namespace
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void teacher_attn_kernel(TeacherArgs a) {
+// Two wavefronts per SIMD (the registers a wavefront needs allow no more):
+// with that budget the compiler keeps the output accumulators in VGPRs, so
+// the per-block softmax work on them needs no moves to and from AGPRs.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void teacher_attn_kernel(TeacherArgs a) {
   typedef TeacherLayout<T, D> Lay;
   typedef Mfma<T> M;
   typedef typename M::frag frag;
@@ -102,7 +105,8 @@ __global__ __launch_bounds__(256) void teacher_attn_kernel(TeacherArgs a) {
   f32x4 oacc[NJT];
 #pragma unroll
   for (int jt = 0; jt < NJT; ++jt) oacc[jt] = zero4();
-  float mrun = -INFINITY, lrun = 0.f;     // running max (log2 units, scaled) and sum for query tq
+  float mrun = -INFINITY, lrun = 0.f;     // reference point (log2 units, scaled) and sum for query tq
+  constexpr float kLazyLog2 = 8.f;        // largest log2 of a weight before the reference moves
 
   // one key block's keys (16-byte vectors, row-major) and values (32-bit
   // words of VC columns, RPT consecutive keys per thread), loaded a block ahead
@@ -115,6 +119,21 @@ __global__ __launch_bounds__(256) void teacher_attn_kernel(TeacherArgs a) {
   uint32_t vreg[RPT];
   auto load_rows = [&](int kb, bool full) __attribute__((always_inline)) {
     const int k0 = kb * 64;
+    if (full) {
+      // one address per thread and array, the other rows at fixed offsets
+      // from it (no per-row 64-bit address arithmetic): key vector tid % KRV
+      // of rows tid / KRV + KRS u, value words of rows RPT (tid / VRW) + rr
+      constexpr int KRV = D / EPV, KRS = 256 / KRV;
+      const unsigned ut = static_cast<unsigned>(tid);
+      const T* kb0 = kg + ((size_t)k0 + ut / KRV) * D + (ut % KRV) * EPV;
+#pragma unroll
+      for (int u = 0; u < KVEC; ++u) kreg[u] = ld16(kb0 + (size_t)(KRS * u) * D);
+      const uint32_t* vb0 =
+          reinterpret_cast<const uint32_t*>(vg + ((size_t)k0 + (size_t)RPT * (ut / VRW)) * D + VC * (ut % VRW));
+#pragma unroll
+      for (int rr = 0; rr < RPT; ++rr) vreg[rr] = vb0[rr * (D / VC)];
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < KVEC; ++u) {
       const int i = tid + 256 * u;
@@ -203,27 +222,36 @@ __global__ __launch_bounds__(256) void teacher_attn_kernel(TeacherArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) mx = fmaxf(mx, z[kt][r]);
     // finite: key tq (or key 0) is always valid in the first block
-    const float mnew = fmaxf(mrun, xgroup_max(mx) * a.scale_log2);
-    const float corr = exp_2(mrun - mnew);  // 0 on the first block (mrun = -inf)
-    mrun = mnew;
+    const float mblk = xgroup_max(mx) * a.scale_log2;
+    // The reference point of the exponentials moves only when some query's
+    // block maximum exceeds it by more than 2^kLazyLog2 (so every weight stays
+    // at most 2^kLazyLog2, and most blocks skip rescaling the accumulators);
+    // O / l and the lse are the same up to rounding.  Always taken on the
+    // first block (mrun = -inf), where corr = 0.
+    if (__any(mblk > mrun + kLazyLog2)) {
+      const float mnew = fmaxf(mrun, mblk);
+      const float corr = exp_2(mrun - mnew);
+      mrun = mnew;
+      lrun *= corr;
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) oacc[jt][r] *= corr;
+    }
     float ls = 0.f;
     float p[4][4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p[kt][r] = exp_2(fmaf(z[kt][r], a.scale_log2, -mnew));
+        p[kt][r] = exp_2(fmaf(z[kt][r], a.scale_log2, -mrun));
         ls += p[kt][r];
       }
     if constexpr (sizeof(T) != 2) {
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) store_pack<T, 4>(sPw + m * Lay::LDP + 16 * kt + 4 * g, p[kt]);
     }
-    lrun = lrun * corr + xgroup_sum(ls);
-#pragma unroll
-    for (int jt = 0; jt < NJT; ++jt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) oacc[jt][r] *= corr;
+    lrun += xgroup_sum(ls);
 
     // ---- O^T[j][tq] += sum over the block's keys of V^T[j][s] P[tq][s] ----
     if constexpr (sizeof(T) == 2) {
