@@ -30,6 +30,12 @@ namespace lizard {
 
 namespace {
 
+// Query tiles of 16 per wavefront: bf16 takes two, so each key and value
+// fragment read from LDS feeds two products; float32 passes P through an LDS
+// tile per wavefront and takes one.
+template <typename T>
+constexpr int teacher_query_tiles() { return sizeof(T) == 2 ? 2 : 1; }
+
 template <typename T, int D>
 struct TeacherLayout {
   static constexpr int PAD = 16 / sizeof(T);
@@ -57,10 +63,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void t
   constexpr int QV = D / 4 / EPV;          // 16-byte vectors in a lane's k-quarter of a row
   constexpr int NF = D / 4 / M::KPL;       // MFMA steps over a D contraction
   constexpr int NJT = D / 16;              // output column tiles
+  constexpr int QT = teacher_query_tiles<T>();  // query tiles of 16 per wavefront
+  constexpr int QB = 64 * QT;              // queries per workgroup
   __shared__ __align__(16) unsigned char smem[Lay::TOTAL];
   T* sP = reinterpret_cast<T*>(smem + Lay::OFF_P);
 
-  const int L = a.L, nqb = (L + 63) / 64;
+  const int L = a.L, nqb = (L + QB - 1) / QB;
   // block -> (b*h, query block), the longest rows (last query blocks) first
   const int x = blockIdx.x;
   const int bh = x % a.BH;
@@ -80,32 +88,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void t
   T* yg = reinterpret_cast<T*>(a.y) + (size_t)bh * L * D;
   T* sPw = sP + w * 16 * Lay::LDP;
 
-  // this lane's query (column m of the wavefront's tiles), its k-quarter g
-  const int tq = qb * 64 + 16 * w + m;
-  frag qf[NF];
-  {
+  // this lane's query in tile qt (column m of the wavefront's tiles): row
+  // 16w + m of the workgroup's 64-query half qt, so every wavefront has one
+  // tile in each half; its k-quarter g
+  int tq[QT];
+  frag qf[QT][NF];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    tq[qt] = qb * QB + 64 * qt + 16 * w + m;
     uint4 raw[QV];
-    const bool ok = tq < L;
-    const T* p = qg + (size_t)(ok ? tq : 0) * D + g * (D / 4);
+    const bool ok = tq[qt] < L;
+    const T* p = qg + (size_t)(ok ? tq[qt] : 0) * D + g * (D / 4);
 #pragma unroll
     for (int e = 0; e < QV; ++e) raw[e] = ok ? ld16(p + e * EPV) : make_uint4(0, 0, 0, 0);
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
-      for (int e = 0; e < NF; ++e) qf[e] = __builtin_bit_cast(bf16x8, raw[e]);
+      for (int e = 0; e < NF; ++e) qf[qt][e] = __builtin_bit_cast(bf16x8, raw[e]);
     } else {
 #pragma unroll
       for (int e = 0; e < NF; ++e) {
         const uint4 r = raw[e >> 2];
         const uint32_t u = (e & 3) == 0 ? r.x : (e & 3) == 1 ? r.y : (e & 3) == 2 ? r.z : r.w;
-        qf[e] = __builtin_bit_cast(float, u);
+        qf[qt][e] = __builtin_bit_cast(float, u);
       }
     }
   }
 
-  f32x4 oacc[NJT];
+  f32x4 oacc[QT][NJT];
 #pragma unroll
-  for (int jt = 0; jt < NJT; ++jt) oacc[jt] = zero4();
-  float mrun = -INFINITY, lrun = 0.f;     // reference point (log2 units, scaled) and sum for query tq
+  for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+    for (int jt = 0; jt < NJT; ++jt) oacc[qt][jt] = zero4();
+  // per query tq[qt]: reference point (log2 units, scaled) and sum
+  float mrun[QT], lrun[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    mrun[qt] = -INFINITY;
+    lrun[qt] = 0.f;
+  }
   constexpr float kLazyLog2 = 8.f;        // largest log2 of a weight before the reference moves
 
   // one key block's keys (16-byte vectors, row-major) and values (32-bit
@@ -188,112 +208,138 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void t
 
   // Key block kb is in buffer kb & 1.  Block kb + 1's loads fly while kb is
   // multiplied, then go to the other buffer, whose last readers (block kb - 1)
-  // finished before the previous barrier: one barrier per block.
-  for (int kb = 0; kb <= qb; ++kb) {
+  // finished before the previous barrier: one barrier per block.  The last
+  // key block is the one holding the workgroup's last query (or key L - 1).
+  const int kb_end = (min(qb * QB + QB, L) - 1) / 64;
+  for (int kb = 0; kb <= kb_end; ++kb) {
     const int k0 = kb * 64;
     const T* sK = reinterpret_cast<const T*>(smem + (kb & 1) * Lay::BUF + Lay::OFF_K);
     const T* sVt = reinterpret_cast<const T*>(smem + (kb & 1) * Lay::BUF + Lay::OFF_V);
-    if (kb < qb) load_block(kb + 1);
+    if (kb < kb_end) load_block(kb + 1);
 
-    // ---- S^T tiles: keys key_of(kt, 4g + r) (rows) x query tq (column m) ----
-    f32x4 z[4];
+    // ---- S^T tiles: keys key_of(kt, 4g + r) (rows) x query tq[qt] (column m);
+    // each key fragment read once for all QT query tiles ----
+    f32x4 z[QT][4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       const T* kp = sK + key_of(kt, m) * Lay::LDK + g * (D / 4);
-      z[kt] = zero4();
 #pragma unroll
-      for (int e = 0; e < NF; ++e) z[kt] = M::mma(M::load(kp + e * M::KPL), qf[e], z[kt]);
+      for (int qt = 0; qt < QT; ++qt) z[qt][kt] = zero4();
+#pragma unroll
+      for (int e = 0; e < NF; ++e) {
+        const frag kf = M::load(kp + e * M::KPL);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) z[qt][kt] = M::mma(kf, qf[qt][e], z[qt][kt]);
+      }
     }
-    // causal mask, only on the diagonal block (keys past L lie only there:
-    // every earlier block is full); maxima on raw logits (the scale is
-    // positive), the scale folded into the exponent
-    if (kb == qb) {
+    // causal mask, only on the key blocks from the workgroup's first query on
+    // (keys past L lie only there: every earlier block is full); a tile whose
+    // queries all precede the block gets -inf everywhere, weights 0.  Maxima
+    // on raw logits (the scale is positive), the scale folded into the exponent
+    if (kb >= qb * QT) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int s = k0 + key_of(kt, 4 * g + r);
+            z[qt][kt][r] = s <= tq[qt] && s < L ? z[qt][kt][r] : -INFINITY;
+          }
+    }
+    float p[QT][4][4];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, z[qt][kt][r]);
+      // finite on the first block (key 0 is valid for every query); -inf for a
+      // tile the block lies wholly after, which then leaves its state alone
+      const float mblk = xgroup_max(mx) * a.scale_log2;
+      // The reference point of the exponentials moves only when some query's
+      // block maximum exceeds it by more than 2^kLazyLog2 (so every weight
+      // stays at most 2^kLazyLog2, and most blocks skip rescaling the
+      // accumulators); O / l and the lse are the same up to rounding.  Always
+      // taken on the first block (mrun = -inf), where corr = 0.
+      if (__any(mblk > mrun[qt] + kLazyLog2)) {
+        const float mnew = fmaxf(mrun[qt], mblk);
+        const float corr = exp_2(mrun[qt] - mnew);
+        mrun[qt] = mnew;
+        lrun[qt] *= corr;
+#pragma unroll
+        for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) oacc[qt][jt][r] *= corr;
+      }
+      float ls = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int s = k0 + key_of(kt, 4 * g + r);
-          z[kt][r] = s <= tq && s < L ? z[kt][r] : -INFINITY;
+          p[qt][kt][r] = exp_2(fmaf(z[qt][kt][r], a.scale_log2, -mrun[qt]));
+          ls += p[qt][kt][r];
         }
+      lrun[qt] += xgroup_sum(ls);
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, z[kt][r]);
-    // finite: key tq (or key 0) is always valid in the first block
-    const float mblk = xgroup_max(mx) * a.scale_log2;
-    // The reference point of the exponentials moves only when some query's
-    // block maximum exceeds it by more than 2^kLazyLog2 (so every weight stays
-    // at most 2^kLazyLog2, and most blocks skip rescaling the accumulators);
-    // O / l and the lse are the same up to rounding.  Always taken on the
-    // first block (mrun = -inf), where corr = 0.
-    if (__any(mblk > mrun + kLazyLog2)) {
-      const float mnew = fmaxf(mrun, mblk);
-      const float corr = exp_2(mrun - mnew);
-      mrun = mnew;
-      lrun *= corr;
-#pragma unroll
-      for (int jt = 0; jt < NJT; ++jt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) oacc[jt][r] *= corr;
-    }
-    float ls = 0.f;
-    float p[4][4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[kt][r] = exp_2(fmaf(z[kt][r], a.scale_log2, -mrun));
-        ls += p[kt][r];
-      }
     if constexpr (sizeof(T) != 2) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) store_pack<T, 4>(sPw + m * Lay::LDP + 16 * kt + 4 * g, p[kt]);
+      for (int kt = 0; kt < 4; ++kt) store_pack<T, 4>(sPw + m * Lay::LDP + 16 * kt + 4 * g, p[0][kt]);
     }
-    lrun += xgroup_sum(ls);
 
     // ---- O^T[j][tq] += sum over the block's keys of V^T[j][s] P[tq][s] ----
     if constexpr (sizeof(T) == 2) {
       // contraction step e over keys 32e .. 32e + 31: lane group g takes
       // keys 32e + 8g .. + 7, which are the scores of tiles 2e and 2e + 1
       // this lane holds
-      frag pf[2];
+      frag pf[QT][2];
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        bf16x8 f;
+      for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          f[r] = static_cast<bf16>(p[2 * e][r]);
-          f[4 + r] = static_cast<bf16>(p[2 * e + 1][r]);
+        for (int e = 0; e < 2; ++e) {
+          bf16x8 f;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            f[r] = static_cast<bf16>(p[qt][2 * e][r]);
+            f[4 + r] = static_cast<bf16>(p[qt][2 * e + 1][r]);
+          }
+          pf[qt][e] = f;
         }
-        pf[e] = f;
-      }
+      // each value fragment read once for all QT query tiles
 #pragma unroll
       for (int jt = 0; jt < NJT; ++jt)
 #pragma unroll
-        for (int e = 0; e < 2; ++e)
-          oacc[jt] = M::mma(M::load(sVt + (16 * jt + m) * Lay::LDV + 32 * e + 8 * g), pf[e], oacc[jt]);
+        for (int e = 0; e < 2; ++e) {
+          const frag vf = M::load(sVt + (16 * jt + m) * Lay::LDV + 32 * e + 8 * g);
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) oacc[qt][jt] = M::mma(vf, pf[qt][e], oacc[qt][jt]);
+        }
     } else {
+      static_assert(QT == 1, "the float32 teacher passes P through one LDS tile per wavefront");
       wave_lds_sync();
 #pragma unroll
       for (int jt = 0; jt < NJT; ++jt)
-        oacc[jt] = mma_rows<T, 64>(oacc[jt], sVt + (16 * jt + m) * Lay::LDV + g * 16, sPw + m * Lay::LDP + g * 16);
+        oacc[0][jt] = mma_rows<T, 64>(oacc[0][jt], sVt + (16 * jt + m) * Lay::LDV + g * 16, sPw + m * Lay::LDP + g * 16);
     }
-    if (kb < qb) store_block((kb + 1) & 1);
+    if (kb < kb_end) store_block((kb + 1) & 1);
     // the next block is in place; this wavefront's P tile is free again
     __syncthreads();
   }
 
   // ---- epilogue: O[tq][16jt + 4g + r] = O^T / l ----
-  if (tq < L) {
-    const float inv = 1.0f / lrun;
 #pragma unroll
-    for (int jt = 0; jt < NJT; ++jt) {
-      const float o4[4] = {oacc[jt][0] * inv, oacc[jt][1] * inv, oacc[jt][2] * inv, oacc[jt][3] * inv};
-      store_pack<T, 4>(yg + (size_t)tq * D + 16 * jt + 4 * g, o4);
+  for (int qt = 0; qt < QT; ++qt) {
+    if (tq[qt] < L) {
+      const float inv = 1.0f / lrun[qt];
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt) {
+        const float o4[4] = {oacc[qt][jt][0] * inv, oacc[qt][jt][1] * inv, oacc[qt][jt][2] * inv,
+                             oacc[qt][jt][3] * inv};
+        store_pack<T, 4>(yg + (size_t)tq[qt] * D + 16 * jt + 4 * g, o4);
+      }
+      if (a.lse && g == 0) a.lse[(size_t)bh * L + tq[qt]] = (mrun[qt] + __log2f(lrun[qt])) * kLn2;
     }
-    if (a.lse && g == 0) a.lse[(size_t)bh * L + tq] = (mrun + __log2f(lrun)) * kLn2;
   }
 }
 
@@ -340,7 +386,8 @@ __global__ __launch_bounds__(256) void transfer_loss_kernel(const T* y, const T*
 }
 
 hipError_t launch_teacher(const TeacherArgs& a, int dtype_bf16, int D, hipStream_t st) {
-  const int nqb = (a.L + 63) / 64;
+  const int qb_rows = 64 * (dtype_bf16 ? teacher_query_tiles<bf16>() : teacher_query_tiles<float>());
+  const int nqb = (a.L + qb_rows - 1) / qb_rows;
   dim3 grid(a.BH * nqb);
   if (dtype_bf16 && D == 128) hipLaunchKernelGGL((teacher_attn_kernel<bf16, 128>), grid, dim3(256), 0, st, a);
   else if (dtype_bf16 && D == 64) hipLaunchKernelGGL((teacher_attn_kernel<bf16, 64>), grid, dim3(256), 0, st, a);
