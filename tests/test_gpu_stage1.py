@@ -13,7 +13,7 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128)])
-@pytest.mark.parametrize("L", [1, 64, 150, 300])
+@pytest.mark.parametrize("L", [1, 64, 150, 200, 257, 300])
 def test_teacher(gpu_lib, dtype, d, L):
     import torch
 
