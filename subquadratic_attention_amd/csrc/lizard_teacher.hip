@@ -12,17 +12,20 @@
 //   loss = mean((Y - Y_T)^2),  dY = 2 (Y - Y_T) / N (this file, loss kernel)
 //   the Lizard backward of dY                       (lizard_bwd.hip)
 //
-// Teacher kernel: one workgroup of 4 wavefronts per (b*h, block of 64
-// queries); wavefront w owns queries 16w..16w+15 of the block (MFMA column m)
+// Teacher kernel: one workgroup of 4 wavefronts per (b*h, block of 64 QT
+// queries); wavefront w owns query tiles of 16 (MFMA column m): queries
+// 64qt + 16w .. + 15 of the block for qt < QT (QT = 2 in bf16, 1 in fp32),
 // and walks the key blocks up to the diagonal.  Per key block the keys and
-// the transposed values are staged in LDS; S^T tiles (keys x queries) come
-// from MFMA with the queries as the B operand, the online softmax keeps one
-// running maximum and sum per query in every lane of its column, and P goes
-// into the O^T = V^T P^T product, whose accumulators hold O[query m][j =
-// 16jt + 4g + r].  In bf16, P stays in registers: the S^T tiles take their
-// key rows in an order under which the scores a lane holds are exactly the
-// keys its lane group contracts over in the product (see key_of below); in
-// fp32 it goes through LDS (per wavefront).
+// the transposed values are staged in LDS, and each key or value fragment a
+// wavefront reads feeds the products of all its query tiles.  S^T tiles
+// (keys x queries) come from MFMA with the queries as the B operand, the
+// online softmax keeps one reference point and sum per query in every lane
+// of its column, and P goes into the O^T = V^T P^T product, whose
+// accumulators hold O[query m][j = 16jt + 4g + r].  In bf16, P stays in
+// registers: the S^T tiles take their key rows in an order under which the
+// scores a lane holds are exactly the keys its lane group contracts over in
+// the product (see key_of below); in fp32 it goes through LDS (per
+// wavefront).
 #include "lizard_common.hpp"
 #include "lizard_kernels.hpp"
 
