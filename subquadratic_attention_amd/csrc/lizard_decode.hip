@@ -31,9 +31,14 @@ namespace lizard {
 // MULTI = false: one token per row (the loop below runs once and the state
 // registers die after the update, which keeps the kernel at ~90 VGPRs and
 // five workgroups per CU); MULTI = true: a.T tokens with the state held in
-// registers across them.
+// registers across them.  In bf16 the multi-token form is held to three
+// wavefronts per SIMD (168 VGPRs, a 20-byte spill): at d = 128 it would
+// otherwise take 203 VGPRs and two, and the third workgroup per CU hides
+// more of the state and window reads (4 tokens per call: 29.1 -> 27.6 us
+// per token at batch 64).
 template <typename T, int D, bool LOGIT, bool MULTI>
-__global__ __launch_bounds__(256) void lizard_decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MULTI && sizeof(T) == 2 ? 3 : 1)))
+void lizard_decode_kernel(DecodeArgs a) {
   constexpr int CG = D / 4;            // float4 column groups per row
   constexpr int RG = 256 / CG;         // row groups
   constexpr int RPT = D / RG;          // rows per thread
