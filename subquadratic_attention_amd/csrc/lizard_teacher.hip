@@ -347,12 +347,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void t
 }
 
 // dY = 2 (Y - Y_T) / N and, per (b, h), sum((Y - Y_T)^2) / N in a fixed order.
-// One workgroup of 256 threads per (b, h); thread t sums elements t, t + 256,
-// ... of the head, then the 256 partial sums are added by a fixed tree.
+// One workgroup of kLossThreads threads per (b, h) (16 wavefronts, so a
+// head's stream has four per SIMD in flight); thread t sums elements t,
+// t + kLossThreads, ... of the head, then the partial sums are added by a
+// fixed tree.
+constexpr int kLossThreads = 1024;
 template <typename T>
-__global__ __launch_bounds__(256) void transfer_loss_kernel(const T* y, const T* yt, T* dy, float* loss_bh,
-                                                            long long per_head, float inv_n) {
-  __shared__ float sRed[256];
+__global__ __launch_bounds__(kLossThreads) void transfer_loss_kernel(const T* y, const T* yt, T* dy, float* loss_bh,
+                                                                     long long per_head, float inv_n) {
+  __shared__ float sRed[kLossThreads];
   const int bh = blockIdx.x, tid = threadIdx.x;
   const T* yp = y + (size_t)bh * per_head;
   const T* tp = yt + (size_t)bh * per_head;
@@ -360,7 +363,7 @@ __global__ __launch_bounds__(256) void transfer_loss_kernel(const T* y, const T*
   float acc = 0.f;
   constexpr int V = 16 / sizeof(T);
   const long long nvec = per_head / V;
-  for (long long i = tid; i < nvec; i += 256) {
+  for (long long i = tid; i < nvec; i += kLossThreads) {
     float a8[V], b8[V], d8[V];
     unpack16<T>(ld16(yp + i * V), a8);
     unpack16<T>(ld16(tp + i * V), b8);
@@ -373,7 +376,7 @@ __global__ __launch_bounds__(256) void transfer_loss_kernel(const T* y, const T*
     if constexpr (V == 8) store_pack<T, 8>(dp + i * V, d8);
     else store_pack<T, 4>(dp + i * V, d8);
   }
-  for (long long i = nvec * V + tid; i < per_head; i += 256) {   // tail (per_head not a multiple of V)
+  for (long long i = nvec * V + tid; i < per_head; i += kLossThreads) {   // tail (per_head not a multiple of V)
     const float e = to_f32(yp[i]) - to_f32(tp[i]);
     acc += e * e;
     dp[i] = from_f32<T>(2.f * inv_n * e);
@@ -381,7 +384,7 @@ __global__ __launch_bounds__(256) void transfer_loss_kernel(const T* y, const T*
   sRed[tid] = acc;
   __syncthreads();
 #pragma unroll
-  for (int s = 128; s >= 1; s >>= 1) {
+  for (int s = kLossThreads / 2; s >= 1; s >>= 1) {
     if (tid < s) sRed[tid] += sRed[tid + s];
     __syncthreads();
   }
@@ -402,10 +405,10 @@ hipError_t launch_teacher(const TeacherArgs& a, int dtype_bf16, int D, hipStream
 hipError_t launch_transfer_loss(const void* y, const void* yt, void* dy, float* loss_bh, int BH, long long per_head,
                                 float inv_n, int dtype_bf16, hipStream_t st) {
   if (dtype_bf16)
-    hipLaunchKernelGGL(transfer_loss_kernel<bf16>, dim3(BH), dim3(256), 0, st, static_cast<const bf16*>(y),
+    hipLaunchKernelGGL(transfer_loss_kernel<bf16>, dim3(BH), dim3(kLossThreads), 0, st, static_cast<const bf16*>(y),
                        static_cast<const bf16*>(yt), static_cast<bf16*>(dy), loss_bh, per_head, inv_n);
   else
-    hipLaunchKernelGGL(transfer_loss_kernel<float>, dim3(BH), dim3(256), 0, st, static_cast<const float*>(y),
+    hipLaunchKernelGGL(transfer_loss_kernel<float>, dim3(BH), dim3(kLossThreads), 0, st, static_cast<const float*>(y),
                        static_cast<const float*>(yt), static_cast<float*>(dy), loss_bh, per_head, inv_n);
   return hipGetLastError();
 }
